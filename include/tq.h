@@ -1,0 +1,195 @@
+/*
+ * tq.h — C ABI of the MI355X (gfx950) library for online KV-vector
+ * quantization and decode attention computed from the packed codes.
+ *
+ * Method (web pages, cited by title and section):
+ *  [WIT]  "什么是TurboQuant？谷歌突破性AI压缩技术实现6倍KV缓存缩减和8倍推理加速"
+ *         (a2a-mcp.org blog, "What is TurboQuant?"):
+ *         - "TurboQuant 工作原理" > "第一阶段" item 1: one data-independent random
+ *           orthogonal rotation (QR of a Gaussian matrix); rotated coordinates
+ *           follow Beta((d-1)/2,(d-1)/2) on [-1, 1].
+ *         - "第一阶段" item 2: normalise the vector; a Lloyd-Max quantizer that
+ *           is MSE-optimal for that law gives a few bits per coordinate.
+ *         - "第二阶段：QJL 残差校正": a 1-bit quantized Johnson-Lindenstrauss
+ *           sketch of the residual corrects inner-product bias.
+ *         - "如何实现 TurboQuant" item 1: the codebook is precomputed per head
+ *           dimension and bit width; vectors are quantized on every cache
+ *           update; the query is rotated once and attention dot products are
+ *           taken straight from the stored indices.
+ *  [VLLM] "A First Comprehensive Study of TurboQuant: Accuracy and
+ *         Performance" (papercache.org), section A3: variants k8v4, 4bit_nc,
+ *         k3v4_nc, 3bit_nc (nc = norm correction).
+ *
+ * Conventions for every call:
+ *  - Tensor pointers are DEVICE pointers owned by the caller, unless a
+ *    parameter says "host".  The library owns only tq_codebook objects.
+ *  - Calls that take a `stream` (a hipStream_t passed as void*; NULL = the
+ *    default stream) only enqueue work on it and return before it runs; the
+ *    other calls are synchronous.
+ *  - Every call returns a tq_status.  On failure nothing has been enqueued
+ *    and tq_last_error() returns a message (thread-local, valid until the
+ *    next failing call on the same thread).  No C++ exception crosses the ABI.
+ *  - Non-finite inputs are undefined behaviour (not checked on the hot path).
+ *  - Only tq_codebook_build allocates device memory.
+ */
+#ifndef TQ_H_
+#define TQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TQ_OK = 0,
+  TQ_ERR_INVALID = 1,     /* bad argument (null, out of range, inconsistent) */
+  TQ_ERR_UNSUPPORTED = 2, /* valid request this build has no kernel for      */
+  TQ_ERR_HIP = 3,         /* a HIP runtime call failed                        */
+  TQ_ERR_ALLOC = 4,       /* device or host allocation failed                 */
+  TQ_ERR_NUMERIC = 5      /* codebook solver did not converge                 */
+} tq_status;
+
+typedef enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 } tq_dtype;
+
+/* Code layouts (the pages only say "bit-packed"; both are LSB-first).
+ *  TQ_LAYOUT_ROW: vector v of sequence s is row r = s*seq_stride + v.
+ *    idx  row r at idx + r*idx_row_bytes: coordinate i at bits [i*b, i*b+b)
+ *         of a little-endian bit stream (bit p in byte p>>3, position p&7),
+ *         zero bits after coordinate d-1.  Minimum idx_row_bytes is
+ *         4*b*ceil(d/32).
+ *    sign row r at sign + r*sign_row_bytes: sketch row j at bit j, zero bits
+ *         after j = m-1.  Minimum sign_row_bytes is 4*ceil(m/32).
+ *  TQ_LAYOUT_TILE32 (value codes for decode): sequence s is cut into blocks
+ *    of 32 vectors; block k of sequence s starts at
+ *    idx + (s*(seq_stride/32) + k) * (d*b*4) bytes and holds, for each
+ *    coordinate i, b little-endian 32-bit words (a 32*b-bit stream) whose
+ *    slot q in 0..31 holds vector tile32_token(q) of the block at bits
+ *    [q*b, q*b+b), where tile32_token(q) = 4*(q/8) + q%8 for q%8 < 4 and
+ *    16 + 4*(q/8) + q%8 - 4 otherwise.  seq_stride must be a multiple of 32;
+ *    idx_row_bytes is ignored.  Sign codes are not supported in this layout.
+ *  scale[r] / rnorm[r] (fp32) are indexed by r = s*seq_stride + v in both. */
+typedef enum { TQ_LAYOUT_ROW = 0, TQ_LAYOUT_TILE32 = 1 } tq_layout;
+
+typedef struct tq_codebook tq_codebook; /* opaque; immutable after build */
+
+/* Everything a codebook is a pure function of.
+ *  d               vector length, 3..256
+ *  bits            Lloyd-Max bits per coordinate, 1..8 (L = 2^bits levels)
+ *  qjl_m           QJL sketch rows, 0 (off) or 1..256
+ *  norm_correction 0: scale = |x|; 1: scale = |x| / |c[idx]| (nc variants)
+ *  rot_seed        seed of the Gaussian matrix whose QR gives the rotation
+ *  qjl_seed        seed of the Gaussian sketch matrix S (m x d)           */
+typedef struct {
+  int32_t d, bits, qjl_m, norm_correction;
+  uint64_t rot_seed, qjl_seed;
+} tq_params;
+
+/* Caller-owned code planes of one tensor (keys or values).
+ *  idx    packed indices (layout above)                       device
+ *  sign   packed QJL sign bits, NULL iff the codebook's qjl_m == 0
+ *  scale  fp32 per vector: |x| (or |x|/|c[idx]| with nc)
+ *  rnorm  fp32 per vector: |x| * |r| (QJL residual norm), NULL iff qjl_m == 0
+ *  idx_row_bytes, sign_row_bytes  row pitch (ROW layout), multiple of 4
+ *  seq_stride  capacity in vectors per sequence
+ *  layout      a tq_layout                                                */
+typedef struct {
+  void* idx;
+  void* sign;
+  float* scale;
+  float* rnorm;
+  int64_t idx_row_bytes;
+  int64_t sign_row_bytes;
+  int64_t seq_stride;
+  int32_t layout;
+  int32_t reserved;
+} tq_codes;
+
+/* Builds a codebook on the host and uploads it to the current HIP device
+ * ([WIT] 第一阶段 items 1-2; 如何实现 item 1):
+ *  - Lloyd-Max centroids c[0..L-1] and boundaries t_k = (c[k-1]+c[k])/2 for
+ *    the density f_d(y) = (1-y^2)^((d-3)/2) / B(1/2,(d-1)/2) on [-1, 1];
+ *  - rotation Pi = Q of G = QR with diag(R) > 0, G (d x d, row-major) drawn
+ *    by splitmix64(rot_seed) + Box-Muller (cosine branch);
+ *  - S (m x d, row-major) drawn the same way from qjl_seed.
+ * Synchronous.  On success *out owns device memory until
+ * tq_codebook_destroy.  Errors: TQ_ERR_INVALID (params), TQ_ERR_NUMERIC,
+ * TQ_ERR_ALLOC / TQ_ERR_HIP (upload). */
+tq_status tq_codebook_build(const tq_params* params, tq_codebook** out);
+
+/* Frees a codebook (NULL is accepted).  The caller must make sure no
+ * enqueued call still uses it.  Synchronous. */
+tq_status tq_codebook_destroy(tq_codebook* cb);
+
+/* Copies the codebook's float64 values to HOST buffers (any may be NULL):
+ * centroids[L], boundaries[L-1], rot[d*d] (row-major Pi), qjl[m*d]. */
+tq_status tq_codebook_export(const tq_codebook* cb, double* centroids, double* boundaries,
+                             double* rot, double* qjl);
+
+/* Host only (no device is touched): computes the float64 values a codebook
+ * with these params holds, into HOST buffers (any may be NULL):
+ * centroids[L], boundaries[L-1], rot[d*d] (row-major Pi), qjl[m*d].
+ * Same construction and errors as tq_codebook_build. */
+tq_status tq_codebook_values(const tq_params* params, double* centroids, double* boundaries,
+                             double* rot, double* qjl);
+
+/* Minimum ROW-layout pitches for this codebook: 4*bits*ceil(d/32) and
+ * 4*ceil(m/32) (0 when qjl_m == 0). */
+tq_status tq_code_row_bytes(const tq_codebook* cb, int64_t* idx_row_bytes,
+                            int64_t* sign_row_bytes);
+
+/* Online quantization of a batch of key and/or value vectors
+ * ([WIT] 第一阶段, 第二阶段; 如何实现 item 1: quantize at each cache update):
+ * for each vector x: n = |x|, y = Pi x / n (y = 0 if n = 0),
+ * idx_i = #{k : y_i >= t_k}, scale = n (nc: n/|c[idx]|); with QJL,
+ * r = y - (scale/n) c[idx], sign_j = [(S r)_j >= 0], rnorm = n |r|.
+ *  k, v        inputs [n_seq][n_tok][d] contiguous, dtype dt; v may be NULL
+ *              (then vcb and v_out are ignored); k may be NULL likewise.
+ *              n_seq == 0 or n_tok == 0 is a no-op that returns TQ_OK.
+ *  tok_offset  vector t of the input goes to position tok_offset + t of its
+ *              sequence; tok_offset + n_tok <= seq_stride.  Codes of other
+ *              positions are left untouched (tile32 blocks are updated by
+ *              read-modify-write; calls on one stream are ordered).
+ * Errors: TQ_ERR_INVALID, TQ_ERR_UNSUPPORTED (layout/d combination),
+ * TQ_ERR_HIP (launch). */
+tq_status tq_quantize_kv(const tq_codebook* kcb, const tq_codebook* vcb, const void* k,
+                         const void* v, tq_dtype dt, int64_t n_seq, int64_t n_tok,
+                         int64_t tok_offset, const tq_codes* k_out, const tq_codes* v_out,
+                         void* stream);
+
+/* Workspace bytes tq_attn_decode needs for this shape (host only). */
+tq_status tq_attn_decode_workspace(int64_t B, int64_t Hq, int64_t Hkv, int64_t n_ctx,
+                                   int32_t d, size_t* bytes);
+
+/* Decode attention straight from packed codes ([WIT] 如何实现 item 1; 专业提示):
+ * per query head hq of batch b (KV head h = hq / (Hq/Hkv), sequence
+ * s = b*Hkv + h), with q~ = Pi_K q:
+ *   logit_j = sm_scale * ( scaleK_j <q~, cK[idxK_j]>
+ *                          + sqrt(pi/2)/m rnormK_j <S_K q~, 2 sign_j - 1> )
+ *   p = softmax over j < len_b (no mask otherwise)
+ *   out = Pi_V^T sum_j p_j scaleV_j cV[idxV_j]
+ *  q         [B][Hq][d], dtype qdt
+ *  k         key codes, TQ_LAYOUT_ROW; v value codes, TQ_LAYOUT_TILE32;
+ *            both with seq_stride a multiple of 32 and >= n_ctx
+ *  seq_lens  device int32 [B] with 0 <= len_b <= n_ctx, or NULL (all n_ctx);
+ *            len_b = 0 gives out = 0 and logits -inf
+ *  out       fp32 [B][Hq][d]
+ *  logits    fp32 [B][Hq][n_ctx] or NULL; -inf for j >= len_b
+ *  workspace device scratch of >= tq_attn_decode_workspace bytes
+ * Errors: TQ_ERR_INVALID, TQ_ERR_UNSUPPORTED (d != 128 or bit widths
+ * without a kernel), TQ_ERR_HIP. */
+tq_status tq_attn_decode(const tq_codebook* kcb, const tq_codebook* vcb, const void* q,
+                         tq_dtype qdt, int64_t B, int64_t Hq, int64_t Hkv, const tq_codes* k,
+                         const tq_codes* v, const int32_t* seq_lens, int64_t n_ctx,
+                         float sm_scale, float* out, float* logits, void* workspace,
+                         size_t ws_bytes, void* stream);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* tq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H_ */

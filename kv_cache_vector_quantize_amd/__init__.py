@@ -1,0 +1,20 @@
+"""MI355X (gfx950) online KV-vector quantization and decode attention from
+packed codes.  The compute runs in libtq.so (hand-written HIP kernels behind
+a C ABI, declared in include/tq.h); this package is a thin ctypes binding."""
+from ._lib import (  # noqa: F401
+    EXPORTS,
+    LIB_PATH,
+    TQ_BF16,
+    TQ_F16,
+    TQ_F32,
+    TQ_LAYOUT_ROW,
+    TQ_LAYOUT_TILE32,
+    Codebook,
+    Codes,
+    TQError,
+    lib,
+    tq_attn_decode,
+    tq_attn_decode_workspace,
+    tq_codebook_values,
+    tq_quantize_kv,
+)

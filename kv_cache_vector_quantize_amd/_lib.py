@@ -1,0 +1,250 @@
+"""ctypes binding of libtq.so (argument marshalling only).
+
+Every function here has the name of the C entry point it calls.  torch is
+used for device memory and streams; all arithmetic of the method runs in the
+library's HIP kernels.  If libtq.so is missing, importing the functions
+raises: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtq.so")
+
+TQ_OK, TQ_ERR_INVALID, TQ_ERR_UNSUPPORTED, TQ_ERR_HIP, TQ_ERR_ALLOC, TQ_ERR_NUMERIC = range(6)
+TQ_F32, TQ_BF16, TQ_F16 = 0, 1, 2
+TQ_LAYOUT_ROW, TQ_LAYOUT_TILE32 = 0, 1
+
+# every symbol include/tq.h declares
+EXPORTS = (
+    "tq_codebook_build", "tq_codebook_destroy", "tq_codebook_export", "tq_codebook_values",
+    "tq_code_row_bytes", "tq_quantize_kv", "tq_attn_decode_workspace", "tq_attn_decode",
+    "tq_last_error",
+)
+
+
+class TQError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"tq status {status}: {msg}")
+        self.status = status
+
+
+class tq_params(ctypes.Structure):
+    _fields_ = [("d", ctypes.c_int32), ("bits", ctypes.c_int32), ("qjl_m", ctypes.c_int32),
+                ("norm_correction", ctypes.c_int32), ("rot_seed", ctypes.c_uint64),
+                ("qjl_seed", ctypes.c_uint64)]
+
+
+class tq_codes(ctypes.Structure):
+    _fields_ = [("idx", ctypes.c_void_p), ("sign", ctypes.c_void_p), ("scale", ctypes.c_void_p),
+                ("rnorm", ctypes.c_void_p), ("idx_row_bytes", ctypes.c_int64),
+                ("sign_row_bytes", ctypes.c_int64), ("seq_stride", ctypes.c_int64),
+                ("layout", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libtq.so (once).  Raises if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m kv_cache_vector_quantize_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, dp = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.POINTER(ctypes.c_double)
+    L.tq_last_error.restype = ctypes.c_char_p
+    L.tq_last_error.argtypes = []
+    L.tq_codebook_build.argtypes = [ctypes.POINTER(tq_params), ctypes.POINTER(vp)]
+    L.tq_codebook_destroy.argtypes = [vp]
+    L.tq_codebook_export.argtypes = [vp, dp, dp, dp, dp]
+    L.tq_codebook_values.argtypes = [ctypes.POINTER(tq_params), dp, dp, dp, dp]
+    L.tq_code_row_bytes.argtypes = [vp, ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    L.tq_quantize_kv.argtypes = [vp, vp, vp, vp, i32, i64, i64, i64,
+                                 ctypes.POINTER(tq_codes), ctypes.POINTER(tq_codes), vp]
+    L.tq_attn_decode_workspace.argtypes = [i64, i64, i64, i64, i32, ctypes.POINTER(ctypes.c_size_t)]
+    L.tq_attn_decode.argtypes = [vp, vp, vp, i32, i64, i64, i64, ctypes.POINTER(tq_codes),
+                                 ctypes.POINTER(tq_codes), vp, i64, ctypes.c_float, vp, vp, vp,
+                                 ctypes.c_size_t, vp]
+    for name in EXPORTS:
+        if name != "tq_last_error":
+            getattr(L, name).restype = ctypes.c_int
+    _LIB = L
+    return L
+
+
+def _check(status: int):
+    if status != TQ_OK:
+        raise TQError(status, lib().tq_last_error().decode())
+
+
+def _dptr(a: np.ndarray | None):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _dtype_code(t) -> int:
+    import torch
+    return {torch.float32: TQ_F32, torch.bfloat16: TQ_BF16, torch.float16: TQ_F16}[t.dtype]
+
+
+def _stream_handle(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+# ------------------------------------------------------------------ codebook
+
+
+def _params(d, bits, qjl_m, norm_correction, rot_seed, qjl_seed) -> tq_params:
+    return tq_params(int(d), int(bits), int(qjl_m), int(bool(norm_correction)),
+                     int(rot_seed), int(qjl_seed))
+
+
+def tq_codebook_values(d, bits, qjl_m=0, norm_correction=False, rot_seed=1, qjl_seed=2):
+    """Host-only float64 codebook values: dict(centroids, boundaries, rot, qjl)."""
+    L = 1 << int(bits)
+    c, t = np.zeros(L), np.zeros(L - 1)
+    r = np.zeros((d, d))
+    q = np.zeros((qjl_m, d)) if qjl_m > 0 else None
+    p = _params(d, bits, qjl_m, norm_correction, rot_seed, qjl_seed)
+    _check(lib().tq_codebook_values(ctypes.byref(p), _dptr(c), _dptr(t), _dptr(r), _dptr(q)))
+    return dict(centroids=c, boundaries=t, rot=r, qjl=q)
+
+
+class Codebook:
+    """Owns a tq_codebook (built on the current HIP device)."""
+
+    def __init__(self, d, bits, qjl_m=0, norm_correction=False, rot_seed=1, qjl_seed=2):
+        self.d, self.bits, self.m = int(d), int(bits), int(qjl_m)
+        self.nc = bool(norm_correction)
+        self.rot_seed, self.qjl_seed = int(rot_seed), int(qjl_seed)
+        self._h = ctypes.c_void_p()
+        p = _params(d, bits, qjl_m, norm_correction, rot_seed, qjl_seed)
+        _check(lib().tq_codebook_build(ctypes.byref(p), ctypes.byref(self._h)))
+
+    @property
+    def handle(self):
+        return self._h
+
+    def export(self):
+        L = 1 << self.bits
+        c, t = np.zeros(L), np.zeros(L - 1)
+        r = np.zeros((self.d, self.d))
+        q = np.zeros((self.m, self.d)) if self.m > 0 else None
+        _check(lib().tq_codebook_export(self._h, _dptr(c), _dptr(t), _dptr(r), _dptr(q)))
+        return dict(centroids=c, boundaries=t, rot=r, qjl=q)
+
+    def row_bytes(self):
+        a, b = ctypes.c_int64(), ctypes.c_int64()
+        _check(lib().tq_code_row_bytes(self._h, ctypes.byref(a), ctypes.byref(b)))
+        return a.value, b.value
+
+    def close(self):
+        if self._h:
+            lib().tq_codebook_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class Codes:
+    """Device code planes of one tensor (torch tensors) plus their layout."""
+
+    def __init__(self, cb: Codebook, n_seq: int, seq_stride: int, layout: int = TQ_LAYOUT_ROW,
+                 device="cuda"):
+        import torch
+        self.cb, self.n_seq, self.seq_stride, self.layout = cb, int(n_seq), int(seq_stride), int(layout)
+        n = self.n_seq * self.seq_stride
+        if layout == TQ_LAYOUT_ROW:
+            self.idx_row_bytes, self.sign_row_bytes = cb.row_bytes()
+            self.idx = torch.zeros(max(1, n * self.idx_row_bytes), dtype=torch.uint8, device=device)
+        else:
+            if seq_stride % 32:
+                raise ValueError("tile32 codes need seq_stride % 32 == 0")
+            self.idx_row_bytes, self.sign_row_bytes = 0, 0
+            self.idx = torch.zeros(max(1, self.n_seq * (self.seq_stride // 32) * cb.d * cb.bits * 4),
+                                   dtype=torch.uint8, device=device)
+        self.scale = torch.zeros(max(1, n), dtype=torch.float32, device=device)
+        if cb.m > 0:
+            if layout == TQ_LAYOUT_ROW:
+                self.sign = torch.zeros(max(1, n * self.sign_row_bytes), dtype=torch.uint8, device=device)
+            else:
+                self.sign = None
+            self.rnorm = torch.zeros(max(1, n), dtype=torch.float32, device=device)
+        else:
+            self.sign, self.rnorm = None, None
+
+    def descriptor(self) -> tq_codes:
+        return tq_codes(self.idx.data_ptr(),
+                        self.sign.data_ptr() if self.sign is not None else None,
+                        self.scale.data_ptr(),
+                        self.rnorm.data_ptr() if self.rnorm is not None else None,
+                        self.idx_row_bytes, self.sign_row_bytes, self.seq_stride, self.layout, 0)
+
+    def nbytes_per_vector(self) -> float:
+        b = self.cb.d * self.cb.bits / 8 + 4
+        if self.cb.m > 0:
+            b += self.cb.m / 8 + 4
+        return b
+
+
+# ------------------------------------------------------------------ calls
+
+
+def tq_quantize_kv(kcb, vcb, k, v, k_out: Codes | None, v_out: Codes | None,
+                   tok_offset: int = 0, stream=None):
+    """k, v: torch tensors [n_seq, n_tok, d] (contiguous, same dtype), or None."""
+    ref = k if k is not None else v
+    n_seq, n_tok = ref.shape[0], ref.shape[1]
+    for t in (k, v):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("inputs must be contiguous")
+    kd = k_out.descriptor() if k_out is not None else None
+    vd = v_out.descriptor() if v_out is not None else None
+    _check(lib().tq_quantize_kv(
+        kcb.handle if kcb is not None else None, vcb.handle if vcb is not None else None,
+        k.data_ptr() if k is not None else None, v.data_ptr() if v is not None else None,
+        _dtype_code(ref), n_seq, n_tok, int(tok_offset),
+        ctypes.byref(kd) if kd is not None else None, ctypes.byref(vd) if vd is not None else None,
+        _stream_handle(stream)))
+
+
+def tq_attn_decode_workspace(B, Hq, Hkv, n_ctx, d) -> int:
+    out = ctypes.c_size_t()
+    _check(lib().tq_attn_decode_workspace(int(B), int(Hq), int(Hkv), int(n_ctx), int(d),
+                                          ctypes.byref(out)))
+    return out.value
+
+
+def tq_attn_decode(kcb, vcb, q, k_codes: Codes, v_codes: Codes, n_ctx: int, sm_scale: float,
+                   seq_lens=None, out=None, logits=None, workspace=None, stream=None):
+    """q: [B, Hq, d] torch tensor.  Returns out (fp32 [B, Hq, d])."""
+    import torch
+    B, Hq, d = q.shape
+    Hkv = k_codes.n_seq // B
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        ws = tq_attn_decode_workspace(B, Hq, Hkv, n_ctx, d)
+        workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=q.device)
+    kd, vd = k_codes.descriptor(), v_codes.descriptor()
+    _check(lib().tq_attn_decode(
+        kcb.handle, vcb.handle, q.data_ptr(), _dtype_code(q), B, Hq, Hkv, ctypes.byref(kd),
+        ctypes.byref(vd), seq_lens.data_ptr() if seq_lens is not None else None, int(n_ctx),
+        float(sm_scale), out.data_ptr(), logits.data_ptr() if logits is not None else None,
+        workspace.data_ptr(), workspace.numel(), _stream_handle(stream)))
+    return out

@@ -1,0 +1,335 @@
+// C-ABI front end: argument validation, codebook upload, kernel dispatch.
+// Every exported function catches everything and reports through
+// tq_last_error(); no exception crosses the ABI.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "tq_internal.hpp"
+
+namespace tq {
+namespace {
+thread_local std::string g_err;
+
+uint16_t bf16_rne(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+float bf16_to_f(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+// c ~ hi + lo, both bf16
+void split_bf16(double c, uint16_t& hi, uint16_t& lo) {
+  hi = bf16_rne((float)c);
+  lo = bf16_rne((float)(c - (double)bf16_to_f(hi)));
+}
+
+tq_status fail(tq_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+tq_status hip_fail(hipError_t e, const char* what) {
+  return fail(TQ_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+void free_dev(DeviceCodebook& d) {
+  if (d.cent) (void)hipFree(d.cent);
+  if (d.bnd) (void)hipFree(d.bnd);
+  if (d.rot) (void)hipFree(d.rot);
+  if (d.qjl) (void)hipFree(d.qjl);
+  if (d.pair_tab) (void)hipFree(d.pair_tab);
+  d = DeviceCodebook{};
+}
+
+template <typename T>
+hipError_t upload(T** dst, const std::vector<T>& src) {
+  hipError_t e = hipMalloc((void**)dst, src.size() * sizeof(T));
+  if (e != hipSuccess) return e;
+  return hipMemcpy(*dst, src.data(), src.size() * sizeof(T), hipMemcpyHostToDevice);
+}
+
+tq_status check_params(const tq_params* p) {
+  if (!p) return fail(TQ_ERR_INVALID, "params is NULL");
+  if (p->d < 3 || p->d > 256) return fail(TQ_ERR_INVALID, "d must be in 3..256");
+  if (p->bits < 1 || p->bits > 8) return fail(TQ_ERR_INVALID, "bits must be in 1..8");
+  if (p->qjl_m < 0 || p->qjl_m > 256) return fail(TQ_ERR_INVALID, "qjl_m must be in 0..256");
+  if (p->norm_correction != 0 && p->norm_correction != 1)
+    return fail(TQ_ERR_INVALID, "norm_correction must be 0 or 1");
+  return TQ_OK;
+}
+
+tq_status check_codes(const tq_codebook* cb, const tq_codes* c, int64_t needed_len,
+                      const char* name, bool need_stride32) {
+  const std::string n(name);
+  if (!c) return fail(TQ_ERR_INVALID, n + ": codes descriptor is NULL");
+  if (!c->idx || !c->scale) return fail(TQ_ERR_INVALID, n + ": idx and scale must be non-NULL");
+  if (!aligned(c->idx, 4) || !aligned(c->scale, 16))
+    return fail(TQ_ERR_INVALID, n + ": idx must be 4-byte and scale 16-byte aligned");
+  const bool qjl = cb->p.qjl_m > 0;
+  if (qjl != (c->sign != nullptr) || qjl != (c->rnorm != nullptr))
+    return fail(TQ_ERR_INVALID, n + ": sign/rnorm must be non-NULL exactly when qjl_m > 0");
+  if (qjl && (!aligned(c->sign, 4) || !aligned(c->rnorm, 16)))
+    return fail(TQ_ERR_INVALID, n + ": sign must be 4-byte and rnorm 16-byte aligned");
+  if (c->seq_stride < needed_len || c->seq_stride < 0)
+    return fail(TQ_ERR_INVALID, n + ": seq_stride too small");
+  if (c->layout == TQ_LAYOUT_ROW) {
+    const int64_t min_idx = 4LL * cb->p.bits * ((cb->p.d + 31) / 32);
+    if (c->idx_row_bytes < min_idx || c->idx_row_bytes % 4)
+      return fail(TQ_ERR_INVALID, n + ": idx_row_bytes below minimum or not a multiple of 4");
+    if (qjl) {
+      const int64_t min_s = 4LL * ((cb->p.qjl_m + 31) / 32);
+      if (c->sign_row_bytes < min_s || c->sign_row_bytes % 4)
+        return fail(TQ_ERR_INVALID, n + ": sign_row_bytes below minimum or not a multiple of 4");
+    }
+    if (need_stride32 && c->seq_stride % 32)
+      return fail(TQ_ERR_INVALID, n + ": seq_stride must be a multiple of 32");
+  } else if (c->layout == TQ_LAYOUT_TILE32) {
+    if (c->seq_stride % 32) return fail(TQ_ERR_INVALID, n + ": tile32 seq_stride must be a multiple of 32");
+    if (qjl) return fail(TQ_ERR_UNSUPPORTED, n + ": QJL signs are not supported in the tile32 layout");
+  } else {
+    return fail(TQ_ERR_INVALID, n + ": unknown layout");
+  }
+  return TQ_OK;
+}
+
+tq_status current_device_matches(const tq_codebook* cb) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != cb->device) return fail(TQ_ERR_INVALID, "codebook was built on another device");
+  return TQ_OK;
+}
+
+}  // namespace
+
+void set_error(const std::string& msg) { g_err = msg; }
+
+bool quantize_supported(const tq_codebook* cb);
+
+}  // namespace tq
+
+using namespace tq;
+
+extern "C" {
+
+const char* tq_last_error(void) { return g_err.c_str(); }
+
+tq_status tq_codebook_build(const tq_params* params, tq_codebook** out) {
+  try {
+    if (!out) return fail(TQ_ERR_INVALID, "out is NULL");
+    *out = nullptr;
+    tq_status s = check_params(params);
+    if (s != TQ_OK) return s;
+    tq_codebook* cb = new (std::nothrow) tq_codebook();
+    if (!cb) return fail(TQ_ERR_ALLOC, "host allocation failed");
+    cb->p = *params;
+    cb->L = 1 << params->bits;
+    cb->dp = pad32(params->d);
+    cb->mp = params->qjl_m > 0 ? pad32(params->qjl_m) : 0;
+    std::string err;
+    if (!build_codebook_host(cb->p, cb->host, err)) {
+      delete cb;
+      return fail(TQ_ERR_NUMERIC, err);
+    }
+    hipError_t e = hipGetDevice(&cb->device);
+    if (e != hipSuccess) { delete cb; return hip_fail(e, "hipGetDevice"); }
+    const int d = cb->p.d, dp = cb->dp, L = cb->L, m = cb->p.qjl_m, mp = cb->mp;
+    std::vector<float> cent(L), bnd(L - 1), rot((size_t)dp * dp, 0.f);
+    for (int k = 0; k < L; ++k) cent[k] = (float)cb->host.centroids[k];
+    for (int k = 0; k < L - 1; ++k) bnd[k] = (float)cb->host.boundaries[k];
+    for (int i = 0; i < d; ++i)
+      for (int j = 0; j < d; ++j) rot[(size_t)i * dp + j] = (float)cb->host.rot[(size_t)i * d + j];
+    std::vector<uint32_t> tab;
+    if (cb->p.bits <= 4) {
+      const int b = cb->p.bits;
+      tab.resize((size_t)2 << (2 * b));
+      for (int x = 0; x < L; ++x)
+        for (int y = 0; y < L; ++y) {
+          uint16_t hx, lx, hy, ly;
+          split_bf16(cb->host.centroids[x], hx, lx);
+          split_bf16(cb->host.centroids[y], hy, ly);
+          const size_t e2 = (size_t)(x | (y << b));
+          tab[2 * e2 + 0] = (uint32_t)hx | ((uint32_t)hy << 16);
+          tab[2 * e2 + 1] = (uint32_t)lx | ((uint32_t)ly << 16);
+        }
+    } else {
+      tab.resize(L);
+      for (int x = 0; x < L; ++x) {
+        uint16_t hx, lx;
+        split_bf16(cb->host.centroids[x], hx, lx);
+        tab[x] = (uint32_t)hx | ((uint32_t)lx << 16);
+      }
+    }
+    cb->dev.pair_tab_dwords = (int)tab.size();
+    if ((e = upload(&cb->dev.cent, cent)) != hipSuccess ||
+        (e = upload(&cb->dev.bnd, bnd.empty() ? std::vector<float>{0.f} : bnd)) != hipSuccess ||
+        (e = upload(&cb->dev.rot, rot)) != hipSuccess ||
+        (e = upload(&cb->dev.pair_tab, tab)) != hipSuccess) {
+      free_dev(cb->dev);
+      delete cb;
+      return hip_fail(e, "codebook upload");
+    }
+    if (m > 0) {
+      std::vector<float> qjl((size_t)mp * dp, 0.f);
+      for (int j = 0; j < m; ++j)
+        for (int i = 0; i < d; ++i) qjl[(size_t)j * dp + i] = (float)cb->host.qjl[(size_t)j * d + i];
+      if ((e = upload(&cb->dev.qjl, qjl)) != hipSuccess) {
+        free_dev(cb->dev);
+        delete cb;
+        return hip_fail(e, "codebook upload");
+      }
+    }
+    *out = cb;
+    return TQ_OK;
+  } catch (const std::exception& ex) {
+    return fail(TQ_ERR_ALLOC, std::string("tq_codebook_build: ") + ex.what());
+  } catch (...) {
+    return fail(TQ_ERR_ALLOC, "tq_codebook_build: unknown exception");
+  }
+}
+
+tq_status tq_codebook_values(const tq_params* params, double* centroids, double* boundaries,
+                             double* rot, double* qjl) {
+  try {
+    tq_status s = check_params(params);
+    if (s != TQ_OK) return s;
+    HostCodebook hc;
+    std::string err;
+    if (!build_codebook_host(*params, hc, err)) return fail(TQ_ERR_NUMERIC, err);
+    if (centroids) std::memcpy(centroids, hc.centroids.data(), hc.centroids.size() * sizeof(double));
+    if (boundaries) std::memcpy(boundaries, hc.boundaries.data(), hc.boundaries.size() * sizeof(double));
+    if (rot) std::memcpy(rot, hc.rot.data(), hc.rot.size() * sizeof(double));
+    if (qjl && !hc.qjl.empty()) std::memcpy(qjl, hc.qjl.data(), hc.qjl.size() * sizeof(double));
+    return TQ_OK;
+  } catch (...) {
+    return fail(TQ_ERR_ALLOC, "tq_codebook_values: unexpected exception");
+  }
+}
+
+tq_status tq_codebook_destroy(tq_codebook* cb) {
+  if (!cb) return TQ_OK;
+  free_dev(cb->dev);
+  delete cb;
+  return TQ_OK;
+}
+
+tq_status tq_codebook_export(const tq_codebook* cb, double* centroids, double* boundaries,
+                             double* rot, double* qjl) {
+  if (!cb) return fail(TQ_ERR_INVALID, "codebook is NULL");
+  if (centroids) std::memcpy(centroids, cb->host.centroids.data(), cb->L * sizeof(double));
+  if (boundaries)
+    std::memcpy(boundaries, cb->host.boundaries.data(), (cb->L - 1) * sizeof(double));
+  if (rot) std::memcpy(rot, cb->host.rot.data(), cb->host.rot.size() * sizeof(double));
+  if (qjl && !cb->host.qjl.empty())
+    std::memcpy(qjl, cb->host.qjl.data(), cb->host.qjl.size() * sizeof(double));
+  return TQ_OK;
+}
+
+tq_status tq_code_row_bytes(const tq_codebook* cb, int64_t* idx_row_bytes,
+                            int64_t* sign_row_bytes) {
+  if (!cb) return fail(TQ_ERR_INVALID, "codebook is NULL");
+  if (idx_row_bytes) *idx_row_bytes = 4LL * cb->p.bits * ((cb->p.d + 31) / 32);
+  if (sign_row_bytes) *sign_row_bytes = cb->p.qjl_m > 0 ? 4LL * ((cb->p.qjl_m + 31) / 32) : 0;
+  return TQ_OK;
+}
+
+tq_status tq_quantize_kv(const tq_codebook* kcb, const tq_codebook* vcb, const void* k,
+                         const void* v, tq_dtype dt, int64_t n_seq, int64_t n_tok,
+                         int64_t tok_offset, const tq_codes* k_out, const tq_codes* v_out,
+                         void* stream) {
+  try {
+    if (dt != TQ_F32 && dt != TQ_BF16 && dt != TQ_F16) return fail(TQ_ERR_INVALID, "bad dtype");
+    if (n_seq < 0 || n_tok < 0 || tok_offset < 0)
+      return fail(TQ_ERR_INVALID, "n_seq, n_tok and tok_offset must be >= 0");
+    if (n_seq == 0 || n_tok == 0) return TQ_OK;   // nothing is read or written
+    if (!k && !v) return fail(TQ_ERR_INVALID, "k and v are both NULL");
+    const void* xs[2] = {k, v};
+    const tq_codebook* cbs[2] = {kcb, vcb};
+    const tq_codes* outs[2] = {k_out, v_out};
+    const char* names[2] = {"k", "v"};
+    for (int t = 0; t < 2; ++t) {
+      if (!xs[t]) continue;
+      if (!cbs[t]) return fail(TQ_ERR_INVALID, std::string(names[t]) + ": codebook is NULL");
+      tq_status s = check_codes(cbs[t], outs[t], tok_offset + n_tok, names[t], false);
+      if (s != TQ_OK) return s;
+      if (!quantize_supported(cbs[t]))
+        return fail(TQ_ERR_UNSUPPORTED, std::string(names[t]) + ": quantize supports d <= 128 and qjl_m <= 128");
+      s = current_device_matches(cbs[t]);
+      if (s != TQ_OK) return s;
+    }
+    for (int t = 0; t < 2; ++t) {
+      if (!xs[t]) continue;
+      QuantJob job{xs[t], dt, n_seq, n_tok, tok_offset, *outs[t]};
+      hipError_t e = launch_quantize(cbs[t], job, static_cast<hipStream_t>(stream));
+      if (e != hipSuccess) return hip_fail(e, "quantize launch");
+    }
+    return TQ_OK;
+  } catch (...) {
+    return fail(TQ_ERR_ALLOC, "tq_quantize_kv: unexpected exception");
+  }
+}
+
+tq_status tq_attn_decode_workspace(int64_t B, int64_t Hq, int64_t Hkv, int64_t n_ctx,
+                                   int32_t d, size_t* bytes) {
+  if (!bytes) return fail(TQ_ERR_INVALID, "bytes is NULL");
+  if (B < 0 || Hq < 0 || Hkv <= 0 || n_ctx < 0 || Hq % Hkv)
+    return fail(TQ_ERR_INVALID, "need B, n_ctx >= 0, Hkv > 0, Hq a multiple of Hkv");
+  if (d != 128) return fail(TQ_ERR_UNSUPPORTED, "decode supports d = 128");
+  *bytes = plan_decode(B, Hq, Hkv, n_ctx, d).bytes;
+  return TQ_OK;
+}
+
+tq_status tq_attn_decode(const tq_codebook* kcb, const tq_codebook* vcb, const void* q,
+                         tq_dtype qdt, int64_t B, int64_t Hq, int64_t Hkv, const tq_codes* k,
+                         const tq_codes* v, const int32_t* seq_lens, int64_t n_ctx,
+                         float sm_scale, float* out, float* logits, void* workspace,
+                         size_t ws_bytes, void* stream) {
+  try {
+    if (!kcb || !vcb) return fail(TQ_ERR_INVALID, "codebook is NULL");
+    if (qdt != TQ_F32 && qdt != TQ_BF16 && qdt != TQ_F16) return fail(TQ_ERR_INVALID, "bad dtype");
+    if (B < 0 || Hq < 0 || Hkv <= 0 || n_ctx < 0 || Hq % Hkv)
+      return fail(TQ_ERR_INVALID, "need B, n_ctx >= 0, Hkv > 0, Hq a multiple of Hkv");
+    if (kcb->p.d != vcb->p.d) return fail(TQ_ERR_INVALID, "key and value codebooks differ in d");
+    if (!decode_supported(kcb, vcb))
+      return fail(TQ_ERR_UNSUPPORTED,
+                  "decode supports d = 128, bits in {2,3,4,8}, qjl_m <= 128");
+    if (!std::isfinite(sm_scale)) return fail(TQ_ERR_INVALID, "sm_scale must be finite");
+    if (B * Hq == 0) return TQ_OK;
+    if (!q || !out) return fail(TQ_ERR_INVALID, "q and out must be non-NULL");
+    if (!k || k->layout != TQ_LAYOUT_ROW) return fail(TQ_ERR_INVALID, "key codes must use the row layout");
+    if (!v || v->layout != TQ_LAYOUT_TILE32)
+      return fail(TQ_ERR_INVALID, "value codes must use the tile32 layout");
+    tq_status s = check_codes(kcb, k, n_ctx, "k", true);
+    if (s != TQ_OK) return s;
+    s = check_codes(vcb, v, n_ctx, "v", true);
+    if (s != TQ_OK) return s;
+    if ((s = current_device_matches(kcb)) != TQ_OK) return s;
+    if ((s = current_device_matches(vcb)) != TQ_OK) return s;
+    const DecodePlan plan = plan_decode(B, Hq, Hkv, n_ctx, kcb->p.d);
+    if (plan.rows > 65535 || B * Hq > 0x7FFFFFFF)
+      return fail(TQ_ERR_UNSUPPORTED, "B * Hkv * ceil(g/8) must be <= 65535");
+    if (!workspace || ws_bytes < plan.bytes)
+      return fail(TQ_ERR_INVALID, "workspace missing or smaller than tq_attn_decode_workspace()");
+    if (!aligned(workspace, 256)) return fail(TQ_ERR_INVALID, "workspace must be 256-byte aligned");
+    if (!aligned(out, 16)) return fail(TQ_ERR_INVALID, "out must be 16-byte aligned");
+    hipError_t e = launch_decode(kcb, vcb, q, qdt, plan, *k, *v, seq_lens, sm_scale, out,
+                                 logits, workspace, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+    return TQ_OK;
+  } catch (...) {
+    return fail(TQ_ERR_ALLOC, "tq_attn_decode: unexpected exception");
+  }
+}
+
+}  // extern "C"

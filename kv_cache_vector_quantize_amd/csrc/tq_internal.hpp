@@ -1,0 +1,86 @@
+// Internal declarations shared by the C-ABI front end and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "tq.h"
+
+namespace tq {
+
+// float64 results of the host-side construction
+struct HostCodebook {
+  std::vector<double> centroids;   // [L]
+  std::vector<double> boundaries;  // [L-1]
+  std::vector<double> rot;         // [d*d] row-major Pi
+  std::vector<double> qjl;         // [m*d] row-major S (empty when m == 0)
+};
+
+bool build_codebook_host(const tq_params& p, HostCodebook& out, std::string& err);
+
+// Device-resident tables of one codebook.
+struct DeviceCodebook {
+  float* cent = nullptr;    // [L] fp32
+  float* bnd = nullptr;     // [L-1] fp32
+  float* rot = nullptr;     // [dp*dp] fp32 row-major Pi, zero-padded to dp
+  float* qjl = nullptr;     // [mp*dp] fp32 row-major S, zero-padded (or null)
+  // decode operand tables (bf16 hi/lo split of the centroids):
+  //  bits <= 4: entry e = a | (b << bits) holds two dwords
+  //             {hi(c[a]) | hi(c[b]) << 16, lo(c[a]) | lo(c[b]) << 16}
+  //  bits  > 4: entry a holds one dword {hi(c[a]) | lo(c[a]) << 16}
+  uint32_t* pair_tab = nullptr;
+  int pair_tab_dwords = 0;
+};
+
+// padded sizes used by the kernels
+inline int pad32(int x) { return (x + 31) / 32 * 32; }
+
+}  // namespace tq
+
+struct tq_codebook {
+  tq_params p;
+  int L = 0, dp = 0, mp = 0;
+  int device = 0;
+  tq::HostCodebook host;
+  tq::DeviceCodebook dev;
+};
+
+namespace tq {
+
+void set_error(const std::string& msg);
+
+// ---- kernels (launchers return hipSuccess or the launch error)
+
+struct QuantJob {
+  const void* x;          // [n_seq][n_tok][d]
+  tq_dtype dt;
+  int64_t n_seq, n_tok, tok_offset;
+  tq_codes out;
+};
+
+hipError_t launch_quantize(const tq_codebook* cb, const QuantJob& job, hipStream_t stream);
+
+struct DecodePlan {
+  int64_t B, Hq, Hkv, n_ctx;
+  int d;
+  int g;            // Hq / Hkv
+  int qgroups;      // ceil(g / 8)
+  int64_t rows;     // B * Hkv * qgroups (one row = one KV head and <= 8 query heads)
+  int chunk;        // tokens per wave (multiple of 32)
+  int n_parts;      // waves per row = ceil(n_ctx / chunk)
+  size_t off_qop, off_part_o, off_part_ml, bytes;
+};
+
+DecodePlan plan_decode(int64_t B, int64_t Hq, int64_t Hkv, int64_t n_ctx, int d);
+
+hipError_t launch_decode(const tq_codebook* kcb, const tq_codebook* vcb, const void* q,
+                         tq_dtype qdt, const DecodePlan& plan, const tq_codes& k,
+                         const tq_codes& v, const int32_t* seq_lens, float sm_scale,
+                         float* out, float* logits, void* ws, hipStream_t stream);
+
+bool decode_supported(const tq_codebook* kcb, const tq_codebook* vcb);
+
+}  // namespace tq

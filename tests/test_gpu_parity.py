@@ -1,0 +1,288 @@
+"""GPU parity: libtq.so (HIP kernels via the C ABI) against the CPU oracle.
+
+Tolerances are those in tq_testutil.  Inputs come from ``synth`` (seeded);
+the oracle reads the very tensors the GPU quantized.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+import kv_cache_vector_quantize_amd as tq
+from kv_cache_vector_quantize_amd import TQ_LAYOUT_ROW, TQ_LAYOUT_TILE32
+
+import tq_testutil as U
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    tq.lib()
+    return "cuda"
+
+
+# ----------------------------------------------------------------- codebook
+
+
+def test_device_codebook_export_matches_oracle(dev):
+    _say("codebook export d=128 b=3 m=128")
+    cb = tq.Codebook(128, 3, qjl_m=128)
+    ex = cb.export()
+    ref = O.Codebook(128, 3, qjl_m=128)
+    assert np.max(np.abs(ex["centroids"] - ref.centroids)) < 1e-10
+    assert np.max(np.abs(ex["rot"] - ref.rot)) < 1e-12
+    assert cb.row_bytes() == (48, 16)
+
+
+# ----------------------------------------------------------------- quantize
+
+
+def _quant_case(dev, d, bits, m, nc, dtype, n_seq, n_tok, tok_offset=0, layout=TQ_LAYOUT_ROW,
+                seed=0, stride=None, factor=20.0):
+    cb = tq.Codebook(d, bits, qjl_m=m, norm_correction=nc, rot_seed=3, qjl_seed=4)
+    S = stride or ((tok_offset + n_tok + 31) // 32 * 32)
+    codes = tq.Codes(cb, n_seq, S, layout)
+    x = synth.kv_gaussian(1, n_seq, n_tok, d, seed, dtype=dtype, device="cpu",
+                          channels=[i for i in (3, 77, 101) if i < d], factor=factor)[0]
+    xg = x.to(dev).contiguous()
+    tq.tq_quantize_kv(cb, None, xg, None, codes, None, tok_offset=tok_offset)
+    torch.cuda.synchronize()
+    return cb, codes, x
+
+
+@pytest.mark.parametrize("d,bits,m,nc,dtype", [
+    (128, 3, 128, False, "f32"),   # keys of the tiny configuration
+    (128, 4, 0, False, "f32"),     # values of the tiny configuration
+    (128, 4, 0, False, "bf16"),
+    (128, 2, 0, True, "bf16"),
+    (128, 8, 0, False, "bf16"),
+    (128, 1, 64, False, "f16"),
+    (96, 3, 96, True, "bf16"),
+    (64, 4, 32, False, "f32"),
+    (40, 5, 40, False, "f32"),
+    (5, 2, 3, False, "f32"),
+])
+def test_quantize_rows_parity(dev, d, bits, m, nc, dtype):
+    n_seq, n_tok = 3, 333
+    _say("quantize rows", d, bits, m, nc, dtype)
+    cb, codes, x = _quant_case(dev, d, bits, m, nc, dtype, n_seq, n_tok, seed=d + bits)
+    got = U.read_codes(codes, n_tok)
+    ocb = U.oracle_codebook(cb)
+    x64 = x.float().numpy().astype(np.float64).reshape(-1, d)
+    flat = dict(idx=got["idx"].reshape(-1, d), scale=got["scale"].reshape(-1),
+                sign=None if got["sign"] is None else got["sign"].reshape(-1, m),
+                rnorm=None if got["rnorm"] is None else got["rnorm"].reshape(-1))
+    st = U.compare_quant(ocb, x64, flat, name=f"d{d}b{bits}m{m}")
+    # packed format: the GPU's rows equal the oracle's packing of the same
+    # indices byte for byte (padding bits zero)
+    for s in range(n_seq):
+        rows = U.raw_rows(codes, s, n_tok)
+        assert np.array_equal(rows, O.pack_rows(got["idx"][s], bits, codes.idx_row_bytes))
+        if m:
+            sg = codes.sign.cpu().numpy()[s * codes.seq_stride * codes.sign_row_bytes:
+                                          (s * codes.seq_stride + n_tok) * codes.sign_row_bytes]
+            assert np.array_equal(sg.reshape(n_tok, -1), O.pack_signs(got["sign"][s], codes.sign_row_bytes))
+    print(st)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+def test_quantize_tile32_parity_and_append(dev, bits):
+    """Values in the tile32 layout, written in three appends at unaligned
+    offsets (read-modify-write of shared blocks)."""
+    d, n_seq, total = 128, 2, 230
+    _say("quantize tile32 append", bits)
+    cb = tq.Codebook(d, bits, rot_seed=5)
+    codes = tq.Codes(cb, n_seq, 256, TQ_LAYOUT_TILE32)
+    x = synth.kv_gaussian(1, n_seq, total, d, 11, dtype="bf16", device="cpu", channels=[3], factor=20.0)[0]
+    for a, b in [(0, 45), (45, 46), (46, 230)]:
+        tq.tq_quantize_kv(None, cb, None, x[:, a:b].contiguous().to(dev), None, codes, tok_offset=a)
+    torch.cuda.synchronize()
+    got = U.read_codes(codes, total)
+    ocb = U.oracle_codebook(cb)
+    x64 = x.float().numpy().astype(np.float64).reshape(-1, d)
+    flat = dict(idx=got["idx"].reshape(-1, d), scale=got["scale"].reshape(-1), sign=None, rnorm=None)
+    U.compare_quant(ocb, x64, flat, name=f"tile32 b{bits}")
+    # positions >= total keep zero bits and zero scale
+    raw = O.unpack_tile32(codes.idx.cpu().numpy().reshape(n_seq, 8, d, 4 * bits)[0], d, bits, 256)
+    assert np.all(raw[total:] == 0)
+    assert np.all(codes.scale.cpu().numpy()[total:256] == 0)
+    # byte-exact against the oracle's packing of the GPU's indices
+    blocks = codes.idx.cpu().numpy().reshape(n_seq, 8, d, 4 * bits)
+    for s in range(n_seq):
+        assert np.array_equal(blocks[s], O.pack_tile32(got["idx"][s], bits, 8))
+
+
+def test_quantize_rows_offset_and_untouched(dev):
+    d, bits = 128, 4
+    _say("quantize rows with offset")
+    cb = tq.Codebook(d, bits)
+    codes = tq.Codes(cb, 2, 128, TQ_LAYOUT_ROW)
+    codes.scale.fill_(-7.0)
+    x = synth.kv_gaussian(1, 2, 50, d, 3, dtype="f32", device="cpu")[0]
+    tq.tq_quantize_kv(cb, None, x.to(dev), None, codes, None, tok_offset=37)
+    torch.cuda.synchronize()
+    sc = codes.scale.cpu().numpy().reshape(2, 128)
+    assert np.all(sc[:, :37] == -7.0) and np.all(sc[:, 87:] == -7.0)
+    got = U.read_codes(codes, 87)
+    ocb = U.oracle_codebook(cb)
+    flat = dict(idx=got["idx"][:, 37:].reshape(-1, d), scale=got["scale"][:, 37:].reshape(-1),
+                sign=None, rnorm=None)
+    U.compare_quant(ocb, x.numpy().astype(np.float64).reshape(-1, d), flat)
+
+
+def test_quantize_zero_vectors_and_empty(dev):
+    _say("quantize zero vectors / empty")
+    cb = tq.Codebook(128, 3, qjl_m=128)
+    codes = tq.Codes(cb, 1, 32)
+    x = torch.zeros((1, 32, 128), dtype=torch.float32, device=dev)
+    tq.tq_quantize_kv(cb, None, x, None, codes, None)
+    tq.tq_quantize_kv(cb, None, x[:, :0], None, codes, None)
+    torch.cuda.synchronize()
+    got = U.read_codes(codes, 32)
+    assert np.all(got["idx"] == 4) and np.all(got["scale"] == 0) and np.all(got["rnorm"] == 0)
+    ref = O.quantize(U.oracle_codebook(cb), np.zeros((32, 128)))
+    assert np.array_equal(got["sign"][0], ref["sign"])
+
+
+def test_quantize_argument_errors(dev):
+    cb = tq.Codebook(128, 3, qjl_m=128)
+    codes = tq.Codes(cb, 1, 32)
+    x = torch.zeros((1, 40, 128), dtype=torch.float32, device=dev)
+    with pytest.raises(tq.TQError):          # beyond seq_stride
+        tq.tq_quantize_kv(cb, None, x, None, codes, None)
+    big = tq.Codebook(200, 4)
+    bc = tq.Codes(big, 1, 32)
+    with pytest.raises(tq.TQError) as e:
+        tq.tq_quantize_kv(big, None, torch.zeros((1, 4, 200), device=dev), None, bc, None)
+    assert e.value.status == 2
+
+
+# ----------------------------------------------------------------- decode
+
+
+def _decode_case(dev, B, Hkv, Hq, N, kb, km, knc, vb, vnc, qdtype="bf16", kvdtype="bf16",
+                 seq_lens=None, seed=0):
+    kcb = tq.Codebook(128, kb, qjl_m=km, norm_correction=knc, rot_seed=1, qjl_seed=2)
+    vcb = tq.Codebook(128, vb, norm_correction=vnc, rot_seed=3)
+    S = (N + 31) // 32 * 32
+    kc = tq.Codes(kcb, B * Hkv, S, TQ_LAYOUT_ROW)
+    vc = tq.Codes(vcb, B * Hkv, S, TQ_LAYOUT_TILE32)
+    k = synth.kv_gaussian(B, Hkv, N, 128, seed, dtype=kvdtype, device=dev, channels=[3, 77, 101], factor=20.0)
+    v = synth.kv_gaussian(B, Hkv, N, 128, seed + 1, dtype=kvdtype, device=dev, channels=[3, 77, 101], factor=20.0)
+    q = synth.queries_gaussian(B, Hq, 128, seed + 2, dtype=qdtype, device=dev)
+    tq.tq_quantize_kv(kcb, vcb, k.reshape(B * Hkv, N, 128), v.reshape(B * Hkv, N, 128), kc, vc)
+    logits = torch.full((B, Hq, N), 123.0, dtype=torch.float32, device=dev)
+    sl = None
+    if seq_lens is not None:
+        sl = torch.tensor(seq_lens, dtype=torch.int32, device=dev)
+    tau = 1.0 / math.sqrt(128)
+    out = tq.tq_attn_decode(kcb, vcb, q, kc, vc, N, tau, seq_lens=sl, logits=logits)
+    torch.cuda.synchronize()
+    return kcb, vcb, kc, vc, q, k, v, logits, out, tau
+
+
+def _cache_dicts(kc, vc, B, Hkv, N):
+    gk = U.read_codes(kc, N)
+    gv = U.read_codes(vc, N)
+    kd = dict(idx=gk["idx"].reshape(B, Hkv, N, -1), scale=gk["scale"].reshape(B, Hkv, N))
+    if gk["sign"] is not None:
+        kd["sign"] = gk["sign"].reshape(B, Hkv, N, -1)
+        kd["rnorm"] = gk["rnorm"].reshape(B, Hkv, N)
+    vd = dict(idx=gv["idx"].reshape(B, Hkv, N, -1), scale=gv["scale"].reshape(B, Hkv, N))
+    return kd, vd
+
+
+def test_decode_tiny_configuration(dev):
+    """1 KV head, 8 queries, d = 128, N = 4096, fp32 inputs with outlier
+    channels 3/77/101 x20; keys 3-bit + QJL m=128, values 4-bit."""
+    _say("decode tiny configuration")
+    k, v, q = synth.tiny_case(0)
+    N = 4096
+    kcb = tq.Codebook(128, 3, qjl_m=128)
+    vcb = tq.Codebook(128, 4, rot_seed=3)
+    kc = tq.Codes(kcb, 1, N, TQ_LAYOUT_ROW)
+    vc = tq.Codes(vcb, 1, N, TQ_LAYOUT_TILE32)
+    kg, vg = torch.from_numpy(k)[None].to(dev), torch.from_numpy(v)[None].to(dev)
+    tq.tq_quantize_kv(kcb, vcb, kg, vg, kc, vc)
+    qg = torch.from_numpy(q)[None].to(dev)
+    logits = torch.empty((1, 8, N), dtype=torch.float32, device=dev)
+    tau = 1 / math.sqrt(128)
+    out = tq.tq_attn_decode(kcb, vcb, qg, kc, vc, N, tau, logits=logits)
+    torch.cuda.synchronize()
+    okc, ovc = U.oracle_codebook(kcb), U.oracle_codebook(vcb)
+    # codes parity
+    gk, gv = U.read_codes(kc, N), U.read_codes(vc, N)
+    st_k = U.compare_quant(okc, k.astype(np.float64),
+                           dict(idx=gk["idx"][0], scale=gk["scale"][0], sign=gk["sign"][0], rnorm=gk["rnorm"][0]), "K")
+    st_v = U.compare_quant(ovc, v.astype(np.float64),
+                           dict(idx=gv["idx"][0], scale=gv["scale"][0], sign=None, rnorm=None), "V")
+    kd, vd = _cache_dicts(kc, vc, 1, 1, N)
+    st = U.check_decode(okc, ovc, q[None].astype(np.float64), kd, vd, tau,
+                        logits.cpu().numpy(), out.cpu().numpy(), name="tiny")
+    # end to end: the oracle's own codes (reported; same bar)
+    rk, rv = O.quantize(okc, k.astype(np.float64)), O.quantize(ovc, v.astype(np.float64))
+    kd_o = {n: rk[n][None, None] for n in ("idx", "scale", "sign", "rnorm")}
+    vd_o = {n: rv[n][None, None] for n in ("idx", "scale")}
+    _, out_e2e = O.attn_decode(okc, ovc, q[None].astype(np.float64), kd_o, vd_o, tau)
+    e2e = float(np.max(np.abs(out.cpu().numpy() - out_e2e)))
+    print(st_k, st_v, st, "end-to-end out max-abs", e2e)
+    assert e2e <= U.OUT_ATOL
+
+
+@pytest.mark.parametrize("B,Hkv,Hq,N,lens", [
+    (2, 2, 16, 1000, None),          # ragged tail, two KV heads
+    (3, 1, 8, 700, [700, 333, 0]),   # per-sequence lengths incl. empty
+    (1, 2, 4, 96, None),             # g = 2 (<8 queries per KV head)
+    (1, 2, 24, 160, [150]),          # g = 12: two query groups
+    (1, 1, 8, 1, None),              # one token
+])
+def test_decode_shapes(dev, B, Hkv, Hq, N, lens):
+    _say("decode shapes", B, Hkv, Hq, N, lens)
+    kcb, vcb, kc, vc, q, k, v, logits, out, tau = _decode_case(dev, B, Hkv, Hq, N, 3, 128, False, 4, False,
+                                                                seq_lens=lens, seed=N)
+    kd, vd = _cache_dicts(kc, vc, B, Hkv, N)
+    st = U.check_decode(U.oracle_codebook(kcb), U.oracle_codebook(vcb), U.to_f64(q), kd, vd, tau,
+                        logits.cpu().numpy(), out.cpu().numpy(), n_valid=lens, name="shapes")
+    if lens is not None and 0 in lens:
+        b0 = lens.index(0)
+        assert torch.all(out[b0] == 0)
+    print(st)
+
+
+@pytest.mark.parametrize("kb,vb,nc", [(8, 4, False), (4, 4, True), (3, 4, True), (3, 3, True),
+                                      (2, 2, True), (2, 2, False), (4, 8, False), (2, 3, False)])
+def test_decode_bit_variants(dev, kb, vb, nc):
+    _say("decode variant", kb, vb, nc)
+    B, Hkv, Hq, N = 2, 2, 16, 512
+    kcb, vcb, kc, vc, q, k, v, logits, out, tau = _decode_case(dev, B, Hkv, Hq, N, kb, 0, nc, vb, nc, seed=kb * 10 + vb)
+    kd, vd = _cache_dicts(kc, vc, B, Hkv, N)
+    st = U.check_decode(U.oracle_codebook(kcb), U.oracle_codebook(vcb), U.to_f64(q), kd, vd, tau,
+                        logits.cpu().numpy(), out.cpu().numpy(), name=f"k{kb}v{vb}")
+    print(st)
+
+
+def test_decode_qjl_smaller_m(dev):
+    _say("decode QJL m=64")
+    B, Hkv, Hq, N = 1, 1, 8, 256
+    kcb, vcb, kc, vc, q, k, v, logits, out, tau = _decode_case(dev, B, Hkv, Hq, N, 3, 64, False, 4, False, qdtype="f32")
+    kd, vd = _cache_dicts(kc, vc, B, Hkv, N)
+    U.check_decode(U.oracle_codebook(kcb), U.oracle_codebook(vcb), U.to_f64(q), kd, vd, tau,
+                   logits.cpu().numpy(), out.cpu().numpy(), name="m64")
+
+
+def test_decode_deterministic(dev):
+    _say("decode determinism")
+    r1 = _decode_case(dev, 2, 2, 16, 2048, 3, 128, False, 4, False, seed=5)
+    r2 = _decode_case(dev, 2, 2, 16, 2048, 3, 128, False, 4, False, seed=5)
+    assert torch.equal(r1[8], r2[8]) and torch.equal(r1[7], r2[7])
+    assert torch.equal(r1[2].idx, r2[2].idx) and torch.equal(r1[3].idx, r2[3].idx)

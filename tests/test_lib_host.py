@@ -1,0 +1,92 @@
+"""Host-side checks of libtq.so that need no GPU: exports, the library's own
+codebook construction against the oracle's independent one, and argument
+validation that fails before any device call."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+import kv_cache_vector_quantize_amd as tq
+from kv_cache_vector_quantize_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    txt = open(os.path.join(ROOT, "include", "tq.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(tq_[a-z_]+)\s*\(", txt)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = tq.lib()
+    decl = _declared()
+    assert set(decl) == set(tq.EXPORTS)
+    for name in decl:
+        assert hasattr(L, name), name
+
+
+@pytest.mark.parametrize("d,bits,m", [(3, 2, 0), (8, 3, 8), (64, 4, 16), (128, 1, 0), (128, 2, 0),
+                                      (128, 3, 128), (128, 4, 0), (200, 4, 200), (128, 8, 0)])
+def test_host_codebook_matches_oracle(d, bits, m):
+    lib_v = tq.tq_codebook_values(d, bits, m, rot_seed=1, qjl_seed=2)
+    ref = O.Codebook(d, bits, qjl_m=m, rot_seed=1, qjl_seed=2)
+    # the 256-level fixed point amplifies fp64 residuals ~1e4x, so two
+    # independent solvers agree to ~1e-11 there; fp32 storage needs ~1e-8
+    assert np.max(np.abs(lib_v["centroids"] - ref.centroids)) < 1e-10
+    assert np.max(np.abs(lib_v["boundaries"] - ref.boundaries)) < 1e-10
+    # Householder (library) vs Gram-Schmidt (oracle): same Q by uniqueness
+    assert np.max(np.abs(lib_v["rot"] - ref.rot)) < 1e-12
+    if m:
+        assert np.max(np.abs(lib_v["qjl"] - ref.qjl)) < 1e-13
+
+
+def test_host_codebook_seeds_and_nc():
+    a = tq.tq_codebook_values(16, 3, 8, norm_correction=True, rot_seed=7, qjl_seed=9)
+    ref = O.Codebook(16, 3, qjl_m=8, nc=True, rot_seed=7, qjl_seed=9)
+    assert np.max(np.abs(a["rot"] - ref.rot)) < 1e-12
+    assert np.max(np.abs(a["qjl"] - ref.qjl)) < 1e-13
+
+
+@pytest.mark.parametrize("kw", [dict(d=2, bits=3), dict(d=300, bits=3), dict(d=16, bits=0),
+                                dict(d=16, bits=9), dict(d=16, bits=3, qjl_m=-1),
+                                dict(d=16, bits=3, qjl_m=257)])
+def test_invalid_params_rejected(kw):
+    with pytest.raises(tq.TQError) as e:
+        tq.tq_codebook_values(**kw)
+    assert e.value.status == _lib.TQ_ERR_INVALID
+
+
+def test_norm_correction_flag_validated():
+    p = _lib.tq_params(16, 3, 0, 2, 1, 2)
+    st = tq.lib().tq_codebook_values(ctypes.byref(p), None, None, None, None)
+    assert st == _lib.TQ_ERR_INVALID
+    assert b"norm_correction" in tq.lib().tq_last_error()
+
+
+def test_decode_workspace_validation():
+    assert tq.tq_attn_decode_workspace(8, 64, 8, 131072, 128) > 0
+    assert tq.tq_attn_decode_workspace(1, 8, 1, 0, 128) > 0
+    with pytest.raises(tq.TQError):
+        tq.tq_attn_decode_workspace(1, 7, 2, 100, 128)       # Hq not a multiple of Hkv
+    with pytest.raises(tq.TQError) as e:
+        tq.tq_attn_decode_workspace(1, 8, 1, 100, 64)
+    assert e.value.status == _lib.TQ_ERR_UNSUPPORTED
+
+
+def test_quantize_rejects_null_inputs_before_device():
+    L = tq.lib()
+    st = L.tq_quantize_kv(None, None, None, None, 0, 1, 1, 0, None, None, None)
+    assert st == _lib.TQ_ERR_INVALID
+    st = L.tq_quantize_kv(None, None, None, None, 7, 1, 1, 0, None, None, None)
+    assert st == _lib.TQ_ERR_INVALID and b"dtype" in L.tq_last_error()
+
+
+def test_decode_rejects_null_codebooks():
+    L = tq.lib()
+    st = L.tq_attn_decode(None, None, None, 0, 1, 8, 1, None, None, None, 16, 0.1, None, None,
+                          None, 0, None)
+    assert st == _lib.TQ_ERR_INVALID
