@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Benchmark of the hot path on one MI355X.
+
+A step is one serving-style pass over the 128K-context decode layer
+(B=8, 64 query heads, 8 KV heads, d=128, context 131072; keys 3-bit + 1-bit
+QJL m=128, values 4-bit): quantize the step's new key/value vector of every
+sequence into the compressed cache (position ctx-1), then decode attention
+for all 512 query heads straight from the packed codes.  Inputs and the
+compressed cache are resident in HBM before the timed region.
+
+Printed: ONE JSON line with the contract fields plus
+* roofline of the dominant kernel (the decode split kernel), from HIP events
+  recorded on its stream around every launch in the timed region;
+* quantize: tq_quantize_kv bandwidth on the quantize-only layer
+  (B=16, 8 KV heads, d=128, 32768 tokens, bf16 K and V, 4-bit, no QJL);
+* cpu_baseline: the float64 CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "KV tokens/s in compressed decode attention & quantize GB/s, % of HBM peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-quantize", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (HBM counter calibration)")
+    return ap.parse_args()
+
+
+def decode_workload(torch, tq, synth, dev):
+    B, Hq, Hkv, d, N = 8, 64, 8, 128, 131072
+    kcb = tq.Codebook(d, 3, qjl_m=128, rot_seed=1, qjl_seed=2)
+    vcb = tq.Codebook(d, 4, rot_seed=3)
+    k = synth.kv_gaussian(B, Hkv, N, d, 0, dtype="bf16", device=dev, channels=[3, 77, 101], factor=20.0)
+    v = synth.kv_gaussian(B, Hkv, N, d, 1, dtype="bf16", device=dev, channels=[3, 77, 101], factor=20.0)
+    q = synth.queries_gaussian(B, Hq, d, 2, dtype="bf16", device=dev)
+    kc = tq.Codes(kcb, B * Hkv, N, tq.TQ_LAYOUT_ROW)
+    vc = tq.Codes(vcb, B * Hkv, N, tq.TQ_LAYOUT_TILE32)
+    # cache build (untimed): all N positions
+    tq.tq_quantize_kv(kcb, vcb, k.view(B * Hkv, N, d), v.view(B * Hkv, N, d), kc, vc)
+    # the step's new token per sequence = the last position
+    k_new = k[:, :, N - 1:N].reshape(B * Hkv, 1, d).contiguous()
+    v_new = v[:, :, N - 1:N].reshape(B * Hkv, 1, d).contiguous()
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(tq.tq_attn_decode_workspace(B, Hq, Hkv, N, d), dtype=torch.uint8, device=dev)
+    tau = 1.0 / math.sqrt(d)
+
+    def step():
+        tq.tq_quantize_kv(kcb, vcb, k_new, v_new, kc, vc, tok_offset=N - 1)
+        tq.tq_attn_decode(kcb, vcb, q, kc, vc, N, tau, out=out, workspace=ws)
+
+    per_token_head = (3 * d // 8) + 4 * ((128 + 31) // 32) + 4 + 4 + (4 * d // 8) + 4   # 140 B
+    cfg = dict(workload="decode-128k GQA layer", B=B, Hq=Hq, Hkv=Hkv, d=d, context=N,
+               keys="3-bit Lloyd-Max + 1-bit QJL m=128", values="4-bit Lloyd-Max",
+               kv_input="bf16, N(0,1), channels 3/77/101 x20", query="bf16")
+    return dict(step=step, B=B, Hq=Hq, Hkv=Hkv, d=d, N=N, kcb=kcb, vcb=vcb, k=k, v=v, q=q,
+                tau=tau, bytes_per_token_head=per_token_head, cfg=cfg)
+
+
+def quantize_leg(torch, tq, synth, dev, iters, warm):
+    B, H, N, d = 16, 8, 32768, 128
+    chk = synth.outlier_channels(10, H, d, 4)
+    chv = synth.outlier_channels(11, H, d, 4)
+    k = synth.kv_gaussian(B, H, N, d, 10, dtype="bf16", device=dev, per_head_channels=chk, factor=15.0)
+    v = synth.kv_gaussian(B, H, N, d, 11, dtype="bf16", device=dev, per_head_channels=chv, factor=15.0)
+    kcb = tq.Codebook(d, 4, rot_seed=1)
+    vcb = tq.Codebook(d, 4, rot_seed=3)
+    kc = tq.Codes(kcb, B * H, N, tq.TQ_LAYOUT_ROW)
+    vc = tq.Codes(vcb, B * H, N, tq.TQ_LAYOUT_TILE32)
+    kf, vf = k.view(B * H, N, d), v.view(B * H, N, d)
+    for _ in range(warm):
+        tq.tq_quantize_kv(kcb, vcb, kf, vf, kc, vc)
+    torch.cuda.synchronize()
+    tq.tq_profile_enable(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        tq.tq_quantize_kv(kcb, vcb, kf, vf, kc, vc)
+    e1.record()
+    torch.cuda.synchronize()
+    tq.tq_profile_enable(False)
+    kms, kn = tq.tq_profile_read(tq.TQ_KERNEL_QUANTIZE)
+    ms = e0.elapsed_time(e1) / iters
+    n_vec = 2 * B * H * N
+    in_bytes = n_vec * d * 2
+    out_bytes = n_vec * (d * 4 // 8 + 4)
+    gbs = (in_bytes + out_bytes) / (ms * 1e-3) / 1e9
+    kern_ms = kms / kn
+    per_launch_bytes = (in_bytes + out_bytes) / 2
+    flops = 2.0 * d * d * n_vec
+    del k, v, kc, vc
+    return dict(workload="quantize-only layer: B=16, Hkv=8, d=128, 32768 tokens, bf16 K and V "
+                         "(4 outlier channels/head x15), 4-bit, no QJL",
+                GB_per_s=round(gbs, 1), frac_hbm=round(gbs / HBM_PEAK_GBS, 4), ms_per_call=round(ms, 4),
+                kernel_ms=round(kern_ms, 4),
+                kernel_GB_per_s=round(per_launch_bytes / (kern_ms * 1e-3) / 1e9, 1),
+                rotation_TFLOP_per_s=round(flops / (ms * 1e-3) / 1e12, 2),
+                bytes_per_call=int(in_bytes + out_bytes))
+
+
+def cpu_baseline(torch, O, W, n_pairs=2):
+    """float64 oracle: per sampled (batch, KV head) pair, quantize the step's
+    new vectors and decode its 8 query heads over the full context."""
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    B, Hkv, Hq, d, N = W["B"], W["Hkv"], W["Hq"], W["d"], W["N"]
+    g = Hq // Hkv
+    okc = O.Codebook(d, 3, qjl_m=128, rot_seed=1, qjl_seed=2)
+    ovc = O.Codebook(d, 4, rot_seed=3)
+    pairs = [(0, 0), (B - 1, Hkv - 1), (B // 2, Hkv // 2)][:n_pairs]
+    q64 = W["q"].float().cpu().numpy().astype(np.float64)
+    t_total = 0.0
+    for (b, h) in pairs:
+        k64 = W["k"][b, h].float().cpu().numpy().astype(np.float64)
+        v64 = W["v"][b, h].float().cpu().numpy().astype(np.float64)
+        rk = O.quantize(okc, k64[:N - 1])          # cache build (untimed)
+        rv = O.quantize(ovc, v64[:N - 1])
+        t0 = time.perf_counter()
+        nk = O.quantize(okc, k64[N - 1:])
+        nv = O.quantize(ovc, v64[N - 1:])
+        kd = {n: np.concatenate([rk[n], nk[n]])[None, None] for n in ("idx", "scale", "sign", "rnorm")}
+        vd = {n: np.concatenate([rv[n], nv[n]])[None, None] for n in ("idx", "scale")}
+        O.attn_decode(okc, ovc, q64[b:b + 1, h * g:(h + 1) * g], kd, vd, W["tau"])
+        t_total += time.perf_counter() - t0
+    kv_tokens = len(pairs) * N / Hkv         # each pair is 1/Hkv of a batch row
+    return dict(value=round(kv_tokens / t_total, 1), unit="KV tokens/s", cores=int(threads),
+                kind="oracle",
+                sample=f"{len(pairs)} of {B * Hkv} (batch, KV head) pairs of the decode-128k layer at "
+                       f"full context {N}, all {g} query heads each, float64; "
+                       f"{t_total:.1f} s of CPU time, scaled to KV tokens/s")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import synth
+    import kv_cache_vector_quantize_amd as tq
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    tq.lib()
+    dev = "cuda"
+    print("[bench] building decode-128k workload", file=sys.stderr, flush=True)
+    W = decode_workload(torch, tq, synth, dev)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        W["step"]()
+    torch.cuda.synchronize()
+    print("[bench] timing", args.steps, "steps", file=sys.stderr, flush=True)
+    tq.tq_profile_enable(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        W["step"]()
+    e1.record()
+    torch.cuda.synchronize()
+    tq.tq_profile_enable(False)
+    ms_step = e0.elapsed_time(e1) / args.steps
+    split_ms, split_n = tq.tq_profile_read(tq.TQ_KERNEL_DECODE_SPLIT)
+    split_avg = split_ms / max(1, split_n)
+    B, Hkv, N = W["B"], W["Hkv"], W["N"]
+    value = B * N / (ms_step * 1e-3)
+    alg_bytes = W["bytes_per_token_head"] * B * Hkv * N
+    achieved = alg_bytes / (split_avg * 1e-3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "KV tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": W["cfg"],
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "decode split (k_split<3,4,qjl>)",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel_ms": round(split_avg, 5),
+            "algorithmic_bytes_per_launch": int(alg_bytes),
+        },
+    }
+    if not args.no_quantize:
+        print("[bench] quantize leg", file=sys.stderr, flush=True)
+        res["quantize"] = quantize_leg(torch, tq, synth, dev, iters=max(5, args.steps // 2),
+                                       warm=max(1, args.warmup // 2))
+    if args.calib_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        res["calib_copy_bytes"] = 1 << 30
+    if not args.no_cpu_baseline:
+        import oracle as O
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(torch, O, W)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

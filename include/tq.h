@@ -62,13 +62,14 @@ typedef enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 } tq_dtype;
  *    sign row r at sign + r*sign_row_bytes: sketch row j at bit j, zero bits
  *         after j = m-1.  Minimum sign_row_bytes is 4*ceil(m/32).
  *  TQ_LAYOUT_TILE32 (value codes for decode): sequence s is cut into blocks
- *    of 32 vectors; block k of sequence s starts at
- *    idx + (s*(seq_stride/32) + k) * (d*b*4) bytes and holds, for each
- *    coordinate i, b little-endian 32-bit words (a 32*b-bit stream) whose
- *    slot q in 0..31 holds vector tile32_token(q) of the block at bits
- *    [q*b, q*b+b), where tile32_token(q) = 4*(q/8) + q%8 for q%8 < 4 and
- *    16 + 4*(q/8) + q%8 - 4 otherwise.  seq_stride must be a multiple of 32;
- *    idx_row_bytes is ignored.  Sign codes are not supported in this layout.
+ *    of 32 vectors of BB = 64*ceil(d/16)*b bytes; block k of sequence s
+ *    starts at idx + (s*(seq_stride/32) + k)*BB.  Inside a block, index i of
+ *    vector t (0..31) sits at bits [p, p+b) of the block's little-endian bit
+ *    stream with p = ((r*ceil(d/16) + i/16)*8 + e)*b, r = 16*((t%16)/4) + i%16,
+ *    e = t%4 + 4*(t/16): 64 records, each holding 8 vectors x ceil(d/16)
+ *    groups of 16-strided coordinates.  Padding bits are zero.  seq_stride
+ *    must be a multiple of 32; idx_row_bytes is ignored.  Sign codes are not
+ *    supported in this layout.
  *  scale[r] / rnorm[r] (fp32) are indexed by r = s*seq_stride + v in both. */
 typedef enum { TQ_LAYOUT_ROW = 0, TQ_LAYOUT_TILE32 = 1 } tq_layout;
 
@@ -184,6 +185,20 @@ tq_status tq_attn_decode(const tq_codebook* kcb, const tq_codebook* vcb, const v
                          const tq_codes* v, const int32_t* seq_lens, int64_t n_ctx,
                          float sm_scale, float* out, float* logits, void* workspace,
                          size_t ws_bytes, void* stream);
+
+/* Kernel timing (instrumentation; not part of the method).
+ * tq_profile_enable(1) clears the calling thread's records and starts
+ * recording: every later tq_quantize_kv / tq_attn_decode on this thread
+ * records a hipEvent pair on its stream around each launch of its main
+ * kernel (the quantize kernel, once per tensor; the decode split kernel).
+ * tq_profile_enable(0) stops recording and keeps the records.
+ * tq_profile_read waits for the recorded events and returns the summed
+ * elapsed milliseconds and the number of launches of one kernel
+ * (TQ_KERNEL_QUANTIZE or TQ_KERNEL_DECODE_SPLIT).  Events are created by the
+ * library (no device memory is allocated). */
+typedef enum { TQ_KERNEL_QUANTIZE = 0, TQ_KERNEL_DECODE_SPLIT = 1 } tq_kernel;
+tq_status tq_profile_enable(int32_t on);
+tq_status tq_profile_read(int32_t kernel, double* total_ms, int64_t* launches);
 
 /* Message of the last failing call on this thread ("" if none). */
 const char* tq_last_error(void);

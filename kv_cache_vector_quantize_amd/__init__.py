@@ -8,6 +8,8 @@ from ._lib import (  # noqa: F401
     TQ_F16,
     TQ_F32,
     TQ_LAYOUT_ROW,
+    TQ_KERNEL_DECODE_SPLIT,
+    TQ_KERNEL_QUANTIZE,
     TQ_LAYOUT_TILE32,
     Codebook,
     Codes,
@@ -16,5 +18,7 @@ from ._lib import (  # noqa: F401
     tq_attn_decode,
     tq_attn_decode_workspace,
     tq_codebook_values,
+    tq_profile_enable,
+    tq_profile_read,
     tq_quantize_kv,
 )

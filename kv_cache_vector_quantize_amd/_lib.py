@@ -23,8 +23,9 @@ TQ_LAYOUT_ROW, TQ_LAYOUT_TILE32 = 0, 1
 EXPORTS = (
     "tq_codebook_build", "tq_codebook_destroy", "tq_codebook_export", "tq_codebook_values",
     "tq_code_row_bytes", "tq_quantize_kv", "tq_attn_decode_workspace", "tq_attn_decode",
-    "tq_last_error",
+    "tq_profile_enable", "tq_profile_read", "tq_last_error",
 )
+TQ_KERNEL_QUANTIZE, TQ_KERNEL_DECODE_SPLIT = 0, 1
 
 
 class TQError(RuntimeError):
@@ -72,6 +73,8 @@ def lib() -> ctypes.CDLL:
     L.tq_attn_decode.argtypes = [vp, vp, vp, i32, i64, i64, i64, ctypes.POINTER(tq_codes),
                                  ctypes.POINTER(tq_codes), vp, i64, ctypes.c_float, vp, vp, vp,
                                  ctypes.c_size_t, vp]
+    L.tq_profile_enable.argtypes = [i32]
+    L.tq_profile_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
     for name in EXPORTS:
         if name != "tq_last_error":
             getattr(L, name).restype = ctypes.c_int
@@ -176,7 +179,8 @@ class Codes:
             if seq_stride % 32:
                 raise ValueError("tile32 codes need seq_stride % 32 == 0")
             self.idx_row_bytes, self.sign_row_bytes = 0, 0
-            self.idx = torch.zeros(max(1, self.n_seq * (self.seq_stride // 32) * cb.d * cb.bits * 4),
+            block = 64 * ((cb.d + 15) // 16) * cb.bits
+            self.idx = torch.zeros(max(1, self.n_seq * (self.seq_stride // 32) * block),
                                    dtype=torch.uint8, device=device)
         self.scale = torch.zeros(max(1, n), dtype=torch.float32, device=device)
         if cb.m > 0:
@@ -248,3 +252,14 @@ def tq_attn_decode(kcb, vcb, q, k_codes: Codes, v_codes: Codes, n_ctx: int, sm_s
         float(sm_scale), out.data_ptr(), logits.data_ptr() if logits is not None else None,
         workspace.data_ptr(), workspace.numel(), _stream_handle(stream)))
     return out
+
+
+def tq_profile_enable(on: bool = True):
+    _check(lib().tq_profile_enable(1 if on else 0))
+
+
+def tq_profile_read(kernel: int):
+    """(total milliseconds, launches) recorded for one kernel id."""
+    ms, n = ctypes.c_double(), ctypes.c_int64()
+    _check(lib().tq_profile_read(int(kernel), ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value

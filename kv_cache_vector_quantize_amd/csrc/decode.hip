@@ -6,20 +6,28 @@
 // correction of the inner product.
 //
 // Three launches:
-//  1. prologue, one workgroup per (batch, KV head, group of <= 8 query
-//     heads): q~ = Pi_K q scaled by sm_scale*log2(e), t = sqrt(pi/2)/m S_K q~;
-//     both are split into bf16 hi + lo and written in the lane order of the
-//     B operand of v_mfma_f32_16x16x32_bf16 (columns 0-7 = hi of the 8
-//     queries, 8-15 = lo).
-//  2. split: each wave streams 32-token tiles of one KV head's codes and
-//     computes, on MFMA, S^T = K^ Q~^T (tokens x query columns), the QJL term
-//     T^ (2 sigma) - sum(t) (the -sum(t) enters as the accumulator's initial
-//     value), the online softmax in base 2, and O^T += V^T P^T in the
-//     rotated value domain.  Code operands are expanded through bf16 hi/lo
-//     tables in LDS indexed by pairs of packed indices.  hi and lo query
-//     columns are summed with one DPP row rotation.
-//  3. combine, one workgroup per (batch, query head): log-sum-exp merge of
-//     the waves' partials in a fixed order, then out = Pi_V^T o~ / l.
+//  1. prologue, one workgroup per row = (batch, KV head, group of <= 8 query
+//     heads): q~ = Pi_K q scaled by sm_scale*log2(e), t = sqrt(pi/2)/m S_K q~,
+//     split into bf16 hi + lo and written in the lane order of the B operand
+//     of v_mfma_f32_16x16x32_bf16 (columns 0-7 = hi of the 8 queries, 8-15 =
+//     lo of the same queries).
+//  2. split: a workgroup of 4 waves covers 4 consecutive token chunks of one
+//     row; each wave streams 32-token tiles and computes on MFMA
+//       S^T = K^ Q~^T   (16 tokens x 16 query columns per block),
+//       the QJL term T^ (2 sigma) - sum(t)  (-sum(t) is the accumulator's
+//       initial value; sign bits become bf16 {0, 2.0} with two ALU ops),
+//       O^T += V^ P^T   (in the value codebook's rotated domain),
+//     with an online softmax in base 2 whose reference maximum is only moved
+//     when a tile exceeds it by more than 2^8.  Code operands come from bf16
+//     hi/lo tables in LDS indexed by a pair of packed indices; hi and lo sit
+//     next to each other in the contraction dimension (operand dwords
+//     hi,lo,hi,lo against a duplicated other operand), so a 64-bit table read
+//     lands directly in the MFMA operand registers.  The 4 waves' partial
+//     (max, sum, o~) are merged in LDS and written once per workgroup.
+//  3. combine, one workgroup per row: log-sum-exp merge of the workgroups'
+//     partials in a fixed order, then out = Pi_V^T o~ / l.
+#include <type_traits>
+
 #include "tq_internal.hpp"
 
 namespace tq {
@@ -29,10 +37,13 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 
-constexpr int D = 128;           // head dimension of this kernel family
-constexpr int QOP_DWORDS = 2 * 4 * 64 * 4 + 16;   // Q op, T op, 16 C-init floats
+constexpr int D = 128;                 // head dimension of this kernel family
+constexpr int QOP_Q = 8 * 64 * 4;      // Q operand dwords: 8 MFMAs x 64 lanes x 4
+constexpr int QOP_T = 4 * 64 * 4;      // T operand dwords
+constexpr int QOP_DWORDS = QOP_Q + QOP_T + 16;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
+constexpr float LAZY = 8.0f;           // max moves when a tile exceeds it by 2^8
 
 __device__ inline uint32_t bf16_rne_bits(float v) {
   uint32_t u = __float_as_uint(v);
@@ -49,16 +60,20 @@ __device__ inline bf16x8 as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t 
   return __builtin_bit_cast(bf16x8, v);
 }
 
+__device__ inline f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 // ------------------------------------------------------------ 1. prologue
 
 struct PArgs {
   const void* q;
   int qdt;
   int Hq, Hkv, g, qgroups;
-  int m;
+  int m, mp;
   float qscale;           // sm_scale * log2(e)
-  const float* rotK;      // [D][D]
-  const float* qjlK;      // [mp][D] or null
+  const float* rotKT;     // [D][D], rotKT[k][i] = Pi_K[i][k]
+  const float* qjlKT;     // [D][mp], qjlKT[i][j] = S_K[j][i] (or null)
   uint32_t* qop;          // [rows][QOP_DWORDS]
 };
 
@@ -80,61 +95,74 @@ __global__ void __launch_bounds__(256) k_prologue(PArgs a) {
   for (int e = tid; e < 8 * D; e += 256) {
     const int c = e / D, i = e % D;
     const int j = qg * 8 + c;
-    float v = 0.f;
-    if (j < a.g) v = load_q(a.q, a.qdt, ((int64_t)b * a.Hq + h * a.g + j) * D + i);
-    qs[c][i] = v;
+    qs[c][i] = (j < a.g) ? load_q(a.q, a.qdt, ((int64_t)b * a.Hq + h * a.g + j) * D + i) : 0.f;
   }
   __syncthreads();
-  for (int e = tid; e < 8 * D; e += 256) {
-    const int c = e / D, i = e % D;
-    float s = 0.f;
-    for (int k = 0; k < D; ++k) s += a.rotK[i * D + k] * qs[c][k];
-    qt[c][i] = s * a.qscale;
+  // thread (i, half): queries 4*half .. 4*half+3, coalesced over i
+  const int i = tid & (D - 1), c0 = (tid >> 7) * 4;
+  {
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+    for (int k = 0; k < D; ++k) {
+      const float r = a.rotKT[k * D + i];
+      s0 += r * qs[c0][k]; s1 += r * qs[c0 + 1][k]; s2 += r * qs[c0 + 2][k]; s3 += r * qs[c0 + 3][k];
+    }
+    qt[c0][i] = s0 * a.qscale; qt[c0 + 1][i] = s1 * a.qscale;
+    qt[c0 + 2][i] = s2 * a.qscale; qt[c0 + 3][i] = s3 * a.qscale;
   }
   __syncthreads();
-  const float cq = a.m > 0 ? 1.2533141373155003f / (float)a.m : 0.f;   // sqrt(pi/2)/m
-  for (int e = tid; e < 8 * D; e += 256) {
-    const int c = e / D, j = e % D;
-    float s = 0.f;
-    if (j < a.m)
-      for (int i = 0; i < D; ++i) s += a.qjlK[j * D + i] * qt[c][i];
-    tt[c][j] = s * cq;
+  {
+    const float cq = a.m > 0 ? 1.2533141373155003f / (float)a.m : 0.f;   // sqrt(pi/2)/m
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+    if (i < a.m) {
+      for (int k = 0; k < D; ++k) {
+        const float r = a.qjlKT[k * a.mp + i];
+        s0 += r * qt[c0][k]; s1 += r * qt[c0 + 1][k]; s2 += r * qt[c0 + 2][k]; s3 += r * qt[c0 + 3][k];
+      }
+    }
+    tt[c0][i] = s0 * cq; tt[c0 + 1][i] = s1 * cq; tt[c0 + 2][i] = s2 * cq; tt[c0 + 3][i] = s3 * cq;
   }
   __syncthreads();
   uint32_t* dst = a.qop + (int64_t)row * QOP_DWORDS;
-  // operand dwords: [op][chunk][lane][4]
-  for (int e = tid; e < 2 * 4 * 64 * 4; e += 256) {
-    const int p = e & 3, lane = (e >> 2) & 63, chunk = (e >> 8) & 3, op = e >> 10;
-    const int col = lane & 15, g4 = lane >> 4;
-    const int c = col & 7;
-    const bool lo = col >= 8;
-    uint32_t halves[2];
+  // Q operand [u][lane][p]: MFMA u, lane group g4 covers dims 32*g4 + 4u .. +3;
+  // dwords p = 0,1 -> dims (4u, 4u+1) (hi then lo slot of the key operand),
+  // p = 2,3 -> dims (4u+2, 4u+3).
+  for (int e = tid; e < QOP_Q; e += 256) {
+    const int p = e & 3, lane = (e >> 2) & 63, u = e >> 8;
+    const int col = lane & 15, g4 = lane >> 4, c = col & 7;
+    const int dim = 32 * g4 + 4 * u + 2 * (p >> 1);
+    uint32_t hv[2];
     for (int h2 = 0; h2 < 2; ++h2) {
-      const int el = 2 * p + h2;           // element 0..7 of the lane's operand
-      float v;
-      if (op == 0) {
-        v = qt[c][32 * g4 + 8 * chunk + el];
-      } else {
-        const int j = 32 * g4 + 4 * chunk + (el >> 1) + 16 * (el & 1);
-        v = tt[c][j];
-      }
+      const float v = qt[c][dim + h2];
       const uint32_t hi = bf16_rne_bits(v);
-      halves[h2] = lo ? bf16_rne_bits(v - __uint_as_float(hi << 16)) : hi;
+      hv[h2] = (col >= 8) ? bf16_rne_bits(v - __uint_as_float(hi << 16)) : hi;
     }
-    dst[e] = halves[0] | (halves[1] << 16);
+    dst[e] = hv[0] | (hv[1] << 16);
+  }
+  // T operand [c][lane][p]: element el of lane group g4, MFMA c holds sketch
+  // row j = 32*g4 + 4c + el/2 + 16*(el%2)
+  for (int e = tid; e < QOP_T; e += 256) {
+    const int p = e & 3, lane = (e >> 2) & 63, cc = e >> 8;
+    const int col = lane & 15, g4 = lane >> 4, c = col & 7;
+    uint32_t hv[2];
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int el = 2 * p + h2;
+      const float v = tt[c][32 * g4 + 4 * cc + (el >> 1) + 16 * (el & 1)];
+      const uint32_t hi = bf16_rne_bits(v);
+      hv[h2] = (col >= 8) ? bf16_rne_bits(v - __uint_as_float(hi << 16)) : hi;
+    }
+    dst[QOP_Q + e] = hv[0] | (hv[1] << 16);
   }
   if (tid < 16) {
     float s = 0.f;
     if (tid < 8) {
       for (int j = 0; j < D; ++j) {
         const float v = tt[tid][j];
-        const uint32_t hi = bf16_rne_bits(v);
-        const float fh = __uint_as_float(hi << 16);
+        const float fh = __uint_as_float(bf16_rne_bits(v) << 16);
         const float fl = __uint_as_float(bf16_rne_bits(v - fh) << 16);
         s += fh + fl;
       }
     }
-    reinterpret_cast<float*>(dst)[2 * 4 * 64 * 4 + tid] = -s;
+    reinterpret_cast<float*>(dst)[QOP_Q + QOP_T + tid] = -s;
   }
 }
 
@@ -156,50 +184,89 @@ struct SArgs {
   const int32_t* seq_lens;
   int64_t n_ctx;
   int Hq, Hkv, g, qgroups, m;
-  int chunk, n_parts;
-  float* part_o;     // [rows][n_parts][8][D]
-  float* part_ml;    // [rows][n_parts][8][2]
+  int chunk, n_parts, n_wg;
+  float* part_o;     // [rows][n_wg][8][D]
+  float* part_ml;    // [rows][n_wg][8][2]
   float* logits;     // [B][Hq][n_ctx] or null
 };
 
-// Bits [off, off+w) of a little-endian multi-word field (w <= 32).
+// Bits [off, off + w) of a little-endian multi-word field (w <= 16).
 template <int NW>
 __device__ inline uint32_t field(const uint32_t (&wd)[NW], int off, int w) {
   const int i = off >> 5, s = off & 31;
-  uint64_t v = wd[i];
-  if (i + 1 < NW) v |= (uint64_t)wd[i + 1] << 32;
-  return (uint32_t)(v >> s) & (w >= 32 ? 0xFFFFFFFFu : ((1u << w) - 1u));
+  uint32_t v;
+  if (s + w <= 32 || i + 1 >= NW) v = wd[i] >> s;
+  else v = __builtin_amdgcn_alignbit(wd[i + 1], wd[i], s);
+  return v & ((1u << w) - 1u);
 }
 
-// Two bf16 hi/lo dwords for codes (a at element 2p, b at 2p+1) from a pair
-// field of 2*B bits.
 template <int B>
-__device__ inline void expand_pair(const uint32_t* tab, uint32_t pair, uint32_t& hi, uint32_t& lo) {
+constexpr int table_entries() { return (B <= 4) ? (1 << (2 * B)) : (1 << B); }
+
+// hi and lo operand dwords of two codes from the table in LDS: for B <= 4
+// entry e = a | b << B is the dword pair {hi(c[a]) | hi(c[b]) << 16,
+// lo(c[a]) | lo(c[b]) << 16} (one 64-bit read lands both in consecutive
+// registers); for B > 4 a single-code table holds hi | lo << 16.
+template <int B>
+__device__ inline uint2 lookup(const uint32_t* tab, uint32_t pair) {
   if constexpr (B <= 4) {
-    const uint2 e = reinterpret_cast<const uint2*>(tab)[pair];
-    hi = e.x;
-    lo = e.y;
+    return reinterpret_cast<const uint2*>(tab)[pair];
   } else {
     const uint32_t e0 = tab[pair & ((1u << B) - 1u)];
     const uint32_t e1 = tab[pair >> B];
-    hi = __builtin_amdgcn_perm(e1, e0, 0x05040100u);
-    lo = __builtin_amdgcn_perm(e1, e0, 0x07060302u);
+    return make_uint2(__builtin_amdgcn_perm(e1, e0, 0x05040100u),
+                      __builtin_amdgcn_perm(e1, e0, 0x07060302u));
   }
 }
 
+// sign operand dword: bits x and x+16 of w at positions 14 and 30 (bf16 2.0)
+template <int X>
+__device__ inline uint32_t sign_pair(uint32_t w) {
+  if constexpr (X <= 14) return (w << (14 - X)) & 0x40004000u;
+  else return (w >> (X - 14)) & 0x40004000u;
+}
+
+// Value-code group db (8 token slots of one coordinate) from a lane's tile32
+// record of 2*BV dwords.
+template <int BV>
+__device__ inline uint32_t vgroup(const uint32_t* rec, int db, uint32_t& hi32) {
+  hi32 = 0u;
+  if constexpr (BV == 4) return rec[db];
+  else if constexpr (BV == 2) return rec[db >> 1] >> (16 * (db & 1));
+  else if constexpr (BV == 8) { hi32 = rec[2 * db + 1]; return rec[2 * db]; }
+  else {   // BV == 3: 24-bit groups
+    const int bit = 24 * db, w = bit >> 5, sh = bit & 31;
+    if (sh + 24 <= 32) return rec[w] >> sh;
+    return __builtin_amdgcn_alignbit(rec[w + 1], rec[w], sh);
+  }
+}
+
+// Global loads of one 32-token tile for one lane.
+template <int BK, int BV>
+struct Tile {
+  uint32_t kw[2][BK];   // key index bits of this lane's token (per 16-token block)
+  uint32_t sw[2];       // QJL sign word
+  uint32_t vr[2 * BV];  // value record: 8 coordinates x 8 token slots
+  float sc0, sc1;       // per-token scalars staged through LDS
+};
+
 template <int BK, int BV, bool QJL>
-__global__ void __launch_bounds__(256) k_split(SArgs a) {
-  __shared__ uint32_t s_ktab[(BK <= 4) ? (2 << (2 * BK)) : (1 << BK)];
-  __shared__ uint32_t s_vtab[(BV <= 4) ? (2 << (2 * BV)) : (1 << BV)];
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) k_split(SArgs a) {
+  constexpr int KE = table_entries<BK>(), VE = table_entries<BV>();
+  constexpr int KTD = (BK <= 4) ? 2 * KE : KE, VTD = (BV <= 4) ? 2 * VE : VE;   // dwords
+  __shared__ __align__(16) uint32_t s_kt[KTD];
+  __shared__ __align__(16) uint32_t s_vt[VTD];
+  __shared__ __align__(16) float s_sc[4][96];     // per wave: kscale[32], rnorm[32], vscale[32]
+  __shared__ float s_M[4][8], s_l[4][8];
+  __shared__ __align__(16) float s_o[4][8][D];
   const int tid = threadIdx.x;
-  for (int i = tid; i < a.ktab_dwords; i += 256) s_ktab[i] = a.ktab[i];
-  for (int i = tid; i < a.vtab_dwords; i += 256) s_vtab[i] = a.vtab[i];
+  for (int i = tid; i < KTD; i += 256) s_kt[i] = a.ktab[i];
+  for (int i = tid; i < VTD; i += 256) s_vt[i] = a.vtab[i];
   __syncthreads();
 
   const int wave = tid >> 6, lane = tid & 63;
   const int c16 = lane & 15, g4 = lane >> 4;
   const int part = blockIdx.x * 4 + wave;
-  if (part >= a.n_parts) return;
   const int row = blockIdx.y;
   const int qg = row % a.qgroups;
   const int bh = row / a.qgroups;
@@ -210,178 +277,216 @@ __global__ void __launch_bounds__(256) k_split(SArgs a) {
   const int64_t t_begin = (int64_t)part * a.chunk;
   int64_t t_end = t_begin + a.chunk;
   if (t_end > n_valid) t_end = n_valid;
+  if (part >= a.n_parts) t_end = t_begin;
 
-  // query operands
-  const uint32_t* qop = a.qop + (int64_t)row * QOP_DWORDS;
-  bf16x8 qa[4], ta[4];
+  // query operands (per row): qa[u] = dims 32*g4 + 4u + (0,1,0,1,2,3,2,3)
+  const u32x4* qop = reinterpret_cast<const u32x4*>(a.qop + (int64_t)row * QOP_DWORDS);
+  bf16x8 qa[8], ta[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const u32x4 v = reinterpret_cast<const u32x4*>(qop)[(0 * 4 + c) * 64 + lane];
-    qa[c] = __builtin_bit_cast(bf16x8, v);
-    const u32x4 w = reinterpret_cast<const u32x4*>(qop)[(1 * 4 + c) * 64 + lane];
-    ta[c] = __builtin_bit_cast(bf16x8, w);
+  for (int u = 0; u < 8; ++u) qa[u] = __builtin_bit_cast(bf16x8, qop[u * 64 + lane]);
+  if constexpr (QJL) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) ta[c] = __builtin_bit_cast(bf16x8, qop[QOP_Q / 4 + c * 64 + lane]);
   }
-  const float cinit = reinterpret_cast<const float*>(qop)[2 * 4 * 64 * 4 + c16];
+  const float cinit = QJL ? reinterpret_cast<const float*>(a.qop + (int64_t)row * QOP_DWORDS)[QOP_Q + QOP_T + c16] : 0.f;
+  const float sel_lo = (c16 >= 8) ? 1.f : 0.f;
 
   float M = -INFINITY, l = 0.f;
   f32x4 acc_o[8];
 #pragma unroll
   for (int db = 0; db < 8; ++db) acc_o[db] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  const int hq_lane = h * a.g + qg * 8 + (c16 & 7);
-  const bool q_valid = qg * 8 + (c16 & 7) < a.g;
-  const float* kscale = a.kscale + seq * a.k_stride;
-  const float* krnorm = QJL ? a.krnorm + seq * a.k_stride : nullptr;
-  const float* vscale = a.vscale + seq * a.v_stride;
+  // per-sequence (uniform) bases and 32-bit lane offsets
+  const char* kbase = reinterpret_cast<const char*>(a.kidx) + seq * a.k_stride * a.k_pitch;
+  const uint32_t klane = (uint32_t)(c16 * a.k_pitch + g4 * BK * 4);
+  const uint32_t kblk = (uint32_t)(16 * a.k_pitch);
+  const uint32_t* sbase = QJL ? a.ksign + seq * a.k_stride * (a.ks_pitch >> 2) : nullptr;
+  const uint32_t slane = (uint32_t)(c16 * (a.ks_pitch >> 2) + g4);
+  const uint32_t sblk = (uint32_t)(16 * (a.ks_pitch >> 2));
+  const bool sign_lane = QJL && (32 * g4 < a.m);
+  constexpr int VBLK = 64 * 8 * BV / 4;                  // dwords per tile32 block (d = 128)
+  const uint32_t* vbase = a.vidx + seq * (a.v_stride / 32) * (int64_t)VBLK;
+  const uint32_t vlane = (uint32_t)((16 * g4 + c16) * 2 * BV);
+  const float* sc0base = (lane < 32) ? a.kscale + seq * a.k_stride + lane
+                                     : (QJL ? a.krnorm + seq * a.k_stride + (lane - 32) : a.kscale + seq * a.k_stride);
+  const float* sc1base = a.vscale + seq * a.v_stride + (lane & 31);
+  float* stage = &s_sc[wave][0];
 
-  int64_t t0 = t_begin;
-  for (; t0 < t_end; t0 += 32) {
-    // ---- loads
-    uint32_t kw[2][BK];
-    uint32_t sw[2] = {0u, 0u};
+  auto load = [&](Tile<BK, BV>& T, const int64_t t0) {
+    const uint32_t t32 = (uint32_t)(t0 - 0);
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-      const int64_t r = seq * a.k_stride + t0 + 16 * blk + c16;
-      const uint32_t* src = reinterpret_cast<const uint32_t*>(a.kidx + r * a.k_pitch) + g4 * BK;
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(kbase + (t32 * (uint32_t)a.k_pitch + blk * kblk + klane));
 #pragma unroll
-      for (int i = 0; i < BK; ++i) kw[blk][i] = src[i];
+      for (int i = 0; i < BK; ++i) T.kw[blk][i] = src[i];
+      T.sw[blk] = 0u;
       if constexpr (QJL) {
-        if (32 * g4 < a.m) sw[blk] = a.ksign[(r * a.ks_pitch >> 2) + g4];
+        if (sign_lane) T.sw[blk] = sbase[t32 * (uint32_t)(a.ks_pitch >> 2) + blk * sblk + slane];
       }
     }
-    f32x4 ks[2], kr[2], vs[2];
+    const uint32_t* vsrc = vbase + (t32 / 32) * (uint32_t)VBLK + vlane;
+    if constexpr (BV == 4 || BV == 2 || BV == 8) {
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      const int64_t t = t0 + 16 * blk + 4 * g4;
-      ks[blk] = *reinterpret_cast<const f32x4*>(kscale + t);
-      vs[blk] = *reinterpret_cast<const f32x4*>(vscale + t);
-      if constexpr (QJL) kr[blk] = *reinterpret_cast<const f32x4*>(krnorm + t);
-    }
-    constexpr int VW = (8 * BV + 31) / 32 + 1 > BV ? BV : (8 * BV + 31) / 32 + 1;
-    uint32_t vw[8][2];
-    {
-      const uint32_t* vb = a.vidx + (seq * (a.v_stride / 32) + t0 / 32) * (int64_t)(D * BV);
-      const int off = 8 * BV * g4;
-      const int w0 = off >> 5;
-#pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        const uint32_t* src = vb + (16 * db + c16) * BV;
-        vw[db][0] = src[w0];
-        vw[db][1] = (w0 + 1 < BV) ? src[w0 + 1] : 0u;
+      for (int i = 0; i < 2 * BV; i += 4) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(vsrc + i);
+        T.vr[i] = v[0]; T.vr[i + 1] = v[1]; T.vr[i + 2] = v[2]; T.vr[i + 3] = v[3];
       }
-      (void)VW;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2 * BV; i += 2) {
+        const uint2 v = *reinterpret_cast<const uint2*>(vsrc + i);
+        T.vr[i] = v.x; T.vr[i + 1] = v.y;
+      }
     }
+    T.sc0 = sc0base[t32];
+    T.sc1 = sc1base[t32];
+  };
 
-    // ---- logits S^T (tokens x 16 query columns)
+  auto compute = [&](const Tile<BK, BV>& T, const int64_t t0, auto partial_tag) {
+    constexpr bool partial = decltype(partial_tag)::value;
+    // per-token scalars: 96 floats through the wave's LDS slot
+    stage[lane] = T.sc0;
+    stage[64 + (lane & 31)] = T.sc1;
+    // ---- logits S^T: rows = tokens 4*g4 + r (+16 for block 1), cols = query hi/lo
     float lg[2][4];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        uint32_t ah[4], al[4];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const uint32_t pr = field<BK>(kw[blk], (8 * c + 2 * p) * BK, 2 * BK);
-          expand_pair<BK>(s_ktab, pr, ah[p], al[p]);
-        }
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ah[0], ah[1], ah[2], ah[3]), qa[c], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(al[0], al[1], al[2], al[3]), qa[c], acc, 0, 0, 0);
+      for (int u = 0; u < 8; ++u) {
+        const uint2 e0 = lookup<BK>(s_kt, field<BK>(T.kw[blk], (4 * u) * BK, 2 * BK));
+        const uint2 e1 = lookup<BK>(s_kt, field<BK>(T.kw[blk], (4 * u + 2) * BK, 2 * BK));
+        acc = mfma(as_bf16x8(e0.x, e0.y, e1.x, e1.y), qa[u], acc);
       }
       f32x4 accq = {cinit, cinit, cinit, cinit};
       if constexpr (QJL) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          uint32_t as[4];
-#pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            const int x = 4 * c + p;
-            as[p] = ((sw[blk] >> x) & 0x00010001u) << 14;   // bf16 2.0 or 0 at j, j+16
-          }
-          accq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(as[0], as[1], as[2], as[3]), ta[c], accq, 0, 0, 0);
-        }
+        const uint32_t w = T.sw[blk];
+        accq = mfma(as_bf16x8(sign_pair<0>(w), sign_pair<1>(w), sign_pair<2>(w), sign_pair<3>(w)), ta[0], accq);
+        accq = mfma(as_bf16x8(sign_pair<4>(w), sign_pair<5>(w), sign_pair<6>(w), sign_pair<7>(w)), ta[1], accq);
+        accq = mfma(as_bf16x8(sign_pair<8>(w), sign_pair<9>(w), sign_pair<10>(w), sign_pair<11>(w)), ta[2], accq);
+        accq = mfma(as_bf16x8(sign_pair<12>(w), sign_pair<13>(w), sign_pair<14>(w), sign_pair<15>(w)), ta[3], accq);
       }
+      const f32x4 ks = *reinterpret_cast<const f32x4*>(stage + 16 * blk + 4 * g4);
+      f32x4 kr = ks;
+      if constexpr (QJL) kr = *reinterpret_cast<const f32x4*>(stage + 32 + 16 * blk + 4 * g4);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float mse = acc[r] + dpp_ror8(acc[r]);
-        float v = ks[blk][r] * mse;
-        if constexpr (QJL) {
-          const float qj = accq[r] + dpp_ror8(accq[r]);
-          v += kr[blk][r] * qj;
-        }
-        const int64_t t = t0 + 16 * blk + 4 * g4 + r;
-        lg[blk][r] = (t < t_end) ? v : -INFINITY;
+        float v = ks[r] * mse;
+        if constexpr (QJL) v = fmaf(kr[r], accq[r] + dpp_ror8(accq[r]), v);
+        lg[blk][r] = v;
       }
     }
-    if (a.logits && c16 < 8 && q_valid) {
-      float* dst = a.logits + ((int64_t)b * a.Hq + hq_lane) * a.n_ctx;
+    if constexpr (partial) {
+      const int lim = (int)(t_end - t0);
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int64_t t = t0 + 16 * blk + 4 * g4 + r;
-          if (t < a.n_ctx) dst[t] = lg[blk][r] * LN2;
-        }
+        for (int r = 0; r < 4; ++r)
+          if (16 * blk + 4 * g4 + r >= lim) lg[blk][r] = -INFINITY;
+    }
+    if (a.logits) {
+      if (c16 < 8 && qg * 8 + c16 < a.g) {
+        float* dst = a.logits + ((int64_t)b * a.Hq + h * a.g + qg * 8 + c16) * a.n_ctx + t0;
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int tt = 16 * blk + 4 * g4 + r;
+            if (t0 + tt < a.n_ctx) dst[tt] = lg[blk][r] * LN2;
+          }
+      }
     }
 
-    // ---- online softmax (base 2), per query column
-    float mt = fmaxf(fmaxf(fmaxf(lg[0][0], lg[0][1]), fmaxf(lg[0][2], lg[0][3])),
+    // ---- online softmax in base 2; the reference maximum M moves only when
+    // a logit exceeds it by more than LAZY (then exactly, per query column)
+    float lm = fmaxf(fmaxf(fmaxf(lg[0][0], lg[0][1]), fmaxf(lg[0][2], lg[0][3])),
                      fmaxf(fmaxf(lg[1][0], lg[1][1]), fmaxf(lg[1][2], lg[1][3])));
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float Mn = fmaxf(M, mt);
-    const float alpha = (Mn == -INFINITY) ? 1.f : exp2f(M - Mn);
-    M = Mn;
+    if (__builtin_expect(__ballot(lm > M + LAZY) != 0ull, 0)) {
+      float mt = fmaxf(lm, __shfl_xor(lm, 16));
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      const float Mn = fmaxf(M, mt);
+      const float alpha = (Mn == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(M - Mn);
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) acc_o[db] *= alpha;
+      M = Mn;
+    }
+    const f32x4 vs0 = *reinterpret_cast<const f32x4*>(stage + 64 + 4 * g4);
+    const f32x4 vs1 = *reinterpret_cast<const f32x4*>(stage + 80 + 4 * g4);
     float w[2][4];
-    float psum = 0.f;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float p = (lg[blk][r] == -INFINITY) ? 0.f : exp2f(lg[blk][r] - Mn);
-        psum += p;
-        w[blk][r] = (p == 0.f) ? 0.f : p * vs[blk][r];
+        const float p = __builtin_amdgcn_exp2f(lg[blk][r] - M);
+        l += p;
+        w[blk][r] = p * (blk == 0 ? vs0[r] : vs1[r]);
       }
-    l = l * alpha + psum;
+    if constexpr (partial) {
+      const int lim = (int)(t_end - t0);
 #pragma unroll
-    for (int db = 0; db < 8; ++db) acc_o[db] *= alpha;
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (16 * blk + 4 * g4 + r >= lim) w[blk][r] = 0.f;
+    }
 
-    // ---- P^T operand: slot 8*g4+e <-> this lane's tokens; hi or lo column
+    // ---- P^T operand: slot e = token 4*g4 + e (e < 4) or 16 + 4*g4 + e - 4;
+    // hi columns take the bf16-truncated weight, lo columns the remainder
     uint32_t pb[4];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      uint32_t hv[2];
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const int e = 2 * p + h2;
-        const float x = w[e >> 2][e & 3];
-        const float xh = __uint_as_float(__float_as_uint(x) & 0xFFFF0000u);
-        const float v = (c16 < 8) ? x : (x - xh);
-        hv[h2] = __float_as_uint(v) >> 16;
-      }
-      pb[p] = hv[0] | (hv[1] << 16);
+    for (int q = 0; q < 4; ++q) {
+      const float x0 = w[q >> 1][2 * (q & 1)], x1 = w[q >> 1][2 * (q & 1) + 1];
+      const float v0 = fmaf(-sel_lo, __uint_as_float(__float_as_uint(x0) & 0xFFFF0000u), x0);
+      const float v1 = fmaf(-sel_lo, __uint_as_float(__float_as_uint(x1) & 0xFFFF0000u), x1);
+      pb[q] = __builtin_amdgcn_perm(__float_as_uint(v1), __float_as_uint(v0), 0x07060302u);
     }
-    const bf16x8 pop = as_bf16x8(pb[0], pb[1], pb[2], pb[3]);
+    const bf16x8 pop0 = as_bf16x8(pb[0], pb[0], pb[1], pb[1]);
+    const bf16x8 pop1 = as_bf16x8(pb[2], pb[2], pb[3], pb[3]);
 
-    // ---- O^T += V^T P^T
+    // ---- O^T += V^ P^T (coordinates 16*db + c16); operand dwords
+    // (hi, lo, hi, lo) of token slot pairs against duplicated weights
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
-      const int off = 8 * BV * g4;
-      const int s = off & 31;
-      const uint64_t fld = (((uint64_t)vw[db][1] << 32) | vw[db][0]) >> s;
-      uint32_t ah[4], al[4];
+      uint32_t fhi;
+      const uint32_t f = vgroup<BV>(T.vr, db, fhi);
+      uint2 e[4];
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const uint32_t pr = (uint32_t)(fld >> (2 * p * BV)) & ((1u << (2 * BV)) - 1u);
-        expand_pair<BV>(s_vtab, pr, ah[p], al[p]);
+      for (int q = 0; q < 4; ++q) {
+        uint32_t pr;
+        if constexpr (BV == 8) pr = ((q < 2 ? f : fhi) >> (16 * (q & 1))) & 0xFFFFu;
+        else pr = (f >> (2 * q * BV)) & ((1u << (2 * BV)) - 1u);
+        e[q] = lookup<BV>(s_vt, pr);
       }
-      acc_o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ah[0], ah[1], ah[2], ah[3]), pop, acc_o[db], 0, 0, 0);
-      acc_o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(al[0], al[1], al[2], al[3]), pop, acc_o[db], 0, 0, 0);
+      acc_o[db] = mfma(as_bf16x8(e[0].x, e[0].y, e[1].x, e[1].y), pop0, acc_o[db]);
+      acc_o[db] = mfma(as_bf16x8(e[2].x, e[2].y, e[3].x, e[3].y), pop1, acc_o[db]);
     }
+  };
+
+  // two-stage pipeline over full tiles: the next tile's loads are in flight
+  // while the current one is computed
+  const int64_t nfull = (t_end > t_begin) ? (t_end - t_begin) / 32 : 0;
+  int64_t t0 = t_begin;
+  Tile<BK, BV> A, Bt;
+  if (nfull > 0) load(A, t0);
+  for (int64_t i = 0; i < nfull; i += 2) {
+    if (i + 1 < nfull) load(Bt, t0 + 32);
+    compute(A, t0, std::false_type{});
+    t0 += 32;
+    if (i + 1 >= nfull) break;
+    if (i + 2 < nfull) load(A, t0 + 32);
+    compute(Bt, t0, std::false_type{});
+    t0 += 32;
+  }
+  if (t0 < t_end) {
+    load(A, t0);
+    compute(A, t0, std::true_type{});
+    t0 += 32;
   }
 
   // positions of this wave's range that no tile covered (beyond len_b)
-  if (a.logits) {
+  if (a.logits && part < a.n_parts) {
     int64_t to = t_begin + a.chunk;
     if (to > a.n_ctx) to = a.n_ctx;
     for (int c = 0; c < 8; ++c) {
@@ -391,20 +496,42 @@ __global__ void __launch_bounds__(256) k_split(SArgs a) {
     }
   }
 
-  // ---- wave partial: (M, l, o~) per query column
+  // ---- wave partial -> LDS
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
-  const int64_t rec = ((int64_t)row * a.n_parts + part) * 8 + (c16 & 7);
 #pragma unroll
   for (int db = 0; db < 8; ++db) {
     f32x4 o;
 #pragma unroll
     for (int r = 0; r < 4; ++r) o[r] = acc_o[db][r] + dpp_ror8(acc_o[db][r]);
-    if (c16 < 8) *reinterpret_cast<f32x4*>(a.part_o + rec * D + 16 * db + 4 * g4) = o;
+    if (c16 < 8) *reinterpret_cast<f32x4*>(&s_o[wave][c16][16 * db + 4 * g4]) = o;
   }
   if (c16 < 8 && g4 == 0) {
-    a.part_ml[rec * 2 + 0] = M;
-    a.part_ml[rec * 2 + 1] = l;
+    s_M[wave][c16] = M;
+    s_l[wave][c16] = l;
+  }
+  __syncthreads();
+
+  // ---- merge the 4 waves (fixed order) and write one partial per workgroup
+  const int64_t rec0 = ((int64_t)row * a.n_wg + blockIdx.x) * 8;
+  for (int e = tid; e < 8 * D; e += 256) {
+    const int c = e / D, i = e % D;
+    float Mx = fmaxf(fmaxf(s_M[0][c], s_M[1][c]), fmaxf(s_M[2][c], s_M[3][c]));
+    float o = 0.f, ls = 0.f;
+    if (Mx != -INFINITY) {
+#pragma unroll
+      for (int wv = 0; wv < 4; ++wv) {
+        if (s_M[wv][c] == -INFINITY) continue;
+        const float sc = __builtin_amdgcn_exp2f(s_M[wv][c] - Mx);
+        o += sc * s_o[wv][c][i];
+        ls += sc * s_l[wv][c];
+      }
+    }
+    a.part_o[(rec0 + c) * D + i] = o;
+    if (i == 0) {
+      a.part_ml[(rec0 + c) * 2 + 0] = Mx;
+      a.part_ml[(rec0 + c) * 2 + 1] = ls;
+    }
   }
 }
 
@@ -413,38 +540,64 @@ __global__ void __launch_bounds__(256) k_split(SArgs a) {
 struct CArgs {
   const float* part_o;
   const float* part_ml;
-  const float* rotV;   // [D][D]
-  int Hq, Hkv, g, qgroups, n_parts;
+  const float* rotV;   // [D][D] row-major Pi_V
+  int Hq, Hkv, g, qgroups, n_wg;
   float* out;          // [B][Hq][D]
 };
 
-__global__ void __launch_bounds__(D) k_combine(CArgs a) {
-  __shared__ float ov[D];
-  const int bq = blockIdx.x;                  // b * Hq + hq
-  const int b = bq / a.Hq, hq = bq % a.Hq;
-  const int h = hq / a.g, j = hq % a.g;
-  const int row = (b * a.Hkv + h) * a.qgroups + j / 8;
-  const int c = j % 8;
-  const int i = threadIdx.x;
-  float Mx = -INFINITY;
-  for (int p = 0; p < a.n_parts; ++p)
-    Mx = fmaxf(Mx, a.part_ml[(((int64_t)row * a.n_parts + p) * 8 + c) * 2]);
-  float lsum = 0.f, o = 0.f;
-  if (Mx != -INFINITY) {
-    for (int p = 0; p < a.n_parts; ++p) {
-      const int64_t rec = ((int64_t)row * a.n_parts + p) * 8 + c;
-      const float Mp = a.part_ml[rec * 2];
-      if (Mp == -INFINITY) continue;
-      const float s = exp2f(Mp - Mx);
-      lsum += s * a.part_ml[rec * 2 + 1];
-      o += s * a.part_o[rec * D + i];
+__global__ void __launch_bounds__(256) k_combine(CArgs a) {
+  __shared__ float ov[8][D];
+  __shared__ float s_mx[8];
+  __shared__ float inv_l[8];
+  const int row = blockIdx.x;
+  const int qg = row % a.qgroups;
+  const int bh = row / a.qgroups;
+  const int b = bh / a.Hkv, h = bh % a.Hkv;
+  const int tid = threadIdx.x;
+  const int64_t base = (int64_t)row * a.n_wg * 8;
+  // per query: max and normaliser over the workgroup partials (fixed order)
+  if (tid < 8) {
+    const int c = tid;
+    float Mx = -INFINITY;
+    for (int p = 0; p < a.n_wg; ++p) Mx = fmaxf(Mx, a.part_ml[(base + p * 8 + c) * 2]);
+    float ls = 0.f;
+    if (Mx != -INFINITY) {
+      for (int p = 0; p < a.n_wg; ++p) {
+        const float Mp = a.part_ml[(base + p * 8 + c) * 2];
+        if (Mp == -INFINITY) continue;
+        ls += __builtin_amdgcn_exp2f(Mp - Mx) * a.part_ml[(base + p * 8 + c) * 2 + 1];
+      }
     }
+    s_mx[c] = Mx;
+    inv_l[c] = (ls > 0.f) ? 1.0f / ls : 0.f;
   }
-  ov[i] = (lsum > 0.f) ? o / lsum : 0.f;
   __syncthreads();
-  float r = 0.f;
-  for (int k = 0; k < D; ++k) r += a.rotV[k * D + i] * ov[k];
-  a.out[(int64_t)bq * D + i] = r;
+  for (int e = tid; e < 8 * D; e += 256) {
+    const int c = e / D, i = e % D;
+    const float Mx = s_mx[c];
+    float o = 0.f;
+    if (Mx != -INFINITY) {
+      for (int p = 0; p < a.n_wg; ++p) {
+        const float Mp = a.part_ml[(base + p * 8 + c) * 2];
+        if (Mp == -INFINITY) continue;
+        o += __builtin_amdgcn_exp2f(Mp - Mx) * a.part_o[(base + p * 8 + c) * D + i];
+      }
+    }
+    ov[c][i] = o * inv_l[c];
+  }
+  __syncthreads();
+  // out = Pi_V^T o~ : out_j = sum_i Pi_V[i][j] o~_i (coalesced over j)
+  const int j = tid & (D - 1), c0 = (tid >> 7) * 4;
+  float r0 = 0.f, r1 = 0.f, r2 = 0.f, r3 = 0.f;
+  for (int i = 0; i < D; ++i) {
+    const float pv = a.rotV[i * D + j];
+    r0 += pv * ov[c0][i]; r1 += pv * ov[c0 + 1][i]; r2 += pv * ov[c0 + 2][i]; r3 += pv * ov[c0 + 3][i];
+  }
+  const float rr[4] = {r0, r1, r2, r3};
+  for (int k = 0; k < 4; ++k) {
+    const int jq = qg * 8 + c0 + k;
+    if (jq < a.g) a.out[((int64_t)b * a.Hq + h * a.g + jq) * D + j] = rr[k];
+  }
 }
 
 template <int BK, int BV>
@@ -478,7 +631,7 @@ DecodePlan plan_decode(int64_t B, int64_t Hq, int64_t Hkv, int64_t n_ctx, int d)
   p.g = Hkv > 0 ? (int)(Hq / Hkv) : 0;
   p.qgroups = (p.g + 7) / 8;
   p.rows = B * Hkv * p.qgroups;
-  const int64_t target_waves = 2048;
+  const int64_t target_waves = 4096;          // 16 waves per CU on 256 CUs
   int64_t parts = p.rows > 0 ? (target_waves + p.rows - 1) / p.rows : 1;
   if (parts < 1) parts = 1;
   int64_t chunk = (n_ctx + parts - 1) / parts;
@@ -486,11 +639,12 @@ DecodePlan plan_decode(int64_t B, int64_t Hq, int64_t Hkv, int64_t n_ctx, int d)
   if (chunk < 32) chunk = 32;
   p.chunk = (int)chunk;
   p.n_parts = n_ctx > 0 ? (int)((n_ctx + chunk - 1) / chunk) : 0;
+  p.n_wg = (p.n_parts + 3) / 4;
   size_t off = 0;
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
   p.off_qop = off; off = al(off + (size_t)p.rows * QOP_DWORDS * 4);
-  p.off_part_o = off; off = al(off + (size_t)p.rows * p.n_parts * 8 * D * 4);
-  p.off_part_ml = off; off = al(off + (size_t)p.rows * p.n_parts * 8 * 2 * 4);
+  p.off_part_o = off; off = al(off + (size_t)p.rows * p.n_wg * 8 * D * 4);
+  p.off_part_ml = off; off = al(off + (size_t)p.rows * p.n_wg * 8 * 2 * 4);
   p.bytes = off;
   return p;
 }
@@ -509,9 +663,10 @@ hipError_t launch_decode(const tq_codebook* kcb, const tq_codebook* vcb, const v
   pa.q = q; pa.qdt = qdt;
   pa.Hq = (int)plan.Hq; pa.Hkv = (int)plan.Hkv; pa.g = plan.g; pa.qgroups = plan.qgroups;
   pa.m = kcb->p.qjl_m;
+  pa.mp = kcb->mp;
   pa.qscale = sm_scale * LOG2E;
-  pa.rotK = kcb->dev.rot;
-  pa.qjlK = kcb->dev.qjl;
+  pa.rotKT = kcb->dev.rotT;
+  pa.qjlKT = kcb->dev.qjlT;
   pa.qop = qop;
   hipLaunchKernelGGL(k_prologue, dim3((unsigned)plan.rows), dim3(256), 0, stream, pa);
   hipError_t e = hipGetLastError();
@@ -540,11 +695,13 @@ hipError_t launch_decode(const tq_codebook* kcb, const tq_codebook* vcb, const v
     sa.m = kcb->p.qjl_m;
     sa.chunk = plan.chunk;
     sa.n_parts = plan.n_parts;
+    sa.n_wg = plan.n_wg;
     sa.part_o = part_o;
     sa.part_ml = part_ml;
     sa.logits = logits;
-    const dim3 grid((unsigned)((plan.n_parts + 3) / 4), (unsigned)plan.rows);
+    const dim3 grid((unsigned)plan.n_wg, (unsigned)plan.rows);
     const bool qjl = kcb->p.qjl_m > 0;
+    ProfileScope prof(TQ_KERNEL_DECODE_SPLIT, stream);
     switch (kcb->p.bits) {
       case 2: launch_split_bv<2>(sa, vcb->p.bits, qjl, grid, stream); break;
       case 3: launch_split_bv<3>(sa, vcb->p.bits, qjl, grid, stream); break;
@@ -560,9 +717,9 @@ hipError_t launch_decode(const tq_codebook* kcb, const tq_codebook* vcb, const v
   ca.part_ml = part_ml;
   ca.rotV = vcb->dev.rot;
   ca.Hq = (int)plan.Hq; ca.Hkv = (int)plan.Hkv; ca.g = plan.g; ca.qgroups = plan.qgroups;
-  ca.n_parts = plan.n_parts;
+  ca.n_wg = plan.n_wg;
   ca.out = out;
-  hipLaunchKernelGGL(k_combine, dim3((unsigned)(plan.B * plan.Hq)), dim3(D), 0, stream, ca);
+  hipLaunchKernelGGL(k_combine, dim3((unsigned)plan.rows), dim3(256), 0, stream, ca);
   return hipGetLastError();
 }
 

@@ -49,9 +49,14 @@ __device__ inline float load_elem(const void* p, int64_t i) {
   }
 }
 
-__device__ inline int tile32_token(int s) {
-  const int g = s >> 3, i = s & 7;
-  return (i < 4) ? 4 * g + i : 16 + 4 * g + (i - 4);
+// tile32 element q of a block (q-th b-bit field of its bit stream) ->
+// (coordinate i, token t): q = (r*ndb + j)*8 + e, record r = 16*G + C holds
+// coordinate 16*j + C for the tokens 4*G + e%4 + 16*(e/4).
+__device__ inline void tile32_element(int q, int ndb, int& i, int& t) {
+  const int e = q & 7, rj = q >> 3;
+  const int j = rj % ndb, r = rj / ndb;
+  i = 16 * j + (r & 15);
+  t = 4 * (r >> 4) + (e & 3) + 16 * (e >> 2);
 }
 
 template <int DP, int DT>
@@ -227,31 +232,32 @@ __global__ void __launch_bounds__(512) k_quantize(QArgs a) {
         dst[w] = (uint32_t)(accw >> 32);
       }
     } else {
-      // tile32: per coordinate, b words; slot s holds token tile32_token(s)
+      // tile32: the block's bit stream is 64 records x ndb groups x 8 fields
       bool full = true;
       for (int r = 0; r < TILE; ++r) full = full && s_valid[r];
+      const int ndb = (a.d + 15) / 16;
+      const int words = 16 * ndb * b;                 // 64*ndb*b bytes
       uint32_t* dst = reinterpret_cast<uint32_t*>(a.idx) +
-                      (seq * (a.seq_stride / TILE) + blk) * (int64_t)a.d * b;
-      for (int e = tid; e < a.d * b; e += nthr) {
-        const int i = e / b, w = e % b;
+                      (seq * (a.seq_stride / TILE) + blk) * (int64_t)words;
+      for (int w = tid; w < words; w += nthr) {
         const int bit0 = 32 * w;
-        const int s0 = bit0 / b;
-        int s1 = (bit0 + 31) / b;
-        if (s1 > TILE - 1) s1 = TILE - 1;
+        const int q0 = bit0 / b;
+        const int q1 = (bit0 + 31) / b;
         uint64_t val = 0, msk = 0;
-        for (int s = s0; s <= s1; ++s) {
-          const int t = tile32_token(s);
-          const int sh = s * b - bit0 + 32;
+        for (int q = q0; q <= q1; ++q) {
+          int i, t;
+          tile32_element(q, ndb, i, t);
+          const int sh = q * b - bit0 + 32;
           if (s_valid[t]) {
-            val |= (uint64_t)ids[t][i] << sh;
+            if (i < a.d) val |= (uint64_t)ids[t][i] << sh;
             msk |= (uint64_t)((1u << b) - 1u) << sh;
           }
         }
         const uint32_t nv = (uint32_t)(val >> 32), nm = (uint32_t)(msk >> 32);
         if (full) {
-          dst[e] = nv;
+          dst[w] = nv;
         } else if (nm != 0u) {
-          dst[e] = (dst[e] & ~nm) | (nv & nm);
+          dst[w] = (dst[w] & ~nm) | (nv & nm);
         }
       }
     }
@@ -304,6 +310,7 @@ hipError_t launch_quantize(const tq_codebook* cb, const QuantJob& job, hipStream
   const int nw = waves_needed < 4 ? 4 : waves_needed;
   const int nthr = 64 * nw;
   int64_t grid = a.n_tiles < 2048 ? a.n_tiles : 2048;
+  ProfileScope prof(TQ_KERNEL_QUANTIZE, stream);
   switch (cb->dp) {
     case 32: return launch_dp<32>(a, job.dt, nthr, (int)grid, stream);
     case 64: return launch_dp<64>(a, job.dt, nthr, (int)grid, stream);

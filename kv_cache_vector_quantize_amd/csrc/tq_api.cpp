@@ -48,6 +48,8 @@ void free_dev(DeviceCodebook& d) {
   if (d.bnd) (void)hipFree(d.bnd);
   if (d.rot) (void)hipFree(d.rot);
   if (d.qjl) (void)hipFree(d.qjl);
+  if (d.rotT) (void)hipFree(d.rotT);
+  if (d.qjlT) (void)hipFree(d.qjlT);
   if (d.pair_tab) (void)hipFree(d.pair_tab);
   d = DeviceCodebook{};
 }
@@ -115,6 +117,33 @@ tq_status current_device_matches(const tq_codebook* cb) {
 
 void set_error(const std::string& msg) { g_err = msg; }
 
+namespace {
+struct EventPair { hipEvent_t a = nullptr, b = nullptr; };
+struct ProfileState {
+  bool on = false;
+  std::vector<EventPair> rec[2];
+  ~ProfileState() {
+    for (auto& v : rec)
+      for (auto& p : v) { (void)hipEventDestroy(p.a); (void)hipEventDestroy(p.b); }
+  }
+};
+thread_local ProfileState g_prof;
+}  // namespace
+
+ProfileScope::ProfileScope(int k, hipStream_t s) : kernel(k), stream(s) {
+  if (!g_prof.on) return;
+  EventPair p;
+  if (hipEventCreate(&p.a) != hipSuccess) return;
+  if (hipEventCreate(&p.b) != hipSuccess) { (void)hipEventDestroy(p.a); return; }
+  (void)hipEventRecord(p.a, stream);
+  g_prof.rec[kernel].push_back(p);
+  stop = p.b;
+}
+
+ProfileScope::~ProfileScope() {
+  if (stop) (void)hipEventRecord(static_cast<hipEvent_t>(stop), stream);
+}
+
 bool quantize_supported(const tq_codebook* cb);
 
 }  // namespace tq
@@ -145,11 +174,14 @@ tq_status tq_codebook_build(const tq_params* params, tq_codebook** out) {
     hipError_t e = hipGetDevice(&cb->device);
     if (e != hipSuccess) { delete cb; return hip_fail(e, "hipGetDevice"); }
     const int d = cb->p.d, dp = cb->dp, L = cb->L, m = cb->p.qjl_m, mp = cb->mp;
-    std::vector<float> cent(L), bnd(L - 1), rot((size_t)dp * dp, 0.f);
+    std::vector<float> cent(L), bnd(L - 1), rot((size_t)dp * dp, 0.f), rotT((size_t)dp * dp, 0.f);
     for (int k = 0; k < L; ++k) cent[k] = (float)cb->host.centroids[k];
     for (int k = 0; k < L - 1; ++k) bnd[k] = (float)cb->host.boundaries[k];
     for (int i = 0; i < d; ++i)
-      for (int j = 0; j < d; ++j) rot[(size_t)i * dp + j] = (float)cb->host.rot[(size_t)i * d + j];
+      for (int j = 0; j < d; ++j) {
+        rot[(size_t)i * dp + j] = (float)cb->host.rot[(size_t)i * d + j];
+        rotT[(size_t)j * dp + i] = (float)cb->host.rot[(size_t)i * d + j];
+      }
     std::vector<uint32_t> tab;
     if (cb->p.bits <= 4) {
       const int b = cb->p.bits;
@@ -175,16 +207,21 @@ tq_status tq_codebook_build(const tq_params* params, tq_codebook** out) {
     if ((e = upload(&cb->dev.cent, cent)) != hipSuccess ||
         (e = upload(&cb->dev.bnd, bnd.empty() ? std::vector<float>{0.f} : bnd)) != hipSuccess ||
         (e = upload(&cb->dev.rot, rot)) != hipSuccess ||
+        (e = upload(&cb->dev.rotT, rotT)) != hipSuccess ||
         (e = upload(&cb->dev.pair_tab, tab)) != hipSuccess) {
       free_dev(cb->dev);
       delete cb;
       return hip_fail(e, "codebook upload");
     }
     if (m > 0) {
-      std::vector<float> qjl((size_t)mp * dp, 0.f);
+      std::vector<float> qjl((size_t)mp * dp, 0.f), qjlT((size_t)dp * mp, 0.f);
       for (int j = 0; j < m; ++j)
-        for (int i = 0; i < d; ++i) qjl[(size_t)j * dp + i] = (float)cb->host.qjl[(size_t)j * d + i];
-      if ((e = upload(&cb->dev.qjl, qjl)) != hipSuccess) {
+        for (int i = 0; i < d; ++i) {
+          qjl[(size_t)j * dp + i] = (float)cb->host.qjl[(size_t)j * d + i];
+          qjlT[(size_t)i * mp + j] = (float)cb->host.qjl[(size_t)j * d + i];
+        }
+      if ((e = upload(&cb->dev.qjl, qjl)) != hipSuccess ||
+          (e = upload(&cb->dev.qjlT, qjlT)) != hipSuccess) {
         free_dev(cb->dev);
         delete cb;
         return hip_fail(e, "codebook upload");
@@ -330,6 +367,33 @@ tq_status tq_attn_decode(const tq_codebook* kcb, const tq_codebook* vcb, const v
   } catch (...) {
     return fail(TQ_ERR_ALLOC, "tq_attn_decode: unexpected exception");
   }
+}
+
+tq_status tq_profile_enable(int32_t on) {
+  if (on) {
+    for (auto& v : g_prof.rec) {
+      for (auto& p : v) { (void)hipEventDestroy(p.a); (void)hipEventDestroy(p.b); }
+      v.clear();
+    }
+  }
+  g_prof.on = on != 0;
+  return TQ_OK;
+}
+
+tq_status tq_profile_read(int32_t kernel, double* total_ms, int64_t* launches) {
+  if (kernel < 0 || kernel > 1) return fail(TQ_ERR_INVALID, "unknown kernel id");
+  double tot = 0.0;
+  for (auto& p : g_prof.rec[kernel]) {
+    hipError_t e = hipEventSynchronize(p.b);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, p.a, p.b);
+    if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+    tot += ms;
+  }
+  if (total_ms) *total_ms = tot;
+  if (launches) *launches = (int64_t)g_prof.rec[kernel].size();
+  return TQ_OK;
 }
 
 }  // extern "C"

@@ -27,6 +27,8 @@ struct DeviceCodebook {
   float* bnd = nullptr;     // [L-1] fp32
   float* rot = nullptr;     // [dp*dp] fp32 row-major Pi, zero-padded to dp
   float* qjl = nullptr;     // [mp*dp] fp32 row-major S, zero-padded (or null)
+  float* rotT = nullptr;    // [dp*dp] fp32, rotT[k][i] = Pi[i][k]
+  float* qjlT = nullptr;    // [dp*mp] fp32, qjlT[i][j] = S[j][i] (or null)
   // decode operand tables (bf16 hi/lo split of the centroids):
   //  bits <= 4: entry e = a | (b << bits) holds two dwords
   //             {hi(c[a]) | hi(c[b]) << 16, lo(c[a]) | lo(c[b]) << 16}
@@ -52,6 +54,15 @@ namespace tq {
 
 void set_error(const std::string& msg);
 
+// Instrumentation: hipEvent pairs around main-kernel launches (per thread).
+struct ProfileScope {
+  ProfileScope(int kernel, hipStream_t stream);
+  ~ProfileScope();
+  int kernel;
+  hipStream_t stream;
+  void* stop = nullptr;
+};
+
 // ---- kernels (launchers return hipSuccess or the launch error)
 
 struct QuantJob {
@@ -71,6 +82,7 @@ struct DecodePlan {
   int64_t rows;     // B * Hkv * qgroups (one row = one KV head and <= 8 query heads)
   int chunk;        // tokens per wave (multiple of 32)
   int n_parts;      // waves per row = ceil(n_ctx / chunk)
+  int n_wg;         // workgroups per row = ceil(n_parts / 4)
   size_t off_qop, off_part_o, off_part_ml, bytes;
 };
 

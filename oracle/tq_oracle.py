@@ -53,9 +53,10 @@ Readings where the pages are silent (each is listed in the design notes):
   - row layout: index i of a vector at bits [i*b, i*b+b) of a little-endian
     bit stream (bit p in byte p>>3, position p&7), row padded with zero bits
     to 4*b*ceil(d/32) bytes; sign j at bit j of a 4*ceil(m/32)-byte row.
-  - tile32 layout (value codes): per sequence, blocks of 32 tokens; per block
-    and coordinate i, a 32*b-bit little-endian stream (b 32-bit words) whose
-    slot s holds token tile32_token(s) of the block at bits [s*b, s*b+b).
+  - tile32 layout (value codes): per sequence, blocks of 32 tokens; inside a
+    block, the bit of (coordinate i, token t) is given by tile32_position:
+    64 records of 8 tokens x ceil(d/16) coordinates, so that one GPU lane
+    reads the codes of its 8 tokens for 8 coordinates as one contiguous run.
 """
 from __future__ import annotations
 
@@ -366,41 +367,56 @@ def unpack_signs(rows, m: int) -> np.ndarray:
                          bitorder="little")[:, :m]
 
 
-def tile32_token(s: int) -> int:
-    """Token (within a 32-token block) held by slot s of the tile32 layout."""
-    g, i = divmod(s, 8)
-    return 4 * g + i if i < 4 else 16 + 4 * g + (i - 4)
+def tile32_position(i: int, t: int, bits: int, d: int) -> int:
+    """Bit position of (coordinate i, token t in 0..31) inside a tile32 block.
+
+    The block is 64 records; record r = 16*G + C holds coordinates
+    i = 16*j + C (j = 0..ceil(d/16)-1, one b-byte group each) for the eight
+    token slots e = 0..7 of slot group G, where slot e holds token
+    4*G + (e % 4) + 16*(e // 4).  Inside the group, slot e is at bits
+    [e*b, e*b + b)."""
+    ndb = (d + 15) // 16
+    C, j = i % 16, i // 16
+    G = (t % 16) // 4
+    e = (t % 4) + 4 * (t // 16)
+    r = 16 * G + C
+    return ((r * ndb + j) * 8 + e) * bits
+
+
+def tile32_block_bytes(d: int, bits: int) -> int:
+    return 64 * ((d + 15) // 16) * bits
+
+
+def _tile32_positions(d: int, bits: int) -> np.ndarray:
+    """[32, d] bit positions of (token, coordinate) inside a block."""
+    return np.array([[tile32_position(i, t, bits, d) for i in range(d)] for t in range(32)],
+                    dtype=np.int64)
 
 
 def pack_tile32(idx, bits: int, n_blocks: int) -> np.ndarray:
-    """idx [n_tok, d] of one sequence -> uint8 [n_blocks, d, 4*bits].
-    Tokens >= n_tok leave zero bits."""
+    """idx [n_tok, d] of one sequence -> uint8 [n_blocks, block_bytes].
+    Tokens >= n_tok and padding coordinates leave zero bits."""
     idx = np.asarray(idx, dtype=np.int64)
     n_tok, d = idx.shape
-    out = np.zeros((n_blocks, d, 32 * bits), dtype=np.uint8)   # one byte per bit
-    for blk in range(n_blocks):
-        for s in range(32):
-            tok = blk * 32 + tile32_token(s)
-            if tok >= n_tok:
-                continue
-            for bb in range(bits):
-                out[blk, :, s * bits + bb] = (idx[tok] >> bb) & 1
-    return np.packbits(out, axis=2, bitorder="little")
+    pos = _tile32_positions(d, bits)
+    full = np.zeros((n_blocks * 32, d), dtype=np.int64)
+    full[:n_tok] = idx
+    full = full.reshape(n_blocks, 32, d)
+    out = np.zeros((n_blocks, tile32_block_bytes(d, bits) * 8), dtype=np.uint8)   # one byte per bit
+    for bb in range(bits):
+        out[:, (pos + bb).reshape(-1)] = ((full >> bb) & 1).reshape(n_blocks, -1)
+    return np.packbits(out, axis=1, bitorder="little")
 
 
 def unpack_tile32(blocks, d: int, bits: int, n_tok: int) -> np.ndarray:
     blocks = np.asarray(blocks, dtype=np.uint8)
-    n_blocks = blocks.shape[0]
-    bitarr = np.unpackbits(blocks, axis=2, bitorder="little").astype(np.int64)
-    out = np.zeros((n_blocks * 32, d), dtype=np.int64)
-    for blk in range(n_blocks):
-        for s in range(32):
-            tok = blk * 32 + tile32_token(s)
-            v = np.zeros(d, dtype=np.int64)
-            for bb in range(bits):
-                v |= bitarr[blk, :, s * bits + bb] << bb
-            out[tok] = v
-    return out[:n_tok]
+    nb = blocks.shape[0]
+    bitarr = np.unpackbits(blocks, axis=1, bitorder="little").astype(np.int64)
+    pos = _tile32_positions(d, bits).reshape(-1)
+    out = np.zeros((nb, 32 * d), dtype=np.int64)
+    for bb in range(bits):
+        out |= bitarr[:, pos + bb] << bb
+    return out.reshape(nb * 32, d)[:n_tok]
 
 
 # ---------------------------------------------------------------------------

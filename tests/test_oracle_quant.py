@@ -188,22 +188,30 @@ def test_pack_signs():
     assert np.array_equal(O.unpack_signs(rows, 40), s)
 
 
-def test_tile32_permutation_and_roundtrip():
-    perm = [O.tile32_token(s) for s in range(32)]
-    assert sorted(perm) == list(range(32))
-    assert perm[:8] == [0, 1, 2, 3, 16, 17, 18, 19]
+def test_tile32_layout_and_roundtrip():
+    # hand example: d = 16, b = 4 -> one coordinate group, record r = 16 G + C
+    # holds coordinate C for tokens 4G..4G+3 (slots 0-3) and 16+4G.. (4-7)
+    assert O.tile32_position(0, 0, 4, 16) == 0
+    assert O.tile32_position(0, 1, 4, 16) == 4
+    assert O.tile32_position(0, 16, 4, 16) == 16          # slot 4 of record 0
+    assert O.tile32_position(1, 0, 4, 16) == 32           # record 1 = coordinate 1
+    assert O.tile32_position(0, 4, 4, 16) == 16 * 32      # record 16 = group G=1
+    # d = 128: coordinate i = 16 j + C sits in group j of record 16 G + C
+    assert O.tile32_position(17, 5, 4, 128) == ((16 * 1 + 1) * 8 + 1) * 8 * 4 + 1 * 4
     rng = np.random.default_rng(8)
-    for b in (2, 3, 4, 8):
-        idx = rng.integers(0, 1 << b, size=(70, 6))
+    for d, b in ((128, 4), (128, 3), (40, 2), (16, 8), (5, 3)):
+        idx = rng.integers(0, 1 << b, size=(70, d))
         blocks = O.pack_tile32(idx, b, 3)
-        assert blocks.shape == (3, 6, 4 * b)
-        assert np.array_equal(O.unpack_tile32(blocks, 6, b, 70), idx)
-        # brute force on one block / coordinate
-        word = int.from_bytes(bytes(blocks[1, 2]), "little")
-        for s in range(32):
-            assert (word >> (s * b)) & ((1 << b) - 1) == idx[32 + perm[s], 2]
-        # tokens beyond 70 are zero bits
-        w2 = int.from_bytes(bytes(blocks[2, 0]), "little")
-        for s in range(32):
-            if 64 + perm[s] >= 70:
-                assert (w2 >> (s * b)) & ((1 << b) - 1) == 0
+        assert blocks.shape == (3, O.tile32_block_bytes(d, b))
+        assert np.array_equal(O.unpack_tile32(blocks, d, b, 70), idx)
+        # brute force on block 1 with python integers
+        word = int.from_bytes(bytes(blocks[1]), "little")
+        for t in range(32):
+            for i in range(d):
+                p = O.tile32_position(i, t, b, d)
+                assert (word >> p) & ((1 << b) - 1) == idx[32 + t, i]
+        # tokens beyond 70 leave zero bits
+        w2 = int.from_bytes(bytes(blocks[2]), "little")
+        for t in range(6, 32):
+            for i in range(d):
+                assert (w2 >> O.tile32_position(i, t, b, d)) & ((1 << b) - 1) == 0
