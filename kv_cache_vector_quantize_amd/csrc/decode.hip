@@ -77,13 +77,42 @@ struct PArgs {
   uint32_t* qop;          // [rows][QOP_DWORDS]
 };
 
-__device__ inline float load_q(const void* p, int dt, int64_t i) {
-  if (dt == TQ_F32) return static_cast<const float*>(p)[i];
-  if (dt == TQ_BF16) return __uint_as_float((uint32_t) static_cast<const uint16_t*>(p)[i] << 16);
-  return (float)static_cast<const _Float16*>(p)[i];
+// One workgroup (256 threads) per row: the 8 query slots share the
+// transposed rotation and sketch, both staged in LDS by one batch of
+// coalesced 16-byte loads; thread (i, half) owns coordinate i of queries
+// 4*half .. 4*half + 3.
+// A D-row matrix (row-major, `cols` floats per row, cols a multiple of 4 and
+// >= 4) is staged into LDS as dst[k][i], columns >= cols zero-filled.  The 16
+// loads of a thread are issued together (clamped addresses, no branches) and
+// stored once all have landed.
+struct Stage {
+  f32x4 r[16];
+};
+
+__device__ inline void stage_load(Stage& st, const float* src, int cols, int tid) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int e = tid + 256 * j;
+    const int k = e >> 5, i4 = (e & 31) * 4;
+    const int ic = i4 < cols ? i4 : cols - 4;
+    st.r[j] = *reinterpret_cast<const f32x4*>(src + (int64_t)k * cols + ic);
+  }
+}
+
+__device__ inline void stage_store(float (*dst)[D], const Stage& st, int cols, int tid) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int e = tid + 256 * j;
+    const int k = e >> 5, i4 = (e & 31) * 4;
+    f32x4 v = st.r[j];
+    if (i4 >= cols) v = f32x4{0.f, 0.f, 0.f, 0.f};
+    *reinterpret_cast<f32x4*>(&dst[k][i4]) = v;
+  }
 }
 
 __global__ void __launch_bounds__(256) k_prologue(PArgs a) {
+  __shared__ __align__(16) float mat[D][D];
+  __shared__ __align__(16) float mat2[D][D];
   __shared__ float qs[8][D];
   __shared__ float qt[8][D];
   __shared__ float tt[8][D];
@@ -92,18 +121,48 @@ __global__ void __launch_bounds__(256) k_prologue(PArgs a) {
   const int bh = row / a.qgroups;          // b * Hkv + h
   const int b = bh / a.Hkv, h = bh % a.Hkv;
   const int tid = threadIdx.x;
-  for (int e = tid; e < 8 * D; e += 256) {
-    const int c = e / D, i = e % D;
-    const int j = qg * 8 + c;
-    qs[c][i] = (j < a.g) ? load_q(a.q, a.qdt, ((int64_t)b * a.Hq + h * a.g + j) * D + i) : 0.f;
+  {
+    // thread tid loads coordinate tid % D of slots tid / D + 2 u, u < 4
+    int64_t off[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = qg * 8 + (tid >> 7) + 2 * u;
+      off[u] = ((int64_t)b * a.Hq + h * a.g + (j < a.g ? j : a.g - 1)) * D + (tid & (D - 1));
+    }
+    float v[4];
+    if (a.qdt == TQ_F32) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = static_cast<const float*>(a.q)[off[u]];
+    } else if (a.qdt == TQ_BF16) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = __uint_as_float((uint32_t) static_cast<const uint16_t*>(a.q)[off[u]] << 16);
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = (float)static_cast<const _Float16*>(a.q)[off[u]];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = (tid >> 7) + 2 * u;
+      qs[c][tid & (D - 1)] = (qg * 8 + c < a.g) ? v[u] : 0.f;
+    }
+  }
+  {
+    Stage st;
+    stage_load(st, a.rotKT, D, tid);
+    if (a.m > 0) {
+      Stage st2;
+      stage_load(st2, a.qjlKT, a.mp, tid);
+      stage_store(mat2, st2, a.mp, tid);
+    }
+    stage_store(mat, st, D, tid);
   }
   __syncthreads();
-  // thread (i, half): queries 4*half .. 4*half+3, coalesced over i
   const int i = tid & (D - 1), c0 = (tid >> 7) * 4;
   {
     float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll 8
     for (int k = 0; k < D; ++k) {
-      const float r = a.rotKT[k * D + i];
+      const float r = mat[k][i];
       s0 += r * qs[c0][k]; s1 += r * qs[c0 + 1][k]; s2 += r * qs[c0 + 2][k]; s3 += r * qs[c0 + 3][k];
     }
     qt[c0][i] = s0 * a.qscale; qt[c0 + 1][i] = s1 * a.qscale;
@@ -114,8 +173,9 @@ __global__ void __launch_bounds__(256) k_prologue(PArgs a) {
     const float cq = a.m > 0 ? 1.2533141373155003f / (float)a.m : 0.f;   // sqrt(pi/2)/m
     float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
     if (i < a.m) {
+#pragma unroll 8
       for (int k = 0; k < D; ++k) {
-        const float r = a.qjlKT[k * a.mp + i];
+        const float r = mat2[k][i];
         s0 += r * qt[c0][k]; s1 += r * qt[c0 + 1][k]; s2 += r * qt[c0 + 2][k]; s3 += r * qt[c0 + 3][k];
       }
     }
@@ -125,7 +185,7 @@ __global__ void __launch_bounds__(256) k_prologue(PArgs a) {
   uint32_t* dst = a.qop + (int64_t)row * QOP_DWORDS;
   // Q operand [u][lane][p]: MFMA u, lane group g4 covers dims 32*g4 + 4u .. +3;
   // dwords p = 0,1 -> dims (4u, 4u+1) (hi then lo slot of the key operand),
-  // p = 2,3 -> dims (4u+2, 4u+3).
+  // p = 2,3 -> dims (4u+2, 4u+3).  Columns 0-7 hold hi, 8-15 lo.
   for (int e = tid; e < QOP_Q; e += 256) {
     const int p = e & 3, lane = (e >> 2) & 63, u = e >> 8;
     const int col = lane & 15, g4 = lane >> 4, c = col & 7;
@@ -138,8 +198,8 @@ __global__ void __launch_bounds__(256) k_prologue(PArgs a) {
     }
     dst[e] = hv[0] | (hv[1] << 16);
   }
-  // T operand [c][lane][p]: element el of lane group g4, MFMA c holds sketch
-  // row j = 32*g4 + 4c + el/2 + 16*(el%2)
+  // T operand [cc][lane][p]: element el of lane group g4, MFMA cc holds sketch
+  // row 32*g4 + 4cc + el/2 + 16*(el%2)
   for (int e = tid; e < QOP_T; e += 256) {
     const int p = e & 3, lane = (e >> 2) & 63, cc = e >> 8;
     const int col = lane & 15, g4 = lane >> 4, c = col & 7;
@@ -152,17 +212,20 @@ __global__ void __launch_bounds__(256) k_prologue(PArgs a) {
     }
     dst[QOP_Q + e] = hv[0] | (hv[1] << 16);
   }
-  if (tid < 16) {
+  // QJL accumulator offsets: -sum_j (hi + lo) of t for the hi columns
+  if (tid < 64) {
+    const int c = tid >> 3, part = tid & 7;
     float s = 0.f;
-    if (tid < 8) {
-      for (int j = 0; j < D; ++j) {
-        const float v = tt[tid][j];
-        const float fh = __uint_as_float(bf16_rne_bits(v) << 16);
-        const float fl = __uint_as_float(bf16_rne_bits(v - fh) << 16);
-        s += fh + fl;
-      }
+    for (int j = part; j < D; j += 8) {
+      const float v = tt[c][j];
+      const float fh = __uint_as_float(bf16_rne_bits(v) << 16);
+      s += fh + __uint_as_float(bf16_rne_bits(v - fh) << 16);
     }
-    reinterpret_cast<float*>(dst)[QOP_Q + QOP_T + tid] = -s;
+    s += __shfl_xor(s, 1);
+    s += __shfl_xor(s, 2);
+    s += __shfl_xor(s, 4);
+    float* cinit = reinterpret_cast<float*>(dst) + QOP_Q + QOP_T;
+    if (part == 0) { cinit[c] = -s; cinit[c + 8] = 0.f; }
   }
 }
 
@@ -545,58 +608,81 @@ struct CArgs {
   float* out;          // [B][Hq][D]
 };
 
+// One workgroup (256 threads) per row.  The row's workgroup partials are
+// merged per query slot c with the usual max / rescale rule: the maximum and
+// the normaliser are reduced over all 256 threads (thread t visits partials
+// p = t/8 + 32 j of slot c = t%8), the per-partial factors 2^(M_p - M) go to
+// LDS, and thread (i, half) then sums coordinate i of slots 4*half .. +3 in
+// partial order.  Finally out = Pi_V^T o~ / l with Pi_V staged in LDS.
+constexpr int kMaxWg = 1024;   // plan_decode caps the partials of a row at 4096 / 4
+
 __global__ void __launch_bounds__(256) k_combine(CArgs a) {
+  __shared__ __align__(16) float mat[D][D];
+  __shared__ __align__(16) float scl[kMaxWg * 8];
   __shared__ float ov[8][D];
-  __shared__ float s_mx[8];
-  __shared__ float inv_l[8];
+  __shared__ float red[2][4][8];
   const int row = blockIdx.x;
   const int qg = row % a.qgroups;
   const int bh = row / a.qgroups;
   const int b = bh / a.Hkv, h = bh % a.Hkv;
-  const int tid = threadIdx.x;
-  const int64_t base = (int64_t)row * a.n_wg * 8;
-  // per query: max and normaliser over the workgroup partials (fixed order)
-  if (tid < 8) {
-    const int c = tid;
-    float Mx = -INFINITY;
-    for (int p = 0; p < a.n_wg; ++p) Mx = fmaxf(Mx, a.part_ml[(base + p * 8 + c) * 2]);
-    float ls = 0.f;
-    if (Mx != -INFINITY) {
-      for (int p = 0; p < a.n_wg; ++p) {
-        const float Mp = a.part_ml[(base + p * 8 + c) * 2];
-        if (Mp == -INFINITY) continue;
-        ls += __builtin_amdgcn_exp2f(Mp - Mx) * a.part_ml[(base + p * 8 + c) * 2 + 1];
-      }
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t base = (int64_t)row * a.n_wg * 8;       // record (p, c) = base + 8p + c
+  Stage st;
+  stage_load(st, a.rotV, D, tid);
+  const int cs = tid & 7;
+  float Mx = -INFINITY;
+  for (int p = tid >> 3; p < a.n_wg; p += 32) Mx = fmaxf(Mx, a.part_ml[(base + 8 * p + cs) * 2]);
+  Mx = fmaxf(Mx, __shfl_xor(Mx, 8));
+  Mx = fmaxf(Mx, __shfl_xor(Mx, 16));
+  Mx = fmaxf(Mx, __shfl_xor(Mx, 32));
+  if (lane < 8) red[0][wv][lane] = Mx;
+  __syncthreads();
+  Mx = fmaxf(fmaxf(red[0][0][cs], red[0][1][cs]), fmaxf(red[0][2][cs], red[0][3][cs]));
+  float ls = 0.f;
+  for (int p = tid >> 3; p < a.n_wg; p += 32) {
+    const float Mp = a.part_ml[(base + 8 * p + cs) * 2];
+    const float lp = a.part_ml[(base + 8 * p + cs) * 2 + 1];
+    const float f = (Mx == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(Mp - Mx);
+    scl[8 * p + cs] = f;
+    ls += f * lp;
+  }
+  ls += __shfl_xor(ls, 8);
+  ls += __shfl_xor(ls, 16);
+  ls += __shfl_xor(ls, 32);
+  if (lane < 8) red[1][wv][lane] = ls;
+  stage_store(mat, st, D, tid);
+  __syncthreads();
+  const int i = tid & (D - 1), c0 = (tid >> 7) * 4;
+  float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+  const float* po = a.part_o + (base + c0) * D + i;
+#pragma unroll 8
+  for (int p = 0; p < a.n_wg; ++p) {
+    const f32x4 f = *reinterpret_cast<const f32x4*>(&scl[8 * p + c0]);
+    const float* pp = po + (int64_t)p * 8 * D;
+    o0 += f[0] * pp[0];
+    o1 += f[1] * pp[D];
+    o2 += f[2] * pp[2 * D];
+    o3 += f[3] * pp[3 * D];
+  }
+  {
+    const float oo[4] = {o0, o1, o2, o3};
+    for (int k = 0; k < 4; ++k) {
+      const int c = c0 + k;
+      const float l = ((red[1][0][c] + red[1][1][c]) + red[1][2][c]) + red[1][3][c];
+      ov[c][i] = oo[k] * (l > 0.f ? 1.0f / l : 0.f);
     }
-    s_mx[c] = Mx;
-    inv_l[c] = (ls > 0.f) ? 1.0f / ls : 0.f;
   }
   __syncthreads();
-  for (int e = tid; e < 8 * D; e += 256) {
-    const int c = e / D, i = e % D;
-    const float Mx = s_mx[c];
-    float o = 0.f;
-    if (Mx != -INFINITY) {
-      for (int p = 0; p < a.n_wg; ++p) {
-        const float Mp = a.part_ml[(base + p * 8 + c) * 2];
-        if (Mp == -INFINITY) continue;
-        o += __builtin_amdgcn_exp2f(Mp - Mx) * a.part_o[(base + p * 8 + c) * D + i];
-      }
-    }
-    ov[c][i] = o * inv_l[c];
-  }
-  __syncthreads();
-  // out = Pi_V^T o~ : out_j = sum_i Pi_V[i][j] o~_i (coalesced over j)
-  const int j = tid & (D - 1), c0 = (tid >> 7) * 4;
   float r0 = 0.f, r1 = 0.f, r2 = 0.f, r3 = 0.f;
-  for (int i = 0; i < D; ++i) {
-    const float pv = a.rotV[i * D + j];
-    r0 += pv * ov[c0][i]; r1 += pv * ov[c0 + 1][i]; r2 += pv * ov[c0 + 2][i]; r3 += pv * ov[c0 + 3][i];
+#pragma unroll 8
+  for (int k = 0; k < D; ++k) {
+    const float pv = mat[k][i];
+    r0 += pv * ov[c0][k]; r1 += pv * ov[c0 + 1][k]; r2 += pv * ov[c0 + 2][k]; r3 += pv * ov[c0 + 3][k];
   }
   const float rr[4] = {r0, r1, r2, r3};
   for (int k = 0; k < 4; ++k) {
     const int jq = qg * 8 + c0 + k;
-    if (jq < a.g) a.out[((int64_t)b * a.Hq + h * a.g + jq) * D + j] = rr[k];
+    if (jq < a.g) a.out[((int64_t)b * a.Hq + h * a.g + jq) * D + i] = rr[k];
   }
 }
 
@@ -658,6 +744,7 @@ hipError_t launch_decode(const tq_codebook* kcb, const tq_codebook* vcb, const v
   float* part_o = reinterpret_cast<float*>(w + plan.off_part_o);
   float* part_ml = reinterpret_cast<float*>(w + plan.off_part_ml);
   if (plan.rows == 0) return hipSuccess;
+  if (plan.n_wg > kMaxWg) return hipErrorInvalidValue;
 
   PArgs pa{};
   pa.q = q; pa.qdt = qdt;

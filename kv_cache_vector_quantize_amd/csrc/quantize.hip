@@ -265,6 +265,164 @@ __global__ void __launch_bounds__(512) k_quantize(QArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- appends
+//
+// Few vectors (decode-time appends): one wave per vector.  Lane l owns
+// coordinates l and l + 64; y = Pi x / |x| and u = S r are matrix-vector
+// products over the transposed matrices (coalesced rows), with the input
+// coordinate broadcast from the lane that holds it.  tile32 fields of
+// different vectors can share a 32-bit word, so they are updated with an
+// atomic AND (clear) and an atomic OR (set).
+
+struct SmallJob {
+  const void* x;
+  int64_t n_tok, tok_off;
+  int d, bits, m, nc, layout, dp, mp;
+  const float* cent;
+  const float* bnd;
+  const float* rotT;  // [dp][dp], rotT[k][i] = Pi[i][k]
+  const float* qjlT;  // [dp][mp], qjlT[i][j] = S[j][i]
+  uint8_t* idx;
+  uint32_t* sign;
+  float* scale;
+  float* rnorm;
+  int64_t idx_pitch, sign_pitch, seq_stride;
+};
+
+struct SmallArgs {
+  SmallJob job[2];
+};
+
+__device__ inline float wave_sum(float v) {
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+template <int DT>
+__global__ void __launch_bounds__(512) k_quantize_small(SmallArgs sa) {
+  // One 512-thread workgroup per vector: thread (i, kq) = (tid % 128,
+  // tid / 128) forms the partial product of output coordinate i over the
+  // input coordinates 32 kq .. 32 kq + 31, so every matrix load of a thread is
+  // independent and issued together; the four partials are summed in LDS in a
+  // fixed order.
+  const SmallJob& a = sa.job[blockIdx.y];
+  __shared__ float xs[128];
+  __shared__ float part[4][128];
+  __shared__ float rs[128];
+  __shared__ uint8_t ids[128];
+  __shared__ float red[2][2];
+  const int64_t vec = blockIdx.x;                 // seq * n_tok + t
+  const int64_t seq = vec / a.n_tok, t = vec % a.n_tok;
+  const int64_t pos = a.tok_off + t;              // position in the sequence
+  const int64_t row = seq * a.seq_stride + pos;
+  const int tid = threadIdx.x;
+  const int i = tid & 127, kq = tid >> 7, l = tid & 63, w = tid >> 6;
+  if (tid < 128) xs[tid] = (tid < a.d) ? load_elem<DT>(a.x, vec * a.d + tid) : 0.f;
+  __syncthreads();
+  const float n = sqrtf(wave_sum(xs[l] * xs[l] + xs[l + 64] * xs[l + 64]));
+  const float inv = n > 0.f ? 1.0f / n : 0.f;
+  {
+    float z = 0.f;
+    if (i < a.dp) {
+#pragma unroll
+      for (int kk = 0; kk < 32; ++kk) {
+        const int k = 32 * kq + kk;
+        const int kc = k < a.d ? k : a.d - 1;     // xs[k] = 0 beyond d
+        z += a.rotT[kc * a.dp + i] * xs[k];
+      }
+    }
+    part[kq][i] = z;
+  }
+  __syncthreads();
+  float y = 0.f, c = 0.f;
+  if (tid < 128) {
+    y = (((part[0][i] + part[1][i]) + part[2][i]) + part[3][i]) * inv;
+    const int L = 1 << a.bits;
+    int q = 0;
+    for (int step = L >> 1; step >= 1; step >>= 1)
+      if (y >= a.bnd[q + step - 1]) q += step;
+    c = (i < a.d) ? a.cent[q] : 0.f;
+    if (i < a.d) ids[i] = (uint8_t)q;
+    const float s2 = wave_sum(c * c);
+    if (l == 0) red[0][w] = s2;
+  }
+  __syncthreads();
+  const float nh = sqrtf(red[0][0] + red[0][1]);
+  const float sc = a.nc ? n / nh : n;
+  if (a.m > 0) {
+    if (tid < 128) {
+      const float f = a.nc ? 1.0f / nh : 1.0f;
+      const float r = (i < a.d) ? y - c * f : 0.f;
+      rs[i] = r;
+      const float s2 = wave_sum(r * r);
+      if (l == 0) red[1][w] = s2;
+    }
+    __syncthreads();
+    {
+      float u = 0.f;
+      if (i < a.m) {
+#pragma unroll
+        for (int kk = 0; kk < 32; ++kk) {
+          const int k = 32 * kq + kk;
+          const int kc = k < a.d ? k : a.d - 1;   // rs[k] = 0 beyond d
+          u += a.qjlT[kc * a.mp + i] * rs[k];
+        }
+      }
+      part[kq][i] = u;
+    }
+    __syncthreads();
+    if (tid < 128) {
+      const float u = ((part[0][i] + part[1][i]) + part[2][i]) + part[3][i];
+      const unsigned long long bb = __ballot(u >= 0.f);
+      uint32_t* srow = a.sign + ((row * a.sign_pitch) >> 2);
+      const int words = (a.m + 31) / 32;
+      const int wd = 2 * w + l;                     // word of this wave's half
+      if (l < 2 && wd < words) {
+        uint32_t wv = (uint32_t)(bb >> (32 * l));
+        const int nbits = a.m - 32 * wd;
+        if (nbits < 32) wv &= (1u << nbits) - 1u;
+        srow[wd] = wv;
+      }
+      if (tid == 0) a.rnorm[row] = n * sqrtf(red[1][0] + red[1][1]);
+    }
+  }
+  if (tid == 0) a.scale[row] = sc;
+  __syncthreads();
+  const int b = a.bits;
+  if (a.layout == TQ_LAYOUT_ROW) {
+    const int W = b * a.dp / 32;
+    uint32_t* dst = reinterpret_cast<uint32_t*>(a.idx + row * a.idx_pitch);
+    for (int wd = tid; wd < W; wd += 512) {
+      const int bit0 = 32 * wd;
+      const int j0 = bit0 / b;
+      int j1 = (bit0 + 31) / b;
+      if (j1 > a.d - 1) j1 = a.d - 1;
+      uint64_t acc = 0;
+      for (int j = j0; j <= j1; ++j) acc |= (uint64_t)ids[j] << (j * b - bit0 + 32);
+      dst[wd] = (uint32_t)(acc >> 32);
+    }
+  } else {
+    const int ndb = (a.d + 15) / 16;
+    const int words = 16 * ndb * b;
+    uint32_t* dst = reinterpret_cast<uint32_t*>(a.idx) + (seq * (a.seq_stride / 32) + pos / 32) * (int64_t)words;
+    const int tt = (int)(pos & 31);
+    const int G = (tt & 15) >> 2, e = (tt & 3) + 4 * (tt >> 4);
+    if (tid < a.d) {
+      const int r = 16 * G + (tid & 15), j = tid >> 4;
+      const int bit = ((r * ndb + j) * 8 + e) * b;
+      const uint64_t v = (uint64_t)ids[tid] << (bit & 31);
+      const uint64_t mk = (uint64_t)((1u << b) - 1u) << (bit & 31);
+      const int wd = bit >> 5;
+      atomicAnd(dst + wd, ~(uint32_t)mk);
+      atomicOr(dst + wd, (uint32_t)v);
+      if ((mk >> 32) != 0) {
+        atomicAnd(dst + wd + 1, ~(uint32_t)(mk >> 32));
+        atomicOr(dst + wd + 1, (uint32_t)(v >> 32));
+      }
+    }
+  }
+}
+
 template <int DP>
 hipError_t launch_dp(const QArgs& a, int dt, int nthr, int grid, hipStream_t st) {
   switch (dt) {
@@ -276,6 +434,37 @@ hipError_t launch_dp(const QArgs& a, int dt, int nthr, int grid, hipStream_t st)
 }
 
 }  // namespace
+
+static SmallJob make_small_job(const tq_codebook* cb, const QuantJob& job) {
+  SmallJob s{};
+  s.x = job.x;
+  s.n_tok = job.n_tok;
+  s.tok_off = job.tok_offset;
+  s.d = cb->p.d; s.bits = cb->p.bits; s.m = cb->p.qjl_m; s.nc = cb->p.norm_correction;
+  s.layout = job.out.layout; s.dp = cb->dp; s.mp = cb->mp;
+  s.cent = cb->dev.cent; s.bnd = cb->dev.bnd; s.rotT = cb->dev.rotT; s.qjlT = cb->dev.qjlT;
+  s.idx = static_cast<uint8_t*>(job.out.idx);
+  s.sign = static_cast<uint32_t*>(job.out.sign);
+  s.scale = job.out.scale; s.rnorm = job.out.rnorm;
+  s.idx_pitch = job.out.idx_row_bytes; s.sign_pitch = job.out.sign_row_bytes;
+  s.seq_stride = job.out.seq_stride;
+  return s;
+}
+
+hipError_t launch_quantize_small(const tq_codebook* const* cbs, const QuantJob* jobs, int njobs,
+                                 hipStream_t stream) {
+  SmallArgs sa{};
+  for (int t = 0; t < njobs; ++t) sa.job[t] = make_small_job(cbs[t], jobs[t]);
+  const int64_t nvec = jobs[0].n_seq * jobs[0].n_tok;
+  const dim3 grid((unsigned)nvec, (unsigned)njobs);
+  ProfileScope prof(TQ_KERNEL_QUANTIZE, stream);
+  switch (jobs[0].dt) {
+    case TQ_F32: hipLaunchKernelGGL(k_quantize_small<TQ_F32>, grid, dim3(512), 0, stream, sa); break;
+    case TQ_BF16: hipLaunchKernelGGL(k_quantize_small<TQ_BF16>, grid, dim3(512), 0, stream, sa); break;
+    default: hipLaunchKernelGGL(k_quantize_small<TQ_F16>, grid, dim3(512), 0, stream, sa); break;
+  }
+  return hipGetLastError();
+}
 
 bool quantize_supported(const tq_codebook* cb) {
   return cb->dp <= 128 && (cb->p.qjl_m == 0 || cb->mp <= 128);

@@ -305,6 +305,19 @@ tq_status tq_quantize_kv(const tq_codebook* kcb, const tq_codebook* vcb, const v
       s = current_device_matches(cbs[t]);
       if (s != TQ_OK) return s;
     }
+    if (n_tok <= kSmallMaxTok && n_seq * n_tok <= 0x7FFFFFFF) {
+      const tq_codebook* sc[2];
+      QuantJob sj[2];
+      int nj = 0;
+      for (int t = 0; t < 2; ++t) {
+        if (!xs[t]) continue;
+        sc[nj] = cbs[t];
+        sj[nj++] = QuantJob{xs[t], dt, n_seq, n_tok, tok_offset, *outs[t]};
+      }
+      hipError_t e = launch_quantize_small(sc, sj, nj, static_cast<hipStream_t>(stream));
+      if (e != hipSuccess) return hip_fail(e, "quantize launch");
+      return TQ_OK;
+    }
     for (int t = 0; t < 2; ++t) {
       if (!xs[t]) continue;
       QuantJob job{xs[t], dt, n_seq, n_tok, tok_offset, *outs[t]};

@@ -74,6 +74,12 @@ struct QuantJob {
 
 hipError_t launch_quantize(const tq_codebook* cb, const QuantJob& job, hipStream_t stream);
 
+// Few vectors per sequence (appends): one wave per vector; K and V jobs in
+// one launch.  njobs in 1..2, jobs share n_seq, n_tok and dtype.
+hipError_t launch_quantize_small(const tq_codebook* const* cbs, const QuantJob* jobs, int njobs,
+                                 hipStream_t stream);
+constexpr int64_t kSmallMaxTok = 8;   // appends of up to this many tokens per sequence
+
 struct DecodePlan {
   int64_t B, Hq, Hkv, n_ctx;
   int d;

@@ -134,6 +134,44 @@ def test_quantize_tile32_parity_and_append(dev, bits):
                 assert np.array_equal(ib[blk], exp[blk])
 
 
+@pytest.mark.parametrize("d,bits,m,nc,layout,n_tok", [
+    (128, 3, 128, False, TQ_LAYOUT_ROW, 1),
+    (128, 4, 0, False, TQ_LAYOUT_TILE32, 1),
+    (128, 3, 0, True, TQ_LAYOUT_TILE32, 3),
+    (128, 8, 0, False, TQ_LAYOUT_TILE32, 8),
+    (96, 2, 40, True, TQ_LAYOUT_ROW, 5),
+    (64, 4, 64, False, TQ_LAYOUT_ROW, 2),
+    (40, 5, 0, False, TQ_LAYOUT_TILE32, 1),
+])
+def test_quantize_append_path(dev, d, bits, m, nc, layout, n_tok):
+    """Appends of a few tokens per sequence at unaligned offsets (the
+    decode-time path), on top of a cache written by the bulk path."""
+    _say("quantize append", d, bits, m, nc, layout, n_tok)
+    n_seq, base = 3, 70
+    cb = tq.Codebook(d, bits, qjl_m=m, norm_correction=nc, rot_seed=7, qjl_seed=8)
+    codes = tq.Codes(cb, n_seq, 96, layout)
+    x = synth.kv_gaussian(1, n_seq, base + 2 * n_tok, d, 21, dtype="bf16", device="cpu",
+                          channels=[i for i in (3, 77) if i < d], factor=20.0)[0]
+    tq.tq_quantize_kv(cb, None, x[:, :base].contiguous().to(dev), None, codes, None, tok_offset=0)
+    tq.tq_quantize_kv(cb, None, x[:, base:base + n_tok].contiguous().to(dev), None, codes, None, tok_offset=base)
+    # re-append over already written positions (must replace, not OR)
+    tq.tq_quantize_kv(cb, None, x[:, base + n_tok:base + 2 * n_tok].contiguous().to(dev), None, codes, None,
+                      tok_offset=base)
+    torch.cuda.synchronize()
+    total = base + n_tok
+    expect = torch.cat([x[:, :base], x[:, base + n_tok:base + 2 * n_tok]], dim=1)
+    got = U.read_codes(codes, total)
+    flat = dict(idx=got["idx"].reshape(-1, d), scale=got["scale"].reshape(-1),
+                sign=None if got["sign"] is None else got["sign"].reshape(-1, m),
+                rnorm=None if got["rnorm"] is None else got["rnorm"].reshape(-1))
+    st, _ = U.compare_quant(U.oracle_codebook(cb), expect.float().numpy().astype(np.float64).reshape(-1, d),
+                            flat, name="append")
+    if layout == TQ_LAYOUT_TILE32:
+        assert np.all(U.read_tile32(U.seq_bytes(codes, 1, 96)[0], d, bits, 96)[total:] == 0)
+    st.pop("vec_ok")
+    print(st)
+
+
 def test_quantize_rows_offset_and_untouched(dev):
     d, bits = 128, 4
     _say("quantize rows with offset")
