@@ -41,6 +41,7 @@ constexpr int D = 128;                 // head dimension of this kernel family
 constexpr int QOP_Q = 8 * 64 * 4;      // Q operand dwords: 8 MFMAs x 64 lanes x 4
 constexpr int QOP_T = 4 * 64 * 4;      // T operand dwords
 constexpr int QOP_DWORDS = QOP_Q + QOP_T + 16;
+constexpr int kSignShift = 64;    // the sketch-query operand carries 2^-kSignShift
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 constexpr float LAZY = 8.0f;           // max moves when a tile exceeds it by 2^8
@@ -198,21 +199,27 @@ __global__ void __launch_bounds__(256) k_prologue(PArgs a) {
     }
     dst[e] = hv[0] | (hv[1] << 16);
   }
-  // T operand [cc][lane][p]: element el of lane group g4, MFMA cc holds sketch
-  // row 32*g4 + 4cc + el/2 + 16*(el%2)
+  // T operand [cc][lane][p]: dword p of MFMA cc faces sign dword K = 4cc + p
+  // of lane group g4, whose low / high halves hold sign bits jl / jh at bf16
+  // bit P; the entry is t of sketch row 32*g4 + j times 2^(128 - 2^(P-7)) and
+  // 2^-kSignShift (exact power-of-two scalings).
   for (int e = tid; e < QOP_T; e += 256) {
     const int p = e & 3, lane = (e >> 2) & 63, cc = e >> 8;
     const int col = lane & 15, g4 = lane >> 4, c = col & 7;
+    const int K = 4 * cc + p;
+    const int P = (K < 8) ? 14 - K : 22 - K;
+    const int ex = 128 - (1 << (P - 7)) - kSignShift;
     uint32_t hv[2];
     for (int h2 = 0; h2 < 2; ++h2) {
-      const int el = 2 * p + h2;
-      const float v = tt[c][32 * g4 + 4 * cc + (el >> 1) + 16 * (el & 1)];
+      const int j = h2 ? 30 - K : (K == 15 ? 31 : 14 - K);
+      const float v = ldexpf(tt[c][32 * g4 + j], ex);
       const uint32_t hi = bf16_rne_bits(v);
       hv[h2] = (col >= 8) ? bf16_rne_bits(v - __uint_as_float(hi << 16)) : hi;
     }
     dst[QOP_Q + e] = hv[0] | (hv[1] << 16);
   }
-  // QJL accumulator offsets: -sum_j (hi + lo) of t for the hi columns
+  // QJL accumulator offsets: -sum_j (hi + lo) of t for the hi columns, in the
+  // scale of the sign products (2^-kSignShift)
   if (tid < 64) {
     const int c = tid >> 3, part = tid & 7;
     float s = 0.f;
@@ -225,7 +232,7 @@ __global__ void __launch_bounds__(256) k_prologue(PArgs a) {
     s += __shfl_xor(s, 2);
     s += __shfl_xor(s, 4);
     float* cinit = reinterpret_cast<float*>(dst) + QOP_Q + QOP_T;
-    if (part == 0) { cinit[c] = -s; cinit[c + 8] = 0.f; }
+    if (part == 0) { cinit[c] = -ldexpf(s, -kSignShift); cinit[c + 8] = 0.f; }
   }
 }
 
@@ -266,27 +273,59 @@ __device__ inline uint32_t field(const uint32_t (&wd)[NW], int off, int w) {
 template <int B>
 constexpr int table_entries() { return (B <= 4) ? (1 << (2 * B)) : (1 << B); }
 
-// hi and lo operand dwords of two codes from the table in LDS: for B <= 4
-// entry e = a | b << B is the dword pair {hi(c[a]) | hi(c[b]) << 16,
-// lo(c[a]) | lo(c[b]) << 16} (one 64-bit read lands both in consecutive
-// registers); for B > 4 a single-code table holds hi | lo << 16.
-template <int B>
-__device__ inline uint2 lookup(const uint32_t* tab, uint32_t pair) {
+// Random 8-byte reads of one small table from all 64 lanes collide in the LDS
+// banks (a read of 8 bytes serves 32 lanes per pass).  A pair table can
+// therefore be held as kCopies interleaved copies: entry e of copy c at byte
+// e * 256 + c * 8, and lane l reads copy l % 32, so the 32 lanes of a pass
+// always hit 32 distinct bank pairs.
+constexpr int kWaves = 8;                  // waves per split workgroup
+constexpr int kCopies = 32;
+constexpr int kCopyBudget = 80 * 1024;     // LDS bytes for the two tables
+
+constexpr int table_entries_rt(int b) { return (b <= 4) ? (1 << (2 * b)) : (1 << b); }
+constexpr int plain_bytes(int b) { return (b <= 4) ? table_entries_rt(b) * 8 : table_entries_rt(b) * 4; }
+
+template <int BK, int BV>
+struct SplitLds {
+  static constexpr bool VC = BV <= 4 && table_entries_rt(BV) * 8 * kCopies <= kCopyBudget;
+  static constexpr int VBYTES = VC ? table_entries_rt(BV) * 8 * kCopies : plain_bytes(BV);
+  static constexpr bool KC = BK <= 4 && VBYTES + table_entries_rt(BK) * 8 * kCopies <= kCopyBudget;
+  static constexpr int KBYTES = KC ? table_entries_rt(BK) * 8 * kCopies : plain_bytes(BK);
+  static constexpr int OBYTES = kWaves * 8 * D * 4;    // merge buffer, aliases the tables
+  static constexpr int RAW = (KBYTES + VBYTES > OBYTES) ? KBYTES + VBYTES : OBYTES;
+};
+
+// hi and lo operand dwords of two codes: for B <= 4 entry e = a | b << B is
+// the dword pair {hi(c[a]) | hi(c[b]) << 16, lo(c[a]) | lo(c[b]) << 16} (one
+// 64-bit read lands both in consecutive registers), read from the lane's copy
+// when the table is interleaved; for B > 4 a single-code table holds
+// hi | lo << 16.
+template <int B, bool COPIED>
+__device__ inline uint2 lookup(const char* tab, uint32_t pair, uint32_t laneoff) {
   if constexpr (B <= 4) {
-    return reinterpret_cast<const uint2*>(tab)[pair];
+    if constexpr (COPIED) return *reinterpret_cast<const uint2*>(tab + ((pair << 8) | laneoff));
+    else return *reinterpret_cast<const uint2*>(tab + (pair << 3));
   } else {
-    const uint32_t e0 = tab[pair & ((1u << B) - 1u)];
-    const uint32_t e1 = tab[pair >> B];
+    const uint32_t* t = reinterpret_cast<const uint32_t*>(tab);
+    const uint32_t e0 = t[pair & ((1u << B) - 1u)];
+    const uint32_t e1 = t[pair >> B];
     return make_uint2(__builtin_amdgcn_perm(e1, e0, 0x05040100u),
                       __builtin_amdgcn_perm(e1, e0, 0x07060302u));
   }
 }
 
-// sign operand dword: bits x and x+16 of w at positions 14 and 30 (bf16 2.0)
-template <int X>
-__device__ inline uint32_t sign_pair(uint32_t w) {
-  if constexpr (X <= 14) return (w << (14 - X)) & 0x40004000u;
-  else return (w >> (X - 14)) & 0x40004000u;
+// Sign operand dword K (0..15) of a lane's 32 sign bits w (r = w rotated
+// left by 8): one bit per bf16 half, left where it lies.  A single set bit at
+// position P (7..14) of a half is the normal bf16 2^(2^(P-7) - 127); the
+// matching entry of the sketch-query operand is pre-scaled by 2 / that value
+// times 2^-kSignShift, so every product is exactly 2 t_j sigma_j 2^-kSignShift.
+// Dword K < 8 takes bits 14-K and 30-K of w at P = 14-K; dword K >= 8 takes
+// bits 14-K (31 for K = 15) and 30-K through r at P = 22-K.
+template <int K>
+__device__ inline uint32_t sgn(uint32_t w, uint32_t r) {
+  constexpr int P = (K < 8) ? 14 - K : 22 - K;
+  constexpr uint32_t m = (1u << P) | (1u << (P + 16));
+  return ((K < 8) ? w : r) & m;
 }
 
 // Value-code group db (8 token slots of one coordinate) from a lane's tile32
@@ -314,22 +353,30 @@ struct Tile {
 };
 
 template <int BK, int BV, bool QJL>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) k_split(SArgs a) {
-  constexpr int KE = table_entries<BK>(), VE = table_entries<BV>();
-  constexpr int KTD = (BK <= 4) ? 2 * KE : KE, VTD = (BV <= 4) ? 2 * VE : VE;   // dwords
-  __shared__ __align__(16) uint32_t s_kt[KTD];
-  __shared__ __align__(16) uint32_t s_vt[VTD];
-  __shared__ __align__(16) float s_sc[4][96];     // per wave: kscale[32], rnorm[32], vscale[32]
-  __shared__ float s_M[4][8], s_l[4][8];
-  __shared__ __align__(16) float s_o[4][8][D];
+__global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) k_split(SArgs a) {
+  using L = SplitLds<BK, BV>;
+  constexpr int NT = 64 * kWaves;
+  __shared__ __align__(16) char s_raw[L::RAW];              // tables; merge buffer afterwards
+  __shared__ __align__(16) float s_sc[kWaves][96];          // per wave: kscale[32], rnorm[32], vscale[32]
+  __shared__ float s_M[kWaves][8], s_l[kWaves][8];
+  const char* s_kt = s_raw;
+  const char* s_vt = s_raw + L::KBYTES;
   const int tid = threadIdx.x;
-  for (int i = tid; i < KTD; i += 256) s_kt[i] = a.ktab[i];
-  for (int i = tid; i < VTD; i += 256) s_vt[i] = a.vtab[i];
+  {
+    // interleaved copy i of 8-byte entry i / 32 sits at byte 8 i
+    const uint2* kt = reinterpret_cast<const uint2*>(a.ktab);
+    const uint2* vt = reinterpret_cast<const uint2*>(a.vtab);
+    uint2* dk = reinterpret_cast<uint2*>(s_raw);
+    uint2* dv = reinterpret_cast<uint2*>(s_raw + L::KBYTES);
+    for (int i = tid; i < L::KBYTES / 8; i += NT) dk[i] = kt[L::KC ? (i >> 5) : i];
+    for (int i = tid; i < L::VBYTES / 8; i += NT) dv[i] = vt[L::VC ? (i >> 5) : i];
+  }
   __syncthreads();
 
   const int wave = tid >> 6, lane = tid & 63;
   const int c16 = lane & 15, g4 = lane >> 4;
-  const int part = blockIdx.x * 4 + wave;
+  const int part = blockIdx.x * kWaves + wave;
+  const uint32_t laneoff = (uint32_t)(lane & 31) << 3;
   const int row = blockIdx.y;
   const int qg = row % a.qgroups;
   const int bh = row / a.qgroups;
@@ -353,6 +400,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
   const float cinit = QJL ? reinterpret_cast<const float*>(a.qop + (int64_t)row * QOP_DWORDS)[QOP_Q + QOP_T + c16] : 0.f;
   const float sel_lo = (c16 >= 8) ? 1.f : 0.f;
+  static_assert(kSignShift == 64, "sc0mul below is 2^kSignShift");
+  const float sc0mul = (QJL && lane >= 32) ? 0x1p64f : 1.f;     // 2^kSignShift on the residual norms
 
   float M = -INFINITY, l = 0.f;
   f32x4 acc_o[8];
@@ -405,38 +454,78 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     T.sc1 = sc1base[t32];
   };
 
+  // value operands of coordinate block db (4 lookups = token slot pairs)
+  auto vlook = [&](const Tile<BK, BV>& T, const int db, uint2 (&e)[4]) {
+    uint32_t fhi;
+    const uint32_t f = vgroup<BV>(T.vr, db, fhi);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if constexpr (BV == 4 && L::VC) {
+        // byte q of f is the pair index: (index << 8) | laneoff in one byte permute
+        const uint32_t addr = __builtin_amdgcn_perm(f, laneoff, 0x0C0C0000u | ((4u + q) << 8));
+        e[q] = *reinterpret_cast<const uint2*>(s_vt + addr);
+      } else {
+        uint32_t pr;
+        if constexpr (BV == 8) pr = ((q < 2 ? f : fhi) >> (16 * (q & 1))) & 0xFFFFu;
+        else pr = (f >> (2 * q * BV)) & ((1u << (2 * BV)) - 1u);
+        e[q] = lookup<BV, L::VC>(s_vt, pr, laneoff);
+      }
+    }
+  };
+
   auto compute = [&](const Tile<BK, BV>& T, const int64_t t0, auto partial_tag) {
     constexpr bool partial = decltype(partial_tag)::value;
-    // per-token scalars: 96 floats through the wave's LDS slot
-    stage[lane] = T.sc0;
+    // per-token scalars: 96 floats through the wave's LDS slot (the residual
+    // norms carry back the power of two the sign operand takes out)
+    stage[lane] = T.sc0 * sc0mul;
     stage[64 + (lane & 31)] = T.sc1;
-    // ---- logits S^T: rows = tokens 4*g4 + r (+16 for block 1), cols = query hi/lo
+    // ---- key operands of block 0: all 16 lookups in flight
+    uint2 ek[8][2];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      ek[u][0] = lookup<BK, L::KC>(s_kt, field<BK>(T.kw[0], (4 * u) * BK, 2 * BK), laneoff);
+      ek[u][1] = lookup<BK, L::KC>(s_kt, field<BK>(T.kw[0], (4 * u + 2) * BK, 2 * BK), laneoff);
+    }
+    // ---- QJL sign products (VALU work while the lookups land)
+    f32x4 accq[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      accq[blk] = (f32x4){cinit, cinit, cinit, cinit};
+      if constexpr (QJL) {
+        const uint32_t w = T.sw[blk];
+        const uint32_t r = __builtin_amdgcn_alignbit(w, w, 24);     // w rotated left by 8
+        accq[blk] = mfma(as_bf16x8(sgn<0>(w, r), sgn<1>(w, r), sgn<2>(w, r), sgn<3>(w, r)), ta[0], accq[blk]);
+        accq[blk] = mfma(as_bf16x8(sgn<4>(w, r), sgn<5>(w, r), sgn<6>(w, r), sgn<7>(w, r)), ta[1], accq[blk]);
+        accq[blk] = mfma(as_bf16x8(sgn<8>(w, r), sgn<9>(w, r), sgn<10>(w, r), sgn<11>(w, r)), ta[2], accq[blk]);
+        accq[blk] = mfma(as_bf16x8(sgn<12>(w, r), sgn<13>(w, r), sgn<14>(w, r), sgn<15>(w, r)), ta[3], accq[blk]);
+      }
+    }
+    // ---- S^T block 0; block 1's lookups replace each consumed pair
+    f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      acc[0] = mfma(as_bf16x8(ek[u][0].x, ek[u][0].y, ek[u][1].x, ek[u][1].y), qa[u], acc[0]);
+      ek[u][0] = lookup<BK, L::KC>(s_kt, field<BK>(T.kw[1], (4 * u) * BK, 2 * BK), laneoff);
+      ek[u][1] = lookup<BK, L::KC>(s_kt, field<BK>(T.kw[1], (4 * u + 2) * BK, 2 * BK), laneoff);
+    }
+    // ---- S^T block 1; the value operands of coordinate blocks 0..3 go in flight
+    uint2 ev[4][4];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      acc[1] = mfma(as_bf16x8(ek[u][0].x, ek[u][0].y, ek[u][1].x, ek[u][1].y), qa[u], acc[1]);
+      if (u & 1) vlook(T, u >> 1, ev[u >> 1]);
+    }
     float lg[2][4];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const uint2 e0 = lookup<BK>(s_kt, field<BK>(T.kw[blk], (4 * u) * BK, 2 * BK));
-        const uint2 e1 = lookup<BK>(s_kt, field<BK>(T.kw[blk], (4 * u + 2) * BK, 2 * BK));
-        acc = mfma(as_bf16x8(e0.x, e0.y, e1.x, e1.y), qa[u], acc);
-      }
-      f32x4 accq = {cinit, cinit, cinit, cinit};
-      if constexpr (QJL) {
-        const uint32_t w = T.sw[blk];
-        accq = mfma(as_bf16x8(sign_pair<0>(w), sign_pair<1>(w), sign_pair<2>(w), sign_pair<3>(w)), ta[0], accq);
-        accq = mfma(as_bf16x8(sign_pair<4>(w), sign_pair<5>(w), sign_pair<6>(w), sign_pair<7>(w)), ta[1], accq);
-        accq = mfma(as_bf16x8(sign_pair<8>(w), sign_pair<9>(w), sign_pair<10>(w), sign_pair<11>(w)), ta[2], accq);
-        accq = mfma(as_bf16x8(sign_pair<12>(w), sign_pair<13>(w), sign_pair<14>(w), sign_pair<15>(w)), ta[3], accq);
-      }
       const f32x4 ks = *reinterpret_cast<const f32x4*>(stage + 16 * blk + 4 * g4);
       f32x4 kr = ks;
       if constexpr (QJL) kr = *reinterpret_cast<const f32x4*>(stage + 32 + 16 * blk + 4 * g4);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float mse = acc[r] + dpp_ror8(acc[r]);
+        const float mse = acc[blk][r] + dpp_ror8(acc[blk][r]);
         float v = ks[r] * mse;
-        if constexpr (QJL) v = fmaf(kr[r], accq[r] + dpp_ror8(accq[r]), v);
+        if constexpr (QJL) v = fmaf(kr[r], accq[blk][r] + dpp_ror8(accq[blk][r]), v);
         lg[blk][r] = v;
       }
     }
@@ -509,21 +598,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     const bf16x8 pop1 = as_bf16x8(pb[2], pb[2], pb[3], pb[3]);
 
     // ---- O^T += V^ P^T (coordinates 16*db + c16); operand dwords
-    // (hi, lo, hi, lo) of token slot pairs against duplicated weights
+    // (hi, lo, hi, lo) of token slot pairs against duplicated weights; the
+    // lookups of block db + 4 replace those of block db
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
-      uint32_t fhi;
-      const uint32_t f = vgroup<BV>(T.vr, db, fhi);
-      uint2 e[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint32_t pr;
-        if constexpr (BV == 8) pr = ((q < 2 ? f : fhi) >> (16 * (q & 1))) & 0xFFFFu;
-        else pr = (f >> (2 * q * BV)) & ((1u << (2 * BV)) - 1u);
-        e[q] = lookup<BV>(s_vt, pr);
-      }
+      uint2 (&e)[4] = ev[db & 3];
       acc_o[db] = mfma(as_bf16x8(e[0].x, e[0].y, e[1].x, e[1].y), pop0, acc_o[db]);
       acc_o[db] = mfma(as_bf16x8(e[2].x, e[2].y, e[3].x, e[3].y), pop1, acc_o[db]);
+      if (db < 4) vlook(T, db + 4, ev[db & 3]);
     }
   };
 
@@ -559,9 +641,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
   }
 
-  // ---- wave partial -> LDS
+  // ---- wave partial -> LDS (the merge buffer reuses the table space)
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
+  __syncthreads();
+  float (*s_o)[8][D] = reinterpret_cast<float (*)[8][D]>(s_raw);
 #pragma unroll
   for (int db = 0; db < 8; ++db) {
     f32x4 o;
@@ -575,15 +659,17 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
   __syncthreads();
 
-  // ---- merge the 4 waves (fixed order) and write one partial per workgroup
+  // ---- merge the waves (fixed order) and write one partial per workgroup
   const int64_t rec0 = ((int64_t)row * a.n_wg + blockIdx.x) * 8;
-  for (int e = tid; e < 8 * D; e += 256) {
+  for (int e = tid; e < 8 * D; e += NT) {
     const int c = e / D, i = e % D;
-    float Mx = fmaxf(fmaxf(s_M[0][c], s_M[1][c]), fmaxf(s_M[2][c], s_M[3][c]));
+    float Mx = s_M[0][c];
+#pragma unroll
+    for (int wv = 1; wv < kWaves; ++wv) Mx = fmaxf(Mx, s_M[wv][c]);
     float o = 0.f, ls = 0.f;
     if (Mx != -INFINITY) {
 #pragma unroll
-      for (int wv = 0; wv < 4; ++wv) {
+      for (int wv = 0; wv < kWaves; ++wv) {
         if (s_M[wv][c] == -INFINITY) continue;
         const float sc = __builtin_amdgcn_exp2f(s_M[wv][c] - Mx);
         o += sc * s_o[wv][c][i];
@@ -614,7 +700,7 @@ struct CArgs {
 // p = t/8 + 32 j of slot c = t%8), the per-partial factors 2^(M_p - M) go to
 // LDS, and thread (i, half) then sums coordinate i of slots 4*half .. +3 in
 // partial order.  Finally out = Pi_V^T o~ / l with Pi_V staged in LDS.
-constexpr int kMaxWg = 1024;   // plan_decode caps the partials of a row at 4096 / 4
+constexpr int kMaxWg = 1024;   // plan_decode keeps a row at <= 4096 / kWaves partials
 
 __global__ void __launch_bounds__(256) k_combine(CArgs a) {
   __shared__ __align__(16) float mat[D][D];
@@ -688,8 +774,8 @@ __global__ void __launch_bounds__(256) k_combine(CArgs a) {
 
 template <int BK, int BV>
 void launch_split_bits(const SArgs& a, bool qjl, dim3 grid, hipStream_t st) {
-  if (qjl) hipLaunchKernelGGL((k_split<BK, BV, true>), grid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((k_split<BK, BV, false>), grid, dim3(256), 0, st, a);
+  if (qjl) hipLaunchKernelGGL((k_split<BK, BV, true>), grid, dim3(64 * kWaves), 0, st, a);
+  else hipLaunchKernelGGL((k_split<BK, BV, false>), grid, dim3(64 * kWaves), 0, st, a);
 }
 
 template <int BK>
@@ -717,7 +803,7 @@ DecodePlan plan_decode(int64_t B, int64_t Hq, int64_t Hkv, int64_t n_ctx, int d)
   p.g = Hkv > 0 ? (int)(Hq / Hkv) : 0;
   p.qgroups = (p.g + 7) / 8;
   p.rows = B * Hkv * p.qgroups;
-  const int64_t target_waves = 4096;          // 16 waves per CU on 256 CUs
+  const int64_t target_waves = 4096;          // two rounds of 8 waves on each of 256 CUs
   int64_t parts = p.rows > 0 ? (target_waves + p.rows - 1) / p.rows : 1;
   if (parts < 1) parts = 1;
   int64_t chunk = (n_ctx + parts - 1) / parts;
@@ -725,7 +811,7 @@ DecodePlan plan_decode(int64_t B, int64_t Hq, int64_t Hkv, int64_t n_ctx, int d)
   if (chunk < 32) chunk = 32;
   p.chunk = (int)chunk;
   p.n_parts = n_ctx > 0 ? (int)((n_ctx + chunk - 1) / chunk) : 0;
-  p.n_wg = (p.n_parts + 3) / 4;
+  p.n_wg = (p.n_parts + kWaves - 1) / kWaves;
   size_t off = 0;
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
   p.off_qop = off; off = al(off + (size_t)p.rows * QOP_DWORDS * 4);
