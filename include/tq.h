@@ -186,17 +186,45 @@ tq_status tq_attn_decode(const tq_codebook* kcb, const tq_codebook* vcb, const v
                          float sm_scale, float* out, float* logits, void* workspace,
                          size_t ws_bytes, void* stream);
 
+/* Workspace bytes tq_ip_topk needs (host only); valid for any qjl_m of a
+ * codebook with this d. */
+tq_status tq_ip_topk_workspace(int64_t nq, int64_t n_db, int32_t k, int32_t d, size_t* bytes);
+
+/* Inner-product top-k over coded vectors ([WIT] 基准测试与实际性能表现: the
+ * top-k recall evaluation of vector search at d = 200; the estimate of
+ * 第二阶段: QJL 残差校正).  The score of database vector j for
+ * query q (fp32 [d]) is
+ *   s_j = scale_j <Pi q, c[idx_j]> + sqrt(pi/2)/m rnorm_j <S Pi q, 2 sign_j - 1>
+ * (the QJL term only when qjl_m > 0), the unbiased estimate of <q, x_j>.
+ *  queries   device fp32 [nq][d], row-major
+ *  db        database codes, TQ_LAYOUT_ROW, vectors 0..n_db-1 of sequence 0
+ *            (idx_row_bytes <= 256, sign_row_bytes <= 32)
+ *  k         1..32, k <= n_db (k == 0 or nq == 0: no-op)
+ *  out_idx   device int64 [nq][k]: indices by descending score, ties to the
+ *            lower index
+ *  out_score device fp32 [nq][k]: their scores
+ *  workspace device scratch of >= tq_ip_topk_workspace bytes, 256-byte aligned
+ * Scores are formed with bf16 hi/lo splits of the centroids and of Pi q and
+ * S Pi q (about 2^-16 relative), so rows whose exact scores differ by less
+ * than that may trade places.
+ * Errors: TQ_ERR_INVALID, TQ_ERR_UNSUPPORTED (k > 32, oversized rows),
+ * TQ_ERR_HIP. */
+tq_status tq_ip_topk(const tq_codebook* cb, const float* queries, int64_t nq,
+                     const tq_codes* db, int64_t n_db, int32_t k, int64_t* out_idx,
+                     float* out_score, void* workspace, size_t ws_bytes, void* stream);
+
 /* Kernel timing (instrumentation; not part of the method).
  * tq_profile_enable(1) clears the calling thread's records and starts
- * recording: every later tq_quantize_kv / tq_attn_decode on this thread
+ * recording: every later tq_quantize_kv / tq_attn_decode / tq_ip_topk on this thread
  * records a hipEvent pair on its stream around each launch of its main
- * kernel (the quantize kernel, once per tensor; the decode split kernel).
+ * kernel (the quantize kernel, once per tensor; the decode split kernel;
+ * the top-k score kernel).
  * tq_profile_enable(0) stops recording and keeps the records.
  * tq_profile_read waits for the recorded events and returns the summed
  * elapsed milliseconds and the number of launches of one kernel
- * (TQ_KERNEL_QUANTIZE or TQ_KERNEL_DECODE_SPLIT).  Events are created by the
+ * (TQ_KERNEL_QUANTIZE, TQ_KERNEL_DECODE_SPLIT or TQ_KERNEL_TOPK).  Events are created by the
  * library (no device memory is allocated). */
-typedef enum { TQ_KERNEL_QUANTIZE = 0, TQ_KERNEL_DECODE_SPLIT = 1 } tq_kernel;
+typedef enum { TQ_KERNEL_QUANTIZE = 0, TQ_KERNEL_DECODE_SPLIT = 1, TQ_KERNEL_TOPK = 2 } tq_kernel;
 tq_status tq_profile_enable(int32_t on);
 tq_status tq_profile_read(int32_t kernel, double* total_ms, int64_t* launches);
 

@@ -1,5 +1,5 @@
-"""MI355X (gfx950) online KV-vector quantization and decode attention from
-packed codes.  The compute runs in libtq.so (hand-written HIP kernels behind
+"""MI355X (gfx950) online KV-vector quantization, decode attention from
+packed codes and inner-product top-k over codes.  The compute runs in libtq.so (hand-written HIP kernels behind
 a C ABI, declared in include/tq.h); this package is a thin ctypes binding."""
 from ._lib import (  # noqa: F401
     EXPORTS,
@@ -10,6 +10,7 @@ from ._lib import (  # noqa: F401
     TQ_LAYOUT_ROW,
     TQ_KERNEL_DECODE_SPLIT,
     TQ_KERNEL_QUANTIZE,
+    TQ_KERNEL_TOPK,
     TQ_LAYOUT_TILE32,
     Codebook,
     Codes,
@@ -18,6 +19,8 @@ from ._lib import (  # noqa: F401
     tq_attn_decode,
     tq_attn_decode_workspace,
     tq_codebook_values,
+    tq_ip_topk,
+    tq_ip_topk_workspace,
     tq_profile_enable,
     tq_profile_read,
     tq_quantize_kv,

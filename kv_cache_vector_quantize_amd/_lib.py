@@ -23,9 +23,9 @@ TQ_LAYOUT_ROW, TQ_LAYOUT_TILE32 = 0, 1
 EXPORTS = (
     "tq_codebook_build", "tq_codebook_destroy", "tq_codebook_export", "tq_codebook_values",
     "tq_code_row_bytes", "tq_quantize_kv", "tq_attn_decode_workspace", "tq_attn_decode",
-    "tq_profile_enable", "tq_profile_read", "tq_last_error",
+    "tq_ip_topk_workspace", "tq_ip_topk", "tq_profile_enable", "tq_profile_read", "tq_last_error",
 )
-TQ_KERNEL_QUANTIZE, TQ_KERNEL_DECODE_SPLIT = 0, 1
+TQ_KERNEL_QUANTIZE, TQ_KERNEL_DECODE_SPLIT, TQ_KERNEL_TOPK = 0, 1, 2
 
 
 class TQError(RuntimeError):
@@ -73,6 +73,9 @@ def lib() -> ctypes.CDLL:
     L.tq_attn_decode.argtypes = [vp, vp, vp, i32, i64, i64, i64, ctypes.POINTER(tq_codes),
                                  ctypes.POINTER(tq_codes), vp, i64, ctypes.c_float, vp, vp, vp,
                                  ctypes.c_size_t, vp]
+    L.tq_ip_topk_workspace.argtypes = [i64, i64, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
+    L.tq_ip_topk.argtypes = [vp, vp, i64, ctypes.POINTER(tq_codes), i64, i32, vp, vp, vp,
+                             ctypes.c_size_t, vp]
     L.tq_profile_enable.argtypes = [i32]
     L.tq_profile_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
     for name in EXPORTS:
@@ -252,6 +255,32 @@ def tq_attn_decode(kcb, vcb, q, k_codes: Codes, v_codes: Codes, n_ctx: int, sm_s
         float(sm_scale), out.data_ptr(), logits.data_ptr() if logits is not None else None,
         workspace.data_ptr(), workspace.numel(), _stream_handle(stream)))
     return out
+
+
+def tq_ip_topk_workspace(nq, n_db, k, d) -> int:
+    out = ctypes.c_size_t()
+    _check(lib().tq_ip_topk_workspace(int(nq), int(n_db), int(k), int(d), ctypes.byref(out)))
+    return out.value
+
+
+def tq_ip_topk(cb, queries, db: Codes, n_db: int, k: int, out_idx=None, out_score=None,
+               workspace=None, stream=None):
+    """queries: fp32 [nq, d] torch tensor; db: codes of sequence 0.
+    Returns (idx int64 [nq, k], score fp32 [nq, k])."""
+    import torch
+    nq, d = queries.shape
+    if out_idx is None:
+        out_idx = torch.empty((nq, k), dtype=torch.int64, device=queries.device)
+    if out_score is None:
+        out_score = torch.empty((nq, k), dtype=torch.float32, device=queries.device)
+    if workspace is None:
+        ws = tq_ip_topk_workspace(nq, n_db, k, d)
+        workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=queries.device)
+    dd = db.descriptor()
+    _check(lib().tq_ip_topk(cb.handle, queries.data_ptr(), int(nq), ctypes.byref(dd), int(n_db),
+                            int(k), out_idx.data_ptr(), out_score.data_ptr(), workspace.data_ptr(),
+                            workspace.numel(), _stream_handle(stream)))
+    return out_idx, out_score
 
 
 def tq_profile_enable(on: bool = True):

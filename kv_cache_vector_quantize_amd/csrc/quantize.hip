@@ -59,11 +59,16 @@ __device__ inline void tile32_element(int q, int ndb, int& i, int& t) {
   t = 4 * (r >> 4) + (e & 3) + 16 * (e >> 2);
 }
 
-template <int DP, int DT>
-__global__ void __launch_bounds__(512) k_quantize(QArgs a) {
+// WIDE = false (dp <= 128): one wave per 32-column block of Pi (and of S),
+// whose B operand stays in registers.  WIDE = true (dp up to 256): four waves
+// loop over the column blocks and stream the B operand from L2 (each row of
+// Pi / S is read by every tile; 16 loads per wave are in flight).
+template <int DP, int DT, bool WIDE>
+__global__ void __launch_bounds__(WIDE ? 256 : 512) k_quantize(QArgs a) {
   constexpr int KS = DP / 2;      // k-steps of the 32x32x2 MFMA
-  constexpr int RW = DP / 32;     // rotation waves
-  __shared__ float xs[TILE][DP + 1];   // X, then Y, then the residual R
+  constexpr int RW = DP / 32;     // rotation column blocks
+  __shared__ float xs[TILE][DP + 1];   // X, then the residual R
+  __shared__ float ys[TILE][DP + 1];   // Y = Pi x / |x|
   __shared__ uint8_t ids[TILE][DP];
   __shared__ float s_cent[256];
   __shared__ float s_bnd[256];
@@ -72,25 +77,40 @@ __global__ void __launch_bounds__(512) k_quantize(QArgs a) {
 
   const int tid = threadIdx.x, nthr = blockDim.x;
   const int wave = tid >> 6, lane = tid & 63;
+  const int nwaves = nthr >> 6;
   const int L = 1 << a.bits;
   const int mp = (a.m + 31) & ~31;
+  const int QW = a.m > 0 ? mp / 32 : 0;      // QJL column blocks
   for (int i = tid; i < L; i += nthr) s_cent[i] = a.cent[i];
   for (int i = tid; i < L - 1; i += nthr) s_bnd[i] = a.bnd[i];
 
-  // B operands in registers: B[k][j] = M[j][k], lane holds k = 2kk + lane/32
-  float bop[KS];
-  const bool rot_wave = wave < RW;
-  const bool qjl_wave = a.m > 0 && wave >= RW && wave < RW + mp / 32;
-  if (rot_wave) {
-    const float* src = a.rot + (int64_t)(32 * wave + (lane & 31)) * DP + (lane >> 5);
+  // register B operands (WIDE = false): B[k][j] = M[j][k], lane holds k = 2kk + lane/32
+  float bop[WIDE ? 1 : KS];
+  const bool rot_wave = !WIDE && wave < RW;
+  const bool qjl_wave = !WIDE && a.m > 0 && wave >= RW && wave < RW + QW;
+  if constexpr (!WIDE) {
+    if (rot_wave) {
+      const float* src = a.rot + (int64_t)(32 * wave + (lane & 31)) * DP + (lane >> 5);
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) bop[kk] = src[2 * kk];
-  } else if (qjl_wave) {
-    const float* src = a.qjl + (int64_t)(32 * (wave - RW) + (lane & 31)) * DP + (lane >> 5);
+      for (int kk = 0; kk < KS; ++kk) bop[kk] = src[2 * kk];
+    } else if (qjl_wave) {
+      const float* src = a.qjl + (int64_t)(32 * (wave - RW) + (lane & 31)) * DP + (lane >> 5);
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) bop[kk] = src[2 * kk];
+      for (int kk = 0; kk < KS; ++kk) bop[kk] = src[2 * kk];
+    }
   }
   __syncthreads();
+
+  // 32x32 block of X M^T (rows = tile rows, columns 32*cb..) with M = Pi or S
+  auto gemm_block = [&](const float (*in)[DP + 1], const float* M, int cb) {
+    f32x16 acc = {};
+    const float* src = M + (int64_t)(32 * cb + (lane & 31)) * DP + (lane >> 5);
+#pragma unroll 16
+    for (int kk = 0; kk < KS; ++kk)
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(in[lane & 31][2 * kk + (lane >> 5)], src[2 * kk],
+                                                 acc, 0, 0, 0);
+    return acc;
+  };
 
   for (int64_t tile = blockIdx.x; tile < a.n_tiles; tile += gridDim.x) {
     const int64_t seq = tile / a.tiles_per_seq;
@@ -130,19 +150,10 @@ __global__ void __launch_bounds__(512) k_quantize(QArgs a) {
     }
     __syncthreads();
 
-    // (c) rotation Z = X Pi^T on fp32 MFMA
-    f32x16 acc = {};
-    if (rot_wave) {
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk)
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(xs[lane & 31][2 * kk + (lane >> 5)], bop[kk],
-                                                   acc, 0, 0, 0);
-    }
-    __syncthreads();
-
-    // (d) y = z / n and idx = #{k : y >= t_k} (binary search on sorted t)
-    if (rot_wave) {
-      const int col = 32 * wave + (lane & 31);
+    // (c) rotation Z = X Pi^T on fp32 MFMA; (d) y = z / n and
+    // idx = #{k : y >= t_k} (binary search on sorted t)
+    auto finish_rot = [&](const f32x16& acc, int cb) {
+      const int col = 32 * cb + (lane & 31);
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int row = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
@@ -150,9 +161,19 @@ __global__ void __launch_bounds__(512) k_quantize(QArgs a) {
         int idx = 0;
         for (int step = L >> 1; step >= 1; step >>= 1)
           if (y >= s_bnd[idx + step - 1]) idx += step;
-        xs[row][col] = y;
+        ys[row][col] = y;
         ids[row][col] = (uint8_t)idx;
       }
+    };
+    if constexpr (WIDE) {
+      for (int cb = wave; cb < RW; cb += nwaves) finish_rot(gemm_block(xs, a.rot, cb), cb);
+    } else if (rot_wave) {
+      f32x16 acc = {};
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk)
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(xs[lane & 31][2 * kk + (lane >> 5)], bop[kk],
+                                                   acc, 0, 0, 0);
+      finish_rot(acc, wave);
     }
     __syncthreads();
 
@@ -175,7 +196,7 @@ __global__ void __launch_bounds__(512) k_quantize(QArgs a) {
         const float f = a.nc ? 1.0f / nh : 1.0f;
         for (int i = part; i < DP; i += 8) {
           float rr = 0.f;
-          if (i < a.d) rr = xs[r][i] - s_cent[ids[r][i]] * f;
+          if (i < a.d) rr = ys[r][i] - s_cent[ids[r][i]] * f;
           xs[r][i] = rr;
           rho2 += rr * rr;
         }
@@ -191,13 +212,7 @@ __global__ void __launch_bounds__(512) k_quantize(QArgs a) {
     __syncthreads();
 
     // (f) QJL signs: U = R S^T, one ballot = two 32-bit sign words
-    if (qjl_wave) {
-      f32x16 u = {};
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk)
-        u = __builtin_amdgcn_mfma_f32_32x32x2f32(xs[lane & 31][2 * kk + (lane >> 5)], bop[kk], u,
-                                                 0, 0, 0);
-      const int wj = wave - RW;                      // sign word index
+    auto finish_qjl = [&](const f32x16& u, int wj) {
       const int nbits = a.m - 32 * wj;               // valid bits in this word
       const uint32_t keep = nbits >= 32 ? 0xFFFFFFFFu : ((1u << nbits) - 1u);
 #pragma unroll
@@ -212,6 +227,16 @@ __global__ void __launch_bounds__(512) k_quantize(QArgs a) {
             a.sign[((pos0 + row_hi) * a.sign_pitch >> 2) + wj] = (uint32_t)(msk >> 32) & keep;
         }
       }
+    };
+    if constexpr (WIDE) {
+      for (int cb = wave; cb < QW; cb += nwaves) finish_qjl(gemm_block(xs, a.qjl, cb), cb);
+    } else if (qjl_wave) {
+      f32x16 u = {};
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk)
+        u = __builtin_amdgcn_mfma_f32_32x32x2f32(xs[lane & 31][2 * kk + (lane >> 5)], bop[kk], u,
+                                                 0, 0, 0);
+      finish_qjl(u, wave - RW);
     }
 
     // (g) pack indices
@@ -267,12 +292,10 @@ __global__ void __launch_bounds__(512) k_quantize(QArgs a) {
 
 // ---------------------------------------------------------------- appends
 //
-// Few vectors (decode-time appends): one wave per vector.  Lane l owns
-// coordinates l and l + 64; y = Pi x / |x| and u = S r are matrix-vector
-// products over the transposed matrices (coalesced rows), with the input
-// coordinate broadcast from the lane that holds it.  tile32 fields of
-// different vectors can share a 32-bit word, so they are updated with an
-// atomic AND (clear) and an atomic OR (set).
+// Few vectors (decode-time appends): one workgroup per vector; y = Pi x / |x|
+// and u = S r are matrix-vector products over the transposed matrices
+// (coalesced rows).  tile32 fields of different vectors can share a 32-bit
+// word, so they are updated with an atomic AND (clear) and an atomic OR (set).
 
 struct SmallJob {
   const void* x;
@@ -298,35 +321,39 @@ __device__ inline float wave_sum(float v) {
   return v;
 }
 
-template <int DT>
-__global__ void __launch_bounds__(512) k_quantize_small(SmallArgs sa) {
-  // One 512-thread workgroup per vector: thread (i, kq) = (tid % 128,
-  // tid / 128) forms the partial product of output coordinate i over the
-  // input coordinates 32 kq .. 32 kq + 31, so every matrix load of a thread is
-  // independent and issued together; the four partials are summed in LDS in a
-  // fixed order.
+template <int DT, int NI>
+__global__ void __launch_bounds__(4 * NI) k_quantize_small(SmallArgs sa) {
+  // One workgroup of 4*NI threads per vector (NI = 128 or 256 >= dp, mp):
+  // thread (i, kq) = (tid % NI, tid / NI) forms the partial product of output
+  // coordinate i over the input coordinates NI/4 kq .. NI/4 (kq + 1) - 1, so
+  // every matrix load of a thread is independent and issued together; the
+  // four partials are summed in LDS in a fixed order.
+  constexpr int NT = 4 * NI, KQ = NI / 4, NW = NI / 64;
   const SmallJob& a = sa.job[blockIdx.y];
-  __shared__ float xs[128];
-  __shared__ float part[4][128];
-  __shared__ float rs[128];
-  __shared__ uint8_t ids[128];
-  __shared__ float red[2][2];
+  __shared__ float xs[NI];
+  __shared__ float part[4][NI];
+  __shared__ float rs[NI];
+  __shared__ uint8_t ids[NI];
+  __shared__ float red[2][NW];
   const int64_t vec = blockIdx.x;                 // seq * n_tok + t
   const int64_t seq = vec / a.n_tok, t = vec % a.n_tok;
   const int64_t pos = a.tok_off + t;              // position in the sequence
   const int64_t row = seq * a.seq_stride + pos;
   const int tid = threadIdx.x;
-  const int i = tid & 127, kq = tid >> 7, l = tid & 63, w = tid >> 6;
-  if (tid < 128) xs[tid] = (tid < a.d) ? load_elem<DT>(a.x, vec * a.d + tid) : 0.f;
+  const int i = tid & (NI - 1), kq = tid / NI, l = tid & 63, w = tid >> 6;
+  if (tid < NI) xs[tid] = (tid < a.d) ? load_elem<DT>(a.x, vec * a.d + tid) : 0.f;
   __syncthreads();
-  const float n = sqrtf(wave_sum(xs[l] * xs[l] + xs[l + 64] * xs[l + 64]));
+  float n2 = 0.f;
+#pragma unroll
+  for (int j = 0; j < NW; ++j) n2 += xs[l + 64 * j] * xs[l + 64 * j];
+  const float n = sqrtf(wave_sum(n2));
   const float inv = n > 0.f ? 1.0f / n : 0.f;
   {
     float z = 0.f;
     if (i < a.dp) {
 #pragma unroll
-      for (int kk = 0; kk < 32; ++kk) {
-        const int k = 32 * kq + kk;
+      for (int kk = 0; kk < KQ; ++kk) {
+        const int k = KQ * kq + kk;
         const int kc = k < a.d ? k : a.d - 1;     // xs[k] = 0 beyond d
         z += a.rotT[kc * a.dp + i] * xs[k];
       }
@@ -335,7 +362,7 @@ __global__ void __launch_bounds__(512) k_quantize_small(SmallArgs sa) {
   }
   __syncthreads();
   float y = 0.f, c = 0.f;
-  if (tid < 128) {
+  if (tid < NI) {
     y = (((part[0][i] + part[1][i]) + part[2][i]) + part[3][i]) * inv;
     const int L = 1 << a.bits;
     int q = 0;
@@ -347,10 +374,13 @@ __global__ void __launch_bounds__(512) k_quantize_small(SmallArgs sa) {
     if (l == 0) red[0][w] = s2;
   }
   __syncthreads();
-  const float nh = sqrtf(red[0][0] + red[0][1]);
+  float nh2 = 0.f;
+#pragma unroll
+  for (int j = 0; j < NW; ++j) nh2 += red[0][j];
+  const float nh = sqrtf(nh2);
   const float sc = a.nc ? n / nh : n;
   if (a.m > 0) {
-    if (tid < 128) {
+    if (tid < NI) {
       const float f = a.nc ? 1.0f / nh : 1.0f;
       const float r = (i < a.d) ? y - c * f : 0.f;
       rs[i] = r;
@@ -362,8 +392,8 @@ __global__ void __launch_bounds__(512) k_quantize_small(SmallArgs sa) {
       float u = 0.f;
       if (i < a.m) {
 #pragma unroll
-        for (int kk = 0; kk < 32; ++kk) {
-          const int k = 32 * kq + kk;
+        for (int kk = 0; kk < KQ; ++kk) {
+          const int k = KQ * kq + kk;
           const int kc = k < a.d ? k : a.d - 1;   // rs[k] = 0 beyond d
           u += a.qjlT[kc * a.mp + i] * rs[k];
         }
@@ -371,19 +401,23 @@ __global__ void __launch_bounds__(512) k_quantize_small(SmallArgs sa) {
       part[kq][i] = u;
     }
     __syncthreads();
-    if (tid < 128) {
+    if (tid < NI) {
       const float u = ((part[0][i] + part[1][i]) + part[2][i]) + part[3][i];
       const unsigned long long bb = __ballot(u >= 0.f);
       uint32_t* srow = a.sign + ((row * a.sign_pitch) >> 2);
       const int words = (a.m + 31) / 32;
-      const int wd = 2 * w + l;                     // word of this wave's half
+      const int wd = 2 * w + l;                     // word of this wave's coordinates
       if (l < 2 && wd < words) {
         uint32_t wv = (uint32_t)(bb >> (32 * l));
         const int nbits = a.m - 32 * wd;
         if (nbits < 32) wv &= (1u << nbits) - 1u;
         srow[wd] = wv;
       }
-      if (tid == 0) a.rnorm[row] = n * sqrtf(red[1][0] + red[1][1]);
+      if (tid == 0) {
+        float r2 = 0.f;
+        for (int j = 0; j < NW; ++j) r2 += red[1][j];
+        a.rnorm[row] = n * sqrtf(r2);
+      }
     }
   }
   if (tid == 0) a.scale[row] = sc;
@@ -392,7 +426,7 @@ __global__ void __launch_bounds__(512) k_quantize_small(SmallArgs sa) {
   if (a.layout == TQ_LAYOUT_ROW) {
     const int W = b * a.dp / 32;
     uint32_t* dst = reinterpret_cast<uint32_t*>(a.idx + row * a.idx_pitch);
-    for (int wd = tid; wd < W; wd += 512) {
+    for (int wd = tid; wd < W; wd += NT) {
       const int bit0 = 32 * wd;
       const int j0 = bit0 / b;
       int j1 = (bit0 + 31) / b;
@@ -423,12 +457,12 @@ __global__ void __launch_bounds__(512) k_quantize_small(SmallArgs sa) {
   }
 }
 
-template <int DP>
+template <int DP, bool WIDE>
 hipError_t launch_dp(const QArgs& a, int dt, int nthr, int grid, hipStream_t st) {
   switch (dt) {
-    case TQ_F32: hipLaunchKernelGGL((k_quantize<DP, TQ_F32>), dim3(grid), dim3(nthr), 0, st, a); break;
-    case TQ_BF16: hipLaunchKernelGGL((k_quantize<DP, TQ_BF16>), dim3(grid), dim3(nthr), 0, st, a); break;
-    default: hipLaunchKernelGGL((k_quantize<DP, TQ_F16>), dim3(grid), dim3(nthr), 0, st, a); break;
+    case TQ_F32: hipLaunchKernelGGL((k_quantize<DP, TQ_F32, WIDE>), dim3(grid), dim3(nthr), 0, st, a); break;
+    case TQ_BF16: hipLaunchKernelGGL((k_quantize<DP, TQ_BF16, WIDE>), dim3(grid), dim3(nthr), 0, st, a); break;
+    default: hipLaunchKernelGGL((k_quantize<DP, TQ_F16, WIDE>), dim3(grid), dim3(nthr), 0, st, a); break;
   }
   return hipGetLastError();
 }
@@ -458,16 +492,26 @@ hipError_t launch_quantize_small(const tq_codebook* const* cbs, const QuantJob* 
   const int64_t nvec = jobs[0].n_seq * jobs[0].n_tok;
   const dim3 grid((unsigned)nvec, (unsigned)njobs);
   ProfileScope prof(TQ_KERNEL_QUANTIZE, stream);
-  switch (jobs[0].dt) {
-    case TQ_F32: hipLaunchKernelGGL(k_quantize_small<TQ_F32>, grid, dim3(512), 0, stream, sa); break;
-    case TQ_BF16: hipLaunchKernelGGL(k_quantize_small<TQ_BF16>, grid, dim3(512), 0, stream, sa); break;
-    default: hipLaunchKernelGGL(k_quantize_small<TQ_F16>, grid, dim3(512), 0, stream, sa); break;
+  bool wide = false;
+  for (int t = 0; t < njobs; ++t) wide = wide || cbs[t]->dp > 128 || cbs[t]->mp > 128;
+  if (!wide) {
+    switch (jobs[0].dt) {
+      case TQ_F32: hipLaunchKernelGGL((k_quantize_small<TQ_F32, 128>), grid, dim3(512), 0, stream, sa); break;
+      case TQ_BF16: hipLaunchKernelGGL((k_quantize_small<TQ_BF16, 128>), grid, dim3(512), 0, stream, sa); break;
+      default: hipLaunchKernelGGL((k_quantize_small<TQ_F16, 128>), grid, dim3(512), 0, stream, sa); break;
+    }
+  } else {
+    switch (jobs[0].dt) {
+      case TQ_F32: hipLaunchKernelGGL((k_quantize_small<TQ_F32, 256>), grid, dim3(1024), 0, stream, sa); break;
+      case TQ_BF16: hipLaunchKernelGGL((k_quantize_small<TQ_BF16, 256>), grid, dim3(1024), 0, stream, sa); break;
+      default: hipLaunchKernelGGL((k_quantize_small<TQ_F16, 256>), grid, dim3(1024), 0, stream, sa); break;
+    }
   }
   return hipGetLastError();
 }
 
 bool quantize_supported(const tq_codebook* cb) {
-  return cb->dp <= 128 && (cb->p.qjl_m == 0 || cb->mp <= 128);
+  return cb->dp <= 256 && (cb->p.qjl_m == 0 || cb->mp <= 256);
 }
 
 hipError_t launch_quantize(const tq_codebook* cb, const QuantJob& job, hipStream_t stream) {
@@ -495,16 +539,31 @@ hipError_t launch_quantize(const tq_codebook* cb, const QuantJob& job, hipStream
   a.idx_pitch = job.out.idx_row_bytes;
   a.sign_pitch = job.out.sign_row_bytes;
   a.seq_stride = job.out.seq_stride;
-  const int waves_needed = cb->dp / 32 + (cb->p.qjl_m > 0 ? cb->mp / 32 : 0);
-  const int nw = waves_needed < 4 ? 4 : waves_needed;
-  const int nthr = 64 * nw;
-  int64_t grid = a.n_tiles < 2048 ? a.n_tiles : 2048;
   ProfileScope prof(TQ_KERNEL_QUANTIZE, stream);
+  if (cb->dp <= 128 && (cb->p.qjl_m == 0 || cb->mp <= 128)) {
+    const int waves_needed = cb->dp / 32 + (cb->p.qjl_m > 0 ? cb->mp / 32 : 0);
+    const int nw = waves_needed < 4 ? 4 : waves_needed;
+    const int nthr = 64 * nw;
+    const int grid = (int)(a.n_tiles < 2048 ? a.n_tiles : 2048);
+    switch (cb->dp) {
+      case 32: return launch_dp<32, false>(a, job.dt, nthr, grid, stream);
+      case 64: return launch_dp<64, false>(a, job.dt, nthr, grid, stream);
+      case 96: return launch_dp<96, false>(a, job.dt, nthr, grid, stream);
+      default: return launch_dp<128, false>(a, job.dt, nthr, grid, stream);
+    }
+  }
+  // d in (128, 256] or a sketch of more than 128 rows: four waves stream Pi
+  // and S from L2 (DP is the row stride of both matrices, = dp)
+  const int grid = (int)(a.n_tiles < 1024 ? a.n_tiles : 1024);
   switch (cb->dp) {
-    case 32: return launch_dp<32>(a, job.dt, nthr, (int)grid, stream);
-    case 64: return launch_dp<64>(a, job.dt, nthr, (int)grid, stream);
-    case 96: return launch_dp<96>(a, job.dt, nthr, (int)grid, stream);
-    default: return launch_dp<128>(a, job.dt, nthr, (int)grid, stream);
+    case 32: return launch_dp<32, true>(a, job.dt, 256, grid, stream);
+    case 64: return launch_dp<64, true>(a, job.dt, 256, grid, stream);
+    case 96: return launch_dp<96, true>(a, job.dt, 256, grid, stream);
+    case 128: return launch_dp<128, true>(a, job.dt, 256, grid, stream);
+    case 160: return launch_dp<160, true>(a, job.dt, 256, grid, stream);
+    case 192: return launch_dp<192, true>(a, job.dt, 256, grid, stream);
+    case 224: return launch_dp<224, true>(a, job.dt, 256, grid, stream);
+    default: return launch_dp<256, true>(a, job.dt, 256, grid, stream);
   }
 }
 

@@ -1,0 +1,451 @@
+// Inner-product top-k over coded database vectors (gfx950).
+//
+// Page "什么是TurboQuant？…" (a2a-mcp.org blog): the inner-product estimate of
+// the two-stage scheme ("第二阶段：QJL 残差校正": the 1-bit sketch of the
+// residual corrects the bias of the MSE stage) and its use for nearest
+// neighbour search ("基准测试与实际性能表现": top-k recall of vector search at
+// d = 200).  The score of database vector
+// j for query q is
+//     s_j = scale_j <Pi q, c[idx_j]> + sqrt(pi/2)/m * rnorm_j <S Pi q, 2 sigma_j - 1>
+// (no softmax scale), and the result is the k largest s_j per query, ties to
+// the lower index.
+//
+// k_ip_prologue  one workgroup per query: q~ = Pi q, t = sqrt(pi/2)/m S q~,
+//                written as bf16 hi/lo MFMA B operands for blocks of 8 queries.
+// k_ip_score     grid (database chunk, query block); each wave stages 16 code
+//                rows in LDS, forms the centroid operand with the pair table
+//                and the sign operand from sign bytes, runs
+//                v_mfma_f32_16x16x32_bf16 against the block's 8 queries (hi/lo
+//                columns) and keeps a per-lane top-k list in LDS behind a
+//                register threshold; the workgroup merges its lists into k
+//                candidates per (query, chunk).
+// k_ip_merge     one wave per query selects the final k from the candidates.
+#include "tq_internal.hpp"
+
+namespace tq {
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kIpWaves = 4;
+constexpr int kSignShiftIp = 64;    // the sketch-query operand carries 2^-64
+constexpr int32_t kNoIndex = 0x7FFFFFFF;
+
+__device__ inline uint32_t bf16_rne_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ inline f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ inline bf16x8 as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+  u32x4v v = {a, b, c, d};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// lane j gets x[j] + x[j + 8] within each row of 16 lanes (hi + lo columns)
+__device__ inline float dpp_ror8(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
+}
+
+// (score, index) order: larger score first, then lower index
+__device__ inline bool better(float s, int32_t i, float ps, int32_t pi) {
+  return s > ps || (s == ps && i < pi);
+}
+
+// ------------------------------------------------------------ prologue
+
+struct IPArgs {
+  const float* q;       // [nq][d]
+  int64_t nq;
+  int d, m, dp, mp, nu, ns;
+  const float* rotT;    // [dp][dp], rotT[k][i] = Pi[i][k]
+  const float* qjlT;    // [dp][mp], qjlT[i][j] = S[j][i]
+  uint32_t* qop;        // [nqb][nu + ns][64 lanes][4 dwords]
+  float* cinit;         // [nqb * 8]
+};
+
+// Operand layouts (lane = column j + 16 g4 of the B operand; columns 0-7 are
+// the hi parts of the block's 8 queries, 8-15 their lo parts):
+//  MSE MFMA u: element el of lane group g4 is coordinate
+//    16 u + 4 g4 + 2 (el / 4) + el % 2, matching the key operand dwords
+//    {hi pair, lo pair} of coordinate pairs (a, b) and (c, d);
+//  sign MFMA v: element el is sketch row 32 v + 8 g4 + el, scaled by
+//    2^(128 - 2^el - 64): the sign operand leaves bit el of the lane's sign
+//    byte at bf16 bit 7 + el, the normal value 2^(2^el - 127).
+__global__ void __launch_bounds__(256) k_ip_prologue(IPArgs a) {
+  __shared__ float qs[256], qt[256], tt[256];
+  const int64_t qi = blockIdx.x;        // over the padded query count
+  const int tid = threadIdx.x;
+  const bool valid = qi < a.nq;
+  qs[tid] = (valid && tid < a.d) ? a.q[qi * a.d + tid] : 0.f;
+  __syncthreads();
+  float z = 0.f;
+  if (tid < a.dp) {
+#pragma unroll 8
+    for (int k = 0; k < a.d; ++k) z += a.rotT[k * a.dp + tid] * qs[k];
+  }
+  qt[tid] = z;
+  __syncthreads();
+  float t = 0.f;
+  if (tid < a.m) {
+#pragma unroll 8
+    for (int i = 0; i < a.d; ++i) t += a.qjlT[i * a.mp + tid] * qt[i];
+    t *= 1.2533141373155003f / (float)a.m;          // sqrt(pi/2) / m
+  }
+  tt[tid] = t;
+  __syncthreads();
+  const int64_t qb = qi >> 3;
+  const int c = (int)(qi & 7);
+  uint32_t* rec = a.qop + qb * (int64_t)(a.nu + a.ns) * 256;
+  for (int e = tid; e < a.nu * 32; e += 256) {
+    const int dw = e & 3, g4 = (e >> 2) & 3, hl = (e >> 4) & 1, u = e >> 5;
+    uint32_t hv[2];
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int el = 2 * dw + h2;
+      const float v = qt[16 * u + 4 * g4 + 2 * (el >> 2) + (el & 1)];
+      const uint32_t hi = bf16_rne_bits(v);
+      hv[h2] = hl ? bf16_rne_bits(v - __uint_as_float(hi << 16)) : hi;
+    }
+    rec[(u * 64 + hl * 8 + c + 16 * g4) * 4 + dw] = hv[0] | (hv[1] << 16);
+  }
+  for (int e = tid; e < a.ns * 32; e += 256) {
+    const int dw = e & 3, g4 = (e >> 2) & 3, hl = (e >> 4) & 1, v = e >> 5;
+    uint32_t hv[2];
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int el = 2 * dw + h2;
+      const float x = ldexpf(tt[32 * v + 8 * g4 + el], 128 - (1 << el) - kSignShiftIp);
+      const uint32_t hi = bf16_rne_bits(x);
+      hv[h2] = hl ? bf16_rne_bits(x - __uint_as_float(hi << 16)) : hi;
+    }
+    rec[((a.nu + v) * 64 + hl * 8 + c + 16 * g4) * 4 + dw] = hv[0] | (hv[1] << 16);
+  }
+  // QJL accumulator offset: -sum_j (hi + lo)(t_j), in the scale of the products
+  if (tid < 64) {
+    float s = 0.f;
+    for (int j = tid; j < 256; j += 64) {
+      const float v = tt[j];
+      const float fh = __uint_as_float(bf16_rne_bits(v) << 16);
+      s += fh + __uint_as_float(bf16_rne_bits(v - fh) << 16);
+    }
+    for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+    if (tid == 0) a.cinit[qi] = -ldexpf(s, -kSignShiftIp);
+  }
+}
+
+// ------------------------------------------------------------ scores + lists
+
+struct ISArgs {
+  const uint32_t* qop;
+  const float* cinit;
+  const uint32_t* idx;     // row layout, idx_pitch bytes per vector
+  const uint32_t* sign;    // sign_pitch bytes per vector (or null)
+  const float* scale;
+  const float* rnorm;
+  const uint32_t* tab;     // decode operand table of the codebook
+  int64_t n_db, n_tiles, tiles_per_chunk;
+  int rw, sw;              // 32-bit words per idx / sign row
+  int nu, ns, k, n_chunks;
+  float* cand_s;           // [nq_pad][n_chunks][k]
+  int32_t* cand_i;
+};
+
+template <int B, bool QJL>
+__global__ void __launch_bounds__(64 * kIpWaves) k_ip_score(ISArgs a) {
+  constexpr int TABW = (B <= 4) ? (2 << (2 * B)) : (1 << B);
+  __shared__ __align__(16) uint4 s_q[(kIpNuMax + kIpNsMax) * 64];
+  __shared__ __align__(16) uint32_t s_tab[TABW];
+  __shared__ uint32_t s_st[kIpWaves][16 * 64];      // the wave's 16 idx rows
+  __shared__ uint32_t s_ss[kIpWaves][16 * 8];       // and their sign rows
+  __shared__ float s_ls[kIpTopkMax][kIpWaves * 32];  // per-lane lists, slot-major
+  __shared__ int32_t s_li[kIpTopkMax][kIpWaves * 32];
+  __shared__ float s_cinit[8];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int c16 = lane & 15, g4 = lane >> 4;
+  const int64_t qb = blockIdx.y;
+  const int chunk = blockIdx.x;
+  const int nus = a.nu + a.ns;
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(a.qop) + qb * (int64_t)nus * 64;
+    for (int i = tid; i < nus * 64; i += 64 * kIpWaves) s_q[i] = src[i];
+    for (int i = tid; i < TABW; i += 64 * kIpWaves) s_tab[i] = a.tab[i];
+    if (tid < 8) s_cinit[tid] = a.cinit[qb * 8 + tid];
+    for (int i = tid; i < a.k * kIpWaves * 32; i += 64 * kIpWaves) {
+      s_ls[i / (kIpWaves * 32)][i % (kIpWaves * 32)] = -INFINITY;
+      s_li[i / (kIpWaves * 32)][i % (kIpWaves * 32)] = kNoIndex;
+    }
+  }
+  __syncthreads();
+
+  const int ln = wave * 32 + g4 * 8 + (c16 & 7);   // list column (lanes c16 < 8)
+  const float cin = (QJL && c16 < 8) ? s_cinit[c16] : 0.f;
+  float thr = -INFINITY;
+  const int64_t t_begin = (int64_t)chunk * a.tiles_per_chunk;
+  int64_t t_end = t_begin + a.tiles_per_chunk;
+  if (t_end > a.n_tiles) t_end = a.n_tiles;
+  uint32_t* st = s_st[wave];
+  uint32_t* ss = s_ss[wave];
+  const char* tab = reinterpret_cast<const char*>(s_tab);
+
+  for (int64_t tile = t_begin + wave; tile < t_end; tile += kIpWaves) {
+    const int64_t row0 = tile * 16;
+    // stage the 16 rows (rows past the end repeat the last one; masked below)
+    for (int e = lane; e < 16 * a.rw; e += 64) {
+      const int r = e / a.rw, w = e - r * a.rw;
+      int64_t rr = row0 + r;
+      if (rr > a.n_db - 1) rr = a.n_db - 1;
+      st[e] = a.idx[rr * a.rw + w];
+    }
+    if constexpr (QJL) {
+      for (int e = lane; e < 16 * a.sw; e += 64) {
+        const int r = e / a.sw, w = e - r * a.sw;
+        int64_t rr = row0 + r;
+        if (rr > a.n_db - 1) rr = a.n_db - 1;
+        ss[e] = a.sign[rr * a.sw + w];
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // <q~, c[idx]> over MFMAs of 16 coordinates (hi/lo)
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < a.nu; ++u) {
+      const int o = (16 * u + 4 * g4) * B;
+      const int i0 = o >> 5, sh = o & 31;
+      const int i1 = (i0 + 1 < a.rw) ? i0 + 1 : i0;
+      const uint32_t f = __builtin_amdgcn_alignbit(st[c16 * a.rw + i1], st[c16 * a.rw + i0], sh);
+      uint32_t d0, d1, d2, d3;
+      if constexpr (B <= 4) {
+        constexpr uint32_t PM = (1u << (2 * B)) - 1u;
+        const uint2 e0 = *reinterpret_cast<const uint2*>(tab + ((f & PM) << 3));
+        const uint2 e1 = *reinterpret_cast<const uint2*>(tab + (((f >> (2 * B)) & PM) << 3));
+        d0 = e0.x; d1 = e0.y; d2 = e1.x; d3 = e1.y;
+      } else {
+        constexpr uint32_t CM = (1u << B) - 1u;
+        const uint32_t* t32 = reinterpret_cast<const uint32_t*>(tab);
+        const uint32_t ca = t32[f & CM], cb = t32[(f >> B) & CM];
+        const uint32_t cc = t32[(f >> (2 * B)) & CM], cd = t32[(f >> (3 * B)) & CM];
+        d0 = __builtin_amdgcn_perm(cb, ca, 0x05040100u);
+        d1 = __builtin_amdgcn_perm(cb, ca, 0x07060302u);
+        d2 = __builtin_amdgcn_perm(cd, cc, 0x05040100u);
+        d3 = __builtin_amdgcn_perm(cd, cc, 0x07060302u);
+      }
+      acc = mfma(as_bf16x8(d0, d1, d2, d3), __builtin_bit_cast(bf16x8, s_q[u * 64 + lane]), acc);
+    }
+    // <t, sigma> over MFMAs of 32 sketch rows
+    f32x4 accq = {cin, cin, cin, cin};
+    if constexpr (QJL) {
+      for (int v = 0; v < a.ns; ++v) {
+        const uint32_t sb = (ss[c16 * a.sw + v] >> (8 * g4)) & 0xFFu;
+        const uint32_t x7 = (sb | (sb << 16)) << 7;
+        accq = mfma(as_bf16x8(x7 & 0x01000080u, x7 & 0x04000200u, x7 & 0x10000800u, x7 & 0x40002000u),
+                    __builtin_bit_cast(bf16x8, s_q[(a.nu + v) * 64 + lane]), accq);
+      }
+    }
+    // scores of rows row0 + 4 g4 + r for query c16 (lanes c16 < 8)
+    float sc[4], rn[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      int64_t rr = row0 + 4 * g4 + r;
+      if (rr > a.n_db - 1) rr = a.n_db - 1;
+      sc[r] = a.scale[rr];
+      rn[r] = QJL ? a.rnorm[rr] : 0.f;
+    }
+    float s[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float v = sc[r] * (acc[r] + dpp_ror8(acc[r]));
+      if constexpr (QJL) v = fmaf(rn[r] * 0x1p64f, accq[r] + dpp_ror8(accq[r]), v);
+      s[r] = (row0 + 4 * g4 + r < a.n_db) ? v : -INFINITY;
+    }
+    if (c16 < 8) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (s[r] > thr) {
+          const int32_t id = (int32_t)(row0 + 4 * g4 + r);
+          int j = a.k - 1;
+          while (j > 0) {
+            const float p = s_ls[j - 1][ln];
+            if (!(s[r] > p)) break;
+            s_ls[j][ln] = p;
+            s_li[j][ln] = s_li[j - 1][ln];
+            --j;
+          }
+          s_ls[j][ln] = s[r];
+          s_li[j][ln] = id;
+          thr = s_ls[a.k - 1][ln];
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // merge the 16 lists of each query (4 waves x 4 lane groups) into k candidates
+  if (tid < 8) {
+    const int c = tid;
+    int head[kIpWaves * 4];
+#pragma unroll
+    for (int h = 0; h < kIpWaves * 4; ++h) head[h] = 0;
+    const int64_t base = ((qb * 8 + c) * a.n_chunks + chunk) * (int64_t)a.k;
+    for (int o = 0; o < a.k; ++o) {
+      int best = -1;
+      float bs = -INFINITY;
+      int32_t bi = kNoIndex;
+#pragma unroll
+      for (int h = 0; h < kIpWaves * 4; ++h) {
+        if (head[h] >= a.k) continue;
+        const int col = (h >> 2) * 32 + (h & 3) * 8 + c;
+        const float hs = s_ls[head[h]][col];
+        const int32_t hi = s_li[head[h]][col];
+        if (best < 0 || better(hs, hi, bs, bi)) { best = h; bs = hs; bi = hi; }
+      }
+      head[best]++;
+      a.cand_s[base + o] = bs;
+      a.cand_i[base + o] = bi;
+    }
+  }
+}
+
+// ------------------------------------------------------------ final merge
+
+struct IMArgs {
+  const float* cand_s;
+  const int32_t* cand_i;
+  int64_t nq;
+  int n_chunks, k;
+  int64_t* out_idx;
+  float* out_score;
+};
+
+// One wave per query: k rounds, each picking the best candidate that comes
+// after the previous pick in (score desc, index asc) order; indices are
+// distinct, so the order is strict.
+__global__ void __launch_bounds__(64) k_ip_merge(IMArgs a) {
+  const int64_t q = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int n = a.n_chunks * a.k;
+  const float* cs = a.cand_s + q * n;
+  const int32_t* ci = a.cand_i + q * n;
+  float ps = INFINITY;
+  int32_t pi = -1;
+  for (int o = 0; o < a.k; ++o) {
+    float bs = -INFINITY;
+    int32_t bi = kNoIndex;
+    bool have = false;
+    for (int e = lane; e < n; e += 64) {
+      const float s = cs[e];
+      const int32_t i = ci[e];
+      if (!better(ps, pi, s, i)) continue;          // not after the previous pick
+      if (!have || better(s, i, bs, bi)) { bs = s; bi = i; have = true; }
+    }
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float os = __shfl_xor(bs, off);
+      const int32_t oi = __shfl_xor(bi, off);
+      if (better(os, oi, bs, bi)) { bs = os; bi = oi; }
+    }
+    if (lane == 0) {
+      a.out_score[q * a.k + o] = bs;
+      a.out_idx[q * a.k + o] = (bi == kNoIndex) ? -1 : (int64_t)bi;
+    }
+    ps = bs;
+    pi = bi;
+  }
+}
+
+template <int B>
+void launch_score_b(const ISArgs& a, bool qjl, dim3 grid, hipStream_t st) {
+  if (qjl) hipLaunchKernelGGL((k_ip_score<B, true>), grid, dim3(64 * kIpWaves), 0, st, a);
+  else hipLaunchKernelGGL((k_ip_score<B, false>), grid, dim3(64 * kIpWaves), 0, st, a);
+}
+
+}  // namespace
+
+TopkPlan plan_topk(int64_t nq, int64_t n_db, int k, int d, int m) {
+  TopkPlan p{};
+  p.nq = nq; p.n_db = n_db; p.k = k;
+  p.nu = (pad32(d) + 15) / 16;
+  p.ns = m > 0 ? (m + 31) / 32 : 0;
+  p.nqb = (nq + 7) / 8;
+  p.n_tiles = (n_db + 15) / 16;
+  int64_t chunks = p.nqb > 0 ? (2048 + p.nqb - 1) / p.nqb : 1;    // ~2048 workgroups
+  int64_t cap = p.n_tiles / 8;                                   // >= 8 tiles per chunk
+  if (chunks > cap) chunks = cap;
+  if (chunks > 4096) chunks = 4096;
+  if (chunks < 1) chunks = 1;
+  p.tiles_per_chunk = p.n_tiles > 0 ? (p.n_tiles + chunks - 1) / chunks : 1;
+  p.n_chunks = p.n_tiles > 0 ? (int)((p.n_tiles + p.tiles_per_chunk - 1) / p.tiles_per_chunk) : 1;
+  size_t off = 0;
+  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  p.off_qop = off; off = al(off + (size_t)p.nqb * (p.nu + p.ns) * 64 * 16);
+  p.off_cinit = off; off = al(off + (size_t)p.nqb * 8 * 4);
+  const size_t nc = (size_t)p.nqb * 8 * p.n_chunks * (size_t)k;
+  p.off_cand_s = off; off = al(off + nc * 4);
+  p.off_cand_i = off; off = al(off + nc * 4);
+  p.bytes = off;
+  return p;
+}
+
+hipError_t launch_topk(const tq_codebook* cb, const float* queries, const TopkPlan& plan,
+                       const tq_codes& db, int64_t* out_idx, float* out_score, void* ws,
+                       hipStream_t stream) {
+  if (plan.nq == 0 || plan.k == 0) return hipSuccess;
+  char* w = static_cast<char*>(ws);
+  uint32_t* qop = reinterpret_cast<uint32_t*>(w + plan.off_qop);
+  float* cinit = reinterpret_cast<float*>(w + plan.off_cinit);
+  float* cand_s = reinterpret_cast<float*>(w + plan.off_cand_s);
+  int32_t* cand_i = reinterpret_cast<int32_t*>(w + plan.off_cand_i);
+
+  IPArgs pa{};
+  pa.q = queries; pa.nq = plan.nq;
+  pa.d = cb->p.d; pa.m = cb->p.qjl_m; pa.dp = cb->dp; pa.mp = cb->mp;
+  pa.nu = plan.nu; pa.ns = plan.ns;
+  pa.rotT = cb->dev.rotT; pa.qjlT = cb->dev.qjlT;
+  pa.qop = qop; pa.cinit = cinit;
+  hipLaunchKernelGGL(k_ip_prologue, dim3((unsigned)(plan.nqb * 8)), dim3(256), 0, stream, pa);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  ISArgs sa{};
+  sa.qop = qop; sa.cinit = cinit;
+  sa.idx = static_cast<const uint32_t*>(db.idx);
+  sa.sign = static_cast<const uint32_t*>(db.sign);
+  sa.scale = db.scale; sa.rnorm = db.rnorm;
+  sa.tab = cb->dev.pair_tab;
+  sa.n_db = plan.n_db; sa.n_tiles = plan.n_tiles; sa.tiles_per_chunk = plan.tiles_per_chunk;
+  sa.rw = (int)(db.idx_row_bytes / 4);
+  sa.sw = cb->p.qjl_m > 0 ? (int)(db.sign_row_bytes / 4) : 0;
+  sa.nu = plan.nu; sa.ns = plan.ns; sa.k = plan.k; sa.n_chunks = plan.n_chunks;
+  sa.cand_s = cand_s; sa.cand_i = cand_i;
+  const dim3 grid((unsigned)plan.n_chunks, (unsigned)plan.nqb);
+  const bool qjl = cb->p.qjl_m > 0;
+  {
+    ProfileScope prof(TQ_KERNEL_TOPK, stream);
+    switch (cb->p.bits) {
+      case 1: launch_score_b<1>(sa, qjl, grid, stream); break;
+      case 2: launch_score_b<2>(sa, qjl, grid, stream); break;
+      case 3: launch_score_b<3>(sa, qjl, grid, stream); break;
+      case 4: launch_score_b<4>(sa, qjl, grid, stream); break;
+      case 5: launch_score_b<5>(sa, qjl, grid, stream); break;
+      case 6: launch_score_b<6>(sa, qjl, grid, stream); break;
+      case 7: launch_score_b<7>(sa, qjl, grid, stream); break;
+      default: launch_score_b<8>(sa, qjl, grid, stream); break;
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+
+  IMArgs ma{};
+  ma.cand_s = cand_s; ma.cand_i = cand_i;
+  ma.nq = plan.nq; ma.n_chunks = plan.n_chunks; ma.k = plan.k;
+  ma.out_idx = out_idx; ma.out_score = out_score;
+  hipLaunchKernelGGL(k_ip_merge, dim3((unsigned)plan.nq), dim3(64), 0, stream, ma);
+  return hipGetLastError();
+}
+
+}  // namespace tq

@@ -121,7 +121,7 @@ namespace {
 struct EventPair { hipEvent_t a = nullptr, b = nullptr; };
 struct ProfileState {
   bool on = false;
-  std::vector<EventPair> rec[2];
+  std::vector<EventPair> rec[3];
   ~ProfileState() {
     for (auto& v : rec)
       for (auto& p : v) { (void)hipEventDestroy(p.a); (void)hipEventDestroy(p.b); }
@@ -301,7 +301,7 @@ tq_status tq_quantize_kv(const tq_codebook* kcb, const tq_codebook* vcb, const v
       tq_status s = check_codes(cbs[t], outs[t], tok_offset + n_tok, names[t], false);
       if (s != TQ_OK) return s;
       if (!quantize_supported(cbs[t]))
-        return fail(TQ_ERR_UNSUPPORTED, std::string(names[t]) + ": quantize supports d <= 128 and qjl_m <= 128");
+        return fail(TQ_ERR_UNSUPPORTED, std::string(names[t]) + ": quantize supports d <= 256 and qjl_m <= 256");
       s = current_device_matches(cbs[t]);
       if (s != TQ_OK) return s;
     }
@@ -382,6 +382,52 @@ tq_status tq_attn_decode(const tq_codebook* kcb, const tq_codebook* vcb, const v
   }
 }
 
+tq_status tq_ip_topk_workspace(int64_t nq, int64_t n_db, int32_t k, int32_t d, size_t* bytes) {
+  if (!bytes) return fail(TQ_ERR_INVALID, "bytes is NULL");
+  if (nq < 0 || n_db < 0 || k < 0 || d < 3 || d > 256)
+    return fail(TQ_ERR_INVALID, "need nq, n_db, k >= 0 and d in 3..256");
+  if (k > kIpTopkMax) return fail(TQ_ERR_UNSUPPORTED, "k must be <= 32");
+  *bytes = plan_topk(nq, n_db, k, d, 256).bytes;     // sized for any qjl_m <= 256
+  return TQ_OK;
+}
+
+tq_status tq_ip_topk(const tq_codebook* cb, const float* queries, int64_t nq,
+                     const tq_codes* db, int64_t n_db, int32_t k, int64_t* out_idx,
+                     float* out_score, void* workspace, size_t ws_bytes, void* stream) {
+  try {
+    if (!cb) return fail(TQ_ERR_INVALID, "codebook is NULL");
+    if (nq < 0 || n_db < 0 || k < 0) return fail(TQ_ERR_INVALID, "need nq, n_db, k >= 0");
+    if (k > kIpTopkMax) return fail(TQ_ERR_UNSUPPORTED, "k must be <= 32");
+    if (k > n_db) return fail(TQ_ERR_INVALID, "k must be <= n_db");
+    if (nq == 0 || k == 0) return TQ_OK;
+    if (!queries || !out_idx || !out_score)
+      return fail(TQ_ERR_INVALID, "queries, out_idx and out_score must be non-NULL");
+    if (!db || db->layout != TQ_LAYOUT_ROW)
+      return fail(TQ_ERR_INVALID, "database codes must use the row layout");
+    tq_status s = check_codes(cb, db, n_db, "db", false);
+    if (s != TQ_OK) return s;
+    if (db->idx_row_bytes > kIpMaxRowBytes || (cb->p.qjl_m > 0 && db->sign_row_bytes > kIpMaxSignRowBytes))
+      return fail(TQ_ERR_UNSUPPORTED, "top-k supports idx_row_bytes <= 256 and sign_row_bytes <= 32");
+    if ((s = current_device_matches(cb)) != TQ_OK) return s;
+    if (n_db > 0x7FFFFFF0LL) return fail(TQ_ERR_UNSUPPORTED, "n_db must fit in 31 bits");
+    const TopkPlan plan = plan_topk(nq, n_db, k, cb->p.d, cb->p.qjl_m);
+    if (plan.nqb > 65535) return fail(TQ_ERR_UNSUPPORTED, "nq must be <= 524280");
+    size_t need = 0;
+    (void)tq_ip_topk_workspace(nq, n_db, k, cb->p.d, &need);
+    if (!workspace || ws_bytes < need)
+      return fail(TQ_ERR_INVALID, "workspace missing or smaller than tq_ip_topk_workspace()");
+    if (!aligned(workspace, 256)) return fail(TQ_ERR_INVALID, "workspace must be 256-byte aligned");
+    if (!aligned(queries, 4) || !aligned(out_idx, 8) || !aligned(out_score, 4))
+      return fail(TQ_ERR_INVALID, "queries, out_idx and out_score must be naturally aligned");
+    hipError_t e = launch_topk(cb, queries, plan, *db, out_idx, out_score, workspace,
+                               static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "top-k launch");
+    return TQ_OK;
+  } catch (...) {
+    return fail(TQ_ERR_ALLOC, "tq_ip_topk: unexpected exception");
+  }
+}
+
 tq_status tq_profile_enable(int32_t on) {
   if (on) {
     for (auto& v : g_prof.rec) {
@@ -394,7 +440,7 @@ tq_status tq_profile_enable(int32_t on) {
 }
 
 tq_status tq_profile_read(int32_t kernel, double* total_ms, int64_t* launches) {
-  if (kernel < 0 || kernel > 1) return fail(TQ_ERR_INVALID, "unknown kernel id");
+  if (kernel < 0 || kernel > 2) return fail(TQ_ERR_INVALID, "unknown kernel id");
   double tot = 0.0;
   for (auto& p : g_prof.rec[kernel]) {
     hipError_t e = hipEventSynchronize(p.b);

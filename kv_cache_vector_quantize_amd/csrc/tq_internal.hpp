@@ -74,7 +74,7 @@ struct QuantJob {
 
 hipError_t launch_quantize(const tq_codebook* cb, const QuantJob& job, hipStream_t stream);
 
-// Few vectors per sequence (appends): one wave per vector; K and V jobs in
+// Few vectors per sequence (appends): one workgroup per vector; K and V jobs in
 // one launch.  njobs in 1..2, jobs share n_seq, n_tok and dtype.
 hipError_t launch_quantize_small(const tq_codebook* const* cbs, const QuantJob* jobs, int njobs,
                                  hipStream_t stream);
@@ -88,7 +88,7 @@ struct DecodePlan {
   int64_t rows;     // B * Hkv * qgroups (one row = one KV head and <= 8 query heads)
   int chunk;        // tokens per wave (multiple of 32)
   int n_parts;      // waves per row = ceil(n_ctx / chunk)
-  int n_wg;         // workgroups per row = ceil(n_parts / 4)
+  int n_wg;         // workgroups per row = ceil(n_parts / waves per workgroup)
   size_t off_qop, off_part_o, off_part_ml, bytes;
 };
 
@@ -100,5 +100,23 @@ hipError_t launch_decode(const tq_codebook* kcb, const tq_codebook* vcb, const v
                          float* out, float* logits, void* ws, hipStream_t stream);
 
 bool decode_supported(const tq_codebook* kcb, const tq_codebook* vcb);
+
+// Inner-product top-k (limits of the LDS-resident per-lane lists and operands)
+constexpr int kIpTopkMax = 32;   // k
+constexpr int kIpNuMax = 16;     // MSE MFMAs per query block: dp / 16 (d <= 256)
+constexpr int kIpNsMax = 8;      // sign MFMAs: ceil(m / 32) (m <= 256)
+constexpr int64_t kIpMaxRowBytes = 256, kIpMaxSignRowBytes = 32;
+
+struct TopkPlan {
+  int64_t nq, n_db, nqb, n_tiles, tiles_per_chunk;
+  int k, nu, ns, n_chunks;
+  size_t off_qop, off_cinit, off_cand_s, off_cand_i, bytes;
+};
+
+TopkPlan plan_topk(int64_t nq, int64_t n_db, int k, int d, int m);
+
+hipError_t launch_topk(const tq_codebook* cb, const float* queries, const TopkPlan& plan,
+                       const tq_codes& db, int64_t* out_idx, float* out_score, void* ws,
+                       hipStream_t stream);
 
 }  // namespace tq

@@ -71,6 +71,10 @@ def _quant_case(dev, d, bits, m, nc, dtype, n_seq, n_tok, tok_offset=0, layout=T
     (64, 4, 32, False, "f32"),
     (40, 5, 40, False, "f32"),
     (5, 2, 3, False, "f32"),
+    (200, 4, 200, False, "f32"),   # vector-search shape (wide kernel)
+    (256, 3, 256, True, "bf16"),
+    (160, 8, 0, False, "bf16"),
+    (128, 3, 200, False, "f32"),   # sketch wider than 128 rows (wide kernel)
 ])
 def test_quantize_rows_parity(dev, d, bits, m, nc, dtype):
     n_seq, n_tok = 3, 333
@@ -142,6 +146,8 @@ def test_quantize_tile32_parity_and_append(dev, bits):
     (96, 2, 40, True, TQ_LAYOUT_ROW, 5),
     (64, 4, 64, False, TQ_LAYOUT_ROW, 2),
     (40, 5, 0, False, TQ_LAYOUT_TILE32, 1),
+    (200, 4, 200, False, TQ_LAYOUT_ROW, 2),     # 256-coordinate append kernel
+    (256, 3, 0, True, TQ_LAYOUT_TILE32, 3),
 ])
 def test_quantize_append_path(dev, d, bits, m, nc, layout, n_tok):
     """Appends of a few tokens per sequence at unaligned offsets (the
@@ -211,10 +217,10 @@ def test_quantize_argument_errors(dev):
     x = torch.zeros((1, 40, 128), dtype=torch.float32, device=dev)
     with pytest.raises(tq.TQError):          # beyond seq_stride
         tq.tq_quantize_kv(cb, None, x, None, codes, None)
-    big = tq.Codebook(200, 4)
-    bc = tq.Codes(big, 1, 32)
+    tc = tq.Codes(cb, 1, 32, TQ_LAYOUT_TILE32)      # QJL signs have no tile32 layout
+    tc.sign = torch.zeros(32 * 16, dtype=torch.uint8, device=dev)
     with pytest.raises(tq.TQError) as e:
-        tq.tq_quantize_kv(big, None, torch.zeros((1, 4, 200), device=dev), None, bc, None)
+        tq.tq_quantize_kv(cb, None, torch.zeros((1, 4, 128), device=dev), None, tc, None)
     assert e.value.status == 2
 
 
