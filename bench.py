@@ -13,6 +13,12 @@ Printed: ONE JSON line with the contract fields plus
   recorded on its stream around every launch in the timed region;
 * quantize: tq_quantize_kv bandwidth on the quantize-only layer
   (B=16, 8 KV heads, d=128, 32768 tokens, bf16 K and V, 4-bit, no QJL);
+* bit_sweep: decode KV tokens/s, HBM fraction and error against exact
+  attention for k8v4, k4v4, k3v4, k3v3, k2v2 on the 32K GQA layer
+  (B=32, 32 query / 4 KV heads);
+* vector_search: tq_ip_topk queries/s, MFMA rate and recall on 1e6 coded
+  vectors of d=200 with 1000 queries;
+* copy_GBps: the box's device-to-device copy rate (1 GiB);
 * cpu_baseline: the float64 CPU oracle timed on a bounded sample.
 """
 from __future__ import annotations
@@ -52,6 +58,8 @@ def split_traffic():
         return int(kv["traffic_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
         return None
+
+
 METRIC = "KV tokens/s in compressed decode attention & quantize GB/s, % of HBM peak"
 
 
@@ -62,6 +70,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-quantize", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the bit-width sweep leg")
+    ap.add_argument("--no-search", action="store_true", help="skip the vector-search leg")
     ap.add_argument("--calib-copy", action="store_true",
                     help="accepted for profiling commands; the 1 GiB copy always runs")
     return ap.parse_args()
@@ -138,9 +148,153 @@ def quantize_leg(torch, tq, synth, dev, iters, warm):
                 bytes_per_call=int(in_bytes + out_bytes))
 
 
-def cpu_baseline(torch, O, W, n_pairs=2):
+def _exact_attention_np(q, k, v, tau):
+    """float64 softmax(tau q k^T) v on the raw (bf16) inputs of one KV head;
+    q [g, d], k/v [N, d] -> (logits [g, N], out [g, d])."""
+    lg = tau * (q @ k.T)
+    p = np.exp(lg - lg.max(axis=1, keepdims=True))
+    return lg, (p / p.sum(axis=1, keepdims=True)) @ v
+
+
+def bit_sweep_leg(torch, tq, synth, dev, iters, warm):
+    """Bit-width sweep on the 32K GQA layer (B=32, 32 query / 4 KV heads,
+    d=128, context 32768, bf16 K/V as the 128K layer, no QJL): per variant
+    the decode KV tokens/s and HBM fraction of the split kernel, and the error
+    of the outputs and logits against exact float64 attention on the raw
+    inputs for two sampled (batch, KV head) rows."""
+    B, Hq, Hkv, d, N = 32, 32, 4, 128, 32768
+    g = Hq // Hkv
+    tau = 1.0 / math.sqrt(d)
+    k = synth.kv_gaussian(B, Hkv, N, d, 20, dtype="bf16", device=dev, channels=[3, 77, 101], factor=20.0)
+    v = synth.kv_gaussian(B, Hkv, N, d, 21, dtype="bf16", device=dev, channels=[3, 77, 101], factor=20.0)
+    q = synth.queries_gaussian(B, Hq, d, 22, dtype="bf16", device=dev)
+    kf, vf = k.view(B * Hkv, N, d), v.view(B * Hkv, N, d)
+    rows = [(0, 0), (B - 1, Hkv - 1)]
+    ref = {}
+    for (b, h) in rows:
+        ref[(b, h)] = _exact_attention_np(q[b, h * g:(h + 1) * g].float().cpu().numpy().astype(np.float64),
+                                          k[b, h].float().cpu().numpy().astype(np.float64),
+                                          v[b, h].float().cpu().numpy().astype(np.float64), tau)
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    logits = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+    ws = torch.empty(tq.tq_attn_decode_workspace(B, Hq, Hkv, N, d), dtype=torch.uint8, device=dev)
+    res = []
+    for name, kb, vb, nc in [("k8v4", 8, 4, True), ("k4v4", 4, 4, True), ("k3v4", 3, 4, True),
+                             ("k3v3", 3, 3, True), ("k2v2", 2, 2, True), ("k2v2 nc off", 2, 2, False)]:
+        kcb = tq.Codebook(d, kb, norm_correction=nc, rot_seed=1)
+        vcb = tq.Codebook(d, vb, norm_correction=nc, rot_seed=3)
+        kc = tq.Codes(kcb, B * Hkv, N, tq.TQ_LAYOUT_ROW)
+        vc = tq.Codes(vcb, B * Hkv, N, tq.TQ_LAYOUT_TILE32)
+        tq.tq_quantize_kv(kcb, vcb, kf, vf, kc, vc)
+        tq.tq_attn_decode(kcb, vcb, q, kc, vc, N, tau, out=out, logits=logits, workspace=ws)
+        torch.cuda.synchronize()
+        errs = dict(out_rel_l2=0.0, out_cos_min=1.0, logit_max_abs=0.0)
+        for (b, h) in rows:
+            lg_e, o_e = ref[(b, h)]
+            o_g = out[b, h * g:(h + 1) * g].cpu().numpy().astype(np.float64)
+            lg_g = logits[b, h * g:(h + 1) * g].cpu().numpy().astype(np.float64)
+            errs["out_rel_l2"] = max(errs["out_rel_l2"], float(np.linalg.norm(o_g - o_e) / np.linalg.norm(o_e)))
+            cos = np.sum(o_g * o_e, axis=1) / (np.linalg.norm(o_g, axis=1) * np.linalg.norm(o_e, axis=1))
+            errs["out_cos_min"] = min(errs["out_cos_min"], float(cos.min()))
+            errs["logit_max_abs"] = max(errs["logit_max_abs"], float(np.max(np.abs(lg_g - lg_e))))
+        for _ in range(warm):
+            tq.tq_attn_decode(kcb, vcb, q, kc, vc, N, tau, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        tq.tq_profile_enable(True)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            tq.tq_attn_decode(kcb, vcb, q, kc, vc, N, tau, out=out, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        tq.tq_profile_enable(False)
+        ms = e0.elapsed_time(e1) / iters
+        sms, sn = tq.tq_profile_read(tq.TQ_KERNEL_DECODE_SPLIT)
+        split_ms = sms / max(1, sn)
+        bpt = kb * d // 8 + 4 + vb * d // 8 + 4
+        gbs = bpt * B * Hkv * N / (split_ms * 1e-3) / 1e9
+        res.append(dict(variant=name, KV_tokens_per_s=round(B * N / (ms * 1e-3), 1),
+                        ms_per_decode=round(ms, 4), split_kernel_ms=round(split_ms, 4),
+                        bytes_per_token_head=bpt, split_GBps=round(gbs, 1),
+                        frac_hbm=round(gbs / HBM_PEAK_GBS, 4),
+                        **{kk: round(vv, 6) for kk, vv in errs.items()}))
+        del kc, vc, kcb, vcb
+    del k, v
+    return dict(workload="bit sweep: B=32, Hq=32, Hkv=4, d=128, context 32768, bf16 K/V N(0,1) "
+                         "with channels 3/77/101 x20, no QJL; errors vs exact float64 attention "
+                         "on the raw inputs of (b=0,h=0) and (b=31,h=3)",
+                variants=res)
+
+
+def vector_search_leg(torch, tq, synth, dev, iters, warm):
+    """1,000,000 unit-norm vectors d=200 (256-cluster mixture), 4-bit + QJL
+    m=200 codes, 1000 queries, k=10: queries/s of tq_ip_topk, MFMA
+    utilisation of its score kernel and recall@10 against the exact top-10
+    of the raw vectors."""
+    d, n_db, nq, k, m = 200, 1_000_000, 1000, 10, 200
+    db = synth.mixture_db(n_db, d, 256, seed=7, device=dev)
+    qs = synth.mixture_db(nq, d, 256, seed=8, device=dev)
+    cb = tq.Codebook(d, 4, qjl_m=m, rot_seed=1, qjl_seed=2)
+    codes = tq.Codes(cb, 1, n_db, tq.TQ_LAYOUT_ROW)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    tq.tq_quantize_kv(cb, None, db[None], None, codes, None)
+    c1.record()
+    torch.cuda.synchronize()
+    quant_ms = c0.elapsed_time(c1)
+    ws = torch.empty(tq.tq_ip_topk_workspace(nq, n_db, k, d), dtype=torch.uint8, device=dev)
+    gi = torch.empty((nq, k), dtype=torch.int64, device=dev)
+    gs = torch.empty((nq, k), dtype=torch.float32, device=dev)
+    for _ in range(warm):
+        tq.tq_ip_topk(cb, qs, codes, n_db, k, out_idx=gi, out_score=gs, workspace=ws)
+    torch.cuda.synchronize()
+    tq.tq_profile_enable(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        tq.tq_ip_topk(cb, qs, codes, n_db, k, out_idx=gi, out_score=gs, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    tq.tq_profile_enable(False)
+    ms = e0.elapsed_time(e1) / iters
+    sms, sn = tq.tq_profile_read(tq.TQ_KERNEL_TOPK)
+    score_ms = sms / max(1, sn)
+    # MFMA work the score kernel issues: per 8-query block and 16-row tile,
+    # dp/16 centroid MFMAs and ceil(m/32) sign MFMAs of 16x16x32 (16384 flop)
+    dp = (d + 31) // 32 * 32
+    n_mfma = ((nq + 7) // 8) * ((n_db + 15) // 16) * (dp // 16 + (m + 31) // 32)
+    mfma_tflops = n_mfma * 16384 / (score_ms * 1e-3) / 1e12
+    useful = nq * n_db * (2 * d + 2 * m)
+    # exact top-10 of the raw vectors (fp32 matmul, chunked) for recall
+    ex_s = torch.full((nq, k), -float("inf"), device=dev)
+    ex_i = torch.zeros((nq, k), dtype=torch.int64, device=dev)
+    for s in range(0, n_db, 250000):
+        sc = qs @ db[s:s + 250000].T
+        cs, ci = torch.topk(sc, k, dim=1)
+        allv = torch.cat([ex_s, cs], dim=1)
+        alli = torch.cat([ex_i, ci + s], dim=1)
+        ex_s, pos = torch.topk(allv, k, dim=1)
+        ex_i = torch.gather(alli, 1, pos)
+    hit = (gi[:, :, None] == ex_i[:, None, :]).any(dim=2).sum().item()
+    hit1 = (gi == ex_i[:, :1]).any(dim=1).sum().item()
+    del db, codes
+    return dict(workload="vector search: 1e6 unit-norm vectors d=200 (256-cluster mixture), "
+                         "4-bit + QJL m=200, 1000 queries, top-10",
+                queries_per_s=round(nq / (ms * 1e-3), 1), ms_per_call=round(ms, 4),
+                score_kernel_ms=round(score_ms, 4),
+                mfma_TFLOPs=round(mfma_tflops, 1),
+                mfma_frac_bf16_peak=round(mfma_tflops / 2500.0, 4),
+                useful_TFLOPs=round(useful / (ms * 1e-3) / 1e12, 1),
+                recall_10_at_10=round(hit / (nq * k), 4),
+                recall_1_at_10=round(hit1 / nq, 4),
+                quantize_db_ms=round(quant_ms, 3))
+
+
+def cpu_baseline(torch, O, W, budget_s=10.0):
     """float64 oracle: per sampled (batch, KV head) pair, quantize the step's
-    new vectors and decode its 8 query heads over the full context."""
+    new vectors and decode its 8 query heads over the full context; pairs are
+    taken in a fixed shuffled order until about budget_s of timed CPU work."""
     try:
         from threadpoolctl import threadpool_info
         threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
@@ -150,10 +304,15 @@ def cpu_baseline(torch, O, W, n_pairs=2):
     g = Hq // Hkv
     okc = O.Codebook(d, 3, qjl_m=128, rot_seed=1, qjl_seed=2)
     ovc = O.Codebook(d, 4, rot_seed=3)
-    pairs = [(0, 0), (B - 1, Hkv - 1), (B // 2, Hkv // 2)][:n_pairs]
+    order = np.random.default_rng(123).permutation(B * Hkv)
+    pairs = [(int(x) // Hkv, int(x) % Hkv) for x in order]
     q64 = W["q"].float().cpu().numpy().astype(np.float64)
     t_total = 0.0
+    done = 0
     for (b, h) in pairs:
+        if t_total >= budget_s:
+            break
+        done += 1
         k64 = W["k"][b, h].float().cpu().numpy().astype(np.float64)
         v64 = W["v"][b, h].float().cpu().numpy().astype(np.float64)
         rk = O.quantize(okc, k64[:N - 1])          # cache build (untimed)
@@ -165,10 +324,10 @@ def cpu_baseline(torch, O, W, n_pairs=2):
         vd = {n: np.concatenate([rv[n], nv[n]])[None, None] for n in ("idx", "scale")}
         O.attn_decode(okc, ovc, q64[b:b + 1, h * g:(h + 1) * g], kd, vd, W["tau"])
         t_total += time.perf_counter() - t0
-    kv_tokens = len(pairs) * N / Hkv         # each pair is 1/Hkv of a batch row
+    kv_tokens = done * N / Hkv               # each pair is 1/Hkv of a batch row
     return dict(value=round(kv_tokens / t_total, 1), unit="KV tokens/s", cores=int(threads),
                 kind="oracle",
-                sample=f"{len(pairs)} of {B * Hkv} (batch, KV head) pairs of the decode-128k layer at "
+                sample=f"{done} of {B * Hkv} (batch, KV head) pairs of the decode-128k layer at "
                        f"full context {N}, all {g} query heads each, float64; "
                        f"{t_total:.1f} s of CPU time, scaled to KV tokens/s")
 
@@ -240,6 +399,14 @@ def main():
         print("[bench] quantize leg", file=sys.stderr, flush=True)
         res["quantize"] = quantize_leg(torch, tq, synth, dev, iters=max(5, args.steps // 2),
                                        warm=max(1, args.warmup // 2))
+    if not args.no_sweep:
+        print("[bench] bit-width sweep leg", file=sys.stderr, flush=True)
+        res["bit_sweep"] = bit_sweep_leg(torch, tq, synth, dev, iters=max(5, args.steps // 2),
+                                         warm=max(1, args.warmup // 2))
+    if not args.no_search:
+        print("[bench] vector-search leg", file=sys.stderr, flush=True)
+        res["vector_search"] = vector_search_leg(torch, tq, synth, dev, iters=max(3, args.steps // 5),
+                                                 warm=max(1, args.warmup // 5))
     # achievable device-to-device copy rate of this machine (1 GiB read + 1 GiB
     # written per copy); with --calib-copy it is also the counter calibration
     src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
