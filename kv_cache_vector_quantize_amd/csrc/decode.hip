@@ -349,7 +349,7 @@ struct Tile {
   uint32_t kw[2][BK];   // key index bits of this lane's token (per 16-token block)
   uint32_t sw[2];       // QJL sign word
   uint32_t vr[2 * BV];  // value record: 8 coordinates x 8 token slots
-  float sc0, sc1;       // per-token scalars staged through LDS
+  float ks, kr, vs;     // per-token scalars of token (lane % 32), staged through LDS
 };
 
 template <int BK, int BV, bool QJL>
@@ -373,7 +373,7 @@ __global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_e
   }
   __syncthreads();
 
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int c16 = lane & 15, g4 = lane >> 4;
   const int part = blockIdx.x * kWaves + wave;
   const uint32_t laneoff = (uint32_t)(lane & 31) << 3;
@@ -400,58 +400,76 @@ __global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_e
   }
   const float cinit = QJL ? reinterpret_cast<const float*>(a.qop + (int64_t)row * QOP_DWORDS)[QOP_Q + QOP_T + c16] : 0.f;
   const float sel_lo = (c16 >= 8) ? 1.f : 0.f;
-  static_assert(kSignShift == 64, "sc0mul below is 2^kSignShift");
-  const float sc0mul = (QJL && lane >= 32) ? 0x1p64f : 1.f;     // 2^kSignShift on the residual norms
+  static_assert(kSignShift == 64, "the staged residual norms carry 2^kSignShift");
 
   float M = -INFINITY, l = 0.f;
+  float Meff = 0.f, nhm = 0.f, lazy_thr = -INFINITY;   // see the softmax below
   f32x4 acc_o[8];
 #pragma unroll
   for (int db = 0; db < 8; ++db) acc_o[db] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  // per-sequence (uniform) bases and 32-bit lane offsets
-  const char* kbase = reinterpret_cast<const char*>(a.kidx) + seq * a.k_stride * a.k_pitch;
-  const uint32_t klane = (uint32_t)(c16 * a.k_pitch + g4 * BK * 4);
-  const uint32_t kblk = (uint32_t)(16 * a.k_pitch);
-  const uint32_t* sbase = QJL ? a.ksign + seq * a.k_stride * (a.ks_pitch >> 2) : nullptr;
-  const uint32_t slane = (uint32_t)(c16 * (a.ks_pitch >> 2) + g4);
-  const uint32_t sblk = (uint32_t)(16 * (a.ks_pitch >> 2));
-  const bool sign_lane = QJL && (32 * g4 < a.m);
+  // Tile loads are raw buffer loads: one descriptor per plane of the
+  // sequence (uniform), a per-lane byte offset that is the same for every
+  // tile (VGPR) and the tile's uniform byte offset (SGPR).  Offsets stay below
+  // 2^31: the host checks the size of a sequence's planes.
+  auto rsrc = [](const void* base) {
+    const uint64_t v = reinterpret_cast<uint64_t>(base);
+    // (readfirstlane returns int: widen through uint32_t, never by sign extension)
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    const uint64_t u = ((uint64_t)hi << 32) | (uint64_t)lo;    // uniform by construction
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(u), (short)0, (int)0x7FFFFFFF, 0x00020000);
+  };
+  const auto rk = rsrc(reinterpret_cast<const char*>(a.kidx) + seq * a.k_stride * a.k_pitch);
+  const int klane0 = c16 * (int)a.k_pitch + g4 * BK * 4;
+  const int klane1 = klane0 + 16 * (int)a.k_pitch;
+  const auto rs = rsrc(QJL ? reinterpret_cast<const char*>(a.ksign) + seq * a.k_stride * a.ks_pitch
+                           : reinterpret_cast<const char*>(a.kidx));
+  // sign word g4 of the row; lanes past the row read word 0 (their sketch
+  // rows have t = 0 in the query operand, so those bits add nothing)
+  const int slane0 = c16 * (int)a.ks_pitch + 4 * (4 * g4 < a.ks_pitch ? g4 : 0);
+  const int slane1 = slane0 + 16 * (int)a.ks_pitch;
   constexpr int VBLK = 64 * 8 * BV / 4;                  // dwords per tile32 block (d = 128)
-  const uint32_t* vbase = a.vidx + seq * (a.v_stride / 32) * (int64_t)VBLK;
-  const uint32_t vlane = (uint32_t)((16 * g4 + c16) * 2 * BV);
-  const float* sc0base = (lane < 32) ? a.kscale + seq * a.k_stride + lane
-                                     : (QJL ? a.krnorm + seq * a.k_stride + (lane - 32) : a.kscale + seq * a.k_stride);
-  const float* sc1base = a.vscale + seq * a.v_stride + (lane & 31);
+  const auto rv = rsrc(a.vidx + seq * (a.v_stride / 32) * (int64_t)VBLK);
+  const int vlane = (16 * g4 + c16) * 2 * BV * 4;
+  const auto rks = rsrc(a.kscale + seq * a.k_stride);
+  const auto rkr = rsrc(QJL ? a.krnorm + seq * a.k_stride : a.kscale);
+  const auto rvs = rsrc(a.vscale + seq * a.v_stride);
+  const int sl4 = (lane & 31) * 4;
   float* stage = &s_sc[wave][0];
 
   auto load = [&](Tile<BK, BV>& T, const int64_t t0) {
-    const uint32_t t32 = (uint32_t)(t0 - 0);
+    const int t = __builtin_amdgcn_readfirstlane((int)t0);
+    const int kt = t * (int)a.k_pitch;
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      const uint32_t* src = reinterpret_cast<const uint32_t*>(kbase + (t32 * (uint32_t)a.k_pitch + blk * kblk + klane));
-#pragma unroll
-      for (int i = 0; i < BK; ++i) T.kw[blk][i] = src[i];
-      T.sw[blk] = 0u;
-      if constexpr (QJL) {
-        if (sign_lane) T.sw[blk] = sbase[t32 * (uint32_t)(a.ks_pitch >> 2) + blk * sblk + slane];
-      }
+    for (int i = 0; i < BK; ++i) {
+      T.kw[0][i] = __builtin_amdgcn_raw_buffer_load_b32(rk, klane0 + 4 * i, kt, 0);
+      T.kw[1][i] = __builtin_amdgcn_raw_buffer_load_b32(rk, klane1 + 4 * i, kt, 0);
     }
-    const uint32_t* vsrc = vbase + (t32 / 32) * (uint32_t)VBLK + vlane;
+    T.sw[0] = T.sw[1] = 0u;
+    if constexpr (QJL) {
+      const int st = t * (int)a.ks_pitch;
+      T.sw[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, slane0, st, 0);
+      T.sw[1] = __builtin_amdgcn_raw_buffer_load_b32(rs, slane1, st, 0);
+    }
+    const int vt = (t >> 5) * VBLK * 4;
     if constexpr (BV == 4 || BV == 2 || BV == 8) {
 #pragma unroll
       for (int i = 0; i < 2 * BV; i += 4) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(vsrc + i);
+        const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, vlane + 4 * i, vt, 0));
         T.vr[i] = v[0]; T.vr[i + 1] = v[1]; T.vr[i + 2] = v[2]; T.vr[i + 3] = v[3];
       }
     } else {
 #pragma unroll
       for (int i = 0; i < 2 * BV; i += 2) {
-        const uint2 v = *reinterpret_cast<const uint2*>(vsrc + i);
-        T.vr[i] = v.x; T.vr[i + 1] = v.y;
+        typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+        const u32x2v v = __builtin_bit_cast(u32x2v, __builtin_amdgcn_raw_buffer_load_b64(rv, vlane + 4 * i, vt, 0));
+        T.vr[i] = v[0]; T.vr[i + 1] = v[1];
       }
     }
-    T.sc0 = sc0base[t32];
-    T.sc1 = sc1base[t32];
+    T.ks = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rks, sl4, 4 * t, 0));
+    T.kr = QJL ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rkr, sl4, 4 * t, 0)) : 0.f;
+    T.vs = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rvs, sl4, 4 * t, 0));
   };
 
   // value operands of coordinate block db (4 lookups = token slot pairs)
@@ -477,8 +495,8 @@ __global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_e
     constexpr bool partial = decltype(partial_tag)::value;
     // per-token scalars: 96 floats through the wave's LDS slot (the residual
     // norms carry back the power of two the sign operand takes out)
-    stage[lane] = T.sc0 * sc0mul;
-    stage[64 + (lane & 31)] = T.sc1;
+    stage[lane] = (QJL && lane >= 32) ? T.kr * 0x1p64f : T.ks;
+    stage[64 + (lane & 31)] = T.vs;
     // ---- key operands of block 0: all 16 lookups in flight
     uint2 ek[8][2];
 #pragma unroll
@@ -515,6 +533,9 @@ __global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_e
       acc[1] = mfma(as_bf16x8(ek[u][0].x, ek[u][0].y, ek[u][1].x, ek[u][1].y), qa[u], acc[1]);
       if (u & 1) vlook(T, u >> 1, ev[u >> 1]);
     }
+    // lg = logit - Meff (base 2): the scales are applied per column before the
+    // hi and lo columns are summed (both columns of a row share the token), and
+    // each column carries -Meff/2
     float lg[2][4];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
@@ -523,10 +544,9 @@ __global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_e
       if constexpr (QJL) kr = *reinterpret_cast<const f32x4*>(stage + 32 + 16 * blk + 4 * g4);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float mse = acc[blk][r] + dpp_ror8(acc[blk][r]);
-        float v = ks[r] * mse;
-        if constexpr (QJL) v = fmaf(kr[r], accq[blk][r] + dpp_ror8(accq[blk][r]), v);
-        lg[blk][r] = v;
+        float u = fmaf(ks[r], acc[blk][r], nhm);
+        if constexpr (QJL) u = fmaf(kr[r], accq[blk][r], u);
+        lg[blk][r] = u + dpp_ror8(u);
       }
     }
     if constexpr (partial) {
@@ -545,24 +565,34 @@ __global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_e
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int tt = 16 * blk + 4 * g4 + r;
-            if (t0 + tt < a.n_ctx) dst[tt] = lg[blk][r] * LN2;
+            if (t0 + tt < a.n_ctx) dst[tt] = (lg[blk][r] + Meff) * LN2;
           }
       }
     }
 
     // ---- online softmax in base 2; the reference maximum M moves only when
-    // a logit exceeds it by more than LAZY (then exactly, per query column)
+    // a logit exceeds it by more than LAZY (then exactly, per query column).
+    // lg holds logit - Meff with Meff = M (0 while M = -inf).
     float lm = fmaxf(fmaxf(fmaxf(lg[0][0], lg[0][1]), fmaxf(lg[0][2], lg[0][3])),
                      fmaxf(fmaxf(lg[1][0], lg[1][1]), fmaxf(lg[1][2], lg[1][3])));
-    if (__builtin_expect(__ballot(lm > M + LAZY) != 0ull, 0)) {
+    if (__builtin_expect(__ballot(lm > lazy_thr) != 0ull, 0)) {
       float mt = fmaxf(lm, __shfl_xor(lm, 16));
       mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float Mn = fmaxf(M, mt);
+      const float Mn = fmaxf(M, mt + Meff);
       const float alpha = (Mn == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(M - Mn);
       l *= alpha;
 #pragma unroll
       for (int db = 0; db < 8; ++db) acc_o[db] *= alpha;
+      const float Mneff = (Mn == -INFINITY) ? 0.f : Mn;
+      const float shift = Meff - Mneff;
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) lg[blk][r] += shift;
       M = Mn;
+      Meff = Mneff;
+      nhm = -0.5f * Meff;
+      lazy_thr = (M == -INFINITY) ? -INFINITY : LAZY;
     }
     const f32x4 vs0 = *reinterpret_cast<const f32x4*>(stage + 64 + 4 * g4);
     const f32x4 vs1 = *reinterpret_cast<const f32x4*>(stage + 80 + 4 * g4);
@@ -571,7 +601,7 @@ __global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_e
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float p = __builtin_amdgcn_exp2f(lg[blk][r] - M);
+        const float p = __builtin_amdgcn_exp2f(lg[blk][r]);
         l += p;
         w[blk][r] = p * (blk == 0 ? vs0[r] : vs1[r]);
       }

@@ -366,6 +366,14 @@ tq_status tq_attn_decode(const tq_codebook* kcb, const tq_codebook* vcb, const v
     if (s != TQ_OK) return s;
     if ((s = current_device_matches(kcb)) != TQ_OK) return s;
     if ((s = current_device_matches(vcb)) != TQ_OK) return s;
+    {
+      // the split kernel addresses one sequence's planes with 32-bit byte offsets
+      const int64_t lim = 0x7FFFFFFFLL;
+      const int64_t vblk = 64LL * ((vcb->p.d + 15) / 16) * vcb->p.bits;
+      if (k->seq_stride * k->idx_row_bytes >= lim || k->seq_stride * k->sign_row_bytes >= lim ||
+          (v->seq_stride / 32) * vblk >= lim || 4 * k->seq_stride >= lim || 4 * v->seq_stride >= lim)
+        return fail(TQ_ERR_UNSUPPORTED, "a sequence's code planes must each stay below 2 GiB");
+    }
     const DecodePlan plan = plan_decode(B, Hq, Hkv, n_ctx, kcb->p.d);
     if (plan.rows > 65535 || B * Hq > 0x7FFFFFFF)
       return fail(TQ_ERR_UNSUPPORTED, "B * Hkv * ceil(g/8) must be <= 65535");
