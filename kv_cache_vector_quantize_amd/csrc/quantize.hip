@@ -49,16 +49,6 @@ __device__ inline float load_elem(const void* p, int64_t i) {
   }
 }
 
-// tile32 element q of a block (q-th b-bit field of its bit stream) ->
-// (coordinate i, token t): q = (r*ndb + j)*8 + e, record r = 16*G + C holds
-// coordinate 16*j + C for the tokens 4*G + e%4 + 16*(e/4).
-__device__ inline void tile32_element(int q, int ndb, int& i, int& t) {
-  const int e = q & 7, rj = q >> 3;
-  const int j = rj % ndb, r = rj / ndb;
-  i = 16 * j + (r & 15);
-  t = 4 * (r >> 4) + (e & 3) + 16 * (e >> 2);
-}
-
 // WIDE = false (dp <= 128): one wave per 32-column block of Pi (and of S),
 // whose B operand stays in registers.  WIDE = true (dp up to 256): four waves
 // loop over the column blocks and stream the B operand from L2 (each row of
@@ -124,13 +114,40 @@ __global__ void __launch_bounds__(WIDE ? 256 : 512) k_quantize(QArgs a) {
       const int64_t p = abs0 + tid;
       s_valid[tid] = (p >= a.tok_off && p < a.tok_off + a.n_tok) ? 1 : 0;
     }
-    for (int e = tid; e < TILE * DP; e += nthr) {
-      const int r = e / DP, i = e % DP;
-      const int64_t p = abs0 + r;
-      float v = 0.f;
-      if (i < a.d && p >= a.tok_off && p < a.tok_off + a.n_tok)
-        v = load_elem<DT>(a.x, (src0 + r) * a.d + i);
-      xs[r][i] = v;
+    const bool full_tile = abs0 >= a.tok_off && abs0 + TILE <= a.tok_off + a.n_tok;
+    if (full_tile && a.d == DP && (reinterpret_cast<uintptr_t>(a.x) & 15) == 0) {
+      // the tile's 32 rows are contiguous in the input: 16-byte loads
+      constexpr int EPV = DT == TQ_F32 ? 4 : 8;          // elements per 16 bytes
+      const char* base = static_cast<const char*>(a.x) + src0 * DP * (DT == TQ_F32 ? 4 : 2);
+      for (int c = tid; c < TILE * DP / EPV; c += nthr) {
+        const uint4 u = reinterpret_cast<const uint4*>(base)[c];
+        const int e0 = c * EPV, r = e0 / DP, i0 = e0 % DP;
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+        if constexpr (DT == TQ_F32) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) xs[r][i0 + k] = __uint_as_float(w[k]);
+        } else {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            if constexpr (DT == TQ_BF16) {
+              xs[r][i0 + 2 * k] = __uint_as_float(w[k] << 16);
+              xs[r][i0 + 2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+            } else {
+              xs[r][i0 + 2 * k] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[k] & 0xFFFFu));
+              xs[r][i0 + 2 * k + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[k] >> 16));
+            }
+          }
+        }
+      }
+    } else {
+      for (int e = tid; e < TILE * DP; e += nthr) {
+        const int r = e / DP, i = e % DP;
+        const int64_t p = abs0 + r;
+        float v = 0.f;
+        if (i < a.d && p >= a.tok_off && p < a.tok_off + a.n_tok)
+          v = load_elem<DT>(a.x, (src0 + r) * a.d + i);
+        xs[r][i] = v;
+      }
     }
     __syncthreads();
 
@@ -257,7 +274,9 @@ __global__ void __launch_bounds__(WIDE ? 256 : 512) k_quantize(QArgs a) {
         dst[w] = (uint32_t)(accw >> 32);
       }
     } else {
-      // tile32: the block's bit stream is 64 records x ndb groups x 8 fields
+      // tile32: the block's bit stream is 64 records x ndb groups x 8 fields;
+      // field q = (r*ndb + j)*8 + e of record r = 16*G + C holds coordinate
+      // 16*j + C of token 4*G + e%4 + 16*(e/4)
       bool full = true;
       for (int r = 0; r < TILE; ++r) full = full && s_valid[r];
       const int ndb = (a.d + 15) / 16;
@@ -269,13 +288,19 @@ __global__ void __launch_bounds__(WIDE ? 256 : 512) k_quantize(QArgs a) {
         const int q0 = bit0 / b;
         const int q1 = (bit0 + 31) / b;
         uint64_t val = 0, msk = 0;
+        // walk the fields q0..q1: field q = (r*ndb + j)*8 + e, one division per word
+        int e = q0 & 7, j = (q0 >> 3) % ndb, r = (q0 >> 3) / ndb;
         for (int q = q0; q <= q1; ++q) {
-          int i, t;
-          tile32_element(q, ndb, i, t);
+          const int i = 16 * j + (r & 15);
+          const int t = 4 * (r >> 4) + (e & 3) + 16 * (e >> 2);
           const int sh = q * b - bit0 + 32;
           if (s_valid[t]) {
             if (i < a.d) val |= (uint64_t)ids[t][i] << sh;
             msk |= (uint64_t)((1u << b) - 1u) << sh;
+          }
+          if (++e == 8) {
+            e = 0;
+            if (++j == ndb) { j = 0; ++r; }
           }
         }
         const uint32_t nv = (uint32_t)(val >> 32), nm = (uint32_t)(msk >> 32);
@@ -515,6 +540,7 @@ bool quantize_supported(const tq_codebook* cb) {
 }
 
 hipError_t launch_quantize(const tq_codebook* cb, const QuantJob& job, hipStream_t stream) {
+  if (quantize128_supported(cb, job)) return launch_quantize128(cb, job, stream);
   QArgs a{};
   a.x = job.x;
   a.n_tok = job.n_tok;

@@ -1,6 +1,7 @@
 // C-ABI front end: argument validation, codebook upload, kernel dispatch.
 // Every exported function catches everything and reports through
 // tq_last_error(); no exception crosses the ABI.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -32,6 +33,59 @@ void split_bf16(double c, uint16_t& hi, uint16_t& lo) {
   lo = bf16_rne((float)(c - (double)bf16_to_f(hi)));
 }
 
+// bf16 MFMA operands of Pi (row-major, 128 x 128) in three parts hi + lo +
+// lo2 (Pi - hi - lo - lo2 is below 2^-26 |Pi|): uint4 [4][8][3][64], lane l
+// of wave w at k-step s holds Pi[32w + l%32][16s + 8(l/32) + j], j = 0..7,
+// two bf16 per dword (lower column in the low half).
+void build_q128_operands(const std::vector<double>& M, std::vector<uint32_t>& out) {
+  out.assign((size_t)4 * 8 * 3 * 64 * 4, 0u);
+  for (int w = 0; w < 4; ++w)
+    for (int s = 0; s < 8; ++s)
+      for (int l = 0; l < 64; ++l) {
+        const int r = 32 * w + (l & 31);
+        for (int j = 0; j < 8; ++j) {
+          const int c = 16 * s + 8 * (l >> 5) + j;
+          double rest = M[(size_t)r * 128 + c];
+          for (int part = 0; part < 3; ++part) {
+            const uint16_t h = bf16_rne((float)rest);
+            rest -= (double)bf16_to_f(h);
+            const size_t base = ((((size_t)w * 8 + s) * 3 + part) * 64 + l) * 4;
+            out[base + j / 2] |= (uint32_t)h << (16 * (j & 1));
+          }
+        }
+      }
+}
+
+// Index cells over y in [-1, 1] for the fp32 boundaries t: cell width 1/G is
+// below 0.9 x the smallest gap between consecutive boundaries, so a cell holds
+// at most one.  Entry c = {#t < c/G - 1, bits of the t inside the cell or of
+// 2.0f}.  Returns false when the table would exceed kQ128Cells entries.
+bool build_q128_cells(const std::vector<float>& t, std::vector<uint32_t>& out, float& G_out) {
+  double gap = 2.0;
+  for (size_t k = 1; k < t.size(); ++k) gap = std::min(gap, (double)t[k] - (double)t[k - 1]);
+  if (!(gap > 0.0)) return false;
+  const double G = std::ceil(1.0 / (0.9 * gap));
+  const int64_t cells = 2 * (int64_t)G + 1;
+  if (cells > kQ128Cells) return false;
+  out.assign((size_t)cells * 2, 0u);
+  for (int64_t c = 0; c < cells; ++c) {
+    const double lo = (double)c / G - 1.0, hi = (double)(c + 1) / G - 1.0;
+    uint32_t below = 0, inside = 0;
+    float p = 2.0f;
+    for (float v : t) {
+      if ((double)v < lo) ++below;
+      else if ((double)v < hi) { ++inside; p = v; }
+    }
+    if (inside > 1) return false;
+    uint32_t pb;
+    std::memcpy(&pb, &p, 4);
+    out[2 * c] = below;
+    out[2 * c + 1] = pb;
+  }
+  G_out = (float)G;
+  return true;
+}
+
 tq_status fail(tq_status s, const std::string& msg) {
   g_err = msg;
   return s;
@@ -51,6 +105,8 @@ void free_dev(DeviceCodebook& d) {
   if (d.rotT) (void)hipFree(d.rotT);
   if (d.qjlT) (void)hipFree(d.qjlT);
   if (d.pair_tab) (void)hipFree(d.pair_tab);
+  if (d.rop) (void)hipFree(d.rop);
+  if (d.qtab) (void)hipFree(d.qtab);
   d = DeviceCodebook{};
 }
 
@@ -225,6 +281,22 @@ tq_status tq_codebook_build(const tq_params* params, tq_codebook** out) {
         free_dev(cb->dev);
         delete cb;
         return hip_fail(e, "codebook upload");
+      }
+    }
+    if (d == 128 && m == 0) {
+      // operands and index cells of the d = 128 quantize kernel
+      std::vector<uint32_t> rop, qtab;
+      float qG = 0.f;
+      build_q128_operands(cb->host.rot, rop);
+      if (build_q128_cells(bnd, qtab, qG)) {
+        if ((e = upload(&cb->dev.rop, rop)) != hipSuccess ||
+            (e = upload(&cb->dev.qtab, qtab)) != hipSuccess) {
+          free_dev(cb->dev);
+          delete cb;
+          return hip_fail(e, "codebook upload");
+        }
+        cb->dev.qcells = (int)(qtab.size() / 2);
+        cb->dev.qG = qG;
       }
     }
     *out = cb;

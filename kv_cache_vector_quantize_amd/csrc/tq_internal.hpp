@@ -35,7 +35,21 @@ struct DeviceCodebook {
   //  bits  > 4: entry a holds one dword {hi(c[a]) | lo(c[a]) << 16}
   uint32_t* pair_tab = nullptr;
   int pair_tab_dwords = 0;
+  // d = 128 quantize (see quantize128.hip), absent for other d:
+  //  rop: Pi as bf16 operands of v_mfma_f32_32x32x16_bf16 in three parts
+  //  (hi, lo, lo2), uint4 [wave 4][k-step 8][part 3][lane 64]; lane l of wave
+  //  w, step s holds Pi[32w + l%32][16s + 8(l/32) + 0..7]
+  //  qtab: index cells of y in [-1, 1]: cell c = floor((y + 1) * qG) covers
+  //  [c/qG - 1, (c+1)/qG - 1) and holds {#boundaries below it, the boundary
+  //  inside it (fp32 bits) or 2.0f}; cells are narrower than the closest pair
+  //  of boundaries, so at most one lies inside
+  uint32_t* rop = nullptr;
+  uint32_t* qtab = nullptr;
+  int qcells = 0;
+  float qG = 0.f;
 };
+
+constexpr int kQ128Cells = 2048;   // largest index-cell table the d = 128 kernel stages
 
 // padded sizes used by the kernels
 inline int pad32(int x) { return (x + 31) / 32 * 32; }
@@ -73,6 +87,11 @@ struct QuantJob {
 };
 
 hipError_t launch_quantize(const tq_codebook* cb, const QuantJob& job, hipStream_t stream);
+
+// d = 128 bulk quantize without a sketch (bf16 hi/lo MFMA rotation, table
+// index); used by launch_quantize when quantize128_supported
+bool quantize128_supported(const tq_codebook* cb, const QuantJob& job);
+hipError_t launch_quantize128(const tq_codebook* cb, const QuantJob& job, hipStream_t stream);
 
 // Few vectors per sequence (appends): one workgroup per vector; K and V jobs in
 // one launch.  njobs in 1..2, jobs share n_seq, n_tok and dtype.
