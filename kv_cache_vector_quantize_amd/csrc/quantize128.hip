@@ -24,14 +24,21 @@
 // Index.  y = z / |x| lies in [-1, 1]; cell floor((y + 1) G) of a uniform grid
 // (cells narrower than the closest pair of decision boundaries, built with
 // the codebook) holds the number of boundaries below the cell and the one
-// inside it, so idx = count + (y >= boundary).  fp32 rounding of the cell can
-// only matter when a boundary lies within ~1e-7 of y.
+// inside it, so idx = count + (y >= boundary).  Both sides of the compare are
+// taken in cell coordinates, key = z (G / |x|) + G against (t + 1) G, one FMA
+// per coordinate; fp32 rounding of the key only matters when a boundary lies
+// within ~3e-7 of y.
+//
+// Pipeline.  The next tile's input is loaded into registers while the current
+// tile is rotated, indexed and packed; the grid holds as many workgroups as
+// stay resident, each looping over tiles.
 #include "tq_internal.hpp"
 
 namespace tq {
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 constexpr int TILE = 32;
@@ -40,7 +47,8 @@ constexpr int XS = 136;   // bf16 row stride of the staged tile (272 bytes: 16-b
 struct Q128Args {
   const void* x;
   int64_t n_tok, tok_off;
-  int64_t tiles_per_seq, first_block, n_tiles;
+  int tiles_per_seq, n_tiles;
+  int64_t first_block;
   int bits, nc, ncell;
   float G;
   const uint4* rop;    // Pi operands [4][8][3][64]
@@ -63,57 +71,40 @@ __device__ inline uint32_t bf16_bits(float v) {   // round to nearest even
 
 __device__ inline float bf16_float(uint32_t h) { return __uint_as_float(h << 16); }
 
-// 16 consecutive input elements as fp32 (zeros when !valid)
+// A thread's share of a tile: row tid/8, 16 consecutive input elements from
+// coordinate 16*(tid%8), as raw 16-byte words (zero for rows outside the
+// written range).
 template <int DT>
-__device__ inline void load16(const void* x, int64_t e0, bool valid, bool vec_ok, float (&v)[16]) {
+struct Share {
+  static constexpr int NW = DT == TQ_F32 ? 4 : 2;
+  uint4 w[NW];
+};
+
+template <int DT>
+__device__ inline void share_load(Share<DT>& sh, const void* x, int64_t e0, bool valid, bool vec_ok) {
+  constexpr int EB = DT == TQ_F32 ? 4 : 2;
   if (!valid) {
 #pragma unroll
-    for (int k = 0; k < 16; ++k) v[k] = 0.f;
+    for (int c = 0; c < Share<DT>::NW; ++c) sh.w[c] = make_uint4(0u, 0u, 0u, 0u);
     return;
   }
-  if constexpr (DT == TQ_F32) {
-    const float* p = static_cast<const float*>(x) + e0;
-    if (vec_ok) {
+  const char* p = static_cast<const char*>(x) + e0 * EB;
+  if (vec_ok) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const float4 u = reinterpret_cast<const float4*>(p)[c];
-        v[4 * c] = u.x; v[4 * c + 1] = u.y; v[4 * c + 2] = u.z; v[4 * c + 3] = u.w;
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < 16; ++k) v[k] = p[k];
-    }
+    for (int c = 0; c < Share<DT>::NW; ++c) sh.w[c] = reinterpret_cast<const uint4*>(p)[c];
   } else {
-    const uint16_t* p = static_cast<const uint16_t*>(x) + e0;
-    uint32_t w[8];
-    if (vec_ok) {
+    uint32_t t[4 * Share<DT>::NW];
+    if constexpr (DT == TQ_F32) {
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const uint4 u = reinterpret_cast<const uint4*>(p)[c];
-        w[4 * c] = u.x; w[4 * c + 1] = u.y; w[4 * c + 2] = u.z; w[4 * c + 3] = u.w;
-      }
+      for (int k = 0; k < 16; ++k) t[k] = reinterpret_cast<const uint32_t*>(p)[k];
     } else {
+      const uint16_t* h = reinterpret_cast<const uint16_t*>(p);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) w[k] = (uint32_t)p[2 * k] | ((uint32_t)p[2 * k + 1] << 16);
+      for (int k = 0; k < 8; ++k) t[k] = (uint32_t)h[2 * k] | ((uint32_t)h[2 * k + 1] << 16);
     }
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      if constexpr (DT == TQ_BF16) {
-        v[2 * k] = __uint_as_float(w[k] << 16);
-        v[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
-      } else {
-        v[2 * k] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[k] & 0xFFFFu));
-        v[2 * k + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[k] >> 16));
-      }
-    }
+    for (int c = 0; c < Share<DT>::NW; ++c) sh.w[c] = make_uint4(t[4 * c], t[4 * c + 1], t[4 * c + 2], t[4 * c + 3]);
   }
-}
-
-__device__ inline int qindex(float y, const int2* tab, float G, int ncell) {
-  int c = (int)fmaf(y, G, G);
-  c = c < 0 ? 0 : (c > ncell - 1 ? ncell - 1 : c);
-  const int2 e = tab[c];
-  return e.x + (y >= __int_as_float(e.y) ? 1 : 0);
 }
 
 template <int DT, bool T32>
@@ -125,7 +116,7 @@ __global__ void __launch_bounds__(256) k_q128(Q128Args a) {
   __shared__ __align__(16) uint32_t tb[T32 ? 2 : 1][T32 ? 1024 : 1];   // tile32 block values, field masks
   __shared__ int2 s_tab[kQ128Cells];
   __shared__ float s_cent[256];
-  __shared__ float s_n[TILE], s_inv[TILE];
+  __shared__ float s_n[TILE], s_ig[TILE];
   __shared__ float s_c2[4][TILE];
   __shared__ int s_valid[TILE];
 
@@ -133,6 +124,8 @@ __global__ void __launch_bounds__(256) k_q128(Q128Args a) {
   const int c32 = lane & 31, hl = lane >> 5;
   const int b = a.bits, L = 1 << b;
   const bool need_c = a.nc != 0;
+  const float G = a.G;
+  const int cmax = a.ncell - 1;
   for (int i = tid; i < a.ncell; i += 256) s_tab[i] = a.qtab[i];
   for (int i = tid; i < L; i += 256) s_cent[i] = a.cent[i];
 
@@ -144,61 +137,106 @@ __global__ void __launch_bounds__(256) k_q128(Q128Args a) {
     pm[s] = __builtin_bit_cast(bf16x8, a.rop[((wave * 8 + s) * 3 + 2) * 64 + lane]);
   }
   const bool vec_ok = (reinterpret_cast<uintptr_t>(a.x) & 15) == 0;
+  const bool row16 = (a.idx_pitch & 15) == 0;
+  const int r8 = tid >> 3, c0 = 16 * (tid & 7);
+
+  // tile -> (sequence, block): positions [32 blk, 32 blk + 32) of sequence seq
+  auto where = [&](int tile, int& seq, int64_t& blk) {
+    seq = tile / a.tiles_per_seq;
+    blk = a.first_block + (tile - seq * a.tiles_per_seq);
+  };
+  auto fetch = [&](Share<DT>& sh, int tile) {
+    int seq;
+    int64_t blk;
+    where(tile, seq, blk);
+    const int64_t p = blk * TILE + r8;
+    const bool valid = p >= a.tok_off && p < a.tok_off + a.n_tok;
+    share_load<DT>(sh, a.x, ((int64_t)seq * a.n_tok + (p - a.tok_off)) * 128 + c0, valid, vec_ok);
+  };
+
+  Share<DT> cur;
+  int tile = blockIdx.x;
+  if (tile < a.n_tiles) fetch(cur, tile);
   __syncthreads();
 
-  for (int64_t tile = blockIdx.x; tile < a.n_tiles; tile += gridDim.x) {
-    const int64_t seq = tile / a.tiles_per_seq;
-    const int64_t blk = a.first_block + tile % a.tiles_per_seq;
+  for (; tile < a.n_tiles; tile += gridDim.x) {
+    int seq;
+    int64_t blk;
+    where(tile, seq, blk);
     const int64_t abs0 = blk * TILE;
-    const int64_t pos0 = seq * a.seq_stride + abs0;            // code row of tile row 0
-    const int64_t src0 = seq * a.n_tok + (abs0 - a.tok_off);  // input row of tile row 0
+    const int64_t pos0 = (int64_t)seq * a.seq_stride + abs0;   // code row of tile row 0
     const bool full = abs0 >= a.tok_off && abs0 + TILE <= a.tok_off + a.n_tok;
 
-    // (a) stage the tile: thread -> row tid/8, coordinates 16*(tid%8) .. +15;
-    // |x| in fp32 from the input values, reduced over the row's 8 threads
+    // (a) stage this thread's share; |x| in fp32 from the input values,
+    // reduced over the row's 8 threads
     {
-      const int r = tid >> 3, c0 = 16 * (tid & 7);
-      const int64_t p = abs0 + r;
-      const bool valid = p >= a.tok_off && p < a.tok_off + a.n_tok;
-      float xv[16];
-      load16<DT>(a.x, (src0 + r) * 128 + c0, valid, vec_ok, xv);
       float s2 = 0.f;
-      uint32_t hw[8], lw[8], mw[8];
+      if constexpr (DT == TQ_BF16) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        s2 = fmaf(xv[2 * k], xv[2 * k], s2);
-        s2 = fmaf(xv[2 * k + 1], xv[2 * k + 1], s2);
-        const uint32_t h0 = bf16_bits(xv[2 * k]), h1 = bf16_bits(xv[2 * k + 1]);
-        hw[k] = h0 | (h1 << 16);
-        if constexpr (XLO) {
+        for (int c = 0; c < 2; ++c) {
+          const uint32_t w4[4] = {cur.w[c].x, cur.w[c].y, cur.w[c].z, cur.w[c].w};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const bf16x2 v = __builtin_bit_cast(bf16x2, w4[k]);
+            s2 = __builtin_amdgcn_fdot2_f32_bf16(v, v, s2, false);
+          }
+          *reinterpret_cast<uint4*>(&xh[r8][c0 + 8 * c]) = cur.w[c];
+        }
+      } else {
+        float xv[16];
+        if constexpr (DT == TQ_F32) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            xv[4 * c] = __uint_as_float(cur.w[c].x); xv[4 * c + 1] = __uint_as_float(cur.w[c].y);
+            xv[4 * c + 2] = __uint_as_float(cur.w[c].z); xv[4 * c + 3] = __uint_as_float(cur.w[c].w);
+          }
+        } else {
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const uint32_t w4[4] = {cur.w[c].x, cur.w[c].y, cur.w[c].z, cur.w[c].w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              xv[8 * c + 2 * k] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w4[k] & 0xFFFFu));
+              xv[8 * c + 2 * k + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w4[k] >> 16));
+            }
+          }
+        }
+        uint32_t hw[8], lw[8], mw[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          s2 = fmaf(xv[2 * k], xv[2 * k], s2);
+          s2 = fmaf(xv[2 * k + 1], xv[2 * k + 1], s2);
+          const uint32_t h0 = bf16_bits(xv[2 * k]), h1 = bf16_bits(xv[2 * k + 1]);
+          hw[k] = h0 | (h1 << 16);
           const float e0 = xv[2 * k] - bf16_float(h0), e1 = xv[2 * k + 1] - bf16_float(h1);
           const uint32_t l0 = bf16_bits(e0), l1 = bf16_bits(e1);
           lw[k] = l0 | (l1 << 16);
           if constexpr (XLO2)
             mw[k] = bf16_bits(e0 - bf16_float(l0)) | (bf16_bits(e1 - bf16_float(l1)) << 16);
         }
-      }
-      *reinterpret_cast<uint4*>(&xh[r][c0]) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-      *reinterpret_cast<uint4*>(&xh[r][c0 + 8]) = make_uint4(hw[4], hw[5], hw[6], hw[7]);
-      if constexpr (XLO) {
-        *reinterpret_cast<uint4*>(&xl[r][c0]) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-        *reinterpret_cast<uint4*>(&xl[r][c0 + 8]) = make_uint4(lw[4], lw[5], lw[6], lw[7]);
-      }
-      if constexpr (XLO2) {
-        *reinterpret_cast<uint4*>(&xl2[r][c0]) = make_uint4(mw[0], mw[1], mw[2], mw[3]);
-        *reinterpret_cast<uint4*>(&xl2[r][c0 + 8]) = make_uint4(mw[4], mw[5], mw[6], mw[7]);
+        *reinterpret_cast<uint4*>(&xh[r8][c0]) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        *reinterpret_cast<uint4*>(&xh[r8][c0 + 8]) = make_uint4(hw[4], hw[5], hw[6], hw[7]);
+        *reinterpret_cast<uint4*>(&xl[r8][c0]) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+        *reinterpret_cast<uint4*>(&xl[r8][c0 + 8]) = make_uint4(lw[4], lw[5], lw[6], lw[7]);
+        if constexpr (XLO2) {
+          *reinterpret_cast<uint4*>(&xl2[r8][c0]) = make_uint4(mw[0], mw[1], mw[2], mw[3]);
+          *reinterpret_cast<uint4*>(&xl2[r8][c0 + 8]) = make_uint4(mw[4], mw[5], mw[6], mw[7]);
+        }
       }
       s2 += __shfl_xor(s2, 1);
       s2 += __shfl_xor(s2, 2);
       s2 += __shfl_xor(s2, 4);
       if ((tid & 7) == 0) {
+        const int64_t p = abs0 + r8;
         const float n = sqrtf(s2);
-        s_n[r] = n;
-        s_inv[r] = n > 0.f ? 1.0f / n : 0.f;
-        s_valid[r] = valid ? 1 : 0;
+        s_n[r8] = n;
+        s_ig[r8] = n > 0.f ? G / n : 0.f;
+        s_valid[r8] = (p >= a.tok_off && p < a.tok_off + a.n_tok) ? 1 : 0;
       }
     }
     __syncthreads();
+    // the next tile's share is in flight while this one is computed
+    if (tile + (int)gridDim.x < a.n_tiles) fetch(cur, tile + (int)gridDim.x);
 
     // (b) rotation: row layout -> D[coordinate][vector], tile32 -> D[vector][coordinate]
     auto prod = [&](f32x16 c, bf16x8 xo, bf16x8 po) { return T32 ? mfma32(xo, po, c) : mfma32(po, xo, c); };
@@ -222,17 +260,19 @@ __global__ void __launch_bounds__(256) k_q128(Q128Args a) {
 
     // (c) indices; element v of the lane: row layout -> coordinate
     // 32w + 8(v/4) + 4hl + v%4 of vector c32; tile32 -> coordinate 32w + c32
-    // of vector 8(v/4) + 4hl + v%4
-    float yv[16];
+    // of vector 8(v/4) + 4hl + v%4.  key = (y + 1) G.
     int iv[16];
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int vec = T32 ? 8 * (v >> 2) + 4 * hl + (v & 3) : c32;
-      yv[v] = acc[v] * s_inv[vec];
-      iv[v] = qindex(yv[v], s_tab, a.G, a.ncell);
+      const float key = fmaf(acc[v], s_ig[vec], G);
+      const int c = min((int)key, cmax);
+      const int2 e = s_tab[c];
+      iv[v] = e.x + (key >= __int_as_float(e.y) ? 1 : 0);
     }
-    float cv[16];
     if (need_c) {
+      // norm correction: per-wave partial |y^|^2 of each vector
+      float cv[16];
 #pragma unroll
       for (int v = 0; v < 16; ++v) cv[v] = s_cent[iv[v]];
       if constexpr (!T32) {
@@ -271,17 +311,22 @@ __global__ void __launch_bounds__(256) k_q128(Q128Args a) {
       for (int q = 0; q < 4; ++q) go[q] = (uint32_t)__shfl_xor((int)gv[q], 32);
       if (hl == 0 && s_valid[c32]) {
         uint32_t* dst = reinterpret_cast<uint32_t*>(a.idx + (pos0 + c32) * a.idx_pitch) + wave * b;
-        uint64_t buf = 0;
-        int nb = 0, wo = 0;
+        if (b == 4 && row16) {
+          *reinterpret_cast<uint4*>(dst) = make_uint4(gv[0] | (go[0] << 16), gv[1] | (go[1] << 16),
+                                                      gv[2] | (go[2] << 16), gv[3] | (go[3] << 16));
+        } else {
+          uint64_t buf = 0;
+          int nb = 0, wo = 0;
 #pragma unroll
-        for (int g = 0; g < 8; ++g) {
-          const uint32_t val = (g & 1) ? go[g >> 1] : gv[g >> 1];
-          buf |= (uint64_t)val << nb;
-          nb += 4 * b;
-          if (nb >= 32) {
-            dst[wo++] = (uint32_t)buf;
-            buf >>= 32;
-            nb -= 32;
+          for (int g = 0; g < 8; ++g) {
+            const uint32_t val = (g & 1) ? go[g >> 1] : gv[g >> 1];
+            buf |= (uint64_t)val << nb;
+            nb += 4 * b;
+            if (nb >= 32) {
+              dst[wo++] = (uint32_t)buf;
+              buf >>= 32;
+              nb -= 32;
+            }
           }
         }
       }
@@ -295,16 +340,15 @@ __global__ void __launch_bounds__(256) k_q128(Q128Args a) {
       const uint64_t fm = (uint64_t)((1u << b) - 1u);
 #pragma unroll
       for (int qq = 0; qq < 2; ++qq) {
-        const int G = hl + 2 * qq;
+        const int Gq = hl + 2 * qq;
         uint64_t val = 0, msk = 0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int v = 4 * (qq + 2 * (e >> 2)) + (e & 3);
-          const int tok = 8 * (v >> 2) + 4 * hl + (v & 3);
           val |= (uint64_t)iv[v] << (e * b);
-          if (s_valid[tok]) msk |= fm << (e * b);
+          if (!full && s_valid[8 * (v >> 2) + 4 * hl + (v & 3)]) msk |= fm << (e * b);
         }
-        const int grp = (16 * G + C) * 8 + j;
+        const int grp = (16 * Gq + C) * 8 + j;
         uint8_t* vb = reinterpret_cast<uint8_t*>(tb[0]) + grp * b;
         uint8_t* mb = reinterpret_cast<uint8_t*>(tb[1]) + grp * b;
         if (b == 4) {
@@ -325,12 +369,12 @@ __global__ void __launch_bounds__(256) k_q128(Q128Args a) {
       }
     }
 
-    // (e) scale (norm correction: |x| / |y^|)
+    // (e) scale: |x|, or |x| / |y^| with norm correction
     if (need_c) __syncthreads();
     if (wave == 0 && hl == 0 && s_valid[c32]) {
       const float n = s_n[c32];
       float sc = n;
-      if (a.nc) {
+      if (need_c) {
         const float nh = sqrtf(((s_c2[0][c32] + s_c2[1][c32]) + s_c2[2][c32]) + s_c2[3][c32]);
         sc = n / nh;
       }
@@ -341,7 +385,7 @@ __global__ void __launch_bounds__(256) k_q128(Q128Args a) {
     if constexpr (T32) {
       // (f) the assembled tile32 block: 512*b bytes = 128*b words
       const int words = 128 * b;
-      uint32_t* dst = reinterpret_cast<uint32_t*>(a.idx) + (seq * (a.seq_stride / TILE) + blk) * (int64_t)words;
+      uint32_t* dst = reinterpret_cast<uint32_t*>(a.idx) + ((int64_t)seq * (a.seq_stride / TILE) + blk) * (int64_t)words;
       for (int w = tid; w < words; w += 256) {
         if (full) {
           dst[w] = tb[0][w];
@@ -355,18 +399,37 @@ __global__ void __launch_bounds__(256) k_q128(Q128Args a) {
   }
 }
 
+template <int DT, bool T32>
+int resident_grid(int n_tiles) {
+  // workgroups that stay resident at once (per device, computed once)
+  static int per_device[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (per_device[dev] == 0) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_q128<DT, T32>, 256, 0) != hipSuccess || per_cu < 1)
+      per_cu = 2;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+      cus = 256;
+    per_device[dev] = per_cu * cus;
+  }
+  return n_tiles < per_device[dev] ? n_tiles : per_device[dev];
+}
+
 template <int DT>
-hipError_t launch_dt(const Q128Args& a, bool t32, int grid, hipStream_t st) {
-  if (t32) hipLaunchKernelGGL((k_q128<DT, true>), dim3(grid), dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((k_q128<DT, false>), dim3(grid), dim3(256), 0, st, a);
+hipError_t launch_dt(const Q128Args& a, bool t32, hipStream_t st) {
+  if (t32) hipLaunchKernelGGL((k_q128<DT, true>), dim3(resident_grid<DT, true>(a.n_tiles)), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((k_q128<DT, false>), dim3(resident_grid<DT, false>(a.n_tiles)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 bool quantize128_supported(const tq_codebook* cb, const QuantJob& job) {
-  (void)job;
-  return cb->p.d == 128 && cb->p.qjl_m == 0 && cb->dev.rop && cb->dev.qtab && cb->dev.qcells >= 1;
+  const int64_t first = job.tok_offset / TILE, last = (job.tok_offset + job.n_tok - 1) / TILE;
+  const int64_t tiles = (last - first + 1) * job.n_seq;
+  return cb->p.d == 128 && cb->p.qjl_m == 0 && cb->dev.rop && cb->dev.qtab && cb->dev.qcells >= 1 &&
+         tiles < 0x7FFFFFFFLL && job.n_seq < 0x7FFFFFFFLL;
 }
 
 hipError_t launch_quantize128(const tq_codebook* cb, const QuantJob& job, hipStream_t stream) {
@@ -376,8 +439,8 @@ hipError_t launch_quantize128(const tq_codebook* cb, const QuantJob& job, hipStr
   a.tok_off = job.tok_offset;
   a.first_block = job.tok_offset / TILE;
   const int64_t last_block = (job.tok_offset + job.n_tok - 1) / TILE;
-  a.tiles_per_seq = last_block - a.first_block + 1;
-  a.n_tiles = a.tiles_per_seq * job.n_seq;
+  a.tiles_per_seq = (int)(last_block - a.first_block + 1);
+  a.n_tiles = (int)(a.tiles_per_seq * job.n_seq);
   a.bits = cb->p.bits;
   a.nc = cb->p.norm_correction;
   a.ncell = cb->dev.qcells;
@@ -389,13 +452,12 @@ hipError_t launch_quantize128(const tq_codebook* cb, const QuantJob& job, hipStr
   a.scale = job.out.scale;
   a.idx_pitch = job.out.idx_row_bytes;
   a.seq_stride = job.out.seq_stride;
-  const int grid = (int)(a.n_tiles < 2048 ? a.n_tiles : 2048);
   const bool t32 = job.out.layout == TQ_LAYOUT_TILE32;
   ProfileScope prof(TQ_KERNEL_QUANTIZE, stream);
   switch (job.dt) {
-    case TQ_F32: return launch_dt<TQ_F32>(a, t32, grid, stream);
-    case TQ_BF16: return launch_dt<TQ_BF16>(a, t32, grid, stream);
-    default: return launch_dt<TQ_F16>(a, t32, grid, stream);
+    case TQ_F32: return launch_dt<TQ_F32>(a, t32, stream);
+    case TQ_BF16: return launch_dt<TQ_BF16>(a, t32, stream);
+    default: return launch_dt<TQ_F16>(a, t32, stream);
   }
 }
 

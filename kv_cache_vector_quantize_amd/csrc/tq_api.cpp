@@ -58,8 +58,9 @@ void build_q128_operands(const std::vector<double>& M, std::vector<uint32_t>& ou
 
 // Index cells over y in [-1, 1] for the fp32 boundaries t: cell width 1/G is
 // below 0.9 x the smallest gap between consecutive boundaries, so a cell holds
-// at most one.  Entry c = {#t < c/G - 1, bits of the t inside the cell or of
-// 2.0f}.  Returns false when the table would exceed kQ128Cells entries.
+// at most one.  Entry c = {#t < c/G - 1, bits of (t G + G) for the t inside
+// the cell, or of FLT_MAX}: the kernel compares the cell coordinate y G + G
+// itself.  Returns false when the table would exceed kQ128Cells entries.
 bool build_q128_cells(const std::vector<float>& t, std::vector<uint32_t>& out, float& G_out) {
   double gap = 2.0;
   for (size_t k = 1; k < t.size(); ++k) gap = std::min(gap, (double)t[k] - (double)t[k - 1]);
@@ -71,10 +72,10 @@ bool build_q128_cells(const std::vector<float>& t, std::vector<uint32_t>& out, f
   for (int64_t c = 0; c < cells; ++c) {
     const double lo = (double)c / G - 1.0, hi = (double)(c + 1) / G - 1.0;
     uint32_t below = 0, inside = 0;
-    float p = 2.0f;
+    float p = 3.0e38f;
     for (float v : t) {
       if ((double)v < lo) ++below;
-      else if ((double)v < hi) { ++inside; p = v; }
+      else if ((double)v < hi) { ++inside; p = (float)((double)v * G + G); }
     }
     if (inside > 1) return false;
     uint32_t pb;

@@ -40,9 +40,9 @@ struct DeviceCodebook {
   //  (hi, lo, lo2), uint4 [wave 4][k-step 8][part 3][lane 64]; lane l of wave
   //  w, step s holds Pi[32w + l%32][16s + 8(l/32) + 0..7]
   //  qtab: index cells of y in [-1, 1]: cell c = floor((y + 1) * qG) covers
-  //  [c/qG - 1, (c+1)/qG - 1) and holds {#boundaries below it, the boundary
-  //  inside it (fp32 bits) or 2.0f}; cells are narrower than the closest pair
-  //  of boundaries, so at most one lies inside
+  //  [c/qG - 1, (c+1)/qG - 1) and holds {#boundaries below it, (t + 1) qG for
+  //  the boundary t inside it (fp32 bits) or FLT_MAX}; cells are narrower than
+  //  the closest pair of boundaries, so at most one lies inside
   uint32_t* rop = nullptr;
   uint32_t* qtab = nullptr;
   int qcells = 0;

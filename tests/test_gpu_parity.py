@@ -66,6 +66,11 @@ def _quant_case(dev, d, bits, m, nc, dtype, n_seq, n_tok, tok_offset=0, layout=T
     (128, 4, 0, False, "bf16"),
     (128, 2, 0, True, "bf16"),
     (128, 8, 0, False, "bf16"),
+    (128, 3, 0, True, "f16"),      # d = 128 without a sketch: bf16-split MFMA kernel, odd widths
+    (128, 5, 0, False, "bf16"),
+    (128, 6, 0, False, "f16"),
+    (128, 7, 0, True, "f32"),
+    (128, 1, 0, False, "bf16"),
     (128, 1, 64, False, "f16"),
     (96, 3, 96, True, "bf16"),
     (64, 4, 32, False, "f32"),
@@ -104,7 +109,7 @@ def test_quantize_rows_parity(dev, d, bits, m, nc, dtype):
     print(st)
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_quantize_tile32_parity_and_append(dev, bits):
     """Values in the tile32 layout, written in three appends at unaligned
     offsets (read-modify-write of shared blocks)."""
