@@ -8,15 +8,17 @@
 // sequence (tile32-aligned in absolute position) and loops over tiles.
 //
 // Rotation.  Wave w computes coordinates 32w .. 32w + 31 of z = Pi x for the
-// 32 vectors with v_mfma_f32_32x32x16_bf16.  Pi is split into three bf16
-// parts hi + lo + lo2 kept in registers (8 k-steps x 3 operands); the tile is
+// 32 vectors with v_mfma_f32_32x32x16_bf16.  Pi is split into bf16 parts
+// hi + lo (+ lo2) kept in registers (8 k-steps x NP operands); the tile is
 // staged in LDS as bf16 parts of x: one for bf16 input (exact), two for fp16
-// (exact), three for fp32.  Every product of parts whose orders add up to at
-// most 2^-18 is accumulated in fp32 (3, 5 or 6 MFMAs per k-step); the rest is
-// below 2^-26 of each product, so y carries fp32-level error only (a two-part
-// split leaves 2^-18 and moves 8-bit indices in the 1e-5 boundary zone more
-// often than the codes allow).  Keys with a QJL sketch take the fp32-MFMA
-// kernel.
+// (exact), three for fp32.  With three parts every product of parts whose
+// orders add up to at most 2^-18 is accumulated in fp32 (3, 5 or 6 MFMAs per
+// k-step) and y carries fp32-level error.  Two parts (codes of up to 4 bits)
+// leave 2^-18 |Pi| per entry, ~2e-7 in y: an index moves only for a
+// coordinate that close to a boundary, about 1.5e-5 of the coordinates at 4
+// bits against the 1e-4 the zone rule allows (8-bit codebooks have 16x the
+// boundaries and need the third part).  Keys with a QJL sketch take the
+// fp32-MFMA kernel.
 // Row layout codes take z^T (rows = coordinates: a lane holds 16 coordinates
 // of one vector); tile32 codes take z (rows = vectors: a lane holds one
 // coordinate of 16 vectors, which is how a tile32 record is ordered).
@@ -107,7 +109,7 @@ __device__ inline void share_load(Share<DT>& sh, const void* x, int64_t e0, bool
   }
 }
 
-template <int DT, bool T32>
+template <int DT, bool T32, int NP>
 __global__ void __launch_bounds__(256) k_q128(Q128Args a) {
   constexpr bool XLO = DT != TQ_BF16, XLO2 = DT == TQ_F32;
   __shared__ __align__(16) uint16_t xh[TILE][XS];
@@ -129,12 +131,12 @@ __global__ void __launch_bounds__(256) k_q128(Q128Args a) {
   for (int i = tid; i < a.ncell; i += 256) s_tab[i] = a.qtab[i];
   for (int i = tid; i < L; i += 256) s_cent[i] = a.cent[i];
 
-  bf16x8 ph[8], pl[8], pm[8];
+  bf16x8 ph[8], pl[8], pm[NP == 3 ? 8 : 1];
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
     ph[s] = __builtin_bit_cast(bf16x8, a.rop[((wave * 8 + s) * 3 + 0) * 64 + lane]);
     pl[s] = __builtin_bit_cast(bf16x8, a.rop[((wave * 8 + s) * 3 + 1) * 64 + lane]);
-    pm[s] = __builtin_bit_cast(bf16x8, a.rop[((wave * 8 + s) * 3 + 2) * 64 + lane]);
+    if constexpr (NP == 3) pm[s] = __builtin_bit_cast(bf16x8, a.rop[((wave * 8 + s) * 3 + 2) * 64 + lane]);
   }
   const bool vec_ok = (reinterpret_cast<uintptr_t>(a.x) & 15) == 0;
   const bool row16 = (a.idx_pitch & 15) == 0;
@@ -253,7 +255,7 @@ __global__ void __launch_bounds__(256) k_q128(Q128Args a) {
         acc = prod(acc, xq, pl[s]);
         acc = prod(acc, xq, ph[s]);
       }
-      acc = prod(acc, xo, pm[s]);
+      if constexpr (NP == 3) acc = prod(acc, xo, pm[s]);
       acc = prod(acc, xo, pl[s]);
       acc = prod(acc, xo, ph[s]);
     }
@@ -399,7 +401,7 @@ __global__ void __launch_bounds__(256) k_q128(Q128Args a) {
   }
 }
 
-template <int DT, bool T32>
+template <int DT, bool T32, int NP>
 int resident_grid(int n_tiles) {
   // workgroups that stay resident at once (per device, computed once)
   static int per_device[64] = {0};
@@ -407,7 +409,7 @@ int resident_grid(int n_tiles) {
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
   if (per_device[dev] == 0) {
     int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_q128<DT, T32>, 256, 0) != hipSuccess || per_cu < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_q128<DT, T32, NP>, 256, 0) != hipSuccess || per_cu < 1)
       per_cu = 2;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
       cus = 256;
@@ -416,10 +418,21 @@ int resident_grid(int n_tiles) {
   return n_tiles < per_device[dev] ? n_tiles : per_device[dev];
 }
 
+template <int DT, bool T32, int NP>
+void launch_np(const Q128Args& a, hipStream_t st) {
+  hipLaunchKernelGGL((k_q128<DT, T32, NP>), dim3(resident_grid<DT, T32, NP>(a.n_tiles)), dim3(256), 0, st, a);
+}
+
 template <int DT>
 hipError_t launch_dt(const Q128Args& a, bool t32, hipStream_t st) {
-  if (t32) hipLaunchKernelGGL((k_q128<DT, true>), dim3(resident_grid<DT, true>(a.n_tiles)), dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((k_q128<DT, false>), dim3(resident_grid<DT, false>(a.n_tiles)), dim3(256), 0, st, a);
+  const bool two = a.bits <= 4;      // two parts of Pi suffice up to 4 bits
+  if (t32) {
+    if (two) launch_np<DT, true, 2>(a, st);
+    else launch_np<DT, true, 3>(a, st);
+  } else {
+    if (two) launch_np<DT, false, 2>(a, st);
+    else launch_np<DT, false, 3>(a, st);
+  }
   return hipGetLastError();
 }
 

@@ -109,6 +109,26 @@ def test_quantize_rows_parity(dev, d, bits, m, nc, dtype):
     print(st)
 
 
+@pytest.mark.parametrize("bits,layout", [(4, TQ_LAYOUT_ROW), (4, TQ_LAYOUT_TILE32), (3, TQ_LAYOUT_ROW),
+                                         (5, TQ_LAYOUT_ROW), (8, TQ_LAYOUT_TILE32)])
+def test_quantize_zone_rate_large(dev, bits, layout):
+    """16384 bf16 vectors (2.1 M coordinates) with outlier channels: every
+    index outside the 1e-5 boundary zone matches the oracle and the zone
+    mismatches stay within 1e-4 of the coordinates.  This is the check that
+    bounds the rotation's split-bf16 error (two parts of Pi up to 4 bits,
+    three beyond)."""
+    _say("quantize zone rate", bits, layout)
+    n_seq, n_tok, d = 8, 2048, 128
+    cb, codes, x = _quant_case(dev, d, bits, 0, False, "bf16", n_seq, n_tok, layout=layout, seed=100 + bits)
+    got = U.read_codes(codes, n_tok)
+    ocb = U.oracle_codebook(cb)
+    x64 = x.float().numpy().astype(np.float64).reshape(-1, d)
+    flat = dict(idx=got["idx"].reshape(-1, d), scale=got["scale"].reshape(-1), sign=None, rnorm=None)
+    st, _ = U.compare_quant(ocb, x64, flat, name=f"zone b{bits}")
+    st.pop("vec_ok")
+    print(st, "mismatch rate", st["idx_mismatch"] / (n_seq * n_tok * d))
+
+
 @pytest.mark.parametrize("bits", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_quantize_tile32_parity_and_append(dev, bits):
     """Values in the tile32 layout, written in three appends at unaligned
