@@ -138,6 +138,9 @@ def quantize_leg(torch, tq, synth, dev, iters, warm):
     kern_ms = kms / kn
     per_launch_bytes = (in_bytes + out_bytes) / 2
     flops = 2.0 * d * d * n_vec
+    # the rotation runs as bf16 MFMAs on a two-part split of Pi (bf16 input,
+    # codes of up to 4 bits): two issued products per useful one
+    mfma_flops = 2 * flops
     del k, v, kc, vc
     return dict(workload="quantize-only layer: B=16, Hkv=8, d=128, 32768 tokens, bf16 K and V "
                          "(4 outlier channels/head x15), 4-bit, no QJL",
@@ -145,6 +148,8 @@ def quantize_leg(torch, tq, synth, dev, iters, warm):
                 kernel_ms=round(kern_ms, 4),
                 kernel_GB_per_s=round(per_launch_bytes / (kern_ms * 1e-3) / 1e9, 1),
                 rotation_TFLOP_per_s=round(flops / (ms * 1e-3) / 1e12, 2),
+                mfma_TFLOP_per_s=round(mfma_flops / (ms * 1e-3) / 1e12, 2),
+                mfma_frac_bf16_peak=round(mfma_flops / (ms * 1e-3) / 2.5e15, 4),
                 bytes_per_call=int(in_bytes + out_bytes))
 
 
