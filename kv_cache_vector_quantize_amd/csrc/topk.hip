@@ -12,13 +12,27 @@
 //
 // k_ip_prologue  one workgroup per query: q~ = Pi q, t = sqrt(pi/2)/m S q~,
 //                written as bf16 hi/lo MFMA B operands for blocks of 8 queries.
-// k_ip_score     grid (database chunk, query block); each wave stages 16 code
-//                rows in LDS, forms the centroid operand with the pair table
-//                and the sign operand from sign bytes, runs
-//                v_mfma_f32_16x16x32_bf16 against the block's 8 queries (hi/lo
-//                columns) and keeps a per-lane top-k list in LDS behind a
-//                register threshold; the workgroup merges its lists into k
-//                candidates per (query, chunk).
+// k_ip_score2    (k <= 16) grid (database chunk, group of 128 queries); eight
+//                waves (two per SIMD) hold two 8-query blocks each as MFMA B
+//                operands in registers.  Each 16-row database tile is unpacked once per
+//                workgroup into A operands in LDS (centroid operand from the
+//                pair table, sign operand from sign bytes) and feeds all 16
+//                blocks through v_mfma_f32_16x16x32_bf16 (hi/lo query
+//                columns); raw code rows are fetched two tiles ahead and the
+//                next tile is unpacked while the current one is multiplied.
+//                Each query keeps one unsorted top-k list in LDS with its
+//                worst entry (score, slot): the four lanes that hold the
+//                query's rows insert in row order, a better candidate
+//                overwrites the worst slot and one 128-bit read pass finds
+//                the new worst; every lane filters against a cached copy of
+//                the worst score.  The workgroup then sorts each list into k
+//                candidates per (query, chunk).  For large databases a first
+//                pass over every 64th tile gives each query the k-th best
+//                score of that sample, a lower bound of its final k-th score
+//                that the full pass starts from, so few candidates reach the
+//                lists.
+// k_ip_score     (k > 16) the same product with one 8-query block per
+//                workgroup and each wave unpacking its own tiles.
 // k_ip_merge     one wave per query selects the final k from the candidates.
 #include "tq_internal.hpp"
 
@@ -312,6 +326,316 @@ __global__ void __launch_bounds__(64 * kIpWaves) k_ip_score(ISArgs a) {
   }
 }
 
+// ------------------------------------------------------------ scores, shared tiles
+
+constexpr int kIp2Waves = 8;        // waves per workgroup, two per SIMD
+constexpr int kIp2Blocks = 2;       // 8-query blocks per wave (their operands fit in VGPRs)
+constexpr int kIp2Queries = 8 * kIp2Waves * kIp2Blocks;   // 128 queries per workgroup
+constexpr int kIp2TopK = 16;        // largest k of this kernel
+constexpr int kIp2Lists = kIp2Queries;                        // one list per query
+constexpr int kIp2Raw = 16 * (kIpMaxRowBytes / 4) + 16 * (kIpMaxSignRowBytes / 4) + 32;  // words of a raw tile
+constexpr int kIp2IdxPer = 16 * (kIpMaxRowBytes / 4) / (64 * kIp2Waves);                   // idx words per thread
+static_assert(16 * (kIpMaxSignRowBytes / 4) + 32 <= 64 * kIp2Waves, "one sign / scalar word per thread");
+static_assert(kIp2IdxPer >= 1, "at least one idx word per thread");
+
+struct IS2Args {
+  const uint32_t* qop;
+  const float* cinit;
+  const uint32_t* idx;     // row layout, rw words per vector
+  const uint32_t* sign;    // sw words per vector (or null)
+  const float* scale;
+  const float* rnorm;
+  const uint32_t* tab;     // decode operand table of the codebook
+  int64_t n_db, n_tiles, tiles_per_chunk;
+  int64_t tstride;         // tile i of a chunk is database tile (t_begin + i) * tstride
+  int64_t nq;
+  const float* floor_s;    // [nq][k] sample top-k scores (entry k-1 is the floor), or null
+  int rw, sw, bits, nu, ns, k, n_chunks;
+  float* cand_s;           // [nq_pad][n_chunks][k]
+  int32_t* cand_i;
+};
+
+template <int NU, int NS>
+__global__ void __launch_bounds__(64 * kIp2Waves) k_ip_score2(IS2Args a) {
+  constexpr int NUS = NU + NS;
+  __shared__ __align__(16) uint4 s_a[2][NUS][64];          // A operands of a tile
+  __shared__ float s_sr[2][2][16];                         // its scale and 2^64 rnorm
+  __shared__ __align__(16) uint32_t s_raw[2][kIp2Raw];     // raw code rows of a tile
+  __shared__ __align__(16) uint32_t s_tab[512];
+  __shared__ __align__(16) float s_ls[kIp2Lists][kIp2TopK];    // per-query lists (unsorted)
+  __shared__ __align__(16) int32_t s_li[kIp2Lists][kIp2TopK];
+  __shared__ float s_ws[kIp2Lists];                           // worst score of each list
+  __shared__ int s_wj[kIp2Lists];                             // and its slot
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int c16 = lane & 15, g4 = lane >> 4;
+  const int chunk = blockIdx.x;
+  const int64_t qb0 = (int64_t)blockIdx.y * (kIp2Waves * kIp2Blocks) + wave * kIp2Blocks;
+  const int B = a.bits, nu = NU, nus = NUS;
+  const int tabw = B <= 4 ? (2 << (2 * B)) : (1 << B);
+  for (int i = tid; i < tabw; i += 64 * kIp2Waves) s_tab[i] = a.tab[i];
+  // slots below k start empty (-inf, no index); slots from k on hold +inf so
+  // that they are never the worst entry
+  for (int i = tid; i < kIp2Lists * kIp2TopK; i += 64 * kIp2Waves) {
+    const bool live = (i % kIp2TopK) < a.k;
+    s_ls[i / kIp2TopK][i % kIp2TopK] = live ? -INFINITY : INFINITY;
+    s_li[i / kIp2TopK][i % kIp2TopK] = live ? kNoIndex : -1;
+  }
+  for (int i = tid; i < kIp2Lists; i += 64 * kIp2Waves) {
+    s_ws[i] = -INFINITY;
+    s_wj[i] = 0;
+  }
+  // this wave's query operands (registers) and QJL accumulator offsets
+  bf16x8 bq[kIp2Blocks][NUS];
+  float cin[kIp2Blocks];
+#pragma unroll
+  for (int qb = 0; qb < kIp2Blocks; ++qb) {
+    const uint4* src = reinterpret_cast<const uint4*>(a.qop) + (qb0 + qb) * (int64_t)nus * 64;
+#pragma unroll
+    for (int u = 0; u < NUS; ++u) bq[qb][u] = __builtin_bit_cast(bf16x8, src[u * 64 + lane]);
+    cin[qb] = (NS > 0 && c16 < 8) ? a.cinit[(qb0 + qb) * 8 + c16] : 0.f;
+  }
+
+  // fixed share of the raw tile words of this thread: up to kIp2IdxPer words
+  // of the 16 idx rows, and one word that is a sign word, a scale or an rnorm
+  const int n_idx = 16 * a.rw, n_sgn = 16 * a.sw;
+  int ioff[kIp2IdxPer], irow[kIp2IdxPer];
+#pragma unroll
+  for (int j = 0; j < kIp2IdxPer; ++j) {
+    const int e = tid + 64 * kIp2Waves * j;
+    irow[j] = e < n_idx ? e / a.rw : -1;
+    ioff[j] = e < n_idx ? e - irow[j] * a.rw : 0;
+  }
+  const uint32_t* mbase;
+  int mrow, mstr, mw;
+  if (tid < n_sgn) { mbase = a.sign; mrow = tid / a.sw; mw = tid - mrow * a.sw; mstr = a.sw; }
+  else if (tid < n_sgn + 16) { mbase = reinterpret_cast<const uint32_t*>(a.scale); mrow = tid - n_sgn; mw = 0; mstr = 1; }
+  else if (tid < n_sgn + 32) { mbase = reinterpret_cast<const uint32_t*>(a.rnorm); mrow = tid - n_sgn - 16; mw = 0; mstr = 1; }
+  else { mbase = nullptr; mrow = 0; mw = 0; mstr = 0; }
+  const int last = (int)(a.n_db - 1);
+  uint32_t pre_i[kIp2IdxPer], pre_m = 0u;
+  auto raw_load = [&](int64_t tile) {
+    const int r0 = (int)(tile * 16);
+#pragma unroll
+    for (int j = 0; j < kIp2IdxPer; ++j) {
+      pre_i[j] = 0u;
+      if (irow[j] >= 0) {
+        const int row = min(r0 + irow[j], last);                // rows past the end repeat the last one
+        pre_i[j] = a.idx[(uint32_t)(row * a.rw + ioff[j])];
+      }
+    }
+    if (mbase) pre_m = mbase[(uint32_t)(min(r0 + mrow, last) * mstr + mw)];
+  };
+  // raw tile layout: idx rows [0, n_idx), sign rows [n_idx, n_idx + n_sgn),
+  // scale [.., +16), rnorm [.., +16)
+  auto raw_store = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < kIp2IdxPer; ++j)
+      if (irow[j] >= 0) s_raw[buf][tid + 64 * kIp2Waves * j] = pre_i[j];
+    if (mbase) s_raw[buf][n_idx + tid] = pre_m;
+  };
+  // unpack raw buffer rb into operand buffer ob: task (u, lane) = tid + 512 j
+  auto build = [&](int rb, int ob) {
+    const uint32_t* raw = s_raw[rb];
+    const char* tab = reinterpret_cast<const char*>(s_tab);
+    for (int t = tid; t < nus * 64; t += 64 * kIp2Waves) {
+      const int u = t >> 6, l = t & 63, r = l & 15, g = l >> 4;
+      uint32_t d0, d1, d2, d3;
+      if (u < nu) {
+        const int o = (16 * u + 4 * g) * B;
+        const int i0 = o >> 5, sh = o & 31;
+        const int i1 = (i0 + 1 < a.rw) ? i0 + 1 : i0;
+        const uint32_t f = __builtin_amdgcn_alignbit(raw[r * a.rw + i1], raw[r * a.rw + i0], sh);
+        if (B <= 4) {
+          const uint32_t pm = (1u << (2 * B)) - 1u;
+          const uint2 e0 = *reinterpret_cast<const uint2*>(tab + ((f & pm) << 3));
+          const uint2 e1 = *reinterpret_cast<const uint2*>(tab + (((f >> (2 * B)) & pm) << 3));
+          d0 = e0.x; d1 = e0.y; d2 = e1.x; d3 = e1.y;
+        } else {
+          const uint32_t cm = (1u << B) - 1u;
+          const uint32_t* t32 = reinterpret_cast<const uint32_t*>(tab);
+          const uint32_t ca = t32[f & cm], cb = t32[(f >> B) & cm];
+          const uint32_t cc = t32[(f >> (2 * B)) & cm], cd = t32[(f >> (3 * B)) & cm];
+          d0 = __builtin_amdgcn_perm(cb, ca, 0x05040100u);
+          d1 = __builtin_amdgcn_perm(cb, ca, 0x07060302u);
+          d2 = __builtin_amdgcn_perm(cd, cc, 0x05040100u);
+          d3 = __builtin_amdgcn_perm(cd, cc, 0x07060302u);
+        }
+      } else {
+        const uint32_t sb = (raw[n_idx + r * a.sw + (u - nu)] >> (8 * g)) & 0xFFu;
+        const uint32_t x7 = (sb | (sb << 16)) << 7;
+        d0 = x7 & 0x01000080u; d1 = x7 & 0x04000200u; d2 = x7 & 0x10000800u; d3 = x7 & 0x40002000u;
+      }
+      s_a[ob][u][l] = make_uint4(d0, d1, d2, d3);
+    }
+    if (tid < 32) {
+      const float v = __uint_as_float(raw[n_idx + n_sgn + tid]);
+      s_sr[ob][tid >> 4][tid & 15] = (tid < 16) ? v : v * 0x1p64f;
+    }
+  };
+
+  // thq: cached worst score of the list of this lane's query in a block.  A
+  // query's candidates are inserted in increasing row order (tile by tile,
+  // lane group g4 = 0..3 within a tile, then its 4 rows), so a candidate that
+  // only ties the worst entry loses to it and the strict tests are exact.
+  // tqf: the sample floor of the query (candidates below it cannot be in the
+  // final top k; equal ones may, so that test is not strict)
+  float thq[kIp2Blocks], tqf[kIp2Blocks];
+#pragma unroll
+  for (int qb = 0; qb < kIp2Blocks; ++qb) {
+    thq[qb] = -INFINITY;
+    const int64_t q = (qb0 + qb) * 8 + c16;
+    tqf[qb] = (a.floor_s && c16 < 8 && q < a.nq) ? a.floor_s[q * a.k + a.k - 1] : -INFINITY;
+  }
+  const int64_t t_begin = (int64_t)chunk * a.tiles_per_chunk;
+  int64_t t_end = t_begin + a.tiles_per_chunk;
+  if (t_end > a.n_tiles) t_end = a.n_tiles;
+  const int64_t nt = t_end > t_begin ? t_end - t_begin : 0;
+
+  auto dbt = [&](int64_t i) { return (t_begin + i) * a.tstride; };   // database tile of step i
+  if (nt > 0) {
+    raw_load(dbt(0));
+    raw_store(0);
+    if (nt > 1) raw_load(dbt(1));
+  }
+  __syncthreads();
+  if (nt > 0) build(0, 0);
+  if (nt > 1) {
+    raw_store(1);
+    if (nt > 2) raw_load(dbt(2));
+  }
+  __syncthreads();
+
+  for (int64_t i = 0; i < nt; ++i) {
+    const int cur = (int)(i & 1), nxt = cur ^ 1;
+    const int64_t row0 = dbt(i) * 16;
+    // (1) tile i against this wave's two query blocks
+    f32x4 acc[kIp2Blocks], accq[kIp2Blocks];
+#pragma unroll
+    for (int qb = 0; qb < kIp2Blocks; ++qb) {
+      acc[qb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      accq[qb] = (f32x4){cin[qb], cin[qb], cin[qb], cin[qb]};
+    }
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const bf16x8 av = __builtin_bit_cast(bf16x8, s_a[cur][u][lane]);
+#pragma unroll
+      for (int qb = 0; qb < kIp2Blocks; ++qb) acc[qb] = mfma(av, bq[qb][u], acc[qb]);
+    }
+#pragma unroll
+    for (int v = 0; v < NS; ++v) {
+      const bf16x8 av = __builtin_bit_cast(bf16x8, s_a[cur][NU + v][lane]);
+#pragma unroll
+      for (int qb = 0; qb < kIp2Blocks; ++qb) accq[qb] = mfma(av, bq[qb][NU + v], accq[qb]);
+    }
+    float sc[4], rn[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      sc[r] = s_sr[cur][0][4 * g4 + r];
+      rn[r] = s_sr[cur][1][4 * g4 + r];
+    }
+#pragma unroll
+    for (int qb = 0; qb < kIp2Blocks; ++qb) {
+      float sv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float v = sc[r] * (acc[qb][r] + dpp_ror8(acc[qb][r]));
+        if constexpr (NS > 0) v = fmaf(rn[r], accq[qb][r] + dpp_ror8(accq[qb][r]), v);
+        sv[r] = (row0 + 4 * g4 + r < a.n_db) ? v : -INFINITY;
+      }
+      uint32_t pm = 0u;                 // rows of this lane that beat the cached worst
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pm |= (c16 < 8 && sv[r] > thq[qb] && sv[r] >= tqf[qb]) ? (1u << r) : 0u;
+      if (__ballot(pm != 0u) != 0ull) {
+        const int li = (wave * kIp2Blocks + qb) * 8 + c16;     // list of this lane's query
+        for (int g = 0; g < 4; ++g) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const bool me = g4 == g && ((pm >> r) & 1u);
+            if (__ballot(me) != 0ull && me) {
+              if (sv[r] > s_ws[li]) {
+                const int wj = s_wj[li];
+                s_ls[li][wj] = sv[r];
+                s_li[li][wj] = (int32_t)(row0 + 4 * g4 + r);
+                // new worst: lowest score, then highest index
+                float ws = INFINITY;
+                int32_t wi = -1;
+                int nj = 0;
+#pragma unroll
+                for (int c4 = 0; c4 < kIp2TopK / 4; ++c4) {
+                  const float4 sc4 = reinterpret_cast<const float4*>(s_ls[li])[c4];
+                  const int4 id4 = reinterpret_cast<const int4*>(s_li[li])[c4];
+                  const float sa[4] = {sc4.x, sc4.y, sc4.z, sc4.w};
+                  const int32_t ia[4] = {id4.x, id4.y, id4.z, id4.w};
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) {
+                    const bool worse = sa[e] < ws || (sa[e] == ws && ia[e] > wi);
+                    ws = worse ? sa[e] : ws;
+                    wi = worse ? ia[e] : wi;
+                    nj = worse ? 4 * c4 + e : nj;
+                  }
+                }
+                s_ws[li] = ws;
+                s_wj[li] = nj;
+              }
+            }
+          }
+        }
+        if (c16 < 8) thq[qb] = s_ws[li];
+      }
+    }
+    // (2) unpack tile i + 1; (3) stage tile i + 2, fetch tile i + 3
+    if (i + 1 < nt) build(nxt, nxt);
+    if (i + 2 < nt) {
+      raw_store(cur);
+      if (i + 3 < nt) raw_load(dbt(i + 3));
+    }
+    __syncthreads();
+  }
+
+  // sort each query's list into its k candidates, (score desc, index asc)
+  if (tid < kIp2Queries) {
+    const int li = tid;      // list of query tid of the workgroup
+    const int64_t q = (int64_t)blockIdx.y * kIp2Queries + tid;
+    const int64_t base = (q * a.n_chunks + chunk) * (int64_t)a.k;
+    float ps = INFINITY;
+    int32_t pi = -1;
+    for (int o = 0; o < a.k; ++o) {
+      float bs = -INFINITY;
+      int32_t bi = kNoIndex;
+      for (int j = 0; j < a.k; ++j) {
+        const float hs = s_ls[li][j];
+        const int32_t hi = s_li[li][j];
+        if (better(ps, pi, hs, hi) && better(hs, hi, bs, bi)) { bs = hs; bi = hi; }
+      }
+      a.cand_s[base + o] = bs;
+      a.cand_i[base + o] = bi;
+      ps = bs;
+      pi = bi;
+    }
+  }
+}
+
+template <int NU, int NS>
+void launch_score2_ns(const IS2Args& a, int ns, dim3 grid, hipStream_t st) {
+  if constexpr (NS > kIpNsMax) {
+    (void)a; (void)ns; (void)grid; (void)st;
+  } else {
+    if (ns == NS) hipLaunchKernelGGL((k_ip_score2<NU, NS>), grid, dim3(64 * kIp2Waves), 0, st, a);
+    else launch_score2_ns<NU, NS + 1>(a, ns, grid, st);
+  }
+}
+
+// NU = dp / 16 is even (dp is a multiple of 32)
+template <int NU>
+void launch_score2(const IS2Args& a, dim3 grid, hipStream_t st) {
+  if constexpr (NU > kIpNuMax) {
+    (void)a; (void)grid; (void)st;
+  } else {
+    if (a.nu == NU) launch_score2_ns<NU, 0>(a, a.ns, grid, st);
+    else launch_score2<NU + 2>(a, grid, st);
+  }
+}
+
 // ------------------------------------------------------------ final merge
 
 struct IMArgs {
@@ -371,9 +695,13 @@ TopkPlan plan_topk(int64_t nq, int64_t n_db, int k, int d, int m) {
   p.nq = nq; p.n_db = n_db; p.k = k;
   p.nu = (pad32(d) + 15) / 16;
   p.ns = m > 0 ? (m + 31) / 32 : 0;
-  p.nqb = (nq + 7) / 8;
+  p.shared = k <= kIp2TopK;
+  // query blocks of 8, padded to whole workgroups of 128 queries for the shared-tile kernel
+  p.nqb = p.shared ? (nq + kIp2Queries - 1) / kIp2Queries * (kIp2Queries / 8) : (nq + 7) / 8;
   p.n_tiles = (n_db + 15) / 16;
-  int64_t chunks = p.nqb > 0 ? (2048 + p.nqb - 1) / p.nqb : 1;    // ~2048 workgroups
+  const int64_t groups = p.shared ? p.nqb / (kIp2Queries / 8) : p.nqb;
+  const int64_t target = p.shared ? 512 : 2048;                  // workgroups in flight
+  int64_t chunks = groups > 0 ? (target + groups - 1) / groups : 1;
   int64_t cap = p.n_tiles / 8;                                   // >= 8 tiles per chunk
   if (chunks > cap) chunks = cap;
   if (chunks > 4096) chunks = 4096;
@@ -387,6 +715,18 @@ TopkPlan plan_topk(int64_t nq, int64_t n_db, int k, int d, int m) {
   const size_t nc = (size_t)p.nqb * 8 * p.n_chunks * (size_t)k;
   p.off_cand_s = off; off = al(off + nc * 4);
   p.off_cand_i = off; off = al(off + nc * 4);
+  // sample pass (shared-tile kernel, large databases): every 64th tile,
+  // 32 chunks, merged into the top k of the sample per query
+  p.sample_stride = (p.shared && p.n_tiles >= 64 * 256) ? 64 : 0;
+  if (p.sample_stride) {
+    p.sample_tiles = p.n_tiles / p.sample_stride;
+    p.sample_chunks = 32;
+    const size_t ns2 = (size_t)p.nqb * 8 * p.sample_chunks * (size_t)k;
+    p.off_s_cand_s = off; off = al(off + ns2 * 4);
+    p.off_s_cand_i = off; off = al(off + ns2 * 4);
+    p.off_s_idx = off; off = al(off + (size_t)nq * k * 8);
+    p.off_s_score = off; off = al(off + (size_t)nq * k * 4);
+  }
   p.bytes = off;
   return p;
 }
@@ -422,9 +762,45 @@ hipError_t launch_topk(const tq_codebook* cb, const float* queries, const TopkPl
   sa.sw = cb->p.qjl_m > 0 ? (int)(db.sign_row_bytes / 4) : 0;
   sa.nu = plan.nu; sa.ns = plan.ns; sa.k = plan.k; sa.n_chunks = plan.n_chunks;
   sa.cand_s = cand_s; sa.cand_i = cand_i;
-  const dim3 grid((unsigned)plan.n_chunks, (unsigned)plan.nqb);
   const bool qjl = cb->p.qjl_m > 0;
-  {
+  if (plan.shared) {
+    IS2Args s2{};
+    s2.qop = qop; s2.cinit = cinit;
+    s2.idx = sa.idx; s2.sign = sa.sign; s2.scale = sa.scale; s2.rnorm = qjl ? sa.rnorm : sa.scale;
+    s2.tab = sa.tab;
+    s2.n_db = plan.n_db; s2.n_tiles = plan.n_tiles; s2.tiles_per_chunk = plan.tiles_per_chunk;
+    s2.rw = sa.rw; s2.sw = sa.sw; s2.bits = cb->p.bits; s2.nu = plan.nu; s2.ns = plan.ns;
+    s2.k = plan.k; s2.n_chunks = plan.n_chunks;
+    s2.cand_s = cand_s; s2.cand_i = cand_i;
+    s2.tstride = 1;
+    s2.nq = plan.nq;
+    s2.floor_s = nullptr;
+    const unsigned groups = (unsigned)(plan.nqb / (kIp2Queries / 8));
+    ProfileScope prof(TQ_KERNEL_TOPK, stream);
+    if (plan.sample_stride) {
+      IS2Args sp = s2;
+      sp.tstride = plan.sample_stride;
+      sp.n_tiles = plan.sample_tiles;
+      sp.n_chunks = plan.sample_chunks;
+      sp.tiles_per_chunk = (plan.sample_tiles + plan.sample_chunks - 1) / plan.sample_chunks;
+      sp.cand_s = reinterpret_cast<float*>(w + plan.off_s_cand_s);
+      sp.cand_i = reinterpret_cast<int32_t*>(w + plan.off_s_cand_i);
+      launch_score2<2>(sp, dim3((unsigned)plan.sample_chunks, groups), stream);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      IMArgs sm{};
+      sm.cand_s = sp.cand_s; sm.cand_i = sp.cand_i;
+      sm.nq = plan.nq; sm.n_chunks = plan.sample_chunks; sm.k = plan.k;
+      sm.out_idx = reinterpret_cast<int64_t*>(w + plan.off_s_idx);
+      sm.out_score = reinterpret_cast<float*>(w + plan.off_s_score);
+      hipLaunchKernelGGL(k_ip_merge, dim3((unsigned)plan.nq), dim3(64), 0, stream, sm);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      s2.floor_s = sm.out_score;
+    }
+    launch_score2<2>(s2, dim3((unsigned)plan.n_chunks, groups), stream);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  } else {
+    const dim3 grid((unsigned)plan.n_chunks, (unsigned)plan.nqb);
     ProfileScope prof(TQ_KERNEL_TOPK, stream);
     switch (cb->p.bits) {
       case 1: launch_score_b<1>(sa, qjl, grid, stream); break;

@@ -129,6 +129,10 @@ constexpr int64_t kIpMaxRowBytes = 256, kIpMaxSignRowBytes = 32;
 struct TopkPlan {
   int64_t nq, n_db, nqb, n_tiles, tiles_per_chunk;
   int k, nu, ns, n_chunks;
+  bool shared;          // k <= 16: workgroups of 128 queries share unpacked tiles
+  int64_t sample_stride, sample_tiles;   // sample pass over every sample_stride-th tile (0: none)
+  int sample_chunks;
+  size_t off_s_cand_s, off_s_cand_i, off_s_idx, off_s_score;
   size_t off_qop, off_cinit, off_cand_s, off_cand_i, bytes;
 };
 
