@@ -640,17 +640,22 @@ __global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_e
   };
 
   // two-stage pipeline over full tiles: the next tile's loads are in flight
-  // while the current one is computed
+  // while the current one is computed.  Every pass issues them (past the
+  // last full tile they repeat that tile), so the number of loads in flight
+  // is the same on every path into a tile's computation and its waits only
+  // cover the tile's own loads; with a conditional load the count differs
+  // between paths and the wait falls back to draining every load.
   const int64_t nfull = (t_end > t_begin) ? (t_end - t_begin) / 32 : 0;
+  const int64_t t_last = t_begin + 32 * (nfull - 1);
   int64_t t0 = t_begin;
   Tile<BK, BV> A, Bt;
   if (nfull > 0) load(A, t0);
   for (int64_t i = 0; i < nfull; i += 2) {
-    if (i + 1 < nfull) load(Bt, t0 + 32);
+    load(Bt, t0 + 32 < t_last ? t0 + 32 : t_last);
     compute(A, t0, std::false_type{});
     t0 += 32;
     if (i + 1 >= nfull) break;
-    if (i + 2 < nfull) load(A, t0 + 32);
+    load(A, t0 + 32 < t_last ? t0 + 32 : t_last);
     compute(Bt, t0, std::false_type{});
     t0 += 32;
   }
