@@ -361,6 +361,56 @@ def test_decode_qjl_smaller_m_f32_query(dev):
     U.check_decode(okc, ovc, U.to_f64(q), kd, vd, tau, lg, out, name="m64")
 
 
+def test_decode_full_size_128k(dev):
+    """The 128K decode layer at full size and in the launch configuration the
+    benchmark times: B=8, Hq=64, Hkv=8, d=128, N=131072, bf16 K/V N(0,1) with
+    channels 3/77/101 x20, bf16 queries, keys 3-bit + QJL m=128, values 4-bit.
+    The GPU quantizes the whole cache; the oracle's codes then replace three
+    sampled sequences (first, middle, last), and those sequences' outputs
+    (call without logits, as timed) and logits (second call) must meet the
+    bars against the oracle's decode of the same codes."""
+    B, Hq, Hkv, N = 8, 64, 8, 131072
+    _say("decode full size 128K")
+    kcb, vcb, S, k, v, q = _decode_setup(dev, B, Hkv, Hq, N, 3, 128, False, 4, False, seed=0)
+    kc = tq.Codes(kcb, B * Hkv, S, TQ_LAYOUT_ROW)
+    vc = tq.Codes(vcb, B * Hkv, S, TQ_LAYOUT_TILE32)
+    tq.tq_quantize_kv(kcb, vcb, k.view(B * Hkv, N, 128), v.view(B * Hkv, N, 128), kc, vc)
+    okc, ovc = U.oracle_codebook(kcb), U.oracle_codebook(vcb)
+    sampled = [(0, 0), (3, 5), (7, 7)]
+    refs = {}
+    for b, h in sampled:
+        s = b * Hkv + h
+        rk = O.quantize(okc, U.to_f64(k[b, h]))
+        rv = O.quantize(ovc, U.to_f64(v[b, h]))
+        U.upload_oracle_codes(kc, s, rk, N)
+        U.upload_oracle_codes(vc, s, rv, N)
+        refs[(b, h)] = (rk, rv)
+    torch.cuda.synchronize()
+    tau = 1.0 / math.sqrt(128)
+    ws = torch.empty(tq.tq_attn_decode_workspace(B, Hq, Hkv, N, 128), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, Hq, 128), dtype=torch.float32, device=dev)
+    tq.tq_attn_decode(kcb, vcb, q, kc, vc, N, tau, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    out_np = out.cpu().numpy()
+    assert np.all(np.isfinite(out_np))
+    lg_t = torch.full((B, Hq, N), 123.0, dtype=torch.float32, device=dev)
+    out2 = tq.tq_attn_decode(kcb, vcb, q, kc, vc, N, tau, logits=lg_t, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out2, out), "outputs differ between the calls with and without logits"
+    q64 = U.to_f64(q)
+    g = Hq // Hkv
+    worst = {}
+    for (b, h), (rk, rv) in refs.items():
+        heads = slice(h * g, (h + 1) * g)
+        kd = U.oracle_cache([rk], 1, 1, N, True)
+        vd = U.oracle_cache([rv], 1, 1, N, False)
+        lg_gpu = lg_t[b, heads].cpu().numpy()[None]
+        st = U.check_decode(okc, ovc, q64[b:b + 1, heads], kd, vd, tau, lg_gpu,
+                            out_np[b:b + 1, heads], name=f"128K ({b},{h})")
+        worst[(b, h)] = st
+    print(worst)
+
+
 def test_decode_deterministic(dev):
     _say("decode determinism")
     B, Hkv, Hq, N = 2, 2, 16, 2048
