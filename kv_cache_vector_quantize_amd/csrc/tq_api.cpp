@@ -189,9 +189,14 @@ thread_local ProfileState g_prof;
 
 ProfileScope::ProfileScope(int k, hipStream_t s) : kernel(k), stream(s) {
   if (!g_prof.on) return;
+  // timing-only events: without the system-scope fence a record costs no
+  // cache writeback / invalidate, so it does not slow the work around it
   EventPair p;
-  if (hipEventCreate(&p.a) != hipSuccess) return;
-  if (hipEventCreate(&p.b) != hipSuccess) { (void)hipEventDestroy(p.a); return; }
+  if (hipEventCreateWithFlags(&p.a, hipEventDisableSystemFence) != hipSuccess) return;
+  if (hipEventCreateWithFlags(&p.b, hipEventDisableSystemFence) != hipSuccess) {
+    (void)hipEventDestroy(p.a);
+    return;
+  }
   (void)hipEventRecord(p.a, stream);
   g_prof.rec[kernel].push_back(p);
   stop = p.b;
