@@ -74,14 +74,10 @@ struct PArgs {
   int m, mp;
   float qscale;           // sm_scale * log2(e)
   const float* rotKT;     // [D][D], rotKT[k][i] = Pi_K[i][k]
-  const float* qjlKT;     // [D][mp], qjlKT[i][j] = S_K[j][i] (or null)
+  const float* sprotKT;   // [D][mp], sprotKT[k][j] = sqrt(pi/2)/m (S_K Pi_K)[j][k] (or null)
   uint32_t* qop;          // [rows][QOP_DWORDS]
 };
 
-// One workgroup (256 threads) per row: the 8 query slots share the
-// transposed rotation and sketch, both staged in LDS by one batch of
-// coalesced 16-byte loads; thread (i, half) owns coordinate i of queries
-// 4*half .. 4*half + 3.
 // A D-row matrix (row-major, `cols` floats per row, cols a multiple of 4 and
 // >= 4) is staged into LDS as dst[k][i], columns >= cols zero-filled.  The 16
 // loads of a thread are issued together (clamped addresses, no branches) and
@@ -111,120 +107,108 @@ __device__ inline void stage_store(float (*dst)[D], const Stage& st, int cols, i
   }
 }
 
+// Grid (4, rows): workgroup (part, row) serves query slots 2 part and
+// 2 part + 1 of the row.  The rotation and the folded sketch S Pi are staged
+// in LDS by one batch of coalesced 16-byte loads; thread (i, c) forms
+// coordinate i of q~ = Pi q' and of t = sqrt(pi/2)/m (S Pi) q' for slot c in
+// one pass (q' = sm_scale log2(e) q), then writes the operand dwords of its
+// two columns (hi and lo) of the slots.
 __global__ void __launch_bounds__(256) k_prologue(PArgs a) {
   __shared__ __align__(16) float mat[D][D];
   __shared__ __align__(16) float mat2[D][D];
-  __shared__ float qs[8][D];
-  __shared__ float qt[8][D];
-  __shared__ float tt[8][D];
-  const int row = blockIdx.x;
+  __shared__ __align__(16) float qs[2][D];
+  __shared__ float qt[2][D];
+  __shared__ float tt[2][D];
+  const int part = blockIdx.x, row = blockIdx.y;
   const int qg = row % a.qgroups;
   const int bh = row / a.qgroups;          // b * Hkv + h
   const int b = bh / a.Hkv, h = bh % a.Hkv;
   const int tid = threadIdx.x;
+  const int i = tid & (D - 1), c = tid >> 7;
+  const int slot = 2 * part + c;           // query slot within the row's group of 8
+  const bool live = qg * 8 + slot < a.g;
+  // all matrix loads first (one round trip; without a sketch the second batch
+  // re-reads the rotation and is not stored), then the query element
+  const bool sk = a.m > 0;
+  Stage st, st2;
+  stage_load(st, a.rotKT, D, tid);
+  stage_load(st2, sk ? a.sprotKT : a.rotKT, sk ? a.mp : D, tid);
   {
-    // thread tid loads coordinate tid % D of slots tid / D + 2 u, u < 4
-    int64_t off[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int j = qg * 8 + (tid >> 7) + 2 * u;
-      off[u] = ((int64_t)b * a.Hq + h * a.g + (j < a.g ? j : a.g - 1)) * D + (tid & (D - 1));
-    }
-    float v[4];
-    if (a.qdt == TQ_F32) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = static_cast<const float*>(a.q)[off[u]];
-    } else if (a.qdt == TQ_BF16) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = __uint_as_float((uint32_t) static_cast<const uint16_t*>(a.q)[off[u]] << 16);
-    } else {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = (float)static_cast<const _Float16*>(a.q)[off[u]];
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int c = (tid >> 7) + 2 * u;
-      qs[c][tid & (D - 1)] = (qg * 8 + c < a.g) ? v[u] : 0.f;
-    }
+    const int j = qg * 8 + (live ? slot : 0);
+    const int64_t off = ((int64_t)b * a.Hq + h * a.g + j) * D + i;
+    float v;
+    if (a.qdt == TQ_F32) v = static_cast<const float*>(a.q)[off];
+    else if (a.qdt == TQ_BF16) v = __uint_as_float((uint32_t) static_cast<const uint16_t*>(a.q)[off] << 16);
+    else v = (float)static_cast<const _Float16*>(a.q)[off];
+    qs[c][i] = live ? v * a.qscale : 0.f;
   }
-  {
-    Stage st;
-    stage_load(st, a.rotKT, D, tid);
-    if (a.m > 0) {
-      Stage st2;
-      stage_load(st2, a.qjlKT, a.mp, tid);
-      stage_store(mat2, st2, a.mp, tid);
-    }
-    stage_store(mat, st, D, tid);
-  }
-  __syncthreads();
-  const int i = tid & (D - 1), c0 = (tid >> 7) * 4;
-  {
-    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-#pragma unroll 8
-    for (int k = 0; k < D; ++k) {
-      const float r = mat[k][i];
-      s0 += r * qs[c0][k]; s1 += r * qs[c0 + 1][k]; s2 += r * qs[c0 + 2][k]; s3 += r * qs[c0 + 3][k];
-    }
-    qt[c0][i] = s0 * a.qscale; qt[c0 + 1][i] = s1 * a.qscale;
-    qt[c0 + 2][i] = s2 * a.qscale; qt[c0 + 3][i] = s3 * a.qscale;
-  }
+  stage_store(mat, st, D, tid);
+  if (sk) stage_store(mat2, st2, a.mp, tid);
   __syncthreads();
   {
-    const float cq = a.m > 0 ? 1.2533141373155003f / (float)a.m : 0.f;   // sqrt(pi/2)/m
-    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-    if (i < a.m) {
-#pragma unroll 8
-      for (int k = 0; k < D; ++k) {
-        const float r = mat2[k][i];
-        s0 += r * qt[c0][k]; s1 += r * qt[c0 + 1][k]; s2 += r * qt[c0 + 2][k]; s3 += r * qt[c0 + 3][k];
+    float s1 = 0.f, s2 = 0.f;
+#pragma unroll 4
+    for (int k = 0; k < D; k += 4) {
+      const f32x4 qv = *reinterpret_cast<const f32x4*>(&qs[c][k]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) s1 = fmaf(mat[k + u][i], qv[u], s1);
+      if (sk) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) s2 = fmaf(mat2[k + u][i], qv[u], s2);
       }
     }
-    tt[c0][i] = s0 * cq; tt[c0 + 1][i] = s1 * cq; tt[c0 + 2][i] = s2 * cq; tt[c0 + 3][i] = s3 * cq;
+    qt[c][i] = s1;
+    tt[c][i] = s2;
   }
   __syncthreads();
   uint32_t* dst = a.qop + (int64_t)row * QOP_DWORDS;
   // Q operand [u][lane][p]: MFMA u, lane group g4 covers dims 32*g4 + 4u .. +3;
   // dwords p = 0,1 -> dims (4u, 4u+1) (hi then lo slot of the key operand),
-  // p = 2,3 -> dims (4u+2, 4u+3).  Columns 0-7 hold hi, 8-15 lo.
-  for (int e = tid; e < QOP_Q; e += 256) {
-    const int p = e & 3, lane = (e >> 2) & 63, u = e >> 8;
-    const int col = lane & 15, g4 = lane >> 4, c = col & 7;
+  // p = 2,3 -> dims (4u+2, 4u+3).  Columns 0-7 hold hi, 8-15 lo.  This
+  // workgroup writes the columns of its slots: f -> (u, g4, lo, c, p).
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int f = tid + 256 * r;
+    const int p = f & 3, cl = (f >> 2) & 1, lo = (f >> 3) & 1, g4 = (f >> 4) & 3, u = f >> 6;
+    const int col = 8 * lo + 2 * part + cl;
+    const int lane = 16 * g4 + col;
     const int dim = 32 * g4 + 4 * u + 2 * (p >> 1);
     uint32_t hv[2];
     for (int h2 = 0; h2 < 2; ++h2) {
-      const float v = qt[c][dim + h2];
+      const float v = qt[cl][dim + h2];
       const uint32_t hi = bf16_rne_bits(v);
-      hv[h2] = (col >= 8) ? bf16_rne_bits(v - __uint_as_float(hi << 16)) : hi;
+      hv[h2] = lo ? bf16_rne_bits(v - __uint_as_float(hi << 16)) : hi;
     }
-    dst[e] = hv[0] | (hv[1] << 16);
+    dst[(u * 64 + lane) * 4 + p] = hv[0] | (hv[1] << 16);
   }
   // T operand [cc][lane][p]: dword p of MFMA cc faces sign dword K = 4cc + p
   // of lane group g4, whose low / high halves hold sign bits jl / jh at bf16
   // bit P; the entry is t of sketch row 32*g4 + j times 2^(128 - 2^(P-7)) and
   // 2^-kSignShift (exact power-of-two scalings).
-  for (int e = tid; e < QOP_T; e += 256) {
-    const int p = e & 3, lane = (e >> 2) & 63, cc = e >> 8;
-    const int col = lane & 15, g4 = lane >> 4, c = col & 7;
+  if (a.m > 0) {
+    const int f = tid;
+    const int p = f & 3, cl = (f >> 2) & 1, lo = (f >> 3) & 1, g4 = (f >> 4) & 3, cc = f >> 6;
+    const int col = 8 * lo + 2 * part + cl;
+    const int lane = 16 * g4 + col;
     const int K = 4 * cc + p;
     const int P = (K < 8) ? 14 - K : 22 - K;
     const int ex = 128 - (1 << (P - 7)) - kSignShift;
     uint32_t hv[2];
     for (int h2 = 0; h2 < 2; ++h2) {
       const int j = h2 ? 30 - K : (K == 15 ? 31 : 14 - K);
-      const float v = ldexpf(tt[c][32 * g4 + j], ex);
+      const float v = ldexpf(tt[cl][32 * g4 + j], ex);
       const uint32_t hi = bf16_rne_bits(v);
-      hv[h2] = (col >= 8) ? bf16_rne_bits(v - __uint_as_float(hi << 16)) : hi;
+      hv[h2] = lo ? bf16_rne_bits(v - __uint_as_float(hi << 16)) : hi;
     }
-    dst[QOP_Q + e] = hv[0] | (hv[1] << 16);
+    dst[QOP_Q + (cc * 64 + lane) * 4 + p] = hv[0] | (hv[1] << 16);
   }
   // QJL accumulator offsets: -sum_j (hi + lo) of t for the hi columns, in the
-  // scale of the sign products (2^-kSignShift)
-  if (tid < 64) {
-    const int c = tid >> 3, part = tid & 7;
+  // scale of the sign products (2^-kSignShift); the lo columns start at 0
+  if (tid < 16) {
+    const int cl = tid >> 3, pp = tid & 7;
     float s = 0.f;
-    for (int j = part; j < D; j += 8) {
-      const float v = tt[c][j];
+    for (int j = pp; j < D; j += 8) {
+      const float v = tt[cl][j];
       const float fh = __uint_as_float(bf16_rne_bits(v) << 16);
       s += fh + __uint_as_float(bf16_rne_bits(v - fh) << 16);
     }
@@ -232,7 +216,7 @@ __global__ void __launch_bounds__(256) k_prologue(PArgs a) {
     s += __shfl_xor(s, 2);
     s += __shfl_xor(s, 4);
     float* cinit = reinterpret_cast<float*>(dst) + QOP_Q + QOP_T;
-    if (part == 0) { cinit[c] = -ldexpf(s, -kSignShift); cinit[c + 8] = 0.f; }
+    if (pp == 0) { cinit[2 * part + cl] = -ldexpf(s, -kSignShift); cinit[2 * part + cl + 8] = 0.f; }
   }
 }
 
@@ -729,82 +713,70 @@ struct CArgs {
   float* out;          // [B][Hq][D]
 };
 
-// One workgroup (256 threads) per row.  The row's workgroup partials are
-// merged per query slot c with the usual max / rescale rule: the maximum and
-// the normaliser are reduced over all 256 threads (thread t visits partials
-// p = t/8 + 32 j of slot c = t%8), the per-partial factors 2^(M_p - M) go to
-// LDS, and thread (i, half) then sums coordinate i of slots 4*half .. +3 in
-// partial order.  Finally out = Pi_V^T o~ / l with Pi_V staged in LDS.
+// Grid (4, rows): workgroup (part, row) finishes query slots 2 part and
+// 2 part + 1 of the row.  The row's workgroup partials of a slot are merged
+// with the usual max / rescale rule: the maximum and the normaliser are
+// reduced over the workgroup (thread t visits partials p = t/2 + 128 j of
+// local slot t%2), the per-partial factors 2^(M_p - M) go to LDS, and thread
+// (i, c) sums coordinate i of local slot c in partial order.  Finally
+// out = Pi_V^T o~ / l with Pi_V staged in LDS.
 constexpr int kMaxWg = 1024;   // plan_decode keeps a row at <= 4096 / kWaves partials
 
 __global__ void __launch_bounds__(256) k_combine(CArgs a) {
   __shared__ __align__(16) float mat[D][D];
-  __shared__ __align__(16) float scl[kMaxWg * 8];
-  __shared__ float ov[8][D];
-  __shared__ float red[2][4][8];
-  const int row = blockIdx.x;
+  __shared__ __align__(16) float scl[kMaxWg * 2];
+  __shared__ __align__(16) float ov[2][D];
+  __shared__ float red[2][4][2];
+  const int part = blockIdx.x, row = blockIdx.y;
   const int qg = row % a.qgroups;
   const int bh = row / a.qgroups;
   const int b = bh / a.Hkv, h = bh % a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int64_t base = (int64_t)row * a.n_wg * 8;       // record (p, c) = base + 8p + c
+  const int64_t base = (int64_t)row * a.n_wg * 8 + 2 * part;   // record (p, slot) = base + 8p + local slot
   Stage st;
   stage_load(st, a.rotV, D, tid);
-  const int cs = tid & 7;
+  const int cr = tid & 1;
   float Mx = -INFINITY;
-  for (int p = tid >> 3; p < a.n_wg; p += 32) Mx = fmaxf(Mx, a.part_ml[(base + 8 * p + cs) * 2]);
-  Mx = fmaxf(Mx, __shfl_xor(Mx, 8));
-  Mx = fmaxf(Mx, __shfl_xor(Mx, 16));
-  Mx = fmaxf(Mx, __shfl_xor(Mx, 32));
-  if (lane < 8) red[0][wv][lane] = Mx;
+  for (int p = tid >> 1; p < a.n_wg; p += 128) Mx = fmaxf(Mx, a.part_ml[(base + 8 * p + cr) * 2]);
+#pragma unroll
+  for (int o = 2; o < 64; o <<= 1) Mx = fmaxf(Mx, __shfl_xor(Mx, o));
+  if (lane < 2) red[0][wv][lane] = Mx;
   __syncthreads();
-  Mx = fmaxf(fmaxf(red[0][0][cs], red[0][1][cs]), fmaxf(red[0][2][cs], red[0][3][cs]));
+  Mx = fmaxf(fmaxf(red[0][0][cr], red[0][1][cr]), fmaxf(red[0][2][cr], red[0][3][cr]));
   float ls = 0.f;
-  for (int p = tid >> 3; p < a.n_wg; p += 32) {
-    const float Mp = a.part_ml[(base + 8 * p + cs) * 2];
-    const float lp = a.part_ml[(base + 8 * p + cs) * 2 + 1];
+  for (int p = tid >> 1; p < a.n_wg; p += 128) {
+    const float Mp = a.part_ml[(base + 8 * p + cr) * 2];
+    const float lp = a.part_ml[(base + 8 * p + cr) * 2 + 1];
     const float f = (Mx == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(Mp - Mx);
-    scl[8 * p + cs] = f;
+    scl[2 * p + cr] = f;
     ls += f * lp;
   }
-  ls += __shfl_xor(ls, 8);
-  ls += __shfl_xor(ls, 16);
-  ls += __shfl_xor(ls, 32);
-  if (lane < 8) red[1][wv][lane] = ls;
+#pragma unroll
+  for (int o = 2; o < 64; o <<= 1) ls += __shfl_xor(ls, o);
+  if (lane < 2) red[1][wv][lane] = ls;
   stage_store(mat, st, D, tid);
   __syncthreads();
-  const int i = tid & (D - 1), c0 = (tid >> 7) * 4;
-  float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
-  const float* po = a.part_o + (base + c0) * D + i;
+  const int i = tid & (D - 1), c = tid >> 7;
+  float o = 0.f;
+  {
+    const float* po = a.part_o + (base + c) * D + i;
 #pragma unroll 8
-  for (int p = 0; p < a.n_wg; ++p) {
-    const f32x4 f = *reinterpret_cast<const f32x4*>(&scl[8 * p + c0]);
-    const float* pp = po + (int64_t)p * 8 * D;
-    o0 += f[0] * pp[0];
-    o1 += f[1] * pp[D];
-    o2 += f[2] * pp[2 * D];
-    o3 += f[3] * pp[3 * D];
+    for (int p = 0; p < a.n_wg; ++p) o = fmaf(scl[2 * p + c], po[(int64_t)p * 8 * D], o);
   }
   {
-    const float oo[4] = {o0, o1, o2, o3};
-    for (int k = 0; k < 4; ++k) {
-      const int c = c0 + k;
-      const float l = ((red[1][0][c] + red[1][1][c]) + red[1][2][c]) + red[1][3][c];
-      ov[c][i] = oo[k] * (l > 0.f ? 1.0f / l : 0.f);
-    }
+    const float l = ((red[1][0][c] + red[1][1][c]) + red[1][2][c]) + red[1][3][c];
+    ov[c][i] = o * (l > 0.f ? 1.0f / l : 0.f);
   }
   __syncthreads();
-  float r0 = 0.f, r1 = 0.f, r2 = 0.f, r3 = 0.f;
-#pragma unroll 8
-  for (int k = 0; k < D; ++k) {
-    const float pv = mat[k][i];
-    r0 += pv * ov[c0][k]; r1 += pv * ov[c0 + 1][k]; r2 += pv * ov[c0 + 2][k]; r3 += pv * ov[c0 + 3][k];
+  float r = 0.f;
+#pragma unroll 4
+  for (int k = 0; k < D; k += 4) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(&ov[c][k]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) r = fmaf(mat[k + u][i], v[u], r);
   }
-  const float rr[4] = {r0, r1, r2, r3};
-  for (int k = 0; k < 4; ++k) {
-    const int jq = qg * 8 + c0 + k;
-    if (jq < a.g) a.out[((int64_t)b * a.Hq + h * a.g + jq) * D + i] = rr[k];
-  }
+  const int jq = qg * 8 + 2 * part + c;
+  if (jq < a.g) a.out[((int64_t)b * a.Hq + h * a.g + jq) * D + i] = r;
 }
 
 template <int BK, int BV>
@@ -874,9 +846,9 @@ hipError_t launch_decode(const tq_codebook* kcb, const tq_codebook* vcb, const v
   pa.mp = kcb->mp;
   pa.qscale = sm_scale * LOG2E;
   pa.rotKT = kcb->dev.rotT;
-  pa.qjlKT = kcb->dev.qjlT;
+  pa.sprotKT = kcb->dev.sprotT;
   pa.qop = qop;
-  hipLaunchKernelGGL(k_prologue, dim3((unsigned)plan.rows), dim3(256), 0, stream, pa);
+  hipLaunchKernelGGL(k_prologue, dim3(4, (unsigned)plan.rows), dim3(256), 0, stream, pa);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
@@ -927,7 +899,7 @@ hipError_t launch_decode(const tq_codebook* kcb, const tq_codebook* vcb, const v
   ca.Hq = (int)plan.Hq; ca.Hkv = (int)plan.Hkv; ca.g = plan.g; ca.qgroups = plan.qgroups;
   ca.n_wg = plan.n_wg;
   ca.out = out;
-  hipLaunchKernelGGL(k_combine, dim3((unsigned)plan.rows), dim3(256), 0, stream, ca);
+  hipLaunchKernelGGL(k_combine, dim3(4, (unsigned)plan.rows), dim3(256), 0, stream, ca);
   return hipGetLastError();
 }
 

@@ -352,21 +352,44 @@ __global__ void __launch_bounds__(4 * NI) k_quantize_small(SmallArgs sa) {
   // thread (i, kq) = (tid % NI, tid / NI) forms the partial product of output
   // coordinate i over the input coordinates NI/4 kq .. NI/4 (kq + 1) - 1, so
   // every matrix load of a thread is independent and issued together; the
-  // four partials are summed in LDS in a fixed order.
+  // four partials are summed in LDS in a fixed order.  With NI = 128 the
+  // thread's rotation and sketch entries, the boundaries and the centroids
+  // are all requested before the vector itself, so the vector costs one
+  // memory round trip in total.
   constexpr int NT = 4 * NI, KQ = NI / 4, NW = NI / 64;
+  constexpr bool PRE = NI == 128;
   const SmallJob& a = sa.job[blockIdx.y];
   __shared__ float xs[NI];
   __shared__ float part[4][NI];
   __shared__ float rs[NI];
   __shared__ uint8_t ids[NI];
   __shared__ float red[2][NW];
+  __shared__ float s_bnd[256], s_cent[256];
   const int64_t vec = blockIdx.x;                 // seq * n_tok + t
   const int64_t seq = vec / a.n_tok, t = vec % a.n_tok;
   const int64_t pos = a.tok_off + t;              // position in the sequence
   const int64_t row = seq * a.seq_stride + pos;
   const int tid = threadIdx.x;
   const int i = tid & (NI - 1), kq = tid / NI, l = tid & 63, w = tid >> 6;
+  const int L = 1 << a.bits;
+  float rv[PRE ? KQ : 1], qv[PRE ? KQ : 1];
+  if constexpr (PRE) {
+    const bool sk = a.m > 0;
+    const float* qsrc = sk ? a.qjlT : a.rotT;
+    const int qstr = sk ? a.mp : a.dp;
+    const int ir = i < a.dp ? i : a.dp - 1, iq = i < qstr ? i : qstr - 1;
+#pragma unroll
+    for (int kk = 0; kk < KQ; ++kk) {
+      const int k = KQ * kq + kk;
+      const int kc = k < a.d ? k : a.d - 1;
+      rv[kk] = a.rotT[kc * a.dp + ir];
+      qv[kk] = qsrc[kc * qstr + iq];
+    }
+  }
+  const float bv = tid < L - 1 ? a.bnd[tid] : 0.f;
+  const float cv = tid < L ? a.cent[tid] : 0.f;
   if (tid < NI) xs[tid] = (tid < a.d) ? load_elem<DT>(a.x, vec * a.d + tid) : 0.f;
+  if (tid < 256) { s_bnd[tid] = bv; s_cent[tid] = cv; }
   __syncthreads();
   float n2 = 0.f;
 #pragma unroll
@@ -380,7 +403,8 @@ __global__ void __launch_bounds__(4 * NI) k_quantize_small(SmallArgs sa) {
       for (int kk = 0; kk < KQ; ++kk) {
         const int k = KQ * kq + kk;
         const int kc = k < a.d ? k : a.d - 1;     // xs[k] = 0 beyond d
-        z += a.rotT[kc * a.dp + i] * xs[k];
+        if constexpr (PRE) z += rv[kk] * xs[k];
+        else z += a.rotT[kc * a.dp + i] * xs[k];
       }
     }
     part[kq][i] = z;
@@ -389,11 +413,10 @@ __global__ void __launch_bounds__(4 * NI) k_quantize_small(SmallArgs sa) {
   float y = 0.f, c = 0.f;
   if (tid < NI) {
     y = (((part[0][i] + part[1][i]) + part[2][i]) + part[3][i]) * inv;
-    const int L = 1 << a.bits;
     int q = 0;
     for (int step = L >> 1; step >= 1; step >>= 1)
-      if (y >= a.bnd[q + step - 1]) q += step;
-    c = (i < a.d) ? a.cent[q] : 0.f;
+      if (y >= s_bnd[q + step - 1]) q += step;
+    c = (i < a.d) ? s_cent[q] : 0.f;
     if (i < a.d) ids[i] = (uint8_t)q;
     const float s2 = wave_sum(c * c);
     if (l == 0) red[0][w] = s2;
@@ -420,7 +443,8 @@ __global__ void __launch_bounds__(4 * NI) k_quantize_small(SmallArgs sa) {
         for (int kk = 0; kk < KQ; ++kk) {
           const int k = KQ * kq + kk;
           const int kc = k < a.d ? k : a.d - 1;   // rs[k] = 0 beyond d
-          u += a.qjlT[kc * a.mp + i] * rs[k];
+          if constexpr (PRE) u += qv[kk] * rs[k];
+          else u += a.qjlT[kc * a.mp + i] * rs[k];
         }
       }
       part[kq][i] = u;

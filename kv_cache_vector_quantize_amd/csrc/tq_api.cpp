@@ -105,6 +105,7 @@ void free_dev(DeviceCodebook& d) {
   if (d.qjl) (void)hipFree(d.qjl);
   if (d.rotT) (void)hipFree(d.rotT);
   if (d.qjlT) (void)hipFree(d.qjlT);
+  if (d.sprotT) (void)hipFree(d.sprotT);
   if (d.pair_tab) (void)hipFree(d.pair_tab);
   if (d.rop) (void)hipFree(d.rop);
   if (d.qtab) (void)hipFree(d.qtab);
@@ -276,14 +277,24 @@ tq_status tq_codebook_build(const tq_params* params, tq_codebook** out) {
       return hip_fail(e, "codebook upload");
     }
     if (m > 0) {
-      std::vector<float> qjl((size_t)mp * dp, 0.f), qjlT((size_t)dp * mp, 0.f);
+      std::vector<float> qjl((size_t)mp * dp, 0.f), qjlT((size_t)dp * mp, 0.f), sprotT((size_t)dp * mp, 0.f);
       for (int j = 0; j < m; ++j)
         for (int i = 0; i < d; ++i) {
           qjl[(size_t)j * dp + i] = (float)cb->host.qjl[(size_t)j * d + i];
           qjlT[(size_t)i * mp + j] = (float)cb->host.qjl[(size_t)j * d + i];
         }
+      // sqrt(pi/2)/m S Pi in double, rounded once
+      const double cq = std::sqrt(std::acos(-1.0) / 2.0) / (double)m;
+      for (int j = 0; j < m; ++j)
+        for (int k = 0; k < d; ++k) {
+          double acc = 0.0;
+          for (int i = 0; i < d; ++i)
+            acc += cb->host.qjl[(size_t)j * d + i] * cb->host.rot[(size_t)i * d + k];
+          sprotT[(size_t)k * mp + j] = (float)(cq * acc);
+        }
       if ((e = upload(&cb->dev.qjl, qjl)) != hipSuccess ||
-          (e = upload(&cb->dev.qjlT, qjlT)) != hipSuccess) {
+          (e = upload(&cb->dev.qjlT, qjlT)) != hipSuccess ||
+          (e = upload(&cb->dev.sprotT, sprotT)) != hipSuccess) {
         free_dev(cb->dev);
         delete cb;
         return hip_fail(e, "codebook upload");

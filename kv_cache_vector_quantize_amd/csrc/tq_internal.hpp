@@ -29,6 +29,9 @@ struct DeviceCodebook {
   float* qjl = nullptr;     // [mp*dp] fp32 row-major S, zero-padded (or null)
   float* rotT = nullptr;    // [dp*dp] fp32, rotT[k][i] = Pi[i][k]
   float* qjlT = nullptr;    // [dp*mp] fp32, qjlT[i][j] = S[j][i] (or null)
+  // [dp*mp] fp32, sprotT[k][j] = sqrt(pi/2)/m * (S Pi)[j][k] (or null): the
+  // sketch of a rotated query in one product, t = sqrt(pi/2)/m S (Pi q)
+  float* sprotT = nullptr;
   // decode operand tables (bf16 hi/lo split of the centroids):
   //  bits <= 4: entry e = a | (b << bits) holds two dwords
   //             {hi(c[a]) | hi(c[b]) << 16, lo(c[a]) | lo(c[b]) << 16}
