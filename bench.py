@@ -141,6 +141,7 @@ def quantize_leg(torch, tq, synth, dev, iters, warm):
     # the rotation runs as bf16 MFMAs on a two-part split of Pi (bf16 input,
     # codes of up to 4 bits): two issued products per useful one
     mfma_flops = 2 * flops
+    deq = dequantize_leg(torch, tq, kcb, vcb, kc, vc, B * H, N, iters, warm)
     del k, v, kc, vc
     return dict(workload="quantize-only layer: B=16, Hkv=8, d=128, 32768 tokens, bf16 K and V "
                          "(4 outlier channels/head x15), 4-bit, no QJL",
@@ -150,7 +151,46 @@ def quantize_leg(torch, tq, synth, dev, iters, warm):
                 rotation_TFLOP_per_s=round(flops / (ms * 1e-3) / 1e12, 2),
                 mfma_TFLOP_per_s=round(mfma_flops / (ms * 1e-3) / 1e12, 2),
                 mfma_frac_bf16_peak=round(mfma_flops / (ms * 1e-3) / 2.5e15, 4),
-                bytes_per_call=int(in_bytes + out_bytes))
+                bytes_per_call=int(in_bytes + out_bytes), dequantize=deq)
+
+
+def dequantize_leg(torch, tq, kcb, vcb, kc, vc, n_seq, n_tok, iters, warm):
+    """tq_dequantize of the quantize layer's K (row) and V (tile32) codes back
+    to bf16: reads 68 B of codes and writes 256 B per vector."""
+    d = kcb.d
+    ko = torch.empty((n_seq, n_tok, d), dtype=torch.bfloat16, device="cuda")
+    vo = torch.empty_like(ko)
+
+    def call():
+        tq.tq_dequantize(kcb, kc, n_seq, n_tok, out=ko)
+        tq.tq_dequantize(vcb, vc, n_seq, n_tok, out=vo)
+    for _ in range(warm):
+        call()
+    torch.cuda.synchronize()
+    tq.tq_profile_enable(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    tq.tq_profile_enable(False)
+    kms, kn = tq.tq_profile_read(tq.TQ_KERNEL_DEQUANTIZE)
+    ms = e0.elapsed_time(e1) / iters
+    n_vec = 2 * n_seq * n_tok
+    nbytes = n_vec * ((d * kcb.bits // 8 + 4) + d * 2)
+    kern_ms = kms / kn
+    # Pi^T hi.hi + hi.lo + lo.hi on 32x32x16 bf16 MFMAs: three issued products
+    # per useful one
+    mfma_flops = 3 * 2.0 * d * d * n_vec
+    del ko, vo
+    return dict(workload=f"dequantize the quantize layer's K (row) and V (tile32) {kcb.bits}-bit codes "
+                         f"to bf16: {n_vec} vectors, d={d}",
+                GB_per_s=round(nbytes / (ms * 1e-3) / 1e9, 1), frac_hbm=round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                ms_per_call=round(ms, 4), kernel_ms=round(kern_ms, 4),
+                kernel_GB_per_s=round(nbytes / 2 / (kern_ms * 1e-3) / 1e9, 1),
+                mfma_TFLOP_per_s=round(mfma_flops / (ms * 1e-3) / 1e12, 2),
+                bytes_per_call=int(nbytes))
 
 
 def _exact_attention_np(q, k, v, tau):

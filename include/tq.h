@@ -213,18 +213,46 @@ tq_status tq_ip_topk(const tq_codebook* cb, const float* queries, int64_t nq,
                      const tq_codes* db, int64_t n_db, int32_t k, int64_t* out_idx,
                      float* out_score, void* workspace, size_t ws_bytes, void* stream);
 
+/* Vectors back from their codes: the decompress half of the compress /
+ * decompress pair of [AGENT] 三、工程实现 item 1, computing the estimate of
+ * [WIT] 工作原理 > 第一阶段 items 1-2 and 第二阶段：QJL 残差校正 in the original
+ * domain:
+ *   x_hat = Pi^T ( scale c[idx] + sqrt(pi/2)/m rnorm S^T (2 sign - 1) )
+ * (the sketch term only when qjl_m > 0), so <q, x_hat> is the estimate that
+ * tq_attn_decode and tq_ip_topk form from the codes.
+ *  codes       positions [tok_offset, tok_offset + n_tok) of sequences
+ *              0..n_seq-1, ROW or TILE32 layout as tq_quantize_kv writes them
+ *              (tok_offset + n_tok <= seq_stride)
+ *  out         device [n_seq][n_tok][d] of out_dt (TQ_F32, TQ_BF16 or TQ_F16;
+ *              the 16-bit types round to nearest even), 16-byte aligned
+ *  n_seq == 0 or n_tok == 0 is a no-op that returns TQ_OK.
+ * With d == 128 and qjl_m <= 128 the contractions run on bf16 MFMA with
+ * two-part (hi + lo) splits of Pi, of the centroids and of the sketch
+ * operand (about 2^-16 relative to |x_hat|); other shapes use fp32 FMAs.
+ * Errors: TQ_ERR_INVALID, TQ_ERR_HIP. */
+tq_status tq_dequantize(const tq_codebook* cb, const tq_codes* codes, int64_t n_seq,
+                        int64_t n_tok, int64_t tok_offset, void* out, tq_dtype out_dt,
+                        void* stream);
+
 /* Kernel timing (instrumentation; not part of the method).
  * tq_profile_enable(1) clears the calling thread's records and starts
- * recording: every later tq_quantize_kv / tq_attn_decode / tq_ip_topk on this thread
+ * recording: every later tq_quantize_kv / tq_attn_decode / tq_ip_topk /
+ * tq_dequantize on this thread
  * records a hipEvent pair on its stream around each launch of its main
  * kernel (the quantize kernel, once per tensor; the decode split kernel;
- * the top-k score kernel).
+ * the top-k score kernel; the dequantize kernel).
  * tq_profile_enable(0) stops recording and keeps the records.
  * tq_profile_read waits for the recorded events and returns the summed
  * elapsed milliseconds and the number of launches of one kernel
- * (TQ_KERNEL_QUANTIZE, TQ_KERNEL_DECODE_SPLIT or TQ_KERNEL_TOPK).  Events are created by the
+ * (TQ_KERNEL_QUANTIZE, TQ_KERNEL_DECODE_SPLIT, TQ_KERNEL_TOPK or
+ * TQ_KERNEL_DEQUANTIZE).  Events are created by the
  * library (no device memory is allocated). */
-typedef enum { TQ_KERNEL_QUANTIZE = 0, TQ_KERNEL_DECODE_SPLIT = 1, TQ_KERNEL_TOPK = 2 } tq_kernel;
+typedef enum {
+  TQ_KERNEL_QUANTIZE = 0,
+  TQ_KERNEL_DECODE_SPLIT = 1,
+  TQ_KERNEL_TOPK = 2,
+  TQ_KERNEL_DEQUANTIZE = 3
+} tq_kernel;
 tq_status tq_profile_enable(int32_t on);
 tq_status tq_profile_read(int32_t kernel, double* total_ms, int64_t* launches);
 

@@ -1,5 +1,5 @@
 """MI355X (gfx950) online KV-vector quantization, decode attention from
-packed codes and inner-product top-k over codes.  The compute runs in libtq.so (hand-written HIP kernels behind
+packed codes, inner-product top-k over codes and dequantization.  The compute runs in libtq.so (hand-written HIP kernels behind
 a C ABI, declared in include/tq.h); this package is a thin ctypes binding."""
 from ._lib import (  # noqa: F401
     EXPORTS,
@@ -9,6 +9,7 @@ from ._lib import (  # noqa: F401
     TQ_F32,
     TQ_LAYOUT_ROW,
     TQ_KERNEL_DECODE_SPLIT,
+    TQ_KERNEL_DEQUANTIZE,
     TQ_KERNEL_QUANTIZE,
     TQ_KERNEL_TOPK,
     TQ_LAYOUT_TILE32,
@@ -19,6 +20,7 @@ from ._lib import (  # noqa: F401
     tq_attn_decode,
     tq_attn_decode_workspace,
     tq_codebook_values,
+    tq_dequantize,
     tq_ip_topk,
     tq_ip_topk_workspace,
     tq_profile_enable,

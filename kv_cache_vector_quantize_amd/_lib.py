@@ -23,9 +23,10 @@ TQ_LAYOUT_ROW, TQ_LAYOUT_TILE32 = 0, 1
 EXPORTS = (
     "tq_codebook_build", "tq_codebook_destroy", "tq_codebook_export", "tq_codebook_values",
     "tq_code_row_bytes", "tq_quantize_kv", "tq_attn_decode_workspace", "tq_attn_decode",
-    "tq_ip_topk_workspace", "tq_ip_topk", "tq_profile_enable", "tq_profile_read", "tq_last_error",
+    "tq_ip_topk_workspace", "tq_ip_topk", "tq_dequantize", "tq_profile_enable", "tq_profile_read",
+    "tq_last_error",
 )
-TQ_KERNEL_QUANTIZE, TQ_KERNEL_DECODE_SPLIT, TQ_KERNEL_TOPK = 0, 1, 2
+TQ_KERNEL_QUANTIZE, TQ_KERNEL_DECODE_SPLIT, TQ_KERNEL_TOPK, TQ_KERNEL_DEQUANTIZE = 0, 1, 2, 3
 
 
 class TQError(RuntimeError):
@@ -76,6 +77,7 @@ def lib() -> ctypes.CDLL:
     L.tq_ip_topk_workspace.argtypes = [i64, i64, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
     L.tq_ip_topk.argtypes = [vp, vp, i64, ctypes.POINTER(tq_codes), i64, i32, vp, vp, vp,
                              ctypes.c_size_t, vp]
+    L.tq_dequantize.argtypes = [vp, ctypes.POINTER(tq_codes), i64, i64, i64, vp, i32, vp]
     L.tq_profile_enable.argtypes = [i32]
     L.tq_profile_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
     for name in EXPORTS:
@@ -228,6 +230,22 @@ def tq_quantize_kv(kcb, vcb, k, v, k_out: Codes | None, v_out: Codes | None,
         _dtype_code(ref), n_seq, n_tok, int(tok_offset),
         ctypes.byref(kd) if kd is not None else None, ctypes.byref(vd) if vd is not None else None,
         _stream_handle(stream)))
+
+
+def tq_dequantize(cb, codes: Codes, n_seq: int, n_tok: int, tok_offset: int = 0, out=None,
+                  dtype=None, stream=None):
+    """Vectors of positions [tok_offset, tok_offset + n_tok) of sequences
+    0..n_seq-1 back from their codes.  Returns out ([n_seq, n_tok, d], fp32
+    unless dtype / out say otherwise)."""
+    import torch
+    if out is None:
+        out = torch.empty((n_seq, n_tok, cb.d), dtype=dtype or torch.float32, device=codes.scale.device)
+    if not out.is_contiguous():
+        raise ValueError("out must be contiguous")
+    cd = codes.descriptor()
+    _check(lib().tq_dequantize(cb.handle, ctypes.byref(cd), int(n_seq), int(n_tok), int(tok_offset),
+                               out.data_ptr(), _dtype_code(out), _stream_handle(stream)))
+    return out
 
 
 def tq_attn_decode_workspace(B, Hq, Hkv, n_ctx, d) -> int:

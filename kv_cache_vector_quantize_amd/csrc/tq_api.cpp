@@ -106,6 +106,10 @@ void free_dev(DeviceCodebook& d) {
   if (d.rotT) (void)hipFree(d.rotT);
   if (d.qjlT) (void)hipFree(d.qjlT);
   if (d.sprotT) (void)hipFree(d.sprotT);
+  if (d.sprot) (void)hipFree(d.sprot);
+  if (d.dqop) (void)hipFree(d.dqop);
+  if (d.dqs) (void)hipFree(d.dqs);
+  if (d.dqcs) (void)hipFree(d.dqcs);
   if (d.pair_tab) (void)hipFree(d.pair_tab);
   if (d.rop) (void)hipFree(d.rop);
   if (d.qtab) (void)hipFree(d.qtab);
@@ -179,7 +183,7 @@ namespace {
 struct EventPair { hipEvent_t a = nullptr, b = nullptr; };
 struct ProfileState {
   bool on = false;
-  std::vector<EventPair> rec[3];
+  std::vector<EventPair> rec[4];
   ~ProfileState() {
     for (auto& v : rec)
       for (auto& p : v) { (void)hipEventDestroy(p.a); (void)hipEventDestroy(p.b); }
@@ -277,7 +281,8 @@ tq_status tq_codebook_build(const tq_params* params, tq_codebook** out) {
       return hip_fail(e, "codebook upload");
     }
     if (m > 0) {
-      std::vector<float> qjl((size_t)mp * dp, 0.f), qjlT((size_t)dp * mp, 0.f), sprotT((size_t)dp * mp, 0.f);
+      std::vector<float> qjl((size_t)mp * dp, 0.f), qjlT((size_t)dp * mp, 0.f), sprotT((size_t)dp * mp, 0.f),
+          sprot((size_t)mp * dp, 0.f);
       for (int j = 0; j < m; ++j)
         for (int i = 0; i < d; ++i) {
           qjl[(size_t)j * dp + i] = (float)cb->host.qjl[(size_t)j * d + i];
@@ -285,16 +290,59 @@ tq_status tq_codebook_build(const tq_params* params, tq_codebook** out) {
         }
       // sqrt(pi/2)/m S Pi in double, rounded once
       const double cq = std::sqrt(std::acos(-1.0) / 2.0) / (double)m;
+      std::vector<double> sp((size_t)m * d, 0.0);   // cq (S Pi)[j][k]
       for (int j = 0; j < m; ++j)
         for (int k = 0; k < d; ++k) {
           double acc = 0.0;
           for (int i = 0; i < d; ++i)
             acc += cb->host.qjl[(size_t)j * d + i] * cb->host.rot[(size_t)i * d + k];
+          sp[(size_t)j * d + k] = cq * acc;
           sprotT[(size_t)k * mp + j] = (float)(cq * acc);
+          sprot[(size_t)j * dp + k] = (float)(cq * acc);
         }
+      if ((e = upload(&cb->dev.sprot, sprot)) != hipSuccess) {
+        free_dev(cb->dev);
+        delete cb;
+        return hip_fail(e, "codebook upload");
+      }
+      if (d == 128 && m <= 128) {
+        // dequantize operands: column j of (S Pi)^T scaled by 2^(127 - 2^(j % 8))
+        // to meet the sign bit of row j left at bf16 bit 7 + j % 8
+        std::vector<double> a2((size_t)128 * 128, 0.0);
+        std::vector<float> cs(128, 0.f);
+        for (int k = 0; k < 128; ++k) {
+          double sum = 0.0;
+          for (int j = 0; j < m; ++j) {
+            const double v = sp[(size_t)j * d + k];
+            sum += v;
+            a2[(size_t)k * 128 + j] = std::ldexp(v, 127 - (1 << (j % 8)));
+          }
+          cs[k] = (float)sum;
+        }
+        std::vector<uint32_t> dqs;
+        build_q128_operands(a2, dqs);
+        if ((e = upload(&cb->dev.dqs, dqs)) != hipSuccess || (e = upload(&cb->dev.dqcs, cs)) != hipSuccess) {
+          free_dev(cb->dev);
+          delete cb;
+          return hip_fail(e, "codebook upload");
+        }
+      }
       if ((e = upload(&cb->dev.qjl, qjl)) != hipSuccess ||
           (e = upload(&cb->dev.qjlT, qjlT)) != hipSuccess ||
           (e = upload(&cb->dev.sprotT, sprotT)) != hipSuccess) {
+        free_dev(cb->dev);
+        delete cb;
+        return hip_fail(e, "codebook upload");
+      }
+    }
+    if (d == 128) {
+      // Pi^T operands of the d = 128 dequantize kernel
+      std::vector<double> pt((size_t)128 * 128);
+      for (int r = 0; r < 128; ++r)
+        for (int c = 0; c < 128; ++c) pt[(size_t)r * 128 + c] = cb->host.rot[(size_t)c * 128 + r];
+      std::vector<uint32_t> dqop;
+      build_q128_operands(pt, dqop);
+      if ((e = upload(&cb->dev.dqop, dqop)) != hipSuccess) {
         free_dev(cb->dev);
         delete cb;
         return hip_fail(e, "codebook upload");
@@ -525,6 +573,34 @@ tq_status tq_ip_topk(const tq_codebook* cb, const float* queries, int64_t nq,
   }
 }
 
+tq_status tq_dequantize(const tq_codebook* cb, const tq_codes* codes, int64_t n_seq,
+                        int64_t n_tok, int64_t tok_offset, void* out, tq_dtype out_dt,
+                        void* stream) {
+  try {
+    if (!cb) return fail(TQ_ERR_INVALID, "codebook is NULL");
+    if (out_dt != TQ_F32 && out_dt != TQ_BF16 && out_dt != TQ_F16) return fail(TQ_ERR_INVALID, "bad out dtype");
+    if (n_seq < 0 || n_tok < 0 || tok_offset < 0)
+      return fail(TQ_ERR_INVALID, "n_seq, n_tok and tok_offset must be >= 0");
+    if (n_seq == 0 || n_tok == 0) return TQ_OK;
+    if (!out) return fail(TQ_ERR_INVALID, "out is NULL");
+    if (!aligned(out, 16)) return fail(TQ_ERR_INVALID, "out must be 16-byte aligned");
+    tq_status s = check_codes(cb, codes, tok_offset + n_tok, "codes", false);
+    if (s != TQ_OK) return s;
+    if (!quantize_supported(cb))
+      return fail(TQ_ERR_UNSUPPORTED, "dequantize supports d <= 256 and qjl_m <= 256");
+    if (n_seq * n_tok > 0x7FFFFFFF || n_seq > 0x7FFFFFFF)
+      return fail(TQ_ERR_UNSUPPORTED, "n_seq * n_tok must stay below 2^31");
+    s = current_device_matches(cb);
+    if (s != TQ_OK) return s;
+    DequantJob job{*codes, n_seq, n_tok, tok_offset, out, out_dt};
+    hipError_t e = launch_dequantize(cb, job, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "dequantize launch");
+    return TQ_OK;
+  } catch (...) {
+    return fail(TQ_ERR_ALLOC, "tq_dequantize: unexpected exception");
+  }
+}
+
 tq_status tq_profile_enable(int32_t on) {
   if (on) {
     for (auto& v : g_prof.rec) {
@@ -537,7 +613,7 @@ tq_status tq_profile_enable(int32_t on) {
 }
 
 tq_status tq_profile_read(int32_t kernel, double* total_ms, int64_t* launches) {
-  if (kernel < 0 || kernel > 2) return fail(TQ_ERR_INVALID, "unknown kernel id");
+  if (kernel < 0 || kernel > 3) return fail(TQ_ERR_INVALID, "unknown kernel id");
   double tot = 0.0;
   for (auto& p : g_prof.rec[kernel]) {
     hipError_t e = hipEventSynchronize(p.b);

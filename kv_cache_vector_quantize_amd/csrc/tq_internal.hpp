@@ -32,6 +32,17 @@ struct DeviceCodebook {
   // [dp*mp] fp32, sprotT[k][j] = sqrt(pi/2)/m * (S Pi)[j][k] (or null): the
   // sketch of a rotated query in one product, t = sqrt(pi/2)/m S (Pi q)
   float* sprotT = nullptr;
+  // dequantize (dequantize.hip):
+  //  sprot: [mp*dp] fp32 row-major sqrt(pi/2)/m (S Pi) (or null)
+  //  dqop:  Pi^T as bf16 A operands of v_mfma_f32_32x32x16_bf16 in the layout
+  //         of rop (d = 128 only)
+  //  dqs:   sqrt(pi/2)/m (S Pi)^T with column j scaled by 2^(127 - 2^(j % 8)),
+  //         same layout, zero columns past m (d = 128, m <= 128)
+  //  dqcs:  [128] fp32 column sums sum_j sqrt(pi/2)/m (S Pi)[j][k]
+  float* sprot = nullptr;
+  uint32_t* dqop = nullptr;
+  uint32_t* dqs = nullptr;
+  float* dqcs = nullptr;
   // decode operand tables (bf16 hi/lo split of the centroids):
   //  bits <= 4: entry e = a | (b << bits) holds two dwords
   //             {hi(c[a]) | hi(c[b]) << 16, lo(c[a]) | lo(c[b]) << 16}
@@ -101,6 +112,17 @@ hipError_t launch_quantize128(const tq_codebook* cb, const QuantJob& job, hipStr
 hipError_t launch_quantize_small(const tq_codebook* const* cbs, const QuantJob* jobs, int njobs,
                                  hipStream_t stream);
 constexpr int64_t kSmallMaxTok = 8;   // appends of up to this many tokens per sequence
+
+// Dequantize positions [tok_offset, tok_offset + n_tok) of n_seq sequences
+// into out [n_seq][n_tok][d] of dtype dt.
+struct DequantJob {
+  tq_codes codes;
+  int64_t n_seq, n_tok, tok_offset;
+  void* out;
+  tq_dtype dt;
+};
+bool dequantize128_supported(const tq_codebook* cb);
+hipError_t launch_dequantize(const tq_codebook* cb, const DequantJob& job, hipStream_t stream);
 
 struct DecodePlan {
   int64_t B, Hq, Hkv, n_ctx;
