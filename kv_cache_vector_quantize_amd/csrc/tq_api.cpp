@@ -56,6 +56,19 @@ void build_q128_operands(const std::vector<double>& M, std::vector<uint32_t>& ou
       }
 }
 
+// Column order of the d = 128 dequantize operands: k-step s, lane half h,
+// element j of an MFMA operand is column 64h + 8s + j of M (so a lane's codes
+// of two consecutive steps are one contiguous run of a code row).
+std::vector<double> dq_permute_columns(const std::vector<double>& M) {
+  std::vector<double> out((size_t)128 * 128);
+  for (int r = 0; r < 128; ++r)
+    for (int s = 0; s < 8; ++s)
+      for (int h = 0; h < 2; ++h)
+        for (int j = 0; j < 8; ++j)
+          out[(size_t)r * 128 + 16 * s + 8 * h + j] = M[(size_t)r * 128 + 64 * h + 8 * s + j];
+  return out;
+}
+
 // Index cells over y in [-1, 1] for the fp32 boundaries t: cell width 1/G is
 // below 0.9 x the smallest gap between consecutive boundaries, so a cell holds
 // at most one.  Entry c = {#t < c/G - 1, bits of (t G + G) for the t inside
@@ -320,7 +333,7 @@ tq_status tq_codebook_build(const tq_params* params, tq_codebook** out) {
           cs[k] = (float)sum;
         }
         std::vector<uint32_t> dqs;
-        build_q128_operands(a2, dqs);
+        build_q128_operands(dq_permute_columns(a2), dqs);
         if ((e = upload(&cb->dev.dqs, dqs)) != hipSuccess || (e = upload(&cb->dev.dqcs, cs)) != hipSuccess) {
           free_dev(cb->dev);
           delete cb;
@@ -341,7 +354,7 @@ tq_status tq_codebook_build(const tq_params* params, tq_codebook** out) {
       for (int r = 0; r < 128; ++r)
         for (int c = 0; c < 128; ++c) pt[(size_t)r * 128 + c] = cb->host.rot[(size_t)c * 128 + r];
       std::vector<uint32_t> dqop;
-      build_q128_operands(pt, dqop);
+      build_q128_operands(dq_permute_columns(pt), dqop);
       if ((e = upload(&cb->dev.dqop, dqop)) != hipSuccess) {
         free_dev(cb->dev);
         delete cb;

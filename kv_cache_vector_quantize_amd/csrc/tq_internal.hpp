@@ -35,9 +35,10 @@ struct DeviceCodebook {
   // dequantize (dequantize.hip):
   //  sprot: [mp*dp] fp32 row-major sqrt(pi/2)/m (S Pi) (or null)
   //  dqop:  Pi^T as bf16 A operands of v_mfma_f32_32x32x16_bf16 in the layout
-  //         of rop (d = 128 only)
+  //         of rop, columns permuted so that k-step s, lane half h, element j
+  //         is column 64h + 8s + j (d = 128 only)
   //  dqs:   sqrt(pi/2)/m (S Pi)^T with column j scaled by 2^(127 - 2^(j % 8)),
-  //         same layout, zero columns past m (d = 128, m <= 128)
+  //         same layout and permutation, zero columns past m (d = 128, m <= 128)
   //  dqcs:  [128] fp32 column sums sum_j sqrt(pi/2)/m (S Pi)[j][k]
   float* sprot = nullptr;
   uint32_t* dqop = nullptr;
