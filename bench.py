@@ -72,6 +72,7 @@ def parse():
     ap.add_argument("--no-quantize", action="store_true")
     ap.add_argument("--no-sweep", action="store_true", help="skip the bit-width sweep leg")
     ap.add_argument("--no-search", action="store_true", help="skip the vector-search leg")
+    ap.add_argument("--no-ab", action="store_true", help="skip the dequantize-then-attend leg")
     ap.add_argument("--calib-copy", action="store_true",
                     help="accepted for profiling commands; the 1 GiB copy always runs")
     return ap.parse_args()
@@ -103,8 +104,8 @@ def decode_workload(torch, tq, synth, dev):
     cfg = dict(workload="decode-128k GQA layer", B=B, Hq=Hq, Hkv=Hkv, d=d, context=N,
                keys="3-bit Lloyd-Max + 1-bit QJL m=128", values="4-bit Lloyd-Max",
                kv_input="bf16, N(0,1), channels 3/77/101 x20", query="bf16")
-    return dict(step=step, B=B, Hq=Hq, Hkv=Hkv, d=d, N=N, kcb=kcb, vcb=vcb, k=k, v=v, q=q,
-                tau=tau, bytes_per_token_head=per_token_head, cfg=cfg)
+    return dict(step=step, B=B, Hq=Hq, Hkv=Hkv, d=d, N=N, kcb=kcb, vcb=vcb, k=k, v=v, q=q, kc=kc, vc=vc,
+                out=out, ws=ws, tau=tau, bytes_per_token_head=per_token_head, cfg=cfg)
 
 
 def quantize_leg(torch, tq, synth, dev, iters, warm):
@@ -191,6 +192,77 @@ def dequantize_leg(torch, tq, kcb, vcb, kc, vc, n_seq, n_tok, iters, warm):
                 kernel_GB_per_s=round(nbytes / 2 / (kern_ms * 1e-3) / 1e9, 1),
                 mfma_TFLOP_per_s=round(mfma_flops / (ms * 1e-3) / 1e12, 2),
                 bytes_per_call=int(nbytes))
+
+
+def dequant_attend_leg(torch, tq, W, iters, warm, copy_gbps):
+    """The 128K layer's attention done dequantize-first, against decode from
+    the codes.  A: tq_dequantize of K (3-bit + QJL, row) and V (4-bit, tile32)
+    to bf16, then dense bf16 attention over them (torch batched products and
+    softmax: S = K_hat q^T, P = softmax(tau S) in fp32, o = P^T V_hat; every
+    right operand contiguous).  B: tq_attn_decode straight from the codes.
+    Both compute the same estimate: <q, K_hat_j> is the codes' logit
+    estimate.  dense_floor_ms is the time to read the bf16 K and V once at
+    the box's copy rate, the least any dense kernel over them needs."""
+    B, Hq, Hkv, d, N, tau = W["B"], W["Hq"], W["Hkv"], W["d"], W["N"], W["tau"]
+    g = Hq // Hkv
+    S_ = B * Hkv
+    kd = torch.empty((S_, N, d), dtype=torch.bfloat16, device="cuda")
+    vd = torch.empty_like(kd)
+    qt = W["q"].view(B, Hkv, g, d).reshape(S_, g, d).transpose(1, 2).contiguous()   # [S, d, g]
+
+    def dequant():
+        tq.tq_dequantize(W["kcb"], W["kc"], S_, N, out=kd)
+        tq.tq_dequantize(W["vcb"], W["vc"], S_, N, out=vd)
+
+    # logits straight to fp32 where this torch offers it (bf16 logits of
+    # magnitude ~30 lose ~0.1 to rounding, which moves the softmax by ~1%)
+    try:
+        torch.bmm(kd[:1, :64], qt[:1], out_dtype=torch.float32)
+        lg_dtype = "fp32"
+    except (RuntimeError, TypeError):
+        lg_dtype = "bf16"
+
+    def attend():
+        if lg_dtype == "fp32":
+            s = torch.bmm(kd, qt, out_dtype=torch.float32)             # [S, N, g]
+        else:
+            s = torch.bmm(kd, qt).float()
+        p = torch.softmax(s * tau, dim=1)                              # over the context
+        pt = p.to(torch.bfloat16).transpose(1, 2).contiguous()         # [S, g, N]
+        return torch.bmm(pt, vd)                                       # [S, g, d]
+
+    def direct():
+        tq.tq_attn_decode(W["kcb"], W["vcb"], W["q"], W["kc"], W["vc"], N, tau, out=W["out"], workspace=W["ws"])
+
+    def timed(fn):
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            r = fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters, r
+
+    deq_ms, _ = timed(dequant)
+    att_ms, o_ab = timed(attend)
+    dir_ms, _ = timed(direct)
+    o_ab = o_ab.float().view(B, Hkv, g, d).reshape(B, Hq, d)
+    err = float((o_ab - W["out"]).abs().max() / W["out"].abs().max())
+    kv_bytes = 2 * S_ * N * d * 2
+    floor_ms = kv_bytes / (copy_gbps * 1e9) * 1e3 if copy_gbps else None
+    del kd, vd
+    return dict(workload="decode-128k GQA layer, dequantize K and V to bf16 then dense bf16 attention, "
+                         "against decode from the codes",
+                dequantize_ms=round(deq_ms, 4), dense_attend_ms=round(att_ms, 4),
+                dequant_then_attend_ms=round(deq_ms + att_ms, 4),
+                dense_floor_ms=round(floor_ms, 4) if floor_ms else None,
+                decode_from_codes_ms=round(dir_ms, 4),
+                speedup_vs_dequant_first=round((deq_ms + att_ms) / dir_ms, 2),
+                max_rel_diff_of_outputs=round(err, 5), dense_logits=lg_dtype,
+                bf16_kv_bytes=int(kv_bytes))
 
 
 def _exact_attention_np(q, k, v, tau):
@@ -467,6 +539,10 @@ def main():
     torch.cuda.synchronize()
     res["copy_GBps"] = round(2 * (1 << 30) * n_copy / (c0.elapsed_time(c1) * 1e-3) / 1e9, 1)
     del src, dst
+    if not args.no_ab:
+        print("[bench] dequantize-then-attend leg", file=sys.stderr, flush=True)
+        res["dequant_then_attend"] = dequant_attend_leg(torch, tq, W, iters=max(3, args.steps // 5),
+                                                        warm=max(1, args.warmup // 5), copy_gbps=res["copy_GBps"])
     if not args.no_cpu_baseline:
         import oracle as O
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

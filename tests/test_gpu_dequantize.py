@@ -152,3 +152,45 @@ def test_dequantize_argument_errors(dev):
     # empty ranges are no-ops
     tq.tq_dequantize(cb, codes, 0, 8, 0, out=out)
     tq.tq_dequantize(cb, codes, 1, 0, 0, out=out[:, :0])
+
+
+def test_dequantize_then_attend_equals_decode_from_codes(dev):
+    """Dense attention over the GPU's reconstructions of K and V (fp32,
+    evaluated here in float64) equals the oracle's decode attention from the
+    same codes, to the decode bars (logits 1e-4 of the row's max |logit|,
+    outputs 2e-3 max-abs): reconstructing first and attending from the codes
+    compute the same estimate."""
+    _say("dequantize-then-attend vs decode from codes")
+    B, Hq, Hkv, d, N = 1, 4, 2, 128, 200
+    g = Hq // Hkv
+    tau = 1.0 / np.sqrt(d)
+    kcb = tq.Codebook(d, 3, qjl_m=128, rot_seed=1, qjl_seed=2)
+    vcb = tq.Codebook(d, 4, rot_seed=3)
+    okc, ovc = U.oracle_codebook(kcb), U.oracle_codebook(vcb)
+    k = U.to_f64(synth.kv_gaussian(B, Hkv, N, d, 31, dtype="f32", device="cpu", channels=[3, 77, 101], factor=20.0))
+    v = U.to_f64(synth.kv_gaussian(B, Hkv, N, d, 32, dtype="f32", device="cpu", channels=[3, 77, 101], factor=20.0))
+    q = np.random.default_rng(33).standard_normal((B, Hq, d))
+    S = (N + 31) // 32 * 32
+    kc = tq.Codes(kcb, B * Hkv, S, TQ_LAYOUT_ROW, device=dev)
+    vc = tq.Codes(vcb, B * Hkv, S, TQ_LAYOUT_TILE32, device=dev)
+    kr = [O.quantize(okc, k.reshape(B * Hkv, N, d)[s]) for s in range(B * Hkv)]
+    vr = [O.quantize(ovc, v.reshape(B * Hkv, N, d)[s]) for s in range(B * Hkv)]
+    for s in range(B * Hkv):
+        U.upload_oracle_codes(kc, s, kr[s], N)
+        U.upload_oracle_codes(vc, s, vr[s], N)
+    kh = tq.tq_dequantize(kcb, kc, B * Hkv, N).cpu().numpy().astype(np.float64).reshape(B, Hkv, N, d)
+    vh = tq.tq_dequantize(vcb, vc, B * Hkv, N).cpu().numpy().astype(np.float64).reshape(B, Hkv, N, d)
+    f32 = lambda a: a.astype(np.float32).astype(np.float64)
+    stack = lambda rs, key: np.stack([r[key] for r in rs]).reshape(B, Hkv, N, *rs[0][key].shape[1:])
+    okcodes = dict(idx=stack(kr, "idx"), scale=f32(stack(kr, "scale")), sign=stack(kr, "sign"),
+                   rnorm=f32(stack(kr, "rnorm")))
+    ovcodes = dict(idx=stack(vr, "idx"), scale=f32(stack(vr, "scale")))
+    ref_lg, ref_out = O.attn_decode(okc, ovc, q, okcodes, ovcodes, tau)
+    for b in range(B):
+        for hq in range(Hq):
+            h = hq // g
+            lg = tau * (kh[b, h] @ q[b, hq])
+            p = np.exp(lg - lg.max())
+            out = (p / p.sum()) @ vh[b, h]
+            assert np.max(np.abs(lg - ref_lg[b, hq])) <= 1e-4 * np.max(np.abs(ref_lg[b, hq]))
+            assert np.max(np.abs(out - ref_out[b, hq])) <= 2e-3
