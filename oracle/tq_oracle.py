@@ -20,6 +20,9 @@ Sources (web pages; cited by title and section):
     head dimension and bit width; the query is rotated once and attention dot
     products are taken straight from the stored indices.
   - "基准测试与实际性能表现": top-k inner-product search on d=200 vectors.
+* [AGENT] "6倍KV缓存压缩零精度损失：谷歌TurboQuant技术如何提升智能体运行效率",
+  section "三、工程实现" item 1: the method comes as a compress / decompress
+  pair (no formula given for the decompress side).
 * [VLLM] "A First Comprehensive Study of TurboQuant: Accuracy and Performance"
   (papercache.org summary), section A3: variant names k8v4, 4bit_nc,
   k3v4_nc, 3bit_nc ("nc" = norm correction; not defined further).
@@ -57,6 +60,9 @@ Readings where the pages are silent (each is listed in the design notes):
     block, the bit of (coordinate i, token t) is given by tile32_position:
     64 records of 8 tokens x ceil(d/16) coordinates, so that one GPU lane
     reads the codes of its 8 tokens for 8 coordinates as one contiguous run.
+* R13 dequantize: both stages inverted in the original domain,
+  x_hat = Pi^T (scale c[idx]) + rnorm sqrt(pi/2)/m Pi^T S^T (2 sigma - 1), so
+  that <q, x_hat> is the R7 estimate for every q.
 """
 from __future__ import annotations
 
@@ -311,8 +317,9 @@ def quantize(cb: Codebook, x):
 
 
 def dequantize(cb: Codebook, idx, scale, sign=None, rnorm=None):
-    """x_hat in the original domain: scale * Pi^T c[idx], plus (when signs are
-    given) the QJL term rnorm * sqrt(pi/2)/m * Pi^T S^T (2 sigma - 1)."""
+    """x_hat in the original domain (R13; [AGENT] 三、工程实现 item 1, [WIT]
+    第一阶段 and 第二阶段): scale * Pi^T c[idx], plus (when signs are given)
+    the QJL term rnorm * sqrt(pi/2)/m * Pi^T S^T (2 sigma - 1)."""
     yh = cb.centroids[np.asarray(idx)] * np.asarray(scale, dtype=np.float64)[:, None]
     if sign is not None and cb.m > 0:
         pm = 2.0 * np.asarray(sign, dtype=np.float64) - 1.0

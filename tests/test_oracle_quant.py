@@ -215,3 +215,27 @@ def test_tile32_layout_and_roundtrip():
         for t in range(6, 32):
             for i in range(d):
                 assert (w2 >> O.tile32_position(i, t, b, d)) & ((1 << b) - 1) == 0
+
+
+def test_dequantize_sketch_term_is_unbiased_over_sketches():
+    # Averaged over independent Gaussian sketches S, the residual term of the
+    # reconstruction returns the residual itself (E[g sign(g.r)] = sqrt(2/pi)
+    # r/|r| per row), so the mean of x_hat over sketch seeds converges to x at
+    # rate ~ sqrt(d (pi/2) D / (m n)); without the term it stays at the MSE
+    # error sqrt(D).  A flipped sign leaves ~2 sqrt(D), the constant
+    # sqrt(2/pi) in place of sqrt(pi/2) ~0.36 sqrt(D), S in place of S^T
+    # fails on the shapes (m != d).
+    d, m, bits, n = 32, 48, 2, 400
+    x = np.random.default_rng(11).standard_normal((4, d)) * 2.0
+    acc = np.zeros_like(x)
+    for s in range(n):
+        cb = O.Codebook(d, bits, qjl_m=m, qjl_seed=1000 + s)
+        q = O.quantize(cb, x)
+        acc += O.dequantize(cb, q["idx"], q["scale"], q["sign"], q["rnorm"])
+    rel = np.linalg.norm(acc / n - x, axis=1) / np.linalg.norm(x, axis=1)
+    xh0 = O.dequantize(cb, q["idx"], q["scale"])
+    rel0 = np.linalg.norm(xh0 - x, axis=1) / np.linalg.norm(x, axis=1)
+    D = O.mse_closed_form(d, cb.centroids, cb.boundaries)
+    expect = math.sqrt(d * (math.pi / 2) * D / (m * n))
+    assert np.all(rel < 4 * expect), (rel, expect)
+    assert np.all(rel0 > 0.5 * math.sqrt(D)), (rel0, D)
