@@ -73,6 +73,7 @@ def parse():
     ap.add_argument("--no-sweep", action="store_true", help="skip the bit-width sweep leg")
     ap.add_argument("--no-search", action="store_true", help="skip the vector-search leg")
     ap.add_argument("--no-ab", action="store_true", help="skip the dequantize-then-attend leg")
+    ap.add_argument("--no-paged", action="store_true", help="skip the paged-cache leg")
     ap.add_argument("--calib-copy", action="store_true",
                     help="accepted for profiling commands; the 1 GiB copy always runs")
     return ap.parse_args()
@@ -263,6 +264,58 @@ def dequant_attend_leg(torch, tq, W, iters, warm, copy_gbps):
                 speedup_vs_dequant_first=round((deq_ms + att_ms) / dir_ms, 2),
                 max_rel_diff_of_outputs=round(err, 5), dense_logits=lg_dtype,
                 bf16_kv_bytes=int(kv_bytes))
+
+
+def paged_leg(torch, tq, W, iters, warm, page_tokens=64):
+    """The headline step on a paged cache: the 128K layer's K and V codes in
+    pools of page_tokens-position pages placed by a shuffled block table
+    (every sequence's pages scattered over the pool), the step's append
+    through tq_quantize_kv_paged and the decode through tq_attn_decode_paged.
+    Timed like the headline; the split kernel's time is compared with the
+    contiguous one."""
+    B, Hq, Hkv, d, N, tau = W["B"], W["Hq"], W["Hkv"], W["d"], W["N"], W["tau"]
+    n_lp = (N + page_tokens - 1) // page_tokens
+    n_pages = B * n_lp
+    g = torch.Generator(device="cpu")
+    g.manual_seed(12345)
+    table = torch.randperm(n_pages, generator=g).to(torch.int32).view(B, n_lp).contiguous().to("cuda")
+    kp = tq.Codes(W["kcb"], Hkv, n_pages * page_tokens, tq.TQ_LAYOUT_ROW)
+    vp = tq.Codes(W["vcb"], Hkv, n_pages * page_tokens, tq.TQ_LAYOUT_TILE32)
+    kf, vf = W["k"].view(B * Hkv, N, d), W["v"].view(B * Hkv, N, d)
+    tq.tq_quantize_kv_paged(W["kcb"], W["vcb"], kf, vf, kp, vp, table, page_tokens)   # cache build, untimed
+    k_new = W["k"][:, :, N - 1:N].reshape(B * Hkv, 1, d).contiguous()
+    v_new = W["v"][:, :, N - 1:N].reshape(B * Hkv, 1, d).contiguous()
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+    ws = torch.empty(tq.tq_attn_decode_paged_workspace(B, Hq, Hkv, N, d, page_tokens), dtype=torch.uint8,
+                     device="cuda")
+
+    def step():
+        tq.tq_quantize_kv_paged(W["kcb"], W["vcb"], k_new, v_new, kp, vp, table, page_tokens, tok_offset=N - 1)
+        tq.tq_attn_decode_paged(W["kcb"], W["vcb"], W["q"], kp, vp, table, page_tokens, N, tau, out=out,
+                                workspace=ws)
+    for _ in range(warm):
+        step()
+    torch.cuda.synchronize()
+    tq.tq_profile_enable(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    tq.tq_profile_enable(False)
+    ms = e0.elapsed_time(e1) / iters
+    sms, sn = tq.tq_profile_read(tq.TQ_KERNEL_DECODE_SPLIT)
+    split_ms = sms / max(1, sn)
+    diff = float((out - W["out"]).abs().max() / W["out"].abs().max())
+    del kp, vp, ws
+    alg = W["bytes_per_token_head"] * B * Hkv * N
+    return dict(workload=f"decode-128k GQA layer on a paged cache: {page_tokens}-position pages, "
+                         f"{n_pages} pages per KV head placed by a shuffled block table",
+                KV_tokens_per_s=round(B * N / (ms * 1e-3), 1), ms_per_step=round(ms, 5),
+                split_kernel_ms=round(split_ms, 5), split_GBps=round(alg / (split_ms * 1e-3) / 1e9, 1),
+                frac_hbm=round(alg / (split_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                max_rel_diff_vs_contiguous=round(diff, 7))
 
 
 def _exact_attention_np(q, k, v, tau):
@@ -512,6 +565,9 @@ def main():
             "algorithmic_bytes_per_launch": int(alg_bytes),
         },
     }
+    if not args.no_paged:
+        print("[bench] paged-cache leg", file=sys.stderr, flush=True)
+        res["paged"] = paged_leg(torch, tq, W, iters=max(5, args.steps // 2), warm=max(1, args.warmup // 2))
     if not args.no_quantize:
         print("[bench] quantize leg", file=sys.stderr, flush=True)
         res["quantize"] = quantize_leg(torch, tq, synth, dev, iters=max(5, args.steps // 2),

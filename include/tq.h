@@ -186,6 +186,47 @@ tq_status tq_attn_decode(const tq_codebook* kcb, const tq_codebook* vcb, const v
                          float sm_scale, float* out, float* logits, void* workspace,
                          size_t ws_bytes, void* stream);
 
+/* ---- Paged pools.  A serving engine keeps its cache in fixed-size pages
+ * (the pages present TurboQuant as a KV-cache dtype of such an engine,
+ * [VLLM] A3 方法细节, quantized at every cache update, [WIT] 如何实现
+ * item 1).  A pool is a tq_codes whose sequence h (0 <= h < Hkv) is the
+ * plane of KV head h; its seq_stride is n_pages * page_tokens and page p of
+ * head h holds plane positions [p * page_tokens, (p + 1) * page_tokens).
+ *  block_table  device int32 [B][max_pages]: logical page i (positions
+ *               [i * page_tokens, (i + 1) * page_tokens)) of batch b is
+ *               pool page block_table[b * max_pages + i], the same page id
+ *               for every KV head.  Entries outside [0, n_pages) are clamped
+ *               (the result is then wrong, but no access leaves the pool).
+ *  page_tokens  a power of two in 32..65536; pools' seq_stride a multiple.
+ * The pool buffers must hold Hkv planes (Hkv * seq_stride positions). */
+
+/* tq_quantize_kv into paged pools: inputs k, v [B*Hkv][n_tok][d] (sequence
+ * b*Hkv + h), vector t of sequence (b, h) goes to logical position
+ * tok_offset + t of batch b, KV head h, i.e. through block_table into plane
+ * h of k_pool / v_pool.  max_pages * page_tokens >= tok_offset + n_tok.
+ * Otherwise as tq_quantize_kv (same kernels, same codes). */
+tq_status tq_quantize_kv_paged(const tq_codebook* kcb, const tq_codebook* vcb, const void* k,
+                               const void* v, tq_dtype dt, int64_t B, int64_t Hkv, int64_t n_tok,
+                               int64_t tok_offset, const int32_t* block_table, int64_t max_pages,
+                               int32_t page_tokens, const tq_codes* k_pool, const tq_codes* v_pool,
+                               void* stream);
+
+/* Workspace bytes tq_attn_decode_paged needs for this shape (host only). */
+tq_status tq_attn_decode_paged_workspace(int64_t B, int64_t Hq, int64_t Hkv, int64_t n_ctx, int32_t d,
+                                         int32_t page_tokens, size_t* bytes);
+
+/* tq_attn_decode over paged pools: the keys and values of batch b, KV head h
+ * at logical positions j < len_b are read through block_table from plane h
+ * of k_pool (TQ_LAYOUT_ROW) and v_pool (TQ_LAYOUT_TILE32).
+ * max_pages * page_tokens >= n_ctx; workspace >= tq_attn_decode_paged_workspace.
+ * Same results as tq_attn_decode on the same codes laid out contiguously, up
+ * to the order of the split-K partial sums (each wave covers whole pages). */
+tq_status tq_attn_decode_paged(const tq_codebook* kcb, const tq_codebook* vcb, const void* q,
+                               tq_dtype qdt, int64_t B, int64_t Hq, int64_t Hkv, const tq_codes* k_pool,
+                               const tq_codes* v_pool, const int32_t* block_table, int64_t max_pages,
+                               int32_t page_tokens, const int32_t* seq_lens, int64_t n_ctx, float sm_scale,
+                               float* out, float* logits, void* workspace, size_t ws_bytes, void* stream);
+
 /* Workspace bytes tq_ip_topk needs (host only); valid for any qjl_m of a
  * codebook with this d. */
 tq_status tq_ip_topk_workspace(int64_t nq, int64_t n_db, int32_t k, int32_t d, size_t* bytes);

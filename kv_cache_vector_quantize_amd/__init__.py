@@ -1,5 +1,6 @@
 """MI355X (gfx950) online KV-vector quantization, decode attention from
-packed codes, inner-product top-k over codes and dequantization.  The compute runs in libtq.so (hand-written HIP kernels behind
+packed codes (contiguous or paged caches), inner-product top-k over codes and
+dequantization.  The compute runs in libtq.so (hand-written HIP kernels behind
 a C ABI, declared in include/tq.h); this package is a thin ctypes binding."""
 from ._lib import (  # noqa: F401
     EXPORTS,
@@ -18,6 +19,8 @@ from ._lib import (  # noqa: F401
     TQError,
     lib,
     tq_attn_decode,
+    tq_attn_decode_paged,
+    tq_attn_decode_paged_workspace,
     tq_attn_decode_workspace,
     tq_codebook_values,
     tq_dequantize,
@@ -26,4 +29,5 @@ from ._lib import (  # noqa: F401
     tq_profile_enable,
     tq_profile_read,
     tq_quantize_kv,
+    tq_quantize_kv_paged,
 )

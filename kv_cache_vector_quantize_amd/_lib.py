@@ -23,7 +23,8 @@ TQ_LAYOUT_ROW, TQ_LAYOUT_TILE32 = 0, 1
 EXPORTS = (
     "tq_codebook_build", "tq_codebook_destroy", "tq_codebook_export", "tq_codebook_values",
     "tq_code_row_bytes", "tq_quantize_kv", "tq_attn_decode_workspace", "tq_attn_decode",
-    "tq_ip_topk_workspace", "tq_ip_topk", "tq_dequantize", "tq_profile_enable", "tq_profile_read",
+    "tq_ip_topk_workspace", "tq_ip_topk", "tq_dequantize", "tq_quantize_kv_paged",
+    "tq_attn_decode_paged_workspace", "tq_attn_decode_paged", "tq_profile_enable", "tq_profile_read",
     "tq_last_error",
 )
 TQ_KERNEL_QUANTIZE, TQ_KERNEL_DECODE_SPLIT, TQ_KERNEL_TOPK, TQ_KERNEL_DEQUANTIZE = 0, 1, 2, 3
@@ -78,6 +79,12 @@ def lib() -> ctypes.CDLL:
     L.tq_ip_topk.argtypes = [vp, vp, i64, ctypes.POINTER(tq_codes), i64, i32, vp, vp, vp,
                              ctypes.c_size_t, vp]
     L.tq_dequantize.argtypes = [vp, ctypes.POINTER(tq_codes), i64, i64, i64, vp, i32, vp]
+    L.tq_quantize_kv_paged.argtypes = [vp, vp, vp, vp, i32, i64, i64, i64, i64, vp, i64, i32,
+                                       ctypes.POINTER(tq_codes), ctypes.POINTER(tq_codes), vp]
+    L.tq_attn_decode_paged_workspace.argtypes = [i64, i64, i64, i64, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
+    L.tq_attn_decode_paged.argtypes = [vp, vp, vp, i32, i64, i64, i64, ctypes.POINTER(tq_codes),
+                                       ctypes.POINTER(tq_codes), vp, i64, i32, vp, i64, ctypes.c_float,
+                                       vp, vp, vp, ctypes.c_size_t, vp]
     L.tq_profile_enable.argtypes = [i32]
     L.tq_profile_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
     for name in EXPORTS:
@@ -271,6 +278,68 @@ def tq_attn_decode(kcb, vcb, q, k_codes: Codes, v_codes: Codes, n_ctx: int, sm_s
         kcb.handle, vcb.handle, q.data_ptr(), _dtype_code(q), B, Hq, Hkv, ctypes.byref(kd),
         ctypes.byref(vd), seq_lens.data_ptr() if seq_lens is not None else None, int(n_ctx),
         float(sm_scale), out.data_ptr(), logits.data_ptr() if logits is not None else None,
+        workspace.data_ptr(), workspace.numel(), _stream_handle(stream)))
+    return out
+
+
+def _table(block_table):
+    import torch
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or not block_table.is_contiguous():
+        raise ValueError("block_table must be a contiguous int32 [B, max_pages] tensor")
+    return block_table
+
+
+def tq_quantize_kv_paged(kcb, vcb, k, v, k_pool: Codes | None, v_pool: Codes | None, block_table,
+                         page_tokens: int, tok_offset: int = 0, stream=None):
+    """k, v: [B*Hkv, n_tok, d] (sequence b*Hkv + h) or None; the pools hold
+    Hkv planes (n_seq = Hkv); block_table: int32 [B, max_pages]."""
+    ref = k if k is not None else v
+    pool = k_pool if k is not None else v_pool
+    bt = _table(block_table)
+    B, Hkv = bt.shape[0], pool.n_seq
+    if ref.shape[0] != B * Hkv:
+        raise ValueError("inputs must have B * Hkv rows (B from block_table, Hkv from the pool)")
+    for t in (k, v):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("inputs must be contiguous")
+    kd = k_pool.descriptor() if k_pool is not None else None
+    vd = v_pool.descriptor() if v_pool is not None else None
+    _check(lib().tq_quantize_kv_paged(
+        kcb.handle if kcb is not None else None, vcb.handle if vcb is not None else None,
+        k.data_ptr() if k is not None else None, v.data_ptr() if v is not None else None,
+        _dtype_code(ref), int(B), int(Hkv), int(ref.shape[1]), int(tok_offset), bt.data_ptr(),
+        int(bt.shape[1]), int(page_tokens),
+        ctypes.byref(kd) if kd is not None else None, ctypes.byref(vd) if vd is not None else None,
+        _stream_handle(stream)))
+
+
+def tq_attn_decode_paged_workspace(B, Hq, Hkv, n_ctx, d, page_tokens) -> int:
+    out = ctypes.c_size_t()
+    _check(lib().tq_attn_decode_paged_workspace(int(B), int(Hq), int(Hkv), int(n_ctx), int(d),
+                                                int(page_tokens), ctypes.byref(out)))
+    return out.value
+
+
+def tq_attn_decode_paged(kcb, vcb, q, k_pool: Codes, v_pool: Codes, block_table, page_tokens: int,
+                         n_ctx: int, sm_scale: float, seq_lens=None, out=None, logits=None,
+                         workspace=None, stream=None):
+    """q: [B, Hq, d]; the pools hold Hkv planes; block_table int32 [B, max_pages].
+    Returns out (fp32 [B, Hq, d])."""
+    import torch
+    B, Hq, d = q.shape
+    Hkv = k_pool.n_seq
+    bt = _table(block_table)
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        ws = tq_attn_decode_paged_workspace(B, Hq, Hkv, n_ctx, d, page_tokens)
+        workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=q.device)
+    kd, vd = k_pool.descriptor(), v_pool.descriptor()
+    _check(lib().tq_attn_decode_paged(
+        kcb.handle, vcb.handle, q.data_ptr(), _dtype_code(q), B, Hq, Hkv, ctypes.byref(kd),
+        ctypes.byref(vd), bt.data_ptr(), int(bt.shape[1]), int(page_tokens),
+        seq_lens.data_ptr() if seq_lens is not None else None, int(n_ctx), float(sm_scale),
+        out.data_ptr(), logits.data_ptr() if logits is not None else None,
         workspace.data_ptr(), workspace.numel(), _stream_handle(stream)))
     return out
 

@@ -242,6 +242,12 @@ struct SArgs {
   float* part_o;     // [rows][n_wg][8][D]
   float* part_ml;    // [rows][n_wg][8][2]
   float* logits;     // [B][Hq][n_ctx] or null
+  // paged pools (k_split<..., true>): plane h holds KV head h; logical page
+  // i of batch b is page table[b * max_pages + i] (clamped to [0, n_pages))
+  // of 2^psh positions
+  const int32_t* table;
+  int64_t max_pages, n_pages;
+  int psh;
 };
 
 // Bits [off, off + w) of a little-endian multi-word field (w <= 16).
@@ -336,7 +342,7 @@ struct Tile {
   float ks, kr, vs;     // per-token scalars of token (lane % 32), staged through LDS
 };
 
-template <int BK, int BV, bool QJL>
+template <int BK, int BV, bool QJL, bool PG>
 __global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) k_split(SArgs a) {
   using L = SplitLds<BK, BV>;
   constexpr int NT = 64 * kWaves;
@@ -365,13 +371,23 @@ __global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_e
   const int qg = row % a.qgroups;
   const int bh = row / a.qgroups;
   const int b = bh / a.Hkv, h = bh % a.Hkv;
-  const int64_t seq = bh;                                   // b * Hkv + h
+  const int64_t seq = PG ? h : bh;                          // code plane: b * Hkv + h, or pool plane h
   int64_t n_valid = a.n_ctx;
   if (a.seq_lens) n_valid = a.seq_lens[b];
   const int64_t t_begin = (int64_t)part * a.chunk;
   int64_t t_end = t_begin + a.chunk;
   if (t_end > n_valid) t_end = n_valid;
   if (part >= a.n_parts) t_end = t_begin;
+  // paged: lane i holds the page of logical page lp0 + i; a wave's chunk is
+  // whole pages, at most 64 of them
+  const int lp0 = PG ? (int)(t_begin >> a.psh) : 0;
+  int32_t win = 0;
+  if constexpr (PG) {
+    int64_t lp = (int64_t)lp0 + lane;
+    lp = lp < a.max_pages ? lp : a.max_pages - 1;
+    const int32_t pg = a.table[(int64_t)b * a.max_pages + lp];
+    win = pg < 0 ? 0 : (pg >= a.n_pages ? (int32_t)(a.n_pages - 1) : pg);
+  }
 
   // query operands (per row): qa[u] = dims 32*g4 + 4u + (0,1,0,1,2,3,2,3)
   const u32x4* qop = reinterpret_cast<const u32x4*>(a.qop + (int64_t)row * QOP_DWORDS);
@@ -423,7 +439,14 @@ __global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_e
   float* stage = &s_sc[wave][0];
 
   auto load = [&](Tile<BK, BV>& T, const int64_t t0) {
-    const int t = __builtin_amdgcn_readfirstlane((int)t0);
+    int t = __builtin_amdgcn_readfirstlane((int)t0);
+    if constexpr (PG) {
+      // the tile's 32 positions lie in one page: map the logical position
+      int li = (t >> a.psh) - lp0;
+      li = li < 0 ? 0 : (li > 63 ? 63 : li);
+      const int pg = __builtin_amdgcn_readlane(win, li);
+      t = (pg << a.psh) | (t & ((1 << a.psh) - 1));
+    }
     const int kt = t * (int)a.k_pitch;
 #pragma unroll
     for (int i = 0; i < BK; ++i) {
@@ -781,8 +804,13 @@ __global__ void __launch_bounds__(256) k_combine(CArgs a) {
 
 template <int BK, int BV>
 void launch_split_bits(const SArgs& a, bool qjl, dim3 grid, hipStream_t st) {
-  if (qjl) hipLaunchKernelGGL((k_split<BK, BV, true>), grid, dim3(64 * kWaves), 0, st, a);
-  else hipLaunchKernelGGL((k_split<BK, BV, false>), grid, dim3(64 * kWaves), 0, st, a);
+  if (a.table) {
+    if (qjl) hipLaunchKernelGGL((k_split<BK, BV, true, true>), grid, dim3(64 * kWaves), 0, st, a);
+    else hipLaunchKernelGGL((k_split<BK, BV, false, true>), grid, dim3(64 * kWaves), 0, st, a);
+  } else {
+    if (qjl) hipLaunchKernelGGL((k_split<BK, BV, true, false>), grid, dim3(64 * kWaves), 0, st, a);
+    else hipLaunchKernelGGL((k_split<BK, BV, false, false>), grid, dim3(64 * kWaves), 0, st, a);
+  }
 }
 
 template <int BK>
@@ -804,9 +832,10 @@ bool decode_supported(const tq_codebook* kcb, const tq_codebook* vcb) {
          kcb->p.qjl_m <= 128;
 }
 
-DecodePlan plan_decode(int64_t B, int64_t Hq, int64_t Hkv, int64_t n_ctx, int d) {
+DecodePlan plan_decode(int64_t B, int64_t Hq, int64_t Hkv, int64_t n_ctx, int d, int page_tokens) {
   DecodePlan p{};
   p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.n_ctx = n_ctx; p.d = d;
+  p.page_tokens = page_tokens;
   p.g = Hkv > 0 ? (int)(Hq / Hkv) : 0;
   p.qgroups = (p.g + 7) / 8;
   p.rows = B * Hkv * p.qgroups;
@@ -816,6 +845,11 @@ DecodePlan plan_decode(int64_t B, int64_t Hq, int64_t Hkv, int64_t n_ctx, int d)
   int64_t chunk = (n_ctx + parts - 1) / parts;
   chunk = (chunk + 31) / 32 * 32;
   if (chunk < 32) chunk = 32;
+  if (page_tokens > 0) {
+    // whole pages per wave, at most 64 (the page window a wave holds)
+    chunk = (chunk + page_tokens - 1) / page_tokens * page_tokens;
+    if (chunk > 64LL * page_tokens) chunk = 64LL * page_tokens;
+  }
   p.chunk = (int)chunk;
   p.n_parts = n_ctx > 0 ? (int)((n_ctx + chunk - 1) / chunk) : 0;
   p.n_wg = (p.n_parts + kWaves - 1) / kWaves;
@@ -831,7 +865,7 @@ DecodePlan plan_decode(int64_t B, int64_t Hq, int64_t Hkv, int64_t n_ctx, int d)
 hipError_t launch_decode(const tq_codebook* kcb, const tq_codebook* vcb, const void* q,
                          tq_dtype qdt, const DecodePlan& plan, const tq_codes& k,
                          const tq_codes& v, const int32_t* seq_lens, float sm_scale,
-                         float* out, float* logits, void* ws, hipStream_t stream) {
+                         float* out, float* logits, void* ws, hipStream_t stream, const PageMap& pm) {
   char* w = static_cast<char*>(ws);
   uint32_t* qop = reinterpret_cast<uint32_t*>(w + plan.off_qop);
   float* part_o = reinterpret_cast<float*>(w + plan.off_part_o);
@@ -879,6 +913,11 @@ hipError_t launch_decode(const tq_codebook* kcb, const tq_codebook* vcb, const v
     sa.part_o = part_o;
     sa.part_ml = part_ml;
     sa.logits = logits;
+    sa.table = pm.table;
+    sa.max_pages = pm.max_pages;
+    sa.n_pages = pm.n_pages;
+    sa.psh = 5 + pm.ppb_shift;
+    if (pm.table && plan.page_tokens != (32 << pm.ppb_shift)) return hipErrorInvalidValue;
     const dim3 grid((unsigned)plan.n_wg, (unsigned)plan.rows);
     const bool qjl = kcb->p.qjl_m > 0;
     ProfileScope prof(TQ_KERNEL_DECODE_SPLIT, stream);

@@ -35,6 +35,7 @@ struct QArgs {
   float* scale;
   float* rnorm;
   int64_t idx_pitch, sign_pitch, seq_stride;
+  PageMap pm;         // where a sequence's blocks are written (identity unless paged)
 };
 
 template <int DT>
@@ -106,7 +107,9 @@ __global__ void __launch_bounds__(WIDE ? 256 : 512) k_quantize(QArgs a) {
     const int64_t seq = tile / a.tiles_per_seq;
     const int64_t blk = a.first_block + tile % a.tiles_per_seq;
     const int64_t abs0 = blk * TILE;
-    const int64_t pos0 = seq * a.seq_stride + abs0;      // code row of tile row 0
+    int64_t oseq, oblk;                                   // output plane and block
+    page_block(a.pm, seq, blk, oseq, oblk);
+    const int64_t pos0 = oseq * a.seq_stride + oblk * TILE;   // code row of tile row 0
     const int64_t src0 = seq * a.n_tok + (abs0 - a.tok_off);  // input row of tile row 0
 
     // (a) load X (fp32) -- rows outside [tok_off, tok_off + n_tok) are zero
@@ -282,7 +285,7 @@ __global__ void __launch_bounds__(WIDE ? 256 : 512) k_quantize(QArgs a) {
       const int ndb = (a.d + 15) / 16;
       const int words = 16 * ndb * b;                 // 64*ndb*b bytes
       uint32_t* dst = reinterpret_cast<uint32_t*>(a.idx) +
-                      (seq * (a.seq_stride / TILE) + blk) * (int64_t)words;
+                      (oseq * (a.seq_stride / TILE) + oblk) * (int64_t)words;
       for (int w = tid; w < words; w += nthr) {
         const int bit0 = 32 * w;
         const int q0 = bit0 / b;
@@ -335,6 +338,7 @@ struct SmallJob {
   float* scale;
   float* rnorm;
   int64_t idx_pitch, sign_pitch, seq_stride;
+  PageMap pm;
 };
 
 struct SmallArgs {
@@ -368,7 +372,9 @@ __global__ void __launch_bounds__(4 * NI) k_quantize_small(SmallArgs sa) {
   const int64_t vec = blockIdx.x;                 // seq * n_tok + t
   const int64_t seq = vec / a.n_tok, t = vec % a.n_tok;
   const int64_t pos = a.tok_off + t;              // position in the sequence
-  const int64_t row = seq * a.seq_stride + pos;
+  int64_t oseq, oblk;                             // output plane and block of the position
+  page_block(a.pm, seq, pos >> 5, oseq, oblk);
+  const int64_t row = oseq * a.seq_stride + oblk * 32 + (pos & 31);
   const int tid = threadIdx.x;
   const int i = tid & (NI - 1), kq = tid / NI, l = tid & 63, w = tid >> 6;
   const int L = 1 << a.bits;
@@ -487,7 +493,7 @@ __global__ void __launch_bounds__(4 * NI) k_quantize_small(SmallArgs sa) {
   } else {
     const int ndb = (a.d + 15) / 16;
     const int words = 16 * ndb * b;
-    uint32_t* dst = reinterpret_cast<uint32_t*>(a.idx) + (seq * (a.seq_stride / 32) + pos / 32) * (int64_t)words;
+    uint32_t* dst = reinterpret_cast<uint32_t*>(a.idx) + (oseq * (a.seq_stride / 32) + oblk) * (int64_t)words;
     const int tt = (int)(pos & 31);
     const int G = (tt & 15) >> 2, e = (tt & 3) + 4 * (tt >> 4);
     if (tid < a.d) {
@@ -531,6 +537,7 @@ static SmallJob make_small_job(const tq_codebook* cb, const QuantJob& job) {
   s.scale = job.out.scale; s.rnorm = job.out.rnorm;
   s.idx_pitch = job.out.idx_row_bytes; s.sign_pitch = job.out.sign_row_bytes;
   s.seq_stride = job.out.seq_stride;
+  s.pm = job.pm;
   return s;
 }
 
@@ -589,6 +596,7 @@ hipError_t launch_quantize(const tq_codebook* cb, const QuantJob& job, hipStream
   a.idx_pitch = job.out.idx_row_bytes;
   a.sign_pitch = job.out.sign_row_bytes;
   a.seq_stride = job.out.seq_stride;
+  a.pm = job.pm;
   ProfileScope prof(TQ_KERNEL_QUANTIZE, stream);
   if (cb->dp <= 128 && (cb->p.qjl_m == 0 || cb->mp <= 128)) {
     const int waves_needed = cb->dp / 32 + (cb->p.qjl_m > 0 ? cb->mp / 32 : 0);

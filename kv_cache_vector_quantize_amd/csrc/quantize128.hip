@@ -59,6 +59,7 @@ struct Q128Args {
   uint8_t* idx;
   float* scale;
   int64_t idx_pitch, seq_stride;
+  PageMap pm;          // where a sequence's blocks are written (identity unless paged)
 };
 
 __device__ inline f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -166,7 +167,9 @@ __global__ void __launch_bounds__(256) k_q128(Q128Args a) {
     int64_t blk;
     where(tile, seq, blk);
     const int64_t abs0 = blk * TILE;
-    const int64_t pos0 = (int64_t)seq * a.seq_stride + abs0;   // code row of tile row 0
+    int64_t oseq, oblk;                                         // output plane and block
+    page_block(a.pm, seq, blk, oseq, oblk);
+    const int64_t pos0 = oseq * a.seq_stride + oblk * TILE;     // code row of tile row 0
     const bool full = abs0 >= a.tok_off && abs0 + TILE <= a.tok_off + a.n_tok;
 
     // (a) stage this thread's share; |x| in fp32 from the input values,
@@ -387,7 +390,7 @@ __global__ void __launch_bounds__(256) k_q128(Q128Args a) {
     if constexpr (T32) {
       // (f) the assembled tile32 block: 512*b bytes = 128*b words
       const int words = 128 * b;
-      uint32_t* dst = reinterpret_cast<uint32_t*>(a.idx) + ((int64_t)seq * (a.seq_stride / TILE) + blk) * (int64_t)words;
+      uint32_t* dst = reinterpret_cast<uint32_t*>(a.idx) + (oseq * (a.seq_stride / TILE) + oblk) * (int64_t)words;
       for (int w = tid; w < words; w += 256) {
         if (full) {
           dst[w] = tb[0][w];
@@ -465,6 +468,7 @@ hipError_t launch_quantize128(const tq_codebook* cb, const QuantJob& job, hipStr
   a.scale = job.out.scale;
   a.idx_pitch = job.out.idx_row_bytes;
   a.seq_stride = job.out.seq_stride;
+  a.pm = job.pm;
   const bool t32 = job.out.layout == TQ_LAYOUT_TILE32;
   ProfileScope prof(TQ_KERNEL_QUANTIZE, stream);
   switch (job.dt) {

@@ -431,6 +431,85 @@ tq_status tq_code_row_bytes(const tq_codebook* cb, int64_t* idx_row_bytes,
   return TQ_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Validation and dispatch shared by tq_quantize_kv and tq_quantize_kv_paged:
+// code planes must hold need_len positions; pm maps a sequence's blocks to
+// its output plane and blocks.
+tq_status quantize_impl(const tq_codebook* kcb, const tq_codebook* vcb, const void* k, const void* v,
+                        tq_dtype dt, int64_t n_seq, int64_t n_tok, int64_t tok_offset,
+                        const tq_codes* k_out, const tq_codes* v_out, void* stream, int64_t need_len,
+                        const PageMap& pm) {
+  const void* xs[2] = {k, v};
+  const tq_codebook* cbs[2] = {kcb, vcb};
+  const tq_codes* outs[2] = {k_out, v_out};
+  const char* names[2] = {"k", "v"};
+  for (int t = 0; t < 2; ++t) {
+    if (!xs[t]) continue;
+    if (!cbs[t]) return fail(TQ_ERR_INVALID, std::string(names[t]) + ": codebook is NULL");
+    tq_status s = check_codes(cbs[t], outs[t], need_len, names[t], false);
+    if (s != TQ_OK) return s;
+    if (!quantize_supported(cbs[t]))
+      return fail(TQ_ERR_UNSUPPORTED, std::string(names[t]) + ": quantize supports d <= 256 and qjl_m <= 256");
+    s = current_device_matches(cbs[t]);
+    if (s != TQ_OK) return s;
+  }
+  if (n_tok <= kSmallMaxTok && n_seq * n_tok <= 0x7FFFFFFF) {
+    const tq_codebook* sc[2];
+    QuantJob sj[2];
+    int nj = 0;
+    for (int t = 0; t < 2; ++t) {
+      if (!xs[t]) continue;
+      sc[nj] = cbs[t];
+      sj[nj++] = QuantJob{xs[t], dt, n_seq, n_tok, tok_offset, *outs[t], pm};
+    }
+    hipError_t e = launch_quantize_small(sc, sj, nj, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "quantize launch");
+    return TQ_OK;
+  }
+  for (int t = 0; t < 2; ++t) {
+    if (!xs[t]) continue;
+    QuantJob job{xs[t], dt, n_seq, n_tok, tok_offset, *outs[t], pm};
+    hipError_t e = launch_quantize(cbs[t], job, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "quantize launch");
+  }
+  return TQ_OK;
+}
+
+// Page size and table of a paged call; n_pages comes from the pool planes.
+tq_status check_pages(int32_t page_tokens, const int32_t* block_table, int64_t max_pages, int64_t n_logical,
+                      const tq_codes* k_pool, const tq_codes* v_pool, PageMap& pm, int64_t hkv) {
+  if (page_tokens < 32 || page_tokens > 65536 || (page_tokens & (page_tokens - 1)))
+    return fail(TQ_ERR_INVALID, "page_tokens must be a power of two in 32..65536");
+  if (!block_table) return fail(TQ_ERR_INVALID, "block_table is NULL");
+  if (max_pages < 1 || max_pages * page_tokens < n_logical)
+    return fail(TQ_ERR_INVALID, "max_pages * page_tokens must cover every position of the call");
+  int64_t n_pages = -1;
+  const tq_codes* pools[2] = {k_pool, v_pool};
+  for (const tq_codes* c : pools) {
+    if (!c) continue;
+    if (c->seq_stride < page_tokens || c->seq_stride % page_tokens)
+      return fail(TQ_ERR_INVALID, "a pool's seq_stride must be a positive multiple of page_tokens");
+    const int64_t np = c->seq_stride / page_tokens;
+    n_pages = n_pages < 0 ? np : (np < n_pages ? np : n_pages);
+  }
+  if (n_pages > 0x7FFFFFFFLL) return fail(TQ_ERR_UNSUPPORTED, "at most 2^31 - 1 pages per pool");
+  pm.table = block_table;
+  pm.max_pages = max_pages;
+  pm.n_pages = n_pages < 1 ? 1 : n_pages;
+  pm.hkv = hkv;
+  int sh = 0;
+  while ((32 << sh) < page_tokens) ++sh;
+  pm.ppb_shift = sh;
+  return TQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 tq_status tq_quantize_kv(const tq_codebook* kcb, const tq_codebook* vcb, const void* k,
                          const void* v, tq_dtype dt, int64_t n_seq, int64_t n_tok,
                          int64_t tok_offset, const tq_codes* k_out, const tq_codes* v_out,
@@ -441,42 +520,31 @@ tq_status tq_quantize_kv(const tq_codebook* kcb, const tq_codebook* vcb, const v
       return fail(TQ_ERR_INVALID, "n_seq, n_tok and tok_offset must be >= 0");
     if (n_seq == 0 || n_tok == 0) return TQ_OK;   // nothing is read or written
     if (!k && !v) return fail(TQ_ERR_INVALID, "k and v are both NULL");
-    const void* xs[2] = {k, v};
-    const tq_codebook* cbs[2] = {kcb, vcb};
-    const tq_codes* outs[2] = {k_out, v_out};
-    const char* names[2] = {"k", "v"};
-    for (int t = 0; t < 2; ++t) {
-      if (!xs[t]) continue;
-      if (!cbs[t]) return fail(TQ_ERR_INVALID, std::string(names[t]) + ": codebook is NULL");
-      tq_status s = check_codes(cbs[t], outs[t], tok_offset + n_tok, names[t], false);
-      if (s != TQ_OK) return s;
-      if (!quantize_supported(cbs[t]))
-        return fail(TQ_ERR_UNSUPPORTED, std::string(names[t]) + ": quantize supports d <= 256 and qjl_m <= 256");
-      s = current_device_matches(cbs[t]);
-      if (s != TQ_OK) return s;
-    }
-    if (n_tok <= kSmallMaxTok && n_seq * n_tok <= 0x7FFFFFFF) {
-      const tq_codebook* sc[2];
-      QuantJob sj[2];
-      int nj = 0;
-      for (int t = 0; t < 2; ++t) {
-        if (!xs[t]) continue;
-        sc[nj] = cbs[t];
-        sj[nj++] = QuantJob{xs[t], dt, n_seq, n_tok, tok_offset, *outs[t]};
-      }
-      hipError_t e = launch_quantize_small(sc, sj, nj, static_cast<hipStream_t>(stream));
-      if (e != hipSuccess) return hip_fail(e, "quantize launch");
-      return TQ_OK;
-    }
-    for (int t = 0; t < 2; ++t) {
-      if (!xs[t]) continue;
-      QuantJob job{xs[t], dt, n_seq, n_tok, tok_offset, *outs[t]};
-      hipError_t e = launch_quantize(cbs[t], job, static_cast<hipStream_t>(stream));
-      if (e != hipSuccess) return hip_fail(e, "quantize launch");
-    }
-    return TQ_OK;
+    return quantize_impl(kcb, vcb, k, v, dt, n_seq, n_tok, tok_offset, k_out, v_out, stream,
+                         tok_offset + n_tok, PageMap{});
   } catch (...) {
     return fail(TQ_ERR_ALLOC, "tq_quantize_kv: unexpected exception");
+  }
+}
+
+tq_status tq_quantize_kv_paged(const tq_codebook* kcb, const tq_codebook* vcb, const void* k,
+                               const void* v, tq_dtype dt, int64_t B, int64_t Hkv, int64_t n_tok,
+                               int64_t tok_offset, const int32_t* block_table, int64_t max_pages,
+                               int32_t page_tokens, const tq_codes* k_pool, const tq_codes* v_pool,
+                               void* stream) {
+  try {
+    if (dt != TQ_F32 && dt != TQ_BF16 && dt != TQ_F16) return fail(TQ_ERR_INVALID, "bad dtype");
+    if (B < 0 || Hkv <= 0 || n_tok < 0 || tok_offset < 0)
+      return fail(TQ_ERR_INVALID, "need B, n_tok, tok_offset >= 0 and Hkv > 0");
+    if (B == 0 || n_tok == 0) return TQ_OK;
+    if (!k && !v) return fail(TQ_ERR_INVALID, "k and v are both NULL");
+    PageMap pm;
+    tq_status s = check_pages(page_tokens, block_table, max_pages, tok_offset + n_tok, k ? k_pool : nullptr,
+                              v ? v_pool : nullptr, pm, Hkv);
+    if (s != TQ_OK) return s;
+    return quantize_impl(kcb, vcb, k, v, dt, B * Hkv, n_tok, tok_offset, k_pool, v_pool, stream, page_tokens, pm);
+  } catch (...) {
+    return fail(TQ_ERR_ALLOC, "tq_quantize_kv_paged: unexpected exception");
   }
 }
 
@@ -490,53 +558,102 @@ tq_status tq_attn_decode_workspace(int64_t B, int64_t Hq, int64_t Hkv, int64_t n
   return TQ_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Validation and launch shared by tq_attn_decode and tq_attn_decode_paged.
+tq_status decode_impl(const tq_codebook* kcb, const tq_codebook* vcb, const void* q, tq_dtype qdt, int64_t B,
+                      int64_t Hq, int64_t Hkv, const tq_codes* k, const tq_codes* v, const int32_t* seq_lens,
+                      int64_t n_ctx, float sm_scale, float* out, float* logits, void* workspace,
+                      size_t ws_bytes, void* stream, int64_t need_len, int page_tokens, const PageMap& pm) {
+  if (!kcb || !vcb) return fail(TQ_ERR_INVALID, "codebook is NULL");
+  if (qdt != TQ_F32 && qdt != TQ_BF16 && qdt != TQ_F16) return fail(TQ_ERR_INVALID, "bad dtype");
+  if (B < 0 || Hq < 0 || Hkv <= 0 || n_ctx < 0 || Hq % Hkv)
+    return fail(TQ_ERR_INVALID, "need B, n_ctx >= 0, Hkv > 0, Hq a multiple of Hkv");
+  if (kcb->p.d != vcb->p.d) return fail(TQ_ERR_INVALID, "key and value codebooks differ in d");
+  if (!decode_supported(kcb, vcb))
+    return fail(TQ_ERR_UNSUPPORTED,
+                "decode supports d = 128, bits in {2,3,4,8}, qjl_m <= 128");
+  if (!std::isfinite(sm_scale)) return fail(TQ_ERR_INVALID, "sm_scale must be finite");
+  if (B * Hq == 0) return TQ_OK;
+  if (!q || !out) return fail(TQ_ERR_INVALID, "q and out must be non-NULL");
+  if (!k || k->layout != TQ_LAYOUT_ROW) return fail(TQ_ERR_INVALID, "key codes must use the row layout");
+  if (!v || v->layout != TQ_LAYOUT_TILE32)
+    return fail(TQ_ERR_INVALID, "value codes must use the tile32 layout");
+  tq_status s = check_codes(kcb, k, need_len, "k", true);
+  if (s != TQ_OK) return s;
+  s = check_codes(vcb, v, need_len, "v", true);
+  if (s != TQ_OK) return s;
+  if ((s = current_device_matches(kcb)) != TQ_OK) return s;
+  if ((s = current_device_matches(vcb)) != TQ_OK) return s;
+  {
+    // the split kernel addresses one sequence's (or pool plane's) planes
+    // with 32-bit byte offsets
+    const int64_t lim = 0x7FFFFFFFLL;
+    const int64_t vblk = 64LL * ((vcb->p.d + 15) / 16) * vcb->p.bits;
+    if (k->seq_stride * k->idx_row_bytes >= lim || k->seq_stride * k->sign_row_bytes >= lim ||
+        (v->seq_stride / 32) * vblk >= lim || 4 * k->seq_stride >= lim || 4 * v->seq_stride >= lim)
+      return fail(TQ_ERR_UNSUPPORTED, "a sequence's code planes must each stay below 2 GiB");
+  }
+  const DecodePlan plan = plan_decode(B, Hq, Hkv, n_ctx, kcb->p.d, page_tokens);
+  if (plan.rows > 65535 || B * Hq > 0x7FFFFFFF)
+    return fail(TQ_ERR_UNSUPPORTED, "B * Hkv * ceil(g/8) must be <= 65535");
+  if (plan.n_wg > 1024) return fail(TQ_ERR_UNSUPPORTED, "context too long for the split plan");
+  if (!workspace || ws_bytes < plan.bytes)
+    return fail(TQ_ERR_INVALID, "workspace missing or smaller than the workspace query");
+  if (!aligned(workspace, 256)) return fail(TQ_ERR_INVALID, "workspace must be 256-byte aligned");
+  if (!aligned(out, 16)) return fail(TQ_ERR_INVALID, "out must be 16-byte aligned");
+  hipError_t e = launch_decode(kcb, vcb, q, qdt, plan, *k, *v, seq_lens, sm_scale, out,
+                               logits, workspace, static_cast<hipStream_t>(stream), pm);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return TQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 tq_status tq_attn_decode(const tq_codebook* kcb, const tq_codebook* vcb, const void* q,
                          tq_dtype qdt, int64_t B, int64_t Hq, int64_t Hkv, const tq_codes* k,
                          const tq_codes* v, const int32_t* seq_lens, int64_t n_ctx,
                          float sm_scale, float* out, float* logits, void* workspace,
                          size_t ws_bytes, void* stream) {
   try {
-    if (!kcb || !vcb) return fail(TQ_ERR_INVALID, "codebook is NULL");
-    if (qdt != TQ_F32 && qdt != TQ_BF16 && qdt != TQ_F16) return fail(TQ_ERR_INVALID, "bad dtype");
-    if (B < 0 || Hq < 0 || Hkv <= 0 || n_ctx < 0 || Hq % Hkv)
-      return fail(TQ_ERR_INVALID, "need B, n_ctx >= 0, Hkv > 0, Hq a multiple of Hkv");
-    if (kcb->p.d != vcb->p.d) return fail(TQ_ERR_INVALID, "key and value codebooks differ in d");
-    if (!decode_supported(kcb, vcb))
-      return fail(TQ_ERR_UNSUPPORTED,
-                  "decode supports d = 128, bits in {2,3,4,8}, qjl_m <= 128");
-    if (!std::isfinite(sm_scale)) return fail(TQ_ERR_INVALID, "sm_scale must be finite");
-    if (B * Hq == 0) return TQ_OK;
-    if (!q || !out) return fail(TQ_ERR_INVALID, "q and out must be non-NULL");
-    if (!k || k->layout != TQ_LAYOUT_ROW) return fail(TQ_ERR_INVALID, "key codes must use the row layout");
-    if (!v || v->layout != TQ_LAYOUT_TILE32)
-      return fail(TQ_ERR_INVALID, "value codes must use the tile32 layout");
-    tq_status s = check_codes(kcb, k, n_ctx, "k", true);
-    if (s != TQ_OK) return s;
-    s = check_codes(vcb, v, n_ctx, "v", true);
-    if (s != TQ_OK) return s;
-    if ((s = current_device_matches(kcb)) != TQ_OK) return s;
-    if ((s = current_device_matches(vcb)) != TQ_OK) return s;
-    {
-      // the split kernel addresses one sequence's planes with 32-bit byte offsets
-      const int64_t lim = 0x7FFFFFFFLL;
-      const int64_t vblk = 64LL * ((vcb->p.d + 15) / 16) * vcb->p.bits;
-      if (k->seq_stride * k->idx_row_bytes >= lim || k->seq_stride * k->sign_row_bytes >= lim ||
-          (v->seq_stride / 32) * vblk >= lim || 4 * k->seq_stride >= lim || 4 * v->seq_stride >= lim)
-        return fail(TQ_ERR_UNSUPPORTED, "a sequence's code planes must each stay below 2 GiB");
-    }
-    const DecodePlan plan = plan_decode(B, Hq, Hkv, n_ctx, kcb->p.d);
-    if (plan.rows > 65535 || B * Hq > 0x7FFFFFFF)
-      return fail(TQ_ERR_UNSUPPORTED, "B * Hkv * ceil(g/8) must be <= 65535");
-    if (!workspace || ws_bytes < plan.bytes)
-      return fail(TQ_ERR_INVALID, "workspace missing or smaller than tq_attn_decode_workspace()");
-    if (!aligned(workspace, 256)) return fail(TQ_ERR_INVALID, "workspace must be 256-byte aligned");
-    if (!aligned(out, 16)) return fail(TQ_ERR_INVALID, "out must be 16-byte aligned");
-    hipError_t e = launch_decode(kcb, vcb, q, qdt, plan, *k, *v, seq_lens, sm_scale, out,
-                                 logits, workspace, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail(e, "decode launch");
-    return TQ_OK;
+    return decode_impl(kcb, vcb, q, qdt, B, Hq, Hkv, k, v, seq_lens, n_ctx, sm_scale, out, logits,
+                       workspace, ws_bytes, stream, n_ctx, 0, PageMap{});
   } catch (...) {
     return fail(TQ_ERR_ALLOC, "tq_attn_decode: unexpected exception");
+  }
+}
+
+tq_status tq_attn_decode_paged_workspace(int64_t B, int64_t Hq, int64_t Hkv, int64_t n_ctx, int32_t d,
+                                         int32_t page_tokens, size_t* bytes) {
+  if (!bytes) return fail(TQ_ERR_INVALID, "bytes is NULL");
+  if (B < 0 || Hq < 0 || Hkv <= 0 || n_ctx < 0 || Hq % Hkv)
+    return fail(TQ_ERR_INVALID, "need B, n_ctx >= 0, Hkv > 0, Hq a multiple of Hkv");
+  if (page_tokens < 32 || page_tokens > 65536 || (page_tokens & (page_tokens - 1)))
+    return fail(TQ_ERR_INVALID, "page_tokens must be a power of two in 32..65536");
+  if (d != 128) return fail(TQ_ERR_UNSUPPORTED, "decode supports d = 128");
+  *bytes = plan_decode(B, Hq, Hkv, n_ctx, d, page_tokens).bytes;
+  return TQ_OK;
+}
+
+tq_status tq_attn_decode_paged(const tq_codebook* kcb, const tq_codebook* vcb, const void* q,
+                               tq_dtype qdt, int64_t B, int64_t Hq, int64_t Hkv, const tq_codes* k_pool,
+                               const tq_codes* v_pool, const int32_t* block_table, int64_t max_pages,
+                               int32_t page_tokens, const int32_t* seq_lens, int64_t n_ctx, float sm_scale,
+                               float* out, float* logits, void* workspace, size_t ws_bytes, void* stream) {
+  try {
+    if (B < 0 || Hq < 0 || Hkv <= 0 || n_ctx < 0)
+      return fail(TQ_ERR_INVALID, "need B, Hq, n_ctx >= 0 and Hkv > 0");
+    PageMap pm;
+    tq_status s = check_pages(page_tokens, block_table, max_pages, n_ctx, k_pool, v_pool, pm, Hkv);
+    if (s != TQ_OK) return s;
+    return decode_impl(kcb, vcb, q, qdt, B, Hq, Hkv, k_pool, v_pool, seq_lens, n_ctx, sm_scale, out, logits,
+                       workspace, ws_bytes, stream, page_tokens, page_tokens, pm);
+  } catch (...) {
+    return fail(TQ_ERR_ALLOC, "tq_attn_decode_paged: unexpected exception");
   }
 }
 

@@ -94,11 +94,40 @@ struct ProfileScope {
 
 // ---- kernels (launchers return hipSuccess or the launch error)
 
+// Paged code pools.  Sequence s = b * hkv + h of a job lives in pool plane h:
+// its 32-position block blk is block page * ppb + blk % ppb of that plane,
+// page = table[b * max_pages + blk / ppb] clamped to [0, n_pages), with
+// ppb = 2^ppb_shift blocks per page.  table == nullptr: no paging (sequence
+// s is plane s and block blk is block blk).
+struct PageMap {
+  const int32_t* table = nullptr;
+  int64_t max_pages = 0;
+  int64_t n_pages = 0;
+  int64_t hkv = 1;
+  int ppb_shift = 0;
+};
+
+__device__ inline void page_block(const PageMap& pm, int64_t seq, int64_t blk, int64_t& oseq, int64_t& oblk) {
+  if (pm.table == nullptr) {
+    oseq = seq;
+    oblk = blk;
+    return;
+  }
+  const int64_t b = seq / pm.hkv;
+  oseq = seq - b * pm.hkv;
+  int64_t lp = blk >> pm.ppb_shift;
+  lp = lp < pm.max_pages ? lp : pm.max_pages - 1;
+  int64_t pg = pm.table[b * pm.max_pages + lp];
+  pg = pg < 0 ? 0 : (pg >= pm.n_pages ? pm.n_pages - 1 : pg);
+  oblk = (pg << pm.ppb_shift) + (blk & ((1LL << pm.ppb_shift) - 1));
+}
+
 struct QuantJob {
   const void* x;          // [n_seq][n_tok][d]
   tq_dtype dt;
   int64_t n_seq, n_tok, tok_offset;
   tq_codes out;
+  PageMap pm{};
 };
 
 hipError_t launch_quantize(const tq_codebook* cb, const QuantJob& job, hipStream_t stream);
@@ -128,6 +157,7 @@ hipError_t launch_dequantize(const tq_codebook* cb, const DequantJob& job, hipSt
 struct DecodePlan {
   int64_t B, Hq, Hkv, n_ctx;
   int d;
+  int page_tokens;  // 0, or the page size of a paged pool (chunks are whole pages, <= 64 per wave)
   int g;            // Hq / Hkv
   int qgroups;      // ceil(g / 8)
   int64_t rows;     // B * Hkv * qgroups (one row = one KV head and <= 8 query heads)
@@ -137,12 +167,15 @@ struct DecodePlan {
   size_t off_qop, off_part_o, off_part_ml, bytes;
 };
 
-DecodePlan plan_decode(int64_t B, int64_t Hq, int64_t Hkv, int64_t n_ctx, int d);
+DecodePlan plan_decode(int64_t B, int64_t Hq, int64_t Hkv, int64_t n_ctx, int d, int page_tokens = 0);
 
+// pm.table != nullptr: k and v are page pools (plane h = KV head h), read
+// through pm (plan.page_tokens = 32 << pm.ppb_shift)
 hipError_t launch_decode(const tq_codebook* kcb, const tq_codebook* vcb, const void* q,
                          tq_dtype qdt, const DecodePlan& plan, const tq_codes& k,
                          const tq_codes& v, const int32_t* seq_lens, float sm_scale,
-                         float* out, float* logits, void* ws, hipStream_t stream);
+                         float* out, float* logits, void* ws, hipStream_t stream,
+                         const PageMap& pm = PageMap{});
 
 bool decode_supported(const tq_codebook* kcb, const tq_codebook* vcb);
 
