@@ -437,7 +437,10 @@ __global__ void __launch_bounds__(64 * kIp2Waves) k_ip_score2(IS2Args a) {
   auto build = [&](int rb, int ob) {
     const uint32_t* raw = s_raw[rb];
     const char* tab = reinterpret_cast<const char*>(s_tab);
-    for (int t = tid; t < nus * 64; t += 64 * kIp2Waves) {
+#pragma unroll
+    for (int jj = 0; jj < (NUS * 64 + 64 * kIp2Waves - 1) / (64 * kIp2Waves); ++jj) {
+      const int t = tid + 64 * kIp2Waves * jj;
+      if (t >= NUS * 64) break;
       const int u = t >> 6, l = t & 63, r = l & 15, g = l >> 4;
       uint32_t d0, d1, d2, d3;
       if (u < nu) {
@@ -527,6 +530,9 @@ __global__ void __launch_bounds__(64 * kIp2Waves) k_ip_score2(IS2Args a) {
 #pragma unroll
       for (int qb = 0; qb < kIp2Blocks; ++qb) accq[qb] = mfma(av, bq[qb][NU + v], accq[qb]);
     }
+    // unpack tile i + 1 while the MFMAs of tile i run (past the last tile it
+    // rebuilds a buffer nobody reads)
+    build(nxt, nxt);
     float sc[4], rn[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -583,8 +589,7 @@ __global__ void __launch_bounds__(64 * kIp2Waves) k_ip_score2(IS2Args a) {
         if (c16 < 8) thq[qb] = s_ws[li];
       }
     }
-    // (2) unpack tile i + 1; (3) stage tile i + 2, fetch tile i + 3
-    if (i + 1 < nt) build(nxt, nxt);
+    // (3) stage tile i + 2, fetch tile i + 3
     if (i + 2 < nt) {
       raw_store(cur);
       if (i + 3 < nt) raw_load(dbt(i + 3));
