@@ -465,11 +465,7 @@ def cpu_baseline(torch, O, W, budget_s=10.0):
     """float64 oracle: per sampled (batch, KV head) pair, quantize the step's
     new vectors and decode its 8 query heads over the full context; pairs are
     taken in a fixed shuffled order until about budget_s of timed CPU work."""
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
-    except Exception:
-        threads = 1
+    threads = _oracle_threads()
     B, Hkv, Hq, d, N = W["B"], W["Hkv"], W["Hq"], W["d"], W["N"]
     g = Hq // Hkv
     okc = O.Codebook(d, 3, qjl_m=128, rot_seed=1, qjl_seed=2)
@@ -500,6 +496,61 @@ def cpu_baseline(torch, O, W, budget_s=10.0):
                 sample=f"{done} of {B * Hkv} (batch, KV head) pairs of the decode-128k layer at "
                        f"full context {N}, all {g} query heads each, float64; "
                        f"{t_total:.1f} s of CPU time, scaled to KV tokens/s")
+
+
+def _oracle_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([t.get("num_threads", 1) for t in threadpool_info()] or [1]))
+    except Exception:
+        return 1
+
+
+def cpu_oracle_legs(O, synth, budget_s=2.0):
+    """float64 oracle rates beside the secondary legs, each on a bounded
+    sample of the leg's workload (repeated until ~budget_s of CPU time):
+    quantize and dequantize of 32768 quantize-layer vectors (4-bit, d=128,
+    outlier channels x15), and top-k (k=10) of 20 queries against a
+    65536-vector sample of the d=200 search database (4-bit + QJL m=200),
+    scaled to the 1e6-vector database."""
+    threads = _oracle_threads()
+    d = 128
+    chk = synth.outlier_channels(10, 8, d, 4)
+    x = synth.kv_gaussian(1, 8, 4096, d, 10, dtype="bf16", device="cpu", per_head_channels=chk, factor=15.0)
+    x64 = x.float().numpy().astype(np.float64).reshape(-1, d)
+    cb = O.Codebook(d, 4, rot_seed=1)
+
+    def rate(fn):
+        t, n = 0.0, 0
+        while t < budget_s:
+            t0 = time.perf_counter()
+            fn()
+            t += time.perf_counter() - t0
+            n += 1
+        return n, t
+    r = O.quantize(cb, x64)
+    nq_, tq_ = rate(lambda: O.quantize(cb, x64))
+    nd_, td_ = rate(lambda: O.dequantize(cb, r["idx"], r["scale"]))
+    vec_q = nq_ * len(x64) / tq_
+    vec_d = nd_ * len(x64) / td_
+    out = {}
+    out["quantize"] = dict(value=round(vec_q * 324 / 1e9, 4), unit="GB/s", vectors_per_s=round(vec_q, 1),
+                           cores=threads, kind="oracle",
+                           sample=f"{len(x64)} quantize-layer vectors x {nq_} passes, float64, {tq_:.1f} s")
+    out["dequantize"] = dict(value=round(vec_d * 324 / 1e9, 4), unit="GB/s", vectors_per_s=round(vec_d, 1),
+                             cores=threads, kind="oracle",
+                             sample=f"{len(x64)} quantize-layer vectors x {nd_} passes, float64, {td_:.1f} s")
+    cb2 = O.Codebook(200, 4, qjl_m=200, rot_seed=1, qjl_seed=2)
+    n_s, n_q = 65536, 20
+    db = synth.mixture_db(n_s, 200, 256, seed=7).double().numpy()
+    qs = synth.mixture_db(n_q, 200, 256, seed=8).double().numpy()
+    codes = O.quantize(cb2, db)
+    nt_, tt_ = rate(lambda: O.ip_topk(cb2, qs, codes, 10))
+    qps = nt_ * n_q / tt_ * n_s / 1e6
+    out["vector_search"] = dict(value=round(qps, 2), unit="queries/s", cores=threads, kind="oracle",
+                                sample=f"{n_q} queries x {n_s} database vectors x {nt_} passes, float64, "
+                                       f"{tt_:.1f} s, scaled to 1e6 vectors")
+    return out
 
 
 def main():
@@ -603,6 +654,12 @@ def main():
         import oracle as O
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(torch, O, W)
+        legs = cpu_oracle_legs(O, synth)
+        if "quantize" in res:
+            res["quantize"]["cpu_oracle"] = legs["quantize"]
+            res["quantize"]["dequantize"]["cpu_oracle"] = legs["dequantize"]
+        if "vector_search" in res:
+            res["vector_search"]["cpu_oracle"] = legs["vector_search"]
     print(json.dumps(res), flush=True)
 
 
