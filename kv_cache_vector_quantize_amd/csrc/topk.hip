@@ -18,8 +18,9 @@
 //                workgroup into A operands in LDS (centroid operand from the
 //                pair table, sign operand from sign bytes) and feeds all 16
 //                blocks through v_mfma_f32_16x16x32_bf16 (hi/lo query
-//                columns); raw code rows are fetched two tiles ahead and the
-//                next tile is unpacked while the current one is multiplied.
+//                columns).  Tiles go in pairs between barriers: while the
+//                MFMAs of a tile run, the tile two ahead is unpacked, and
+//                raw code rows are fetched four to five tiles ahead.
 //                Each query keeps one unsorted top-k list in LDS with its
 //                worst entry (score, slot): the four lanes that hold the
 //                query's rows insert in row order, a better candidate
@@ -358,9 +359,10 @@ struct IS2Args {
 template <int NU, int NS>
 __global__ void __launch_bounds__(64 * kIp2Waves) k_ip_score2(IS2Args a) {
   constexpr int NUS = NU + NS;
-  __shared__ __align__(16) uint4 s_a[2][NUS][64];          // A operands of a tile
-  __shared__ float s_sr[2][2][16];                         // its scale and 2^64 rnorm
-  __shared__ __align__(16) uint32_t s_raw[2][kIp2Raw];     // raw code rows of a tile
+  // tiles go in pairs between barriers: slots 2c, 2c + 1 of buffer c
+  __shared__ __align__(16) uint4 s_a[4][NUS][64];          // A operands of a tile
+  __shared__ float s_sr[4][2][16];                         // its scale and 2^64 rnorm
+  __shared__ __align__(16) uint32_t s_raw[4][kIp2Raw];     // raw code rows of a tile
   __shared__ __align__(16) uint32_t s_tab[512];
   __shared__ __align__(16) float s_ls[kIp2Lists][kIp2TopK];    // per-query lists (unsorted)
   __shared__ __align__(16) int32_t s_li[kIp2Lists][kIp2TopK];
@@ -412,26 +414,33 @@ __global__ void __launch_bounds__(64 * kIp2Waves) k_ip_score2(IS2Args a) {
   else if (tid < n_sgn + 32) { mbase = reinterpret_cast<const uint32_t*>(a.rnorm); mrow = tid - n_sgn - 16; mw = 0; mstr = 1; }
   else { mbase = nullptr; mrow = 0; mw = 0; mstr = 0; }
   const int last = (int)(a.n_db - 1);
-  uint32_t pre_i[kIp2IdxPer], pre_m = 0u;
-  auto raw_load = [&](int64_t tile) {
-    const int r0 = (int)(tile * 16);
+  struct Pre {
+    uint32_t i[kIp2IdxPer];
+    uint32_t m;
+  };
+  Pre ra, rb;
+  auto raw_load = [&](Pre& P, int64_t tile) {
+    uint32_t (&pre_i)[kIp2IdxPer] = P.i;
+    uint32_t& pre_m = P.m;
+    pre_m = 0u;
+    const int64_t r0 = tile * 16;
 #pragma unroll
     for (int j = 0; j < kIp2IdxPer; ++j) {
       pre_i[j] = 0u;
       if (irow[j] >= 0) {
-        const int row = min(r0 + irow[j], last);                // rows past the end repeat the last one
+        const int row = (int)min(r0 + irow[j], (int64_t)last);   // rows past the end repeat the last one
         pre_i[j] = a.idx[(uint32_t)(row * a.rw + ioff[j])];
       }
     }
-    if (mbase) pre_m = mbase[(uint32_t)(min(r0 + mrow, last) * mstr + mw)];
+    if (mbase) pre_m = mbase[(uint32_t)((int)min(r0 + mrow, (int64_t)last) * mstr + mw)];
   };
   // raw tile layout: idx rows [0, n_idx), sign rows [n_idx, n_idx + n_sgn),
   // scale [.., +16), rnorm [.., +16)
-  auto raw_store = [&](int buf) {
+  auto raw_store = [&](const Pre& P, int buf) {
 #pragma unroll
     for (int j = 0; j < kIp2IdxPer; ++j)
-      if (irow[j] >= 0) s_raw[buf][tid + 64 * kIp2Waves * j] = pre_i[j];
-    if (mbase) s_raw[buf][n_idx + tid] = pre_m;
+      if (irow[j] >= 0) s_raw[buf][tid + 64 * kIp2Waves * j] = P.i[j];
+    if (mbase) s_raw[buf][n_idx + tid] = P.m;
   };
   // unpack raw buffer rb into operand buffer ob: task (u, lane) = tid + 512 j
   auto build = [&](int rb, int ob) {
@@ -495,23 +504,27 @@ __global__ void __launch_bounds__(64 * kIp2Waves) k_ip_score2(IS2Args a) {
   const int64_t nt = t_end > t_begin ? t_end - t_begin : 0;
 
   auto dbt = [&](int64_t i) { return (t_begin + i) * a.tstride; };   // database tile of step i
-  if (nt > 0) {
-    raw_load(dbt(0));
-    raw_store(0);
-    if (nt > 1) raw_load(dbt(1));
-  }
+  // prologue: raw tiles 0, 1 -> slots 0, 1 -> operands; raw tiles 2, 3 ->
+  // slots 2, 3; raw tiles 4, 5 in registers
+  raw_load(ra, dbt(0));
+  raw_load(rb, dbt(1));
+  raw_store(ra, 0);
+  raw_store(rb, 1);
+  raw_load(ra, dbt(2));
+  raw_load(rb, dbt(3));
+  raw_store(ra, 2);
+  raw_store(rb, 3);
+  raw_load(ra, dbt(4));
+  raw_load(rb, dbt(5));
   __syncthreads();
-  if (nt > 0) build(0, 0);
-  if (nt > 1) {
-    raw_store(1);
-    if (nt > 2) raw_load(dbt(2));
-  }
+  build(0, 0);
+  build(1, 1);
   __syncthreads();
 
-  for (int64_t i = 0; i < nt; ++i) {
-    const int cur = (int)(i & 1), nxt = cur ^ 1;
-    const int64_t row0 = dbt(i) * 16;
-    // (1) tile i against this wave's two query blocks
+  // one tile: its MFMAs from operand slot ab, then the unpack of raw slot
+  // ub into operand slot ub (a tile two ahead), then its scores and lists
+  auto tile_step = [&](const int ab, const int ub, const int64_t row0, const bool live)
+                       __attribute__((always_inline)) {
     f32x4 acc[kIp2Blocks], accq[kIp2Blocks];
 #pragma unroll
     for (int qb = 0; qb < kIp2Blocks; ++qb) {
@@ -520,24 +533,25 @@ __global__ void __launch_bounds__(64 * kIp2Waves) k_ip_score2(IS2Args a) {
     }
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
-      const bf16x8 av = __builtin_bit_cast(bf16x8, s_a[cur][u][lane]);
+      const bf16x8 av = __builtin_bit_cast(bf16x8, s_a[ab][u][lane]);
 #pragma unroll
       for (int qb = 0; qb < kIp2Blocks; ++qb) acc[qb] = mfma(av, bq[qb][u], acc[qb]);
     }
 #pragma unroll
     for (int v = 0; v < NS; ++v) {
-      const bf16x8 av = __builtin_bit_cast(bf16x8, s_a[cur][NU + v][lane]);
+      const bf16x8 av = __builtin_bit_cast(bf16x8, s_a[ab][NU + v][lane]);
 #pragma unroll
       for (int qb = 0; qb < kIp2Blocks; ++qb) accq[qb] = mfma(av, bq[qb][NU + v], accq[qb]);
     }
-    // unpack tile i + 1 while the MFMAs of tile i run (past the last tile it
-    // rebuilds a buffer nobody reads)
-    build(nxt, nxt);
+    // unpack a tile two ahead while the MFMAs run (past the last tile it
+    // rebuilds a slot nobody reads)
+    build(ub, ub);
+    if (!live) return;
     float sc[4], rn[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      sc[r] = s_sr[cur][0][4 * g4 + r];
-      rn[r] = s_sr[cur][1][4 * g4 + r];
+      sc[r] = s_sr[ab][0][4 * g4 + r];
+      rn[r] = s_sr[ab][1][4 * g4 + r];
     }
 #pragma unroll
     for (int qb = 0; qb < kIp2Blocks; ++qb) {
@@ -589,11 +603,20 @@ __global__ void __launch_bounds__(64 * kIp2Waves) k_ip_score2(IS2Args a) {
         if (c16 < 8) thq[qb] = s_ws[li];
       }
     }
-    // (3) stage tile i + 2, fetch tile i + 3
-    if (i + 2 < nt) {
-      raw_store(cur);
-      if (i + 3 < nt) raw_load(dbt(i + 3));
-    }
+  };
+
+  const int64_t np = (nt + 1) / 2;
+  for (int64_t p = 0; p < np; ++p) {
+    const int c = (int)(p & 1), n = c ^ 1;
+    // tiles 2p, 2p + 1 sit in operand slots 2c, 2c + 1; raw tiles 2p + 2,
+    // 2p + 3 in raw slots 2n, 2n + 1; raw tiles 2p + 4, 2p + 5 in ra, rb
+    tile_step(2 * c, 2 * n, dbt(2 * p) * 16, true);
+    tile_step(2 * c + 1, 2 * n + 1, dbt(2 * p + 1) * 16, 2 * p + 1 < nt);
+    // raw slots 2c, 2c + 1 were unpacked before the last barrier
+    raw_store(ra, 2 * c);
+    raw_store(rb, 2 * c + 1);
+    raw_load(ra, dbt(2 * p + 6));
+    raw_load(rb, dbt(2 * p + 7));
     __syncthreads();
   }
 
