@@ -411,6 +411,55 @@ def test_decode_full_size_128k(dev):
     print(worst)
 
 
+def test_quantize_and_dequantize_full_size(dev):
+    """The quantize layer at full size and in the launch configuration the
+    benchmark times: B=16, Hkv=8, 32768 tokens, d=128, bf16 K and V with 4
+    outlier channels per head x15, 4-bit codes, K in the row layout and V in
+    tile32, quantized in one call.  Three sampled sequences of each tensor
+    meet the quantize rules against the oracle's quantization of the same
+    inputs.  The oracle's codes of those sequences then replace the GPU's, the
+    whole layer is dequantized to bf16 as the benchmark times it, and the
+    sampled sequences match the oracle's reconstruction of its own codes
+    (1e-4 of each vector's max |x_hat| plus one bf16 rounding)."""
+    B, H, N, d = 16, 8, 32768, 128
+    _say("quantize + dequantize full size")
+    chk = synth.outlier_channels(10, H, d, 4)
+    chv = synth.outlier_channels(11, H, d, 4)
+    k = synth.kv_gaussian(B, H, N, d, 10, dtype="bf16", device=dev, per_head_channels=chk, factor=15.0)
+    v = synth.kv_gaussian(B, H, N, d, 11, dtype="bf16", device=dev, per_head_channels=chv, factor=15.0)
+    kcb, vcb = tq.Codebook(d, 4, rot_seed=1), tq.Codebook(d, 4, rot_seed=3)
+    kc = tq.Codes(kcb, B * H, N, TQ_LAYOUT_ROW)
+    vc = tq.Codes(vcb, B * H, N, TQ_LAYOUT_TILE32)
+    tq.tq_quantize_kv(kcb, vcb, k.view(B * H, N, d), v.view(B * H, N, d), kc, vc)
+    torch.cuda.synchronize()
+    sampled = [0, 77, B * H - 1]
+    refs = {}
+    stats = {}
+    for cb, codes, x, name in ((kcb, kc, k, "K"), (vcb, vc, v, "V")):
+        ocb = U.oracle_codebook(cb)
+        got = U.read_codes(codes, N, seqs=sampled)
+        for i, sq in enumerate(sampled):
+            x64 = U.to_f64(x.view(B * H, N, d)[sq])
+            flat = dict(idx=got["idx"][i], scale=got["scale"][i], sign=None, rnorm=None)
+            st, ref = U.compare_quant(ocb, x64, flat, name=f"{name} seq {sq}")
+            st.pop("vec_ok")
+            stats[(name, sq)] = st
+            U.upload_oracle_codes(codes, sq, ref, N)
+            refs[(name, sq)] = (ocb, ref)
+    ko = torch.empty((B * H, N, d), dtype=torch.bfloat16, device=dev)
+    vo = torch.empty_like(ko)
+    tq.tq_dequantize(kcb, kc, B * H, N, out=ko)
+    tq.tq_dequantize(vcb, vc, B * H, N, out=vo)
+    torch.cuda.synchronize()
+    for (name, sq), (ocb, ref) in refs.items():
+        out = (ko if name == "K" else vo)[sq].float().cpu().numpy().astype(np.float64)
+        xh = O.dequantize(ocb, ref["idx"], ref["scale"].astype(np.float32).astype(np.float64))
+        amax = np.max(np.abs(xh), axis=1, keepdims=True)
+        err = np.abs(out - xh)
+        assert np.all(err <= 1e-4 * amax + 2.0 ** -8 * np.abs(xh)), f"{name} seq {sq}: dequantize"
+    print(stats)
+
+
 def test_decode_deterministic(dev):
     _say("decode determinism")
     B, Hkv, Hq, N = 2, 2, 16, 2048
