@@ -45,7 +45,7 @@ extern "C" {
 typedef enum {
   TQ_OK = 0,
   TQ_ERR_INVALID = 1,     /* bad argument (null, out of range, inconsistent) */
-  TQ_ERR_UNSUPPORTED = 2, /* valid request this build has no kernel for      */
+  TQ_ERR_UNSUPPORTED = 2, /* valid request the library has no kernel for    */
   TQ_ERR_HIP = 3,         /* a HIP runtime call failed                        */
   TQ_ERR_ALLOC = 4,       /* device or host allocation failed                 */
   TQ_ERR_NUMERIC = 5      /* codebook solver did not converge                 */
