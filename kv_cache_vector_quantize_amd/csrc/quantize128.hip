@@ -2,7 +2,8 @@
 //
 // Page "什么是TurboQuant？…" (a2a-mcp.org blog): "第一阶段" items 1-2 (rotate by
 // Pi, normalise, Lloyd-Max index per coordinate) and "如何实现 TurboQuant" item 1
-// (quantize on every cache update), for codebooks without a QJL sketch.
+// (quantize on every cache update), and "第二阶段：QJL 残差校正" (the sign
+// sketch of the residual) for keys with m <= 128 sketch rows.
 //
 // One workgroup of four waves owns a tile of 32 consecutive positions of one
 // sequence (tile32-aligned in absolute position) and loops over tiles.
@@ -17,8 +18,16 @@
 // leave 2^-18 |Pi| per entry, ~2e-7 in y: an index moves only for a
 // coordinate that close to a boundary, about 1.5e-5 of the coordinates at 4
 // bits against the 1e-4 the zone rule allows (8-bit codebooks have 16x the
-// boundaries and need the third part).  Keys with a QJL sketch take the
-// fp32-MFMA kernel.
+// boundaries and need the third part).
+//
+// Keys with a sketch (row layout) take three parts of Pi, so y and the
+// residual r = y - (scale/|x|) c[idx] carry fp32-level error and |r| its
+// relative accuracy.  Each wave writes its 32 coordinates of r to LDS as bf16
+// hi + lo; after the tile's barrier wave w forms sketch rows 32w .. 32w + 31
+// of u = S r with hi.hi + hi.lo + lo.hi products of S (registers) and r
+// (about 2^-17 of |S_j| |r|, far inside the 1e-5 zone of the sign rule),
+// packs their signs into word w of each sign row and, in wave 0, writes
+// rnorm = |x| |r|.
 // Row layout codes take z^T (rows = coordinates: a lane holds 16 coordinates
 // of one vector); tile32 codes take z (rows = vectors: a lane holds one
 // coordinate of 16 vectors, which is how a tile32 record is ordered).
@@ -60,6 +69,13 @@ struct Q128Args {
   float* scale;
   int64_t idx_pitch, seq_stride;
   PageMap pm;          // where a sequence's blocks are written (identity unless paged)
+  // keys with a sketch (k_q128<..., true>, row layout): S as hi / lo
+  // operands in the layout of rop (rows past m zero), sign rows, residual norms
+  const uint4* sop;
+  uint32_t* sign;
+  float* rnorm;
+  int64_t sign_pitch;
+  int m;
 };
 
 __device__ inline f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -110,8 +126,9 @@ __device__ inline void share_load(Share<DT>& sh, const void* x, int64_t e0, bool
   }
 }
 
-template <int DT, bool T32, int NP>
+template <int DT, bool T32, int NP, bool QJ>
 __global__ void __launch_bounds__(256) k_q128(Q128Args a) {
+  static_assert(!(QJ && T32), "sketch signs are written in the row layout only");
   constexpr bool XLO = DT != TQ_BF16, XLO2 = DT == TQ_F32;
   __shared__ __align__(16) uint16_t xh[TILE][XS];
   __shared__ __align__(16) uint16_t xl[XLO ? TILE : 1][XS];
@@ -122,6 +139,11 @@ __global__ void __launch_bounds__(256) k_q128(Q128Args a) {
   __shared__ float s_n[TILE], s_ig[TILE];
   __shared__ float s_c2[4][TILE];
   __shared__ int s_valid[TILE];
+  // residual r of the tile in bf16 hi / lo (B operands of the sketch) and
+  // per-wave partial |r|^2
+  __shared__ __align__(16) uint16_t rh[QJ ? TILE : 1][QJ ? XS : 8];
+  __shared__ __align__(16) uint16_t rl[QJ ? TILE : 1][QJ ? XS : 8];
+  __shared__ float s_r2[QJ ? 4 : 1][TILE];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int c32 = lane & 31, hl = lane >> 5;
@@ -132,12 +154,16 @@ __global__ void __launch_bounds__(256) k_q128(Q128Args a) {
   for (int i = tid; i < a.ncell; i += 256) s_tab[i] = a.qtab[i];
   for (int i = tid; i < L; i += 256) s_cent[i] = a.cent[i];
 
-  bf16x8 ph[8], pl[8], pm[NP == 3 ? 8 : 1];
+  bf16x8 ph[8], pl[8], pm[NP == 3 ? 8 : 1], sh[QJ ? 8 : 1], sl[QJ ? 8 : 1];
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
     ph[s] = __builtin_bit_cast(bf16x8, a.rop[((wave * 8 + s) * 3 + 0) * 64 + lane]);
     pl[s] = __builtin_bit_cast(bf16x8, a.rop[((wave * 8 + s) * 3 + 1) * 64 + lane]);
     if constexpr (NP == 3) pm[s] = __builtin_bit_cast(bf16x8, a.rop[((wave * 8 + s) * 3 + 2) * 64 + lane]);
+    if constexpr (QJ) {
+      sh[s] = __builtin_bit_cast(bf16x8, a.sop[((wave * 8 + s) * 3 + 0) * 64 + lane]);
+      sl[s] = __builtin_bit_cast(bf16x8, a.sop[((wave * 8 + s) * 3 + 1) * 64 + lane]);
+    }
   }
   const bool vec_ok = (reinterpret_cast<uintptr_t>(a.x) & 15) == 0;
   const bool row16 = (a.idx_pitch & 15) == 0;
@@ -385,7 +411,72 @@ __global__ void __launch_bounds__(256) k_q128(Q128Args a) {
       }
       a.scale[pos0 + c32] = sc;
     }
+    // (g) keys with a sketch: residual r = y - (scale / |x|) c[idx] of this
+    // lane's 16 coordinates (element v: coordinate 32w + 8(v/4) + 4hl + v%4
+    // of vector c32; scale / |x| is 1, or 1 / |c[idx]| with norm correction,
+    // also for x = 0, where y = 0), staged for the sketch product
+    float qn = 0.f;
+    bool qvalid = false;
+    if constexpr (QJ) {
+      qn = s_n[c32];
+      qvalid = s_valid[c32] != 0;
+      float ratio = 1.f;           // scale / |x|
+      if (need_c) {
+        const float nh = sqrtf(((s_c2[0][c32] + s_c2[1][c32]) + s_c2[2][c32]) + s_c2[3][c32]);
+        ratio = 1.f / nh;
+      }
+      const float inv_n = qn > 0.f ? 1.f / qn : 0.f;
+      float r2 = 0.f;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        uint32_t hw[2], lw[2];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          uint32_t hh[2], ll[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int v = 4 * g + 2 * h2 + e;
+            const float r = acc[v] * inv_n - ratio * s_cent[iv[v]];
+            r2 = fmaf(r, r, r2);
+            hh[e] = bf16_bits(r);
+            ll[e] = bf16_bits(r - bf16_float(hh[e]));
+          }
+          hw[h2] = hh[0] | (hh[1] << 16);
+          lw[h2] = ll[0] | (ll[1] << 16);
+        }
+        const int col = 32 * wave + 8 * g + 4 * hl;
+        *reinterpret_cast<uint2*>(&rh[c32][col]) = make_uint2(hw[0], hw[1]);
+        *reinterpret_cast<uint2*>(&rl[c32][col]) = make_uint2(lw[0], lw[1]);
+      }
+      r2 += __shfl_xor(r2, 32);
+      if (hl == 0) s_r2[wave][c32] = r2;
+    }
     __syncthreads();
+    if constexpr (QJ) {
+      // (h) u = S r: sketch rows 32w .. 32w + 31 of the 32 vectors, then the
+      // sign bits (u >= 0) of those rows as word w of each sign row, and the
+      // residual norm |x| |r|
+      f32x16 au = {};
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const bf16x8 xrh = *reinterpret_cast<const bf16x8*>(&rh[c32][16 * s + 8 * hl]);
+        const bf16x8 xrl = *reinterpret_cast<const bf16x8*>(&rl[c32][16 * s + 8 * hl]);
+        au = mfma32(sh[s], xrl, au);
+        au = mfma32(sl[s], xrh, au);
+        au = mfma32(sh[s], xrh, au);
+      }
+      uint32_t bits = 0u;
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        bits |= (au[v] >= 0.f ? 1u : 0u) << (8 * (v >> 2) + 4 * hl + (v & 3));
+      bits |= (uint32_t)__shfl_xor((int)bits, 32);
+      const int rows = a.m - 32 * wave;     // sketch rows of this word
+      if (rows < 32) bits &= rows > 0 ? (1u << rows) - 1u : 0u;
+      if (hl == 0 && qvalid && rows > 0)
+        a.sign[(((pos0 + c32) * a.sign_pitch) >> 2) + wave] = bits;
+      if (wave == 0 && hl == 0 && qvalid)
+        a.rnorm[pos0 + c32] = qn * sqrtf(((s_r2[0][c32] + s_r2[1][c32]) + s_r2[2][c32]) + s_r2[3][c32]);
+    }
 
     if constexpr (T32) {
       // (f) the assembled tile32 block: 512*b bytes = 128*b words
@@ -404,7 +495,7 @@ __global__ void __launch_bounds__(256) k_q128(Q128Args a) {
   }
 }
 
-template <int DT, bool T32, int NP>
+template <int DT, bool T32, int NP, bool QJ>
 int resident_grid(int n_tiles) {
   // workgroups that stay resident at once (per device, computed once)
   static int per_device[64] = {0};
@@ -412,7 +503,8 @@ int resident_grid(int n_tiles) {
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
   if (per_device[dev] == 0) {
     int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_q128<DT, T32, NP>, 256, 0) != hipSuccess || per_cu < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_q128<DT, T32, NP, QJ>, 256, 0) != hipSuccess ||
+        per_cu < 1)
       per_cu = 2;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
       cus = 256;
@@ -421,15 +513,20 @@ int resident_grid(int n_tiles) {
   return n_tiles < per_device[dev] ? n_tiles : per_device[dev];
 }
 
-template <int DT, bool T32, int NP>
+template <int DT, bool T32, int NP, bool QJ = false>
 void launch_np(const Q128Args& a, hipStream_t st) {
-  hipLaunchKernelGGL((k_q128<DT, T32, NP>), dim3(resident_grid<DT, T32, NP>(a.n_tiles)), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((k_q128<DT, T32, NP, QJ>), dim3(resident_grid<DT, T32, NP, QJ>(a.n_tiles)), dim3(256), 0,
+                     st, a);
 }
 
 template <int DT>
 hipError_t launch_dt(const Q128Args& a, bool t32, hipStream_t st) {
   const bool two = a.bits <= 4;      // two parts of Pi suffice up to 4 bits
-  if (t32) {
+  if (a.m > 0) {
+    // keys with a sketch: three parts of Pi (fp32-level y, so that |r| keeps
+    // its relative accuracy), row layout
+    launch_np<DT, false, 3, true>(a, st);
+  } else if (t32) {
     if (two) launch_np<DT, true, 2>(a, st);
     else launch_np<DT, true, 3>(a, st);
   } else {
@@ -444,7 +541,9 @@ hipError_t launch_dt(const Q128Args& a, bool t32, hipStream_t st) {
 bool quantize128_supported(const tq_codebook* cb, const QuantJob& job) {
   const int64_t first = job.tok_offset / TILE, last = (job.tok_offset + job.n_tok - 1) / TILE;
   const int64_t tiles = (last - first + 1) * job.n_seq;
-  return cb->p.d == 128 && cb->p.qjl_m == 0 && cb->dev.rop && cb->dev.qtab && cb->dev.qcells >= 1 &&
+  const bool sketch_ok = cb->p.qjl_m == 0 ||
+                         (cb->p.qjl_m <= 128 && cb->dev.sop && job.out.layout == TQ_LAYOUT_ROW);
+  return cb->p.d == 128 && sketch_ok && cb->dev.rop && cb->dev.qtab && cb->dev.qcells >= 1 &&
          tiles < 0x7FFFFFFFLL && job.n_seq < 0x7FFFFFFFLL;
 }
 
@@ -469,6 +568,11 @@ hipError_t launch_quantize128(const tq_codebook* cb, const QuantJob& job, hipStr
   a.idx_pitch = job.out.idx_row_bytes;
   a.seq_stride = job.out.seq_stride;
   a.pm = job.pm;
+  a.m = cb->p.qjl_m;
+  a.sop = reinterpret_cast<const uint4*>(cb->dev.sop);
+  a.sign = static_cast<uint32_t*>(job.out.sign);
+  a.rnorm = job.out.rnorm;
+  a.sign_pitch = job.out.sign_row_bytes;
   const bool t32 = job.out.layout == TQ_LAYOUT_TILE32;
   ProfileScope prof(TQ_KERNEL_QUANTIZE, stream);
   switch (job.dt) {

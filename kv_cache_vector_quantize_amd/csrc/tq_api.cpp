@@ -126,6 +126,7 @@ void free_dev(DeviceCodebook& d) {
   if (d.pair_tab) (void)hipFree(d.pair_tab);
   if (d.rop) (void)hipFree(d.rop);
   if (d.qtab) (void)hipFree(d.qtab);
+  if (d.sop) (void)hipFree(d.sop);
   d = DeviceCodebook{};
 }
 
@@ -361,14 +362,22 @@ tq_status tq_codebook_build(const tq_params* params, tq_codebook** out) {
         return hip_fail(e, "codebook upload");
       }
     }
-    if (d == 128 && m == 0) {
-      // operands and index cells of the d = 128 quantize kernel
-      std::vector<uint32_t> rop, qtab;
+    if (d == 128 && m <= 128) {
+      // operands and index cells of the d = 128 quantize kernel, and the
+      // sketch operands of keys with m <= 128 rows
+      std::vector<uint32_t> rop, qtab, sop;
       float qG = 0.f;
       build_q128_operands(cb->host.rot, rop);
+      if (m > 0) {
+        std::vector<double> sp((size_t)128 * 128, 0.0);
+        for (int j = 0; j < m; ++j)
+          for (int i = 0; i < 128; ++i) sp[(size_t)j * 128 + i] = cb->host.qjl[(size_t)j * 128 + i];
+        build_q128_operands(sp, sop);
+      }
       if (build_q128_cells(bnd, qtab, qG)) {
         if ((e = upload(&cb->dev.rop, rop)) != hipSuccess ||
-            (e = upload(&cb->dev.qtab, qtab)) != hipSuccess) {
+            (e = upload(&cb->dev.qtab, qtab)) != hipSuccess ||
+            (m > 0 && (e = upload(&cb->dev.sop, sop)) != hipSuccess)) {
           free_dev(cb->dev);
           delete cb;
           return hip_fail(e, "codebook upload");

@@ -60,6 +60,9 @@ struct DeviceCodebook {
   //  the closest pair of boundaries, so at most one lies inside
   uint32_t* rop = nullptr;
   uint32_t* qtab = nullptr;
+  //  sop: S (rows past m zero) as hi / lo / lo2 operands in the layout of rop
+  //  (d = 128, 0 < m <= 128); keys with a sketch use hi and lo
+  uint32_t* sop = nullptr;
   int qcells = 0;
   float qG = 0.f;
 };

@@ -72,6 +72,10 @@ def _quant_case(dev, d, bits, m, nc, dtype, n_seq, n_tok, tok_offset=0, layout=T
     (128, 7, 0, True, "f32"),
     (128, 1, 0, False, "bf16"),
     (128, 1, 64, False, "f16"),
+    (128, 3, 128, True, "bf16"),   # keys with a sketch: split-bf16 rotation and sketch
+    (128, 4, 100, False, "bf16"),
+    (128, 5, 128, True, "f32"),
+    (128, 2, 32, False, "f16"),
     (96, 3, 96, True, "bf16"),
     (64, 4, 32, False, "f32"),
     (40, 5, 40, False, "f32"),
@@ -127,6 +131,27 @@ def test_quantize_zone_rate_large(dev, bits, layout):
     st, _ = U.compare_quant(ocb, x64, flat, name=f"zone b{bits}")
     st.pop("vec_ok")
     print(st, "mismatch rate", st["idx_mismatch"] / (n_seq * n_tok * d))
+
+
+@pytest.mark.parametrize("bits,m,nc,dtype", [(3, 128, False, "bf16"), (4, 128, True, "bf16"),
+                                          (2, 96, False, "f32")])
+def test_quantize_sketch_large(dev, bits, m, nc, dtype):
+    """16384 vectors with outlier channels through the d = 128 key kernel
+    (three-part split-bf16 rotation, two-part split-bf16 sketch): indices
+    outside the 1e-5 boundary zone, sign bits outside |S r| < 1e-5, scales
+    (2e-6) and residual norms (1e-5) meet the oracle on 2.1 M coordinates and
+    up to 2.1 M sign bits."""
+    _say("quantize sketch large", bits, m, nc, dtype)
+    n_seq, n_tok, d = 8, 2048, 128
+    cb, codes, x = _quant_case(dev, d, bits, m, nc, dtype, n_seq, n_tok, seed=200 + bits + m)
+    got = U.read_codes(codes, n_tok)
+    ocb = U.oracle_codebook(cb)
+    x64 = x.float().numpy().astype(np.float64).reshape(-1, d)
+    flat = dict(idx=got["idx"].reshape(-1, d), scale=got["scale"].reshape(-1),
+                sign=got["sign"].reshape(-1, m), rnorm=got["rnorm"].reshape(-1))
+    st, _ = U.compare_quant(ocb, x64, flat, name=f"sketch b{bits} m{m}")
+    st.pop("vec_ok")
+    print(st)
 
 
 @pytest.mark.parametrize("bits", [1, 2, 3, 4, 5, 6, 7, 8])
