@@ -90,3 +90,36 @@ def test_decode_rejects_null_codebooks():
     st = L.tq_attn_decode(None, None, None, 0, 1, 8, 1, None, None, None, 16, 0.1, None, None,
                           None, 0, None)
     assert st == _lib.TQ_ERR_INVALID
+
+
+def test_paged_workspace_and_page_size_validation():
+    # paged plans take whole pages per wave (at most 64); the workspace query
+    # is host-only and rejects page sizes that are not powers of two >= 32
+    for pt in (32, 64, 128, 4096):
+        assert tq.tq_attn_decode_paged_workspace(8, 64, 8, 131072, 128, pt) > 0
+    assert tq.tq_attn_decode_paged_workspace(2, 16, 2, 0, 128, 64) > 0
+    for pt in (0, 16, 48, 100, 1 << 17):
+        with pytest.raises(tq.TQError) as e:
+            tq.tq_attn_decode_paged_workspace(2, 16, 2, 300, 128, pt)
+        assert e.value.status == _lib.TQ_ERR_INVALID
+    with pytest.raises(tq.TQError) as e:
+        tq.tq_attn_decode_paged_workspace(2, 16, 2, 300, 64, 64)
+    assert e.value.status == _lib.TQ_ERR_UNSUPPORTED
+
+
+def test_paged_calls_reject_bad_pages_before_device():
+    L = tq.lib()
+    bf16 = 1
+    # page size, missing table and too few table entries fail before any device call
+    st = L.tq_quantize_kv_paged(None, None, ctypes.c_void_p(16), None, bf16, 1, 1, 10, 0, ctypes.c_void_p(16), 1,
+                                48, None, None, None)
+    assert st == _lib.TQ_ERR_INVALID and b"page_tokens" in L.tq_last_error()
+    st = L.tq_quantize_kv_paged(None, None, ctypes.c_void_p(16), None, bf16, 1, 1, 10, 0, None, 1, 64,
+                                None, None, None)
+    assert st == _lib.TQ_ERR_INVALID and b"block_table" in L.tq_last_error()
+    st = L.tq_quantize_kv_paged(None, None, ctypes.c_void_p(16), None, bf16, 1, 1, 100, 0, ctypes.c_void_p(16), 1,
+                                64, None, None, None)
+    assert st == _lib.TQ_ERR_INVALID and b"max_pages" in L.tq_last_error()
+    st = L.tq_attn_decode_paged(None, None, None, 0, 1, 8, 1, None, None, ctypes.c_void_p(16), 1, 64, None, 100,
+                                0.1, None, None, None, 0, None)
+    assert st == _lib.TQ_ERR_INVALID and b"max_pages" in L.tq_last_error()
