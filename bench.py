@@ -631,6 +631,17 @@ def main():
         print("[bench] vector-search leg", file=sys.stderr, flush=True)
         res["vector_search"] = vector_search_leg(torch, tq, synth, dev, iters=max(3, args.steps // 5),
                                                  warm=max(1, args.warmup // 5))
+    # codebook construction (host, float64 Lloyd-Max + QR + sketch, then the
+    # device tables), once per (d, bits, m, seeds) in a serving process
+    cbt = {}
+    for name, (d_, b_, m_) in {"d128_b3_m128": (128, 3, 128), "d128_b4": (128, 4, 0),
+                              "d200_b4_m200": (200, 4, 200)}.items():
+        t0 = time.perf_counter()
+        cb_ = tq.Codebook(d_, b_, qjl_m=m_, rot_seed=11, qjl_seed=12)
+        torch.cuda.synchronize()
+        cbt[name] = round((time.perf_counter() - t0) * 1e3, 2)
+        del cb_
+    res["codebook_build_ms"] = cbt
     # achievable device-to-device copy rate of this machine (1 GiB read + 1 GiB
     # written per copy); with --calib-copy it is also the counter calibration
     src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
