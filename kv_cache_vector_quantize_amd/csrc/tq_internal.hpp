@@ -135,8 +135,9 @@ struct QuantJob {
 
 hipError_t launch_quantize(const tq_codebook* cb, const QuantJob& job, hipStream_t stream);
 
-// d = 128 bulk quantize without a sketch (bf16 hi/lo MFMA rotation, table
-// index); used by launch_quantize when quantize128_supported
+// d = 128 bulk quantize (split-bf16 MFMA rotation, table index; sketches of
+// up to 128 rows in the row layout); used by launch_quantize when
+// quantize128_supported
 bool quantize128_supported(const tq_codebook* cb, const QuantJob& job);
 hipError_t launch_quantize128(const tq_codebook* cb, const QuantJob& job, hipStream_t stream);
 
