@@ -112,8 +112,11 @@ struct DqLds {
   static constexpr int ESH = PAIR ? 3 : 2;                    // log2 bytes per entry
   static constexpr int TABB = (PAIR ? (1 << (2 * B)) : (1 << B)) << ESH;
   static constexpr int STAGE = 2 * 8 * 2 * 64 * 16;
+  // A tile32 block holds four token groups of 32 B dwords each; staged, each
+  // group is followed by one pad dword so that the four groups (read together
+  // by the lanes of one instruction) start in different banks.
   static constexpr int BLKW = 128 * B;                        // dwords of a tile32 block
-  static constexpr int BLKP = BLKW + 4;                       // + pad for a straddling read
+  static constexpr int BLKP = BLKW + 8;                       // + group pads, + a straddling read
   static constexpr int BLK = T32 ? 2 * BLKP * 4 : 0;
   static constexpr int OROW = O32 ? 36 : 20;                  // dwords per staged output row
   static constexpr int OST = 4 * 32 * OROW * 4;
@@ -238,8 +241,8 @@ __global__ void __launch_bounds__(256) k_dq128(DQArgs a) {
     if constexpr (T32) {
 #pragma unroll
       for (int i = 0; i < NBL; ++i) {
-        const int k = tid + 256 * i;
-        s_blk[sb][k < L::BLKW ? k : L::BLKW - 1] = R.w[i];
+        const int k0 = tid + 256 * i, k = k0 < L::BLKW ? k0 : L::BLKW - 1;
+        s_blk[sb][k + k / (32 * B)] = R.w[i];
       }
     }
   };
@@ -279,11 +282,12 @@ __global__ void __launch_bounds__(256) k_dq128(DQArgs a) {
       // token tt of the tile sits in record group G = (tt % 16) / 4, slot
       // es = tt % 4 + 4 (tt / 16); coordinate i = 64hl + 8s + j is record
       // r = 16G + 8(s % 2) + j, coordinate group jj = 4hl + s / 2, at bit
-      // ((8 r + jj) 8 + es) B of the block
+      // ((8 r + jj) 8 + es) B of the block, i.e. in token group G's staged
+      // segment (which starts at dword 32 B G + G)
       const uint32_t* blk = s_blk[rb];
       const int G = (c32 & 15) >> 2, es = (c32 & 3) + 4 * (c32 >> 4), jj = 4 * hl + wave;
       const int lb = (1024 * G + 8 * jj + es) * B;
-      const uint32_t* bp = blk + (lb >> 5);
+      const uint32_t* bp = blk + (lb >> 5) + G;
       const uint32_t sh = (uint32_t)(lb & 31);
 #pragma unroll
       for (int ls = 0; ls < 2; ++ls)
