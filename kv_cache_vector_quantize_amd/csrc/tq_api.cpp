@@ -236,6 +236,16 @@ extern "C" {
 const char* tq_last_error(void) { return g_err.c_str(); }
 
 tq_status tq_codebook_build(const tq_params* params, tq_codebook** out) {
+  // set while a codebook is under construction, so that an exception thrown
+  // part-way (a host allocation) releases it and the tables already uploaded
+  tq_codebook* pending = nullptr;
+  auto release_pending = [&]() {
+    if (pending) {
+      free_dev(pending->dev);
+      delete pending;
+      pending = nullptr;
+    }
+  };
   try {
     if (!out) return fail(TQ_ERR_INVALID, "out is NULL");
     *out = nullptr;
@@ -243,17 +253,18 @@ tq_status tq_codebook_build(const tq_params* params, tq_codebook** out) {
     if (s != TQ_OK) return s;
     tq_codebook* cb = new (std::nothrow) tq_codebook();
     if (!cb) return fail(TQ_ERR_ALLOC, "host allocation failed");
+    pending = cb;
     cb->p = *params;
     cb->L = 1 << params->bits;
     cb->dp = pad32(params->d);
     cb->mp = params->qjl_m > 0 ? pad32(params->qjl_m) : 0;
     std::string err;
     if (!build_codebook_host(cb->p, cb->host, err)) {
-      delete cb;
+      release_pending();
       return fail(TQ_ERR_NUMERIC, err);
     }
     hipError_t e = hipGetDevice(&cb->device);
-    if (e != hipSuccess) { delete cb; return hip_fail(e, "hipGetDevice"); }
+    if (e != hipSuccess) { release_pending(); return hip_fail(e, "hipGetDevice"); }
     const int d = cb->p.d, dp = cb->dp, L = cb->L, m = cb->p.qjl_m, mp = cb->mp;
     std::vector<float> cent(L), bnd(L - 1), rot((size_t)dp * dp, 0.f), rotT((size_t)dp * dp, 0.f);
     for (int k = 0; k < L; ++k) cent[k] = (float)cb->host.centroids[k];
@@ -290,8 +301,7 @@ tq_status tq_codebook_build(const tq_params* params, tq_codebook** out) {
         (e = upload(&cb->dev.rot, rot)) != hipSuccess ||
         (e = upload(&cb->dev.rotT, rotT)) != hipSuccess ||
         (e = upload(&cb->dev.pair_tab, tab)) != hipSuccess) {
-      free_dev(cb->dev);
-      delete cb;
+      release_pending();
       return hip_fail(e, "codebook upload");
     }
     if (m > 0) {
@@ -315,8 +325,7 @@ tq_status tq_codebook_build(const tq_params* params, tq_codebook** out) {
           sprot[(size_t)j * dp + k] = (float)(cq * acc);
         }
       if ((e = upload(&cb->dev.sprot, sprot)) != hipSuccess) {
-        free_dev(cb->dev);
-        delete cb;
+        release_pending();
         return hip_fail(e, "codebook upload");
       }
       if (d == 128 && m <= 128) {
@@ -336,16 +345,14 @@ tq_status tq_codebook_build(const tq_params* params, tq_codebook** out) {
         std::vector<uint32_t> dqs;
         build_q128_operands(dq_permute_columns(a2), dqs);
         if ((e = upload(&cb->dev.dqs, dqs)) != hipSuccess || (e = upload(&cb->dev.dqcs, cs)) != hipSuccess) {
-          free_dev(cb->dev);
-          delete cb;
+          release_pending();
           return hip_fail(e, "codebook upload");
         }
       }
       if ((e = upload(&cb->dev.qjl, qjl)) != hipSuccess ||
           (e = upload(&cb->dev.qjlT, qjlT)) != hipSuccess ||
           (e = upload(&cb->dev.sprotT, sprotT)) != hipSuccess) {
-        free_dev(cb->dev);
-        delete cb;
+        release_pending();
         return hip_fail(e, "codebook upload");
       }
     }
@@ -357,8 +364,7 @@ tq_status tq_codebook_build(const tq_params* params, tq_codebook** out) {
       std::vector<uint32_t> dqop;
       build_q128_operands(dq_permute_columns(pt), dqop);
       if ((e = upload(&cb->dev.dqop, dqop)) != hipSuccess) {
-        free_dev(cb->dev);
-        delete cb;
+        release_pending();
         return hip_fail(e, "codebook upload");
       }
     }
@@ -378,19 +384,21 @@ tq_status tq_codebook_build(const tq_params* params, tq_codebook** out) {
         if ((e = upload(&cb->dev.rop, rop)) != hipSuccess ||
             (e = upload(&cb->dev.qtab, qtab)) != hipSuccess ||
             (m > 0 && (e = upload(&cb->dev.sop, sop)) != hipSuccess)) {
-          free_dev(cb->dev);
-          delete cb;
+          release_pending();
           return hip_fail(e, "codebook upload");
         }
         cb->dev.qcells = (int)(qtab.size() / 2);
         cb->dev.qG = qG;
       }
     }
+    pending = nullptr;
     *out = cb;
     return TQ_OK;
   } catch (const std::exception& ex) {
+    release_pending();
     return fail(TQ_ERR_ALLOC, std::string("tq_codebook_build: ") + ex.what());
   } catch (...) {
+    release_pending();
     return fail(TQ_ERR_ALLOC, "tq_codebook_build: unknown exception");
   }
 }
