@@ -839,7 +839,10 @@ DecodePlan plan_decode(int64_t B, int64_t Hq, int64_t Hkv, int64_t n_ctx, int d,
   p.g = Hkv > 0 ? (int)(Hq / Hkv) : 0;
   p.qgroups = (p.g + 7) / 8;
   p.rows = B * Hkv * p.qgroups;
-  const int64_t target_waves = 4096;          // two rounds of 8 waves on each of 256 CUs
+  // one round of 8-wave workgroups on each of the 256 CUs (one workgroup per
+  // CU at a time): against two rounds of half-length chunks this measured 2%
+  // faster at a 128K context, with half the partials to combine
+  const int64_t target_waves = 2048;
   int64_t parts = p.rows > 0 ? (target_waves + p.rows - 1) / p.rows : 1;
   if (parts < 1) parts = 1;
   int64_t chunk = (n_ctx + parts - 1) / parts;
