@@ -728,7 +728,9 @@ TopkPlan plan_topk(int64_t nq, int64_t n_db, int k, int d, int m) {
   p.nqb = p.shared ? (nq + kIp2Queries - 1) / kIp2Queries * (kIp2Queries / 8) : (nq + 7) / 8;
   p.n_tiles = (n_db + 15) / 16;
   const int64_t groups = p.shared ? p.nqb / (kIp2Queries / 8) : p.nqb;
-  const int64_t target = p.shared ? 512 : 2048;                  // workgroups in flight
+  // workgroups: shared tiles take 122 KB of LDS, one workgroup per CU, so
+  // 256 is one round over the CUs (3% faster than two rounds at 10^6 rows)
+  const int64_t target = p.shared ? 256 : 2048;
   int64_t chunks = groups > 0 ? (target + groups - 1) / groups : 1;
   int64_t cap = p.n_tiles / 8;                                   // >= 8 tiles per chunk
   if (chunks > cap) chunks = cap;
