@@ -51,6 +51,8 @@ typedef enum {
   TQ_ERR_NUMERIC = 5      /* codebook solver did not converge                 */
 } tq_status;
 
+/* Element types.  Calls take a dtype as int32_t holding one of these values
+ * (any other value is rejected with TQ_ERR_INVALID). */
 typedef enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 } tq_dtype;
 
 /* Code layouts (the pages only say "bit-packed"; both are LSB-first).
@@ -135,6 +137,15 @@ tq_status tq_codebook_export(const tq_codebook* cb, double* centroids, double* b
 tq_status tq_codebook_values(const tq_params* params, double* centroids, double* boundaries,
                              double* rot, double* qjl);
 
+/* Iteration limits of the Lloyd-Max solve behind tq_codebook_build and
+ * tq_codebook_values on the calling thread (host only): at most lloyd_iters
+ * Lloyd steps (midpoint then centroid condition), then at most newton_iters
+ * Newton steps on the midpoint residual; a solve whose residual is not below
+ * 1e-12 then fails with TQ_ERR_NUMERIC.  A value <= 0 restores that limit's
+ * default (400000 and 80, enough for every d in 3..256 and bits in 1..8).
+ * Meant for exercising the error path; never fails. */
+tq_status tq_codebook_solver_limits(int32_t lloyd_iters, int32_t newton_iters);
+
 /* Minimum ROW-layout pitches for this codebook: 4*bits*ceil(d/32) and
  * 4*ceil(m/32) (0 when qjl_m == 0). */
 tq_status tq_code_row_bytes(const tq_codebook* cb, int64_t* idx_row_bytes,
@@ -155,7 +166,7 @@ tq_status tq_code_row_bytes(const tq_codebook* cb, int64_t* idx_row_bytes,
  * Errors: TQ_ERR_INVALID, TQ_ERR_UNSUPPORTED (layout/d combination),
  * TQ_ERR_HIP (launch). */
 tq_status tq_quantize_kv(const tq_codebook* kcb, const tq_codebook* vcb, const void* k,
-                         const void* v, tq_dtype dt, int64_t n_seq, int64_t n_tok,
+                         const void* v, int32_t dt, int64_t n_seq, int64_t n_tok,
                          int64_t tok_offset, const tq_codes* k_out, const tq_codes* v_out,
                          void* stream);
 
@@ -181,7 +192,7 @@ tq_status tq_attn_decode_workspace(int64_t B, int64_t Hq, int64_t Hkv, int64_t n
  * Errors: TQ_ERR_INVALID, TQ_ERR_UNSUPPORTED (d != 128 or bit widths
  * without a kernel), TQ_ERR_HIP. */
 tq_status tq_attn_decode(const tq_codebook* kcb, const tq_codebook* vcb, const void* q,
-                         tq_dtype qdt, int64_t B, int64_t Hq, int64_t Hkv, const tq_codes* k,
+                         int32_t qdt, int64_t B, int64_t Hq, int64_t Hkv, const tq_codes* k,
                          const tq_codes* v, const int32_t* seq_lens, int64_t n_ctx,
                          float sm_scale, float* out, float* logits, void* workspace,
                          size_t ws_bytes, void* stream);
@@ -206,7 +217,7 @@ tq_status tq_attn_decode(const tq_codebook* kcb, const tq_codebook* vcb, const v
  * h of k_pool / v_pool.  max_pages * page_tokens >= tok_offset + n_tok.
  * Otherwise as tq_quantize_kv (same kernels, same codes). */
 tq_status tq_quantize_kv_paged(const tq_codebook* kcb, const tq_codebook* vcb, const void* k,
-                               const void* v, tq_dtype dt, int64_t B, int64_t Hkv, int64_t n_tok,
+                               const void* v, int32_t dt, int64_t B, int64_t Hkv, int64_t n_tok,
                                int64_t tok_offset, const int32_t* block_table, int64_t max_pages,
                                int32_t page_tokens, const tq_codes* k_pool, const tq_codes* v_pool,
                                void* stream);
@@ -222,7 +233,7 @@ tq_status tq_attn_decode_paged_workspace(int64_t B, int64_t Hq, int64_t Hkv, int
  * Same results as tq_attn_decode on the same codes laid out contiguously, up
  * to the order of the split-K partial sums (each wave covers whole pages). */
 tq_status tq_attn_decode_paged(const tq_codebook* kcb, const tq_codebook* vcb, const void* q,
-                               tq_dtype qdt, int64_t B, int64_t Hq, int64_t Hkv, const tq_codes* k_pool,
+                               int32_t qdt, int64_t B, int64_t Hq, int64_t Hkv, const tq_codes* k_pool,
                                const tq_codes* v_pool, const int32_t* block_table, int64_t max_pages,
                                int32_t page_tokens, const int32_t* seq_lens, int64_t n_ctx, float sm_scale,
                                float* out, float* logits, void* workspace, size_t ws_bytes, void* stream);
@@ -272,7 +283,7 @@ tq_status tq_ip_topk(const tq_codebook* cb, const float* queries, int64_t nq,
  * operand (about 2^-16 relative to |x_hat|); other shapes use fp32 FMAs.
  * Errors: TQ_ERR_INVALID, TQ_ERR_HIP. */
 tq_status tq_dequantize(const tq_codebook* cb, const tq_codes* codes, int64_t n_seq,
-                        int64_t n_tok, int64_t tok_offset, void* out, tq_dtype out_dt,
+                        int64_t n_tok, int64_t tok_offset, void* out, int32_t out_dt,
                         void* stream);
 
 /* Kernel timing (instrumentation; not part of the method).

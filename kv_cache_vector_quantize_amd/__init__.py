@@ -22,6 +22,7 @@ from ._lib import (  # noqa: F401
     tq_attn_decode_paged,
     tq_attn_decode_paged_workspace,
     tq_attn_decode_workspace,
+    tq_codebook_solver_limits,
     tq_codebook_values,
     tq_dequantize,
     tq_ip_topk,

@@ -13,7 +13,9 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libtq.so")
+# TQ_LIBRARY names another build of the same library (the sanitizer build of
+# the host sources); by default the in-tree libtq.so is loaded
+LIB_PATH = os.environ.get("TQ_LIBRARY") or os.path.join(_HERE, "libtq.so")
 
 TQ_OK, TQ_ERR_INVALID, TQ_ERR_UNSUPPORTED, TQ_ERR_HIP, TQ_ERR_ALLOC, TQ_ERR_NUMERIC = range(6)
 TQ_F32, TQ_BF16, TQ_F16 = 0, 1, 2
@@ -25,7 +27,7 @@ EXPORTS = (
     "tq_code_row_bytes", "tq_quantize_kv", "tq_attn_decode_workspace", "tq_attn_decode",
     "tq_ip_topk_workspace", "tq_ip_topk", "tq_dequantize", "tq_quantize_kv_paged",
     "tq_attn_decode_paged_workspace", "tq_attn_decode_paged", "tq_profile_enable", "tq_profile_read",
-    "tq_last_error",
+    "tq_codebook_solver_limits", "tq_last_error",
 )
 TQ_KERNEL_QUANTIZE, TQ_KERNEL_DECODE_SPLIT, TQ_KERNEL_TOPK, TQ_KERNEL_DEQUANTIZE = 0, 1, 2, 3
 
@@ -68,6 +70,7 @@ def lib() -> ctypes.CDLL:
     L.tq_codebook_destroy.argtypes = [vp]
     L.tq_codebook_export.argtypes = [vp, dp, dp, dp, dp]
     L.tq_codebook_values.argtypes = [ctypes.POINTER(tq_params), dp, dp, dp, dp]
+    L.tq_codebook_solver_limits.argtypes = [i32, i32]
     L.tq_code_row_bytes.argtypes = [vp, ctypes.POINTER(i64), ctypes.POINTER(i64)]
     L.tq_quantize_kv.argtypes = [vp, vp, vp, vp, i32, i64, i64, i64,
                                  ctypes.POINTER(tq_codes), ctypes.POINTER(tq_codes), vp]
@@ -134,6 +137,11 @@ def tq_codebook_values(d, bits, qjl_m=0, norm_correction=False, rot_seed=1, qjl_
     p = _params(d, bits, qjl_m, norm_correction, rot_seed, qjl_seed)
     _check(lib().tq_codebook_values(ctypes.byref(p), _dptr(c), _dptr(t), _dptr(r), _dptr(q)))
     return dict(centroids=c, boundaries=t, rot=r, qjl=q)
+
+
+def tq_codebook_solver_limits(lloyd_iters=0, newton_iters=0):
+    """Iteration limits of the codebook solve on this thread (0: defaults)."""
+    _check(lib().tq_codebook_solver_limits(int(lloyd_iters), int(newton_iters)))
 
 
 class Codebook:

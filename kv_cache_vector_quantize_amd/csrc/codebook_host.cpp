@@ -163,7 +163,18 @@ void half_centroids(const BetaLaw& law, const std::vector<double>& t, std::vecto
   }
 }
 
+// Iteration limits of the Lloyd-Max solve (per thread; tests shrink them to
+// reach the non-convergence error path).
+constexpr int kLloydDefault = 400000, kNewtonDefault = 80;
+thread_local int g_lloyd_iters = kLloydDefault;
+thread_local int g_newton_iters = kNewtonDefault;
+
 }  // namespace
+
+void set_solver_limits(int lloyd_iters, int newton_iters) {
+  g_lloyd_iters = lloyd_iters > 0 ? lloyd_iters : kLloydDefault;
+  g_newton_iters = newton_iters > 0 ? newton_iters : kNewtonDefault;
+}
 
 bool build_codebook_host(const tq_params& p, HostCodebook& out, std::string& err) {
   const int d = p.d, bits = p.bits, m = p.qjl_m;
@@ -182,7 +193,7 @@ bool build_codebook_host(const tq_params& p, HostCodebook& out, std::string& err
     }
     c[k] = 0.5 * (lo + hi);
   }
-  for (int it = 0; it < 400000; ++it) {
+  for (int it = 0; it < g_lloyd_iters; ++it) {
     for (int k = 1; k < h; ++k) t[k] = 0.5 * (c[k - 1] + c[k]);
     std::vector<double> cn(h);
     half_centroids(law, t, cn, mass);
@@ -197,7 +208,7 @@ bool build_codebook_host(const tq_params& p, HostCodebook& out, std::string& err
     for (int k = 1; k < h; ++k) t[k] = 0.5 * (c[k - 1] + c[k]);
     double best = INFINITY;
     std::vector<double> best_t(t);
-    for (int it = 0; it < 80; ++it) {
+    for (int it = 0; it < g_newton_iters; ++it) {
       half_centroids(law, t, c, mass);
       std::vector<double> R(n);
       double rmax = 0.0;

@@ -373,7 +373,12 @@ __global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_e
   const int b = bh / a.Hkv, h = bh % a.Hkv;
   const int64_t seq = PG ? h : bh;                          // code plane: b * Hkv + h, or pool plane h
   int64_t n_valid = a.n_ctx;
-  if (a.seq_lens) n_valid = a.seq_lens[b];
+  if (a.seq_lens) {
+    // lengths outside [0, n_ctx] are a caller error; clamping keeps every
+    // tile inside the sequence's planes
+    const int64_t lb = a.seq_lens[b];
+    n_valid = lb < 0 ? 0 : (lb < a.n_ctx ? lb : a.n_ctx);
+  }
   const int64_t t_begin = (int64_t)part * a.chunk;
   int64_t t_end = t_begin + a.chunk;
   if (t_end > n_valid) t_end = n_valid;
@@ -743,7 +748,7 @@ struct CArgs {
 // local slot t%2), the per-partial factors 2^(M_p - M) go to LDS, and thread
 // (i, c) sums coordinate i of local slot c in partial order.  Finally
 // out = Pi_V^T o~ / l with Pi_V staged in LDS.
-constexpr int kMaxWg = 1024;   // plan_decode keeps a row at <= 4096 / kWaves partials
+constexpr int kMaxWg = 1024;   // workgroup partials per row; launch_decode rejects plans beyond it
 
 __global__ void __launch_bounds__(256) k_combine(CArgs a) {
   __shared__ __align__(16) float mat[D][D];

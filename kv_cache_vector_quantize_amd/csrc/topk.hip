@@ -423,16 +423,19 @@ __global__ void __launch_bounds__(64 * kIp2Waves) k_ip_score2(IS2Args a) {
     uint32_t (&pre_i)[kIp2IdxPer] = P.i;
     uint32_t& pre_m = P.m;
     pre_m = 0u;
+    // the tile's base is formed in 64 bits (a database may exceed 2^31
+    // words); a lane's offset from it spans at most 16 rows
     const int64_t r0 = tile * 16;
+    const uint32_t* tbase = a.idx + r0 * a.rw;
 #pragma unroll
     for (int j = 0; j < kIp2IdxPer; ++j) {
       pre_i[j] = 0u;
       if (irow[j] >= 0) {
-        const int row = (int)min(r0 + irow[j], (int64_t)last);   // rows past the end repeat the last one
-        pre_i[j] = a.idx[(uint32_t)(row * a.rw + ioff[j])];
+        const int rr = (int)(min(r0 + irow[j], (int64_t)last) - r0);   // rows past the end repeat the last one
+        pre_i[j] = tbase[rr * a.rw + ioff[j]];
       }
     }
-    if (mbase) pre_m = mbase[(uint32_t)((int)min(r0 + mrow, (int64_t)last) * mstr + mw)];
+    if (mbase) pre_m = (mbase + r0 * mstr)[(int)(min(r0 + mrow, (int64_t)last) - r0) * mstr + mw];
   };
   // raw tile layout: idx rows [0, n_idx), sign rows [n_idx, n_idx + n_sgn),
   // scale [.., +16), rnorm [.., +16)

@@ -111,6 +111,9 @@ tq_status hip_fail(hipError_t e, const char* what) {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// a dtype arrives as a plain integer and is checked before it becomes a tq_dtype
+bool dtype_ok(int32_t v) { return v == TQ_F32 || v == TQ_BF16 || v == TQ_F16; }
+
 void free_dev(DeviceCodebook& d) {
   if (d.cent) (void)hipFree(d.cent);
   if (d.bnd) (void)hipFree(d.bnd);
@@ -421,6 +424,11 @@ tq_status tq_codebook_values(const tq_params* params, double* centroids, double*
   }
 }
 
+tq_status tq_codebook_solver_limits(int32_t lloyd_iters, int32_t newton_iters) {
+  set_solver_limits(lloyd_iters, newton_iters);
+  return TQ_OK;
+}
+
 tq_status tq_codebook_destroy(tq_codebook* cb) {
   if (!cb) return TQ_OK;
   free_dev(cb->dev);
@@ -528,11 +536,12 @@ tq_status check_pages(int32_t page_tokens, const int32_t* block_table, int64_t m
 extern "C" {
 
 tq_status tq_quantize_kv(const tq_codebook* kcb, const tq_codebook* vcb, const void* k,
-                         const void* v, tq_dtype dt, int64_t n_seq, int64_t n_tok,
+                         const void* v, int32_t dt_in, int64_t n_seq, int64_t n_tok,
                          int64_t tok_offset, const tq_codes* k_out, const tq_codes* v_out,
                          void* stream) {
   try {
-    if (dt != TQ_F32 && dt != TQ_BF16 && dt != TQ_F16) return fail(TQ_ERR_INVALID, "bad dtype");
+    if (!dtype_ok(dt_in)) return fail(TQ_ERR_INVALID, "bad dtype");
+    const tq_dtype dt = static_cast<tq_dtype>(dt_in);
     if (n_seq < 0 || n_tok < 0 || tok_offset < 0)
       return fail(TQ_ERR_INVALID, "n_seq, n_tok and tok_offset must be >= 0");
     if (n_seq == 0 || n_tok == 0) return TQ_OK;   // nothing is read or written
@@ -545,12 +554,13 @@ tq_status tq_quantize_kv(const tq_codebook* kcb, const tq_codebook* vcb, const v
 }
 
 tq_status tq_quantize_kv_paged(const tq_codebook* kcb, const tq_codebook* vcb, const void* k,
-                               const void* v, tq_dtype dt, int64_t B, int64_t Hkv, int64_t n_tok,
+                               const void* v, int32_t dt_in, int64_t B, int64_t Hkv, int64_t n_tok,
                                int64_t tok_offset, const int32_t* block_table, int64_t max_pages,
                                int32_t page_tokens, const tq_codes* k_pool, const tq_codes* v_pool,
                                void* stream) {
   try {
-    if (dt != TQ_F32 && dt != TQ_BF16 && dt != TQ_F16) return fail(TQ_ERR_INVALID, "bad dtype");
+    if (!dtype_ok(dt_in)) return fail(TQ_ERR_INVALID, "bad dtype");
+    const tq_dtype dt = static_cast<tq_dtype>(dt_in);
     if (B < 0 || Hkv <= 0 || n_tok < 0 || tok_offset < 0)
       return fail(TQ_ERR_INVALID, "need B, n_tok, tok_offset >= 0 and Hkv > 0");
     if (B == 0 || n_tok == 0) return TQ_OK;
@@ -580,12 +590,13 @@ tq_status tq_attn_decode_workspace(int64_t B, int64_t Hq, int64_t Hkv, int64_t n
 namespace {
 
 // Validation and launch shared by tq_attn_decode and tq_attn_decode_paged.
-tq_status decode_impl(const tq_codebook* kcb, const tq_codebook* vcb, const void* q, tq_dtype qdt, int64_t B,
+tq_status decode_impl(const tq_codebook* kcb, const tq_codebook* vcb, const void* q, int32_t qdt_in, int64_t B,
                       int64_t Hq, int64_t Hkv, const tq_codes* k, const tq_codes* v, const int32_t* seq_lens,
                       int64_t n_ctx, float sm_scale, float* out, float* logits, void* workspace,
                       size_t ws_bytes, void* stream, int64_t need_len, int page_tokens, const PageMap& pm) {
   if (!kcb || !vcb) return fail(TQ_ERR_INVALID, "codebook is NULL");
-  if (qdt != TQ_F32 && qdt != TQ_BF16 && qdt != TQ_F16) return fail(TQ_ERR_INVALID, "bad dtype");
+  if (!dtype_ok(qdt_in)) return fail(TQ_ERR_INVALID, "bad dtype");
+  const tq_dtype qdt = static_cast<tq_dtype>(qdt_in);
   if (B < 0 || Hq < 0 || Hkv <= 0 || n_ctx < 0 || Hq % Hkv)
     return fail(TQ_ERR_INVALID, "need B, n_ctx >= 0, Hkv > 0, Hq a multiple of Hkv");
   if (kcb->p.d != vcb->p.d) return fail(TQ_ERR_INVALID, "key and value codebooks differ in d");
@@ -632,7 +643,7 @@ tq_status decode_impl(const tq_codebook* kcb, const tq_codebook* vcb, const void
 extern "C" {
 
 tq_status tq_attn_decode(const tq_codebook* kcb, const tq_codebook* vcb, const void* q,
-                         tq_dtype qdt, int64_t B, int64_t Hq, int64_t Hkv, const tq_codes* k,
+                         int32_t qdt, int64_t B, int64_t Hq, int64_t Hkv, const tq_codes* k,
                          const tq_codes* v, const int32_t* seq_lens, int64_t n_ctx,
                          float sm_scale, float* out, float* logits, void* workspace,
                          size_t ws_bytes, void* stream) {
@@ -657,7 +668,7 @@ tq_status tq_attn_decode_paged_workspace(int64_t B, int64_t Hq, int64_t Hkv, int
 }
 
 tq_status tq_attn_decode_paged(const tq_codebook* kcb, const tq_codebook* vcb, const void* q,
-                               tq_dtype qdt, int64_t B, int64_t Hq, int64_t Hkv, const tq_codes* k_pool,
+                               int32_t qdt, int64_t B, int64_t Hq, int64_t Hkv, const tq_codes* k_pool,
                                const tq_codes* v_pool, const int32_t* block_table, int64_t max_pages,
                                int32_t page_tokens, const int32_t* seq_lens, int64_t n_ctx, float sm_scale,
                                float* out, float* logits, void* workspace, size_t ws_bytes, void* stream) {
@@ -721,11 +732,12 @@ tq_status tq_ip_topk(const tq_codebook* cb, const float* queries, int64_t nq,
 }
 
 tq_status tq_dequantize(const tq_codebook* cb, const tq_codes* codes, int64_t n_seq,
-                        int64_t n_tok, int64_t tok_offset, void* out, tq_dtype out_dt,
+                        int64_t n_tok, int64_t tok_offset, void* out, int32_t out_dt_in,
                         void* stream) {
   try {
     if (!cb) return fail(TQ_ERR_INVALID, "codebook is NULL");
-    if (out_dt != TQ_F32 && out_dt != TQ_BF16 && out_dt != TQ_F16) return fail(TQ_ERR_INVALID, "bad out dtype");
+    if (!dtype_ok(out_dt_in)) return fail(TQ_ERR_INVALID, "bad out dtype");
+    const tq_dtype out_dt = static_cast<tq_dtype>(out_dt_in);
     if (n_seq < 0 || n_tok < 0 || tok_offset < 0)
       return fail(TQ_ERR_INVALID, "n_seq, n_tok and tok_offset must be >= 0");
     if (n_seq == 0 || n_tok == 0) return TQ_OK;

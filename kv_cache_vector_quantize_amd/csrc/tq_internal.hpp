@@ -20,6 +20,8 @@ struct HostCodebook {
 };
 
 bool build_codebook_host(const tq_params& p, HostCodebook& out, std::string& err);
+// thread-local iteration limits of the Lloyd-Max solve (<= 0: default)
+void set_solver_limits(int lloyd_iters, int newton_iters);
 
 // Device-resident tables of one codebook.
 struct DeviceCodebook {

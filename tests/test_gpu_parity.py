@@ -84,6 +84,11 @@ def _quant_case(dev, d, bits, m, nc, dtype, n_seq, n_tok, tok_offset=0, layout=T
     (256, 3, 256, True, "bf16"),
     (160, 8, 0, False, "bf16"),
     (128, 3, 200, False, "f32"),   # sketch wider than 128 rows (wide kernel)
+    (128, 6, 128, False, "bf16"),  # wide codes with a sketch: |r| < 0.03, rnorm's |x| floor applies
+    (128, 8, 128, True, "f32"),
+    (128, 8, 64, False, "f16"),
+    (64, 7, 64, False, "f32"),     # generic kernel, wide codes with a sketch
+    (200, 8, 200, True, "bf16"),
 ])
 def test_quantize_rows_parity(dev, d, bits, m, nc, dtype):
     n_seq, n_tok = 3, 333
@@ -134,7 +139,8 @@ def test_quantize_zone_rate_large(dev, bits, layout):
 
 
 @pytest.mark.parametrize("bits,m,nc,dtype", [(3, 128, False, "bf16"), (4, 128, True, "bf16"),
-                                          (2, 96, False, "f32")])
+                                          (2, 96, False, "f32"), (6, 128, False, "bf16"),
+                                          (8, 128, True, "bf16")])
 def test_quantize_sketch_large(dev, bits, m, nc, dtype):
     """16384 vectors with outlier channels through the d = 128 key kernel
     (three-part split-bf16 rotation, two-part split-bf16 sketch): indices

@@ -123,3 +123,19 @@ def test_paged_calls_reject_bad_pages_before_device():
     st = L.tq_attn_decode_paged(None, None, None, 0, 1, 8, 1, None, None, ctypes.c_void_p(16), 1, 64, None, 100,
                                 0.1, None, None, None, 0, None)
     assert st == _lib.TQ_ERR_INVALID and b"max_pages" in L.tq_last_error()
+
+
+def test_solver_limit_forces_numeric_error():
+    # too few iterations leave the midpoint residual above 1e-12: the
+    # construction fails with TQ_ERR_NUMERIC instead of returning a codebook
+    try:
+        tq.tq_codebook_solver_limits(5, 1)
+        with pytest.raises(tq.TQError) as e:
+            tq.tq_codebook_values(128, 4)
+        assert e.value.status == _lib.TQ_ERR_NUMERIC
+        assert "converge" in str(e.value)
+    finally:
+        tq.tq_codebook_solver_limits(0, 0)
+    v = tq.tq_codebook_values(128, 4)
+    ref = O.Codebook(128, 4)
+    assert np.max(np.abs(v["centroids"] - ref.centroids)) < 1e-10

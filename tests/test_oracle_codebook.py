@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 from scipy import stats
 from scipy.integrate import quad
-from scipy.special import gammaln
+from scipy.special import betainc, betaln, gammaln
 
 import oracle as O
 
@@ -71,12 +71,16 @@ def test_lloyd_max_conditions(d, b):
     assert t[L // 2 - 1] == 0.0
     # midpoint condition
     assert np.max(np.abs(t - 0.5 * (c[:-1] + c[1:]))) < 1e-15
-    # centroid condition by independent adaptive quadrature
+    # centroid condition from closed forms (the oracle solves with quadrature):
+    # P = I_{(1+v)/2}(a, a) - I_{(1+u)/2}(a, a) and
+    # int_u^v y f_d = ((1-u^2)^a - (1-v^2)^a) / (2 a B(1/2, a)); the lower
+    # half's cells (no cancellation in P), the upper half by symmetry above
+    a = (d - 1) / 2
     edges = np.concatenate([[-1.0], t, [1.0]])
-    for k in range(L):
+    for k in range(L // 2):
         lo, hi = edges[k], edges[k + 1]
-        P = quad(lambda y: O.coord_density(y, d), lo, hi, limit=400, epsabs=1e-16, epsrel=1e-13)[0]
-        M = quad(lambda y: y * O.coord_density(y, d), lo, hi, limit=400, epsabs=1e-16, epsrel=1e-13)[0]
+        P = betainc(a, a, (1 + hi) / 2) - betainc(a, a, (1 + lo) / 2)
+        M = ((1 - lo * lo) ** a - (1 - hi * hi) ** a) / (2 * a * math.exp(betaln(0.5, a)))
         assert abs(M / P - c[k]) < 1e-10, (k, M / P, c[k])
 
 

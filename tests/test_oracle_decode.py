@@ -194,3 +194,22 @@ def test_topk_recall_high_at_8_bits():
     te, _ = O.exact_topk(qs, db, 10)
     recall = np.mean([len(set(a) & set(b)) / 10 for a, b in zip(ti, te)])
     assert recall > 0.9
+
+
+def test_exact_topk_bruteforce_with_ties():
+    # pure-Python inner products and ordering (descending, ties to the lower
+    # index) on a small database with duplicated rows
+    rng = np.random.default_rng(9)
+    d, n, k = 5, 40, 6
+    db = rng.integers(-3, 4, size=(n, d)).astype(np.float64)
+    db[17] = db[2]
+    db[30] = db[2]
+    qs = rng.integers(-2, 3, size=(4, d)).astype(np.float64)
+    qs[0] = db[2]
+    ti, ts = O.exact_topk(qs, db, k)
+    for i in range(len(qs)):
+        s = [sum(qs[i, c] * db[j, c] for c in range(d)) for j in range(n)]
+        ref = sorted(range(n), key=lambda j: (-s[j], j))[:k]
+        assert list(ti[i]) == ref
+        assert list(ts[i]) == [s[j] for j in ref]
+    assert list(ti[0][:3]) == [2, 17, 30]

@@ -137,6 +137,74 @@ def test_qjl_estimator_unbiased_over_seeds():
     assert abs(mse_only - target) > 0
 
 
+def _sketch_estimates(d, m, b, nc, x, qv, seeds, wrong_residual=False):
+    """Code inner products <q, x> over independent sketch matrices (the
+    rotation stays fixed: only S is redrawn per seed).  With
+    ``wrong_residual`` the sketch is taken of y - c[idx] instead of the
+    residual of the direction actually used (a planted mistake)."""
+    cb = O.Codebook(d, b, qjl_m=m, nc=nc)
+    ests = []
+    for s in seeds:
+        cb.qjl = O.qjl_matrix(m, d, s)
+        q = O.quantize(cb, x[None, :])
+        sign, rnorm = q["sign"], q["rnorm"]
+        if wrong_residual:
+            r = q["y"] - cb.centroids[q["idx"]]
+            sign = (r @ cb.qjl.T >= 0).astype(np.uint8)
+            rnorm = np.linalg.norm(x) * np.linalg.norm(r, axis=1)
+        ests.append(O.code_scores(cb, qv, q["idx"], q["scale"], sign, rnorm)[0])
+    return cb, np.array(ests)
+
+
+def test_qjl_estimator_unbiased_with_norm_correction():
+    # nc on: scale = n/|c[idx]| and the sketched residual is y - c[idx]/|c[idx]|,
+    # so scale <q~, c[idx]> + n <q~, r> = n <q~, y> = <q, x> exactly and the
+    # sketch term keeps the estimate unbiased.  q is correlated with x so that
+    # a residual taken against c[idx] (not c[idx]/|c[idx]|) shows its bias,
+    # n <q~, c[idx]> (1/|c[idx]| - 1), far outside the 4-sigma band.
+    d, m, b = 32, 32, 2
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal(d)
+    qv = x + 0.5 * rng.standard_normal(d)
+    seeds = range(5000, 8000)
+    cb, ests = _sketch_estimates(d, m, b, True, x, qv, seeds)
+    q0 = O.quantize(cb, x[None, :])
+    n = np.linalg.norm(x)
+    qt = cb.rot @ qv
+    c = cb.centroids[q0["idx"][0]]
+    used = c / np.linalg.norm(c)
+    r = q0["y"][0] - used
+    rho = np.linalg.norm(r)
+    assert abs(q0["scale"][0] * (qt @ c) + n * (qt @ r) - qv @ x) < 1e-10
+    var = (n * rho) ** 2 / m * (math.pi / 2 * qt @ qt - (qt @ r / rho) ** 2)
+    z = (ests.mean() - qv @ x) / math.sqrt(var / len(ests))
+    assert abs(z) < 4, z
+    assert abs(ests.var() / var - 1) < 0.15
+    # the planted mistake fails the same test
+    _, bad = _sketch_estimates(d, m, b, True, x, qv, seeds, wrong_residual=True)
+    zb = (bad.mean() - qv @ x) / math.sqrt(var / len(bad))
+    assert abs(zb) > 10, zb
+
+
+def test_dequantized_keys_match_code_scores_nc():
+    # the two-path identity with norm correction on
+    d, m = 40, 24
+    cb = O.Codebook(d, 2, qjl_m=m, nc=True)
+    rng = np.random.default_rng(13)
+    x = rng.standard_normal((60, d)) * 3
+    qv = rng.standard_normal(d)
+    q = O.quantize(cb, x)
+    xh = O.dequantize(cb, q["idx"], q["scale"], q["sign"], q["rnorm"])
+    s = O.code_scores(cb, qv, q["idx"], q["scale"], q["sign"], q["rnorm"])
+    assert np.max(np.abs(xh @ qv - s)) < 1e-11 * np.max(np.abs(s))
+    # and the residual norm is that of y - c/|c|, not of y - c
+    c = cb.centroids[q["idx"]]
+    r = q["y"] - c / np.linalg.norm(c, axis=1, keepdims=True)
+    assert np.allclose(q["rnorm"], np.linalg.norm(x, axis=1) * np.linalg.norm(r, axis=1), rtol=1e-12)
+    assert not np.allclose(q["rnorm"], np.linalg.norm(x, axis=1) * np.linalg.norm(q["y"] - c, axis=1),
+                           rtol=1e-3)
+
+
 def test_dequantized_keys_match_code_scores():
     # two paths: <q, x_hat> with explicit dequantization (incl. QJL term)
     # equals the rotated-query score taken from the codes

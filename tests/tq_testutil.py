@@ -12,8 +12,8 @@ fp32 while the oracle works in fp64):
   stay <= 1e-4 of the elements;
 * QJL sign bits: bit-exact except where |(S r)_j| < 1e-5 or the vector had
   an index mismatch;
-* scale within 2e-6 relative, rnorm within 1e-5 relative (vectors without
-  index mismatches);
+* scale within 2e-6 relative, rnorm within 1e-5 relative or 1e-6 |x|,
+  whichever is larger (vectors without index mismatches);
 * logits: per (query, head) row, max |l_gpu - l_ref| <= 1e-4 * max |l_ref|;
 * outputs: max-abs <= 2e-3.
 """
@@ -29,6 +29,7 @@ ZONE = 1e-5
 IDX_BUDGET = 1e-4
 LOGIT_RTOL = 1e-4
 OUT_ATOL = 2e-3
+RNORM_XFLOOR = 1e-6
 
 
 def oracle_codebook(cb):
@@ -144,8 +145,14 @@ def compare_quant(ocb, x64: np.ndarray, got: dict, name="", ref=None):
         smis = (gs != ref["sign"]) & vec_ok[:, None] & (np.abs(ref["u"]) >= ZONE)
         assert not smis.any(), f"{name}: {smis.sum()} sign mismatches"
         grn = got["rnorm"].reshape(-1)
-        rr = np.abs(grn - ref["rnorm"]) / np.maximum(np.abs(ref["rnorm"]), 1e-30)
-        assert np.all(rr[vec_ok] <= 1e-5), f"{name}: rnorm rel err {rr[vec_ok].max()}"
+        nx = np.sqrt(np.sum(x64 * x64, axis=1))
+        # 1e-5 relative, with a floor of 1e-6 |x|: an fp32 rotation leaves y
+        # ~3e-7 (in norm) from the fp64 one, which moves |r| by as much; for
+        # codes of >= 6 bits |r| < 0.03 and the relative bar alone is unmeetable
+        rerr = np.abs(grn - ref["rnorm"])
+        rr = rerr / np.maximum(np.abs(ref["rnorm"]), 1e-30)
+        okr = rerr <= np.maximum(1e-5 * np.abs(ref["rnorm"]), RNORM_XFLOOR * nx)
+        assert np.all(okr[vec_ok]), f"{name}: rnorm err {rerr[vec_ok & ~okr].max()}"
         stats["sign_mismatch_total"] = int((gs != ref["sign"]).sum())
         stats["rnorm_rel"] = float(rr[vec_ok].max() if vec_ok.any() else 0.0)
     stats["vec_ok"] = vec_ok
