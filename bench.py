@@ -63,6 +63,36 @@ def split_traffic():
 METRIC = "KV tokens/s in compressed decode attention & quantize GB/s, % of HBM peak"
 
 
+def spread(ms):
+    """median, p10 and p90 (milliseconds) of per-iteration times."""
+    a = np.asarray(ms, dtype=np.float64)
+    if a.size == 0:
+        return None
+    return dict(median=round(float(np.median(a)), 5), p10=round(float(np.percentile(a, 10)), 5),
+                p90=round(float(np.percentile(a, 90)), 5), n=int(a.size))
+
+
+def timed_iters(torch, fn, iters):
+    """Run fn iters times between a synchronize on either side, with an event
+    at every iteration boundary on the current stream.  Returns (mean ms over
+    the whole region, per-iteration ms list)."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(iters):
+        fn()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(iters)]
+    return ev[0].elapsed_time(ev[iters]) / iters, per
+
+
+def kernel_spread(tq, kernel):
+    """(mean ms, spread) of every recorded launch of one library kernel."""
+    d = tq.tq_profile_durations(kernel)
+    return (float(d.mean()) if d.size else 0.0), spread(d)
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -124,20 +154,13 @@ def quantize_leg(torch, tq, synth, dev, iters, warm):
         tq.tq_quantize_kv(kcb, vcb, kf, vf, kc, vc)
     torch.cuda.synchronize()
     tq.tq_profile_enable(True)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(iters):
-        tq.tq_quantize_kv(kcb, vcb, kf, vf, kc, vc)
-    e1.record()
-    torch.cuda.synchronize()
+    ms, per = timed_iters(torch, lambda: tq.tq_quantize_kv(kcb, vcb, kf, vf, kc, vc), iters)
     tq.tq_profile_enable(False)
-    kms, kn = tq.tq_profile_read(tq.TQ_KERNEL_QUANTIZE)
-    ms = e0.elapsed_time(e1) / iters
+    kern_ms, kern_spread = kernel_spread(tq, tq.TQ_KERNEL_QUANTIZE)
     n_vec = 2 * B * H * N
     in_bytes = n_vec * d * 2
     out_bytes = n_vec * (d * 4 // 8 + 4)
     gbs = (in_bytes + out_bytes) / (ms * 1e-3) / 1e9
-    kern_ms = kms / kn
     per_launch_bytes = (in_bytes + out_bytes) / 2
     flops = 2.0 * d * d * n_vec
     # the rotation runs as bf16 MFMAs on a two-part split of Pi (bf16 input,
@@ -148,7 +171,7 @@ def quantize_leg(torch, tq, synth, dev, iters, warm):
     return dict(workload="quantize-only layer: B=16, Hkv=8, d=128, 32768 tokens, bf16 K and V "
                          "(4 outlier channels/head x15), 4-bit, no QJL",
                 GB_per_s=round(gbs, 1), frac_hbm=round(gbs / HBM_PEAK_GBS, 4), ms_per_call=round(ms, 4),
-                kernel_ms=round(kern_ms, 4),
+                call_ms_spread=spread(per), kernel_ms=round(kern_ms, 4), kernel_ms_spread=kern_spread,
                 kernel_GB_per_s=round(per_launch_bytes / (kern_ms * 1e-3) / 1e9, 1),
                 rotation_TFLOP_per_s=round(flops / (ms * 1e-3) / 1e12, 2),
                 mfma_TFLOP_per_s=round(mfma_flops / (ms * 1e-3) / 1e12, 2),
@@ -170,18 +193,11 @@ def dequantize_leg(torch, tq, kcb, vcb, kc, vc, n_seq, n_tok, iters, warm):
         call()
     torch.cuda.synchronize()
     tq.tq_profile_enable(True)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(iters):
-        call()
-    e1.record()
-    torch.cuda.synchronize()
+    ms, per = timed_iters(torch, call, iters)
     tq.tq_profile_enable(False)
-    kms, kn = tq.tq_profile_read(tq.TQ_KERNEL_DEQUANTIZE)
-    ms = e0.elapsed_time(e1) / iters
+    kern_ms, kern_spread = kernel_spread(tq, tq.TQ_KERNEL_DEQUANTIZE)
     n_vec = 2 * n_seq * n_tok
     nbytes = n_vec * ((d * kcb.bits // 8 + 4) + d * 2)
-    kern_ms = kms / kn
     # Pi^T hi.hi + hi.lo + lo.hi on 32x32x16 bf16 MFMAs: three issued products
     # per useful one
     mfma_flops = 3 * 2.0 * d * d * n_vec
@@ -189,7 +205,8 @@ def dequantize_leg(torch, tq, kcb, vcb, kc, vc, n_seq, n_tok, iters, warm):
     return dict(workload=f"dequantize the quantize layer's K (row) and V (tile32) {kcb.bits}-bit codes "
                          f"to bf16: {n_vec} vectors, d={d}",
                 GB_per_s=round(nbytes / (ms * 1e-3) / 1e9, 1), frac_hbm=round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                ms_per_call=round(ms, 4), kernel_ms=round(kern_ms, 4),
+                ms_per_call=round(ms, 4), call_ms_spread=spread(per), kernel_ms=round(kern_ms, 4),
+                kernel_ms_spread=kern_spread,
                 kernel_GB_per_s=round(nbytes / 2 / (kern_ms * 1e-3) / 1e9, 1),
                 mfma_TFLOP_per_s=round(mfma_flops / (ms * 1e-3) / 1e12, 2),
                 bytes_per_call=int(nbytes))
@@ -297,23 +314,17 @@ def paged_leg(torch, tq, W, iters, warm, page_tokens=64):
         step()
     torch.cuda.synchronize()
     tq.tq_profile_enable(True)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(iters):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
+    ms, per = timed_iters(torch, step, iters)
     tq.tq_profile_enable(False)
-    ms = e0.elapsed_time(e1) / iters
-    sms, sn = tq.tq_profile_read(tq.TQ_KERNEL_DECODE_SPLIT)
-    split_ms = sms / max(1, sn)
+    split_ms, split_spread = kernel_spread(tq, tq.TQ_KERNEL_DECODE_SPLIT)
     diff = float((out - W["out"]).abs().max() / W["out"].abs().max())
     del kp, vp, ws
     alg = W["bytes_per_token_head"] * B * Hkv * N
     return dict(workload=f"decode-128k GQA layer on a paged cache: {page_tokens}-position pages, "
                          f"{n_pages} pages per KV head placed by a shuffled block table",
                 KV_tokens_per_s=round(B * N / (ms * 1e-3), 1), ms_per_step=round(ms, 5),
-                split_kernel_ms=round(split_ms, 5), split_GBps=round(alg / (split_ms * 1e-3) / 1e9, 1),
+                step_ms_spread=spread(per), split_kernel_ms=round(split_ms, 5),
+                split_kernel_ms_spread=split_spread, split_GBps=round(alg / (split_ms * 1e-3) / 1e9, 1),
                 frac_hbm=round(alg / (split_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                 max_rel_diff_vs_contiguous=round(diff, 7))
 
@@ -371,20 +382,15 @@ def bit_sweep_leg(torch, tq, synth, dev, iters, warm):
             tq.tq_attn_decode(kcb, vcb, q, kc, vc, N, tau, out=out, workspace=ws)
         torch.cuda.synchronize()
         tq.tq_profile_enable(True)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(iters):
-            tq.tq_attn_decode(kcb, vcb, q, kc, vc, N, tau, out=out, workspace=ws)
-        e1.record()
-        torch.cuda.synchronize()
+        ms, per = timed_iters(torch, lambda: tq.tq_attn_decode(kcb, vcb, q, kc, vc, N, tau, out=out,
+                                                               workspace=ws), iters)
         tq.tq_profile_enable(False)
-        ms = e0.elapsed_time(e1) / iters
-        sms, sn = tq.tq_profile_read(tq.TQ_KERNEL_DECODE_SPLIT)
-        split_ms = sms / max(1, sn)
+        split_ms, split_spread = kernel_spread(tq, tq.TQ_KERNEL_DECODE_SPLIT)
         bpt = kb * d // 8 + 4 + vb * d // 8 + 4
         gbs = bpt * B * Hkv * N / (split_ms * 1e-3) / 1e9
         res.append(dict(variant=name, KV_tokens_per_s=round(B * N / (ms * 1e-3), 1),
-                        ms_per_decode=round(ms, 4), split_kernel_ms=round(split_ms, 4),
+                        ms_per_decode=round(ms, 4), decode_ms_spread=spread(per),
+                        split_kernel_ms=round(split_ms, 4), split_kernel_ms_spread=split_spread,
                         bytes_per_token_head=bpt, split_GBps=round(gbs, 1),
                         frac_hbm=round(gbs / HBM_PEAK_GBS, 4),
                         **{kk: round(vv, 6) for kk, vv in errs.items()}))
@@ -413,23 +419,31 @@ def vector_search_leg(torch, tq, synth, dev, iters, warm):
     c1.record()
     torch.cuda.synchronize()
     quant_ms = c0.elapsed_time(c1)
+    # the 133 MB of codes fit the 256 MB last-level cache: the timed calls
+    # rotate over three copies, so each call reads its codes from HBM
+    copies = [codes]
+    for _ in range(2):
+        c2 = tq.Codes(cb, 1, n_db, tq.TQ_LAYOUT_ROW)
+        for name in ("idx", "sign", "scale", "rnorm"):
+            getattr(c2, name).copy_(getattr(codes, name))
+        copies.append(c2)
     ws = torch.empty(tq.tq_ip_topk_workspace(nq, n_db, k, d), dtype=torch.uint8, device=dev)
     gi = torch.empty((nq, k), dtype=torch.int64, device=dev)
     gs = torch.empty((nq, k), dtype=torch.float32, device=dev)
+    ctr = [0]
+
+    def call():
+        c = copies[ctr[0] % len(copies)]
+        ctr[0] += 1
+        tq.tq_ip_topk(cb, qs, c, n_db, k, out_idx=gi, out_score=gs, workspace=ws)
     for _ in range(warm):
-        tq.tq_ip_topk(cb, qs, codes, n_db, k, out_idx=gi, out_score=gs, workspace=ws)
+        call()
     torch.cuda.synchronize()
     tq.tq_profile_enable(True)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(iters):
-        tq.tq_ip_topk(cb, qs, codes, n_db, k, out_idx=gi, out_score=gs, workspace=ws)
-    e1.record()
-    torch.cuda.synchronize()
+    ms, per = timed_iters(torch, call, iters)
     tq.tq_profile_enable(False)
-    ms = e0.elapsed_time(e1) / iters
-    sms, sn = tq.tq_profile_read(tq.TQ_KERNEL_TOPK)
-    score_ms = sms / max(1, sn)
+    score_ms, score_spread = kernel_spread(tq, tq.TQ_KERNEL_TOPK)
+    # the last call's results are those of the first copy's codes (identical)
     # MFMA work the score kernel issues: per 8-query block and 16-row tile,
     # dp/16 centroid MFMAs and ceil(m/32) sign MFMAs of 16x16x32 (16384 flop)
     dp = (d + 31) // 32 * 32
@@ -448,17 +462,37 @@ def vector_search_leg(torch, tq, synth, dev, iters, warm):
         ex_i = torch.gather(alli, 1, pos)
     hit = (gi[:, :, None] == ex_i[:, None, :]).any(dim=2).sum().item()
     hit1 = (gi == ex_i[:, :1]).any(dim=1).sum().item()
-    del db, codes
+    del db, codes, copies
     return dict(workload="vector search: 1e6 unit-norm vectors d=200 (256-cluster mixture), "
-                         "4-bit + QJL m=200, 1000 queries, top-10",
+                         "4-bit + QJL m=200, 1000 queries, top-10; timed calls rotate over 3 copies "
+                         "of the codes (399 MB > the 256 MB last-level cache)",
                 queries_per_s=round(nq / (ms * 1e-3), 1), ms_per_call=round(ms, 4),
-                score_kernel_ms=round(score_ms, 4),
+                call_ms_spread=spread(per), score_kernel_ms=round(score_ms, 4),
+                score_kernel_ms_spread=score_spread,
                 mfma_TFLOPs=round(mfma_tflops, 1),
                 mfma_frac_bf16_peak=round(mfma_tflops / 2500.0, 4),
                 useful_TFLOPs=round(useful / (ms * 1e-3) / 1e12, 1),
                 recall_10_at_10=round(hit / (nq * k), 4),
                 recall_1_at_10=round(hit1 / nq, 4),
                 quantize_db_ms=round(quant_ms, 3))
+
+
+def host_info():
+    """Host CPU model and logical core count (the oracle's machine)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count()
+    return dict(host_nproc=os.cpu_count(), host_cpus_available=avail, cpu_model=model)
 
 
 def cpu_baseline(torch, O, W, budget_s=10.0):
@@ -474,6 +508,7 @@ def cpu_baseline(torch, O, W, budget_s=10.0):
     pairs = [(int(x) // Hkv, int(x) % Hkv) for x in order]
     q64 = W["q"].float().cpu().numpy().astype(np.float64)
     t_total = 0.0
+    cpu_total = 0.0
     done = 0
     for (b, h) in pairs:
         if t_total >= budget_s:
@@ -484,15 +519,20 @@ def cpu_baseline(torch, O, W, budget_s=10.0):
         rk = O.quantize(okc, k64[:N - 1])          # cache build (untimed)
         rv = O.quantize(ovc, v64[:N - 1])
         t0 = time.perf_counter()
+        p0 = time.process_time()
         nk = O.quantize(okc, k64[N - 1:])
         nv = O.quantize(ovc, v64[N - 1:])
         kd = {n: np.concatenate([rk[n], nk[n]])[None, None] for n in ("idx", "scale", "sign", "rnorm")}
         vd = {n: np.concatenate([rv[n], nv[n]])[None, None] for n in ("idx", "scale")}
         O.attn_decode(okc, ovc, q64[b:b + 1, h * g:(h + 1) * g], kd, vd, W["tau"])
         t_total += time.perf_counter() - t0
+        cpu_total += time.process_time() - p0
     kv_tokens = done * N / Hkv               # each pair is 1/Hkv of a batch row
     return dict(value=round(kv_tokens / t_total, 1), unit="KV tokens/s", cores=int(threads),
-                kind="oracle",
+                kind="oracle", **host_info(),
+                cores_busy=round(cpu_total / t_total, 2),
+                cores_note="cores: the BLAS threads the oracle's numpy products may use; cores_busy: "
+                           "process CPU time over wall time in the timed region",
                 sample=f"{done} of {B * Hkv} (batch, KV head) pairs of the decode-128k layer at "
                        f"full context {N}, all {g} query heads each, float64; "
                        f"{t_total:.1f} s of CPU time, scaled to KV tokens/s")
@@ -575,17 +615,9 @@ def main():
     torch.cuda.synchronize()
     print("[bench] timing", args.steps, "steps", file=sys.stderr, flush=True)
     tq.tq_profile_enable(True)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(args.steps):
-        W["step"]()
-    e1.record()
-    torch.cuda.synchronize()
+    ms_step, step_per = timed_iters(torch, W["step"], args.steps)
     tq.tq_profile_enable(False)
-    ms_step = e0.elapsed_time(e1) / args.steps
-    split_ms, split_n = tq.tq_profile_read(tq.TQ_KERNEL_DECODE_SPLIT)
-    split_avg = split_ms / max(1, split_n)
+    split_avg, split_spread = kernel_spread(tq, tq.TQ_KERNEL_DECODE_SPLIT)
     B, Hkv, N = W["B"], W["Hkv"], W["N"]
     value = B * N / (ms_step * 1e-3)
     alg_bytes = W["bytes_per_token_head"] * B * Hkv * N
@@ -598,6 +630,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
+        "step_ms_spread": spread(step_per),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -613,24 +646,23 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": split_traffic(),
             "kernel_ms": round(split_avg, 5),
+            "kernel_ms_spread": split_spread,
             "algorithmic_bytes_per_launch": int(alg_bytes),
         },
     }
     if not args.no_paged:
         print("[bench] paged-cache leg", file=sys.stderr, flush=True)
-        res["paged"] = paged_leg(torch, tq, W, iters=max(5, args.steps // 2), warm=max(1, args.warmup // 2))
+        res["paged"] = paged_leg(torch, tq, W, iters=args.steps, warm=args.warmup)
     if not args.no_quantize:
         print("[bench] quantize leg", file=sys.stderr, flush=True)
-        res["quantize"] = quantize_leg(torch, tq, synth, dev, iters=max(5, args.steps // 2),
-                                       warm=max(1, args.warmup // 2))
+        res["quantize"] = quantize_leg(torch, tq, synth, dev, iters=args.steps, warm=args.warmup)
     if not args.no_sweep:
         print("[bench] bit-width sweep leg", file=sys.stderr, flush=True)
-        res["bit_sweep"] = bit_sweep_leg(torch, tq, synth, dev, iters=max(5, args.steps // 2),
-                                         warm=max(1, args.warmup // 2))
+        res["bit_sweep"] = bit_sweep_leg(torch, tq, synth, dev, iters=args.steps, warm=args.warmup)
     if not args.no_search:
         print("[bench] vector-search leg", file=sys.stderr, flush=True)
-        res["vector_search"] = vector_search_leg(torch, tq, synth, dev, iters=max(3, args.steps // 5),
-                                                 warm=max(1, args.warmup // 5))
+        res["vector_search"] = vector_search_leg(torch, tq, synth, dev, iters=max(10, args.steps // 2),
+                                                 warm=max(2, args.warmup // 2))
     # codebook construction (host, float64 Lloyd-Max + QR + sketch, then the
     # device tables), once per (d, bits, m, seeds) in a serving process
     cbt = {}
@@ -656,7 +688,17 @@ def main():
     c1.record()
     torch.cuda.synchronize()
     res["copy_GBps"] = round(2 * (1 << 30) * n_copy / (c0.elapsed_time(c1) * 1e-3) / 1e9, 1)
-    del src, dst
+    del dst
+    # streaming-read ceiling: a kernel that only reads 1 GiB (median of 20)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    for _ in range(3):
+        tq.tq_stream_read(src, sink)
+    _, rper = timed_iters(torch, lambda: tq.tq_stream_read(src, sink), 20)
+    rmed = float(np.median(rper))
+    res["read_GBps"] = round((1 << 30) / (rmed * 1e-3) / 1e9, 1)
+    res["read_ms_spread"] = spread(rper)
+    res["roofline"]["frac_of_read_ceiling"] = round(res["roofline"]["achieved"] / res["read_GBps"], 4)
+    del src, sink
     if not args.no_ab:
         print("[bench] dequantize-then-attend leg", file=sys.stderr, flush=True)
         res["dequant_then_attend"] = dequant_attend_leg(torch, tq, W, iters=max(3, args.steps // 5),

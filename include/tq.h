@@ -308,6 +308,19 @@ typedef enum {
 tq_status tq_profile_enable(int32_t on);
 tq_status tq_profile_read(int32_t kernel, double* total_ms, int64_t* launches);
 
+/* The same records one launch at a time: ms[i] (HOST buffer of capacity
+ * entries) receives the elapsed milliseconds of launch i, for the first
+ * min(capacity, launches) launches; *launches (may be NULL) the count. */
+tq_status tq_profile_durations(int32_t kernel, double* ms, int64_t capacity, int64_t* launches);
+
+/* Measurement helper (not part of the method): enqueues a kernel that only
+ * reads `bytes` bytes of buf (device, 16-byte aligned, bytes a multiple of
+ * 16) with 16-byte loads and writes sink[0] (device uint32) only when the XOR
+ * of everything read equals a fixed value.  Its rate is the device's
+ * streaming-read ceiling, the bound every memory-bound kernel here is read
+ * against.  Errors: TQ_ERR_INVALID, TQ_ERR_HIP. */
+tq_status tq_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream);
+
 /* Message of the last failing call on this thread ("" if none). */
 const char* tq_last_error(void);
 

@@ -27,7 +27,7 @@ EXPORTS = (
     "tq_code_row_bytes", "tq_quantize_kv", "tq_attn_decode_workspace", "tq_attn_decode",
     "tq_ip_topk_workspace", "tq_ip_topk", "tq_dequantize", "tq_quantize_kv_paged",
     "tq_attn_decode_paged_workspace", "tq_attn_decode_paged", "tq_profile_enable", "tq_profile_read",
-    "tq_codebook_solver_limits", "tq_last_error",
+    "tq_codebook_solver_limits", "tq_profile_durations", "tq_stream_read", "tq_last_error",
 )
 TQ_KERNEL_QUANTIZE, TQ_KERNEL_DECODE_SPLIT, TQ_KERNEL_TOPK, TQ_KERNEL_DEQUANTIZE = 0, 1, 2, 3
 
@@ -90,6 +90,8 @@ def lib() -> ctypes.CDLL:
                                        vp, vp, vp, ctypes.c_size_t, vp]
     L.tq_profile_enable.argtypes = [i32]
     L.tq_profile_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
+    L.tq_profile_durations.argtypes = [i32, dp, i64, ctypes.POINTER(i64)]
+    L.tq_stream_read.argtypes = [vp, i64, vp, vp]
     for name in EXPORTS:
         if name != "tq_last_error":
             getattr(L, name).restype = ctypes.c_int
@@ -387,3 +389,20 @@ def tq_profile_read(kernel: int):
     ms, n = ctypes.c_double(), ctypes.c_int64()
     _check(lib().tq_profile_read(int(kernel), ctypes.byref(ms), ctypes.byref(n)))
     return ms.value, n.value
+
+
+def tq_profile_durations(kernel: int):
+    """Milliseconds of every recorded launch of one kernel id (numpy array)."""
+    n = ctypes.c_int64()
+    _check(lib().tq_profile_durations(int(kernel), None, 0, ctypes.byref(n)))
+    ms = np.zeros(max(1, n.value))
+    _check(lib().tq_profile_durations(int(kernel), _dptr(ms), n.value, ctypes.byref(n)))
+    return ms[:n.value]
+
+
+def tq_stream_read(buf, sink, stream=None):
+    """Enqueue a read-only pass over the device tensor ``buf`` (its byte size
+    a multiple of 16); ``sink`` is a device tensor of >= 4 bytes."""
+    nbytes = buf.numel() * buf.element_size()
+    _check(lib().tq_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes, ctypes.c_void_p(sink.data_ptr()),
+                                _stream_handle(stream)))

@@ -771,6 +771,33 @@ tq_status tq_profile_enable(int32_t on) {
   return TQ_OK;
 }
 
+tq_status tq_profile_durations(int32_t kernel, double* ms, int64_t capacity, int64_t* launches) {
+  if (kernel < 0 || kernel > 3) return fail(TQ_ERR_INVALID, "unknown kernel id");
+  if (capacity < 0 || (capacity > 0 && !ms)) return fail(TQ_ERR_INVALID, "ms is NULL");
+  int64_t i = 0;
+  for (auto& p : g_prof.rec[kernel]) {
+    if (i >= capacity) break;
+    hipError_t e = hipEventSynchronize(p.b);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    float v = 0.f;
+    e = hipEventElapsedTime(&v, p.a, p.b);
+    if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+    ms[i++] = v;
+  }
+  if (launches) *launches = (int64_t)g_prof.rec[kernel].size();
+  return TQ_OK;
+}
+
+tq_status tq_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {
+  if (bytes < 0 || bytes % 16) return fail(TQ_ERR_INVALID, "bytes must be a non-negative multiple of 16");
+  if (bytes == 0) return TQ_OK;
+  if (!buf || !sink) return fail(TQ_ERR_INVALID, "buf and sink must be non-NULL");
+  if (!aligned(buf, 16)) return fail(TQ_ERR_INVALID, "buf must be 16-byte aligned");
+  hipError_t e = launch_stream_read(buf, bytes, sink, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "stream read launch");
+  return TQ_OK;
+}
+
 tq_status tq_profile_read(int32_t kernel, double* total_ms, int64_t* launches) {
   if (kernel < 0 || kernel > 3) return fail(TQ_ERR_INVALID, "unknown kernel id");
   double tot = 0.0;

@@ -442,6 +442,62 @@ def test_decode_full_size_128k(dev):
     print(worst)
 
 
+@pytest.mark.parametrize("kb,vb,nc", [(8, 4, True), (4, 4, True), (3, 4, True), (3, 3, True),
+                                      (2, 2, True), (2, 2, False)])
+def test_decode_bit_sweep_full_shape(dev, kb, vb, nc):
+    """Every variant of the bit-width sweep at the shape and in the launch
+    configuration the benchmark times it (B=32, Hq=32, Hkv=4, d=128,
+    N=32768: 16 waves per row, 2048 tokens = 64 tiles per wave, so both
+    register buffers of the tile pipeline and the multi-tile online softmax
+    run).  The GPU quantizes the whole cache; the oracle's codes replace two
+    sampled sequences, whose keys carry planted tokens aligned with a query
+    (logits ~25, ~40, ~60 at tiles 21, 40 and 59 of one wave's chunk, each
+    more than 2^8 above the running maximum in base 2), so the lazy maximum
+    moves mid-chunk, on both buffers.  Logits and outputs of the sampled rows
+    meet the bars against the oracle's decode of the same codes."""
+    B, Hq, Hkv, N, d = 32, 32, 4, 32768, 128
+    g = Hq // Hkv
+    _say("decode bit sweep full shape", kb, vb, nc)
+    kcb, vcb, S, k, v, q = _decode_setup(dev, B, Hkv, Hq, N, kb, 0, nc, vb, nc, seed=20)
+    kc = tq.Codes(kcb, B * Hkv, S, TQ_LAYOUT_ROW)
+    vc = tq.Codes(vcb, B * Hkv, S, TQ_LAYOUT_TILE32)
+    tq.tq_quantize_kv(kcb, vcb, k.view(B * Hkv, N, d), v.view(B * Hkv, N, d), kc, vc)
+    okc, ovc = U.oracle_codebook(kcb), U.oracle_codebook(vcb)
+    tau = 1.0 / math.sqrt(d)
+    q64 = U.to_f64(q)
+    chunk0 = 3 * 2048                           # the chunk of wave 3 of each row
+    refs = {}
+    for b, h in [(0, 0), (B - 1, Hkv - 1)]:
+        k64 = U.to_f64(k[b, h])
+        qa = q64[b, h * g]                        # first query head of the group
+        for off, target in ((700, 25.0), (1300, 40.0), (1900, 60.0)):
+            kk = qa * (target / (tau * (qa @ qa)))
+            k64[chunk0 + off] = torch.tensor(kk, dtype=torch.float32).to(torch.bfloat16).double().numpy()
+        rk = O.quantize(okc, k64)
+        rv = O.quantize(ovc, U.to_f64(v[b, h]))
+        U.upload_oracle_codes(kc, b * Hkv + h, rk, N)
+        U.upload_oracle_codes(vc, b * Hkv + h, rv, N)
+        refs[(b, h)] = (rk, rv)
+    torch.cuda.synchronize()
+    ws = torch.empty(tq.tq_attn_decode_workspace(B, Hq, Hkv, N, d), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    lg_t = torch.full((B, Hq, N), 123.0, dtype=torch.float32, device=dev)
+    tq.tq_attn_decode(kcb, vcb, q, kc, vc, N, tau, out=out, logits=lg_t, workspace=ws)
+    torch.cuda.synchronize()
+    out_np = out.cpu().numpy()
+    assert np.all(np.isfinite(out_np))
+    worst = {}
+    for (b, h), (rk, rv) in refs.items():
+        heads = slice(h * g, (h + 1) * g)
+        lg_gpu = lg_t[b, heads].cpu().numpy()[None]
+        assert lg_gpu[0, 0, chunk0 + 1900] > 50.0, "planted logit missing"
+        st = U.check_decode(okc, ovc, q64[b:b + 1, heads], U.oracle_cache([rk], 1, 1, N, False),
+                            U.oracle_cache([rv], 1, 1, N, False), tau, lg_gpu, out_np[b:b + 1, heads],
+                            name=f"k{kb}v{vb} ({b},{h})")
+        worst[(b, h)] = st
+    print(worst)
+
+
 def test_quantize_and_dequantize_full_size(dev):
     """The quantize layer at full size and in the launch configuration the
     benchmark times: B=16, Hkv=8, 32768 tokens, d=128, bf16 K and V with 4
