@@ -197,6 +197,26 @@ tq_status tq_attn_decode(const tq_codebook* kcb, const tq_codebook* vcb, const v
                          float sm_scale, float* out, float* logits, void* workspace,
                          size_t ws_bytes, void* stream);
 
+/* tq_attn_decode for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same computation, arguments, results and errors as tq_attn_decode, but
+ * with no workspace argument: the scratch it needs (the rotated query
+ * operands and the split partials, the same bytes tq_attn_decode_workspace
+ * reports) lives in a fixed 8 MiB device array inside the library, one per
+ * device, kept until the process ends.  The call allocates nothing and
+ * records no profiling events.
+ *  - Shapes whose scratch exceeds 8 MiB fail with TQ_ERR_UNSUPPORTED before
+ *    anything is enqueued (the 128K layer, B=8, Hq=64, Hkv=8, needs 1.9 MB).
+ *  - Every call on a device uses that device's one array, which keeps the
+ *    last call's contents (no part of it needs to start zeroed).  Calls
+ *    ordered on one stream are safe; calls that may overlap in time on one
+ *    device (several streams or threads) race and give wrong results.
+ *  - The array's address is looked up on the first call on each device. */
+tq_status tq_attn_decode_noalloc(const tq_codebook* kcb, const tq_codebook* vcb, const void* q,
+                                 int32_t qdt, int64_t B, int64_t Hq, int64_t Hkv, const tq_codes* k,
+                                 const tq_codes* v, const int32_t* seq_lens, int64_t n_ctx,
+                                 float sm_scale, float* out, float* logits, void* stream);
+
 /* ---- Paged pools.  A serving engine keeps its cache in fixed-size pages
  * (the pages present TurboQuant as a KV-cache dtype of such an engine,
  * [VLLM] A3 方法细节, quantized at every cache update, [WIT] 如何实现

@@ -27,7 +27,8 @@ EXPORTS = (
     "tq_code_row_bytes", "tq_quantize_kv", "tq_attn_decode_workspace", "tq_attn_decode",
     "tq_ip_topk_workspace", "tq_ip_topk", "tq_dequantize", "tq_quantize_kv_paged",
     "tq_attn_decode_paged_workspace", "tq_attn_decode_paged", "tq_profile_enable", "tq_profile_read",
-    "tq_codebook_solver_limits", "tq_profile_durations", "tq_stream_read", "tq_last_error",
+    "tq_codebook_solver_limits", "tq_profile_durations", "tq_stream_read", "tq_attn_decode_noalloc",
+    "tq_last_error",
 )
 TQ_KERNEL_QUANTIZE, TQ_KERNEL_DECODE_SPLIT, TQ_KERNEL_TOPK, TQ_KERNEL_DEQUANTIZE = 0, 1, 2, 3
 
@@ -78,6 +79,8 @@ def lib() -> ctypes.CDLL:
     L.tq_attn_decode.argtypes = [vp, vp, vp, i32, i64, i64, i64, ctypes.POINTER(tq_codes),
                                  ctypes.POINTER(tq_codes), vp, i64, ctypes.c_float, vp, vp, vp,
                                  ctypes.c_size_t, vp]
+    L.tq_attn_decode_noalloc.argtypes = [vp, vp, vp, i32, i64, i64, i64, ctypes.POINTER(tq_codes),
+                                         ctypes.POINTER(tq_codes), vp, i64, ctypes.c_float, vp, vp, vp]
     L.tq_ip_topk_workspace.argtypes = [i64, i64, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
     L.tq_ip_topk.argtypes = [vp, vp, i64, ctypes.POINTER(tq_codes), i64, i32, vp, vp, vp,
                              ctypes.c_size_t, vp]
@@ -289,6 +292,24 @@ def tq_attn_decode(kcb, vcb, q, k_codes: Codes, v_codes: Codes, n_ctx: int, sm_s
         ctypes.byref(vd), seq_lens.data_ptr() if seq_lens is not None else None, int(n_ctx),
         float(sm_scale), out.data_ptr(), logits.data_ptr() if logits is not None else None,
         workspace.data_ptr(), workspace.numel(), _stream_handle(stream)))
+    return out
+
+
+def tq_attn_decode_noalloc(kcb, vcb, q, k_codes: Codes, v_codes: Codes, n_ctx: int, sm_scale: float,
+                           seq_lens=None, out=None, logits=None, stream=None):
+    """tq_attn_decode without a workspace (the library's fixed per-device
+    scratch).  ``out`` must be given by callers that cannot allocate."""
+    import torch
+    B, Hq, d = q.shape
+    Hkv = k_codes.n_seq // B
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    kd, vd = k_codes.descriptor(), v_codes.descriptor()
+    _check(lib().tq_attn_decode_noalloc(
+        kcb.handle, vcb.handle, q.data_ptr(), _dtype_code(q), B, Hq, Hkv, ctypes.byref(kd),
+        ctypes.byref(vd), seq_lens.data_ptr() if seq_lens is not None else None, int(n_ctx),
+        float(sm_scale), out.data_ptr(), logits.data_ptr() if logits is not None else None,
+        _stream_handle(stream)))
     return out
 
 

@@ -655,6 +655,33 @@ tq_status tq_attn_decode(const tq_codebook* kcb, const tq_codebook* vcb, const v
   }
 }
 
+tq_status tq_attn_decode_noalloc(const tq_codebook* kcb, const tq_codebook* vcb, const void* q,
+                                 int32_t qdt, int64_t B, int64_t Hq, int64_t Hkv, const tq_codes* k,
+                                 const tq_codes* v, const int32_t* seq_lens, int64_t n_ctx,
+                                 float sm_scale, float* out, float* logits, void* stream) {
+  try {
+    if (B < 0 || Hq < 0 || Hkv <= 0 || n_ctx < 0 || Hq % Hkv)
+      return fail(TQ_ERR_INVALID, "need B, n_ctx >= 0, Hkv > 0, Hq a multiple of Hkv");
+    const size_t need = plan_decode(B, Hq, Hkv, n_ctx, 128).bytes;
+    if (need > kNoallocScratchBytes)
+      return fail(TQ_ERR_UNSUPPORTED, "tq_attn_decode_noalloc: this shape needs " + std::to_string(need) +
+                                          " bytes of scratch, above the fixed " +
+                                          std::to_string(kNoallocScratchBytes) + "; use tq_attn_decode");
+    void* ws = nullptr;
+    hipError_t e = noalloc_scratch(&ws);
+    if (e != hipSuccess) return hip_fail(e, "scratch address");
+    // no profiling events either: this path creates nothing
+    const bool prof = g_prof.on;
+    g_prof.on = false;
+    tq_status s = decode_impl(kcb, vcb, q, qdt, B, Hq, Hkv, k, v, seq_lens, n_ctx, sm_scale, out, logits, ws,
+                              kNoallocScratchBytes, stream, n_ctx, 0, PageMap{});
+    g_prof.on = prof;
+    return s;
+  } catch (...) {
+    return fail(TQ_ERR_ALLOC, "tq_attn_decode_noalloc: unexpected exception");
+  }
+}
+
 tq_status tq_attn_decode_paged_workspace(int64_t B, int64_t Hq, int64_t Hkv, int64_t n_ctx, int32_t d,
                                          int32_t page_tokens, size_t* bytes) {
   if (!bytes) return fail(TQ_ERR_INVALID, "bytes is NULL");

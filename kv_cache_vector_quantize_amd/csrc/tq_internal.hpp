@@ -207,6 +207,11 @@ hipError_t launch_topk(const tq_codebook* cb, const float* queries, const TopkPl
                        const tq_codes& db, int64_t* out_idx, float* out_score, void* ws,
                        hipStream_t stream);
 
+// Allocation-free decode: the fixed per-device scratch array (bytes) and its
+// device address on the current device (looked up on the first call there).
+constexpr size_t kNoallocScratchBytes = 8u << 20;
+hipError_t noalloc_scratch(void** out);
+
 // Streaming read of bytes (a multiple of 16) of buf; writes sink[0] only
 // in the rare case that the XOR of the data equals a fixed value.
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t stream);
