@@ -9,3 +9,4 @@ common module is ``synth`` (seeded random inputs, none of the method's
 arithmetic).
 """
 from .tq_oracle import *  # noqa: F401,F403
+from . import polar_oracle as polar  # noqa: F401

@@ -116,12 +116,12 @@ def _density_scalar(d: int):
     return f
 
 
-def _cell_integrals(edges, d):
-    """Mass P_k = int f_d and first moment M_k = int y f_d over each cell
-    [edges[k], edges[k+1]], by adaptive Gauss-Kronrod quadrature (QUADPACK
-    through scipy.integrate.quad) of the density itself: no antiderivative,
-    no incomplete-beta function."""
-    f = _density_scalar(d)
+def _cell_integrals(edges, f):
+    """Mass P_k = int f and first moment M_k = int y f over each cell
+    [edges[k], edges[k+1]] of a density f (a float function of one point),
+    by adaptive Gauss-Kronrod quadrature (QUADPACK through
+    scipy.integrate.quad) of the density itself: no antiderivative, no
+    incomplete-beta function."""
     n = len(edges) - 1
     P, M = np.empty(n), np.empty(n)
     for k in range(n):
@@ -131,55 +131,36 @@ def _cell_integrals(edges, d):
     return P, M
 
 
-# ---------------------------------------------------------------------------
-# R2: Lloyd-Max for f_d ([WIT] 第一阶段 item 2; 如何实现 item 1)
-# ---------------------------------------------------------------------------
-
-
-_LM_CACHE: dict = {}
-
-
-def lloyd_max(d: int, bits: int):
-    """Cached :func:`lloyd_max_solve` (a pure function of d and bits)."""
-    key = (int(d), int(bits))
-    if key not in _LM_CACHE:
-        _LM_CACHE[key] = lloyd_max_solve(*key)
-    c, t = _LM_CACHE[key]
-    return c.copy(), t.copy()
-
-
-def lloyd_max_solve(d: int, bits: int, *, max_newton: int = 100):
-    """Lloyd-Max quantizer of f_d with L = 2^bits levels.
+def symmetric_lloyd_max(f, lo: float, mid: float, start, *, max_newton: int = 100, what: str = ""):
+    """Lloyd-Max quantizer with L = 2 len(start) levels of a density f on
+    [lo, 2 mid - lo] that is symmetric about mid.
 
     The quantizer is the one whose boundaries are the midpoints of adjacent
     centroids and whose centroids are the conditional means of their cells
-    (unique, f_d being log-concave).  By symmetry only the cells inside
-    [-1, 0] are solved, with inner boundaries t_1..t_{h-1} (h = L/2) and
-    t_h = 0; the upper half is the mirror image.  The boundaries are found by
-    damped Newton steps on the midpoint residual
+    (unique for a log-concave f).  By symmetry only the cells inside
+    [lo, mid] are solved, with inner boundaries t_1..t_{h-1} (h = L/2) and
+    t_h = mid; the upper half is the mirror image.  The boundaries are found
+    by damped Newton steps on the midpoint residual
         R_k(t) = t_k - (c_{k-1}(t) + c_k(t)) / 2,   c_k(t) = M_k / P_k,
-    started from the cell-centre quantiles of the law; cell masses and
-    moments come from adaptive quadrature, and dc_k/dt of a cell edge from
-    the density there.  Returns (centroids[L], boundaries[L-1]) in float64,
-    increasing, with the middle boundary exactly 0.
+    started from the midpoints of ``start`` (lower-half centroid guesses,
+    increasing); cell masses and moments come from adaptive quadrature, and
+    dc_k/dt of a cell edge from the density there.  Returns
+    (centroids[L], boundaries[L-1]) in float64, increasing, with the middle
+    boundary exactly mid.
     """
-    if not 1 <= bits <= 8:
-        raise ValueError("bits must be in 1..8")
-    L = 1 << bits
-    h = L // 2
-    a = beta_alpha(d)
-    f = _density_scalar(d)
+    start = np.asarray(start, dtype=np.float64)
+    h = len(start)
+    L = 2 * h
 
     def centroids_of(t):
-        edges = np.concatenate([[-1.0], t, [0.0]])
-        P, M = _cell_integrals(edges, d)
+        edges = np.concatenate([[lo], t, [mid]])
+        P, M = _cell_integrals(edges, f)
         return edges, P, M / P
 
     if h == 1:
         _, _, c = centroids_of(np.empty(0))
     else:
-        q = 2.0 * betaincinv(a, a, (np.arange(h) + 0.5) / L) - 1.0
-        t = 0.5 * (q[:-1] + q[1:])
+        t = 0.5 * (start[:-1] + start[1:])
         edges, P, c = centroids_of(t)
         R = t - 0.5 * (c[:-1] + c[1:])
         r = np.max(np.abs(R))
@@ -200,7 +181,7 @@ def lloyd_max_solve(d: int, bits: int, *, max_newton: int = 100):
             lam, accepted = 1.0, False
             while lam >= 2.0 ** -20:
                 tn = t - lam * step
-                if np.all(np.diff(np.concatenate([[-1.0], tn, [0.0]])) > 0):
+                if np.all(np.diff(np.concatenate([[lo], tn, [mid]])) > 0):
                     en, Pn, cn = centroids_of(tn)
                     Rn = tn - 0.5 * (cn[:-1] + cn[1:])
                     rn = np.max(np.abs(Rn))
@@ -211,12 +192,42 @@ def lloyd_max_solve(d: int, bits: int, *, max_newton: int = 100):
             if not accepted:
                 break
             t, edges, P, c, R, r = tn, en, Pn, cn, Rn, rn
-        if r > 1e-13:
-            raise ArithmeticError(f"Lloyd-Max did not converge (d={d}, bits={bits}, residual {r:.3g})")
-    cent = np.concatenate([c, -c[::-1]])
+        if r > 1e-13 * max(1.0, abs(mid - lo)):
+            raise ArithmeticError(f"Lloyd-Max did not converge ({what}, residual {r:.3g})")
+    cent = np.concatenate([c, 2.0 * mid - c[::-1]])
     bnd = 0.5 * (cent[:-1] + cent[1:])
-    bnd[h - 1] = 0.0
+    bnd[h - 1] = mid
     return cent, bnd
+
+
+# ---------------------------------------------------------------------------
+# R2: Lloyd-Max for f_d ([WIT] 第一阶段 item 2; 如何实现 item 1)
+# ---------------------------------------------------------------------------
+
+
+_LM_CACHE: dict = {}
+
+
+def lloyd_max(d: int, bits: int):
+    """Cached :func:`lloyd_max_solve` (a pure function of d and bits)."""
+    key = (int(d), int(bits))
+    if key not in _LM_CACHE:
+        _LM_CACHE[key] = lloyd_max_solve(*key)
+    c, t = _LM_CACHE[key]
+    return c.copy(), t.copy()
+
+
+def lloyd_max_solve(d: int, bits: int):
+    """Lloyd-Max quantizer of f_d with L = 2^bits levels (symmetric about 0
+    on [-1, 1]), started from the cell-centre quantiles (k + 1/2)/L of the
+    law.  Returns (centroids[L], boundaries[L-1]) in float64, increasing,
+    with the middle boundary exactly 0."""
+    if not 1 <= bits <= 8:
+        raise ValueError("bits must be in 1..8")
+    L = 1 << bits
+    a = beta_alpha(d)
+    start = 2.0 * betaincinv(a, a, (np.arange(L // 2) + 0.5) / L) - 1.0
+    return symmetric_lloyd_max(_density_scalar(d), -1.0, 0.0, start, what=f"d={d}, bits={bits}")
 
 
 def mse_closed_form(d: int, centroids, boundaries) -> float:
