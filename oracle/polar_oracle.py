@@ -197,14 +197,14 @@ def quantize(pcb: PolarCodebook, x):
     safe = np.where(n > 0, n, 1.0)
     y = np.where(n[:, None] > 0, z / safe[:, None], 0.0)
     angles, radii = polar_transform(y)
-    idx, qang, pair_r = [], [], []
-    ones = [np.hypot(y[:, 0::2], y[:, 1::2])] + radii[:-1]
+    idx, qang = [], []
     for lv in range(1, pcb.levels + 1):
         c, t = pcb.books[lv]
         ii = coord_index(angles[lv - 1], t)
         idx.append(ii)
         qang.append(c[ii])
-        pair_r.append(ones[lv - 1])
+    # the pair an angle of level l is taken from has the radius level l makes
+    pair_r = list(radii)
     yh = polar_inverse(qang)
     out = dict(idx=idx, scale=n.copy(), sign=None, rnorm=None, y=y, y_hat=yh, angles=angles,
                pair_radius=pair_r, u=None)

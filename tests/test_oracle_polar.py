@@ -288,3 +288,15 @@ def test_boundary_distance_zero_on_a_ray():
     assert dist[0][0, 0] < 1e-15
     assert dist[0][0, 1] < 1e-15                # (0.8, 0): on the ray at angle 0
     assert r["idx"][0][0, 0] == 1               # a tie goes to the upper cell
+    # level 2 pairs the radii (0.6, 0.8): distance = 1 * |sin(psi - t)|
+    psi = math.atan2(0.8, 0.6)
+    t2 = cb.books[2][1]
+    assert dist[1].shape == (1, 1)
+    assert abs(dist[1][0, 0] - np.min(np.abs(np.sin(psi - t2)))) < 1e-15
+    # shapes: one distance per angle at every level (d = 16)
+    cb16 = P.PolarCodebook(16, 3, 2)
+    r16 = P.quantize(cb16, np.random.default_rng(1).standard_normal((3, 16)))
+    assert [x.shape for x in P.boundary_distance(cb16, r16)] == [a.shape for a in r16["angles"]]
+    assert all(np.allclose(pr, np.hypot(*([r16["y"][:, 0::2], r16["y"][:, 1::2]] if lv == 0 else
+                                            [r16["pair_radius"][lv - 1][:, 0::2], r16["pair_radius"][lv - 1][:, 1::2]])))
+               for lv, pr in enumerate(r16["pair_radius"]))
