@@ -104,6 +104,7 @@ def parse():
     ap.add_argument("--no-search", action="store_true", help="skip the vector-search leg")
     ap.add_argument("--no-ab", action="store_true", help="skip the dequantize-then-attend leg")
     ap.add_argument("--no-paged", action="store_true", help="skip the paged-cache leg")
+    ap.add_argument("--no-polar", action="store_true", help="skip the PolarQuant-keys leg")
     ap.add_argument("--calib-copy", action="store_true",
                     help="accepted for profiling commands; the 1 GiB copy always runs")
     return ap.parse_args()
@@ -327,6 +328,66 @@ def paged_leg(torch, tq, W, iters, warm, page_tokens=64):
                 split_kernel_ms_spread=split_spread, split_GBps=round(alg / (split_ms * 1e-3) / 1e9, 1),
                 frac_hbm=round(alg / (split_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                 max_rel_diff_vs_contiguous=round(diff, 7))
+
+
+def polar_leg(torch, tq, W, iters, warm):
+    """PolarQuant keys on the 128K decode layer: the same K inputs coded as
+    (b1, br) = (4, 2) polar angles + QJL m=128 (48 + 16 + 8 B per key, as
+    the 3-bit scalar keys) against the scalar path's keys, with the same
+    4-bit values.  Reports the decode step's KV tokens/s and split-kernel
+    rate beside the scalar path's, the polar quantize rate of the key cache,
+    and the keys' reconstruction error |k - k_hat|^2 / |k|^2 (mean over one
+    sequence of 131072 keys, GPU dequantize, without the sketch term) for
+    both encodings."""
+    B, Hq, Hkv, d, N, tau = W["B"], W["Hq"], W["Hkv"], W["d"], W["N"], W["tau"]
+    pcb = tq.PolarCodebook(d, 4, 2, qjl_m=128, rot_seed=1, qjl_seed=2)
+    kp = tq.Codes(pcb, B * Hkv, N, tq.TQ_LAYOUT_ROW)
+    kf = W["k"].view(B * Hkv, N, d)
+    tq.tq_quantize_kv(pcb, None, kf, None, kp, None)      # warm-up / cache build
+    torch.cuda.synchronize()
+    tq.tq_profile_enable(True)
+    qms, _ = timed_iters(torch, lambda: tq.tq_quantize_kv(pcb, None, kf, None, kp, None), 3)
+    tq.tq_profile_enable(False)
+    n_vec = B * Hkv * N
+    qbytes = n_vec * (d * 2 + kp.idx_row_bytes + kp.sign_row_bytes + 8)
+    k_new = W["k"][:, :, N - 1:N].reshape(B * Hkv, 1, d).contiguous()
+    v_new = W["v"][:, :, N - 1:N].reshape(B * Hkv, 1, d).contiguous()
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+
+    def step():
+        tq.tq_quantize_kv(pcb, W["vcb"], k_new, v_new, kp, W["vc"], tok_offset=N - 1)
+        tq.tq_attn_decode(pcb, W["vcb"], W["q"], kp, W["vc"], N, tau, out=out, workspace=W["ws"])
+    for _ in range(warm):
+        step()
+    torch.cuda.synchronize()
+    tq.tq_profile_enable(True)
+    ms, per = timed_iters(torch, step, iters)
+    tq.tq_profile_enable(False)
+    split_ms, split_spread = kernel_spread(tq, tq.TQ_KERNEL_DECODE_SPLIT)
+    bpt = kp.idx_row_bytes + kp.sign_row_bytes + 8 + d * 4 // 8 + 4
+    alg = bpt * B * Hkv * N
+
+    # reconstruction error of one sequence's keys, both encodings
+    def rel_mse(cb, codes):
+        xh = torch.empty((1, N, d), dtype=torch.float32, device="cuda")
+        plain = tq.PolarCodebook(d, 4, 2, rot_seed=1) if cb is pcb else tq.Codebook(d, 3, rot_seed=1)
+        c0 = tq.Codes(plain, 1, N, tq.TQ_LAYOUT_ROW)
+        c0.idx.copy_(codes.idx[:N * codes.idx_row_bytes])
+        c0.scale.copy_(codes.scale[:N])
+        tq.tq_dequantize(plain, c0, 1, N, out=xh)
+        x = kf[:1].float()
+        return float((((x - xh) ** 2).sum(-1) / (x ** 2).sum(-1)).mean())
+    mse_polar = rel_mse(pcb, kp)
+    mse_scalar = rel_mse(W["kcb"], W["kc"])
+    del kp
+    return dict(workload="decode-128k GQA layer with PolarQuant keys: (b1, br) = (4, 2) angle codes "
+                         "(382 bits, 48 B) + QJL m=128, 4-bit scalar values",
+                KV_tokens_per_s=round(B * N / (ms * 1e-3), 1), ms_per_step=round(ms, 5), step_ms_spread=spread(per),
+                split_kernel_ms=round(split_ms, 5), split_kernel_ms_spread=split_spread,
+                bytes_per_token_head=bpt, split_GBps=round(alg / (split_ms * 1e-3) / 1e9, 1),
+                frac_hbm=round(alg / (split_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                quantize_keys_ms=round(qms, 4), quantize_keys_GBps=round(qbytes / (qms * 1e-3) / 1e9, 1),
+                key_rel_mse_polar=round(mse_polar, 6), key_rel_mse_scalar3=round(mse_scalar, 6))
 
 
 def _exact_attention_np(q, k, v, tau):
@@ -653,6 +714,11 @@ def main():
     if not args.no_paged:
         print("[bench] paged-cache leg", file=sys.stderr, flush=True)
         res["paged"] = paged_leg(torch, tq, W, iters=args.steps, warm=args.warmup)
+    if not args.no_polar:
+        print("[bench] polar-keys leg", file=sys.stderr, flush=True)
+        res["polar"] = polar_leg(torch, tq, W, iters=args.steps, warm=args.warmup)
+        res["polar"]["scalar_KV_tokens_per_s"] = res["value"]
+        res["polar"]["scalar_split_kernel_ms"] = res["roofline"]["kernel_ms"]
     if not args.no_quantize:
         print("[bench] quantize leg", file=sys.stderr, flush=True)
         res["quantize"] = quantize_leg(torch, tq, synth, dev, iters=args.steps, warm=args.warmup)

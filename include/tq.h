@@ -146,8 +146,49 @@ tq_status tq_codebook_values(const tq_params* params, double* centroids, double*
  * Meant for exercising the error path; never fails. */
 tq_status tq_codebook_solver_limits(int32_t lloyd_iters, int32_t newton_iters);
 
-/* Minimum ROW-layout pitches for this codebook: 4*bits*ceil(d/32) and
- * 4*ceil(m/32) (0 when qjl_m == 0). */
+/* ---- PolarQuant codebooks ([WIT] "TurboQuant 工作原理" > "第一阶段：随机旋转 +
+ * PolarQuant 压缩" item 2: the rotated, normalised vector is carried to polar
+ * form by pairing dimensions recursively; the angles' law is known in
+ * advance and each angle gets a Lloyd-Max code for it).
+ * With y = Pi x / |x| (d a power of two): level 1 pairs coordinates,
+ * angle atan2(y[2i+1], y[2i]) in [-pi, pi] (uniform law: b1-bit uniform
+ * quantizer, centroids at cell centres); level l >= 2 pairs the radii of
+ * level l-1, angle atan2(r[2i+1], r[2i]) in [0, pi/2], whose sin^2 follows
+ * Beta(k/2, k/2) with k = 2^(l-1) (br-bit Lloyd-Max quantizer).  The last
+ * radius is |y| = 1; scale = |x|.  The reconstruction y_hat (rebuilt
+ * top-down from radius 1, |y_hat| = 1) replaces c[idx]; with QJL the
+ * residual is r = y - y_hat.  Codes: ROW layout only, one little-endian bit
+ * stream per vector, level-major (the d/2 level-1 fields of b1 bits, then
+ * the d/4 level-2 fields of br bits, ..., the single top field), row pitch
+ * at least 4 ceil(T/32) bytes with T = (d/2) b1 + (d/2 - 1) br.
+ *  d           power of two, 4..128 on the GPU (2..256 host values)
+ *  bits_first  b1, 1..8;  bits_rest  br, 1..8;  qjl_m 0 or 1..128
+ * A polar codebook works with tq_quantize_kv (and _paged), tq_dequantize,
+ * tq_code_row_bytes, tq_codebook_export (per-level values concatenated:
+ * centroids level 1 then 2 ..., boundaries likewise) and, as the key
+ * codebook of tq_attn_decode (and _paged, _noalloc) with d = 128, b1 = 4,
+ * br = 2 and a scalar value codebook; tq_ip_topk rejects it
+ * (TQ_ERR_UNSUPPORTED). */
+typedef struct {
+  int32_t d, bits_first, bits_rest, qjl_m;
+  uint64_t rot_seed, qjl_seed;
+} tq_polar_params;
+
+/* Builds a polar codebook on the host (angle codebooks in float64, the
+ * rotation and sketch as tq_codebook_build) and uploads it to the current
+ * device.  Synchronous.  Errors: TQ_ERR_INVALID, TQ_ERR_NUMERIC,
+ * TQ_ERR_ALLOC / TQ_ERR_HIP. */
+tq_status tq_polar_codebook_build(const tq_polar_params* params, tq_codebook** out);
+
+/* Host only: the float64 values a polar codebook holds, into HOST buffers
+ * (any may be NULL): centroids and boundaries of every level concatenated
+ * (level 1 first; 2^b1 + (log2 d - 1) 2^br centroids, one fewer boundary per
+ * level), rot[d*d], qjl[m*d]. */
+tq_status tq_polar_codebook_values(const tq_polar_params* params, double* centroids, double* boundaries,
+                                   double* rot, double* qjl);
+
+/* Minimum ROW-layout pitches for this codebook: 4*bits*ceil(d/32) (polar:
+ * 4*ceil(T/32)) and 4*ceil(m/32) (0 when qjl_m == 0). */
 tq_status tq_code_row_bytes(const tq_codebook* cb, int64_t* idx_row_bytes,
                             int64_t* sign_row_bytes);
 

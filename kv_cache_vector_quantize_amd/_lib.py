@@ -28,7 +28,7 @@ EXPORTS = (
     "tq_ip_topk_workspace", "tq_ip_topk", "tq_dequantize", "tq_quantize_kv_paged",
     "tq_attn_decode_paged_workspace", "tq_attn_decode_paged", "tq_profile_enable", "tq_profile_read",
     "tq_codebook_solver_limits", "tq_profile_durations", "tq_stream_read", "tq_attn_decode_noalloc",
-    "tq_last_error",
+    "tq_polar_codebook_build", "tq_polar_codebook_values", "tq_last_error",
 )
 TQ_KERNEL_QUANTIZE, TQ_KERNEL_DECODE_SPLIT, TQ_KERNEL_TOPK, TQ_KERNEL_DEQUANTIZE = 0, 1, 2, 3
 
@@ -72,6 +72,8 @@ def lib() -> ctypes.CDLL:
     L.tq_codebook_export.argtypes = [vp, dp, dp, dp, dp]
     L.tq_codebook_values.argtypes = [ctypes.POINTER(tq_params), dp, dp, dp, dp]
     L.tq_codebook_solver_limits.argtypes = [i32, i32]
+    L.tq_polar_codebook_build.argtypes = [ctypes.POINTER(tq_polar_params), ctypes.POINTER(vp)]
+    L.tq_polar_codebook_values.argtypes = [ctypes.POINTER(tq_polar_params), dp, dp, dp, dp]
     L.tq_code_row_bytes.argtypes = [vp, ctypes.POINTER(i64), ctypes.POINTER(i64)]
     L.tq_quantize_kv.argtypes = [vp, vp, vp, vp, i32, i64, i64, i64,
                                  ctypes.POINTER(tq_codes), ctypes.POINTER(tq_codes), vp]
@@ -189,6 +191,50 @@ class Codebook:
             pass
 
 
+class tq_polar_params(ctypes.Structure):
+    _fields_ = [("d", ctypes.c_int32), ("bits_first", ctypes.c_int32), ("bits_rest", ctypes.c_int32),
+                ("qjl_m", ctypes.c_int32), ("rot_seed", ctypes.c_uint64), ("qjl_seed", ctypes.c_uint64)]
+
+
+def _polar_sizes(d, b1, br):
+    levels = int(d).bit_length() - 1
+    nc = (1 << b1) + (levels - 1) * (1 << br)
+    return levels, nc, nc - levels
+
+
+def tq_polar_codebook_values(d, bits_first=4, bits_rest=2, qjl_m=0, rot_seed=1, qjl_seed=2):
+    """Host-only float64 values of a polar codebook: dict(centroids,
+    boundaries) concatenated per level (level 1 first), rot, qjl."""
+    _, nc, nb = _polar_sizes(d, bits_first, bits_rest)
+    c, t = np.zeros(max(1, nc)), np.zeros(max(1, nb))
+    r = np.zeros((d, d))
+    q = np.zeros((qjl_m, d)) if qjl_m > 0 else None
+    p = tq_polar_params(int(d), int(bits_first), int(bits_rest), int(qjl_m), int(rot_seed), int(qjl_seed))
+    _check(lib().tq_polar_codebook_values(ctypes.byref(p), _dptr(c), _dptr(t), _dptr(r), _dptr(q)))
+    return dict(centroids=c[:nc], boundaries=t[:nb], rot=r, qjl=q)
+
+
+class PolarCodebook(Codebook):
+    """Owns a PolarQuant tq_codebook: b1 bits per level-1 angle, br bits per
+    angle of every higher level."""
+
+    def __init__(self, d, bits_first=4, bits_rest=2, qjl_m=0, rot_seed=1, qjl_seed=2):
+        self.d, self.b1, self.br, self.m = int(d), int(bits_first), int(bits_rest), int(qjl_m)
+        self.bits, self.nc, self.polar = self.b1, False, True
+        self.rot_seed, self.qjl_seed = int(rot_seed), int(qjl_seed)
+        self._h = ctypes.c_void_p()
+        p = tq_polar_params(self.d, self.b1, self.br, self.m, self.rot_seed, self.qjl_seed)
+        _check(lib().tq_polar_codebook_build(ctypes.byref(p), ctypes.byref(self._h)))
+
+    def export(self):
+        _, nc, nb = _polar_sizes(self.d, self.b1, self.br)
+        c, t = np.zeros(max(1, nc)), np.zeros(max(1, nb))
+        r = np.zeros((self.d, self.d))
+        q = np.zeros((self.m, self.d)) if self.m > 0 else None
+        _check(lib().tq_codebook_export(self._h, _dptr(c), _dptr(t), _dptr(r), _dptr(q)))
+        return dict(centroids=c[:nc], boundaries=t[:nb], rot=r, qjl=q)
+
+
 class Codes:
     """Device code planes of one tensor (torch tensors) plus their layout."""
 
@@ -225,7 +271,7 @@ class Codes:
                         self.idx_row_bytes, self.sign_row_bytes, self.seq_stride, self.layout, 0)
 
     def nbytes_per_vector(self) -> float:
-        b = self.cb.d * self.cb.bits / 8 + 4
+        b = self.idx_row_bytes + 4 if getattr(self.cb, "polar", False) else self.cb.d * self.cb.bits / 8 + 4
         if self.cb.m > 0:
             b += self.cb.m / 8 + 4
         return b

@@ -26,6 +26,12 @@
 namespace tq {
 namespace {
 
+// Iteration limits of the Lloyd-Max solve (per thread; tests shrink them to
+// reach the non-convergence error path).
+constexpr int kLloydDefault = 400000, kNewtonDefault = 80;
+thread_local int g_lloyd_iters = kLloydDefault;
+thread_local int g_newton_iters = kNewtonDefault;
+
 // ---------------------------------------------------------------- Gaussian
 
 struct SplitMix64 {
@@ -163,11 +169,167 @@ void half_centroids(const BetaLaw& law, const std::vector<double>& t, std::vecto
   }
 }
 
-// Iteration limits of the Lloyd-Max solve (per thread; tests shrink them to
-// reach the non-convergence error path).
-constexpr int kLloydDefault = 400000, kNewtonDefault = 80;
-thread_local int g_lloyd_iters = kLloydDefault;
-thread_local int g_newton_iters = kNewtonDefault;
+// ---------------------------------------------------------------- polar angles
+
+// Gauss-Legendre nodes and weights on [-1, 1]: roots of P_n by Newton's
+// method from the Chebyshev-like start cos(pi (i + 3/4) / (n + 1/2)),
+// P_n and P_n' by the three-term recurrence; w = 2 / ((1 - x^2) P_n'(x)^2).
+void gauss_legendre(int n, std::vector<double>& x, std::vector<double>& w) {
+  x.assign(n, 0.0);
+  w.assign(n, 0.0);
+  const double pi = std::acos(-1.0);
+  for (int i = 0; i < (n + 1) / 2; ++i) {
+    double z = std::cos(pi * (i + 0.75) / (n + 0.5)), dp = 0.0;
+    for (int it = 0; it < 100; ++it) {
+      double p0 = 1.0, p1 = z;
+      for (int k = 2; k <= n; ++k) {
+        const double p2 = ((2.0 * k - 1.0) * z * p1 - (k - 1.0) * p0) / k;
+        p0 = p1;
+        p1 = p2;
+      }
+      dp = n * (z * p1 - p0) / (z * z - 1.0);
+      const double dz = p1 / dp;
+      z -= dz;
+      if (std::fabs(dz) < 1e-16) break;
+    }
+    x[i] = -z;
+    x[n - 1 - i] = z;
+    w[i] = w[n - 1 - i] = 2.0 / ((1.0 - z * z) * dp * dp);
+  }
+}
+
+// Law of a level-l angle psi in [0, pi/2] (k = 2^(l-1) pooled coordinates):
+// sin^2(psi) ~ Beta(k/2, k/2), density 2 sin^(k-1) cos^(k-1) / B(k/2, k/2).
+// Cell masses on the lower half [0, pi/4] come from the incomplete beta of
+// sin^2 (the coordinate law's continued fraction with a = k/2, i.e. its
+// "d" = k + 1, at y = -cos 2 psi); first moments by composite Gauss-Legendre
+// (panels of at most 0.02 rad, 24 nodes each).
+struct AngleLaw {
+  int k;
+  BetaLaw beta;
+  double logB;
+  std::vector<double> gx, gw;
+  explicit AngleLaw(int kk) : k(kk), beta(kk + 1) {
+    logB = 2.0 * std::lgamma(0.5 * k) - std::lgamma((double)k);
+    gauss_legendre(24, gx, gw);
+  }
+  double density(double p) const {
+    const double s = std::sin(p), c = std::cos(p);
+    if (s <= 0.0 || c <= 0.0) return (k == 1) ? std::exp(std::log(2.0) - logB) : 0.0;
+    return std::exp(std::log(2.0) + (k - 1) * (std::log(s) + std::log(c)) - logB);
+  }
+  double cdf_lower(double p) const {           // p in [0, pi/4]
+    if (p <= 0.0) return 0.0;
+    return beta.cdf_lower(-std::cos(2.0 * p));
+  }
+  double moment(double u, double v) const {
+    const int panels = std::max(1, (int)std::ceil((v - u) / 0.02));
+    const double hw = 0.5 * (v - u) / panels;
+    double acc = 0.0;
+    for (int q = 0; q < panels; ++q) {
+      const double mid = u + (2 * q + 1) * hw;
+      for (size_t i = 0; i < gx.size(); ++i) {
+        const double p = mid + hw * gx[i];
+        acc += gw[i] * p * density(p);
+      }
+    }
+    return acc * hw;
+  }
+};
+
+// Lloyd-Max for one higher-level angle law with L = 2^bits levels:
+// symmetric about pi/4, solved on [0, pi/4] by Lloyd steps from the
+// quantile start, then Newton on the midpoint residual (as the coordinate
+// codebook).
+bool angle_lloyd_max(int k, int bits, std::vector<double>& cent, std::vector<double>& bnd, std::string& err) {
+  const int L = 1 << bits, h = L / 2;
+  const double mid = std::acos(-1.0) / 4.0;
+  AngleLaw law(k);
+  std::vector<double> t(h + 1), c(h), mass(h);
+  t[0] = 0.0;
+  t[h] = mid;
+  auto centroids = [&](const std::vector<double>& tt, std::vector<double>& cc) {
+    std::vector<double> F(h + 1);
+    for (int j = 0; j <= h; ++j) F[j] = law.cdf_lower(tt[j]);
+    for (int j = 0; j < h; ++j) {
+      mass[j] = F[j + 1] - F[j];
+      cc[j] = law.moment(tt[j], tt[j + 1]) / mass[j];
+    }
+  };
+  for (int j = 0; j < h; ++j) {
+    const double target = (j + 0.5) / L;
+    double lo = 0.0, hi = mid;
+    for (int it = 0; it < 200 && hi - lo > 1e-15; ++it) {
+      const double m = 0.5 * (lo + hi);
+      if (law.cdf_lower(m) < target) lo = m; else hi = m;
+    }
+    c[j] = 0.5 * (lo + hi);
+  }
+  for (int it = 0; it < g_lloyd_iters; ++it) {
+    for (int j = 1; j < h; ++j) t[j] = 0.5 * (c[j - 1] + c[j]);
+    std::vector<double> cn(h);
+    centroids(t, cn);
+    double step = 0.0;
+    for (int j = 0; j < h; ++j) step = std::fmax(step, std::fabs(cn[j] - c[j]));
+    c.swap(cn);
+    if (step <= 1e-7) break;
+  }
+  if (h > 1) {
+    const int n = h - 1;
+    for (int j = 1; j < h; ++j) t[j] = 0.5 * (c[j - 1] + c[j]);
+    double best = INFINITY;
+    std::vector<double> best_t(t);
+    for (int it = 0; it < g_newton_iters; ++it) {
+      centroids(t, c);
+      std::vector<double> R(n);
+      double rmax = 0.0;
+      for (int j = 1; j < h; ++j) {
+        R[j - 1] = t[j] - 0.5 * (c[j - 1] + c[j]);
+        rmax = std::fmax(rmax, std::fabs(R[j - 1]));
+      }
+      if (rmax < best) { best = rmax; best_t = t; } else { break; }
+      if (rmax == 0.0) break;
+      std::vector<double> dl(h), dr(h);
+      for (int j = 0; j < h; ++j) {
+        dl[j] = law.density(t[j]) * (c[j] - t[j]) / mass[j];
+        dr[j] = law.density(t[j + 1]) * (t[j + 1] - c[j]) / mass[j];
+      }
+      std::vector<double> sub(n), dia(n), sup(n), rhs(R);
+      for (int i = 0; i < n; ++i) {
+        const int j = i + 1;
+        dia[i] = 1.0 - 0.5 * (dr[j - 1] + dl[j]);
+        sub[i] = (i > 0) ? -0.5 * dl[j - 1] : 0.0;
+        sup[i] = (i < n - 1) ? -0.5 * dr[j] : 0.0;
+      }
+      for (int i = 1; i < n; ++i) {
+        const double wv = sub[i] / dia[i - 1];
+        dia[i] -= wv * sup[i - 1];
+        rhs[i] -= wv * rhs[i - 1];
+      }
+      std::vector<double> dt(n);
+      dt[n - 1] = rhs[n - 1] / dia[n - 1];
+      for (int i = n - 2; i >= 0; --i) dt[i] = (rhs[i] - sup[i] * dt[i + 1]) / dia[i];
+      for (int i = 0; i < n; ++i) t[i + 1] -= dt[i];
+    }
+    t = best_t;
+    centroids(t, c);
+    if (!(best < 1e-12)) {
+      err = "angle Lloyd-Max did not converge (midpoint residual " + std::to_string(best) + ")";
+      return false;
+    }
+  } else {
+    centroids(t, c);
+  }
+  cent.assign(L, 0.0);
+  bnd.assign(L - 1, 0.0);
+  for (int j = 0; j < h; ++j) {
+    cent[j] = c[j];
+    cent[L - 1 - j] = 2.0 * mid - c[j];
+  }
+  for (int j = 0; j < L - 1; ++j) bnd[j] = 0.5 * (cent[j] + cent[j + 1]);
+  bnd[h - 1] = mid;
+  return true;
+}
 
 }  // namespace
 
@@ -264,6 +426,46 @@ bool build_codebook_host(const tq_params& p, HostCodebook& out, std::string& err
   }
 
   // ---- rotation and sketch
+  std::vector<double> G((size_t)d * d);
+  gaussian_fill(p.rot_seed, G);
+  householder_q(d, G, out.rot);
+  out.qjl.clear();
+  if (m > 0) {
+    out.qjl.resize((size_t)m * d);
+    gaussian_fill(p.qjl_seed, out.qjl);
+  }
+  return true;
+}
+
+bool build_polar_codebook_host(const tq_polar_params& p, HostCodebook& out, std::vector<int>& cent_off,
+                               std::vector<int>& bnd_off, std::string& err) {
+  const int d = p.d, m = p.qjl_m;
+  int levels = 0;
+  while ((2 << levels) <= d) ++levels;
+  const double pi = std::acos(-1.0);
+  out.centroids.clear();
+  out.boundaries.clear();
+  cent_off.assign(levels + 2, 0);
+  bnd_off.assign(levels + 2, 0);
+  for (int lv = 1; lv <= levels; ++lv) {
+    const int bits = lv == 1 ? p.bits_first : p.bits_rest;
+    const int L = 1 << bits;
+    cent_off[lv] = (int)out.centroids.size();
+    bnd_off[lv] = (int)out.boundaries.size();
+    std::vector<double> c, t;
+    if (lv == 1) {
+      // uniform law on [-pi, pi]: equal cells, centroids at their centres
+      const double w = 2.0 * pi / L;
+      for (int j = 0; j < L; ++j) c.push_back(-pi + w * (j + 0.5));
+      for (int j = 1; j < L; ++j) t.push_back(j == L / 2 ? 0.0 : -pi + w * j);
+    } else if (!angle_lloyd_max(1 << (lv - 1), bits, c, t, err)) {
+      return false;
+    }
+    out.centroids.insert(out.centroids.end(), c.begin(), c.end());
+    out.boundaries.insert(out.boundaries.end(), t.begin(), t.end());
+  }
+  cent_off[levels + 1] = (int)out.centroids.size();
+  bnd_off[levels + 1] = (int)out.boundaries.size();
   std::vector<double> G((size_t)d * d);
   gaussian_fill(p.rot_seed, G);
   householder_q(d, G, out.rot);

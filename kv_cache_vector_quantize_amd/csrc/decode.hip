@@ -275,12 +275,19 @@ constexpr int kCopyBudget = 80 * 1024;     // LDS bytes for the two tables
 constexpr int table_entries_rt(int b) { return (b <= 4) ? (1 << (2 * b)) : (1 << b); }
 constexpr int plain_bytes(int b) { return (b <= 4) ? table_entries_rt(b) * 8 : table_entries_rt(b) * 4; }
 
+// Polar keys (BK == 0): codes of (b1, br) = (4, 2) at d = 128, seven angle
+// levels; the key table holds (cos, sin) of every centroid angle, level 1's
+// 16 first, then 4 per higher level.
+constexpr int kPolarTrigEntries = 16 + 6 * 4;
+constexpr int kPolarKeyDwords = 5;      // code dwords a lane reads per token
+
 template <int BK, int BV>
 struct SplitLds {
   static constexpr bool VC = BV <= 4 && table_entries_rt(BV) * 8 * kCopies <= kCopyBudget;
   static constexpr int VBYTES = VC ? table_entries_rt(BV) * 8 * kCopies : plain_bytes(BV);
-  static constexpr bool KC = BK <= 4 && VBYTES + table_entries_rt(BK) * 8 * kCopies <= kCopyBudget;
-  static constexpr int KBYTES = KC ? table_entries_rt(BK) * 8 * kCopies : plain_bytes(BK);
+  static constexpr bool KC = BK >= 1 && BK <= 4 && VBYTES + table_entries_rt(BK) * 8 * kCopies <= kCopyBudget;
+  static constexpr int KBYTES = BK == 0 ? kPolarTrigEntries * 8
+                                        : (KC ? table_entries_rt(BK) * 8 * kCopies : plain_bytes(BK));
   static constexpr int OBYTES = kWaves * 8 * D * 4;    // merge buffer, aliases the tables
   static constexpr int RAW = (KBYTES + VBYTES > OBYTES) ? KBYTES + VBYTES : OBYTES;
 };
@@ -333,10 +340,77 @@ __device__ inline uint32_t vgroup(const uint32_t* rec, int db, uint32_t& hi32) {
   }
 }
 
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+
+// Operand dword pair of two values: {hi(y0) | hi(y1) << 16, lo(y0) |
+// lo(y1) << 16}, hi the bf16 rounding of y and lo that of y - hi.
+__device__ inline uint2 split_pair(float y0, float y1) {
+  const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){y0, y1}, bf16x2));
+  const float r0 = y0 - __uint_as_float(h << 16);
+  const float r1 = y1 - __uint_as_float(h & 0xFFFF0000u);
+  return make_uint2(h, __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){r0, r1}, bf16x2)));
+}
+
+// Key operands of one token's 32 coordinates 32 g4 .. 32 g4 + 31 (the
+// lane's subtree of five polar levels) from its polar codes, (b1, br) =
+// (4, 2), d = 128: kw[0..1] = level-1 fields of the subtree (4 bits each),
+// kw[2] >> sh2 = its 8 level-2 fields, kw[3] >> sh3 its 4 level-3 fields,
+// kw[4] the level-4 (at sh4), level-5 (sh5), level-6 (sh6) and level-7 (bit
+// 28) fields.  The subtree's radius is the product of the level-7 and
+// level-6 factors on its path (cos for a lower child, sin for an upper);
+// each level below multiplies a radius by (cos, sin) of its centroid angle.
+struct PolarLane {
+  int sh2, sh3, sh4, sh5, sh6;
+  bool up7, up6;
+};
+
+__device__ inline void polar_operands(const uint32_t (&kw)[kPolarKeyDwords], const PolarLane& pl,
+                                      const f32x2* tt, uint2 (&ek)[8][2]) {
+  const uint32_t w4 = kw[4];
+  const f32x2 t7 = tt[36 + ((w4 >> 28) & 3u)];
+  const f32x2 t6 = tt[32 + ((w4 >> pl.sh6) & 3u)];
+  const float rho = (pl.up7 ? t7.y : t7.x) * (pl.up6 ? t6.y : t6.x);
+  const f32x2 t5 = tt[28 + ((w4 >> pl.sh5) & 3u)];
+  float r4[2] = {rho * t5.x, rho * t5.y};
+  float r3[4];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const f32x2 t = tt[24 + ((w4 >> (pl.sh4 + 2 * j)) & 3u)];
+    r3[2 * j] = r4[j] * t.x;
+    r3[2 * j + 1] = r4[j] * t.y;
+  }
+  const uint32_t w3 = kw[3] >> pl.sh3;
+  float r2[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const f32x2 t = tt[20 + ((w3 >> (2 * j)) & 3u)];
+    r2[2 * j] = r3[j] * t.x;
+    r2[2 * j + 1] = r3[j] * t.y;
+  }
+  const uint32_t w2 = kw[2] >> pl.sh2;
+  float r1[16];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const f32x2 t = tt[16 + ((w2 >> (2 * j)) & 3u)];
+    r1[2 * j] = r2[j] * t.x;
+    r1[2 * j + 1] = r2[j] * t.y;
+  }
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    // level-1 pairs 2u and 2u + 1 give coordinates 4u .. 4u + 3
+    const uint32_t w = kw[u >> 2];
+    const f32x2 ta = tt[(w >> (8 * (u & 3))) & 15u];
+    const f32x2 tb = tt[(w >> (8 * (u & 3) + 4)) & 15u];
+    ek[u][0] = split_pair(r1[2 * u] * ta.x, r1[2 * u] * ta.y);
+    ek[u][1] = split_pair(r1[2 * u + 1] * tb.x, r1[2 * u + 1] * tb.y);
+  }
+}
+
 // Global loads of one 32-token tile for one lane.
 template <int BK, int BV>
 struct Tile {
-  uint32_t kw[2][BK];   // key index bits of this lane's token (per 16-token block)
+  uint32_t kw[2][BK == 0 ? kPolarKeyDwords : BK];   // key code bits of this lane's token (per 16-token block)
   uint32_t sw[2];       // QJL sign word
   uint32_t vr[2 * BV];  // value record: 8 coordinates x 8 token slots
   float ks, kr, vs;     // per-token scalars of token (lane % 32), staged through LDS
@@ -426,8 +500,31 @@ __global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_e
     return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(u), (short)0, (int)0x7FFFFFFF, 0x00020000);
   };
   const auto rk = rsrc(reinterpret_cast<const char*>(a.kidx) + seq * a.k_stride * a.k_pitch);
-  const int klane0 = c16 * (int)a.k_pitch + g4 * BK * 4;
-  const int klane1 = klane0 + 16 * (int)a.k_pitch;
+  constexpr int KW = BK == 0 ? kPolarKeyDwords : BK;
+  // byte offset of key code dword i of this lane's token in block 0: BK
+  // consecutive dwords at g4 * BK for scalar codes; for polar codes the
+  // dwords holding the lane's subtree (see polar_operands)
+  int koff[KW];
+  PolarLane pl{};
+#pragma unroll
+  for (int i = 0; i < KW; ++i) {
+    int dw = g4 * BK + i;
+    if constexpr (BK == 0) {
+      const int pd[kPolarKeyDwords] = {2 * g4, 2 * g4 + 1, 8 + (g4 >> 1), 10, 11};
+      dw = pd[i];
+    }
+    koff[i] = c16 * (int)a.k_pitch + 4 * dw;
+  }
+  if constexpr (BK == 0) {
+    pl.sh2 = 16 * (g4 & 1);
+    pl.sh3 = 8 * g4;
+    pl.sh4 = 4 * g4;
+    pl.sh5 = 16 + 2 * g4;
+    pl.sh6 = 24 + 2 * (g4 >> 1);
+    pl.up7 = g4 >= 2;
+    pl.up6 = (g4 & 1) != 0;
+  }
+  const int kblk1 = 16 * (int)a.k_pitch;
   const auto rs = rsrc(QJL ? reinterpret_cast<const char*>(a.ksign) + seq * a.k_stride * a.ks_pitch
                            : reinterpret_cast<const char*>(a.kidx));
   // sign word g4 of the row; lanes past the row read word 0 (their sketch
@@ -454,9 +551,9 @@ __global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_e
     }
     const int kt = t * (int)a.k_pitch;
 #pragma unroll
-    for (int i = 0; i < BK; ++i) {
-      T.kw[0][i] = __builtin_amdgcn_raw_buffer_load_b32(rk, klane0 + 4 * i, kt, 0);
-      T.kw[1][i] = __builtin_amdgcn_raw_buffer_load_b32(rk, klane1 + 4 * i, kt, 0);
+    for (int i = 0; i < KW; ++i) {
+      T.kw[0][i] = __builtin_amdgcn_raw_buffer_load_b32(rk, koff[i], kt, 0);
+      T.kw[1][i] = __builtin_amdgcn_raw_buffer_load_b32(rk, koff[i] + kblk1, kt, 0);
     }
     T.sw[0] = T.sw[1] = 0u;
     if constexpr (QJL) {
@@ -509,12 +606,17 @@ __global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_e
     // norms carry back the power of two the sign operand takes out)
     stage[lane] = (QJL && lane >= 32) ? T.kr * 0x1p64f : T.ks;
     stage[64 + (lane & 31)] = T.vs;
-    // ---- key operands of block 0: all 16 lookups in flight
+    // ---- key operands of block 0: all 16 lookups in flight (polar codes:
+    // the token's coordinates rebuilt from its angle codes)
     uint2 ek[8][2];
+    if constexpr (BK == 0) {
+      polar_operands(T.kw[0], pl, reinterpret_cast<const f32x2*>(s_kt), ek);
+    } else {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      ek[u][0] = lookup<BK, L::KC>(s_kt, field<BK>(T.kw[0], (4 * u) * BK, 2 * BK), laneoff);
-      ek[u][1] = lookup<BK, L::KC>(s_kt, field<BK>(T.kw[0], (4 * u + 2) * BK, 2 * BK), laneoff);
+      for (int u = 0; u < 8; ++u) {
+        ek[u][0] = lookup<BK, L::KC>(s_kt, field<BK>(T.kw[0], (4 * u) * BK, 2 * BK), laneoff);
+        ek[u][1] = lookup<BK, L::KC>(s_kt, field<BK>(T.kw[0], (4 * u + 2) * BK, 2 * BK), laneoff);
+      }
     }
     // ---- QJL sign products (VALU work while the lookups land)
     f32x4 accq[2];
@@ -532,11 +634,18 @@ __global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_e
     }
     // ---- S^T block 0; block 1's lookups replace each consumed pair
     f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    if constexpr (BK == 0) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      acc[0] = mfma(as_bf16x8(ek[u][0].x, ek[u][0].y, ek[u][1].x, ek[u][1].y), qa[u], acc[0]);
-      ek[u][0] = lookup<BK, L::KC>(s_kt, field<BK>(T.kw[1], (4 * u) * BK, 2 * BK), laneoff);
-      ek[u][1] = lookup<BK, L::KC>(s_kt, field<BK>(T.kw[1], (4 * u + 2) * BK, 2 * BK), laneoff);
+      for (int u = 0; u < 8; ++u)
+        acc[0] = mfma(as_bf16x8(ek[u][0].x, ek[u][0].y, ek[u][1].x, ek[u][1].y), qa[u], acc[0]);
+      polar_operands(T.kw[1], pl, reinterpret_cast<const f32x2*>(s_kt), ek);
+    } else {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        acc[0] = mfma(as_bf16x8(ek[u][0].x, ek[u][0].y, ek[u][1].x, ek[u][1].y), qa[u], acc[0]);
+        ek[u][0] = lookup<BK, L::KC>(s_kt, field<BK>(T.kw[1], (4 * u) * BK, 2 * BK), laneoff);
+        ek[u][1] = lookup<BK, L::KC>(s_kt, field<BK>(T.kw[1], (4 * u + 2) * BK, 2 * BK), laneoff);
+      }
     }
     // ---- S^T block 1; the value operands of coordinate blocks 0..3 go in flight
     uint2 ev[4][4];
@@ -833,8 +942,9 @@ bool bits_ok(int b) { return b == 2 || b == 3 || b == 4 || b == 8; }
 }  // namespace
 
 bool decode_supported(const tq_codebook* kcb, const tq_codebook* vcb) {
-  return kcb->p.d == D && vcb->p.d == D && bits_ok(kcb->p.bits) && bits_ok(vcb->p.bits) &&
-         kcb->p.qjl_m <= 128;
+  if (vcb->pq.polar || kcb->p.d != D || vcb->p.d != D || !bits_ok(vcb->p.bits) || kcb->p.qjl_m > 128) return false;
+  if (kcb->pq.polar) return kcb->pq.b1 == 4 && kcb->pq.br == 2;
+  return bits_ok(kcb->p.bits);
 }
 
 DecodePlan plan_decode(int64_t B, int64_t Hq, int64_t Hkv, int64_t n_ctx, int d, int page_tokens) {
@@ -907,7 +1017,7 @@ hipError_t launch_decode(const tq_codebook* kcb, const tq_codebook* vcb, const v
     sa.vidx = static_cast<const uint32_t*>(v.idx);
     sa.vscale = v.scale;
     sa.v_stride = v.seq_stride;
-    sa.ktab = kcb->dev.pair_tab;
+    sa.ktab = kcb->pq.polar ? reinterpret_cast<const uint32_t*>(kcb->dev.ptrig) : kcb->dev.pair_tab;
     sa.vtab = vcb->dev.pair_tab;
     sa.ktab_dwords = kcb->dev.pair_tab_dwords;
     sa.vtab_dwords = vcb->dev.pair_tab_dwords;
@@ -929,7 +1039,8 @@ hipError_t launch_decode(const tq_codebook* kcb, const tq_codebook* vcb, const v
     const dim3 grid((unsigned)plan.n_wg, (unsigned)plan.rows);
     const bool qjl = kcb->p.qjl_m > 0;
     ProfileScope prof(TQ_KERNEL_DECODE_SPLIT, stream);
-    switch (kcb->p.bits) {
+    switch (kcb->pq.polar ? 0 : kcb->p.bits) {
+      case 0: launch_split_bv<0>(sa, vcb->p.bits, qjl, grid, stream); break;
       case 2: launch_split_bv<2>(sa, vcb->p.bits, qjl, grid, stream); break;
       case 3: launch_split_bv<3>(sa, vcb->p.bits, qjl, grid, stream); break;
       case 4: launch_split_bv<4>(sa, vcb->p.bits, qjl, grid, stream); break;

@@ -130,6 +130,8 @@ void free_dev(DeviceCodebook& d) {
   if (d.rop) (void)hipFree(d.rop);
   if (d.qtab) (void)hipFree(d.qtab);
   if (d.sop) (void)hipFree(d.sop);
+  if (d.ptrig) (void)hipFree(d.ptrig);
+  if (d.pbnd) (void)hipFree(d.pbnd);
   d = DeviceCodebook{};
 }
 
@@ -150,6 +152,22 @@ tq_status check_params(const tq_params* p) {
   return TQ_OK;
 }
 
+// Minimum ROW-layout index pitch of a codebook's codes.
+int64_t min_idx_row_bytes(const tq_codebook* cb) {
+  if (cb->pq.polar) return 4LL * ((cb->pq.field_bits + 31) / 32);
+  return 4LL * cb->p.bits * ((cb->p.d + 31) / 32);
+}
+
+tq_status check_polar_params(const tq_polar_params* p) {
+  if (!p) return fail(TQ_ERR_INVALID, "params is NULL");
+  if (p->d < 2 || p->d > 256 || (p->d & (p->d - 1)))
+    return fail(TQ_ERR_INVALID, "polar d must be a power of two in 2..256");
+  if (p->bits_first < 1 || p->bits_first > 8 || p->bits_rest < 1 || p->bits_rest > 8)
+    return fail(TQ_ERR_INVALID, "bits_first and bits_rest must be in 1..8");
+  if (p->qjl_m < 0 || p->qjl_m > 256) return fail(TQ_ERR_INVALID, "qjl_m must be in 0..256");
+  return TQ_OK;
+}
+
 tq_status check_codes(const tq_codebook* cb, const tq_codes* c, int64_t needed_len,
                       const char* name, bool need_stride32) {
   const std::string n(name);
@@ -165,7 +183,7 @@ tq_status check_codes(const tq_codebook* cb, const tq_codes* c, int64_t needed_l
   if (c->seq_stride < needed_len || c->seq_stride < 0)
     return fail(TQ_ERR_INVALID, n + ": seq_stride too small");
   if (c->layout == TQ_LAYOUT_ROW) {
-    const int64_t min_idx = 4LL * cb->p.bits * ((cb->p.d + 31) / 32);
+    const int64_t min_idx = min_idx_row_bytes(cb);
     if (c->idx_row_bytes < min_idx || c->idx_row_bytes % 4)
       return fail(TQ_ERR_INVALID, n + ": idx_row_bytes below minimum or not a multiple of 4");
     if (qjl) {
@@ -176,6 +194,7 @@ tq_status check_codes(const tq_codebook* cb, const tq_codes* c, int64_t needed_l
     if (need_stride32 && c->seq_stride % 32)
       return fail(TQ_ERR_INVALID, n + ": seq_stride must be a multiple of 32");
   } else if (c->layout == TQ_LAYOUT_TILE32) {
+    if (cb->pq.polar) return fail(TQ_ERR_UNSUPPORTED, n + ": polar codes use the row layout");
     if (c->seq_stride % 32) return fail(TQ_ERR_INVALID, n + ": tile32 seq_stride must be a multiple of 32");
     if (qjl) return fail(TQ_ERR_UNSUPPORTED, n + ": QJL signs are not supported in the tile32 layout");
   } else {
@@ -424,6 +443,120 @@ tq_status tq_codebook_values(const tq_params* params, double* centroids, double*
   }
 }
 
+tq_status tq_polar_codebook_build(const tq_polar_params* params, tq_codebook** out) {
+  tq_codebook* pending = nullptr;
+  auto release_pending = [&]() {
+    if (pending) {
+      free_dev(pending->dev);
+      delete pending;
+      pending = nullptr;
+    }
+  };
+  try {
+    if (!out) return fail(TQ_ERR_INVALID, "out is NULL");
+    *out = nullptr;
+    tq_status s = check_polar_params(params);
+    if (s != TQ_OK) return s;
+    tq_codebook* cb = new (std::nothrow) tq_codebook();
+    if (!cb) return fail(TQ_ERR_ALLOC, "host allocation failed");
+    pending = cb;
+    cb->p.d = params->d;
+    cb->p.bits = params->bits_first;
+    cb->p.qjl_m = params->qjl_m;
+    cb->p.norm_correction = 0;
+    cb->p.rot_seed = params->rot_seed;
+    cb->p.qjl_seed = params->qjl_seed;
+    cb->dp = pad32(params->d);
+    cb->mp = params->qjl_m > 0 ? pad32(params->qjl_m) : 0;
+    std::vector<int> coff, boff;
+    std::string err;
+    if (!build_polar_codebook_host(*params, cb->host, coff, boff, err)) {
+      release_pending();
+      return fail(TQ_ERR_NUMERIC, err);
+    }
+    PolarInfo& pq = cb->pq;
+    pq.polar = true;
+    pq.b1 = params->bits_first;
+    pq.br = params->bits_rest;
+    pq.levels = (int)coff.size() - 2;
+    for (size_t i = 0; i < coff.size() && i < (size_t)kPolarMaxLevels + 2; ++i) {
+      pq.cent_off[i] = coff[i];
+      pq.bnd_off[i] = boff[i];
+    }
+    pq.field_bits = (params->d / 2) * pq.b1 + (params->d / 2 - 1) * pq.br;
+    cb->L = 1 << pq.b1;
+    hipError_t e = hipGetDevice(&cb->device);
+    if (e != hipSuccess) { release_pending(); return hip_fail(e, "hipGetDevice"); }
+    const int d = cb->p.d, dp = cb->dp, m = cb->p.qjl_m, mp = cb->mp;
+    std::vector<float> trig(2 * cb->host.centroids.size()), pb(cb->host.boundaries.size());
+    for (size_t j = 0; j < cb->host.centroids.size(); ++j) {
+      trig[2 * j] = (float)std::cos(cb->host.centroids[j]);
+      trig[2 * j + 1] = (float)std::sin(cb->host.centroids[j]);
+    }
+    for (size_t j = 0; j < pb.size(); ++j) pb[j] = (float)cb->host.boundaries[j];
+    std::vector<float> rot((size_t)dp * dp, 0.f), rotT((size_t)dp * dp, 0.f);
+    for (int i = 0; i < d; ++i)
+      for (int j = 0; j < d; ++j) {
+        rot[(size_t)i * dp + j] = (float)cb->host.rot[(size_t)i * d + j];
+        rotT[(size_t)j * dp + i] = (float)cb->host.rot[(size_t)i * d + j];
+      }
+    if ((e = upload(&cb->dev.ptrig, trig)) != hipSuccess ||
+        (e = upload(&cb->dev.pbnd, pb.empty() ? std::vector<float>{0.f} : pb)) != hipSuccess ||
+        (e = upload(&cb->dev.rot, rot)) != hipSuccess || (e = upload(&cb->dev.rotT, rotT)) != hipSuccess) {
+      release_pending();
+      return hip_fail(e, "codebook upload");
+    }
+    if (m > 0) {
+      // S (quantize), and sqrt(pi/2)/m S Pi in both orientations (the decode
+      // prologue's t = sqrt(pi/2)/m S Pi q, the dequantize sketch term)
+      std::vector<float> qjl((size_t)mp * dp, 0.f), sprotT((size_t)dp * mp, 0.f), sprot((size_t)mp * dp, 0.f);
+      for (int j = 0; j < m; ++j)
+        for (int i = 0; i < d; ++i) qjl[(size_t)j * dp + i] = (float)cb->host.qjl[(size_t)j * d + i];
+      const double cq = std::sqrt(std::acos(-1.0) / 2.0) / (double)m;
+      for (int j = 0; j < m; ++j)
+        for (int k = 0; k < d; ++k) {
+          double acc = 0.0;
+          for (int i = 0; i < d; ++i) acc += cb->host.qjl[(size_t)j * d + i] * cb->host.rot[(size_t)i * d + k];
+          sprotT[(size_t)k * mp + j] = (float)(cq * acc);
+          sprot[(size_t)j * dp + k] = (float)(cq * acc);
+        }
+      if ((e = upload(&cb->dev.qjl, qjl)) != hipSuccess || (e = upload(&cb->dev.sprotT, sprotT)) != hipSuccess ||
+          (e = upload(&cb->dev.sprot, sprot)) != hipSuccess) {
+        release_pending();
+        return hip_fail(e, "codebook upload");
+      }
+    }
+    pending = nullptr;
+    *out = cb;
+    return TQ_OK;
+  } catch (const std::exception& ex) {
+    release_pending();
+    return fail(TQ_ERR_ALLOC, std::string("tq_polar_codebook_build: ") + ex.what());
+  } catch (...) {
+    release_pending();
+    return fail(TQ_ERR_ALLOC, "tq_polar_codebook_build: unknown exception");
+  }
+}
+
+tq_status tq_polar_codebook_values(const tq_polar_params* params, double* centroids, double* boundaries,
+                                   double* rot, double* qjl) {
+  try {
+    tq_status s = check_polar_params(params);
+    if (s != TQ_OK) return s;
+    HostCodebook hc;
+    std::vector<int> coff, boff;
+    std::string err;
+    if (!build_polar_codebook_host(*params, hc, coff, boff, err)) return fail(TQ_ERR_NUMERIC, err);
+    if (centroids) std::memcpy(centroids, hc.centroids.data(), hc.centroids.size() * sizeof(double));
+    if (boundaries) std::memcpy(boundaries, hc.boundaries.data(), hc.boundaries.size() * sizeof(double));
+    if (rot) std::memcpy(rot, hc.rot.data(), hc.rot.size() * sizeof(double));
+    if (qjl && !hc.qjl.empty()) std::memcpy(qjl, hc.qjl.data(), hc.qjl.size() * sizeof(double));
+    return TQ_OK;
+  } catch (...) {
+    return fail(TQ_ERR_ALLOC, "tq_polar_codebook_values: unexpected exception");
+  }
+}
+
 tq_status tq_codebook_solver_limits(int32_t lloyd_iters, int32_t newton_iters) {
   set_solver_limits(lloyd_iters, newton_iters);
   return TQ_OK;
@@ -439,9 +572,10 @@ tq_status tq_codebook_destroy(tq_codebook* cb) {
 tq_status tq_codebook_export(const tq_codebook* cb, double* centroids, double* boundaries,
                              double* rot, double* qjl) {
   if (!cb) return fail(TQ_ERR_INVALID, "codebook is NULL");
-  if (centroids) std::memcpy(centroids, cb->host.centroids.data(), cb->L * sizeof(double));
+  if (centroids)
+    std::memcpy(centroids, cb->host.centroids.data(), cb->host.centroids.size() * sizeof(double));
   if (boundaries)
-    std::memcpy(boundaries, cb->host.boundaries.data(), (cb->L - 1) * sizeof(double));
+    std::memcpy(boundaries, cb->host.boundaries.data(), cb->host.boundaries.size() * sizeof(double));
   if (rot) std::memcpy(rot, cb->host.rot.data(), cb->host.rot.size() * sizeof(double));
   if (qjl && !cb->host.qjl.empty())
     std::memcpy(qjl, cb->host.qjl.data(), cb->host.qjl.size() * sizeof(double));
@@ -451,7 +585,7 @@ tq_status tq_codebook_export(const tq_codebook* cb, double* centroids, double* b
 tq_status tq_code_row_bytes(const tq_codebook* cb, int64_t* idx_row_bytes,
                             int64_t* sign_row_bytes) {
   if (!cb) return fail(TQ_ERR_INVALID, "codebook is NULL");
-  if (idx_row_bytes) *idx_row_bytes = 4LL * cb->p.bits * ((cb->p.d + 31) / 32);
+  if (idx_row_bytes) *idx_row_bytes = min_idx_row_bytes(cb);
   if (sign_row_bytes) *sign_row_bytes = cb->p.qjl_m > 0 ? 4LL * ((cb->p.qjl_m + 31) / 32) : 0;
   return TQ_OK;
 }
@@ -476,11 +610,22 @@ tq_status quantize_impl(const tq_codebook* kcb, const tq_codebook* vcb, const vo
     if (!cbs[t]) return fail(TQ_ERR_INVALID, std::string(names[t]) + ": codebook is NULL");
     tq_status s = check_codes(cbs[t], outs[t], need_len, names[t], false);
     if (s != TQ_OK) return s;
-    if (!quantize_supported(cbs[t]))
-      return fail(TQ_ERR_UNSUPPORTED, std::string(names[t]) + ": quantize supports d <= 256 and qjl_m <= 256");
+    if (cbs[t]->pq.polar ? !polar_quantize_supported(cbs[t]) : !quantize_supported(cbs[t]))
+      return fail(TQ_ERR_UNSUPPORTED, std::string(names[t]) + (cbs[t]->pq.polar
+                                          ? ": polar quantize supports d <= 128 and qjl_m <= 128"
+                                          : ": quantize supports d <= 256 and qjl_m <= 256"));
     s = current_device_matches(cbs[t]);
     if (s != TQ_OK) return s;
   }
+  // polar codebooks: one kernel serves appends and bulk calls
+  for (int t = 0; t < 2; ++t) {
+    if (!xs[t] || !cbs[t]->pq.polar) continue;
+    QuantJob job{xs[t], dt, n_seq, n_tok, tok_offset, *outs[t], pm};
+    hipError_t e = launch_polar_quantize(cbs[t], job, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "quantize launch");
+    xs[t] = nullptr;
+  }
+  if (!xs[0] && !xs[1]) return TQ_OK;
   if (n_tok <= kSmallMaxTok && n_seq * n_tok <= 0x7FFFFFFF) {
     const tq_codebook* sc[2];
     QuantJob sj[2];
@@ -602,7 +747,8 @@ tq_status decode_impl(const tq_codebook* kcb, const tq_codebook* vcb, const void
   if (kcb->p.d != vcb->p.d) return fail(TQ_ERR_INVALID, "key and value codebooks differ in d");
   if (!decode_supported(kcb, vcb))
     return fail(TQ_ERR_UNSUPPORTED,
-                "decode supports d = 128, bits in {2,3,4,8}, qjl_m <= 128");
+                "decode supports d = 128, qjl_m <= 128, value codes of 2, 3, 4 or 8 bits and key codes of "
+                "2, 3, 4 or 8 bits or polar with (b1, br) = (4, 2)");
   if (!std::isfinite(sm_scale)) return fail(TQ_ERR_INVALID, "sm_scale must be finite");
   if (B * Hq == 0) return TQ_OK;
   if (!q || !out) return fail(TQ_ERR_INVALID, "q and out must be non-NULL");
@@ -734,6 +880,7 @@ tq_status tq_ip_topk(const tq_codebook* cb, const float* queries, int64_t nq,
       return fail(TQ_ERR_INVALID, "queries, out_idx and out_score must be non-NULL");
     if (!db || db->layout != TQ_LAYOUT_ROW)
       return fail(TQ_ERR_INVALID, "database codes must use the row layout");
+    if (cb->pq.polar) return fail(TQ_ERR_UNSUPPORTED, "top-k takes scalar codes, not polar codes");
     tq_status s = check_codes(cb, db, n_db, "db", false);
     if (s != TQ_OK) return s;
     if (db->idx_row_bytes > kIpMaxRowBytes || (cb->p.qjl_m > 0 && db->sign_row_bytes > kIpMaxSignRowBytes))
@@ -772,14 +919,15 @@ tq_status tq_dequantize(const tq_codebook* cb, const tq_codes* codes, int64_t n_
     if (!aligned(out, 16)) return fail(TQ_ERR_INVALID, "out must be 16-byte aligned");
     tq_status s = check_codes(cb, codes, tok_offset + n_tok, "codes", false);
     if (s != TQ_OK) return s;
-    if (!quantize_supported(cb))
-      return fail(TQ_ERR_UNSUPPORTED, "dequantize supports d <= 256 and qjl_m <= 256");
+    if (cb->pq.polar ? !polar_quantize_supported(cb) : !quantize_supported(cb))
+      return fail(TQ_ERR_UNSUPPORTED, "dequantize supports d <= 256 and qjl_m <= 256 (polar: d <= 128, qjl_m <= 128)");
     if (n_seq * n_tok > 0x7FFFFFFF || n_seq > 0x7FFFFFFF)
       return fail(TQ_ERR_UNSUPPORTED, "n_seq * n_tok must stay below 2^31");
     s = current_device_matches(cb);
     if (s != TQ_OK) return s;
     DequantJob job{*codes, n_seq, n_tok, tok_offset, out, out_dt};
-    hipError_t e = launch_dequantize(cb, job, static_cast<hipStream_t>(stream));
+    hipError_t e = cb->pq.polar ? launch_polar_dequantize(cb, job, static_cast<hipStream_t>(stream))
+                                : launch_dequantize(cb, job, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "dequantize launch");
     return TQ_OK;
   } catch (...) {

@@ -20,6 +20,12 @@ struct HostCodebook {
 };
 
 bool build_codebook_host(const tq_params& p, HostCodebook& out, std::string& err);
+
+// PolarQuant codebook: centroids / boundaries of every angle level
+// concatenated (level 1 first); cent_off[l] / bnd_off[l] (l = 1..levels+1)
+// index level l's first entry.
+bool build_polar_codebook_host(const tq_polar_params& p, HostCodebook& out, std::vector<int>& cent_off,
+                               std::vector<int>& bnd_off, std::string& err);
 // thread-local iteration limits of the Lloyd-Max solve (<= 0: default)
 void set_solver_limits(int lloyd_iters, int newton_iters);
 
@@ -67,6 +73,20 @@ struct DeviceCodebook {
   uint32_t* sop = nullptr;
   int qcells = 0;
   float qG = 0.f;
+  // PolarQuant codebooks: ptrig [2 * centroids] (cos, sin) of every angle
+  // centroid, pbnd [boundaries] fp32, both level-major as cent_off / bnd_off
+  float* ptrig = nullptr;
+  float* pbnd = nullptr;
+};
+
+// PolarQuant layout of a codebook (polar == false for scalar codebooks)
+constexpr int kPolarMaxLevels = 8;
+struct PolarInfo {
+  bool polar = false;
+  int b1 = 0, br = 0, levels = 0;
+  int cent_off[kPolarMaxLevels + 2] = {};
+  int bnd_off[kPolarMaxLevels + 2] = {};
+  int field_bits = 0;        // (d/2) b1 + (d/2 - 1) br
 };
 
 constexpr int kQ128Cells = 2048;   // largest index-cell table the d = 128 kernel stages
@@ -82,6 +102,7 @@ struct tq_codebook {
   int device = 0;
   tq::HostCodebook host;
   tq::DeviceCodebook dev;
+  tq::PolarInfo pq;
 };
 
 namespace tq {
@@ -211,6 +232,12 @@ hipError_t launch_topk(const tq_codebook* cb, const float* queries, const TopkPl
 // device address on the current device (looked up on the first call there).
 constexpr size_t kNoallocScratchBytes = 8u << 20;
 hipError_t noalloc_scratch(void** out);
+
+// PolarQuant kernels (polar.hip): bulk and append quantize into the row
+// layout (d a power of two <= 128, qjl_m <= 128) and dequantize.
+bool polar_quantize_supported(const tq_codebook* cb);
+hipError_t launch_polar_quantize(const tq_codebook* cb, const QuantJob& job, hipStream_t stream);
+hipError_t launch_polar_dequantize(const tq_codebook* cb, const DequantJob& job, hipStream_t stream);
 
 // Streaming read of bytes (a multiple of 16) of buf; writes sink[0] only
 // in the rare case that the XOR of the data equals a fixed value.
