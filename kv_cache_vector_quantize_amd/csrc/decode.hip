@@ -260,6 +260,27 @@ __device__ inline uint32_t field(const uint32_t (&wd)[NW], int off, int w) {
   return v & ((1u << w) - 1u);
 }
 
+// The 32-bit window of a little-endian multi-word field starting at bit off.
+template <int NW>
+__device__ inline uint32_t window(const uint32_t (&wd)[NW], int off) {
+  const int i = off >> 5, s = off & 31;
+  if (i + 1 < NW) return __builtin_amdgcn_alignbit(wd[i + 1], wd[i], s);
+  return wd[i] >> s;
+}
+
+// Byte address in the quad key table of the operand of coordinates 4u ..
+// 4u + 3 of a lane's key bits (BK = 2: with the lane's copy offset, one
+// byte permute; BK = 3: the 12-bit index moved to bit 4 and masked).
+template <int BK>
+__device__ inline uint32_t quad_addr(const uint32_t (&kw)[BK], int u, uint32_t laneoff16) {
+  if constexpr (BK == 2) {
+    return __builtin_amdgcn_perm(kw[u >> 2], laneoff16, 0x0C0C0000u | ((4u + (u & 3)) << 8));
+  } else {
+    const uint32_t w = u == 0 ? (kw[0] << 4) : window<BK>(kw, 12 * u - 4);
+    return w & 0xFFF0u;
+  }
+}
+
 template <int B>
 constexpr int table_entries() { return (B <= 4) ? (1 << (2 * B)) : (1 << B); }
 
@@ -281,13 +302,28 @@ constexpr int plain_bytes(int b) { return (b <= 4) ? table_entries_rt(b) * 8 : t
 constexpr int kPolarTrigEntries = 16 + 6 * 4;
 constexpr int kPolarKeyDwords = 5;      // code dwords a lane reads per token
 
+// Keys of 2 or 3 bits use a quad table: one 16-byte entry per four
+// coordinates (a 4 b-bit index, contiguous in the packed row) holds the
+// operand dwords {hi, lo} of both coordinate pairs, so one ds_read_b128
+// lands a whole MFMA operand.  The 2-bit table (4 KB) is held as 16
+// interleaved copies (entry e of copy c at byte e * 256 + c * 16: the 16
+// lanes of a read pass hit distinct banks); the 3-bit one (64 KB) once.
+template <int BK>
+struct QuadKeys {
+  static constexpr bool on = BK == 2 || BK == 3;
+  static constexpr int copies = BK == 2 ? 16 : 1;
+  static constexpr int bytes = on ? (16 << (4 * BK)) * copies : 0;
+};
+
 template <int BK, int BV>
 struct SplitLds {
   static constexpr bool VC = BV <= 4 && table_entries_rt(BV) * 8 * kCopies <= kCopyBudget;
   static constexpr int VBYTES = VC ? table_entries_rt(BV) * 8 * kCopies : plain_bytes(BV);
-  static constexpr bool KC = BK >= 1 && BK <= 4 && VBYTES + table_entries_rt(BK) * 8 * kCopies <= kCopyBudget;
+  static constexpr bool KQ = QuadKeys<BK>::on;
+  static constexpr bool KC = !KQ && BK >= 1 && BK <= 4 && VBYTES + table_entries_rt(BK) * 8 * kCopies <= kCopyBudget;
   static constexpr int KBYTES = BK == 0 ? kPolarTrigEntries * 8
-                                        : (KC ? table_entries_rt(BK) * 8 * kCopies : plain_bytes(BK));
+                                        : KQ ? QuadKeys<BK>::bytes
+                                             : (KC ? table_entries_rt(BK) * 8 * kCopies : plain_bytes(BK));
   static constexpr int OBYTES = kWaves * 8 * D * 4;    // merge buffer, aliases the tables
   static constexpr int RAW = (KBYTES + VBYTES > OBYTES) ? KBYTES + VBYTES : OBYTES;
 };
@@ -424,15 +460,27 @@ __global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_e
   __shared__ __align__(16) float s_sc[kWaves][96];          // per wave: kscale[32], rnorm[32], vscale[32]
   __shared__ float s_M[kWaves][8], s_l[kWaves][8];
   const char* s_kt = s_raw;
-  const char* s_vt = s_raw + L::KBYTES;
+  // value table: a key table of >= 64 KB puts it past the reach of a
+  // ds_read's immediate offset, so its base is carried in the lane offset
+  // (bit 16 up, clear of the entry and copy bits) instead
+  constexpr bool kVBaseInLane = L::KBYTES >= 65536 && L::VC;
+  static_assert(!kVBaseInLane || L::KBYTES % 65536 == 0, "value table base must be a multiple of 64 KB");
+  const char* s_vt = s_raw + (kVBaseInLane ? 0 : L::KBYTES);
   const int tid = threadIdx.x;
   {
-    // interleaved copy i of 8-byte entry i / 32 sits at byte 8 i
-    const uint2* kt = reinterpret_cast<const uint2*>(a.ktab);
+    // interleaved copy i of 8-byte entry i / 32 sits at byte 8 i (quad
+    // tables: copy i of 16-byte entry i / copies at byte 16 i)
     const uint2* vt = reinterpret_cast<const uint2*>(a.vtab);
-    uint2* dk = reinterpret_cast<uint2*>(s_raw);
     uint2* dv = reinterpret_cast<uint2*>(s_raw + L::KBYTES);
-    for (int i = tid; i < L::KBYTES / 8; i += NT) dk[i] = kt[L::KC ? (i >> 5) : i];
+    if constexpr (L::KQ) {
+      const uint4* kt = reinterpret_cast<const uint4*>(a.ktab);
+      uint4* dk = reinterpret_cast<uint4*>(s_raw);
+      for (int i = tid; i < L::KBYTES / 16; i += NT) dk[i] = kt[i / QuadKeys<BK>::copies];
+    } else {
+      const uint2* kt = reinterpret_cast<const uint2*>(a.ktab);
+      uint2* dk = reinterpret_cast<uint2*>(s_raw);
+      for (int i = tid; i < L::KBYTES / 8; i += NT) dk[i] = kt[L::KC ? (i >> 5) : i];
+    }
     for (int i = tid; i < L::VBYTES / 8; i += NT) dv[i] = vt[L::VC ? (i >> 5) : i];
   }
   __syncthreads();
@@ -441,6 +489,8 @@ __global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_e
   const int c16 = lane & 15, g4 = lane >> 4;
   const int part = blockIdx.x * kWaves + wave;
   const uint32_t laneoff = (uint32_t)(lane & 31) << 3;
+  const uint32_t laneoff16 = (uint32_t)(lane & 15) << 4;
+  const uint32_t vlaneoff = laneoff | (kVBaseInLane ? (uint32_t)L::KBYTES : 0u);
   const int row = blockIdx.y;
   const int qg = row % a.qgroups;
   const int bh = row / a.qgroups;
@@ -589,13 +639,14 @@ __global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_e
     for (int q = 0; q < 4; ++q) {
       if constexpr (BV == 4 && L::VC) {
         // byte q of f is the pair index: (index << 8) | laneoff in one byte permute
-        const uint32_t addr = __builtin_amdgcn_perm(f, laneoff, 0x0C0C0000u | ((4u + q) << 8));
+        // (bytes 2-3 of the address from the lane offset: the table base)
+        const uint32_t addr = __builtin_amdgcn_perm(f, vlaneoff, 0x03020000u | ((4u + q) << 8));
         e[q] = *reinterpret_cast<const uint2*>(s_vt + addr);
       } else {
         uint32_t pr;
         if constexpr (BV == 8) pr = ((q < 2 ? f : fhi) >> (16 * (q & 1))) & 0xFFFFu;
         else pr = (f >> (2 * q * BV)) & ((1u << (2 * BV)) - 1u);
-        e[q] = lookup<BV, L::VC>(s_vt, pr, laneoff);
+        e[q] = lookup<BV, L::VC>(s_vt, pr, vlaneoff);
       }
     }
   };
@@ -609,7 +660,12 @@ __global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_e
     // ---- key operands of block 0: all 16 lookups in flight (polar codes:
     // the token's coordinates rebuilt from its angle codes)
     uint2 ek[8][2];
-    if constexpr (BK == 0) {
+    uint4 eq[8];
+    if constexpr (L::KQ) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        eq[u] = *reinterpret_cast<const uint4*>(s_kt + quad_addr<BK>(T.kw[0], u, laneoff16));
+    } else if constexpr (BK == 0) {
       polar_operands(T.kw[0], pl, reinterpret_cast<const f32x2*>(s_kt), ek);
     } else {
 #pragma unroll
@@ -634,7 +690,13 @@ __global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_e
     }
     // ---- S^T block 0; block 1's lookups replace each consumed pair
     f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    if constexpr (BK == 0) {
+    if constexpr (L::KQ) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        acc[0] = mfma(__builtin_bit_cast(bf16x8, eq[u]), qa[u], acc[0]);
+        eq[u] = *reinterpret_cast<const uint4*>(s_kt + quad_addr<BK>(T.kw[1], u, laneoff16));
+      }
+    } else if constexpr (BK == 0) {
 #pragma unroll
       for (int u = 0; u < 8; ++u)
         acc[0] = mfma(as_bf16x8(ek[u][0].x, ek[u][0].y, ek[u][1].x, ek[u][1].y), qa[u], acc[0]);
@@ -651,7 +713,8 @@ __global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_e
     uint2 ev[4][4];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      acc[1] = mfma(as_bf16x8(ek[u][0].x, ek[u][0].y, ek[u][1].x, ek[u][1].y), qa[u], acc[1]);
+      if constexpr (L::KQ) acc[1] = mfma(__builtin_bit_cast(bf16x8, eq[u]), qa[u], acc[1]);
+      else acc[1] = mfma(as_bf16x8(ek[u][0].x, ek[u][0].y, ek[u][1].x, ek[u][1].y), qa[u], acc[1]);
       if (u & 1) vlook(T, u >> 1, ev[u >> 1]);
     }
     // lg = logit - Meff (base 2): the scales are applied per column before the
@@ -1017,7 +1080,8 @@ hipError_t launch_decode(const tq_codebook* kcb, const tq_codebook* vcb, const v
     sa.vidx = static_cast<const uint32_t*>(v.idx);
     sa.vscale = v.scale;
     sa.v_stride = v.seq_stride;
-    sa.ktab = kcb->pq.polar ? reinterpret_cast<const uint32_t*>(kcb->dev.ptrig) : kcb->dev.pair_tab;
+    sa.ktab = kcb->pq.polar ? reinterpret_cast<const uint32_t*>(kcb->dev.ptrig)
+                            : (kcb->p.bits <= 3 && kcb->p.bits >= 2 ? kcb->dev.quad_tab : kcb->dev.pair_tab);
     sa.vtab = vcb->dev.pair_tab;
     sa.ktab_dwords = kcb->dev.pair_tab_dwords;
     sa.vtab_dwords = vcb->dev.pair_tab_dwords;

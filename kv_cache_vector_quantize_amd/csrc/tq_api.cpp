@@ -127,6 +127,7 @@ void free_dev(DeviceCodebook& d) {
   if (d.dqs) (void)hipFree(d.dqs);
   if (d.dqcs) (void)hipFree(d.dqcs);
   if (d.pair_tab) (void)hipFree(d.pair_tab);
+  if (d.quad_tab) (void)hipFree(d.quad_tab);
   if (d.rop) (void)hipFree(d.rop);
   if (d.qtab) (void)hipFree(d.qtab);
   if (d.sop) (void)hipFree(d.sop);
@@ -318,6 +319,25 @@ tq_status tq_codebook_build(const tq_params* params, tq_codebook** out) {
       }
     }
     cb->dev.pair_tab_dwords = (int)tab.size();
+    if (cb->p.bits <= 3) {
+      const int b = cb->p.bits;
+      const size_t n4 = (size_t)1 << (4 * b);
+      std::vector<uint32_t> quad(4 * n4);
+      std::vector<uint16_t> hi(L), lo(L);
+      for (int x = 0; x < L; ++x) split_bf16(cb->host.centroids[x], hi[x], lo[x]);
+      const uint32_t msk = (uint32_t)L - 1u;
+      for (size_t e4 = 0; e4 < n4; ++e4) {
+        const uint32_t a = e4 & msk, bb = (e4 >> b) & msk, c = (e4 >> (2 * b)) & msk, dd = (e4 >> (3 * b)) & msk;
+        quad[4 * e4 + 0] = (uint32_t)hi[a] | ((uint32_t)hi[bb] << 16);
+        quad[4 * e4 + 1] = (uint32_t)lo[a] | ((uint32_t)lo[bb] << 16);
+        quad[4 * e4 + 2] = (uint32_t)hi[c] | ((uint32_t)hi[dd] << 16);
+        quad[4 * e4 + 3] = (uint32_t)lo[c] | ((uint32_t)lo[dd] << 16);
+      }
+      if ((e = upload(&cb->dev.quad_tab, quad)) != hipSuccess) {
+        release_pending();
+        return hip_fail(e, "codebook upload");
+      }
+    }
     if ((e = upload(&cb->dev.cent, cent)) != hipSuccess ||
         (e = upload(&cb->dev.bnd, bnd.empty() ? std::vector<float>{0.f} : bnd)) != hipSuccess ||
         (e = upload(&cb->dev.rot, rot)) != hipSuccess ||

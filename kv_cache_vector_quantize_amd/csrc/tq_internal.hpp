@@ -58,6 +58,11 @@ struct DeviceCodebook {
   //  bits  > 4: entry a holds one dword {hi(c[a]) | lo(c[a]) << 16}
   uint32_t* pair_tab = nullptr;
   int pair_tab_dwords = 0;
+  //  quad_tab (bits <= 3): entry e = a | b << bits | c << 2 bits | d << 3 bits
+  //  holds four dwords {hi(c[a]) | hi(c[b]) << 16, lo(c[a]) | lo(c[b]) << 16,
+  //  hi(c[c]) | hi(c[d]) << 16, lo(c[c]) | lo(c[d]) << 16}: one 16-byte read
+  //  gives the decode key operand of four coordinates
+  uint32_t* quad_tab = nullptr;
   // d = 128 quantize (see quantize128.hip), absent for other d:
   //  rop: Pi as bf16 operands of v_mfma_f32_32x32x16_bf16 in three parts
   //  (hi, lo, lo2), uint4 [wave 4][k-step 8][part 3][lane 64]; lane l of wave
