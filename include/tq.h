@@ -317,14 +317,26 @@ tq_status tq_ip_topk_workspace(int64_t nq, int64_t n_db, int32_t k, int32_t d, s
  *            lower index
  *  out_score device fp32 [nq][k]: their scores
  *  workspace device scratch of >= tq_ip_topk_workspace bytes, 256-byte aligned
- * Scores are formed with bf16 hi/lo splits of the centroids and of Pi q and
- * S Pi q (about 2^-16 relative), so rows whose exact scores differ by less
- * than that may trade places.
+ * The result is the exact top-k of s_j evaluated in float64 from the codes
+ * (Pi q and S Pi q formed in float64), and out_score is that float64 score
+ * rounded to fp32.  A bf16 hi/lo MFMA pass keeps kc candidates per query
+ * (kc = 16 for k <= 10, else min(2k, 64)); the candidates are rescored in
+ * float64, and a query is settled when the kc-th approximate score plus a
+ * bound on the approximate score's error (over every row of the database)
+ * stays below the k-th exact score.  Other queries (near-ties at the k-th
+ * place, repeated rows) are answered by an exact float64 scan of the
+ * database.
  * Errors: TQ_ERR_INVALID, TQ_ERR_UNSUPPORTED (k > 32, oversized rows),
  * TQ_ERR_HIP. */
 tq_status tq_ip_topk(const tq_codebook* cb, const float* queries, int64_t nq,
                      const tq_codes* db, int64_t n_db, int32_t k, int64_t* out_idx,
                      float* out_score, void* workspace, size_t ws_bytes, void* stream);
+
+/* Diagnostic switch of tq_ip_topk (process-wide, default 0): 1 sends every
+ * query to the exact float64 scan, skipping the candidates' test, so the
+ * scan can be checked and timed on any input; 0 restores the default.
+ * Errors: TQ_ERR_INVALID (other values). */
+tq_status tq_ip_topk_exact_scan(int32_t always);
 
 /* Vectors back from their codes: the decompress half of the compress /
  * decompress pair of [AGENT] 三、工程实现 item 1, computing the estimate of

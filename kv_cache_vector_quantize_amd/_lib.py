@@ -28,7 +28,7 @@ EXPORTS = (
     "tq_ip_topk_workspace", "tq_ip_topk", "tq_dequantize", "tq_quantize_kv_paged",
     "tq_attn_decode_paged_workspace", "tq_attn_decode_paged", "tq_profile_enable", "tq_profile_read",
     "tq_codebook_solver_limits", "tq_profile_durations", "tq_stream_read", "tq_attn_decode_noalloc",
-    "tq_polar_codebook_build", "tq_polar_codebook_values", "tq_last_error",
+    "tq_polar_codebook_build", "tq_polar_codebook_values", "tq_ip_topk_exact_scan", "tq_last_error",
 )
 TQ_KERNEL_QUANTIZE, TQ_KERNEL_DECODE_SPLIT, TQ_KERNEL_TOPK, TQ_KERNEL_DEQUANTIZE = 0, 1, 2, 3
 
@@ -72,6 +72,7 @@ def lib() -> ctypes.CDLL:
     L.tq_codebook_export.argtypes = [vp, dp, dp, dp, dp]
     L.tq_codebook_values.argtypes = [ctypes.POINTER(tq_params), dp, dp, dp, dp]
     L.tq_codebook_solver_limits.argtypes = [i32, i32]
+    L.tq_ip_topk_exact_scan.argtypes = [i32]
     L.tq_polar_codebook_build.argtypes = [ctypes.POINTER(tq_polar_params), ctypes.POINTER(vp)]
     L.tq_polar_codebook_values.argtypes = [ctypes.POINTER(tq_polar_params), dp, dp, dp, dp]
     L.tq_code_row_bytes.argtypes = [vp, ctypes.POINTER(i64), ctypes.POINTER(i64)]
@@ -149,6 +150,13 @@ def tq_codebook_values(d, bits, qjl_m=0, norm_correction=False, rot_seed=1, qjl_
 def tq_codebook_solver_limits(lloyd_iters=0, newton_iters=0):
     """Iteration limits of the codebook solve on this thread (0: defaults)."""
     _check(lib().tq_codebook_solver_limits(int(lloyd_iters), int(newton_iters)))
+
+
+def tq_ip_topk_exact_scan(always: bool):
+    """Diagnostic switch: True sends every top-k query to the exact float64
+    scan of the database; False (the default) scans only the queries the
+    candidates do not settle."""
+    _check(lib().tq_ip_topk_exact_scan(1 if always else 0))
 
 
 class Codebook:

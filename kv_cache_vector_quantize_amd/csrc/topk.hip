@@ -79,10 +79,14 @@ struct IPArgs {
   const float* q;       // [nq][d]
   int64_t nq;
   int d, m, dp, mp, nu, ns;
-  const float* rotT;    // [dp][dp], rotT[k][i] = Pi[i][k]
-  const float* qjlT;    // [dp][mp], qjlT[i][j] = S[j][i]
+  const double* rotT64; // [d][d], rotT64[k][i] = Pi[i][k]
+  const double* qjlT64; // [d][m], qjlT64[i][j] = S[j][i]
   uint32_t* qop;        // [nqb][nu + ns][64 lanes][4 dwords]
   float* cinit;         // [nqb * 8]
+  double* qt64;         // [nq][256] q~ = Pi q (float64)
+  double* tt64;         // [nq][256] t = sqrt(pi/2)/m S q~ (float64)
+  double* qinfo;        // [nq][2] |q~|_2, |t|_1
+  uint32_t* bounds;     // [2] database max |scale|, max |rnorm| (zeroed here)
 };
 
 // Operand layouts (lane = column j + 16 g4 of the B operand; columns 0-7 are
@@ -93,28 +97,46 @@ struct IPArgs {
 //  sign MFMA v: element el is sketch row 32 v + 8 g4 + el, scaled by
 //    2^(128 - 2^el - 64): the sign operand leaves bit el of the lane's sign
 //    byte at bf16 bit 7 + el, the normal value 2^(2^el - 127).
+// q~ and t are formed in float64 (kept for the exact refinement) and rounded
+// to float before the bf16 hi/lo split.
 __global__ void __launch_bounds__(256) k_ip_prologue(IPArgs a) {
-  __shared__ float qs[256], qt[256], tt[256];
+  __shared__ double qs[256], qt[256], tt[256];
+  __shared__ double red[2][4];
   const int64_t qi = blockIdx.x;        // over the padded query count
   const int tid = threadIdx.x;
   const bool valid = qi < a.nq;
-  qs[tid] = (valid && tid < a.d) ? a.q[qi * a.d + tid] : 0.f;
+  if (qi == 0 && tid < 2) a.bounds[tid] = 0u;
+  qs[tid] = (valid && tid < a.d) ? (double)a.q[qi * a.d + tid] : 0.0;
   __syncthreads();
-  float z = 0.f;
-  if (tid < a.dp) {
-#pragma unroll 8
-    for (int k = 0; k < a.d; ++k) z += a.rotT[k * a.dp + tid] * qs[k];
+  double z = 0.0;
+  if (tid < a.d) {
+    for (int k = 0; k < a.d; ++k) z = fma(a.rotT64[(int64_t)k * a.d + tid], qs[k], z);
   }
   qt[tid] = z;
   __syncthreads();
-  float t = 0.f;
+  double t = 0.0;
   if (tid < a.m) {
-#pragma unroll 8
-    for (int i = 0; i < a.d; ++i) t += a.qjlT[i * a.mp + tid] * qt[i];
-    t *= 1.2533141373155003f / (float)a.m;          // sqrt(pi/2) / m
+    for (int i = 0; i < a.d; ++i) t = fma(a.qjlT64[(int64_t)i * a.m + tid], qt[i], t);
+    t *= 1.2533141373155002512 / (double)a.m;      // sqrt(pi/2) / m
   }
   tt[tid] = t;
+  if (valid) {
+    a.qt64[qi * 256 + tid] = z;
+    a.tt64[qi * 256 + tid] = t;
+  }
+  {
+    double n2 = z * z, n1 = fabs(t);
+    for (int o = 32; o >= 1; o >>= 1) {
+      n2 += __shfl_xor(n2, o);
+      n1 += __shfl_xor(n1, o);
+    }
+    if ((tid & 63) == 0) { red[0][tid >> 6] = n2; red[1][tid >> 6] = n1; }
+  }
   __syncthreads();
+  if (valid && tid == 0) {
+    a.qinfo[qi * 2 + 0] = sqrt(red[0][0] + red[0][1] + red[0][2] + red[0][3]);
+    a.qinfo[qi * 2 + 1] = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+  }
   const int64_t qb = qi >> 3;
   const int c = (int)(qi & 7);
   uint32_t* rec = a.qop + qb * (int64_t)(a.nu + a.ns) * 256;
@@ -123,7 +145,7 @@ __global__ void __launch_bounds__(256) k_ip_prologue(IPArgs a) {
     uint32_t hv[2];
     for (int h2 = 0; h2 < 2; ++h2) {
       const int el = 2 * dw + h2;
-      const float v = qt[16 * u + 4 * g4 + 2 * (el >> 2) + (el & 1)];
+      const float v = (float)qt[16 * u + 4 * g4 + 2 * (el >> 2) + (el & 1)];
       const uint32_t hi = bf16_rne_bits(v);
       hv[h2] = hl ? bf16_rne_bits(v - __uint_as_float(hi << 16)) : hi;
     }
@@ -134,7 +156,7 @@ __global__ void __launch_bounds__(256) k_ip_prologue(IPArgs a) {
     uint32_t hv[2];
     for (int h2 = 0; h2 < 2; ++h2) {
       const int el = 2 * dw + h2;
-      const float x = ldexpf(tt[32 * v + 8 * g4 + el], 128 - (1 << el) - kSignShiftIp);
+      const float x = ldexpf((float)tt[32 * v + 8 * g4 + el], 128 - (1 << el) - kSignShiftIp);
       const uint32_t hi = bf16_rne_bits(x);
       hv[h2] = hl ? bf16_rne_bits(x - __uint_as_float(hi << 16)) : hi;
     }
@@ -144,12 +166,31 @@ __global__ void __launch_bounds__(256) k_ip_prologue(IPArgs a) {
   if (tid < 64) {
     float s = 0.f;
     for (int j = tid; j < 256; j += 64) {
-      const float v = tt[j];
+      const float v = (float)tt[j];
       const float fh = __uint_as_float(bf16_rne_bits(v) << 16);
       s += fh + __uint_as_float(bf16_rne_bits(v - fh) << 16);
     }
     for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
     if (tid == 0) a.cinit[qi] = -ldexpf(s, -kSignShiftIp);
+  }
+}
+
+// Database bounds of the refinement's error bound: max |scale| and max
+// |rnorm| (as float bits; non-negative floats order as their bits).
+__global__ void __launch_bounds__(256) k_ip_bounds(const float* scale, const float* rnorm, int64_t n,
+                                                   uint32_t* bounds) {
+  float ms = 0.f, mr = 0.f;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    ms = fmaxf(ms, fabsf(scale[i]));
+    if (rnorm) mr = fmaxf(mr, fabsf(rnorm[i]));
+  }
+  for (int o = 32; o >= 1; o >>= 1) {
+    ms = fmaxf(ms, __shfl_xor(ms, o));
+    mr = fmaxf(mr, __shfl_xor(mr, o));
+  }
+  if ((threadIdx.x & 63) == 0) {
+    atomicMax(bounds, __float_as_uint(ms));
+    atomicMax(bounds + 1, __float_as_uint(mr));
   }
 }
 
@@ -170,15 +211,16 @@ struct ISArgs {
   int32_t* cand_i;
 };
 
-template <int B, bool QJL>
+// LM: capacity of the per-lane lists (>= k)
+template <int B, bool QJL, int LM>
 __global__ void __launch_bounds__(64 * kIpWaves) k_ip_score(ISArgs a) {
   constexpr int TABW = (B <= 4) ? (2 << (2 * B)) : (1 << B);
   __shared__ __align__(16) uint4 s_q[(kIpNuMax + kIpNsMax) * 64];
   __shared__ __align__(16) uint32_t s_tab[TABW];
   __shared__ uint32_t s_st[kIpWaves][16 * 64];      // the wave's 16 idx rows
   __shared__ uint32_t s_ss[kIpWaves][16 * 8];       // and their sign rows
-  __shared__ float s_ls[kIpTopkMax][kIpWaves * 32];  // per-lane lists, slot-major
-  __shared__ int32_t s_li[kIpTopkMax][kIpWaves * 32];
+  __shared__ float s_ls[LM][kIpWaves * 32];  // per-lane lists, slot-major
+  __shared__ int32_t s_li[LM][kIpWaves * 32];
   __shared__ float s_cinit[8];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int c16 = lane & 15, g4 = lane >> 4;
@@ -674,8 +716,9 @@ struct IMArgs {
   const int32_t* cand_i;
   int64_t nq;
   int n_chunks, k;
-  int64_t* out_idx;
+  int64_t* out_idx;     // final indices (-1: none), or null
   float* out_score;
+  int32_t* out_i32;     // candidate indices (kNoIndex: none), when out_idx is null
 };
 
 // One wave per query: k rounds, each picking the best candidate that comes
@@ -706,7 +749,8 @@ __global__ void __launch_bounds__(64) k_ip_merge(IMArgs a) {
     }
     if (lane == 0) {
       a.out_score[q * a.k + o] = bs;
-      a.out_idx[q * a.k + o] = (bi == kNoIndex) ? -1 : (int64_t)bi;
+      if (a.out_idx) a.out_idx[q * a.k + o] = (bi == kNoIndex) ? -1 : (int64_t)bi;
+      else a.out_i32[q * a.k + o] = bi;
     }
     ps = bs;
     pi = bi;
@@ -715,18 +759,254 @@ __global__ void __launch_bounds__(64) k_ip_merge(IMArgs a) {
 
 template <int B>
 void launch_score_b(const ISArgs& a, bool qjl, dim3 grid, hipStream_t st) {
-  if (qjl) hipLaunchKernelGGL((k_ip_score<B, true>), grid, dim3(64 * kIpWaves), 0, st, a);
-  else hipLaunchKernelGGL((k_ip_score<B, false>), grid, dim3(64 * kIpWaves), 0, st, a);
+  if (a.k <= 32) {
+    if (qjl) hipLaunchKernelGGL((k_ip_score<B, true, 32>), grid, dim3(64 * kIpWaves), 0, st, a);
+    else hipLaunchKernelGGL((k_ip_score<B, false, 32>), grid, dim3(64 * kIpWaves), 0, st, a);
+  } else {
+    if (qjl) hipLaunchKernelGGL((k_ip_score<B, true, kIpCandMax>), grid, dim3(64 * kIpWaves), 0, st, a);
+    else hipLaunchKernelGGL((k_ip_score<B, false, kIpCandMax>), grid, dim3(64 * kIpWaves), 0, st, a);
+  }
+}
+
+// ------------------------------------------------------------ exact refinement
+//
+// The approximate pass keeps the kc best rows by the bf16 hi/lo MFMA score
+// A_j.  Each candidate is rescored in float64 from its codes (E_j, the
+// score's definition evaluated with q~ and t in float64), and the k best by
+// E are the answer when no other row can beat the k-th of them: a row left
+// out has A_j <= A_kc (the kc-th approximate score) and E_j <= A_j + delta,
+// so A_kc + delta < E_k settles it.  delta bounds |A_j - E_j| for every row
+// of the database from the operand rounding (q~, t and the centroids go
+// through float and a bf16 hi + lo pair, relative error <= 2^-16 + 2^-24
+// each), the float accumulation of n products (gamma_n = n u / (1 - n u),
+// u = 2^-24) and the final combination, over the bounds
+//     |scale_j <q~, c[idx_j]>| <= max|scale| sqrt(d) max|c| |q~|_2
+//     |rnorm_j <t, 2 sigma_j - 1>| <= max|rnorm| |t|_1,
+// and is doubled to cover an MFMA that rounds toward zero.  A query that
+// fails the test (near-ties at the k-th score, or a database of repeated
+// rows) is answered by an exact float64 scan of the whole database.
+
+struct IRArgs {
+  const float* acand_s;     // [nq][kc] approximate top-kc (sorted)
+  const int32_t* acand_i;
+  const double* qt64;       // [nq][256]
+  const double* tt64;
+  const double* qinfo;      // [nq][2]
+  const uint32_t* bounds;   // max |scale|, max |rnorm| (float bits)
+  const double* cent64;     // [2^bits]
+  const uint32_t* idx;      // row layout, rw words per vector
+  const uint32_t* sign;     // sw words per vector (or null)
+  const float* scale;
+  const float* rnorm;
+  int64_t nq, n_db;
+  int d, m, bits, rw, sw, nu, ns, k, kc;
+  int force_scan;           // 1: no query is settled by the candidates
+  int64_t* out_idx;
+  float* out_score;
+  int32_t* flags;           // [nq]: 1 settled by the candidates, 0 needs the scan
+  double* fb_s;             // [nq][kIpFbChunks][k] scan lists
+  int32_t* fb_i;
+};
+
+// float64 score of database row `row` from its codes; sq = q~, st = t
+// (sqrt(pi/2)/m folded in), cent = centroids, all in LDS
+__device__ double exact_score(const IRArgs& a, int64_t row, const double* sq, const double* st,
+                              const double* cent) {
+  const uint32_t* ir = a.idx + row * (int64_t)a.rw;
+  const uint32_t mask = (1u << a.bits) - 1u;
+  double mse = 0.0;
+  for (int i = 0; i < a.d; ++i) {
+    const int bit = i * a.bits, w = bit >> 5, sh = bit & 31;
+    uint32_t v = ir[w] >> sh;
+    if (sh + a.bits > 32) v |= ir[w + 1] << (32 - sh);
+    mse = fma(sq[i], cent[v & mask], mse);
+  }
+  double qj = 0.0;
+  if (a.m > 0) {
+    const uint32_t* sr = a.sign + row * (int64_t)a.sw;
+    for (int j = 0; j < a.m; ++j) qj += ((sr[j >> 5] >> (j & 31)) & 1u) ? st[j] : -st[j];
+  }
+  double s = (double)a.scale[row] * mse;
+  if (a.m > 0) s = fma((double)a.rnorm[row], qj, s);
+  return s;
+}
+
+__device__ inline bool better64(double s, int32_t i, double ps, int32_t pi) {
+  return s > ps || (s == ps && i < pi);
+}
+
+__device__ void load_exact_operands(const IRArgs& a, int64_t q, double* sq, double* st, double* cent) {
+  for (int i = threadIdx.x; i < 256; i += blockDim.x) {
+    sq[i] = a.qt64[q * 256 + i];
+    st[i] = a.tt64[q * 256 + i];
+    if (i < (1 << a.bits)) cent[i] = a.cent64[i];
+  }
+}
+
+// One wave per query: float64 scores of the kc candidates, their top k, and
+// the test that settles the query.
+__global__ void __launch_bounds__(64) k_ip_refine(IRArgs a) {
+  __shared__ double sq[256], st[256], cent[256];
+  __shared__ double es[64];
+  __shared__ int32_t ei[64];
+  __shared__ double ek;
+  const int64_t q = blockIdx.x;
+  const int lane = threadIdx.x;
+  load_exact_operands(a, q, sq, st, cent);
+  __syncthreads();
+  double e = -INFINITY;
+  int32_t id = kNoIndex;
+  if (lane < a.kc) {
+    id = a.acand_i[q * a.kc + lane];
+    if (id != kNoIndex) e = exact_score(a, id, sq, st, cent);
+  }
+  es[lane] = e;
+  ei[lane] = id;
+  if (lane == 0) ek = -INFINITY;
+  __syncthreads();
+  if (lane < a.kc) {
+    // rank by (score desc, index asc); empty slots last, in slot order
+    int rank = 0;
+    for (int j = 0; j < a.kc; ++j)
+      rank += (better64(es[j], ei[j], e, id) || (es[j] == e && ei[j] == id && j < lane)) ? 1 : 0;
+    if (rank < a.k) {
+      a.out_idx[q * a.k + rank] = (id == kNoIndex) ? -1 : (int64_t)id;
+      a.out_score[q * a.k + rank] = (id == kNoIndex) ? -INFINITY : (float)e;
+    }
+    if (rank == a.k - 1) ek = e;
+  }
+  double cm = 0.0;
+  for (int i = lane; i < (1 << a.bits); i += 64) cm = fmax(cm, fabs(cent[i]));
+  for (int o = 32; o >= 1; o >>= 1) cm = fmax(cm, __shfl_xor(cm, o));
+  __syncthreads();
+  if (lane == 0) {
+    bool ok = (int64_t)a.kc >= a.n_db;                    // every row was rescored
+    if (!ok && !a.force_scan) {
+      const double u = 0x1p-24;
+      auto gam = [u](double n) { return n * u / (1.0 - n * u); };
+      const double rel = 0x1p-16 + 0x1p-24;
+      const double bm = (double)__uint_as_float(a.bounds[0]) * sqrt((double)a.d) * cm * a.qinfo[q * 2];
+      const double bq = (double)__uint_as_float(a.bounds[1]) * a.qinfo[q * 2 + 1];
+      const double nm = 32.0 * a.nu + 16.0, nsk = 32.0 * a.ns + 16.0;
+      const double delta = 2.0 * ((2.0 * rel + rel * rel + gam(nm)) * (1.0 + 2.0 * rel) * bm +
+                                  (rel + gam(320.0) + 3.0 * gam(nsk)) * bq + 4.0 * u * (bm + bq));
+      const float akc = a.acand_s[q * a.kc + a.kc - 1];
+      ok = (double)akc + delta < ek;
+    }
+    a.flags[q] = ok ? 1 : 0;
+  }
+}
+
+// Exact scan for the queries the candidates did not settle: grid
+// (query slots, kIpFbChunks); each workgroup keeps the k best rows of its
+// share of the database by float64 score, for queries blockIdx.x,
+// blockIdx.x + gridDim.x, ...
+__global__ void __launch_bounds__(256) k_ip_fallback(IRArgs a) {
+  __shared__ double sq[256], st[256], cent[256];
+  __shared__ double ls[kIpTopkMax];
+  __shared__ int32_t li[kIpTopkMax];
+  __shared__ double bs[256];
+  __shared__ int32_t bi[256];
+  __shared__ uint64_t bal[4];
+  const int tid = threadIdx.x;
+  const int64_t per = (a.n_db + kIpFbChunks - 1) / kIpFbChunks;
+  const int64_t r0 = (int64_t)blockIdx.y * per;
+  const int64_t r1 = (r0 + per < a.n_db) ? r0 + per : a.n_db;
+  for (int64_t q = blockIdx.x; q < a.nq; q += gridDim.x) {
+    if (a.flags[q] != 0) continue;                      // uniform over the workgroup
+    __syncthreads();                                    // LDS of the previous query is free
+    load_exact_operands(a, q, sq, st, cent);
+    if (tid < kIpTopkMax) { ls[tid] = -INFINITY; li[tid] = kNoIndex; }
+    __syncthreads();
+    for (int64_t base = r0; base < r1; base += 256) {
+      const int64_t row = base + tid;
+      double s = -INFINITY;
+      int32_t id = kNoIndex;
+      if (row < r1) { s = exact_score(a, row, sq, st, cent); id = (int32_t)row; }
+      bs[tid] = s;
+      bi[tid] = id;
+      const bool pass = id != kNoIndex && better64(s, id, ls[a.k - 1], li[a.k - 1]);
+      const uint64_t b = __ballot(pass);
+      if ((tid & 63) == 0) bal[tid >> 6] = b;
+      __syncthreads();
+      if (tid == 0) {
+        // insert the rows that beat the k-th entry, in row order
+        for (int w = 0; w < 4; ++w) {
+          uint64_t msk = bal[w];
+          while (msk) {
+            const int t = w * 64 + __builtin_ctzll(msk);
+            msk &= msk - 1;
+            const double v = bs[t];
+            const int32_t vi = bi[t];
+            if (!better64(v, vi, ls[a.k - 1], li[a.k - 1])) continue;
+            int j = a.k - 1;
+            while (j > 0 && better64(v, vi, ls[j - 1], li[j - 1])) {
+              ls[j] = ls[j - 1];
+              li[j] = li[j - 1];
+              --j;
+            }
+            ls[j] = v;
+            li[j] = vi;
+          }
+        }
+      }
+      __syncthreads();
+    }
+    if (tid < a.k) {
+      const int64_t o = (q * kIpFbChunks + blockIdx.y) * (int64_t)a.k + tid;
+      a.fb_s[o] = ls[tid];
+      a.fb_i[o] = li[tid];
+    }
+  }
+}
+
+// One wave per unsettled query: the k best of its kIpFbChunks scan lists.
+__global__ void __launch_bounds__(64) k_ip_fbmerge(IRArgs a) {
+  const int64_t q = blockIdx.x;
+  if (a.flags[q] != 0) return;
+  const int lane = threadIdx.x;
+  const int n = kIpFbChunks * a.k;
+  const double* cs = a.fb_s + q * n;
+  const int32_t* ci = a.fb_i + q * n;
+  double ps = INFINITY;
+  int32_t pi = -1;
+  for (int o = 0; o < a.k; ++o) {
+    double bsv = -INFINITY;
+    int32_t biv = kNoIndex;
+    bool have = false;
+    for (int e = lane; e < n; e += 64) {
+      const double s = cs[e];
+      const int32_t i = ci[e];
+      if (i == kNoIndex || !better64(ps, pi, s, i)) continue;
+      if (!have || better64(s, i, bsv, biv)) { bsv = s; biv = i; have = true; }
+    }
+    for (int off = 32; off >= 1; off >>= 1) {
+      const double os = __shfl_xor(bsv, off);
+      const int32_t oi = __shfl_xor(biv, off);
+      if (better64(os, oi, bsv, biv)) { bsv = os; biv = oi; }
+    }
+    if (lane == 0) {
+      a.out_score[q * a.k + o] = (biv == kNoIndex) ? -INFINITY : (float)bsv;
+      a.out_idx[q * a.k + o] = (biv == kNoIndex) ? -1 : (int64_t)biv;
+    }
+    ps = bsv;
+    pi = biv;
+  }
 }
 
 }  // namespace
 
+// candidates of the approximate pass: k <= 10 keeps the shared-tile kernel
+// (16 candidates); larger k take twice k, at most kIpCandMax
+static int topk_candidates(int k) { return k <= 10 ? 16 : (2 * k < kIpCandMax ? 2 * k : kIpCandMax); }
+
 TopkPlan plan_topk(int64_t nq, int64_t n_db, int k, int d, int m) {
   TopkPlan p{};
   p.nq = nq; p.n_db = n_db; p.k = k;
+  p.kc = topk_candidates(k);
   p.nu = (pad32(d) + 15) / 16;
   p.ns = m > 0 ? (m + 31) / 32 : 0;
-  p.shared = k <= kIp2TopK;
+  p.shared = p.kc <= kIp2TopK;
   // query blocks of 8, padded to whole workgroups of 128 queries for the shared-tile kernel
   p.nqb = p.shared ? (nq + kIp2Queries - 1) / kIp2Queries * (kIp2Queries / 8) : (nq + 7) / 8;
   p.n_tiles = (n_db + 15) / 16;
@@ -743,47 +1023,72 @@ TopkPlan plan_topk(int64_t nq, int64_t n_db, int k, int d, int m) {
   p.n_chunks = p.n_tiles > 0 ? (int)((p.n_tiles + p.tiles_per_chunk - 1) / p.tiles_per_chunk) : 1;
   size_t off = 0;
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t kc = (size_t)p.kc, nqp = (size_t)p.nqb * 8;
   p.off_qop = off; off = al(off + (size_t)p.nqb * (p.nu + p.ns) * 64 * 16);
-  p.off_cinit = off; off = al(off + (size_t)p.nqb * 8 * 4);
-  const size_t nc = (size_t)p.nqb * 8 * p.n_chunks * (size_t)k;
+  p.off_cinit = off; off = al(off + nqp * 4);
+  const size_t nc = nqp * p.n_chunks * kc;
   p.off_cand_s = off; off = al(off + nc * 4);
   p.off_cand_i = off; off = al(off + nc * 4);
   // sample pass (shared-tile kernel, large databases): every 64th tile,
-  // 32 chunks, merged into the top k of the sample per query
+  // 32 chunks, merged into the top kc of the sample per query
   p.sample_stride = (p.shared && p.n_tiles >= 64 * 256) ? 64 : 0;
   if (p.sample_stride) {
     p.sample_tiles = p.n_tiles / p.sample_stride;
     p.sample_chunks = 32;
-    const size_t ns2 = (size_t)p.nqb * 8 * p.sample_chunks * (size_t)k;
+    const size_t ns2 = nqp * p.sample_chunks * kc;
     p.off_s_cand_s = off; off = al(off + ns2 * 4);
     p.off_s_cand_i = off; off = al(off + ns2 * 4);
-    p.off_s_idx = off; off = al(off + (size_t)nq * k * 8);
-    p.off_s_score = off; off = al(off + (size_t)nq * k * 4);
+    p.off_s_idx = off; off = al(off + (size_t)nq * kc * 8);
+    p.off_s_score = off; off = al(off + (size_t)nq * kc * 4);
   }
+  p.off_qt64 = off; off = al(off + nqp * 256 * 8);
+  p.off_tt64 = off; off = al(off + nqp * 256 * 8);
+  p.off_qinfo = off; off = al(off + nqp * 2 * 8);
+  p.off_bounds = off; off = al(off + 2 * 4);
+  p.off_acand_s = off; off = al(off + (size_t)nq * kc * 4);
+  p.off_acand_i = off; off = al(off + (size_t)nq * kc * 4);
+  p.off_flags = off; off = al(off + (size_t)nq * 4);
+  p.off_fb_s = off; off = al(off + (size_t)nq * kIpFbChunks * k * 8);
+  p.off_fb_i = off; off = al(off + (size_t)nq * kIpFbChunks * k * 4);
   p.bytes = off;
   return p;
 }
 
 hipError_t launch_topk(const tq_codebook* cb, const float* queries, const TopkPlan& plan,
                        const tq_codes& db, int64_t* out_idx, float* out_score, void* ws,
-                       hipStream_t stream) {
+                       hipStream_t stream, bool force_scan) {
   if (plan.nq == 0 || plan.k == 0) return hipSuccess;
   char* w = static_cast<char*>(ws);
   uint32_t* qop = reinterpret_cast<uint32_t*>(w + plan.off_qop);
   float* cinit = reinterpret_cast<float*>(w + plan.off_cinit);
   float* cand_s = reinterpret_cast<float*>(w + plan.off_cand_s);
   int32_t* cand_i = reinterpret_cast<int32_t*>(w + plan.off_cand_i);
+  uint32_t* bounds = reinterpret_cast<uint32_t*>(w + plan.off_bounds);
+  const bool qjl = cb->p.qjl_m > 0;
 
   IPArgs pa{};
   pa.q = queries; pa.nq = plan.nq;
   pa.d = cb->p.d; pa.m = cb->p.qjl_m; pa.dp = cb->dp; pa.mp = cb->mp;
   pa.nu = plan.nu; pa.ns = plan.ns;
-  pa.rotT = cb->dev.rotT; pa.qjlT = cb->dev.qjlT;
+  pa.rotT64 = cb->dev.rotT64; pa.qjlT64 = cb->dev.qjlT64;
   pa.qop = qop; pa.cinit = cinit;
+  pa.qt64 = reinterpret_cast<double*>(w + plan.off_qt64);
+  pa.tt64 = reinterpret_cast<double*>(w + plan.off_tt64);
+  pa.qinfo = reinterpret_cast<double*>(w + plan.off_qinfo);
+  pa.bounds = bounds;
   hipLaunchKernelGGL(k_ip_prologue, dim3((unsigned)(plan.nqb * 8)), dim3(256), 0, stream, pa);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (plan.n_db > 0) {
+    int64_t nb = (plan.n_db + 255) / 256;
+    if (nb > 1024) nb = 1024;
+    hipLaunchKernelGGL(k_ip_bounds, dim3((unsigned)nb), dim3(256), 0, stream, db.scale, qjl ? db.rnorm : nullptr,
+                       plan.n_db, bounds);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
 
+  float* acand_s = reinterpret_cast<float*>(w + plan.off_acand_s);
+  int32_t* acand_i = reinterpret_cast<int32_t*>(w + plan.off_acand_i);
   ISArgs sa{};
   sa.qop = qop; sa.cinit = cinit;
   sa.idx = static_cast<const uint32_t*>(db.idx);
@@ -792,69 +1097,90 @@ hipError_t launch_topk(const tq_codebook* cb, const float* queries, const TopkPl
   sa.tab = cb->dev.pair_tab;
   sa.n_db = plan.n_db; sa.n_tiles = plan.n_tiles; sa.tiles_per_chunk = plan.tiles_per_chunk;
   sa.rw = (int)(db.idx_row_bytes / 4);
-  sa.sw = cb->p.qjl_m > 0 ? (int)(db.sign_row_bytes / 4) : 0;
-  sa.nu = plan.nu; sa.ns = plan.ns; sa.k = plan.k; sa.n_chunks = plan.n_chunks;
+  sa.sw = qjl ? (int)(db.sign_row_bytes / 4) : 0;
+  sa.nu = plan.nu; sa.ns = plan.ns; sa.k = plan.kc; sa.n_chunks = plan.n_chunks;
   sa.cand_s = cand_s; sa.cand_i = cand_i;
-  const bool qjl = cb->p.qjl_m > 0;
-  if (plan.shared) {
-    IS2Args s2{};
-    s2.qop = qop; s2.cinit = cinit;
-    s2.idx = sa.idx; s2.sign = sa.sign; s2.scale = sa.scale; s2.rnorm = qjl ? sa.rnorm : sa.scale;
-    s2.tab = sa.tab;
-    s2.n_db = plan.n_db; s2.n_tiles = plan.n_tiles; s2.tiles_per_chunk = plan.tiles_per_chunk;
-    s2.rw = sa.rw; s2.sw = sa.sw; s2.bits = cb->p.bits; s2.nu = plan.nu; s2.ns = plan.ns;
-    s2.k = plan.k; s2.n_chunks = plan.n_chunks;
-    s2.cand_s = cand_s; s2.cand_i = cand_i;
-    s2.tstride = 1;
-    s2.nq = plan.nq;
-    s2.floor_s = nullptr;
-    const unsigned groups = (unsigned)(plan.nqb / (kIp2Queries / 8));
+  {
     ProfileScope prof(TQ_KERNEL_TOPK, stream);
-    if (plan.sample_stride) {
-      IS2Args sp = s2;
-      sp.tstride = plan.sample_stride;
-      sp.n_tiles = plan.sample_tiles;
-      sp.n_chunks = plan.sample_chunks;
-      sp.tiles_per_chunk = (plan.sample_tiles + plan.sample_chunks - 1) / plan.sample_chunks;
-      sp.cand_s = reinterpret_cast<float*>(w + plan.off_s_cand_s);
-      sp.cand_i = reinterpret_cast<int32_t*>(w + plan.off_s_cand_i);
-      launch_score2<2>(sp, dim3((unsigned)plan.sample_chunks, groups), stream);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-      IMArgs sm{};
-      sm.cand_s = sp.cand_s; sm.cand_i = sp.cand_i;
-      sm.nq = plan.nq; sm.n_chunks = plan.sample_chunks; sm.k = plan.k;
-      sm.out_idx = reinterpret_cast<int64_t*>(w + plan.off_s_idx);
-      sm.out_score = reinterpret_cast<float*>(w + plan.off_s_score);
-      hipLaunchKernelGGL(k_ip_merge, dim3((unsigned)plan.nq), dim3(64), 0, stream, sm);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-      s2.floor_s = sm.out_score;
+    if (plan.shared) {
+      IS2Args s2{};
+      s2.qop = qop; s2.cinit = cinit;
+      s2.idx = sa.idx; s2.sign = sa.sign; s2.scale = sa.scale; s2.rnorm = qjl ? sa.rnorm : sa.scale;
+      s2.tab = sa.tab;
+      s2.n_db = plan.n_db; s2.n_tiles = plan.n_tiles; s2.tiles_per_chunk = plan.tiles_per_chunk;
+      s2.rw = sa.rw; s2.sw = sa.sw; s2.bits = cb->p.bits; s2.nu = plan.nu; s2.ns = plan.ns;
+      s2.k = plan.kc; s2.n_chunks = plan.n_chunks;
+      s2.cand_s = cand_s; s2.cand_i = cand_i;
+      s2.tstride = 1;
+      s2.nq = plan.nq;
+      s2.floor_s = nullptr;
+      const unsigned groups = (unsigned)(plan.nqb / (kIp2Queries / 8));
+      if (plan.sample_stride) {
+        IS2Args sp = s2;
+        sp.tstride = plan.sample_stride;
+        sp.n_tiles = plan.sample_tiles;
+        sp.n_chunks = plan.sample_chunks;
+        sp.tiles_per_chunk = (plan.sample_tiles + plan.sample_chunks - 1) / plan.sample_chunks;
+        sp.cand_s = reinterpret_cast<float*>(w + plan.off_s_cand_s);
+        sp.cand_i = reinterpret_cast<int32_t*>(w + plan.off_s_cand_i);
+        launch_score2<2>(sp, dim3((unsigned)plan.sample_chunks, groups), stream);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        IMArgs sm{};
+        sm.cand_s = sp.cand_s; sm.cand_i = sp.cand_i;
+        sm.nq = plan.nq; sm.n_chunks = plan.sample_chunks; sm.k = plan.kc;
+        sm.out_idx = reinterpret_cast<int64_t*>(w + plan.off_s_idx);
+        sm.out_score = reinterpret_cast<float*>(w + plan.off_s_score);
+        hipLaunchKernelGGL(k_ip_merge, dim3((unsigned)plan.nq), dim3(64), 0, stream, sm);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        s2.floor_s = sm.out_score;
+      }
+      launch_score2<2>(s2, dim3((unsigned)plan.n_chunks, groups), stream);
+    } else {
+      const dim3 grid((unsigned)plan.n_chunks, (unsigned)plan.nqb);
+      switch (cb->p.bits) {
+        case 1: launch_score_b<1>(sa, qjl, grid, stream); break;
+        case 2: launch_score_b<2>(sa, qjl, grid, stream); break;
+        case 3: launch_score_b<3>(sa, qjl, grid, stream); break;
+        case 4: launch_score_b<4>(sa, qjl, grid, stream); break;
+        case 5: launch_score_b<5>(sa, qjl, grid, stream); break;
+        case 6: launch_score_b<6>(sa, qjl, grid, stream); break;
+        case 7: launch_score_b<7>(sa, qjl, grid, stream); break;
+        default: launch_score_b<8>(sa, qjl, grid, stream); break;
+      }
     }
-    launch_score2<2>(s2, dim3((unsigned)plan.n_chunks, groups), stream);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  } else {
-    const dim3 grid((unsigned)plan.n_chunks, (unsigned)plan.nqb);
-    ProfileScope prof(TQ_KERNEL_TOPK, stream);
-    switch (cb->p.bits) {
-      case 1: launch_score_b<1>(sa, qjl, grid, stream); break;
-      case 2: launch_score_b<2>(sa, qjl, grid, stream); break;
-      case 3: launch_score_b<3>(sa, qjl, grid, stream); break;
-      case 4: launch_score_b<4>(sa, qjl, grid, stream); break;
-      case 5: launch_score_b<5>(sa, qjl, grid, stream); break;
-      case 6: launch_score_b<6>(sa, qjl, grid, stream); break;
-      case 7: launch_score_b<7>(sa, qjl, grid, stream); break;
-      default: launch_score_b<8>(sa, qjl, grid, stream); break;
-    }
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
 
   IMArgs ma{};
   ma.cand_s = cand_s; ma.cand_i = cand_i;
-  ma.nq = plan.nq; ma.n_chunks = plan.n_chunks; ma.k = plan.k;
-  ma.out_idx = out_idx; ma.out_score = out_score;
+  ma.nq = plan.nq; ma.n_chunks = plan.n_chunks; ma.k = plan.kc;
+  ma.out_idx = nullptr; ma.out_score = acand_s; ma.out_i32 = acand_i;
   hipLaunchKernelGGL(k_ip_merge, dim3((unsigned)plan.nq), dim3(64), 0, stream, ma);
-  return hipGetLastError();
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+
+  IRArgs ra{};
+  ra.acand_s = acand_s; ra.acand_i = acand_i;
+  ra.qt64 = pa.qt64; ra.tt64 = pa.tt64; ra.qinfo = pa.qinfo; ra.bounds = bounds;
+  ra.cent64 = cb->dev.cent64;
+  ra.idx = sa.idx; ra.sign = sa.sign; ra.scale = db.scale; ra.rnorm = db.rnorm;
+  ra.nq = plan.nq; ra.n_db = plan.n_db;
+  ra.d = cb->p.d; ra.m = cb->p.qjl_m; ra.bits = cb->p.bits; ra.rw = sa.rw; ra.sw = sa.sw;
+  ra.nu = plan.nu; ra.ns = plan.ns; ra.k = plan.k; ra.kc = plan.kc;
+  ra.force_scan = force_scan ? 1 : 0;
+  ra.out_idx = out_idx; ra.out_score = out_score;
+  ra.flags = reinterpret_cast<int32_t*>(w + plan.off_flags);
+  ra.fb_s = reinterpret_cast<double*>(w + plan.off_fb_s);
+  ra.fb_i = reinterpret_cast<int32_t*>(w + plan.off_fb_i);
+  hipLaunchKernelGGL(k_ip_refine, dim3((unsigned)plan.nq), dim3(64), 0, stream, ra);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((int64_t)plan.kc < plan.n_db) {
+    const unsigned slots = (unsigned)(plan.nq < 4096 ? plan.nq : 4096);
+    hipLaunchKernelGGL(k_ip_fallback, dim3(slots, (unsigned)kIpFbChunks), dim3(256), 0, stream, ra);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(k_ip_fbmerge, dim3((unsigned)plan.nq), dim3(64), 0, stream, ra);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace tq

@@ -2,6 +2,7 @@
 // Every exported function catches everything and reports through
 // tq_last_error(); no exception crosses the ABI.
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -14,6 +15,7 @@
 namespace tq {
 namespace {
 thread_local std::string g_err;
+std::atomic<int> g_topk_force_scan{0};   // tq_ip_topk_exact_scan
 
 uint16_t bf16_rne(float f) {
   uint32_t u;
@@ -128,6 +130,9 @@ void free_dev(DeviceCodebook& d) {
   if (d.dqcs) (void)hipFree(d.dqcs);
   if (d.pair_tab) (void)hipFree(d.pair_tab);
   if (d.quad_tab) (void)hipFree(d.quad_tab);
+  if (d.rotT64) (void)hipFree(d.rotT64);
+  if (d.qjlT64) (void)hipFree(d.qjlT64);
+  if (d.cent64) (void)hipFree(d.cent64);
   if (d.rop) (void)hipFree(d.rop);
   if (d.qtab) (void)hipFree(d.qtab);
   if (d.sop) (void)hipFree(d.sop);
@@ -319,6 +324,19 @@ tq_status tq_codebook_build(const tq_params* params, tq_codebook** out) {
       }
     }
     cb->dev.pair_tab_dwords = (int)tab.size();
+    {
+      // float64 tables of the exact top-k refinement
+      std::vector<double> rt((size_t)d * d), st(m > 0 ? (size_t)d * m : 0);
+      for (int i = 0; i < d; ++i)
+        for (int k2 = 0; k2 < d; ++k2) rt[(size_t)k2 * d + i] = cb->host.rot[(size_t)i * d + k2];
+      for (int j = 0; j < m; ++j)
+        for (int i = 0; i < d; ++i) st[(size_t)i * m + j] = cb->host.qjl[(size_t)j * d + i];
+      if ((e = upload(&cb->dev.rotT64, rt)) != hipSuccess || (e = upload(&cb->dev.cent64, cb->host.centroids)) != hipSuccess ||
+          (m > 0 && (e = upload(&cb->dev.qjlT64, st)) != hipSuccess)) {
+        release_pending();
+        return hip_fail(e, "codebook upload");
+      }
+    }
     if (cb->p.bits <= 3) {
       const int b = cb->p.bits;
       const size_t n4 = (size_t)1 << (4 * b);
@@ -887,6 +905,12 @@ tq_status tq_ip_topk_workspace(int64_t nq, int64_t n_db, int32_t k, int32_t d, s
   return TQ_OK;
 }
 
+tq_status tq_ip_topk_exact_scan(int32_t always) {
+  if (always != 0 && always != 1) return fail(TQ_ERR_INVALID, "always must be 0 or 1");
+  g_topk_force_scan.store(always);
+  return TQ_OK;
+}
+
 tq_status tq_ip_topk(const tq_codebook* cb, const float* queries, int64_t nq,
                      const tq_codes* db, int64_t n_db, int32_t k, int64_t* out_idx,
                      float* out_score, void* workspace, size_t ws_bytes, void* stream) {
@@ -917,7 +941,7 @@ tq_status tq_ip_topk(const tq_codebook* cb, const float* queries, int64_t nq,
     if (!aligned(queries, 4) || !aligned(out_idx, 8) || !aligned(out_score, 4))
       return fail(TQ_ERR_INVALID, "queries, out_idx and out_score must be naturally aligned");
     hipError_t e = launch_topk(cb, queries, plan, *db, out_idx, out_score, workspace,
-                               static_cast<hipStream_t>(stream));
+                               static_cast<hipStream_t>(stream), g_topk_force_scan.load() != 0);
     if (e != hipSuccess) return hip_fail(e, "top-k launch");
     return TQ_OK;
   } catch (...) {

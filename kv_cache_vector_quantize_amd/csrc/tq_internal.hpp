@@ -63,6 +63,11 @@ struct DeviceCodebook {
   //  hi(c[c]) | hi(c[d]) << 16, lo(c[c]) | lo(c[d]) << 16}: one 16-byte read
   //  gives the decode key operand of four coordinates
   uint32_t* quad_tab = nullptr;
+  // exact top-k refinement (float64): rotT64 [d][d] = Pi^T, qjlT64 [d][m]
+  // = S^T (or null), cent64 [L] centroids
+  double* rotT64 = nullptr;
+  double* qjlT64 = nullptr;
+  double* cent64 = nullptr;
   // d = 128 quantize (see quantize128.hip), absent for other d:
   //  rop: Pi as bf16 operands of v_mfma_f32_32x32x16_bf16 in three parts
   //  (hi, lo, lo2), uint4 [wave 4][k-step 8][part 3][lane 64]; lane l of wave
@@ -213,25 +218,35 @@ bool decode_supported(const tq_codebook* kcb, const tq_codebook* vcb);
 
 // Inner-product top-k (limits of the LDS-resident per-lane lists and operands)
 constexpr int kIpTopkMax = 32;   // k
+constexpr int kIpCandMax = 64;   // candidates of the approximate pass (k > 10: 2k)
 constexpr int kIpNuMax = 16;     // MSE MFMAs per query block: dp / 16 (d <= 256)
 constexpr int kIpNsMax = 8;      // sign MFMAs: ceil(m / 32) (m <= 256)
 constexpr int64_t kIpMaxRowBytes = 256, kIpMaxSignRowBytes = 32;
 
+constexpr int kIpFbChunks = 64;   // workgroups per query of the exact fallback scan
+
 struct TopkPlan {
   int64_t nq, n_db, nqb, n_tiles, tiles_per_chunk;
   int k, nu, ns, n_chunks;
+  int kc;               // candidates per query of the approximate pass (>= k)
   bool shared;          // k <= 16: workgroups of 128 queries share unpacked tiles
   int64_t sample_stride, sample_tiles;   // sample pass over every sample_stride-th tile (0: none)
   int sample_chunks;
   size_t off_s_cand_s, off_s_cand_i, off_s_idx, off_s_score;
-  size_t off_qop, off_cinit, off_cand_s, off_cand_i, bytes;
+  size_t off_qop, off_cinit, off_cand_s, off_cand_i;
+  // exact refinement: float64 rotated query and sketch [nqp][d], [nqp][m],
+  // per-query norms, database bounds, the approximate top-kc, flags and the
+  // fallback lists [nq][kIpFbChunks][k]
+  size_t off_qt64, off_tt64, off_qinfo, off_bounds, off_acand_s, off_acand_i, off_flags, off_fb_s, off_fb_i;
+  size_t bytes;
 };
 
 TopkPlan plan_topk(int64_t nq, int64_t n_db, int k, int d, int m);
 
+// force_scan: every query takes the exact scan
 hipError_t launch_topk(const tq_codebook* cb, const float* queries, const TopkPlan& plan,
                        const tq_codes& db, int64_t* out_idx, float* out_score, void* ws,
-                       hipStream_t stream);
+                       hipStream_t stream, bool force_scan);
 
 // Allocation-free decode: the fixed per-device scratch array (bytes) and its
 // device address on the current device (looked up on the first call there).

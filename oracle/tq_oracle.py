@@ -473,6 +473,18 @@ def code_scores(kcb: Codebook, q, idx, scale, sign=None, rnorm=None):
     return s
 
 
+def code_scores_many(kcb: Codebook, queries, idx, scale, sign=None, rnorm=None):
+    """code_scores of several queries [nq, d] at once, as a matrix [n, nq]:
+    the same two terms, each one matrix product over all queries."""
+    qt = np.asarray(queries, dtype=np.float64) @ kcb.rot.T            # row i: Pi q_i
+    s = np.asarray(scale, dtype=np.float64)[:, None] * (kcb.centroids[np.asarray(idx)] @ qt.T)
+    if sign is not None and kcb.m > 0:
+        tq = qt @ kcb.qjl.T                                             # row i: S Pi q_i
+        pm = 2.0 * np.asarray(sign, dtype=np.float64) - 1.0
+        s = s + (SQRT_HALF_PI / kcb.m) * np.asarray(rnorm, dtype=np.float64)[:, None] * (pm @ tq.T)
+    return s
+
+
 def attn_decode(kcb: Codebook, vcb: Codebook, q, kc: dict, vc: dict, sm_scale: float,
                 n_valid=None):
     """q [B, Hq, d]; kc/vc hold unpacked codes with leading dims [B, Hkv, N]:

@@ -139,3 +139,10 @@ def test_solver_limit_forces_numeric_error():
     v = tq.tq_codebook_values(128, 4)
     ref = O.Codebook(128, 4)
     assert np.max(np.abs(v["centroids"] - ref.centroids)) < 1e-10
+
+
+def test_exact_scan_switch_validated():
+    L = tq.lib()
+    assert L.tq_ip_topk_exact_scan(2) == _lib.TQ_ERR_INVALID
+    assert b"always" in L.tq_last_error()
+    assert L.tq_ip_topk_exact_scan(0) == _lib.TQ_OK

@@ -307,3 +307,21 @@ def test_dequantize_sketch_term_is_unbiased_over_sketches():
     expect = math.sqrt(d * (math.pi / 2) * D / (m * n))
     assert np.all(rel < 4 * expect), (rel, expect)
     assert np.all(rel0 > 0.5 * math.sqrt(D)), (rel0, D)
+
+
+@pytest.mark.parametrize("m,nc", [(0, False), (40, False), (24, True)])
+def test_code_scores_many_match_dequantized_keys(m, nc):
+    # the batched scores equal <q_i, x_hat_j> with explicit dequantization,
+    # for every query and row (a transposed operand or a dropped sketch term
+    # fails this)
+    d = 48
+    cb = O.Codebook(d, 3, qjl_m=m, nc=nc)
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((70, d))
+    qs = rng.standard_normal((9, d))
+    q = O.quantize(cb, x)
+    xh = O.dequantize(cb, q["idx"], q["scale"], q.get("sign"), q.get("rnorm"))
+    s = O.code_scores_many(cb, qs, q["idx"], q["scale"], q.get("sign"), q.get("rnorm"))
+    assert s.shape == (70, 9)
+    ref = xh @ qs.T
+    assert np.max(np.abs(s - ref)) < 1e-11 * np.max(np.abs(ref))
