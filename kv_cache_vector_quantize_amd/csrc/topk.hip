@@ -35,43 +35,10 @@
 // k_ip_score     (k > 16) the same product with one 8-query block per
 //                workgroup and each wave unpacking its own tiles.
 // k_ip_merge     one wave per query selects the final k from the candidates.
-#include "tq_internal.hpp"
+#include "topk_common.hpp"
 
 namespace tq {
 namespace {
-
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kIpWaves = 4;
-constexpr int kSignShiftIp = 64;    // the sketch-query operand carries 2^-64
-constexpr int32_t kNoIndex = 0x7FFFFFFF;
-
-__device__ inline uint32_t bf16_rne_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-
-__device__ inline f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ inline bf16x8 as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
-  typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
-  u32x4v v = {a, b, c, d};
-  return __builtin_bit_cast(bf16x8, v);
-}
-
-// lane j gets x[j] + x[j + 8] within each row of 16 lanes (hi + lo columns)
-__device__ inline float dpp_ror8(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
-}
-
-// (score, index) order: larger score first, then lower index
-__device__ inline bool better(float s, int32_t i, float ps, int32_t pi) {
-  return s > ps || (s == ps && i < pi);
-}
 
 // ------------------------------------------------------------ prologue
 
@@ -79,33 +46,58 @@ struct IPArgs {
   const float* q;       // [nq][d]
   int64_t nq;
   int d, m, dp, mp, nu, ns;
+  int half;             // 1: fp16 operands of k_ip_score16; 0: bf16 hi/lo operands of k_ip_score
   const double* rotT64; // [d][d], rotT64[k][i] = Pi[i][k]
   const double* qjlT64; // [d][m], qjlT64[i][j] = S[j][i]
-  uint32_t* qop;        // [nqb][nu + ns][64 lanes][4 dwords]
-  float* cinit;         // [nqb * 8]
+  uint32_t* qop;        // operand records (layout of the mode)
+  float* cinit;         // bf16 mode: [nqp] QJL accumulator offsets; fp16 mode: [nqp][2] 2^-(6+sq), 2^-st
   double* qt64;         // [nq][256] q~ = Pi q (float64)
   double* tt64;         // [nq][256] t = sqrt(pi/2)/m S q~ (float64)
-  double* qinfo;        // [nq][2] |q~|_2, |t|_1
-  uint32_t* bounds;     // [2] database max |scale|, max |rnorm| (zeroed here)
+  double* qinfo;        // [nq][kQInfo] norms for the error bound
+  uint32_t* bounds;     // [3] database max |scale|, max |rnorm|, max |c[idx]| (zeroed here)
 };
 
-// Operand layouts (lane = column j + 16 g4 of the B operand; columns 0-7 are
-// the hi parts of the block's 8 queries, 8-15 their lo parts):
+// qinfo fields: |q~|_2, |t|_1, and in fp16 mode |q~ - q^|_2, |q^|_2,
+// |t - t^|_1, |t^|_1 where q^, t^ are the operand values (unscaled)
+constexpr int kQInfo = 6;
+
+__device__ inline uint16_t f16_bits(float x) {
+  const _Float16 h = (_Float16)x;
+  return __builtin_bit_cast(uint16_t, h);
+}
+__device__ inline float f16_value(uint16_t b) {
+  return (float)__builtin_bit_cast(_Float16, b);
+}
+// x rounded to fp16, with results below the fp16 normal range taken as 0
+// (so the operand is the same whether or not the matrix unit flushes them)
+__device__ inline uint16_t f16_operand(double x) {
+  const uint16_t b = f16_bits((float)x);
+  return ((b & 0x7C00u) == 0u) ? (uint16_t)0u : b;
+}
+
+// Operand layouts.  bf16 mode (blocks of 8 queries; lane = column j + 16 g4
+// of the B operand, columns 0-7 the hi parts of the block's queries, 8-15
+// their lo parts):
 //  MSE MFMA u: element el of lane group g4 is coordinate
 //    16 u + 4 g4 + 2 (el / 4) + el % 2, matching the key operand dwords
 //    {hi pair, lo pair} of coordinate pairs (a, b) and (c, d);
 //  sign MFMA v: element el is sketch row 32 v + 8 g4 + el, scaled by
 //    2^(128 - 2^el - 64): the sign operand leaves bit el of the lane's sign
 //    byte at bf16 bit 7 + el, the normal value 2^(2^el - 127).
-// q~ and t are formed in float64 (kept for the exact refinement) and rounded
-// to float before the bf16 hi/lo split.
+// fp16 mode (blocks of 16 queries, column j = query j of the block): record
+// u < nu / 2 holds coordinates 32 u + 8 g4 + el (one operand that meets the
+// hi and then the lo parts of the centroids in two MFMAs), record nu / 2 + v
+// sketch rows 32 v + 8 g4 + el; q~ is scaled by 2^sq and t by 2^st, powers
+// of two that bring the largest component to [2^14, 2^15).
+// q~ and t are formed in float64 (kept for the exact refinement).
 __global__ void __launch_bounds__(256) k_ip_prologue(IPArgs a) {
   __shared__ double qs[256], qt[256], tt[256];
-  __shared__ double red[2][4];
+  __shared__ double red[6][4];
+  __shared__ int sexp[2];
   const int64_t qi = blockIdx.x;        // over the padded query count
   const int tid = threadIdx.x;
   const bool valid = qi < a.nq;
-  if (qi == 0 && tid < 2) a.bounds[tid] = 0u;
+  if (qi == 0 && tid < 3) a.bounds[tid] = 0u;
   qs[tid] = (valid && tid < a.d) ? (double)a.q[qi * a.d + tid] : 0.0;
   __syncthreads();
   double z = 0.0;
@@ -124,18 +116,63 @@ __global__ void __launch_bounds__(256) k_ip_prologue(IPArgs a) {
     a.qt64[qi * 256 + tid] = z;
     a.tt64[qi * 256 + tid] = t;
   }
-  {
-    double n2 = z * z, n1 = fabs(t);
-    for (int o = 32; o >= 1; o >>= 1) {
-      n2 += __shfl_xor(n2, o);
-      n1 += __shfl_xor(n1, o);
-    }
-    if ((tid & 63) == 0) { red[0][tid >> 6] = n2; red[1][tid >> 6] = n1; }
+  // operand scales (fp16 mode): exponents of the largest |q~_i|, |t_j|
+  double mz = fabs(z), mt = fabs(t);
+  for (int o = 32; o >= 1; o >>= 1) {
+    mz = fmax(mz, __shfl_xor(mz, o));
+    mt = fmax(mt, __shfl_xor(mt, o));
+  }
+  if ((tid & 63) == 0) { red[4][tid >> 6] = mz; red[5][tid >> 6] = mt; }
+  __syncthreads();
+  if (tid < 2) {
+    const double mx = fmax(fmax(red[4 + tid][0], red[4 + tid][1]), fmax(red[4 + tid][2], red[4 + tid][3]));
+    int e = 0;
+    if (mx > 0.0) (void)frexp(mx, &e);       // mx in [2^(e-1), 2^e)
+    int sc = 15 - e;                          // mx 2^sc in [2^14, 2^15)
+    sexp[tid] = sc < -100 ? -100 : (sc > 100 ? 100 : sc);
   }
   __syncthreads();
-  if (valid && tid == 0) {
-    a.qinfo[qi * 2 + 0] = sqrt(red[0][0] + red[0][1] + red[0][2] + red[0][3]);
-    a.qinfo[qi * 2 + 1] = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+  const int sq = sexp[0], st = sexp[1];
+  // operand values and the norms of the error bound
+  double zh = 0.0, th = 0.0;
+  if (a.half) {
+    zh = ldexp((double)f16_value(f16_operand(ldexp(z, sq))), -sq);
+    th = ldexp((double)f16_value(f16_operand(ldexp(t, st))), -st);
+  }
+  {
+    double v0 = z * z, v1 = fabs(t), v2 = (z - zh) * (z - zh), v3 = zh * zh, v4 = fabs(t - th), v5 = fabs(th);
+    for (int o = 32; o >= 1; o >>= 1) {
+      v0 += __shfl_xor(v0, o); v1 += __shfl_xor(v1, o); v2 += __shfl_xor(v2, o);
+      v3 += __shfl_xor(v3, o); v4 += __shfl_xor(v4, o); v5 += __shfl_xor(v5, o);
+    }
+    __syncthreads();
+    if ((tid & 63) == 0) {
+      red[0][tid >> 6] = v0; red[1][tid >> 6] = v1; red[2][tid >> 6] = v2;
+      red[3][tid >> 6] = v3; red[4][tid >> 6] = v4; red[5][tid >> 6] = v5;
+    }
+  }
+  __syncthreads();
+  if (valid && tid < kQInfo) {
+    const double sum = red[tid][0] + red[tid][1] + red[tid][2] + red[tid][3];
+    a.qinfo[qi * kQInfo + tid] = (tid == 0 || tid == 2 || tid == 3) ? sqrt(sum) : sum;
+  }
+  if (a.half) {
+    const int64_t qb = qi >> 4;
+    const int c = (int)(qi & 15);
+    const int nh = a.nu / 2;                  // 32-coordinate groups
+    uint32_t* rec = a.qop + qb * (int64_t)(nh + a.ns) * 256;
+    for (int e = tid; e < (nh + a.ns) * 16; e += 256) {
+      const int dw = e & 3, g4 = (e >> 2) & 3, u = e >> 4;
+      uint32_t hv[2];
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int el = 2 * dw + h2;
+        hv[h2] = (u < nh) ? f16_operand(ldexp(qt[32 * u + 8 * g4 + el], sq))
+                          : f16_operand(ldexp(tt[32 * (u - nh) + 8 * g4 + el], st));
+      }
+      rec[(u * 64 + c + 16 * g4) * 4 + dw] = hv[0] | (hv[1] << 16);
+    }
+    if (tid < 2) a.cinit[qi * 2 + tid] = ldexpf(1.f, tid == 0 ? -(kTabScaleLog2 + sq) : -st);
+    return;
   }
   const int64_t qb = qi >> 3;
   const int c = (int)(qi & 7);
@@ -175,22 +212,62 @@ __global__ void __launch_bounds__(256) k_ip_prologue(IPArgs a) {
   }
 }
 
-// Database bounds of the refinement's error bound: max |scale| and max
-// |rnorm| (as float bits; non-negative floats order as their bits).
-__global__ void __launch_bounds__(256) k_ip_bounds(const float* scale, const float* rnorm, int64_t n,
-                                                   uint32_t* bounds) {
-  float ms = 0.f, mr = 0.f;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
-    ms = fmaxf(ms, fabsf(scale[i]));
-    if (rnorm) mr = fmaxf(mr, fabsf(rnorm[i]));
+// Database bounds of the refinement's error bound: max |scale|, max |rnorm|
+// and max_j |c[idx_j]|_2 (float bits; non-negative floats order as their
+// bits).  Each workgroup stages 256 rows of codes in LDS with coalesced
+// loads, then one thread per row sums c^2 over its codes in float (the
+// result is enlarged by 2^-12 relative where it is used).
+struct IBArgs {
+  const float* scale;
+  const float* rnorm;       // or null
+  const uint32_t* idx;      // row layout, rw words per vector
+  const double* cent64;
+  int64_t n;
+  int d, bits, rw;
+  uint32_t* bounds;
+};
+
+constexpr int kBoundRows = 256;
+
+__global__ void __launch_bounds__(256) k_ip_bounds(IBArgs a) {
+  __shared__ float c2[256];
+  __shared__ uint32_t rows[kBoundRows * (kIpMaxRowBytes / 4) + 1];
+  const int tid = threadIdx.x;
+  if (tid < (1 << a.bits)) {
+    const double c = a.cent64[tid];
+    c2[tid] = (float)(c * c);
+  }
+  const uint32_t mask = (1u << a.bits) - 1u;
+  float ms = 0.f, mr = 0.f, mc = 0.f;
+  for (int64_t base = (int64_t)blockIdx.x * kBoundRows; base < a.n; base += (int64_t)gridDim.x * kBoundRows) {
+    const int nr = (int)(a.n - base < kBoundRows ? a.n - base : kBoundRows);
+    const int nw = nr * a.rw;
+    const uint32_t* src = a.idx + base * a.rw;
+    __syncthreads();                     // the previous rows are consumed
+    for (int e = tid; e < nw; e += 256) rows[e] = src[e];
+    __syncthreads();
+    if (tid < nr) {
+      ms = fmaxf(ms, fabsf(a.scale[base + tid]));
+      if (a.rnorm) mr = fmaxf(mr, fabsf(a.rnorm[base + tid]));
+      const uint32_t* ir = rows + tid * a.rw;
+      float s2 = 0.f;
+      for (int c = 0; c < a.d; ++c) {
+        const int bit = c * a.bits, w = bit >> 5, sh = bit & 31;
+        const uint32_t v = __builtin_amdgcn_alignbit(ir[w + 1], ir[w], sh);   // ir[w + 1] stays in the array
+        s2 += c2[v & mask];
+      }
+      mc = fmaxf(mc, s2);
+    }
   }
   for (int o = 32; o >= 1; o >>= 1) {
     ms = fmaxf(ms, __shfl_xor(ms, o));
     mr = fmaxf(mr, __shfl_xor(mr, o));
+    mc = fmaxf(mc, __shfl_xor(mc, o));
   }
-  if ((threadIdx.x & 63) == 0) {
-    atomicMax(bounds, __float_as_uint(ms));
-    atomicMax(bounds + 1, __float_as_uint(mr));
+  if ((tid & 63) == 0) {
+    atomicMax(a.bounds, __float_as_uint(ms));
+    atomicMax(a.bounds + 1, __float_as_uint(mr));
+    atomicMax(a.bounds + 2, __float_as_uint(sqrtf(mc)));
   }
 }
 
@@ -369,346 +446,6 @@ __global__ void __launch_bounds__(64 * kIpWaves) k_ip_score(ISArgs a) {
   }
 }
 
-// ------------------------------------------------------------ scores, shared tiles
-
-constexpr int kIp2Waves = 8;        // waves per workgroup, two per SIMD
-constexpr int kIp2Blocks = 2;       // 8-query blocks per wave (their operands fit in VGPRs)
-constexpr int kIp2Queries = 8 * kIp2Waves * kIp2Blocks;   // 128 queries per workgroup
-constexpr int kIp2TopK = 16;        // largest k of this kernel
-constexpr int kIp2Lists = kIp2Queries;                        // one list per query
-constexpr int kIp2Raw = 16 * (kIpMaxRowBytes / 4) + 16 * (kIpMaxSignRowBytes / 4) + 32;  // words of a raw tile
-constexpr int kIp2IdxPer = 16 * (kIpMaxRowBytes / 4) / (64 * kIp2Waves);                   // idx words per thread
-static_assert(16 * (kIpMaxSignRowBytes / 4) + 32 <= 64 * kIp2Waves, "one sign / scalar word per thread");
-static_assert(kIp2IdxPer >= 1, "at least one idx word per thread");
-
-struct IS2Args {
-  const uint32_t* qop;
-  const float* cinit;
-  const uint32_t* idx;     // row layout, rw words per vector
-  const uint32_t* sign;    // sw words per vector (or null)
-  const float* scale;
-  const float* rnorm;
-  const uint32_t* tab;     // decode operand table of the codebook
-  int64_t n_db, n_tiles, tiles_per_chunk;
-  int64_t tstride;         // tile i of a chunk is database tile (t_begin + i) * tstride
-  int64_t nq;
-  const float* floor_s;    // [nq][k] sample top-k scores (entry k-1 is the floor), or null
-  int rw, sw, bits, nu, ns, k, n_chunks;
-  float* cand_s;           // [nq_pad][n_chunks][k]
-  int32_t* cand_i;
-};
-
-template <int NU, int NS>
-__global__ void __launch_bounds__(64 * kIp2Waves) k_ip_score2(IS2Args a) {
-  constexpr int NUS = NU + NS;
-  // tiles go in pairs between barriers: slots 2c, 2c + 1 of buffer c
-  __shared__ __align__(16) uint4 s_a[4][NUS][64];          // A operands of a tile
-  __shared__ float s_sr[4][2][16];                         // its scale and 2^64 rnorm
-  __shared__ __align__(16) uint32_t s_raw[4][kIp2Raw];     // raw code rows of a tile
-  __shared__ __align__(16) uint32_t s_tab[512];
-  __shared__ __align__(16) float s_ls[kIp2Lists][kIp2TopK];    // per-query lists (unsorted)
-  __shared__ __align__(16) int32_t s_li[kIp2Lists][kIp2TopK];
-  __shared__ float s_ws[kIp2Lists];                           // worst score of each list
-  __shared__ int s_wj[kIp2Lists];                             // and its slot
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int c16 = lane & 15, g4 = lane >> 4;
-  const int chunk = blockIdx.x;
-  const int64_t qb0 = (int64_t)blockIdx.y * (kIp2Waves * kIp2Blocks) + wave * kIp2Blocks;
-  const int B = a.bits, nu = NU, nus = NUS;
-  const int tabw = B <= 4 ? (2 << (2 * B)) : (1 << B);
-  for (int i = tid; i < tabw; i += 64 * kIp2Waves) s_tab[i] = a.tab[i];
-  // slots below k start empty (-inf, no index); slots from k on hold +inf so
-  // that they are never the worst entry
-  for (int i = tid; i < kIp2Lists * kIp2TopK; i += 64 * kIp2Waves) {
-    const bool live = (i % kIp2TopK) < a.k;
-    s_ls[i / kIp2TopK][i % kIp2TopK] = live ? -INFINITY : INFINITY;
-    s_li[i / kIp2TopK][i % kIp2TopK] = live ? kNoIndex : -1;
-  }
-  for (int i = tid; i < kIp2Lists; i += 64 * kIp2Waves) {
-    s_ws[i] = -INFINITY;
-    s_wj[i] = 0;
-  }
-  // this wave's query operands (registers) and QJL accumulator offsets
-  bf16x8 bq[kIp2Blocks][NUS];
-  float cin[kIp2Blocks];
-#pragma unroll
-  for (int qb = 0; qb < kIp2Blocks; ++qb) {
-    const uint4* src = reinterpret_cast<const uint4*>(a.qop) + (qb0 + qb) * (int64_t)nus * 64;
-#pragma unroll
-    for (int u = 0; u < NUS; ++u) bq[qb][u] = __builtin_bit_cast(bf16x8, src[u * 64 + lane]);
-    cin[qb] = (NS > 0 && c16 < 8) ? a.cinit[(qb0 + qb) * 8 + c16] : 0.f;
-  }
-
-  // fixed share of the raw tile words of this thread: up to kIp2IdxPer words
-  // of the 16 idx rows, and one word that is a sign word, a scale or an rnorm
-  const int n_idx = 16 * a.rw, n_sgn = 16 * a.sw;
-  int ioff[kIp2IdxPer], irow[kIp2IdxPer];
-#pragma unroll
-  for (int j = 0; j < kIp2IdxPer; ++j) {
-    const int e = tid + 64 * kIp2Waves * j;
-    irow[j] = e < n_idx ? e / a.rw : -1;
-    ioff[j] = e < n_idx ? e - irow[j] * a.rw : 0;
-  }
-  const uint32_t* mbase;
-  int mrow, mstr, mw;
-  if (tid < n_sgn) { mbase = a.sign; mrow = tid / a.sw; mw = tid - mrow * a.sw; mstr = a.sw; }
-  else if (tid < n_sgn + 16) { mbase = reinterpret_cast<const uint32_t*>(a.scale); mrow = tid - n_sgn; mw = 0; mstr = 1; }
-  else if (tid < n_sgn + 32) { mbase = reinterpret_cast<const uint32_t*>(a.rnorm); mrow = tid - n_sgn - 16; mw = 0; mstr = 1; }
-  else { mbase = nullptr; mrow = 0; mw = 0; mstr = 0; }
-  const int last = (int)(a.n_db - 1);
-  struct Pre {
-    uint32_t i[kIp2IdxPer];
-    uint32_t m;
-  };
-  Pre ra, rb;
-  auto raw_load = [&](Pre& P, int64_t tile) {
-    uint32_t (&pre_i)[kIp2IdxPer] = P.i;
-    uint32_t& pre_m = P.m;
-    pre_m = 0u;
-    // the tile's base is formed in 64 bits (a database may exceed 2^31
-    // words); a lane's offset from it spans at most 16 rows
-    const int64_t r0 = tile * 16;
-    const uint32_t* tbase = a.idx + r0 * a.rw;
-#pragma unroll
-    for (int j = 0; j < kIp2IdxPer; ++j) {
-      pre_i[j] = 0u;
-      if (irow[j] >= 0) {
-        const int rr = (int)(min(r0 + irow[j], (int64_t)last) - r0);   // rows past the end repeat the last one
-        pre_i[j] = tbase[rr * a.rw + ioff[j]];
-      }
-    }
-    if (mbase) pre_m = (mbase + r0 * mstr)[(int)(min(r0 + mrow, (int64_t)last) - r0) * mstr + mw];
-  };
-  // raw tile layout: idx rows [0, n_idx), sign rows [n_idx, n_idx + n_sgn),
-  // scale [.., +16), rnorm [.., +16)
-  auto raw_store = [&](const Pre& P, int buf) {
-#pragma unroll
-    for (int j = 0; j < kIp2IdxPer; ++j)
-      if (irow[j] >= 0) s_raw[buf][tid + 64 * kIp2Waves * j] = P.i[j];
-    if (mbase) s_raw[buf][n_idx + tid] = P.m;
-  };
-  // unpack raw buffer rb into operand buffer ob: task (u, lane) = tid + 512 j
-  auto build = [&](int rb, int ob) {
-    const uint32_t* raw = s_raw[rb];
-    const char* tab = reinterpret_cast<const char*>(s_tab);
-#pragma unroll
-    for (int jj = 0; jj < (NUS * 64 + 64 * kIp2Waves - 1) / (64 * kIp2Waves); ++jj) {
-      const int t = tid + 64 * kIp2Waves * jj;
-      if (t >= NUS * 64) break;
-      const int u = t >> 6, l = t & 63, r = l & 15, g = l >> 4;
-      uint32_t d0, d1, d2, d3;
-      if (u < nu) {
-        const int o = (16 * u + 4 * g) * B;
-        const int i0 = o >> 5, sh = o & 31;
-        const int i1 = (i0 + 1 < a.rw) ? i0 + 1 : i0;
-        const uint32_t f = __builtin_amdgcn_alignbit(raw[r * a.rw + i1], raw[r * a.rw + i0], sh);
-        if (B <= 4) {
-          const uint32_t pm = (1u << (2 * B)) - 1u;
-          const uint2 e0 = *reinterpret_cast<const uint2*>(tab + ((f & pm) << 3));
-          const uint2 e1 = *reinterpret_cast<const uint2*>(tab + (((f >> (2 * B)) & pm) << 3));
-          d0 = e0.x; d1 = e0.y; d2 = e1.x; d3 = e1.y;
-        } else {
-          const uint32_t cm = (1u << B) - 1u;
-          const uint32_t* t32 = reinterpret_cast<const uint32_t*>(tab);
-          const uint32_t ca = t32[f & cm], cb = t32[(f >> B) & cm];
-          const uint32_t cc = t32[(f >> (2 * B)) & cm], cd = t32[(f >> (3 * B)) & cm];
-          d0 = __builtin_amdgcn_perm(cb, ca, 0x05040100u);
-          d1 = __builtin_amdgcn_perm(cb, ca, 0x07060302u);
-          d2 = __builtin_amdgcn_perm(cd, cc, 0x05040100u);
-          d3 = __builtin_amdgcn_perm(cd, cc, 0x07060302u);
-        }
-      } else {
-        const uint32_t sb = (raw[n_idx + r * a.sw + (u - nu)] >> (8 * g)) & 0xFFu;
-        const uint32_t x7 = (sb | (sb << 16)) << 7;
-        d0 = x7 & 0x01000080u; d1 = x7 & 0x04000200u; d2 = x7 & 0x10000800u; d3 = x7 & 0x40002000u;
-      }
-      s_a[ob][u][l] = make_uint4(d0, d1, d2, d3);
-    }
-    if (tid < 32) {
-      const float v = __uint_as_float(raw[n_idx + n_sgn + tid]);
-      s_sr[ob][tid >> 4][tid & 15] = (tid < 16) ? v : v * 0x1p64f;
-    }
-  };
-
-  // thq: cached worst score of the list of this lane's query in a block.  A
-  // query's candidates are inserted in increasing row order (tile by tile,
-  // lane group g4 = 0..3 within a tile, then its 4 rows), so a candidate that
-  // only ties the worst entry loses to it and the strict tests are exact.
-  // tqf: the sample floor of the query (candidates below it cannot be in the
-  // final top k; equal ones may, so that test is not strict)
-  float thq[kIp2Blocks], tqf[kIp2Blocks];
-#pragma unroll
-  for (int qb = 0; qb < kIp2Blocks; ++qb) {
-    thq[qb] = -INFINITY;
-    const int64_t q = (qb0 + qb) * 8 + c16;
-    tqf[qb] = (a.floor_s && c16 < 8 && q < a.nq) ? a.floor_s[q * a.k + a.k - 1] : -INFINITY;
-  }
-  const int64_t t_begin = (int64_t)chunk * a.tiles_per_chunk;
-  int64_t t_end = t_begin + a.tiles_per_chunk;
-  if (t_end > a.n_tiles) t_end = a.n_tiles;
-  const int64_t nt = t_end > t_begin ? t_end - t_begin : 0;
-
-  auto dbt = [&](int64_t i) { return (t_begin + i) * a.tstride; };   // database tile of step i
-  // prologue: raw tiles 0, 1 -> slots 0, 1 -> operands; raw tiles 2, 3 ->
-  // slots 2, 3; raw tiles 4, 5 in registers
-  raw_load(ra, dbt(0));
-  raw_load(rb, dbt(1));
-  raw_store(ra, 0);
-  raw_store(rb, 1);
-  raw_load(ra, dbt(2));
-  raw_load(rb, dbt(3));
-  raw_store(ra, 2);
-  raw_store(rb, 3);
-  raw_load(ra, dbt(4));
-  raw_load(rb, dbt(5));
-  __syncthreads();
-  build(0, 0);
-  build(1, 1);
-  __syncthreads();
-
-  // one tile: its MFMAs from operand slot ab, then the unpack of raw slot
-  // ub into operand slot ub (a tile two ahead), then its scores and lists
-  auto tile_step = [&](const int ab, const int ub, const int64_t row0, const bool live)
-                       __attribute__((always_inline)) {
-    f32x4 acc[kIp2Blocks], accq[kIp2Blocks];
-#pragma unroll
-    for (int qb = 0; qb < kIp2Blocks; ++qb) {
-      acc[qb] = (f32x4){0.f, 0.f, 0.f, 0.f};
-      accq[qb] = (f32x4){cin[qb], cin[qb], cin[qb], cin[qb]};
-    }
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      const bf16x8 av = __builtin_bit_cast(bf16x8, s_a[ab][u][lane]);
-#pragma unroll
-      for (int qb = 0; qb < kIp2Blocks; ++qb) acc[qb] = mfma(av, bq[qb][u], acc[qb]);
-    }
-#pragma unroll
-    for (int v = 0; v < NS; ++v) {
-      const bf16x8 av = __builtin_bit_cast(bf16x8, s_a[ab][NU + v][lane]);
-#pragma unroll
-      for (int qb = 0; qb < kIp2Blocks; ++qb) accq[qb] = mfma(av, bq[qb][NU + v], accq[qb]);
-    }
-    // unpack a tile two ahead while the MFMAs run (past the last tile it
-    // rebuilds a slot nobody reads)
-    build(ub, ub);
-    if (!live) return;
-    float sc[4], rn[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      sc[r] = s_sr[ab][0][4 * g4 + r];
-      rn[r] = s_sr[ab][1][4 * g4 + r];
-    }
-#pragma unroll
-    for (int qb = 0; qb < kIp2Blocks; ++qb) {
-      float sv[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float v = sc[r] * (acc[qb][r] + dpp_ror8(acc[qb][r]));
-        if constexpr (NS > 0) v = fmaf(rn[r], accq[qb][r] + dpp_ror8(accq[qb][r]), v);
-        sv[r] = (row0 + 4 * g4 + r < a.n_db) ? v : -INFINITY;
-      }
-      uint32_t pm = 0u;                 // rows of this lane that beat the cached worst
-#pragma unroll
-      for (int r = 0; r < 4; ++r) pm |= (c16 < 8 && sv[r] > thq[qb] && sv[r] >= tqf[qb]) ? (1u << r) : 0u;
-      if (__ballot(pm != 0u) != 0ull) {
-        const int li = (wave * kIp2Blocks + qb) * 8 + c16;     // list of this lane's query
-        for (int g = 0; g < 4; ++g) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const bool me = g4 == g && ((pm >> r) & 1u);
-            if (__ballot(me) != 0ull && me) {
-              if (sv[r] > s_ws[li]) {
-                const int wj = s_wj[li];
-                s_ls[li][wj] = sv[r];
-                s_li[li][wj] = (int32_t)(row0 + 4 * g4 + r);
-                // new worst: lowest score, then highest index
-                float ws = INFINITY;
-                int32_t wi = -1;
-                int nj = 0;
-#pragma unroll
-                for (int c4 = 0; c4 < kIp2TopK / 4; ++c4) {
-                  const float4 sc4 = reinterpret_cast<const float4*>(s_ls[li])[c4];
-                  const int4 id4 = reinterpret_cast<const int4*>(s_li[li])[c4];
-                  const float sa[4] = {sc4.x, sc4.y, sc4.z, sc4.w};
-                  const int32_t ia[4] = {id4.x, id4.y, id4.z, id4.w};
-#pragma unroll
-                  for (int e = 0; e < 4; ++e) {
-                    const bool worse = sa[e] < ws || (sa[e] == ws && ia[e] > wi);
-                    ws = worse ? sa[e] : ws;
-                    wi = worse ? ia[e] : wi;
-                    nj = worse ? 4 * c4 + e : nj;
-                  }
-                }
-                s_ws[li] = ws;
-                s_wj[li] = nj;
-              }
-            }
-          }
-        }
-        if (c16 < 8) thq[qb] = s_ws[li];
-      }
-    }
-  };
-
-  const int64_t np = (nt + 1) / 2;
-  for (int64_t p = 0; p < np; ++p) {
-    const int c = (int)(p & 1), n = c ^ 1;
-    // tiles 2p, 2p + 1 sit in operand slots 2c, 2c + 1; raw tiles 2p + 2,
-    // 2p + 3 in raw slots 2n, 2n + 1; raw tiles 2p + 4, 2p + 5 in ra, rb
-    tile_step(2 * c, 2 * n, dbt(2 * p) * 16, true);
-    tile_step(2 * c + 1, 2 * n + 1, dbt(2 * p + 1) * 16, 2 * p + 1 < nt);
-    // raw slots 2c, 2c + 1 were unpacked before the last barrier
-    raw_store(ra, 2 * c);
-    raw_store(rb, 2 * c + 1);
-    raw_load(ra, dbt(2 * p + 6));
-    raw_load(rb, dbt(2 * p + 7));
-    __syncthreads();
-  }
-
-  // sort each query's list into its k candidates, (score desc, index asc)
-  if (tid < kIp2Queries) {
-    const int li = tid;      // list of query tid of the workgroup
-    const int64_t q = (int64_t)blockIdx.y * kIp2Queries + tid;
-    const int64_t base = (q * a.n_chunks + chunk) * (int64_t)a.k;
-    float ps = INFINITY;
-    int32_t pi = -1;
-    for (int o = 0; o < a.k; ++o) {
-      float bs = -INFINITY;
-      int32_t bi = kNoIndex;
-      for (int j = 0; j < a.k; ++j) {
-        const float hs = s_ls[li][j];
-        const int32_t hi = s_li[li][j];
-        if (better(ps, pi, hs, hi) && better(hs, hi, bs, bi)) { bs = hs; bi = hi; }
-      }
-      a.cand_s[base + o] = bs;
-      a.cand_i[base + o] = bi;
-      ps = bs;
-      pi = bi;
-    }
-  }
-}
-
-template <int NU, int NS>
-void launch_score2_ns(const IS2Args& a, int ns, dim3 grid, hipStream_t st) {
-  if constexpr (NS > kIpNsMax) {
-    (void)a; (void)ns; (void)grid; (void)st;
-  } else {
-    if (ns == NS) hipLaunchKernelGGL((k_ip_score2<NU, NS>), grid, dim3(64 * kIp2Waves), 0, st, a);
-    else launch_score2_ns<NU, NS + 1>(a, ns, grid, st);
-  }
-}
-
-// NU = dp / 16 is even (dp is a multiple of 32)
-template <int NU>
-void launch_score2(const IS2Args& a, dim3 grid, hipStream_t st) {
-  if constexpr (NU > kIpNuMax) {
-    (void)a; (void)grid; (void)st;
-  } else {
-    if (a.nu == NU) launch_score2_ns<NU, 0>(a, a.ns, grid, st);
-    else launch_score2<NU + 2>(a, grid, st);
-  }
-}
-
 // ------------------------------------------------------------ final merge
 
 struct IMArgs {
@@ -799,7 +536,9 @@ struct IRArgs {
   const float* scale;
   const float* rnorm;
   int64_t nq, n_db;
-  int d, m, bits, rw, sw, nu, ns, k, kc;
+  int d, m, bits, rw, sw, nu, ns, k, kc, dp, mp;
+  int half;                 // candidates from the fp16 kernel (else bf16 hi/lo)
+  double emax_c;            // max_l |c_l - (hi + lo)_l| of the fp16 centroid operands
   int force_scan;           // 1: no query is settled by the candidates
   int64_t* out_idx;
   float* out_score;
@@ -858,6 +597,7 @@ __global__ void __launch_bounds__(64) k_ip_refine(IRArgs a) {
   int32_t id = kNoIndex;
   if (lane < a.kc) {
     id = a.acand_i[q * a.kc + lane];
+    if (id < 0 || (int64_t)id >= a.n_db) id = kNoIndex;      // empty slot
     if (id != kNoIndex) e = exact_score(a, id, sq, st, cent);
   }
   es[lane] = e;
@@ -875,21 +615,35 @@ __global__ void __launch_bounds__(64) k_ip_refine(IRArgs a) {
     }
     if (rank == a.k - 1) ek = e;
   }
-  double cm = 0.0;
-  for (int i = lane; i < (1 << a.bits); i += 64) cm = fmax(cm, fabs(cent[i]));
-  for (int o = 32; o >= 1; o >>= 1) cm = fmax(cm, __shfl_xor(cm, o));
   __syncthreads();
   if (lane == 0) {
     bool ok = (int64_t)a.kc >= a.n_db;                    // every row was rescored
     if (!ok && !a.force_scan) {
       const double u = 0x1p-24;
       auto gam = [u](double n) { return n * u / (1.0 - n * u); };
-      const double rel = 0x1p-16 + 0x1p-24;
-      const double bm = (double)__uint_as_float(a.bounds[0]) * sqrt((double)a.d) * cm * a.qinfo[q * 2];
-      const double bq = (double)__uint_as_float(a.bounds[1]) * a.qinfo[q * 2 + 1];
-      const double nm = 32.0 * a.nu + 16.0, nsk = 32.0 * a.ns + 16.0;
-      const double delta = 2.0 * ((2.0 * rel + rel * rel + gam(nm)) * (1.0 + 2.0 * rel) * bm +
-                                  (rel + gam(320.0) + 3.0 * gam(nsk)) * bq + 4.0 * u * (bm + bq));
+      const double smax = (double)__uint_as_float(a.bounds[0]);
+      const double rmax = (double)__uint_as_float(a.bounds[1]);
+      const double cn = (double)__uint_as_float(a.bounds[2]) * (1.0 + 0x1p-12);   // >= max_j |c[idx_j]|_2
+      const double* qi = a.qinfo + q * kQInfo;
+      double delta;
+      if (a.half) {
+        // fp16 operands: exact rounding residuals of the query operands,
+        // the centroid table's rounding, accumulation and the final combination
+        const double sd = sqrt((double)a.d);
+        const double cc = (1.0 + 0x1p-9) * (cn + sd * a.emax_c);   // >= | |c^hi| + |c^lo| |_2
+        const double em = smax * (cn * qi[2] + sd * a.emax_c * qi[3]);
+        const double et = rmax * qi[4];
+        const double ea = 2.0 * (gam(2.0 * a.dp + 16.0) * smax * cc * qi[3] + gam(a.mp + 16.0) * rmax * qi[5]);
+        const double ef = 4.0 * u * (smax * cc * qi[3] + rmax * qi[5]);
+        delta = 1.5 * (em + et + ea + ef);
+      } else {
+        const double rel = 0x1p-16 + 0x1p-24;
+        const double bm = smax * cn * qi[0];
+        const double bq = rmax * qi[1];
+        const double nm = 32.0 * a.nu + 16.0, nsk = 32.0 * a.ns + 16.0;
+        delta = 2.0 * ((2.0 * rel + rel * rel + gam(nm)) * (1.0 + 2.0 * rel) * bm +
+                       (rel + gam(320.0) + 3.0 * gam(nsk)) * bq + 4.0 * u * (bm + bq));
+      }
       const float akc = a.acand_s[q * a.kc + a.kc - 1];
       ok = (double)akc + delta < ek;
     }
@@ -996,8 +750,8 @@ __global__ void __launch_bounds__(64) k_ip_fbmerge(IRArgs a) {
 
 }  // namespace
 
-// candidates of the approximate pass: k <= 10 keeps the shared-tile kernel
-// (16 candidates); larger k take twice k, at most kIpCandMax
+// candidates of the approximate pass: k <= 10 keeps 16, larger k twice k
+// (at most kIpCandMax)
 static int topk_candidates(int k) { return k <= 10 ? 16 : (2 * k < kIpCandMax ? 2 * k : kIpCandMax); }
 
 TopkPlan plan_topk(int64_t nq, int64_t n_db, int k, int d, int m) {
@@ -1006,13 +760,16 @@ TopkPlan plan_topk(int64_t nq, int64_t n_db, int k, int d, int m) {
   p.kc = topk_candidates(k);
   p.nu = (pad32(d) + 15) / 16;
   p.ns = m > 0 ? (m + 31) / 32 : 0;
-  p.shared = p.kc <= kIp2TopK;
-  // query blocks of 8, padded to whole workgroups of 128 queries for the shared-tile kernel
-  p.nqb = p.shared ? (nq + kIp2Queries - 1) / kIp2Queries * (kIp2Queries / 8) : (nq + 7) / 8;
+  // kc <= 32: fp16 shared-tile kernel, 256 (kc <= 16) or 128 queries per
+  // workgroup in blocks of 16; else the bf16 kernel with blocks of 8
+  p.shared = p.kc <= 32;
+  const int qw = p.kc <= 16 ? 256 : 128;
+  p.nqb = p.shared ? (nq + qw - 1) / qw * (qw / 16) : (nq + 7) / 8;
+  const int64_t nqp = p.nqb * (p.shared ? 16 : 8);
   p.n_tiles = (n_db + 15) / 16;
-  const int64_t groups = p.shared ? p.nqb / (kIp2Queries / 8) : p.nqb;
-  // workgroups: shared tiles take 122 KB of LDS, one workgroup per CU, so
-  // 256 is one round over the CUs (3% faster than two rounds at 10^6 rows)
+  const int64_t groups = p.shared ? p.nqb / (qw / 16) : p.nqb;
+  // workgroups: the shared-tile kernel holds one workgroup per CU (one wave
+  // per SIMD), so 256 is one round over the CUs
   const int64_t target = p.shared ? 256 : 2048;
   int64_t chunks = groups > 0 ? (target + groups - 1) / groups : 1;
   int64_t cap = p.n_tiles / 8;                                   // >= 8 tiles per chunk
@@ -1023,28 +780,31 @@ TopkPlan plan_topk(int64_t nq, int64_t n_db, int k, int d, int m) {
   p.n_chunks = p.n_tiles > 0 ? (int)((p.n_tiles + p.tiles_per_chunk - 1) / p.tiles_per_chunk) : 1;
   size_t off = 0;
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
-  const size_t kc = (size_t)p.kc, nqp = (size_t)p.nqb * 8;
+  const size_t kc = (size_t)p.kc;
   p.off_qop = off; off = al(off + (size_t)p.nqb * (p.nu + p.ns) * 64 * 16);
-  p.off_cinit = off; off = al(off + nqp * 4);
-  const size_t nc = nqp * p.n_chunks * kc;
+  p.off_cinit = off; off = al(off + (size_t)nqp * 2 * 4);
+  const size_t nc = (size_t)nqp * p.n_chunks * kc;
   p.off_cand_s = off; off = al(off + nc * 4);
   p.off_cand_i = off; off = al(off + nc * 4);
   // sample pass (shared-tile kernel, large databases): every 64th tile,
-  // 32 chunks, merged into the top kc of the sample per query
+  // merged into the top kc of the sample per query
   p.sample_stride = (p.shared && p.n_tiles >= 64 * 256) ? 64 : 0;
   if (p.sample_stride) {
     p.sample_tiles = p.n_tiles / p.sample_stride;
-    p.sample_chunks = 32;
-    const size_t ns2 = nqp * p.sample_chunks * kc;
+    int64_t sc = groups > 0 ? (256 + groups - 1) / groups : 1;
+    if (sc > p.sample_tiles / 8) sc = p.sample_tiles / 8;
+    if (sc < 1) sc = 1;
+    p.sample_chunks = (int)sc;
+    const size_t ns2 = (size_t)nqp * p.sample_chunks * kc;
     p.off_s_cand_s = off; off = al(off + ns2 * 4);
     p.off_s_cand_i = off; off = al(off + ns2 * 4);
     p.off_s_idx = off; off = al(off + (size_t)nq * kc * 8);
     p.off_s_score = off; off = al(off + (size_t)nq * kc * 4);
   }
-  p.off_qt64 = off; off = al(off + nqp * 256 * 8);
-  p.off_tt64 = off; off = al(off + nqp * 256 * 8);
-  p.off_qinfo = off; off = al(off + nqp * 2 * 8);
-  p.off_bounds = off; off = al(off + 2 * 4);
+  p.off_qt64 = off; off = al(off + (size_t)nqp * 256 * 8);
+  p.off_tt64 = off; off = al(off + (size_t)nqp * 256 * 8);
+  p.off_qinfo = off; off = al(off + (size_t)nqp * kQInfo * 8);
+  p.off_bounds = off; off = al(off + 4 * 4);
   p.off_acand_s = off; off = al(off + (size_t)nq * kc * 4);
   p.off_acand_i = off; off = al(off + (size_t)nq * kc * 4);
   p.off_flags = off; off = al(off + (size_t)nq * 4);
@@ -1065,56 +825,69 @@ hipError_t launch_topk(const tq_codebook* cb, const float* queries, const TopkPl
   int32_t* cand_i = reinterpret_cast<int32_t*>(w + plan.off_cand_i);
   uint32_t* bounds = reinterpret_cast<uint32_t*>(w + plan.off_bounds);
   const bool qjl = cb->p.qjl_m > 0;
+  const int64_t nqp = plan.nqb * (plan.shared ? 16 : 8);
 
   IPArgs pa{};
   pa.q = queries; pa.nq = plan.nq;
   pa.d = cb->p.d; pa.m = cb->p.qjl_m; pa.dp = cb->dp; pa.mp = cb->mp;
   pa.nu = plan.nu; pa.ns = plan.ns;
+  pa.half = plan.shared ? 1 : 0;
   pa.rotT64 = cb->dev.rotT64; pa.qjlT64 = cb->dev.qjlT64;
   pa.qop = qop; pa.cinit = cinit;
   pa.qt64 = reinterpret_cast<double*>(w + plan.off_qt64);
   pa.tt64 = reinterpret_cast<double*>(w + plan.off_tt64);
   pa.qinfo = reinterpret_cast<double*>(w + plan.off_qinfo);
   pa.bounds = bounds;
-  hipLaunchKernelGGL(k_ip_prologue, dim3((unsigned)(plan.nqb * 8)), dim3(256), 0, stream, pa);
+  hipLaunchKernelGGL(k_ip_prologue, dim3((unsigned)nqp), dim3(256), 0, stream, pa);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (plan.n_db > 0) {
-    int64_t nb = (plan.n_db + 255) / 256;
+  const uint32_t* idxw = static_cast<const uint32_t*>(db.idx);
+  const int rw = (int)(db.idx_row_bytes / 4);
+  {
+    IBArgs ba{};
+    ba.scale = db.scale; ba.rnorm = qjl ? db.rnorm : nullptr;
+    ba.idx = idxw; ba.cent64 = cb->dev.cent64;
+    ba.n = plan.n_db; ba.d = cb->p.d; ba.bits = cb->p.bits; ba.rw = rw;
+    ba.bounds = bounds;
+    int64_t nb = (plan.n_db + kBoundRows - 1) / kBoundRows;
     if (nb > 1024) nb = 1024;
-    hipLaunchKernelGGL(k_ip_bounds, dim3((unsigned)nb), dim3(256), 0, stream, db.scale, qjl ? db.rnorm : nullptr,
-                       plan.n_db, bounds);
+    if (nb < 1) nb = 1;
+    hipLaunchKernelGGL(k_ip_bounds, dim3((unsigned)nb), dim3(256), 0, stream, ba);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
 
   float* acand_s = reinterpret_cast<float*>(w + plan.off_acand_s);
   int32_t* acand_i = reinterpret_cast<int32_t*>(w + plan.off_acand_i);
-  ISArgs sa{};
-  sa.qop = qop; sa.cinit = cinit;
-  sa.idx = static_cast<const uint32_t*>(db.idx);
-  sa.sign = static_cast<const uint32_t*>(db.sign);
-  sa.scale = db.scale; sa.rnorm = db.rnorm;
-  sa.tab = cb->dev.pair_tab;
-  sa.n_db = plan.n_db; sa.n_tiles = plan.n_tiles; sa.tiles_per_chunk = plan.tiles_per_chunk;
-  sa.rw = (int)(db.idx_row_bytes / 4);
-  sa.sw = qjl ? (int)(db.sign_row_bytes / 4) : 0;
-  sa.nu = plan.nu; sa.ns = plan.ns; sa.k = plan.kc; sa.n_chunks = plan.n_chunks;
-  sa.cand_s = cand_s; sa.cand_i = cand_i;
+  const int sw = qjl ? (int)(db.sign_row_bytes / 4) : 0;
   {
     ProfileScope prof(TQ_KERNEL_TOPK, stream);
     if (plan.shared) {
       IS2Args s2{};
-      s2.qop = qop; s2.cinit = cinit;
-      s2.idx = sa.idx; s2.sign = sa.sign; s2.scale = sa.scale; s2.rnorm = qjl ? sa.rnorm : sa.scale;
-      s2.tab = sa.tab;
+      s2.qop = qop; s2.qsc = cinit;
+      s2.idx = idxw; s2.sign = static_cast<const uint32_t*>(db.sign);
+      s2.scale = db.scale; s2.rnorm = qjl ? db.rnorm : db.scale;
+      s2.tab = cb->dev.pair_tab16;
       s2.n_db = plan.n_db; s2.n_tiles = plan.n_tiles; s2.tiles_per_chunk = plan.tiles_per_chunk;
-      s2.rw = sa.rw; s2.sw = sa.sw; s2.bits = cb->p.bits; s2.nu = plan.nu; s2.ns = plan.ns;
+      s2.rw = rw; s2.sw = sw; s2.bits = cb->p.bits; s2.nu = plan.nu; s2.ns = plan.ns;
       s2.k = plan.kc; s2.n_chunks = plan.n_chunks;
       s2.cand_s = cand_s; s2.cand_i = cand_i;
       s2.tstride = 1;
       s2.nq = plan.nq;
       s2.floor_s = nullptr;
-      const unsigned groups = (unsigned)(plan.nqb / (kIp2Queries / 8));
+      const bool wide = plan.kc <= 16;
+      const unsigned groups = (unsigned)(plan.nqb / (wide ? 16 : 8));
+      auto score = [&](const IS2Args& x, dim3 grid) {
+        switch (x.nu) {
+          case 2: launch_score16_2(x, !wide, grid, stream); break;
+          case 4: launch_score16_4(x, !wide, grid, stream); break;
+          case 6: launch_score16_6(x, !wide, grid, stream); break;
+          case 8: launch_score16_8(x, !wide, grid, stream); break;
+          case 10: launch_score16_10(x, !wide, grid, stream); break;
+          case 12: launch_score16_12(x, !wide, grid, stream); break;
+          case 14: launch_score16_14(x, !wide, grid, stream); break;
+          default: launch_score16_16(x, !wide, grid, stream); break;
+        }
+      };
       if (plan.sample_stride) {
         IS2Args sp = s2;
         sp.tstride = plan.sample_stride;
@@ -1123,7 +896,7 @@ hipError_t launch_topk(const tq_codebook* cb, const float* queries, const TopkPl
         sp.tiles_per_chunk = (plan.sample_tiles + plan.sample_chunks - 1) / plan.sample_chunks;
         sp.cand_s = reinterpret_cast<float*>(w + plan.off_s_cand_s);
         sp.cand_i = reinterpret_cast<int32_t*>(w + plan.off_s_cand_i);
-        launch_score2<2>(sp, dim3((unsigned)plan.sample_chunks, groups), stream);
+        score(sp, dim3((unsigned)plan.sample_chunks, groups));
         if ((e = hipGetLastError()) != hipSuccess) return e;
         IMArgs sm{};
         sm.cand_s = sp.cand_s; sm.cand_i = sp.cand_i;
@@ -1134,8 +907,18 @@ hipError_t launch_topk(const tq_codebook* cb, const float* queries, const TopkPl
         if ((e = hipGetLastError()) != hipSuccess) return e;
         s2.floor_s = sm.out_score;
       }
-      launch_score2<2>(s2, dim3((unsigned)plan.n_chunks, groups), stream);
+      score(s2, dim3((unsigned)plan.n_chunks, groups));
     } else {
+      ISArgs sa{};
+      sa.qop = qop; sa.cinit = cinit;
+      sa.idx = idxw;
+      sa.sign = static_cast<const uint32_t*>(db.sign);
+      sa.scale = db.scale; sa.rnorm = db.rnorm;
+      sa.tab = cb->dev.pair_tab;
+      sa.n_db = plan.n_db; sa.n_tiles = plan.n_tiles; sa.tiles_per_chunk = plan.tiles_per_chunk;
+      sa.rw = rw; sa.sw = sw;
+      sa.nu = plan.nu; sa.ns = plan.ns; sa.k = plan.kc; sa.n_chunks = plan.n_chunks;
+      sa.cand_s = cand_s; sa.cand_i = cand_i;
       const dim3 grid((unsigned)plan.n_chunks, (unsigned)plan.nqb);
       switch (cb->p.bits) {
         case 1: launch_score_b<1>(sa, qjl, grid, stream); break;
@@ -1162,9 +945,10 @@ hipError_t launch_topk(const tq_codebook* cb, const float* queries, const TopkPl
   ra.acand_s = acand_s; ra.acand_i = acand_i;
   ra.qt64 = pa.qt64; ra.tt64 = pa.tt64; ra.qinfo = pa.qinfo; ra.bounds = bounds;
   ra.cent64 = cb->dev.cent64;
-  ra.idx = sa.idx; ra.sign = sa.sign; ra.scale = db.scale; ra.rnorm = db.rnorm;
+  ra.idx = idxw; ra.sign = static_cast<const uint32_t*>(db.sign); ra.scale = db.scale; ra.rnorm = db.rnorm;
   ra.nq = plan.nq; ra.n_db = plan.n_db;
-  ra.d = cb->p.d; ra.m = cb->p.qjl_m; ra.bits = cb->p.bits; ra.rw = sa.rw; ra.sw = sa.sw;
+  ra.d = cb->p.d; ra.m = cb->p.qjl_m; ra.bits = cb->p.bits; ra.rw = rw; ra.sw = sw;
+  ra.dp = cb->dp; ra.mp = cb->mp; ra.half = plan.shared ? 1 : 0; ra.emax_c = cb->emax_c16;
   ra.nu = plan.nu; ra.ns = plan.ns; ra.k = plan.k; ra.kc = plan.kc;
   ra.force_scan = force_scan ? 1 : 0;
   ra.out_idx = out_idx; ra.out_score = out_score;

@@ -29,6 +29,24 @@ float bf16_to_f(uint16_t h) {
   std::memcpy(&f, &u, 4);
   return f;
 }
+// x rounded to the nearest fp16 (ties to even), 0 below the fp16 normal
+// range; |x| < 65504 assumed
+uint16_t f16_normal_rne(double x) {
+  const double ax = std::fabs(x);
+  if (!(ax >= 0x1p-14)) return 0;
+  int e = 0;
+  (void)std::frexp(ax, &e);               // ax in [2^(e-1), 2^e)
+  int E = e - 1;
+  double qm = std::nearbyint(std::ldexp(ax, 10 - E));   // in [1024, 2048]
+  if (qm >= 2048.0) { qm = 1024.0; ++E; }
+  return (uint16_t)((x < 0 ? 0x8000u : 0u) | (uint32_t)(E + 15) << 10 | ((uint32_t)qm - 1024u));
+}
+double f16_to_double(uint16_t b) {
+  const int E = (b >> 10) & 31;
+  if (E == 0) return 0.0;                 // only zeros are produced
+  const double v = std::ldexp(1.0 + (b & 1023) / 1024.0, E - 15);
+  return (b & 0x8000u) ? -v : v;
+}
 // c ~ hi + lo, both bf16
 void split_bf16(double c, uint16_t& hi, uint16_t& lo) {
   hi = bf16_rne((float)c);
@@ -133,6 +151,7 @@ void free_dev(DeviceCodebook& d) {
   if (d.rotT64) (void)hipFree(d.rotT64);
   if (d.qjlT64) (void)hipFree(d.qjlT64);
   if (d.cent64) (void)hipFree(d.cent64);
+  if (d.pair_tab16) (void)hipFree(d.pair_tab16);
   if (d.rop) (void)hipFree(d.rop);
   if (d.qtab) (void)hipFree(d.qtab);
   if (d.sop) (void)hipFree(d.sop);
@@ -324,6 +343,35 @@ tq_status tq_codebook_build(const tq_params* params, tq_codebook** out) {
       }
     }
     cb->dev.pair_tab_dwords = (int)tab.size();
+    {
+      // fp16 hi/lo parts of 2^6 c for the top-k score kernel
+      std::vector<uint16_t> h16(L), l16(L);
+      double emax = 0.0;
+      for (int x = 0; x < L; ++x) {
+        const double v = std::ldexp(cb->host.centroids[x], 6);
+        h16[x] = f16_normal_rne(v);
+        l16[x] = f16_normal_rne(v - f16_to_double(h16[x]));
+        const double back = std::ldexp(f16_to_double(h16[x]) + f16_to_double(l16[x]), -6);
+        emax = std::max(emax, std::fabs(cb->host.centroids[x] - back));
+      }
+      cb->emax_c16 = emax;
+      std::vector<uint32_t> t16(tab.size());
+      if (cb->p.bits <= 4) {
+        const int b = cb->p.bits;
+        for (int x = 0; x < L; ++x)
+          for (int y = 0; y < L; ++y) {
+            const size_t e2 = (size_t)(x | (y << b));
+            t16[2 * e2 + 0] = (uint32_t)h16[x] | ((uint32_t)h16[y] << 16);
+            t16[2 * e2 + 1] = (uint32_t)l16[x] | ((uint32_t)l16[y] << 16);
+          }
+      } else {
+        for (int x = 0; x < L; ++x) t16[x] = (uint32_t)h16[x] | ((uint32_t)l16[x] << 16);
+      }
+      if ((e = upload(&cb->dev.pair_tab16, t16)) != hipSuccess) {
+        release_pending();
+        return hip_fail(e, "codebook upload");
+      }
+    }
     {
       // float64 tables of the exact top-k refinement
       std::vector<double> rt((size_t)d * d), st(m > 0 ? (size_t)d * m : 0);

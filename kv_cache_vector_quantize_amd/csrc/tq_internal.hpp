@@ -68,6 +68,9 @@ struct DeviceCodebook {
   double* rotT64 = nullptr;
   double* qjlT64 = nullptr;
   double* cent64 = nullptr;
+  // top-k fp16 operand table: the layout of pair_tab with fp16 hi/lo parts
+  // of 2^6 c (lo parts below the fp16 normal range are 0)
+  uint32_t* pair_tab16 = nullptr;
   // d = 128 quantize (see quantize128.hip), absent for other d:
   //  rop: Pi as bf16 operands of v_mfma_f32_32x32x16_bf16 in three parts
   //  (hi, lo, lo2), uint4 [wave 4][k-step 8][part 3][lane 64]; lane l of wave
@@ -109,6 +112,7 @@ inline int pad32(int x) { return (x + 31) / 32 * 32; }
 struct tq_codebook {
   tq_params p;
   int L = 0, dp = 0, mp = 0;
+  double emax_c16 = 0.0;   // max_l |c_l - 2^-6 (hi + lo)_l| of pair_tab16
   int device = 0;
   tq::HostCodebook host;
   tq::DeviceCodebook dev;
