@@ -504,11 +504,17 @@ def vector_search_leg(torch, tq, synth, dev, iters, warm):
     ms, per = timed_iters(torch, call, iters)
     tq.tq_profile_enable(False)
     score_ms, score_spread = kernel_spread(tq, tq.TQ_KERNEL_TOPK)
+    n_scan = tq.tq_ip_topk_scan_count(cb, ws, nq, n_db, k)
     # the last call's results are those of the first copy's codes (identical)
-    # MFMA work the score kernel issues: per 8-query block and 16-row tile,
-    # dp/16 centroid MFMAs and ceil(m/32) sign MFMAs of 16x16x32 (16384 flop)
+    # MFMA work the score kernel issues (fp16 16x16x32, 16384 flop each): per
+    # 16-query block (queries padded to whole workgroups of 256) and 16-row
+    # tile, dp/16 centroid MFMAs (hi and lo parts) and ceil(m/32) sign MFMAs,
+    # over every tile and, in the sample pass, every 64th tile
     dp = (d + 31) // 32 * 32
-    n_mfma = ((nq + 7) // 8) * ((n_db + 15) // 16) * (dp // 16 + (m + 31) // 32)
+    nqp = (nq + 255) // 256 * 256
+    n_tiles = (n_db + 15) // 16
+    tiles = n_tiles + (n_tiles // 64 if n_tiles >= 64 * 256 else 0)
+    n_mfma = (nqp // 16) * tiles * (dp // 16 + (m + 31) // 32)
     mfma_tflops = n_mfma * 16384 / (score_ms * 1e-3) / 1e12
     useful = nq * n_db * (2 * d + 2 * m)
     # exact top-10 of the raw vectors (fp32 matmul, chunked) for recall
@@ -531,8 +537,9 @@ def vector_search_leg(torch, tq, synth, dev, iters, warm):
                 call_ms_spread=spread(per), score_kernel_ms=round(score_ms, 4),
                 score_kernel_ms_spread=score_spread,
                 mfma_TFLOPs=round(mfma_tflops, 1),
-                mfma_frac_bf16_peak=round(mfma_tflops / 2500.0, 4),
+                mfma_frac_fp16_peak=round(mfma_tflops / 2500.0, 4),
                 useful_TFLOPs=round(useful / (ms * 1e-3) / 1e12, 1),
+                exact_scan_queries=n_scan,
                 recall_10_at_10=round(hit / (nq * k), 4),
                 recall_1_at_10=round(hit1 / nq, 4),
                 quantize_db_ms=round(quant_ms, 3))

@@ -332,6 +332,13 @@ tq_status tq_ip_topk(const tq_codebook* cb, const float* queries, int64_t nq,
                      const tq_codes* db, int64_t n_db, int32_t k, int64_t* out_idx,
                      float* out_score, void* workspace, size_t ws_bytes, void* stream);
 
+/* Diagnostic: the number of queries of the last tq_ip_topk call made with
+ * this workspace (and the same cb, nq, n_db, k) that the exact scan
+ * answered.  Reads 4 bytes of the workspace on `stream` and waits for it.
+ * Errors: TQ_ERR_INVALID, TQ_ERR_HIP. */
+tq_status tq_ip_topk_scan_count(const tq_codebook* cb, const void* workspace, int64_t nq, int64_t n_db,
+                                int32_t k, void* stream, int64_t* count);
+
 /* Diagnostic switch of tq_ip_topk (process-wide, default 0): 1 sends every
  * query to the exact float64 scan, skipping the candidates' test, so the
  * scan can be checked and timed on any input; 0 restores the default.

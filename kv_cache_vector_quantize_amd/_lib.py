@@ -28,7 +28,8 @@ EXPORTS = (
     "tq_ip_topk_workspace", "tq_ip_topk", "tq_dequantize", "tq_quantize_kv_paged",
     "tq_attn_decode_paged_workspace", "tq_attn_decode_paged", "tq_profile_enable", "tq_profile_read",
     "tq_codebook_solver_limits", "tq_profile_durations", "tq_stream_read", "tq_attn_decode_noalloc",
-    "tq_polar_codebook_build", "tq_polar_codebook_values", "tq_ip_topk_exact_scan", "tq_last_error",
+    "tq_polar_codebook_build", "tq_polar_codebook_values", "tq_ip_topk_exact_scan", "tq_ip_topk_scan_count",
+    "tq_last_error",
 )
 TQ_KERNEL_QUANTIZE, TQ_KERNEL_DECODE_SPLIT, TQ_KERNEL_TOPK, TQ_KERNEL_DEQUANTIZE = 0, 1, 2, 3
 
@@ -73,6 +74,7 @@ def lib() -> ctypes.CDLL:
     L.tq_codebook_values.argtypes = [ctypes.POINTER(tq_params), dp, dp, dp, dp]
     L.tq_codebook_solver_limits.argtypes = [i32, i32]
     L.tq_ip_topk_exact_scan.argtypes = [i32]
+    L.tq_ip_topk_scan_count.argtypes = [vp, vp, i64, i64, i32, vp, ctypes.POINTER(i64)]
     L.tq_polar_codebook_build.argtypes = [ctypes.POINTER(tq_polar_params), ctypes.POINTER(vp)]
     L.tq_polar_codebook_values.argtypes = [ctypes.POINTER(tq_polar_params), dp, dp, dp, dp]
     L.tq_code_row_bytes.argtypes = [vp, ctypes.POINTER(i64), ctypes.POINTER(i64)]
@@ -150,6 +152,15 @@ def tq_codebook_values(d, bits, qjl_m=0, norm_correction=False, rot_seed=1, qjl_
 def tq_codebook_solver_limits(lloyd_iters=0, newton_iters=0):
     """Iteration limits of the codebook solve on this thread (0: defaults)."""
     _check(lib().tq_codebook_solver_limits(int(lloyd_iters), int(newton_iters)))
+
+
+def tq_ip_topk_scan_count(cb, workspace, nq, n_db, k, stream=None) -> int:
+    """Queries of the last tq_ip_topk call with this workspace that the exact
+    scan answered (waits for the call)."""
+    out = ctypes.c_int64(0)
+    _check(lib().tq_ip_topk_scan_count(cb.handle, ctypes.c_void_p(workspace.data_ptr()), int(nq), int(n_db),
+                                       int(k), _stream_handle(stream), ctypes.byref(out)))
+    return int(out.value)
 
 
 def tq_ip_topk_exact_scan(always: bool):

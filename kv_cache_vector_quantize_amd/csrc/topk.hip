@@ -54,7 +54,7 @@ struct IPArgs {
   double* qt64;         // [nq][256] q~ = Pi q (float64)
   double* tt64;         // [nq][256] t = sqrt(pi/2)/m S q~ (float64)
   double* qinfo;        // [nq][kQInfo] norms for the error bound
-  uint32_t* bounds;     // [3] database max |scale|, max |rnorm|, max |c[idx]| (zeroed here)
+  uint32_t* bounds;     // [4] bounds[3]: count of queries for the exact scan (zeroed here)
 };
 
 // qinfo fields: |q~|_2, |t|_1, and in fp16 mode |q~ - q^|_2, |q^|_2,
@@ -90,28 +90,52 @@ __device__ inline uint16_t f16_operand(double x) {
 // sketch rows 32 v + 8 g4 + el; q~ is scaled by 2^sq and t by 2^st, powers
 // of two that bring the largest component to [2^14, 2^15).
 // q~ and t are formed in float64 (kept for the exact refinement).
+constexpr int kProQ = 4;              // queries per prologue workgroup
+
 __global__ void __launch_bounds__(256) k_ip_prologue(IPArgs a) {
-  __shared__ double qs[256], qt[256], tt[256];
+  __shared__ double qs[kProQ][256], qtq[kProQ][256], ttq[kProQ][256];
   __shared__ double red[6][4];
   __shared__ int sexp[2];
-  const int64_t qi = blockIdx.x;        // over the padded query count
   const int tid = threadIdx.x;
-  const bool valid = qi < a.nq;
-  if (qi == 0 && tid < 3) a.bounds[tid] = 0u;
-  qs[tid] = (valid && tid < a.d) ? (double)a.q[qi * a.d + tid] : 0.0;
+  const int64_t q0 = (int64_t)blockIdx.x * kProQ;   // over the padded query count
+  if (blockIdx.x == 0 && tid < 4) a.bounds[tid] = 0u;
+#pragma unroll
+  for (int j = 0; j < kProQ; ++j)
+    qs[j][tid] = (q0 + j < a.nq && tid < a.d) ? (double)a.q[(q0 + j) * a.d + tid] : 0.0;
   __syncthreads();
-  double z = 0.0;
+  // q~ = Pi q and t = sqrt(pi/2)/m S q~ of the workgroup's queries, one pass
+  // over each table
+  double zz[kProQ], tv[kProQ];
+#pragma unroll
+  for (int j = 0; j < kProQ; ++j) { zz[j] = 0.0; tv[j] = 0.0; }
   if (tid < a.d) {
-    for (int k = 0; k < a.d; ++k) z = fma(a.rotT64[(int64_t)k * a.d + tid], qs[k], z);
+    for (int k = 0; k < a.d; ++k) {
+      const double r = a.rotT64[(int64_t)k * a.d + tid];
+#pragma unroll
+      for (int j = 0; j < kProQ; ++j) zz[j] = fma(r, qs[j][k], zz[j]);
+    }
   }
-  qt[tid] = z;
+#pragma unroll
+  for (int j = 0; j < kProQ; ++j) qtq[j][tid] = zz[j];
   __syncthreads();
-  double t = 0.0;
   if (tid < a.m) {
-    for (int i = 0; i < a.d; ++i) t = fma(a.qjlT64[(int64_t)i * a.m + tid], qt[i], t);
-    t *= 1.2533141373155002512 / (double)a.m;      // sqrt(pi/2) / m
+    for (int i = 0; i < a.d; ++i) {
+      const double sv = a.qjlT64[(int64_t)i * a.m + tid];
+#pragma unroll
+      for (int j = 0; j < kProQ; ++j) tv[j] = fma(sv, qtq[j][i], tv[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < kProQ; ++j) tv[j] *= 1.2533141373155002512 / (double)a.m;   // sqrt(pi/2) / m
   }
-  tt[tid] = t;
+#pragma unroll
+  for (int j = 0; j < kProQ; ++j) ttq[j][tid] = tv[j];
+  __syncthreads();
+  for (int j = 0; j < kProQ; ++j) {
+  const int64_t qi = q0 + j;
+  const bool valid = qi < a.nq;
+  const double z = zz[j], t = tv[j];
+  const double* qt = qtq[j];
+  const double* tt = ttq[j];
   if (valid) {
     a.qt64[qi * 256 + tid] = z;
     a.tt64[qi * 256 + tid] = t;
@@ -172,7 +196,8 @@ __global__ void __launch_bounds__(256) k_ip_prologue(IPArgs a) {
       rec[(u * 64 + c + 16 * g4) * 4 + dw] = hv[0] | (hv[1] << 16);
     }
     if (tid < 2) a.cinit[qi * 2 + tid] = ldexpf(1.f, tid == 0 ? -(kTabScaleLog2 + sq) : -st);
-    return;
+    __syncthreads();                  // red and sexp are reused by the next query
+    continue;
   }
   const int64_t qb = qi >> 3;
   const int c = (int)(qi & 7);
@@ -202,21 +227,24 @@ __global__ void __launch_bounds__(256) k_ip_prologue(IPArgs a) {
   // QJL accumulator offset: -sum_j (hi + lo)(t_j), in the scale of the products
   if (tid < 64) {
     float s = 0.f;
-    for (int j = tid; j < 256; j += 64) {
-      const float v = (float)tt[j];
+    for (int jj = tid; jj < 256; jj += 64) {
+      const float v = (float)tt[jj];
       const float fh = __uint_as_float(bf16_rne_bits(v) << 16);
       s += fh + __uint_as_float(bf16_rne_bits(v - fh) << 16);
     }
     for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
     if (tid == 0) a.cinit[qi] = -ldexpf(s, -kSignShiftIp);
   }
+  __syncthreads();                    // red and sexp are reused by the next query
+  }
 }
 
 // Database bounds of the refinement's error bound: max |scale|, max |rnorm|
 // and max_j |c[idx_j]|_2 (float bits; non-negative floats order as their
 // bits).  Each workgroup stages 256 rows of codes in LDS with coalesced
-// loads, then one thread per row sums c^2 over its codes in float (the
-// result is enlarged by 2^-12 relative where it is used).
+// loads; one thread per row then sums c^2 over its codes in float, 32 codes
+// (B words) at a time (the result is enlarged by 2^-12 relative where it is
+// used).
 struct IBArgs {
   const float* scale;
   const float* rnorm;       // or null
@@ -224,51 +252,148 @@ struct IBArgs {
   const double* cent64;
   int64_t n;
   int d, bits, rw;
-  uint32_t* bounds;
+  float* bpart;             // [gridDim.x][3] per-workgroup maxima
 };
 
 constexpr int kBoundRows = 256;
+constexpr int kBoundBlocks = 1024;    // most workgroups of k_ip_bounds
 
+template <int B>
 __global__ void __launch_bounds__(256) k_ip_bounds(IBArgs a) {
-  __shared__ float c2[256];
-  __shared__ uint32_t rows[kBoundRows * (kIpMaxRowBytes / 4) + 1];
+  __shared__ float c2[1 << B];
+  __shared__ __align__(16) uint32_t rows[kBoundRows * (kIpMaxRowBytes / 4) + 8];
   const int tid = threadIdx.x;
-  if (tid < (1 << a.bits)) {
+  if (tid < (1 << B)) {
     const double c = a.cent64[tid];
     c2[tid] = (float)(c * c);
   }
-  const uint32_t mask = (1u << a.bits) - 1u;
+  constexpr uint32_t mask = (1u << B) - 1u;
+  const int groups = (a.d + 31) / 32;
   float ms = 0.f, mr = 0.f, mc = 0.f;
   for (int64_t base = (int64_t)blockIdx.x * kBoundRows; base < a.n; base += (int64_t)gridDim.x * kBoundRows) {
     const int nr = (int)(a.n - base < kBoundRows ? a.n - base : kBoundRows);
     const int nw = nr * a.rw;
     const uint32_t* src = a.idx + base * a.rw;
-    __syncthreads();                     // the previous rows are consumed
-    for (int e = tid; e < nw; e += 256) rows[e] = src[e];
+    __syncthreads();                     // the previous rows are consumed (and c2 is ready)
+    if ((reinterpret_cast<uintptr_t>(src) & 15u) == 0) {
+      // 16-byte loads, all of a thread's share in flight before the stores
+      constexpr int kPer = kBoundRows * (kIpMaxRowBytes / 4) / 4 / 256;
+      const int nw4 = nw >> 2;
+      const uint4* s4 = reinterpret_cast<const uint4*>(src);
+      uint4* r4 = reinterpret_cast<uint4*>(rows);
+      uint4 t4[kPer];
+#pragma unroll
+      for (int j = 0; j < kPer; ++j)
+        if (tid + 256 * j < nw4) t4[j] = s4[tid + 256 * j];
+#pragma unroll
+      for (int j = 0; j < kPer; ++j)
+        if (tid + 256 * j < nw4) r4[tid + 256 * j] = t4[j];
+      if (tid < (nw & 3)) rows[4 * nw4 + tid] = src[4 * nw4 + tid];
+    } else {
+#pragma unroll 8
+      for (int e = tid; e < nw; e += 256) rows[e] = src[e];
+    }
     __syncthreads();
     if (tid < nr) {
       ms = fmaxf(ms, fabsf(a.scale[base + tid]));
       if (a.rnorm) mr = fmaxf(mr, fabsf(a.rnorm[base + tid]));
       const uint32_t* ir = rows + tid * a.rw;
-      float s2 = 0.f;
-      for (int c = 0; c < a.d; ++c) {
-        const int bit = c * a.bits, w = bit >> 5, sh = bit & 31;
-        const uint32_t v = __builtin_amdgcn_alignbit(ir[w + 1], ir[w], sh);   // ir[w + 1] stays in the array
-        s2 += c2[v & mask];
+      float s0 = 0.f, s1 = 0.f;
+      for (int gi = 0; gi < groups; ++gi) {
+        // codes 32 gi .. 32 gi + 31 occupy words B gi .. B gi + B - 1 (past
+        // the row's words only for codes past d, which count 0)
+        uint32_t w[B];
+#pragma unroll
+        for (int j = 0; j < B; ++j) w[j] = ir[B * gi + j];
+#pragma unroll
+        for (int c = 0; c < 32; ++c) {
+          const int bit = c * B, wj = bit >> 5, sh = bit & 31;
+          uint32_t v = w[wj] >> sh;
+          if (sh + B > 32) v |= w[wj + 1] << (32 - sh);
+          const float t = (32 * gi + c < a.d) ? c2[v & mask] : 0.f;
+          if (c & 1) s1 += t; else s0 += t;
+        }
       }
-      mc = fmaxf(mc, s2);
+      mc = fmaxf(mc, s0 + s1);
     }
   }
+  // one partial (max |scale|, max |rnorm|, max |c[idx]|) per workgroup: many
+  // atomics on one address serialise, the refinement reduces the partials
+  __shared__ float part[3][4];
   for (int o = 32; o >= 1; o >>= 1) {
     ms = fmaxf(ms, __shfl_xor(ms, o));
     mr = fmaxf(mr, __shfl_xor(mr, o));
     mc = fmaxf(mc, __shfl_xor(mc, o));
   }
-  if ((tid & 63) == 0) {
-    atomicMax(a.bounds, __float_as_uint(ms));
-    atomicMax(a.bounds + 1, __float_as_uint(mr));
-    atomicMax(a.bounds + 2, __float_as_uint(sqrtf(mc)));
+  if ((tid & 63) == 0) { part[0][tid >> 6] = ms; part[1][tid >> 6] = mr; part[2][tid >> 6] = mc; }
+  __syncthreads();
+  if (tid < 3) {
+    const float v = fmaxf(fmaxf(part[tid][0], part[tid][1]), fmaxf(part[tid][2], part[tid][3]));
+    a.bpart[blockIdx.x * 3 + tid] = (tid == 2) ? sqrtf(v) : v;
   }
+}
+
+// Order-preserving keys of floats (larger float, larger key) and back.
+__device__ inline uint32_t fkey(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ inline float fkey_inv(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// The k-th largest sample score of each query (the floor of its full pass):
+// each thread keeps the KS best of its share in registers (an unrolled
+// compare-exchange chain), then a radix select over the 256 KS survivors in
+// LDS, 8 bits at a time from the top.  k <= KS.
+template <int KS>
+__global__ void __launch_bounds__(256) k_ip_floor(const float* sample, int64_t ld, int64_t n, int k, float* floor_v) {
+  __shared__ uint32_t keys[256 * KS];
+  __shared__ uint32_t hist[256];
+  __shared__ int sel[2];
+  const int tid = threadIdx.x;
+  const float* src = sample + (int64_t)blockIdx.x * ld;
+  float r[KS];
+#pragma unroll
+  for (int j = 0; j < KS; ++j) r[j] = -INFINITY;
+#pragma unroll 4
+  for (int64_t e = tid; e < n; e += 256) {
+    float v = src[e];
+#pragma unroll
+    for (int j = 0; j < KS; ++j) {
+      const float hi = fmaxf(v, r[j]);
+      v = fminf(v, r[j]);
+      r[j] = hi;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < KS; ++j) keys[tid * KS + j] = fkey(r[j]);
+  uint32_t prefix = 0u, pmask = 0u;
+  int kr = k;
+  for (int dgt = 3; dgt >= 0; --dgt) {
+    hist[tid] = 0u;
+    __syncthreads();
+    for (int e = tid; e < 256 * KS; e += 256) {
+      const uint32_t u = keys[e];
+      if ((u & pmask) == prefix) atomicAdd(&hist[(u >> (8 * dgt)) & 255u], 1u);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int acc = 0, bsel = 0;
+      for (int bb = 255; bb >= 0; --bb) {
+        if (acc + (int)hist[bb] >= kr) { bsel = bb; break; }
+        acc += (int)hist[bb];
+      }
+      sel[0] = bsel;
+      sel[1] = kr - acc;
+    }
+    __syncthreads();
+    prefix |= (uint32_t)sel[0] << (8 * dgt);
+    pmask |= 255u << (8 * dgt);
+    kr = sel[1];
+    __syncthreads();
+  }
+  if (tid == 0) floor_v[blockIdx.x] = fkey_inv(prefix);
 }
 
 // ------------------------------------------------------------ scores + lists
@@ -460,13 +585,37 @@ struct IMArgs {
 
 // One wave per query: k rounds, each picking the best candidate that comes
 // after the previous pick in (score desc, index asc) order; indices are
-// distinct, so the order is strict.
+// distinct, so the order is strict.  Up to kMergeLds candidates are staged
+// in LDS first.
+constexpr int kMergeLds = 4096;
+
 __global__ void __launch_bounds__(64) k_ip_merge(IMArgs a) {
+  __shared__ float ms_[kMergeLds];
+  __shared__ int32_t mi_[kMergeLds];
   const int64_t q = blockIdx.x;
   const int lane = threadIdx.x;
   const int n = a.n_chunks * a.k;
   const float* cs = a.cand_s + q * n;
   const int32_t* ci = a.cand_i + q * n;
+  const bool staged = n <= kMergeLds;
+  if (staged) {
+    // eight loads of each array in flight per round
+    for (int e0 = 0; e0 < n; e0 += 8 * 64) {
+      float ts[8];
+      int32_t ti[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int e = e0 + 64 * j + lane;
+        if (e < n) { ts[j] = cs[e]; ti[j] = ci[e]; }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int e = e0 + 64 * j + lane;
+        if (e < n) { ms_[e] = ts[j]; mi_[e] = ti[j]; }
+      }
+    }
+    __syncthreads();
+  }
   float ps = INFINITY;
   int32_t pi = -1;
   for (int o = 0; o < a.k; ++o) {
@@ -474,8 +623,8 @@ __global__ void __launch_bounds__(64) k_ip_merge(IMArgs a) {
     int32_t bi = kNoIndex;
     bool have = false;
     for (int e = lane; e < n; e += 64) {
-      const float s = cs[e];
-      const int32_t i = ci[e];
+      const float s = staged ? ms_[e] : cs[e];
+      const int32_t i = staged ? mi_[e] : ci[e];
       if (!better(ps, pi, s, i)) continue;          // not after the previous pick
       if (!have || better(s, i, bs, bi)) { bs = s; bi = i; have = true; }
     }
@@ -543,6 +692,10 @@ struct IRArgs {
   int64_t* out_idx;
   float* out_score;
   int32_t* flags;           // [nq]: 1 settled by the candidates, 0 needs the scan
+  int32_t* fblist;          // [nq] queries that need the scan, bounds[3] of them
+  uint32_t* nfb;
+  const float* bpart;       // [nbpart][3] per-workgroup database maxima
+  int nbpart;
   double* fb_s;             // [nq][kIpFbChunks][k] scan lists
   int32_t* fb_i;
 };
@@ -603,6 +756,19 @@ __global__ void __launch_bounds__(64) k_ip_refine(IRArgs a) {
   es[lane] = e;
   ei[lane] = id;
   if (lane == 0) ek = -INFINITY;
+  // database maxima from the bounds kernel's per-workgroup partials
+  float pm0 = 0.f, pm1 = 0.f, pm2 = 0.f;
+  for (int b = lane; b < a.nbpart; b += 64) {
+    pm0 = fmaxf(pm0, a.bpart[b * 3]);
+    pm1 = fmaxf(pm1, a.bpart[b * 3 + 1]);
+    pm2 = fmaxf(pm2, a.bpart[b * 3 + 2]);
+  }
+  for (int o = 32; o >= 1; o >>= 1) {
+    pm0 = fmaxf(pm0, __shfl_xor(pm0, o));
+    pm1 = fmaxf(pm1, __shfl_xor(pm1, o));
+    pm2 = fmaxf(pm2, __shfl_xor(pm2, o));
+  }
+  const float dbmax[3] = {pm0, pm1, pm2};
   __syncthreads();
   if (lane < a.kc) {
     // rank by (score desc, index asc); empty slots last, in slot order
@@ -621,9 +787,9 @@ __global__ void __launch_bounds__(64) k_ip_refine(IRArgs a) {
     if (!ok && !a.force_scan) {
       const double u = 0x1p-24;
       auto gam = [u](double n) { return n * u / (1.0 - n * u); };
-      const double smax = (double)__uint_as_float(a.bounds[0]);
-      const double rmax = (double)__uint_as_float(a.bounds[1]);
-      const double cn = (double)__uint_as_float(a.bounds[2]) * (1.0 + 0x1p-12);   // >= max_j |c[idx_j]|_2
+      const double smax = (double)dbmax[0];
+      const double rmax = (double)dbmax[1];
+      const double cn = (double)dbmax[2] * (1.0 + 0x1p-12);   // >= max_j |c[idx_j]|_2
       const double* qi = a.qinfo + q * kQInfo;
       double delta;
       if (a.half) {
@@ -648,13 +814,14 @@ __global__ void __launch_bounds__(64) k_ip_refine(IRArgs a) {
       ok = (double)akc + delta < ek;
     }
     a.flags[q] = ok ? 1 : 0;
+    if (!ok) a.fblist[atomicAdd(a.nfb, 1u)] = (int32_t)q;
   }
 }
 
 // Exact scan for the queries the candidates did not settle: grid
-// (query slots, kIpFbChunks); each workgroup keeps the k best rows of its
-// share of the database by float64 score, for queries blockIdx.x,
-// blockIdx.x + gridDim.x, ...
+// (slots, kIpFbChunks); each workgroup keeps the k best rows of its share of
+// the database by float64 score, for entries blockIdx.x, blockIdx.x +
+// gridDim.x, ... of the list of unsettled queries
 __global__ void __launch_bounds__(256) k_ip_fallback(IRArgs a) {
   __shared__ double sq[256], st[256], cent[256];
   __shared__ double ls[kIpTopkMax];
@@ -666,8 +833,9 @@ __global__ void __launch_bounds__(256) k_ip_fallback(IRArgs a) {
   const int64_t per = (a.n_db + kIpFbChunks - 1) / kIpFbChunks;
   const int64_t r0 = (int64_t)blockIdx.y * per;
   const int64_t r1 = (r0 + per < a.n_db) ? r0 + per : a.n_db;
-  for (int64_t q = blockIdx.x; q < a.nq; q += gridDim.x) {
-    if (a.flags[q] != 0) continue;                      // uniform over the workgroup
+  const int64_t nfb = (int64_t)*a.nfb;
+  for (int64_t f = blockIdx.x; f < nfb; f += gridDim.x) {
+    const int64_t q = a.fblist[f];
     __syncthreads();                                    // LDS of the previous query is free
     load_exact_operands(a, q, sq, st, cent);
     if (tid < kIpTopkMax) { ls[tid] = -INFINITY; li[tid] = kNoIndex; }
@@ -714,10 +882,7 @@ __global__ void __launch_bounds__(256) k_ip_fallback(IRArgs a) {
   }
 }
 
-// One wave per unsettled query: the k best of its kIpFbChunks scan lists.
-__global__ void __launch_bounds__(64) k_ip_fbmerge(IRArgs a) {
-  const int64_t q = blockIdx.x;
-  if (a.flags[q] != 0) return;
+__device__ void fbmerge_one(const IRArgs& a, int64_t q) {
   const int lane = threadIdx.x;
   const int n = kIpFbChunks * a.k;
   const double* cs = a.fb_s + q * n;
@@ -746,6 +911,13 @@ __global__ void __launch_bounds__(64) k_ip_fbmerge(IRArgs a) {
     ps = bsv;
     pi = biv;
   }
+}
+
+// One wave per unsettled query (list entries blockIdx.x, blockIdx.x +
+// gridDim.x, ...): the k best of its kIpFbChunks scan lists.
+__global__ void __launch_bounds__(64) k_ip_fbmerge(IRArgs a) {
+  const int64_t nfb = (int64_t)*a.nfb;
+  for (int64_t f = blockIdx.x; f < nfb; f += gridDim.x) fbmerge_one(a, a.fblist[f]);
 }
 
 }  // namespace
@@ -786,20 +958,23 @@ TopkPlan plan_topk(int64_t nq, int64_t n_db, int k, int d, int m) {
   const size_t nc = (size_t)nqp * p.n_chunks * kc;
   p.off_cand_s = off; off = al(off + nc * 4);
   p.off_cand_i = off; off = al(off + nc * 4);
-  // sample pass (shared-tile kernel, large databases): every 64th tile,
-  // merged into the top kc of the sample per query
-  p.sample_stride = (p.shared && p.n_tiles >= 64 * 256) ? 64 : 0;
-  if (p.sample_stride) {
-    p.sample_tiles = p.n_tiles / p.sample_stride;
+  // sample pass (shared-tile kernel, databases of 4096 tiles or more):
+  // every 64th tile (or a wider stride that keeps the sample scores within
+  // 512 MB), whose scores give each query's floor
+  p.sample_stride = 0;
+  if (p.shared && p.n_tiles >= 64 * 64) {
+    int64_t stride = 64;
+    while ((size_t)nqp * (p.n_tiles / stride) * 16 * 4 > ((size_t)512 << 20) && p.n_tiles / (stride * 2) >= 64)
+      stride *= 2;
+    p.sample_stride = stride;
+    p.sample_tiles = p.n_tiles / stride;
     int64_t sc = groups > 0 ? (256 + groups - 1) / groups : 1;
-    if (sc > p.sample_tiles / 8) sc = p.sample_tiles / 8;
+    if (sc > p.sample_tiles / 4) sc = p.sample_tiles / 4;
     if (sc < 1) sc = 1;
     p.sample_chunks = (int)sc;
-    const size_t ns2 = (size_t)nqp * p.sample_chunks * kc;
-    p.off_s_cand_s = off; off = al(off + ns2 * 4);
-    p.off_s_cand_i = off; off = al(off + ns2 * 4);
-    p.off_s_idx = off; off = al(off + (size_t)nq * kc * 8);
-    p.off_s_score = off; off = al(off + (size_t)nq * kc * 4);
+    p.sample_ld = (p.sample_tiles * 16 + 3) / 4 * 4;
+    p.off_sample = off; off = al(off + (size_t)nqp * p.sample_ld * 4);
+    p.off_floor = off; off = al(off + (size_t)nq * 4);
   }
   p.off_qt64 = off; off = al(off + (size_t)nqp * 256 * 8);
   p.off_tt64 = off; off = al(off + (size_t)nqp * 256 * 8);
@@ -810,6 +985,8 @@ TopkPlan plan_topk(int64_t nq, int64_t n_db, int k, int d, int m) {
   p.off_flags = off; off = al(off + (size_t)nq * 4);
   p.off_fb_s = off; off = al(off + (size_t)nq * kIpFbChunks * k * 8);
   p.off_fb_i = off; off = al(off + (size_t)nq * kIpFbChunks * k * 4);
+  p.off_fblist = off; off = al(off + (size_t)nq * 4);
+  p.off_bpart = off; off = al(off + (size_t)kBoundBlocks * 3 * 4);
   p.bytes = off;
   return p;
 }
@@ -826,6 +1003,7 @@ hipError_t launch_topk(const tq_codebook* cb, const float* queries, const TopkPl
   uint32_t* bounds = reinterpret_cast<uint32_t*>(w + plan.off_bounds);
   const bool qjl = cb->p.qjl_m > 0;
   const int64_t nqp = plan.nqb * (plan.shared ? 16 : 8);
+  int nbp = 1;                          // workgroups of k_ip_bounds
 
   IPArgs pa{};
   pa.q = queries; pa.nq = plan.nq;
@@ -838,7 +1016,7 @@ hipError_t launch_topk(const tq_codebook* cb, const float* queries, const TopkPl
   pa.tt64 = reinterpret_cast<double*>(w + plan.off_tt64);
   pa.qinfo = reinterpret_cast<double*>(w + plan.off_qinfo);
   pa.bounds = bounds;
-  hipLaunchKernelGGL(k_ip_prologue, dim3((unsigned)nqp), dim3(256), 0, stream, pa);
+  hipLaunchKernelGGL(k_ip_prologue, dim3((unsigned)(nqp / kProQ)), dim3(256), 0, stream, pa);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const uint32_t* idxw = static_cast<const uint32_t*>(db.idx);
@@ -848,11 +1026,22 @@ hipError_t launch_topk(const tq_codebook* cb, const float* queries, const TopkPl
     ba.scale = db.scale; ba.rnorm = qjl ? db.rnorm : nullptr;
     ba.idx = idxw; ba.cent64 = cb->dev.cent64;
     ba.n = plan.n_db; ba.d = cb->p.d; ba.bits = cb->p.bits; ba.rw = rw;
-    ba.bounds = bounds;
+    ba.bpart = reinterpret_cast<float*>(w + plan.off_bpart);
     int64_t nb = (plan.n_db + kBoundRows - 1) / kBoundRows;
-    if (nb > 1024) nb = 1024;
+    if (nb > kBoundBlocks) nb = kBoundBlocks;
     if (nb < 1) nb = 1;
-    hipLaunchKernelGGL(k_ip_bounds, dim3((unsigned)nb), dim3(256), 0, stream, ba);
+    nbp = (int)nb;
+    const dim3 g((unsigned)nb), b(256);
+    switch (cb->p.bits) {
+      case 1: hipLaunchKernelGGL(k_ip_bounds<1>, g, b, 0, stream, ba); break;
+      case 2: hipLaunchKernelGGL(k_ip_bounds<2>, g, b, 0, stream, ba); break;
+      case 3: hipLaunchKernelGGL(k_ip_bounds<3>, g, b, 0, stream, ba); break;
+      case 4: hipLaunchKernelGGL(k_ip_bounds<4>, g, b, 0, stream, ba); break;
+      case 5: hipLaunchKernelGGL(k_ip_bounds<5>, g, b, 0, stream, ba); break;
+      case 6: hipLaunchKernelGGL(k_ip_bounds<6>, g, b, 0, stream, ba); break;
+      case 7: hipLaunchKernelGGL(k_ip_bounds<7>, g, b, 0, stream, ba); break;
+      default: hipLaunchKernelGGL(k_ip_bounds<8>, g, b, 0, stream, ba); break;
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
 
@@ -873,7 +1062,8 @@ hipError_t launch_topk(const tq_codebook* cb, const float* queries, const TopkPl
       s2.cand_s = cand_s; s2.cand_i = cand_i;
       s2.tstride = 1;
       s2.nq = plan.nq;
-      s2.floor_s = nullptr;
+      s2.floor_v = nullptr;
+      s2.sample_out = nullptr;
       const bool wide = plan.kc <= 16;
       const unsigned groups = (unsigned)(plan.nqb / (wide ? 16 : 8));
       auto score = [&](const IS2Args& x, dim3 grid) {
@@ -894,18 +1084,19 @@ hipError_t launch_topk(const tq_codebook* cb, const float* queries, const TopkPl
         sp.n_tiles = plan.sample_tiles;
         sp.n_chunks = plan.sample_chunks;
         sp.tiles_per_chunk = (plan.sample_tiles + plan.sample_chunks - 1) / plan.sample_chunks;
-        sp.cand_s = reinterpret_cast<float*>(w + plan.off_s_cand_s);
-        sp.cand_i = reinterpret_cast<int32_t*>(w + plan.off_s_cand_i);
+        sp.sample_out = reinterpret_cast<float*>(w + plan.off_sample);
+        sp.sample_ld = plan.sample_ld;
         score(sp, dim3((unsigned)plan.sample_chunks, groups));
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        IMArgs sm{};
-        sm.cand_s = sp.cand_s; sm.cand_i = sp.cand_i;
-        sm.nq = plan.nq; sm.n_chunks = plan.sample_chunks; sm.k = plan.kc;
-        sm.out_idx = reinterpret_cast<int64_t*>(w + plan.off_s_idx);
-        sm.out_score = reinterpret_cast<float*>(w + plan.off_s_score);
-        hipLaunchKernelGGL(k_ip_merge, dim3((unsigned)plan.nq), dim3(64), 0, stream, sm);
+        float* floor_v = reinterpret_cast<float*>(w + plan.off_floor);
+        if (plan.kc <= 16)
+          hipLaunchKernelGGL(k_ip_floor<16>, dim3((unsigned)plan.nq), dim3(256), 0, stream, sp.sample_out,
+                             plan.sample_ld, plan.sample_tiles * 16, plan.kc, floor_v);
+        else
+          hipLaunchKernelGGL(k_ip_floor<32>, dim3((unsigned)plan.nq), dim3(256), 0, stream, sp.sample_out,
+                             plan.sample_ld, plan.sample_tiles * 16, plan.kc, floor_v);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        s2.floor_s = sm.out_score;
+        s2.floor_v = floor_v;
       }
       score(s2, dim3((unsigned)plan.n_chunks, groups));
     } else {
@@ -953,15 +1144,19 @@ hipError_t launch_topk(const tq_codebook* cb, const float* queries, const TopkPl
   ra.force_scan = force_scan ? 1 : 0;
   ra.out_idx = out_idx; ra.out_score = out_score;
   ra.flags = reinterpret_cast<int32_t*>(w + plan.off_flags);
+  ra.fblist = reinterpret_cast<int32_t*>(w + plan.off_fblist);
+  ra.nfb = bounds + 3;
+  ra.bpart = reinterpret_cast<const float*>(w + plan.off_bpart);
+  ra.nbpart = nbp;
   ra.fb_s = reinterpret_cast<double*>(w + plan.off_fb_s);
   ra.fb_i = reinterpret_cast<int32_t*>(w + plan.off_fb_i);
   hipLaunchKernelGGL(k_ip_refine, dim3((unsigned)plan.nq), dim3(64), 0, stream, ra);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((int64_t)plan.kc < plan.n_db) {
-    const unsigned slots = (unsigned)(plan.nq < 4096 ? plan.nq : 4096);
+    const unsigned slots = (unsigned)(plan.nq < 64 ? plan.nq : 64);
     hipLaunchKernelGGL(k_ip_fallback, dim3(slots, (unsigned)kIpFbChunks), dim3(256), 0, stream, ra);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(k_ip_fbmerge, dim3((unsigned)plan.nq), dim3(64), 0, stream, ra);
+    hipLaunchKernelGGL(k_ip_fbmerge, dim3((unsigned)(plan.nq < 1024 ? plan.nq : 1024)), dim3(64), 0, stream, ra);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;

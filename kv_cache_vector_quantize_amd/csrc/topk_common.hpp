@@ -17,10 +17,12 @@ struct IS2Args {
   int64_t n_db, n_tiles, tiles_per_chunk;
   int64_t tstride;         // tile i of a chunk is database tile (t_begin + i) * tstride
   int64_t nq;
-  const float* floor_s;    // [nq][k] sample top-k scores (entry k-1 is the floor), or null
+  const float* floor_v;    // [nq] the sample floor of each query, or null
   int rw, sw, bits, nu, ns, k, n_chunks;
   float* cand_s;           // [nqp][n_chunks][k]
   int32_t* cand_i;
+  float* sample_out;       // sample pass: [nqp][sample_ld] the score of every sampled row
+  int64_t sample_ld;
 };
 
 namespace {
@@ -94,8 +96,11 @@ __device__ inline f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) {
 // buffer may overflow in the next tile, a refresh (one thread per query)
 // keeps each buffer's best k and raises the threshold to the k-th score.
 // Thresholds start at the sample floor of the query when one is given.
-// WIDE: codes of more than 4 bits (one table entry per code)
-template <int NU, int NS, int QB, int LC, bool WIDE>
+// WIDE: codes of more than 4 bits (one table entry per code).  SAMPLE: the
+// sample pass, which writes the score of every row it visits (sample tile t
+// of the chunk sequence gives rows 16 t .. 16 t + 15 of sample_out) and keeps
+// no candidates.
+template <int NU, int NS, int QB, int LC, bool WIDE, bool SAMPLE>
 __global__ void __launch_bounds__(64 * kHWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 k_ip_score16(IS2Args a) {
   constexpr int NUS = NU + NS;
@@ -108,10 +113,11 @@ k_ip_score16(IS2Args a) {
   // per-query candidate buffers: up to CAP (score, row) pairs; a refresh
   // keeps the best k and raises the query's threshold to the k-th score
   constexpr int CAP = LC + 24;
-  __shared__ float s_cs[QW][CAP];
-  __shared__ int32_t s_ci[QW][CAP];
-  __shared__ int s_cnt[QW];
-  __shared__ float s_thr[QW];                              // a candidate must score above it
+  constexpr int QWB = SAMPLE ? 1 : QW;                     // the sample pass keeps no buffers
+  __shared__ float s_cs[QWB][CAP];
+  __shared__ int32_t s_ci[QWB][CAP];
+  __shared__ int s_cnt[QWB];
+  __shared__ float s_thr[QWB];                             // a candidate must score above it
   __shared__ int s_need;                                   // some buffer holds more than CAP - 16
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int c16 = lane & 15, g4 = lane >> 4;
@@ -131,10 +137,10 @@ k_ip_score16(IS2Args a) {
   // thresholds start at the sample floor: rows scoring below it cannot be
   // among the final candidates, equal ones can (the test is strict, so the
   // floor's predecessor)
-  for (int i = tid; i < QW; i += 64 * kHWaves) {
+  for (int i = tid; i < QWB; i += 64 * kHWaves) {
     const int64_t q = (int64_t)blockIdx.y * QW + i;
     s_cnt[i] = 0;
-    s_thr[i] = (a.floor_s && q < a.nq) ? prev_float(a.floor_s[q * a.k + a.k - 1]) : -INFINITY;
+    s_thr[i] = (a.floor_v && q < a.nq) ? prev_float(a.floor_v[q]) : -INFINITY;
   }
   if (tid == 0) s_need = 0;
   // this wave's query operands (registers), output scales and floors
@@ -150,7 +156,7 @@ k_ip_score16(IS2Args a) {
     const int64_t q = (qb0 + qb) * 16 + c16;
     fm[qb] = a.qsc[q * 2];
     fq[qb] = a.qsc[q * 2 + 1];
-    thq[qb] = (a.floor_s && q < a.nq) ? prev_float(a.floor_s[q * a.k + a.k - 1]) : -INFINITY;
+    thq[qb] = (a.floor_v && q < a.nq) ? prev_float(a.floor_v[q]) : -INFINITY;
   }
 
   // fixed share of the raw tile words of this thread, word e = tid + 512 j:
@@ -248,10 +254,8 @@ k_ip_score16(IS2Args a) {
   const int64_t nt = t_end > t_begin ? t_end - t_begin : 0;
   auto dbt = [&](int64_t i) { return (t_begin + i) * a.tstride; };   // database tile of step i
 
-  // one tile: MFMAs from operand slot cs, unpack of raw slot cs ^ 1 (tile
-  // i + 1), then the scores and lists of tile i
-  auto tile_step = [&](const int cs, const int64_t i) __attribute__((always_inline)) {
-    f32x4 am[QB], aq[QB];
+  // MFMAs of the tile in operand slot cs
+  auto mfma_phase = [&](const int cs, f32x4 (&am)[QB], f32x4 (&aq)[QB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       am[qb] = (f32x4){0.f, 0.f, 0.f, 0.f};
@@ -274,14 +278,19 @@ k_ip_score16(IS2Args a) {
         for (int qb = 0; qb < QB; ++qb) aq[qb] = mfma16(aw[u], bq[qb][NH + u - NU], aq[qb]);
       }
     }
-    build(cs ^ 1, cs ^ 1);          // past the last tile it rebuilds a slot nobody reads
-    const int64_t row0 = dbt(i) * 16;
-    float sc[4], rn[4];
+  };
+  // scale and rnorm of this lane's rows of the tile in slot cs
+  auto load_sr = [&](const int cs, float (&sc)[4], float (&rn)[4]) __attribute__((always_inline)) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       sc[r] = s_sr[cs][0][4 * g4 + r];
       rn[r] = s_sr[cs][1][4 * g4 + r];
     }
+  };
+  // scores of the tile starting at row0 and the appends of those above the
+  // thresholds
+  auto epilogue = [&](const f32x4 (&am)[QB], const f32x4 (&aq)[QB], const float (&sc)[4], const float (&rn)[4],
+                      const int64_t row0, const int64_t srow0) __attribute__((always_inline)) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float sv[4];
@@ -291,23 +300,58 @@ k_ip_score16(IS2Args a) {
         if constexpr (NS > 0) v = fmaf(rn[r] * fq[qb], aq[qb][r], v);
         sv[r] = (row0 + 4 * g4 + r < a.n_db) ? v : -INFINITY;
       }
-      uint32_t pm = 0u;                 // rows of this lane above the query's threshold
+      if constexpr (SAMPLE) {
+        const int64_t q = (qb0 + qb) * 16 + c16;
+        *reinterpret_cast<float4*>(a.sample_out + q * a.sample_ld + srow0 + 4 * g4) =
+            make_float4(sv[0], sv[1], sv[2], sv[3]);
+      } else {
+        uint32_t pm = 0u;               // rows of this lane above the query's threshold
 #pragma unroll
-      for (int r = 0; r < 4; ++r) pm |= (sv[r] > thq[qb]) ? (1u << r) : 0u;
-      if (pm) {
-        // append (at most 16 rows per query and tile; the buffer holds at
-        // most CAP - 16 before the tile)
-        const int li = (wave * QB + qb) * 16 + c16;
+        for (int r = 0; r < 4; ++r) pm |= (sv[r] > thq[qb]) ? (1u << r) : 0u;
+        if (pm) {
+          // append (at most 16 rows per query and step; the buffer holds at
+          // most CAP - 16 before the step)
+          const int li = (wave * QB + qb) * 16 + c16;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          if ((pm >> r) & 1u) {
-            const int slot = atomicAdd(&s_cnt[li], 1);
-            s_cs[li][slot] = sv[r];
-            s_ci[li][slot] = (int32_t)(row0 + 4 * g4 + r);
-            if (slot >= CAP - 16) s_need = 1;
+          for (int r = 0; r < 4; ++r) {
+            if ((pm >> r) & 1u) {
+              const int slot = atomicAdd(&s_cnt[li], 1);
+              s_cs[li][slot] = sv[r];
+              s_ci[li][slot] = (int32_t)(row0 + 4 * g4 + r);
+              if (slot >= CAP - 16) s_need = 1;
+            }
           }
         }
       }
+    }
+  };
+  // The two waves of a SIMD work out of phase so that one's MFMAs overlap the
+  // other's unpack and scores.  Step i, tile i in operand slot cs, tile
+  // i + 1 in raw slot cs ^ 1:
+  //  waves 0-3: MFMAs of tile i, unpack of tile i + 1, scores of tile i;
+  //  waves 4-7: unpack of tile i + 1, scores of tile i - 1 (accumulators
+  //             kept from the previous step), MFMAs of tile i.
+  const bool lead = wave < kHWaves / 2;
+  f32x4 pam[QB], paq[QB];
+  float psc[4], prn[4];
+  int64_t prow0 = -1;                   // row0 of the tile held in pam, paq (-1: none)
+  int64_t psrow0 = 0;
+  auto tile_step = [&](const int cs, const int64_t i) __attribute__((always_inline)) {
+    const int64_t row0 = dbt(i) * 16, srow0 = (t_begin + i) * 16;
+    if (lead) {
+      f32x4 am[QB], aq[QB];
+      float sc[4], rn[4];
+      mfma_phase(cs, am, aq);
+      build(cs ^ 1, cs ^ 1);          // past the last tile it rebuilds a slot nobody reads
+      load_sr(cs, sc, rn);
+      epilogue(am, aq, sc, rn, row0, srow0);
+    } else {
+      build(cs ^ 1, cs ^ 1);
+      if (prow0 >= 0) epilogue(pam, paq, psc, prn, prow0, psrow0);
+      mfma_phase(cs, pam, paq);
+      load_sr(cs, psc, prn);
+      prow0 = row0;
+      psrow0 = srow0;
     }
   };
 
@@ -336,17 +380,19 @@ k_ip_score16(IS2Args a) {
   // buffer above k entries keeps its best k (k <= LC) and its threshold
   // rises to the k-th score (uniform branch: s_need is read after the barrier)
   auto refresh = [&]() {
-    if (s_need) {
-      __syncthreads();
-      if (tid < QW && s_cnt[tid] > a.k) {
-        select_top(tid, a.k);
-        s_cnt[tid] = a.k;
-        s_thr[tid] = fmaxf(s_thr[tid], s_cs[tid][a.k - 1]);
-      }
-      if (tid == 0) s_need = 0;
-      __syncthreads();
+    if constexpr (!SAMPLE) {
+      if (s_need) {
+        __syncthreads();
+        if (tid < QW && s_cnt[tid] > a.k) {
+          select_top(tid, a.k);
+          s_cnt[tid] = a.k;
+          s_thr[tid] = fmaxf(s_thr[tid], s_cs[tid][a.k - 1]);
+        }
+        if (tid == 0) s_need = 0;
+        __syncthreads();
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) thq[qb] = s_thr[(wave * QB + qb) * 16 + c16];
+        for (int qb = 0; qb < QB; ++qb) thq[qb] = s_thr[(wave * QB + qb) * 16 + c16];
+      }
     }
   };
 
@@ -379,15 +425,21 @@ k_ip_score16(IS2Args a) {
       refresh();
     }
   }
+  // the trailing waves' last tile
+  if (!lead && prow0 >= 0) epilogue(pam, paq, psc, prn, prow0, psrow0);
+  if constexpr (!SAMPLE) {
+    __syncthreads();
+    refresh();
 
-  // each query's best k of the chunk, (score desc, index asc)
-  if (tid < QW) {
-    select_top(tid, a.k);
-    const int64_t q = (int64_t)blockIdx.y * QW + tid;
-    const int64_t base = (q * a.n_chunks + chunk) * (int64_t)a.k;
-    for (int o = 0; o < a.k; ++o) {
-      a.cand_s[base + o] = s_cs[tid][o];
-      a.cand_i[base + o] = s_ci[tid][o];
+    // each query's best k of the chunk, (score desc, index asc)
+    if (tid < QW) {
+      select_top(tid, a.k);
+      const int64_t q = (int64_t)blockIdx.y * QW + tid;
+      const int64_t base = (q * a.n_chunks + chunk) * (int64_t)a.k;
+      for (int o = 0; o < a.k; ++o) {
+        a.cand_s[base + o] = s_cs[tid][o];
+        a.cand_i[base + o] = s_ci[tid][o];
+      }
     }
   }
 }
@@ -398,8 +450,14 @@ void launch_score16_ns(const IS2Args& a, int ns, dim3 grid, hipStream_t st) {
     (void)a; (void)ns; (void)grid; (void)st;
   } else {
     if (ns != NS) launch_score16_ns<NU, NS + 1, QB, LC>(a, ns, grid, st);
-    else if (a.bits > 4) hipLaunchKernelGGL((k_ip_score16<NU, NS, QB, LC, true>), grid, dim3(64 * kHWaves), 0, st, a);
-    else hipLaunchKernelGGL((k_ip_score16<NU, NS, QB, LC, false>), grid, dim3(64 * kHWaves), 0, st, a);
+    else if (a.sample_out) {
+      if (a.bits > 4) hipLaunchKernelGGL((k_ip_score16<NU, NS, QB, LC, true, true>), grid, dim3(64 * kHWaves), 0, st, a);
+      else hipLaunchKernelGGL((k_ip_score16<NU, NS, QB, LC, false, true>), grid, dim3(64 * kHWaves), 0, st, a);
+    } else if (a.bits > 4) {
+      hipLaunchKernelGGL((k_ip_score16<NU, NS, QB, LC, true, false>), grid, dim3(64 * kHWaves), 0, st, a);
+    } else {
+      hipLaunchKernelGGL((k_ip_score16<NU, NS, QB, LC, false, false>), grid, dim3(64 * kHWaves), 0, st, a);
+    }
   }
 }
 

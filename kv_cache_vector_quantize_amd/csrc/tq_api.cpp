@@ -953,6 +953,28 @@ tq_status tq_ip_topk_workspace(int64_t nq, int64_t n_db, int32_t k, int32_t d, s
   return TQ_OK;
 }
 
+tq_status tq_ip_topk_scan_count(const tq_codebook* cb, const void* workspace, int64_t nq, int64_t n_db,
+                                int32_t k, void* stream, int64_t* count) {
+  try {
+    if (!cb || !count) return fail(TQ_ERR_INVALID, "codebook and count must be non-NULL");
+    if (nq < 0 || n_db < 0 || k < 0 || k > kIpTopkMax) return fail(TQ_ERR_INVALID, "invalid nq, n_db or k");
+    *count = 0;
+    if (nq == 0 || k == 0) return TQ_OK;
+    if (!workspace) return fail(TQ_ERR_INVALID, "workspace is NULL");
+    const TopkPlan plan = plan_topk(nq, n_db, k, cb->p.d, cb->p.qjl_m);
+    uint32_t c = 0;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(&c, static_cast<const char*>(workspace) + plan.off_bounds + 12, 4,
+                                  hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(e, "scan count read");
+    *count = (int64_t)c;
+    return TQ_OK;
+  } catch (...) {
+    return fail(TQ_ERR_ALLOC, "tq_ip_topk_scan_count: unexpected exception");
+  }
+}
+
 tq_status tq_ip_topk_exact_scan(int32_t always) {
   if (always != 0 && always != 1) return fail(TQ_ERR_INVALID, "always must be 0 or 1");
   g_topk_force_scan.store(always);

@@ -236,12 +236,15 @@ struct TopkPlan {
   bool shared;          // k <= 16: workgroups of 128 queries share unpacked tiles
   int64_t sample_stride, sample_tiles;   // sample pass over every sample_stride-th tile (0: none)
   int sample_chunks;
-  size_t off_s_cand_s, off_s_cand_i, off_s_idx, off_s_score;
+  int64_t sample_ld;                     // floats per query of the sample scores
+  size_t off_sample, off_floor;          // [nqp][sample_ld] sample scores, [nq] floors
   size_t off_qop, off_cinit, off_cand_s, off_cand_i;
   // exact refinement: float64 rotated query and sketch [nqp][d], [nqp][m],
   // per-query norms, database bounds, the approximate top-kc, flags and the
   // fallback lists [nq][kIpFbChunks][k]
   size_t off_qt64, off_tt64, off_qinfo, off_bounds, off_acand_s, off_acand_i, off_flags, off_fb_s, off_fb_i;
+  size_t off_fblist;    // [nq] the queries the exact scan answers (count in bounds[3])
+  size_t off_bpart;     // per-workgroup database maxima of the bounds kernel
   size_t bytes;
 };
 

@@ -155,13 +155,18 @@ def test_topk_parity(dev, d, bits, m, nc, n_db, nq, k):
     gi, gs = _run(cb, qs, codes, n_db, k, dev)
     _check_all(ocb, qs, ref, gi, gs, k, "default")
     # the exact scan alone gives the same answer
+    ws = torch.empty(tq.tq_ip_topk_workspace(nq, n_db, k, d), dtype=torch.uint8, device=dev)
     try:
         tq.tq_ip_topk_exact_scan(True)
-        si, ss = _run(cb, qs, codes, n_db, k, dev)
+        si, ss = tq.tq_ip_topk(cb, torch.from_numpy(qs).to(dev), codes, n_db, k, workspace=ws)
+        n_scan = tq.tq_ip_topk_scan_count(cb, ws, nq, n_db, k)
     finally:
         tq.tq_ip_topk_exact_scan(False)
+    si, ss = si.cpu().numpy(), ss.cpu().numpy().astype(np.float64)
     assert np.array_equal(si, gi)
     assert np.array_equal(ss, gs)
+    # every query was scanned unless all rows are candidates
+    assert n_scan == (nq if n_db > (16 if k <= 10 else min(2 * k, 64)) else 0)
 
 
 def test_topk_ties_go_to_lower_index(dev):
@@ -199,7 +204,10 @@ def test_topk_many_copies_take_the_scan(dev):
     db = np.tile(base, (copies, 1))[perm]
     codes, ref = _db_codes(cb, ocb, db, dev)
     qs = synth.mixture_db(7, d, 4, seed=43).numpy()
-    gi, gs = _run(cb, qs, codes, n_u * copies, k, dev)
+    ws = torch.empty(tq.tq_ip_topk_workspace(len(qs), n_u * copies, k, d), dtype=torch.uint8, device=dev)
+    gi, gs = tq.tq_ip_topk(cb, torch.from_numpy(qs).to(dev), codes, n_u * copies, k, workspace=ws)
+    assert tq.tq_ip_topk_scan_count(cb, ws, len(qs), n_u * copies, k) == len(qs)
+    gi, gs = gi.cpu().numpy(), gs.cpu().numpy().astype(np.float64)
     _check_all(ocb, qs, ref, gi, gs, k, "copies")
     for i in range(len(qs)):
         # the k returned rows are the k lowest indices holding the best vector
@@ -271,6 +279,9 @@ def test_topk_full_size_vector_search(dev):
     qs = synth.mixture_db(nq, d, 256, seed=8).numpy()
     codes, ref = _db_codes(cb, ocb, db.astype(np.float64), dev)
     del db
-    gi, gs = _run(cb, qs, codes, n_db, k, dev)
+    ws = torch.empty(tq.tq_ip_topk_workspace(nq, n_db, k, d), dtype=torch.uint8, device=dev)
+    gi, gs = tq.tq_ip_topk(cb, torch.from_numpy(qs).to(dev), codes, n_db, k, workspace=ws)
+    print("queries answered by the exact scan:", tq.tq_ip_topk_scan_count(cb, ws, nq, n_db, k))
+    gi, gs = gi.cpu().numpy(), gs.cpu().numpy().astype(np.float64)
     n_strict = _check_all(ocb, qs, ref, gi, gs, k, "1e6")
     assert n_strict >= nq - 5

@@ -146,3 +146,9 @@ def test_exact_scan_switch_validated():
     assert L.tq_ip_topk_exact_scan(2) == _lib.TQ_ERR_INVALID
     assert b"always" in L.tq_last_error()
     assert L.tq_ip_topk_exact_scan(0) == _lib.TQ_OK
+
+
+def test_scan_count_validates_arguments():
+    L = tq.lib()
+    c = ctypes.c_int64(5)
+    assert L.tq_ip_topk_scan_count(None, None, 1, 10, 1, None, ctypes.byref(c)) == _lib.TQ_ERR_INVALID
