@@ -127,7 +127,8 @@ __device__ inline void share_load(Share<DT>& sh, const void* x, int64_t e0, bool
 }
 
 template <int DT, bool T32, int NP, bool QJ>
-__global__ void __launch_bounds__(256) k_q128(Q128Args a) {
+// two-part variants without a sketch keep three workgroups per CU
+__global__ void __launch_bounds__(256, (NP == 2 && !QJ) ? 3 : 1) k_q128(Q128Args a) {
   static_assert(!(QJ && T32), "sketch signs are written in the row layout only");
   constexpr bool XLO = DT != TQ_BF16, XLO2 = DT == TQ_F32;
   __shared__ __align__(16) uint16_t xh[TILE][XS];
@@ -183,12 +184,10 @@ __global__ void __launch_bounds__(256) k_q128(Q128Args a) {
     share_load<DT>(sh, a.x, ((int64_t)seq * a.n_tok + (p - a.tok_off)) * 128 + c0, valid, vec_ok);
   };
 
-  Share<DT> cur;
-  int tile = blockIdx.x;
-  if (tile < a.n_tiles) fetch(cur, tile);
-  __syncthreads();
-
-  for (; tile < a.n_tiles; tile += gridDim.x) {
+  // two tiles in flight per workgroup: the share of tile + 2 G is fetched
+  // into the registers of tile as soon as that tile sits in LDS
+  const int G2 = 2 * (int)gridDim.x;
+  auto step = [&](Share<DT>& cur, const int tile) __attribute__((always_inline)) {
     int seq;
     int64_t blk;
     where(tile, seq, blk);
@@ -266,8 +265,8 @@ __global__ void __launch_bounds__(256) k_q128(Q128Args a) {
       }
     }
     __syncthreads();
-    // the next tile's share is in flight while this one is computed
-    if (tile + (int)gridDim.x < a.n_tiles) fetch(cur, tile + (int)gridDim.x);
+    // the share of the tile after next goes in flight while this one is computed
+    if (tile + G2 < a.n_tiles) fetch(cur, tile + G2);
 
     // (b) rotation: row layout -> D[coordinate][vector], tile32 -> D[vector][coordinate]
     auto prod = [&](f32x16 c, bf16x8 xo, bf16x8 po) { return T32 ? mfma32(xo, po, c) : mfma32(po, xo, c); };
@@ -492,6 +491,17 @@ __global__ void __launch_bounds__(256) k_q128(Q128Args a) {
       }
       __syncthreads();
     }
+  };
+
+  Share<DT> s0, s1;
+  int tile = blockIdx.x;
+  if (tile < a.n_tiles) fetch(s0, tile);
+  if (tile + (int)gridDim.x < a.n_tiles) fetch(s1, tile + (int)gridDim.x);
+  __syncthreads();
+  for (; tile < a.n_tiles; tile += G2) {
+    step(s0, tile);
+    if (tile + (int)gridDim.x >= a.n_tiles) break;
+    step(s1, tile + (int)gridDim.x);
   }
 }
 
