@@ -105,6 +105,7 @@ def parse():
     ap.add_argument("--no-ab", action="store_true", help="skip the dequantize-then-attend leg")
     ap.add_argument("--no-paged", action="store_true", help="skip the paged-cache leg")
     ap.add_argument("--no-polar", action="store_true", help="skip the PolarQuant-keys leg")
+    ap.add_argument("--no-dims", action="store_true", help="skip the other-head-dimension leg")
     ap.add_argument("--calib-copy", action="store_true",
                     help="accepted for profiling commands; the 1 GiB copy always runs")
     return ap.parse_args()
@@ -463,6 +464,50 @@ def bit_sweep_leg(torch, tq, synth, dev, iters, warm):
                 variants=res)
 
 
+def head_dims_leg(torch, tq, synth, dev, iters, warm):
+    """Decode at head dimensions other than 128 (the fp32 kernels): the 32K
+    GQA layer (B=32, 32 query / 4 KV heads, context 32768, bf16 K/V N(0,1)
+    with outlier channels 3/77 x20) with 3-bit keys + QJL m=d and 4-bit
+    values, for d = 64, 96 and 256, and at d = 128 with 5-bit keys (a width
+    the MFMA kernels lack)."""
+    B, Hq, Hkv, N = 32, 32, 4, 32768
+    res = []
+    for name, d, kb, km, vb in [("d64 k3+qjl v4", 64, 3, 64, 4), ("d96 k3+qjl v4", 96, 3, 96, 4),
+                                ("d256 k3+qjl v4", 256, 3, 256, 4), ("d128 k5 v4", 128, 5, 0, 4)]:
+        tau = 1.0 / math.sqrt(d)
+        kcb = tq.Codebook(d, kb, qjl_m=km, rot_seed=1, qjl_seed=2)
+        vcb = tq.Codebook(d, vb, rot_seed=3)
+        kc = tq.Codes(kcb, B * Hkv, N, tq.TQ_LAYOUT_ROW)
+        vc = tq.Codes(vcb, B * Hkv, N, tq.TQ_LAYOUT_TILE32)
+        k = synth.kv_gaussian(B, Hkv, N, d, 30, dtype="bf16", device=dev, channels=[3, 77], factor=20.0)
+        tq.tq_quantize_kv(kcb, None, k.view(B * Hkv, N, d), None, kc, None)
+        del k
+        v = synth.kv_gaussian(B, Hkv, N, d, 31, dtype="bf16", device=dev, channels=[3, 77], factor=20.0)
+        tq.tq_quantize_kv(None, vcb, None, v.view(B * Hkv, N, d), None, vc)
+        del v
+        q = synth.queries_gaussian(B, Hq, d, 32, dtype="bf16", device=dev)
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+        ws = torch.empty(tq.tq_attn_decode_workspace(B, Hq, Hkv, N, d), dtype=torch.uint8, device=dev)
+        call = lambda: tq.tq_attn_decode(kcb, vcb, q, kc, vc, N, tau, out=out, workspace=ws)
+        for _ in range(warm):
+            call()
+        torch.cuda.synchronize()
+        tq.tq_profile_enable(True)
+        ms, per = timed_iters(torch, call, iters)
+        tq.tq_profile_enable(False)
+        split_ms, split_spread = kernel_spread(tq, tq.TQ_KERNEL_DECODE_SPLIT)
+        bpt = (kb * d + km + vb * d) // 8 + 4 + (4 if km else 0) + 4
+        gbs = bpt * B * Hkv * N / (split_ms * 1e-3) / 1e9
+        res.append(dict(variant=name, KV_tokens_per_s=round(B * N / (ms * 1e-3), 1), ms_per_decode=round(ms, 4),
+                        decode_ms_spread=spread(per), split_kernel_ms=round(split_ms, 4),
+                        split_kernel_ms_spread=split_spread, bytes_per_token_head=bpt,
+                        split_GBps=round(gbs, 1), frac_hbm=round(gbs / HBM_PEAK_GBS, 4)))
+        del kc, vc, kcb, vcb, ws
+    return dict(workload="decode at other head dimensions (fp32 kernels): B=32, Hq=32, Hkv=4, context 32768, "
+                         "bf16 K/V N(0,1) with channels 3/77 x20, bf16 queries",
+                variants=res)
+
+
 def vector_search_leg(torch, tq, synth, dev, iters, warm):
     """1,000,000 unit-norm vectors d=200 (256-cluster mixture), 4-bit + QJL
     m=200 codes, 1000 queries, k=10: queries/s of tq_ip_topk, MFMA
@@ -732,6 +777,9 @@ def main():
     if not args.no_sweep:
         print("[bench] bit-width sweep leg", file=sys.stderr, flush=True)
         res["bit_sweep"] = bit_sweep_leg(torch, tq, synth, dev, iters=args.steps, warm=args.warmup)
+    if not args.no_dims:
+        print("[bench] head-dimension leg", file=sys.stderr, flush=True)
+        res["head_dims"] = head_dims_leg(torch, tq, synth, dev, iters=args.steps, warm=args.warmup)
     if not args.no_search:
         print("[bench] vector-search leg", file=sys.stderr, flush=True)
         res["vector_search"] = vector_search_leg(torch, tq, synth, dev, iters=max(10, args.steps // 2),

@@ -211,7 +211,8 @@ tq_status tq_quantize_kv(const tq_codebook* kcb, const tq_codebook* vcb, const v
                          int64_t tok_offset, const tq_codes* k_out, const tq_codes* v_out,
                          void* stream);
 
-/* Workspace bytes tq_attn_decode needs for this shape (host only). */
+/* Workspace bytes tq_attn_decode needs for this shape (host only); d in
+ * 3..256 (TQ_ERR_INVALID otherwise), valid for any codebooks of that d. */
 tq_status tq_attn_decode_workspace(int64_t B, int64_t Hq, int64_t Hkv, int64_t n_ctx,
                                    int32_t d, size_t* bytes);
 
@@ -230,8 +231,12 @@ tq_status tq_attn_decode_workspace(int64_t B, int64_t Hq, int64_t Hkv, int64_t n
  *  out       fp32 [B][Hq][d]
  *  logits    fp32 [B][Hq][n_ctx] or NULL; -inf for j >= len_b
  *  workspace device scratch of >= tq_attn_decode_workspace bytes
- * Errors: TQ_ERR_INVALID, TQ_ERR_UNSUPPORTED (d != 128 or bit widths
- * without a kernel), TQ_ERR_HIP. */
+ * Kernels: d = 128 with key and value codes of 2, 3, 4 or 8 bits and
+ * qjl_m <= 128 run on bf16 hi/lo MFMA (about 2^-16 relative per product);
+ * every other scalar shape (d <= 256, 1..8 bits, qjl_m <= 256) on fp32 FMAs.
+ * Errors: TQ_ERR_INVALID, TQ_ERR_UNSUPPORTED (polar codebooks other than
+ * (4, 2) keys at d = 128 with qjl_m <= 128 and scalar values of 2, 3, 4 or
+ * 8 bits), TQ_ERR_HIP. */
 tq_status tq_attn_decode(const tq_codebook* kcb, const tq_codebook* vcb, const void* q,
                          int32_t qdt, int64_t B, int64_t Hq, int64_t Hkv, const tq_codes* k,
                          const tq_codes* v, const int32_t* seq_lens, int64_t n_ctx,
@@ -319,8 +324,9 @@ tq_status tq_ip_topk_workspace(int64_t nq, int64_t n_db, int32_t k, int32_t d, s
  *  workspace device scratch of >= tq_ip_topk_workspace bytes, 256-byte aligned
  * The result is the exact top-k of s_j evaluated in float64 from the codes
  * (Pi q and S Pi q formed in float64), and out_score is that float64 score
- * rounded to fp32.  A bf16 hi/lo MFMA pass keeps kc candidates per query
- * (kc = 16 for k <= 10, else min(2k, 64)); the candidates are rescored in
+ * rounded to fp32.  An MFMA pass keeps kc candidates per query (kc = 16 for
+ * k <= 10, else min(2k, 64); fp16 operands, each query scaled by a power of
+ * two, for kc <= 32, bf16 hi/lo beyond); the candidates are rescored in
  * float64, and a query is settled when the kc-th approximate score plus a
  * bound on the approximate score's error (over every row of the database)
  * stays below the k-th exact score.  Other queries (near-ties at the k-th

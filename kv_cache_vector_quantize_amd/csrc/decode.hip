@@ -26,6 +26,7 @@
 //     (max, sum, o~) are merged in LDS and written once per workgroup.
 //  3. combine, one workgroup per row: log-sum-exp merge of the workgroups'
 //     partials in a fixed order, then out = Pi_V^T o~ / l.
+#include <algorithm>
 #include <type_traits>
 
 #include "tq_internal.hpp"
@@ -1036,8 +1037,11 @@ DecodePlan plan_decode(int64_t B, int64_t Hq, int64_t Hkv, int64_t n_ctx, int d,
   p.n_wg = (p.n_parts + kWaves - 1) / kWaves;
   size_t off = 0;
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
-  p.off_qop = off; off = al(off + (size_t)p.rows * QOP_DWORDS * 4);
-  p.off_part_o = off; off = al(off + (size_t)p.rows * p.n_wg * 8 * D * 4);
+  // query operands: the MFMA kernels' (d = 128) or the fp32 kernels' per row,
+  // whichever is larger, so one size serves every codebook of this d
+  const size_t qrow = std::max<size_t>((size_t)QOP_DWORDS * 4, (size_t)decode_generic_row_bytes(d));
+  p.off_qop = off; off = al(off + (size_t)p.rows * qrow);
+  p.off_part_o = off; off = al(off + (size_t)p.rows * p.n_wg * 8 * pad32(d) * 4);
   p.off_part_ml = off; off = al(off + (size_t)p.rows * p.n_wg * 8 * 2 * 4);
   p.bytes = off;
   return p;
@@ -1053,6 +1057,8 @@ hipError_t launch_decode(const tq_codebook* kcb, const tq_codebook* vcb, const v
   float* part_ml = reinterpret_cast<float*>(w + plan.off_part_ml);
   if (plan.rows == 0) return hipSuccess;
   if (plan.n_wg > kMaxWg) return hipErrorInvalidValue;
+  if (!decode_supported(kcb, vcb))
+    return launch_decode_generic(kcb, vcb, q, qdt, plan, k, v, seq_lens, sm_scale, out, logits, ws, stream, pm);
 
   PArgs pa{};
   pa.q = q; pa.qdt = qdt;

@@ -811,7 +811,7 @@ tq_status tq_attn_decode_workspace(int64_t B, int64_t Hq, int64_t Hkv, int64_t n
   if (!bytes) return fail(TQ_ERR_INVALID, "bytes is NULL");
   if (B < 0 || Hq < 0 || Hkv <= 0 || n_ctx < 0 || Hq % Hkv)
     return fail(TQ_ERR_INVALID, "need B, n_ctx >= 0, Hkv > 0, Hq a multiple of Hkv");
-  if (d != 128) return fail(TQ_ERR_UNSUPPORTED, "decode supports d = 128");
+  if (d < 3 || d > 256) return fail(TQ_ERR_INVALID, "d must be in 3..256");
   *bytes = plan_decode(B, Hq, Hkv, n_ctx, d).bytes;
   return TQ_OK;
 }
@@ -831,10 +831,10 @@ tq_status decode_impl(const tq_codebook* kcb, const tq_codebook* vcb, const void
   if (B < 0 || Hq < 0 || Hkv <= 0 || n_ctx < 0 || Hq % Hkv)
     return fail(TQ_ERR_INVALID, "need B, n_ctx >= 0, Hkv > 0, Hq a multiple of Hkv");
   if (kcb->p.d != vcb->p.d) return fail(TQ_ERR_INVALID, "key and value codebooks differ in d");
-  if (!decode_supported(kcb, vcb))
+  if (!decode_supported(kcb, vcb) && !decode_generic_supported(kcb, vcb))
     return fail(TQ_ERR_UNSUPPORTED,
-                "decode supports d = 128, qjl_m <= 128, value codes of 2, 3, 4 or 8 bits and key codes of "
-                "2, 3, 4 or 8 bits or polar with (b1, br) = (4, 2)");
+                "decode takes scalar codebooks, or polar keys with (b1, br) = (4, 2) at d = 128 and "
+                "qjl_m <= 128 with scalar values of 2, 3, 4 or 8 bits");
   if (!std::isfinite(sm_scale)) return fail(TQ_ERR_INVALID, "sm_scale must be finite");
   if (B * Hq == 0) return TQ_OK;
   if (!q || !out) return fail(TQ_ERR_INVALID, "q and out must be non-NULL");
@@ -894,7 +894,8 @@ tq_status tq_attn_decode_noalloc(const tq_codebook* kcb, const tq_codebook* vcb,
   try {
     if (B < 0 || Hq < 0 || Hkv <= 0 || n_ctx < 0 || Hq % Hkv)
       return fail(TQ_ERR_INVALID, "need B, n_ctx >= 0, Hkv > 0, Hq a multiple of Hkv");
-    const size_t need = plan_decode(B, Hq, Hkv, n_ctx, 128).bytes;
+    if (!kcb || !vcb) return fail(TQ_ERR_INVALID, "codebook is NULL");
+    const size_t need = plan_decode(B, Hq, Hkv, n_ctx, kcb->p.d).bytes;
     if (need > kNoallocScratchBytes)
       return fail(TQ_ERR_UNSUPPORTED, "tq_attn_decode_noalloc: this shape needs " + std::to_string(need) +
                                           " bytes of scratch, above the fixed " +
@@ -921,7 +922,7 @@ tq_status tq_attn_decode_paged_workspace(int64_t B, int64_t Hq, int64_t Hkv, int
     return fail(TQ_ERR_INVALID, "need B, n_ctx >= 0, Hkv > 0, Hq a multiple of Hkv");
   if (page_tokens < 32 || page_tokens > 65536 || (page_tokens & (page_tokens - 1)))
     return fail(TQ_ERR_INVALID, "page_tokens must be a power of two in 32..65536");
-  if (d != 128) return fail(TQ_ERR_UNSUPPORTED, "decode supports d = 128");
+  if (d < 3 || d > 256) return fail(TQ_ERR_INVALID, "d must be in 3..256");
   *bytes = plan_decode(B, Hq, Hkv, n_ctx, d, page_tokens).bytes;
   return TQ_OK;
 }

@@ -218,7 +218,16 @@ hipError_t launch_decode(const tq_codebook* kcb, const tq_codebook* vcb, const v
                          float* out, float* logits, void* ws, hipStream_t stream,
                          const PageMap& pm = PageMap{});
 
+// d = 128 MFMA kernels (decode.hip)
 bool decode_supported(const tq_codebook* kcb, const tq_codebook* vcb);
+// fp32 kernels for every other scalar shape (decode_gen.hip): d <= 256, bits
+// 1..8, sketches <= 256 rows; launch_decode hands them such codebooks
+bool decode_generic_supported(const tq_codebook* kcb, const tq_codebook* vcb);
+int64_t decode_generic_row_bytes(int d);   // prologue output per row
+hipError_t launch_decode_generic(const tq_codebook* kcb, const tq_codebook* vcb, const void* q, tq_dtype qdt,
+                                 const DecodePlan& plan, const tq_codes& k, const tq_codes& v,
+                                 const int32_t* seq_lens, float sm_scale, float* out, float* logits, void* ws,
+                                 hipStream_t stream, const PageMap& pm);
 
 // Inner-product top-k (limits of the LDS-resident per-lane lists and operands)
 constexpr int kIpTopkMax = 32;   // k

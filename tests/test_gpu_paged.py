@@ -79,16 +79,20 @@ def _table(B, n_lp, n_pages, seed):
     return perm.reshape(B, n_lp).astype(np.int32)
 
 
-@pytest.mark.parametrize("pt,N,lens", [(64, 300, None), (32, 200, [200, 77]), (128, 513, [1, 513])])
-def test_paged_decode_matches_oracle(dev, pt, N, lens):
-    _say("paged decode", pt, N, lens)
-    B, Hq, Hkv, d = 2, 16, 2, 128
+@pytest.mark.parametrize("pt,N,lens,d,kb,km,vb", [
+    (64, 300, None, 128, 3, 128, 4), (32, 200, [200, 77], 128, 3, 128, 4), (128, 513, [1, 513], 128, 3, 128, 4),
+    # head dimensions of the fp32 kernels
+    (32, 200, [200, 77], 96, 4, 64, 3), (64, 300, None, 200, 2, 200, 4)])
+def test_paged_decode_matches_oracle(dev, pt, N, lens, d, kb, km, vb):
+    _say("paged decode", pt, N, lens, d, kb, km, vb)
+    B, Hq, Hkv = 2, 16, 2
     tau = 1.0 / np.sqrt(d)
-    kcb = tq.Codebook(d, 3, qjl_m=128, rot_seed=1, qjl_seed=2)
-    vcb = tq.Codebook(d, 4, rot_seed=3)
+    kcb = tq.Codebook(d, kb, qjl_m=km, rot_seed=1, qjl_seed=2)
+    vcb = tq.Codebook(d, vb, rot_seed=3)
     okc, ovc = U.oracle_codebook(kcb), U.oracle_codebook(vcb)
-    k = U.to_f64(synth.kv_gaussian(B, Hkv, N, d, 41, dtype="f32", device="cpu", channels=[3, 77, 101], factor=20.0))
-    v = U.to_f64(synth.kv_gaussian(B, Hkv, N, d, 42, dtype="f32", device="cpu", channels=[3, 77, 101], factor=20.0))
+    ch = [c for c in (3, 77, 101) if c < d]
+    k = U.to_f64(synth.kv_gaussian(B, Hkv, N, d, 41, dtype="f32", device="cpu", channels=ch, factor=20.0))
+    v = U.to_f64(synth.kv_gaussian(B, Hkv, N, d, 42, dtype="f32", device="cpu", channels=ch, factor=20.0))
     q = np.random.default_rng(43).standard_normal((B, Hq, d))
     n_lp = (N + pt - 1) // pt
     n_pages = B * n_lp + 3
@@ -115,8 +119,9 @@ def test_paged_decode_matches_oracle(dev, pt, N, lens):
     torch.cuda.synchronize()
     f32 = lambda a: a.astype(np.float32).astype(np.float64)
     stack = lambda rs, key: np.stack([r[key] for r in rs]).reshape(B, Hkv, N, *rs[0][key].shape[1:])
-    okcodes = dict(idx=stack(kr, "idx"), scale=f32(stack(kr, "scale")), sign=stack(kr, "sign"),
-                   rnorm=f32(stack(kr, "rnorm")))
+    okcodes = dict(idx=stack(kr, "idx"), scale=f32(stack(kr, "scale")))
+    if km:
+        okcodes.update(sign=stack(kr, "sign"), rnorm=f32(stack(kr, "rnorm")))
     ovcodes = dict(idx=stack(vr, "idx"), scale=f32(stack(vr, "scale")))
     ref_lg, ref_out = O.attn_decode(okc, ovc, q, okcodes, ovcodes, tau, n_valid=lens)
     op, oc = out_p.cpu().numpy().astype(np.float64), out_c.cpu().numpy().astype(np.float64)

@@ -72,9 +72,15 @@ def test_decode_workspace_validation():
     assert tq.tq_attn_decode_workspace(1, 8, 1, 0, 128) > 0
     with pytest.raises(tq.TQError):
         tq.tq_attn_decode_workspace(1, 7, 2, 100, 128)       # Hq not a multiple of Hkv
-    with pytest.raises(tq.TQError) as e:
-        tq.tq_attn_decode_workspace(1, 8, 1, 100, 64)
-    assert e.value.status == _lib.TQ_ERR_UNSUPPORTED
+    # every head dimension of a codebook (3..256) has a decode path; the
+    # workspace grows with the padded dimension
+    for d in (3, 64, 100, 200, 256):
+        assert tq.tq_attn_decode_workspace(2, 16, 2, 1000, d) > 0
+    assert tq.tq_attn_decode_workspace(2, 16, 2, 100000, 256) > tq.tq_attn_decode_workspace(2, 16, 2, 100000, 64)
+    for d in (2, 257):
+        with pytest.raises(tq.TQError) as e:
+            tq.tq_attn_decode_workspace(1, 8, 1, 100, d)
+        assert e.value.status == _lib.TQ_ERR_INVALID
 
 
 def test_quantize_rejects_null_inputs_before_device():
@@ -102,9 +108,10 @@ def test_paged_workspace_and_page_size_validation():
         with pytest.raises(tq.TQError) as e:
             tq.tq_attn_decode_paged_workspace(2, 16, 2, 300, 128, pt)
         assert e.value.status == _lib.TQ_ERR_INVALID
+    assert tq.tq_attn_decode_paged_workspace(2, 16, 2, 300, 64, 64) > 0
     with pytest.raises(tq.TQError) as e:
-        tq.tq_attn_decode_paged_workspace(2, 16, 2, 300, 64, 64)
-    assert e.value.status == _lib.TQ_ERR_UNSUPPORTED
+        tq.tq_attn_decode_paged_workspace(2, 16, 2, 300, 300, 64)
+    assert e.value.status == _lib.TQ_ERR_INVALID
 
 
 def test_paged_calls_reject_bad_pages_before_device():
