@@ -79,6 +79,13 @@ def kv_gaussian(B: int, H: int, N: int, d: int, seed: int, *, dtype: str = "bf16
     """
     torch = _torch()
     tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dtype]
+    # channel ids are checked here, on the host: a device index_put with an
+    # id past d would access memory out of bounds
+    ids = list(channels) if channels is not None else []
+    if per_head_channels is not None:
+        ids += [int(c) for c in np.asarray(per_head_channels).reshape(-1)]
+    if any(c < 0 or c >= d for c in ids):
+        raise ValueError(f"outlier channel ids must lie in [0, {d})")
     out = torch.empty((B, H, N, d), dtype=tdt, device=device)
     if device == "cpu":
         for b in range(B):
