@@ -13,9 +13,10 @@
 //     scalar load brings a coordinate's value for all 8 queries, and sum_j t_j.
 //  2. k_gsplit<BK>, 8 waves per workgroup, each wave a chunk of the row in
 //     64-token tiles.  Logits with lane = token: each key index goes through
-//     an LDS centroid table and meets the 8 query values in scalar registers
-//     (8 FMAs per coordinate); each sign bit takes one FMA per query against
-//     t, and the sketch term is rnorm (2 sum_{sign=1} t - sum t).  Online
+//     an LDS centroid table and meets the 8 query values, read from LDS by
+//     all lanes at one address (8 FMAs per coordinate); each sign bit takes
+//     one FMA per query against t, and the sketch term is
+//     rnorm (2 sum_{sign=1} t - sum t).  Online
 //     softmax in base 2.  Weights x values with lane = coordinate (up to 4 per
 //     lane): each 32-token tile32 block is staged in the wave's LDS slot and
 //     every (token, coordinate) index is read from it.  The waves' partials
@@ -29,7 +30,6 @@ namespace tq {
 namespace {
 
 typedef __attribute__((ext_vector_type(4))) float f32x4;
-typedef const __attribute__((address_space(4))) float* cfloat_p;   // scalar-load view
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -173,12 +173,22 @@ template <int BK>
 __global__ void __launch_bounds__(64 * kGWaves) k_gsplit(GSArgs a) {
   __shared__ __align__(16) float s_kc[kGTab];
   __shared__ __align__(16) float s_vc[kGTab];
+  // the row's q~ [dp][8], t [mp][8] and sum t [8]
+  __shared__ __align__(16) float s_q[(kGMaxD + kGMaxM) * 8 + 8];
   __shared__ __align__(16) char s_work[kGLds];
   __shared__ float s_M[kGWaves][8], s_l[kGWaves][8];
   const int tid = threadIdx.x;
   for (int i = tid; i < kGTab; i += 64 * kGWaves) {
     s_kc[i] = i < a.lk ? a.kcent[i] : 0.f;
     s_vc[i] = i < a.lv ? a.vcent[i] : 0.f;
+  }
+  {
+    // q~ and t of the row; every lane of a wave later reads one coordinate's
+    // 8 values at one address (a broadcast)
+    const float* src = a.gq + (int64_t)blockIdx.y * grow_floats(a.dp);
+    const int nqt = (a.dp + 32 * ((a.m + 31) >> 5)) * 8;
+    for (int i = tid; i < nqt; i += 64 * kGWaves) s_q[i] = src[i];
+    if (tid < 8) s_q[(kGMaxD + kGMaxM) * 8 + tid] = src[(int64_t)(a.dp + kGMaxM) * 8 + tid];
   }
   __syncthreads();
 
@@ -200,9 +210,8 @@ __global__ void __launch_bounds__(64 * kGWaves) k_gsplit(GSArgs a) {
   if (t_end > n_valid) t_end = n_valid;
   if (part >= a.n_parts) t_end = t_begin;
 
-  const cfloat_p qrow = (cfloat_p)(a.gq + (int64_t)row * grow_floats(a.dp));
-  const cfloat_p trow = qrow + (int64_t)a.dp * 8;
-  const cfloat_p tsum = qrow + (int64_t)(a.dp + kGMaxM) * 8;
+  const float* trow = s_q + a.dp * 8;
+  const float* tsum = s_q + (kGMaxD + kGMaxM) * 8;
   const int g32 = a.dp >> 5;
   const int ns = (a.m + 31) >> 5;
   const int nq = a.g - qg * 8 < 8 ? a.g - qg * 8 : 8;
@@ -258,12 +267,26 @@ __global__ void __launch_bounds__(64 * kGWaves) k_gsplit(GSArgs a) {
         const int gn = gi + 1 < g32 ? gi + 1 : gi;
 #pragma unroll
         for (int j = 0; j < BK; ++j) kn[j] = kr[gn * BK + j];
-        const cfloat_p qv = qrow + gi * 256;
+        const float* qv = s_q + gi * 256;
+        // four coordinates per batch: all their LDS reads are issued before
+        // the FMAs that consume them
 #pragma unroll
-        for (int u = 0; u < 32; ++u) {
-          const float cv = s_kc[kfield<BK>(kw, u * BK)];
+        for (int u0 = 0; u0 < 32; u0 += 4) {
+          float cv[4];
+          f32x4 q0[4], q1[4];
 #pragma unroll
-          for (int c = 0; c < 8; ++c) acc[c] = fmaf(cv, qv[u * 8 + c], acc[c]);
+          for (int k = 0; k < 4; ++k) {
+            cv[k] = s_kc[kfield<BK>(kw, (u0 + k) * BK)];
+            q0[k] = *reinterpret_cast<const f32x4*>(qv + (u0 + k) * 8);
+            q1[k] = *reinterpret_cast<const f32x4*>(qv + (u0 + k) * 8 + 4);
+          }
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[c] = fmaf(cv[k], q0[k][c], acc[c]);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[4 + c] = fmaf(cv[k], q1[k][c], acc[4 + c]);
+          }
         }
 #pragma unroll
         for (int j = 0; j < BK; ++j) kw[j] = kn[j];
@@ -276,12 +299,23 @@ __global__ void __launch_bounds__(64 * kGWaves) k_gsplit(GSArgs a) {
       rn = a.krnorm[seq * a.k_stride + pp];
       for (int gs = 0; gs < ns; ++gs) {
         const uint32_t sw = sr[gs];
-        const cfloat_p tv = trow + gs * 256;
+        const float* tv = trow + gs * 256;
 #pragma unroll
-        for (int j = 0; j < 32; ++j) {
-          const float f = (float)((sw >> j) & 1u);
+        for (int j0 = 0; j0 < 32; j0 += 4) {
+          f32x4 t0[4], t1[4];
 #pragma unroll
-          for (int c = 0; c < 8; ++c) accs[c] = fmaf(f, tv[j * 8 + c], accs[c]);
+          for (int k = 0; k < 4; ++k) {
+            t0[k] = *reinterpret_cast<const f32x4*>(tv + (j0 + k) * 8);
+            t1[k] = *reinterpret_cast<const f32x4*>(tv + (j0 + k) * 8 + 4);
+          }
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const float f = (float)((sw >> (j0 + k)) & 1u);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) accs[c] = fmaf(f, t0[k][c], accs[c]);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) accs[4 + c] = fmaf(f, t1[k][c], accs[4 + c]);
+          }
         }
       }
     }
@@ -326,21 +360,35 @@ __global__ void __launch_bounds__(64 * kGWaves) k_gsplit(GSArgs a) {
       for (int e = lane; e < (a.blk_bytes >> 4); e += 64) sv[e] = src[e];
       const uint32_t* s32 = reinterpret_cast<const uint32_t*>(s_v);
       const int ntb = t_end - tb < 32 ? (int)(t_end - tb) : 32;
-      for (int t = 0; t < ntb; ++t) {
-        const f32x4 w0 = *reinterpret_cast<const f32x4*>(s_w + (32 * bi + t) * 8);
-        const f32x4 w1 = *reinterpret_cast<const f32x4*>(s_w + (32 * bi + t) * 8 + 4);
-        const int tt = (16 * ((t & 15) >> 2) * a.g16 * 8 + (t & 3) + 4 * (t >> 4)) * a.bv;
+      // two tokens per batch (weights of a token past ntb are 0)
+      for (int t = 0; t < ntb; t += 2) {
+        f32x4 w0[2], w1[2];
+        float cv[2][4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          if (r >= nr) break;
-          const int p = cib[r] + tt;
-          const uint32_t lo = s32[p >> 5], hi = s32[(p >> 5) + 1];
-          const float cv = s_vc[__builtin_amdgcn_alignbit(hi, lo, p & 31) & vmask];
+        for (int k = 0; k < 2; ++k) {
+          const int tk = t + k;
+          w0[k] = *reinterpret_cast<const f32x4*>(s_w + (32 * bi + tk) * 8);
+          w1[k] = *reinterpret_cast<const f32x4*>(s_w + (32 * bi + tk) * 8 + 4);
+          const int tt = (16 * ((tk & 15) >> 2) * a.g16 * 8 + (tk & 3) + 4 * (tk >> 4)) * a.bv;
 #pragma unroll
-          for (int c = 0; c < 4; ++c) o[c][r] = fmaf(w0[c], cv, o[c][r]);
-#pragma unroll
-          for (int c = 0; c < 4; ++c) o[4 + c][r] = fmaf(w1[c], cv, o[4 + c][r]);
+          for (int r = 0; r < 4; ++r) {
+            cv[k][r] = 0.f;
+            if (r >= nr) break;
+            const int p = cib[r] + tt;
+            const uint32_t lo = s32[p >> 5], hi = s32[(p >> 5) + 1];
+            cv[k][r] = s_vc[__builtin_amdgcn_alignbit(hi, lo, p & 31) & vmask];
+          }
         }
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            if (r >= nr) break;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) o[c][r] = fmaf(w0[k][c], cv[k][r], o[c][r]);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) o[4 + c][r] = fmaf(w1[k][c], cv[k][r], o[4 + c][r]);
+          }
       }
     }
   }
