@@ -181,6 +181,30 @@ def quantize_leg(torch, tq, synth, dev, iters, warm):
                 bytes_per_call=int(in_bytes + out_bytes), dequantize=deq)
 
 
+def sketch_build_leg(torch, tq, W, iters, warm):
+    """Keys with a sketch: the whole key cache of the 128K decode layer
+    (8388608 bf16 vectors, 3-bit + QJL m=128) quantized again into its own
+    code planes (the same codes are rewritten)."""
+    B, Hkv, N, d = W["B"], W["Hkv"], W["N"], W["d"]
+    kf = W["k"].view(B * Hkv, N, d)
+    call = lambda: tq.tq_quantize_kv(W["kcb"], None, kf, None, W["kc"], None)
+    for _ in range(warm):
+        call()
+    torch.cuda.synchronize()
+    tq.tq_profile_enable(True)
+    ms, per = timed_iters(torch, call, iters)
+    tq.tq_profile_enable(False)
+    kms, kspread = kernel_spread(tq, tq.TQ_KERNEL_QUANTIZE)
+    n = B * Hkv * N
+    bpv = 2 * d + 3 * d // 8 + 128 // 8 + 4 + 4      # bf16 in; idx, signs, scale, rnorm out
+    return dict(workload="keys of the decode-128k layer with a sketch: 8388608 bf16 vectors, d=128, "
+                         "3-bit + QJL m=128, row layout",
+                ms_per_call=round(ms, 4), call_ms_spread=spread(per), kernel_ms=round(kms, 4),
+                kernel_ms_spread=kspread, bytes_per_vector=bpv,
+                kernel_GB_per_s=round(bpv * n / (kms * 1e-3) / 1e9, 1),
+                frac_hbm=round(bpv * n / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
+
+
 def dequantize_leg(torch, tq, kcb, vcb, kc, vc, n_seq, n_tok, iters, warm):
     """tq_dequantize of the quantize layer's K (row) and V (tile32) codes back
     to bf16: reads 68 B of codes and writes 256 B per vector."""
@@ -775,6 +799,8 @@ def main():
     if not args.no_quantize:
         print("[bench] quantize leg", file=sys.stderr, flush=True)
         res["quantize"] = quantize_leg(torch, tq, synth, dev, iters=args.steps, warm=args.warmup)
+        res["quantize"]["sketched_keys"] = sketch_build_leg(torch, tq, W, iters=max(5, args.steps // 5),
+                                                            warm=2)
     if not args.no_sweep:
         print("[bench] bit-width sweep leg", file=sys.stderr, flush=True)
         res["bit_sweep"] = bit_sweep_leg(torch, tq, synth, dev, iters=args.steps, warm=args.warmup)

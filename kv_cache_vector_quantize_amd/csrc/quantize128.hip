@@ -90,6 +90,17 @@ __device__ inline uint32_t bf16_bits(float v) {   // round to nearest even
 
 __device__ inline float bf16_float(uint32_t h) { return __uint_as_float(h << 16); }
 
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+
+// {hi(y0) | hi(y1) << 16, lo(y0) | lo(y1) << 16}: hi the bf16 rounding (to
+// nearest even) of y, lo that of y - hi, two values per conversion
+__device__ inline uint2 split_pair(float y0, float y1) {
+  const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){y0, y1}, bf16x2));
+  const float r0 = y0 - __uint_as_float(h << 16);
+  const float r1 = y1 - __uint_as_float(h & 0xFFFF0000u);
+  return make_uint2(h, __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){r0, r1}, bf16x2)));
+}
+
 // A thread's share of a tile: row tid/8, 16 consecutive input elements from
 // coordinate 16*(tid%8), as raw 16-byte words (zero for rows outside the
 // written range).
@@ -126,10 +137,9 @@ __device__ inline void share_load(Share<DT>& sh, const void* x, int64_t e0, bool
   }
 }
 
-template <int DT, bool T32, int NP, bool QJ>
-// two-part variants without a sketch keep three workgroups per CU
-__global__ void __launch_bounds__(256, (NP == 2 && !QJ) ? 3 : 1) k_q128(Q128Args a) {
-  static_assert(!(QJ && T32), "sketch signs are written in the row layout only");
+template <int DT, bool T32, int NP>
+// two-part variants keep three workgroups per CU
+__global__ void __launch_bounds__(256, NP == 2 ? 3 : 1) k_q128(Q128Args a) {
   constexpr bool XLO = DT != TQ_BF16, XLO2 = DT == TQ_F32;
   __shared__ __align__(16) uint16_t xh[TILE][XS];
   __shared__ __align__(16) uint16_t xl[XLO ? TILE : 1][XS];
@@ -140,11 +150,6 @@ __global__ void __launch_bounds__(256, (NP == 2 && !QJ) ? 3 : 1) k_q128(Q128Args
   __shared__ float s_n[TILE], s_ig[TILE];
   __shared__ float s_c2[4][TILE];
   __shared__ int s_valid[TILE];
-  // residual r of the tile in bf16 hi / lo (B operands of the sketch) and
-  // per-wave partial |r|^2
-  __shared__ __align__(16) uint16_t rh[QJ ? TILE : 1][QJ ? XS : 8];
-  __shared__ __align__(16) uint16_t rl[QJ ? TILE : 1][QJ ? XS : 8];
-  __shared__ float s_r2[QJ ? 4 : 1][TILE];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int c32 = lane & 31, hl = lane >> 5;
@@ -155,16 +160,12 @@ __global__ void __launch_bounds__(256, (NP == 2 && !QJ) ? 3 : 1) k_q128(Q128Args
   for (int i = tid; i < a.ncell; i += 256) s_tab[i] = a.qtab[i];
   for (int i = tid; i < L; i += 256) s_cent[i] = a.cent[i];
 
-  bf16x8 ph[8], pl[8], pm[NP == 3 ? 8 : 1], sh[QJ ? 8 : 1], sl[QJ ? 8 : 1];
+  bf16x8 ph[8], pl[8], pm[NP == 3 ? 8 : 1];
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
     ph[s] = __builtin_bit_cast(bf16x8, a.rop[((wave * 8 + s) * 3 + 0) * 64 + lane]);
     pl[s] = __builtin_bit_cast(bf16x8, a.rop[((wave * 8 + s) * 3 + 1) * 64 + lane]);
     if constexpr (NP == 3) pm[s] = __builtin_bit_cast(bf16x8, a.rop[((wave * 8 + s) * 3 + 2) * 64 + lane]);
-    if constexpr (QJ) {
-      sh[s] = __builtin_bit_cast(bf16x8, a.sop[((wave * 8 + s) * 3 + 0) * 64 + lane]);
-      sl[s] = __builtin_bit_cast(bf16x8, a.sop[((wave * 8 + s) * 3 + 1) * 64 + lane]);
-    }
   }
   const bool vec_ok = (reinterpret_cast<uintptr_t>(a.x) & 15) == 0;
   const bool row16 = (a.idx_pitch & 15) == 0;
@@ -410,72 +411,8 @@ __global__ void __launch_bounds__(256, (NP == 2 && !QJ) ? 3 : 1) k_q128(Q128Args
       }
       a.scale[pos0 + c32] = sc;
     }
-    // (g) keys with a sketch: residual r = y - (scale / |x|) c[idx] of this
-    // lane's 16 coordinates (element v: coordinate 32w + 8(v/4) + 4hl + v%4
-    // of vector c32; scale / |x| is 1, or 1 / |c[idx]| with norm correction,
-    // also for x = 0, where y = 0), staged for the sketch product
-    float qn = 0.f;
-    bool qvalid = false;
-    if constexpr (QJ) {
-      qn = s_n[c32];
-      qvalid = s_valid[c32] != 0;
-      float ratio = 1.f;           // scale / |x|
-      if (need_c) {
-        const float nh = sqrtf(((s_c2[0][c32] + s_c2[1][c32]) + s_c2[2][c32]) + s_c2[3][c32]);
-        ratio = 1.f / nh;
-      }
-      const float inv_n = qn > 0.f ? 1.f / qn : 0.f;
-      float r2 = 0.f;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        uint32_t hw[2], lw[2];
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          uint32_t hh[2], ll[2];
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const int v = 4 * g + 2 * h2 + e;
-            const float r = acc[v] * inv_n - ratio * s_cent[iv[v]];
-            r2 = fmaf(r, r, r2);
-            hh[e] = bf16_bits(r);
-            ll[e] = bf16_bits(r - bf16_float(hh[e]));
-          }
-          hw[h2] = hh[0] | (hh[1] << 16);
-          lw[h2] = ll[0] | (ll[1] << 16);
-        }
-        const int col = 32 * wave + 8 * g + 4 * hl;
-        *reinterpret_cast<uint2*>(&rh[c32][col]) = make_uint2(hw[0], hw[1]);
-        *reinterpret_cast<uint2*>(&rl[c32][col]) = make_uint2(lw[0], lw[1]);
-      }
-      r2 += __shfl_xor(r2, 32);
-      if (hl == 0) s_r2[wave][c32] = r2;
-    }
+    // the next tile's staging overwrites what this tile's waves still read
     __syncthreads();
-    if constexpr (QJ) {
-      // (h) u = S r: sketch rows 32w .. 32w + 31 of the 32 vectors, then the
-      // sign bits (u >= 0) of those rows as word w of each sign row, and the
-      // residual norm |x| |r|
-      f32x16 au = {};
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const bf16x8 xrh = *reinterpret_cast<const bf16x8*>(&rh[c32][16 * s + 8 * hl]);
-        const bf16x8 xrl = *reinterpret_cast<const bf16x8*>(&rl[c32][16 * s + 8 * hl]);
-        au = mfma32(sh[s], xrl, au);
-        au = mfma32(sl[s], xrh, au);
-        au = mfma32(sh[s], xrh, au);
-      }
-      uint32_t bits = 0u;
-#pragma unroll
-      for (int v = 0; v < 16; ++v)
-        bits |= (au[v] >= 0.f ? 1u : 0u) << (8 * (v >> 2) + 4 * hl + (v & 3));
-      bits |= (uint32_t)__shfl_xor((int)bits, 32);
-      const int rows = a.m - 32 * wave;     // sketch rows of this word
-      if (rows < 32) bits &= rows > 0 ? (1u << rows) - 1u : 0u;
-      if (hl == 0 && qvalid && rows > 0)
-        a.sign[(((pos0 + c32) * a.sign_pitch) >> 2) + wave] = bits;
-      if (wave == 0 && hl == 0 && qvalid)
-        a.rnorm[pos0 + c32] = qn * sqrtf(((s_r2[0][c32] + s_r2[1][c32]) + s_r2[2][c32]) + s_r2[3][c32]);
-    }
 
     if constexpr (T32) {
       // (f) the assembled tile32 block: 512*b bytes = 128*b words
@@ -505,15 +442,334 @@ __global__ void __launch_bounds__(256, (NP == 2 && !QJ) ? 3 : 1) k_q128(Q128Args
   }
 }
 
-template <int DT, bool T32, int NP, bool QJ>
-int resident_grid(int n_tiles) {
-  // workgroups that stay resident at once (per device, computed once)
+// Keys with a sketch: eight waves per workgroup.  Waves 0-3 ("rotation
+// waves") do what k_q128 does for a row-layout tile with three parts of Pi
+// (stage, rotate, index, pack, scale) and write the residual r of their 32
+// coordinates to LDS as bf16 hi + lo; waves 4-7 ("sketch waves") form
+// u = S r for the tile before, its sign words and rnorm.  The two halves of
+// a tile's work thus overlap on every SIMD (one wave of each per SIMD), and a
+// wave holds either the three parts of its slice of Pi or the two of its
+// slice of S, in the same registers.  Residuals and per-vector data of a
+// tile are double-buffered between the halves; one pass of the loop takes a
+// new tile into the rotation waves and the previous one into the sketch waves.
+template <int DT>
+__global__ void __launch_bounds__(512, 1) k_q128sk(Q128Args a) {
+  constexpr bool XLO = DT != TQ_BF16, XLO2 = DT == TQ_F32;
+  __shared__ __align__(16) uint16_t xh[TILE][XS];
+  __shared__ __align__(16) uint16_t xl[XLO ? TILE : 1][XS];
+  __shared__ __align__(16) uint16_t xl2[XLO2 ? TILE : 1][XS];
+  __shared__ int2 s_tab[kQ128Cells];
+  __shared__ float s_cent[256];
+  __shared__ float s_ig[TILE];
+  __shared__ float s_c2[4][TILE];
+  __shared__ float s_n[2][TILE];
+  __shared__ int s_valid[2][TILE];
+  __shared__ __align__(16) uint16_t rh[2][TILE][XS];
+  __shared__ __align__(16) uint16_t rl[2][TILE][XS];
+  __shared__ float s_r2[2][4][TILE];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const bool rot = wave < 4;
+  const int wq = wave & 3;                     // slice of Pi (rotation) or of S (sketch)
+  const int c32 = lane & 31, hl = lane >> 5;
+  const int b = a.bits, L = 1 << b;
+  const bool need_c = a.nc != 0;
+  const float G = a.G;
+  const int cmax = a.ncell - 1;
+  for (int i = tid; i < a.ncell; i += 512) s_tab[i] = a.qtab[i];
+  for (int i = tid; i < L; i += 512) s_cent[i] = a.cent[i];
+
+  // rotation waves: op[8 p + s] = part p (hi, lo, lo2) of Pi at k-step s;
+  // sketch waves: op[8 p + s] = part p (hi, lo) of S
+  bf16x8 op[24];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+      if (p == 2 && !rot) break;
+      const uint4* src = rot ? a.rop : a.sop;
+      op[8 * p + s] = __builtin_bit_cast(bf16x8, src[((wq * 8 + s) * 3 + p) * 64 + lane]);
+    }
+  }
+  const bool vec_ok = (reinterpret_cast<uintptr_t>(a.x) & 15) == 0;
+  const bool row16 = (a.idx_pitch & 15) == 0;
+  const int r8 = (tid & 255) >> 3, c0 = 16 * (tid & 7);
+
+  auto where = [&](int tile, int& seq, int64_t& blk) {
+    seq = tile / a.tiles_per_seq;
+    blk = a.first_block + (tile - seq * a.tiles_per_seq);
+  };
+  auto row0 = [&](int tile) {                  // code row of the tile's row 0
+    int seq;
+    int64_t blk, oseq, oblk;
+    where(tile, seq, blk);
+    page_block(a.pm, seq, blk, oseq, oblk);
+    return oseq * a.seq_stride + oblk * TILE;
+  };
+  auto fetch = [&](Share<DT>& sh, int tile) {
+    int seq;
+    int64_t blk;
+    where(tile, seq, blk);
+    const int64_t p = blk * TILE + r8;
+    const bool valid = p >= a.tok_off && p < a.tok_off + a.n_tok;
+    share_load<DT>(sh, a.x, ((int64_t)seq * a.n_tok + (p - a.tok_off)) * 128 + c0, valid, vec_ok);
+  };
+
+  const int G1 = (int)gridDim.x, G2 = 2 * G1;
+  // one pass: the rotation waves take `tile` (if < n_tiles) into buffer q,
+  // the sketch waves take tile - G1 (if this is not the first pass) from
+  // buffer q ^ 1
+  auto step = [&](Share<DT>& cur, const int tile, const int q) __attribute__((always_inline)) {
+    const bool have = tile < a.n_tiles;
+    const bool prev = tile - G1 >= (int)blockIdx.x;
+    // (a) stage this thread's share; |x| in fp32, reduced over the row's 8 threads
+    if (rot && have) {
+      int seq;
+      int64_t blk;
+      where(tile, seq, blk);
+      const int64_t abs0 = blk * TILE;
+      float s2 = 0.f;
+      if constexpr (DT == TQ_BF16) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const uint32_t w4[4] = {cur.w[c].x, cur.w[c].y, cur.w[c].z, cur.w[c].w};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const bf16x2 v = __builtin_bit_cast(bf16x2, w4[k]);
+            s2 = __builtin_amdgcn_fdot2_f32_bf16(v, v, s2, false);
+          }
+          *reinterpret_cast<uint4*>(&xh[r8][c0 + 8 * c]) = cur.w[c];
+        }
+      } else {
+        float xv[16];
+        if constexpr (DT == TQ_F32) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            xv[4 * c] = __uint_as_float(cur.w[c].x); xv[4 * c + 1] = __uint_as_float(cur.w[c].y);
+            xv[4 * c + 2] = __uint_as_float(cur.w[c].z); xv[4 * c + 3] = __uint_as_float(cur.w[c].w);
+          }
+        } else {
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const uint32_t w4[4] = {cur.w[c].x, cur.w[c].y, cur.w[c].z, cur.w[c].w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              xv[8 * c + 2 * k] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w4[k] & 0xFFFFu));
+              xv[8 * c + 2 * k + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w4[k] >> 16));
+            }
+          }
+        }
+        uint32_t hw[8], lw[8], mw[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          s2 = fmaf(xv[2 * k], xv[2 * k], s2);
+          s2 = fmaf(xv[2 * k + 1], xv[2 * k + 1], s2);
+          const uint32_t h0 = bf16_bits(xv[2 * k]), h1 = bf16_bits(xv[2 * k + 1]);
+          hw[k] = h0 | (h1 << 16);
+          const float e0 = xv[2 * k] - bf16_float(h0), e1 = xv[2 * k + 1] - bf16_float(h1);
+          const uint32_t l0 = bf16_bits(e0), l1 = bf16_bits(e1);
+          lw[k] = l0 | (l1 << 16);
+          if constexpr (XLO2)
+            mw[k] = bf16_bits(e0 - bf16_float(l0)) | (bf16_bits(e1 - bf16_float(l1)) << 16);
+        }
+        *reinterpret_cast<uint4*>(&xh[r8][c0]) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        *reinterpret_cast<uint4*>(&xh[r8][c0 + 8]) = make_uint4(hw[4], hw[5], hw[6], hw[7]);
+        *reinterpret_cast<uint4*>(&xl[r8][c0]) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+        *reinterpret_cast<uint4*>(&xl[r8][c0 + 8]) = make_uint4(lw[4], lw[5], lw[6], lw[7]);
+        if constexpr (XLO2) {
+          *reinterpret_cast<uint4*>(&xl2[r8][c0]) = make_uint4(mw[0], mw[1], mw[2], mw[3]);
+          *reinterpret_cast<uint4*>(&xl2[r8][c0 + 8]) = make_uint4(mw[4], mw[5], mw[6], mw[7]);
+        }
+      }
+      s2 += __shfl_xor(s2, 1);
+      s2 += __shfl_xor(s2, 2);
+      s2 += __shfl_xor(s2, 4);
+      if ((tid & 7) == 0) {
+        const int64_t p = abs0 + r8;
+        const float n = sqrtf(s2);
+        s_n[q][r8] = n;
+        s_ig[r8] = n > 0.f ? G / n : 0.f;
+        s_valid[q][r8] = (p >= a.tok_off && p < a.tok_off + a.n_tok) ? 1 : 0;
+      }
+    }
+    __syncthreads();
+
+    int iv[16];
+    f32x16 acc = {};
+    if (rot && have) {
+      // the share of the tile after next goes in flight while this one is computed
+      if (tile + G2 < a.n_tiles) fetch(cur, tile + G2);
+      // (b) rotation: D[coordinate][vector], coordinates 32 wq .. 32 wq + 31;
+      // the hi.hi products and the smaller ones go to two accumulators so
+      // the two chains interleave
+      f32x16 acs = {};
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const bf16x8 xo = *reinterpret_cast<const bf16x8*>(&xh[c32][16 * s + 8 * hl]);
+        if constexpr (XLO) {
+          const bf16x8 xq = *reinterpret_cast<const bf16x8*>(&xl[c32][16 * s + 8 * hl]);
+          if constexpr (XLO2) {
+            const bf16x8 xr = *reinterpret_cast<const bf16x8*>(&xl2[c32][16 * s + 8 * hl]);
+            acs = mfma32(op[s], xr, acs);
+          }
+          acs = mfma32(op[8 + s], xq, acs);
+          acs = mfma32(op[s], xq, acs);
+        }
+        acs = mfma32(op[16 + s], xo, acs);
+        acs = mfma32(op[8 + s], xo, acs);
+        acc = mfma32(op[s], xo, acc);
+      }
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[v] += acs[v];
+      // (c) indices: element v is coordinate 32 wq + 8(v/4) + 4hl + v%4 of vector c32
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float key = fmaf(acc[v], s_ig[c32], G);
+        const int c = min((int)key, cmax);
+        const int2 e = s_tab[c];
+        iv[v] = e.x + (key >= __int_as_float(e.y) ? 1 : 0);
+      }
+      if (need_c) {
+        float c2 = 0.f;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float cv = s_cent[iv[v]];
+          c2 = fmaf(cv, cv, c2);
+        }
+        c2 += __shfl_xor(c2, 32);
+        if (hl == 0) s_c2[wq][c32] = c2;
+      }
+    } else if (!rot && prev) {
+      // (h) u = S r of the tile before: sketch rows 32 wq .. 32 wq + 31 of
+      // its 32 vectors, their sign bits as word wq of each sign row, and
+      // rnorm = |x| |r| (sketch wave 0)
+      const int pq = q ^ 1;
+      f32x16 au = {}, aus = {};
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const bf16x8 xrh = *reinterpret_cast<const bf16x8*>(&rh[pq][c32][16 * s + 8 * hl]);
+        const bf16x8 xrl = *reinterpret_cast<const bf16x8*>(&rl[pq][c32][16 * s + 8 * hl]);
+        aus = mfma32(op[s], xrl, aus);
+        aus = mfma32(op[8 + s], xrh, aus);
+        au = mfma32(op[s], xrh, au);
+      }
+#pragma unroll
+      for (int v = 0; v < 16; ++v) au[v] += aus[v];
+      uint32_t bits = 0u;
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        bits |= (au[v] >= 0.f ? 1u : 0u) << (8 * (v >> 2) + 4 * hl + (v & 3));
+      bits |= (uint32_t)__shfl_xor((int)bits, 32);
+      const int rows = a.m - 32 * wq;          // sketch rows of this word
+      if (rows < 32) bits &= rows > 0 ? (1u << rows) - 1u : 0u;
+      const bool qvalid = s_valid[pq][c32] != 0;
+      const int64_t pos0 = row0(tile - G1);
+      if (hl == 0 && qvalid && rows > 0) a.sign[(((pos0 + c32) * a.sign_pitch) >> 2) + wq] = bits;
+      if (wq == 0 && hl == 0 && qvalid)
+        a.rnorm[pos0 + c32] =
+            s_n[pq][c32] * sqrtf(((s_r2[pq][0][c32] + s_r2[pq][1][c32]) + s_r2[pq][2][c32]) + s_r2[pq][3][c32]);
+    }
+    if (need_c) __syncthreads();
+
+    if (rot && have) {
+      const int64_t pos0 = row0(tile);
+      // (d) pack and store the indices: this wave's 32 coordinates are b
+      // words [wq b, wq b + b) of the row; group g of 4 coordinates (4b bits)
+      // lives in half g % 2, slot g / 2
+      uint32_t gv[4], go[4];
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        uint32_t g = 0u;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) g |= (uint32_t)iv[4 * qq + r] << (r * b);
+        gv[qq] = g;
+      }
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) go[qq] = (uint32_t)__shfl_xor((int)gv[qq], 32);
+      const bool valid = s_valid[q][c32] != 0;
+      if (hl == 0 && valid) {
+        uint32_t* dst = reinterpret_cast<uint32_t*>(a.idx + (pos0 + c32) * a.idx_pitch) + wq * b;
+        if (b == 4 && row16) {
+          *reinterpret_cast<uint4*>(dst) = make_uint4(gv[0] | (go[0] << 16), gv[1] | (go[1] << 16),
+                                                      gv[2] | (go[2] << 16), gv[3] | (go[3] << 16));
+        } else {
+          uint64_t buf = 0;
+          int nb = 0, wo = 0;
+#pragma unroll
+          for (int g = 0; g < 8; ++g) {
+            const uint32_t val = (g & 1) ? go[g >> 1] : gv[g >> 1];
+            buf |= (uint64_t)val << nb;
+            nb += 4 * b;
+            if (nb >= 32) {
+              dst[wo++] = (uint32_t)buf;
+              buf >>= 32;
+              nb -= 32;
+            }
+          }
+        }
+      }
+      // (e) scale |x| (or |x| / |y^|) and (g) the residual
+      // r = y - (scale / |x|) c[idx] of this lane's 16 coordinates
+      const float qn = s_n[q][c32];
+      float ratio = 1.f;                       // scale / |x|
+      if (need_c) {
+        const float nh = sqrtf(((s_c2[0][c32] + s_c2[1][c32]) + s_c2[2][c32]) + s_c2[3][c32]);
+        ratio = 1.f / nh;
+        if (wq == 0 && hl == 0 && valid) a.scale[pos0 + c32] = qn / nh;
+      } else if (wq == 0 && hl == 0 && valid) {
+        a.scale[pos0 + c32] = qn;
+      }
+      const float inv_n = qn > 0.f ? 1.f / qn : 0.f;
+      float r2 = 0.f;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        uint2 hl2[2];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int v = 4 * g + 2 * h2;
+          const float r0 = fmaf(acc[v], inv_n, -ratio * s_cent[iv[v]]);
+          const float r1 = fmaf(acc[v + 1], inv_n, -ratio * s_cent[iv[v + 1]]);
+          r2 = fmaf(r0, r0, r2);
+          r2 = fmaf(r1, r1, r2);
+          hl2[h2] = split_pair(r0, r1);
+        }
+        const int col = 32 * wq + 8 * g + 4 * hl;
+        *reinterpret_cast<uint2*>(&rh[q][c32][col]) = make_uint2(hl2[0].x, hl2[1].x);
+        *reinterpret_cast<uint2*>(&rl[q][c32][col]) = make_uint2(hl2[0].y, hl2[1].y);
+      }
+      r2 += __shfl_xor(r2, 32);
+      if (hl == 0) s_r2[q][wq][c32] = r2;
+    }
+    __syncthreads();
+  };
+
+  Share<DT> s0, s1;
+  int tile = blockIdx.x;
+  if (rot) {
+    if (tile < a.n_tiles) fetch(s0, tile);
+    if (tile + G1 < a.n_tiles) fetch(s1, tile + G1);
+  }
+  __syncthreads();
+  for (;;) {
+    step(s0, tile, 0);
+    if (tile >= a.n_tiles) break;
+    tile += G1;
+    step(s1, tile, 1);
+    if (tile >= a.n_tiles) break;
+    tile += G1;
+  }
+}
+
+template <void (*K)(Q128Args)>
+int resident_grid(int threads, int n_tiles) {
+  // workgroups of kernel K that stay resident at once (per device, computed once)
   static int per_device[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
   if (per_device[dev] == 0) {
     int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_q128<DT, T32, NP, QJ>, 256, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, K, threads, 0) != hipSuccess ||
         per_cu < 1)
       per_cu = 2;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
@@ -523,9 +779,9 @@ int resident_grid(int n_tiles) {
   return n_tiles < per_device[dev] ? n_tiles : per_device[dev];
 }
 
-template <int DT, bool T32, int NP, bool QJ = false>
+template <int DT, bool T32, int NP>
 void launch_np(const Q128Args& a, hipStream_t st) {
-  hipLaunchKernelGGL((k_q128<DT, T32, NP, QJ>), dim3(resident_grid<DT, T32, NP, QJ>(a.n_tiles)), dim3(256), 0,
+  hipLaunchKernelGGL((k_q128<DT, T32, NP>), dim3(resident_grid<k_q128<DT, T32, NP>>(256, a.n_tiles)), dim3(256), 0,
                      st, a);
 }
 
@@ -534,8 +790,8 @@ hipError_t launch_dt(const Q128Args& a, bool t32, hipStream_t st) {
   const bool two = a.bits <= 4;      // two parts of Pi suffice up to 4 bits
   if (a.m > 0) {
     // keys with a sketch: three parts of Pi (fp32-level y, so that |r| keeps
-    // its relative accuracy), row layout
-    launch_np<DT, false, 3, true>(a, st);
+    // its relative accuracy), row layout, rotation and sketch waves
+    hipLaunchKernelGGL((k_q128sk<DT>), dim3(resident_grid<k_q128sk<DT>>(512, a.n_tiles)), dim3(512), 0, st, a);
   } else if (t32) {
     if (two) launch_np<DT, true, 2>(a, st);
     else launch_np<DT, true, 3>(a, st);

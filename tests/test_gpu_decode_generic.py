@@ -134,12 +134,12 @@ def test_generic_decode_end_to_end(dev):
     vc2 = tq.Codes(vcb, B * Hkv, S, TQ_LAYOUT_TILE32)
     tq.tq_quantize_kv(kcb, vcb, k.view(B * Hkv, N, d), v.view(B * Hkv, N, d), kc2, vc2)
     lg2, out2, tau = _decode(dev, kcb, vcb, q, kc2, vc2, N)
-    lg_ref, out_ref = O.attn_decode(okc, ovc, U.to_f64(q), kd, vd, tau)
-    e_out = float(np.max(np.abs(out2 - out_ref)))
-    e_lg = float(np.max(np.abs(lg2 - lg_ref)) / np.max(np.abs(lg_ref)))
-    print("end-to-end out max-abs", e_out, "logit rel", e_lg)
-    # GPU and oracle codes may differ only inside the boundary zones
-    assert e_out <= U.OUT_ATOL
+    flat = lambda c: {n: (a.reshape(-1, *a.shape[2:]) if a is not None else None)
+                      for n, a in U.read_codes(c, N).items()}
+    st_k, _ = U.compare_quant(okc, U.to_f64(k).reshape(-1, d), flat(kc2), "K")
+    st_v, _ = U.compare_quant(ovc, U.to_f64(v).reshape(-1, d), flat(vc2), "V")
+    _, out_ref = O.attn_decode(okc, ovc, U.to_f64(q), kd, vd, tau)
+    print(U.check_end_to_end(okc, ovc, U.to_f64(q), kc2, vc2, N, B, Hkv, tau, lg2, out2, out_ref, [st_k, st_v]))
 
 
 def test_generic_decode_long_context_sampled(dev):

@@ -347,11 +347,9 @@ def test_decode_tiny_configuration(dev):
     st_k, _ = U.compare_quant(okc, k.astype(np.float64), {n: a[0] if a is not None else None for n, a in U.read_codes(kc2, N).items()}, "K")
     st_v, _ = U.compare_quant(ovc, v.astype(np.float64), {n: a[0] if a is not None else None for n, a in U.read_codes(vc2, N).items()}, "V")
     lg_ref, out_ref = O.attn_decode(okc, ovc, q[None].astype(np.float64), kd, vd, tau)
-    e2e = float(np.max(np.abs(out2 - out_ref)))
-    e2e_l = float(np.max(np.abs(lg2 - lg_ref)) / np.max(np.abs(lg_ref)))
-    print(st, "end-to-end out max-abs", e2e, "logit rel", e2e_l,
-          "K zone mismatches", st_k["idx_mismatch"], "V", st_v["idx_mismatch"])
-    assert e2e <= U.OUT_ATOL
+    e2e = U.check_end_to_end(okc, ovc, q[None].astype(np.float64), kc2, vc2, N, 1, 1, tau, lg2, out2, out_ref,
+                             [st_k, st_v])
+    print(st, "end to end", e2e, "K zone mismatches", st_k["idx_mismatch"], "V", st_v["idx_mismatch"])
 
 
 @pytest.mark.parametrize("B,Hkv,Hq,N,lens", [

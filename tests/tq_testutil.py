@@ -223,3 +223,27 @@ def check_decode(ocb_k, ocb_v, q64, kc, vc, sm_scale, logits_gpu, out_gpu, n_val
     worst_o = float(max(diffs)) if diffs else 0.0
     assert worst_o <= OUT_ATOL, f"{name}: output max-abs err {worst_o}"
     return dict(logit_rel=worst_l, out_abs=worst_o)
+
+
+def check_end_to_end(ocb_k, ocb_v, q64, k_codes, v_codes, n_tok, B, Hkv, sm_scale, lg_gpu, out_gpu,
+                     out_ref, code_stats):
+    """GPU quantize -> GPU decode.  The zone rule lets a GPU code differ from
+    the oracle's where the oracle's y lies within 1e-5 of a boundary (or u of
+    0), and such a token's logit moves with its code, by more than the decode
+    bars allow.  So: with no differing code the chain must meet the output bar
+    against the oracle's quantize -> decode (``out_ref``); in every case the
+    GPU decode must equal the oracle's decode of the GPU's own codes (read
+    back) to the decode bars.  ``code_stats``: compare_quant stats of the K
+    and V codes."""
+    gk, gv = read_codes(k_codes, n_tok), read_codes(v_codes, n_tok)
+    shape = lambda a: a.reshape(B, Hkv, n_tok, *a.shape[2:])
+    kd = dict(idx=shape(gk["idx"]), scale=shape(gk["scale"]))
+    if gk["sign"] is not None:
+        kd.update(sign=shape(gk["sign"]), rnorm=shape(gk["rnorm"]))
+    vd = dict(idx=shape(gv["idx"]), scale=shape(gv["scale"]))
+    st = check_decode(ocb_k, ocb_v, q64, kd, vd, sm_scale, lg_gpu, out_gpu, name="end-to-end codes")
+    differ = sum(int(c["idx_mismatch"]) + int(c.get("sign_mismatch_total", 0)) for c in code_stats)
+    e2e = float(np.max(np.abs(out_gpu - out_ref)))
+    if differ == 0:
+        assert e2e <= OUT_ATOL, f"end-to-end output max-abs {e2e} with identical codes"
+    return dict(st, e2e_out=e2e, differing_codes=differ)
