@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <string>
@@ -120,8 +121,30 @@ bool build_q128_cells(const std::vector<float>& t, std::vector<uint32_t>& out, f
   return true;
 }
 
+// Argument trace: with TQ_LOG set to anything but "0" in the environment
+// (read once), every hot-path entry point prints its arguments, and every
+// failure its status and message, as one line on stderr.
+bool log_on() {
+  static const bool on = [] {
+    const char* e = std::getenv("TQ_LOG");
+    return e != nullptr && e[0] != '\0' && !(e[0] == '0' && e[1] == '\0');
+  }();
+  return on;
+}
+
+__attribute__((format(printf, 1, 2))) void log_call(const char* fmt, ...) {
+  if (!log_on()) return;
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  std::fprintf(stderr, "[tq] %s\n", buf);
+}
+
 tq_status fail(tq_status s, const std::string& msg) {
   g_err = msg;
+  if (log_on()) std::fprintf(stderr, "[tq] -> status %d: %s\n", (int)s, msg.c_str());
   return s;
 }
 
@@ -283,6 +306,10 @@ extern "C" {
 const char* tq_last_error(void) { return g_err.c_str(); }
 
 tq_status tq_codebook_build(const tq_params* params, tq_codebook** out) {
+  if (params)
+    log_call("tq_codebook_build d=%d bits=%d qjl_m=%d nc=%d rot_seed=%llu qjl_seed=%llu", params->d,
+             params->bits, params->qjl_m, params->norm_correction, (unsigned long long)params->rot_seed,
+             (unsigned long long)params->qjl_seed);
   // set while a codebook is under construction, so that an exception thrown
   // part-way (a host allocation) releases it and the tables already uploaded
   tq_codebook* pending = nullptr;
@@ -530,6 +557,9 @@ tq_status tq_codebook_values(const tq_params* params, double* centroids, double*
 }
 
 tq_status tq_polar_codebook_build(const tq_polar_params* params, tq_codebook** out) {
+  if (params)
+    log_call("tq_polar_codebook_build d=%d b1=%d br=%d qjl_m=%d", params->d, params->bits_first,
+             params->bits_rest, params->qjl_m);
   tq_codebook* pending = nullptr;
   auto release_pending = [&]() {
     if (pending) {
@@ -770,6 +800,9 @@ tq_status tq_quantize_kv(const tq_codebook* kcb, const tq_codebook* vcb, const v
                          const void* v, int32_t dt_in, int64_t n_seq, int64_t n_tok,
                          int64_t tok_offset, const tq_codes* k_out, const tq_codes* v_out,
                          void* stream) {
+  log_call("tq_quantize_kv kcb=%p vcb=%p k=%p v=%p dt=%d n_seq=%lld n_tok=%lld tok_offset=%lld stream=%p",
+           (const void*)kcb, (const void*)vcb, k, v, dt_in, (long long)n_seq, (long long)n_tok,
+           (long long)tok_offset, stream);
   try {
     if (!dtype_ok(dt_in)) return fail(TQ_ERR_INVALID, "bad dtype");
     const tq_dtype dt = static_cast<tq_dtype>(dt_in);
@@ -789,6 +822,9 @@ tq_status tq_quantize_kv_paged(const tq_codebook* kcb, const tq_codebook* vcb, c
                                int64_t tok_offset, const int32_t* block_table, int64_t max_pages,
                                int32_t page_tokens, const tq_codes* k_pool, const tq_codes* v_pool,
                                void* stream) {
+  log_call("tq_quantize_kv_paged dt=%d B=%lld Hkv=%lld n_tok=%lld tok_offset=%lld max_pages=%lld page_tokens=%d",
+           dt_in, (long long)B, (long long)Hkv, (long long)n_tok, (long long)tok_offset, (long long)max_pages,
+           page_tokens);
   try {
     if (!dtype_ok(dt_in)) return fail(TQ_ERR_INVALID, "bad dtype");
     const tq_dtype dt = static_cast<tq_dtype>(dt_in);
@@ -879,6 +915,10 @@ tq_status tq_attn_decode(const tq_codebook* kcb, const tq_codebook* vcb, const v
                          const tq_codes* v, const int32_t* seq_lens, int64_t n_ctx,
                          float sm_scale, float* out, float* logits, void* workspace,
                          size_t ws_bytes, void* stream) {
+  log_call("tq_attn_decode qdt=%d B=%lld Hq=%lld Hkv=%lld n_ctx=%lld sm_scale=%g seq_lens=%p out=%p logits=%p "
+           "workspace=%p ws_bytes=%zu stream=%p",
+           qdt, (long long)B, (long long)Hq, (long long)Hkv, (long long)n_ctx, (double)sm_scale,
+           (const void*)seq_lens, (void*)out, (void*)logits, workspace, ws_bytes, stream);
   try {
     return decode_impl(kcb, vcb, q, qdt, B, Hq, Hkv, k, v, seq_lens, n_ctx, sm_scale, out, logits,
                        workspace, ws_bytes, stream, n_ctx, 0, PageMap{});
@@ -891,6 +931,8 @@ tq_status tq_attn_decode_noalloc(const tq_codebook* kcb, const tq_codebook* vcb,
                                  int32_t qdt, int64_t B, int64_t Hq, int64_t Hkv, const tq_codes* k,
                                  const tq_codes* v, const int32_t* seq_lens, int64_t n_ctx,
                                  float sm_scale, float* out, float* logits, void* stream) {
+  log_call("tq_attn_decode_noalloc qdt=%d B=%lld Hq=%lld Hkv=%lld n_ctx=%lld sm_scale=%g", qdt, (long long)B,
+           (long long)Hq, (long long)Hkv, (long long)n_ctx, (double)sm_scale);
   try {
     if (B < 0 || Hq < 0 || Hkv <= 0 || n_ctx < 0 || Hq % Hkv)
       return fail(TQ_ERR_INVALID, "need B, n_ctx >= 0, Hkv > 0, Hq a multiple of Hkv");
@@ -932,6 +974,10 @@ tq_status tq_attn_decode_paged(const tq_codebook* kcb, const tq_codebook* vcb, c
                                const tq_codes* v_pool, const int32_t* block_table, int64_t max_pages,
                                int32_t page_tokens, const int32_t* seq_lens, int64_t n_ctx, float sm_scale,
                                float* out, float* logits, void* workspace, size_t ws_bytes, void* stream) {
+  log_call("tq_attn_decode_paged qdt=%d B=%lld Hq=%lld Hkv=%lld max_pages=%lld page_tokens=%d n_ctx=%lld "
+           "sm_scale=%g ws_bytes=%zu",
+           qdt, (long long)B, (long long)Hq, (long long)Hkv, (long long)max_pages, page_tokens, (long long)n_ctx,
+           (double)sm_scale, ws_bytes);
   try {
     if (B < 0 || Hq < 0 || Hkv <= 0 || n_ctx < 0)
       return fail(TQ_ERR_INVALID, "need B, Hq, n_ctx >= 0 and Hkv > 0");
@@ -985,6 +1031,8 @@ tq_status tq_ip_topk_exact_scan(int32_t always) {
 tq_status tq_ip_topk(const tq_codebook* cb, const float* queries, int64_t nq,
                      const tq_codes* db, int64_t n_db, int32_t k, int64_t* out_idx,
                      float* out_score, void* workspace, size_t ws_bytes, void* stream) {
+  log_call("tq_ip_topk cb=%p queries=%p nq=%lld n_db=%lld k=%d workspace=%p ws_bytes=%zu stream=%p",
+           (const void*)cb, (const void*)queries, (long long)nq, (long long)n_db, k, workspace, ws_bytes, stream);
   try {
     if (!cb) return fail(TQ_ERR_INVALID, "codebook is NULL");
     if (nq < 0 || n_db < 0 || k < 0) return fail(TQ_ERR_INVALID, "need nq, n_db, k >= 0");
@@ -1023,6 +1071,8 @@ tq_status tq_ip_topk(const tq_codebook* cb, const float* queries, int64_t nq,
 tq_status tq_dequantize(const tq_codebook* cb, const tq_codes* codes, int64_t n_seq,
                         int64_t n_tok, int64_t tok_offset, void* out, int32_t out_dt_in,
                         void* stream) {
+  log_call("tq_dequantize cb=%p n_seq=%lld n_tok=%lld tok_offset=%lld out=%p out_dt=%d stream=%p",
+           (const void*)cb, (long long)n_seq, (long long)n_tok, (long long)tok_offset, out, out_dt_in, stream);
   try {
     if (!cb) return fail(TQ_ERR_INVALID, "codebook is NULL");
     if (!dtype_ok(out_dt_in)) return fail(TQ_ERR_INVALID, "bad out dtype");

@@ -159,3 +159,27 @@ def test_scan_count_validates_arguments():
     L = tq.lib()
     c = ctypes.c_int64(5)
     assert L.tq_ip_topk_scan_count(None, None, 1, 10, 1, None, ctypes.byref(c)) == _lib.TQ_ERR_INVALID
+
+
+def test_argument_trace_on_stderr():
+    """TQ_LOG=1 makes each hot-path entry point print its arguments, and each
+    failure its status and message, on stderr (host-only calls here)."""
+    import subprocess
+    import sys
+    code = (
+        "import ctypes, kv_cache_vector_quantize_amd as tq\n"
+        "L = tq.lib()\n"
+        "L.tq_quantize_kv(None, None, None, None, 1, 2, 3, 4, None, None, None)\n"
+        "L.tq_ip_topk(None, None, 5, None, 6, 7, None, None, None, 0, None)\n"
+    )
+    env = dict(os.environ, TQ_LOG="1")
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120,
+                       cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    assert r.returncode == 0, r.stderr
+    assert "[tq] tq_quantize_kv" in r.stderr and "n_seq=2 n_tok=3 tok_offset=4" in r.stderr
+    assert "[tq] tq_ip_topk" in r.stderr and "nq=5 n_db=6 k=7" in r.stderr
+    assert "[tq] -> status 1: codebook is NULL" in r.stderr
+    env["TQ_LOG"] = "0"
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120,
+                       cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    assert "[tq]" not in r.stderr
