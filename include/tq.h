@@ -407,7 +407,11 @@ tq_status tq_profile_durations(int32_t kernel, double* ms, int64_t capacity, int
  * against.  Errors: TQ_ERR_INVALID, TQ_ERR_HIP. */
 tq_status tq_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream);
 
-/* Message of the last failing call on this thread ("" if none). */
+/* Message of the last failing call on this thread ("" if none).  With the
+ * environment variable TQ_LOG set (to anything but "0") when the library is
+ * first used, every hot-path call (codebook builds, quantize, decode, top-k,
+ * dequantize) prints its arguments, and every failure its status and this
+ * message, as one "[tq] ..." line on stderr. */
 const char* tq_last_error(void);
 
 #ifdef __cplusplus
