@@ -1,52 +1,78 @@
-// Decode attention from packed codes for the shapes the d = 128 MFMA kernels
-// of decode.hip do not take: any head dimension 3 <= d <= 256, scalar key and
+// Decode attention from packed codes for the shapes the d = 128 kernels of
+// decode.hip do not take: any head dimension 3 <= d <= 256, scalar key and
 // value codes of 1..8 bits, sketches of up to 256 rows.
 //
 // Page "什么是TurboQuant？…" (a2a-mcp.org blog), "如何实现 TurboQuant" item 1
 // and "专业提示": the query is rotated once and the attention dot products are
 // taken from the stored indices; "第二阶段" supplies the QJL correction.  The
 // computation, the split of the context and the partial records are those of
-// decode.hip:
+// decode.hip, and so is the use of v_mfma_f32_16x16x32_bf16 with bf16 hi/lo
+// operands; only the operand layouts are general:
 //  1. k_gprologue, one workgroup per row (batch, KV head, <= 8 query heads):
-//     q~ = Pi_K q' and t = sqrt(pi/2)/m S_K Pi_K q' in fp32 with
-//     q' = sm_scale log2(e) q, stored coordinate-major ([i][8 queries]) so one
-//     scalar load brings a coordinate's value for all 8 queries, and sum_j t_j.
+//     q~ = Pi_K q' and t = sqrt(pi/2)/m S_K Pi_K q' in fp32 (q' = sm_scale
+//     log2(e) q), written as B operands: the query operand of MFMA u holds,
+//     in lane group g4, coordinates g4 dp/4 + 4u .. + 3 of the 8 queries (hi
+//     parts in columns 0-7, lo parts in 8-15, each value twice, facing the hi
+//     and lo of a centroid); the sketch operand of MFMA c holds sketch rows
+//     32c + 8 g4 .. + 7 (hi / lo columns).
 //  2. k_gsplit<BK>, 8 waves per workgroup, each wave a chunk of the row in
-//     64-token tiles.  Logits with lane = token: each key index goes through
-//     an LDS centroid table and meets the 8 query values, read from LDS by
-//     all lanes at one address (8 FMAs per coordinate); each sign bit takes
-//     one FMA per query against t, and the sketch term is
-//     rnorm (2 sum_{sign=1} t - sum t).  Online
-//     softmax in base 2.  Weights x values with lane = coordinate (up to 4 per
-//     lane): each 32-token tile32 block is staged in the wave's LDS slot and
-//     every (token, coordinate) index is read from it.  The waves' partials
-//     merge in LDS and each workgroup writes one record per query slot.
+//     32-token tiles of two 16-token blocks.  Key logits: a lane holds the
+//     key bits of its token's coordinates g4 dp/4 .. (g4 + 1) dp/4 - 1 in
+//     registers (BK is a template parameter, so the fields of MFMA u sit at
+//     constant offsets), each field indexes an LDS table of bf16 hi | lo;
+//     the sketch term: each byte of sign bits indexes a table of eight bf16
+//     +-1.  Online softmax in base 2.  Weights x values: the tile32 block is
+//     staged in the wave's LDS slot; a lane cuts the eight value fields of
+//     its coordinate and token slots from two 32-bit windows.  The waves'
+//     partials merge in LDS; one record per workgroup and query slot.
 //  3. k_gcombine, one workgroup per (row, query slot): log-sum-exp merge of
 //     the workgroup records in a fixed order, then out = Pi_V^T o~ / l.
-// Every FMA is fp32; the operands are the fp32 centroids and the fp32 q~, t.
 #include "tq_internal.hpp"
 
 namespace tq {
 namespace {
 
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kGWaves = 8;                    // waves per split workgroup
 constexpr int kGMaxD = 256;                   // largest head dimension
 constexpr int kGMaxM = 256;                   // largest sketch
+constexpr int kGNu = kGMaxD / 16;             // query MFMAs per block at most
+constexpr int kGNs = kGMaxM / 32;             // sketch MFMAs per block at most
 constexpr int kGTab = 256;                    // centroid table entries (8 bits)
 constexpr int kGBlkMax = 64 * 16 * 8;         // tile32 block bytes at d = 256, 8 bits
-constexpr int kGSlot = kGBlkMax + 16;         // a wave's value staging slot (+1 dword of slack)
-constexpr int kGW = 64 * 8 * 4;               // a wave's weights: [64 tokens][8 queries] fp32
-constexpr int kGWork = kGWaves * (kGW + kGSlot);          // staging of all waves
+constexpr int kGSlot = kGBlkMax + 16;         // a wave's value slot (+ slack for the last window)
 constexpr int kGMerge = kGWaves * 8 * kGMaxD * 4;         // partials of all waves
-constexpr int kGLds = kGWork > kGMerge ? kGWork : kGMerge;
+constexpr int kGLds = kGWaves * kGSlot > kGMerge ? kGWaves * kGSlot : kGMerge;
 constexpr int kGMaxWg = 1024;                 // workgroup records per row
+// operand dwords per row: query [dp/16][64 lanes][4], then sketch [8][64][4]
+constexpr int kGQop = kGNu * 256, kGTop = kGNs * 256;
+__host__ __device__ inline int64_t grow_dwords(int dp) { return (int64_t)(dp / 16) * 256 + kGTop; }
 
-// Floats per row of the prologue's output: q~ [dp][8], t [256][8], sum t [8].
-__host__ __device__ inline int64_t grow_floats(int dp) { return (int64_t)(dp + kGMaxM) * 8 + 8; }
+__device__ inline uint32_t bf16_rne(float v) {
+  uint32_t u = __float_as_uint(v);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ inline float dpp_ror8(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
+}
+
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+__device__ inline f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
 
 // ------------------------------------------------------------ 1. prologue
 
@@ -58,17 +84,18 @@ struct GPArgs {
   float qscale;            // sm_scale * log2(e)
   const float* rotT;       // [dp][dp], rotT[k][i] = Pi_K[i][k], zero-padded
   const float* sprotT;     // [dp][mp], sqrt(pi/2)/m (S_K Pi_K)[j][k] at [k][j], or null
-  float* gq;               // [rows][grow_floats(dp)]
+  uint32_t* qop;           // [rows][grow_dwords(dp)]
 };
 
 __global__ void __launch_bounds__(256) k_gprologue(GPArgs a) {
   __shared__ float qs[8][kGMaxD];
-  __shared__ float red[4][8];
+  __shared__ float qt[8][kGMaxD + 1];
+  __shared__ float tt[8][kGMaxM + 1];
   const int row = blockIdx.x;
   const int qg = row % a.qgroups;
   const int bh = row / a.qgroups;
   const int b = bh / a.Hkv, h = bh % a.Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x;
   for (int e = tid; e < 8 * kGMaxD; e += 256) {
     const int c = e / kGMaxD, k = e % kGMaxD;
     const int jq = qg * 8 + c;
@@ -83,7 +110,6 @@ __global__ void __launch_bounds__(256) k_gprologue(GPArgs a) {
     qs[c][k] = v;
   }
   __syncthreads();
-  float* dst = a.gq + (int64_t)row * grow_floats(a.dp);
   if (tid < a.dp) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int k = 0; k < a.d; ++k) {
@@ -91,43 +117,56 @@ __global__ void __launch_bounds__(256) k_gprologue(GPArgs a) {
 #pragma unroll
       for (int c = 0; c < 8; ++c) acc[c] = fmaf(r, qs[c][k], acc[c]);
     }
-    const bool in = tid < a.d;
-    *reinterpret_cast<f32x4*>(dst + 8 * tid) =
-        in ? f32x4{acc[0], acc[1], acc[2], acc[3]} : f32x4{0.f, 0.f, 0.f, 0.f};
-    *reinterpret_cast<f32x4*>(dst + 8 * tid + 4) =
-        in ? f32x4{acc[4], acc[5], acc[6], acc[7]} : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 8; ++c) qt[c][tid] = tid < a.d ? acc[c] : 0.f;
   }
-  float tv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  if (a.m > 0 && tid < a.mp) {
-    for (int k = 0; k < a.d; ++k) {
-      const float r = a.sprotT[(int64_t)k * a.mp + tid];
+  if (tid < a.mp) {
+    float tv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (a.m > 0) {
+      for (int k = 0; k < a.d; ++k) {
+        const float r = a.sprotT[(int64_t)k * a.mp + tid];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) tv[c] = fmaf(r, qs[c][k], tv[c]);
+        for (int c = 0; c < 8; ++c) tv[c] = fmaf(r, qs[c][k], tv[c]);
+      }
     }
-    if (tid >= a.m) {
 #pragma unroll
-      for (int c = 0; c < 8; ++c) tv[c] = 0.f;
-    }
-    float* tr = dst + (int64_t)(a.dp + tid) * 8;
-    *reinterpret_cast<f32x4*>(tr) = f32x4{tv[0], tv[1], tv[2], tv[3]};
-    *reinterpret_cast<f32x4*>(tr + 4) = f32x4{tv[4], tv[5], tv[6], tv[7]};
-  }
-  // sum_j t_j per query slot
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    float s = tv[c];
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) s += __shfl_xor(s, o);
-    if (lane == 0) red[wv][c] = s;
+    for (int c = 0; c < 8; ++c) tt[c][tid] = tid < a.m ? tv[c] : 0.f;
   }
   __syncthreads();
-  if (tid < 8) dst[(int64_t)(a.dp + kGMaxM) * 8 + tid] = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+  uint32_t* dst = a.qop + (int64_t)row * grow_dwords(a.dp);
+  // query operand: MFMA u, lane (col, g4), dword p = coordinate
+  // g4 dp/4 + 4u + p, the hi (col < 8) or lo (col >= 8) part twice
+  const int nu = a.dp / 16, q4 = a.dp / 4;
+  for (int e = tid; e < nu * 256; e += 256) {
+    const int u = e >> 8, lane = (e >> 2) & 63, p = e & 3;
+    const int col = lane & 15, g4 = lane >> 4;
+    const float x = qt[col & 7][g4 * q4 + 4 * u + p];
+    const uint32_t hi = bf16_rne(x);
+    const uint32_t v = col < 8 ? hi : bf16_rne(x - __uint_as_float(hi << 16));
+    dst[e] = v | (v << 16);
+  }
+  // sketch operand: MFMA c, lane (col, g4), dword p = sketch rows
+  // 32c + 8 g4 + 2p and + 1, hi or lo parts
+  const int ns = a.mp / 32;
+  for (int e = tid; e < ns * 256; e += 256) {
+    const int c = e >> 8, lane = (e >> 2) & 63, p = e & 3;
+    const int col = lane & 15, g4 = lane >> 4;
+    const int j = 32 * c + 8 * g4 + 2 * p;
+    uint32_t v[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const float x = tt[col & 7][j + k];
+      const uint32_t hi = bf16_rne(x);
+      v[k] = col < 8 ? hi : bf16_rne(x - __uint_as_float(hi << 16));
+    }
+    dst[nu * 256 + e] = v[0] | (v[1] << 16);
+  }
 }
 
 // ------------------------------------------------------------ 2. split
 
 struct GSArgs {
-  const float* gq;
+  const uint32_t* qop;
   const char* kidx;
   const char* ksign;       // null without a sketch
   const float* kscale;
@@ -153,46 +192,48 @@ struct GSArgs {
   int psh;
 };
 
-// Bits [off, off + BK) of the little-endian words wd (compile-time offsets).
-template <int BK>
-__device__ inline uint32_t kfield(const uint32_t (&wd)[BK], int off) {
+// Bits [off, off + w) of the little-endian words wd (compile-time offsets).
+template <int NW>
+__device__ inline uint32_t kfield(const uint32_t (&wd)[NW], int off, int w) {
   const int i = off >> 5, s = off & 31;
   uint32_t v;
-  if (s + BK <= 32 || i + 1 >= BK) v = wd[i] >> s;
+  if (s + w <= 32 || i + 1 >= NW) v = wd[i] >> s;
   else v = __builtin_amdgcn_alignbit(wd[i + 1], wd[i], s);
-  return v & ((1u << BK) - 1u);
-}
-
-__device__ inline float wave_max(float v) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  return v & ((1u << w) - 1u);
 }
 
 template <int BK>
-__global__ void __launch_bounds__(64 * kGWaves) k_gsplit(GSArgs a) {
-  __shared__ __align__(16) float s_kc[kGTab];
-  __shared__ __align__(16) float s_vc[kGTab];
-  // the row's q~ [dp][8], t [mp][8] and sum t [8]
-  __shared__ __align__(16) float s_q[(kGMaxD + kGMaxM) * 8 + 8];
+__global__ void __launch_bounds__(64 * kGWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) k_gsplit(GSArgs a) {
+  constexpr int KW = 2 * BK;                  // key dwords of a lane's coordinate slice (dp/4 <= 64 fields)
+  __shared__ __align__(16) uint32_t s_kt[kGTab];     // bf16 hi | lo << 16 of key centroid e
+  __shared__ __align__(16) uint32_t s_vt[kGTab];     // the same for value centroids
+  __shared__ __align__(16) u32x4 s_sgn[256];         // byte -> eight bf16 +-1
+  __shared__ __align__(16) uint32_t s_op[kGQop + kGTop];   // query operands, sketch operands at kGQop
   __shared__ __align__(16) char s_work[kGLds];
+  __shared__ __align__(16) float s_sc[kGWaves][96];  // per wave: kscale[32], rnorm[32], vscale[32]
   __shared__ float s_M[kGWaves][8], s_l[kGWaves][8];
   const int tid = threadIdx.x;
   for (int i = tid; i < kGTab; i += 64 * kGWaves) {
-    s_kc[i] = i < a.lk ? a.kcent[i] : 0.f;
-    s_vc[i] = i < a.lv ? a.vcent[i] : 0.f;
+    const float ck = i < a.lk ? a.kcent[i] : 0.f, cv = i < a.lv ? a.vcent[i] : 0.f;
+    const uint32_t hk = bf16_rne(ck), hv = bf16_rne(cv);
+    s_kt[i] = hk | (bf16_rne(ck - __uint_as_float(hk << 16)) << 16);
+    s_vt[i] = hv | (bf16_rne(cv - __uint_as_float(hv << 16)) << 16);
+    uint32_t w[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+      w[p] = (((i >> (2 * p)) & 1) ? 0x3F80u : 0xBF80u) | ((((i >> (2 * p + 1)) & 1) ? 0x3F80u : 0xBF80u) << 16);
+    s_sgn[i] = u32x4{w[0], w[1], w[2], w[3]};
   }
   {
-    // q~ and t of the row; every lane of a wave later reads one coordinate's
-    // 8 values at one address (a broadcast)
-    const float* src = a.gq + (int64_t)blockIdx.y * grow_floats(a.dp);
-    const int nqt = (a.dp + 32 * ((a.m + 31) >> 5)) * 8;
-    for (int i = tid; i < nqt; i += 64 * kGWaves) s_q[i] = src[i];
-    if (tid < 8) s_q[(kGMaxD + kGMaxM) * 8 + tid] = src[(int64_t)(a.dp + kGMaxM) * 8 + tid];
+    const int nu = a.dp / 16, ns = (a.m + 31) / 32;
+    const uint32_t* src = a.qop + (int64_t)blockIdx.y * grow_dwords(a.dp);
+    for (int i = tid; i < nu * 256; i += 64 * kGWaves) s_op[i] = src[i];
+    for (int i = tid; i < ns * 256; i += 64 * kGWaves) s_op[kGQop + i] = src[nu * 256 + i];
   }
   __syncthreads();
 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int c16 = lane & 15, g4 = lane >> 4;
   const int part = blockIdx.x * kGWaves + wave;
   const int row = blockIdx.y;
   const int qg = row % a.qgroups;
@@ -210,28 +251,23 @@ __global__ void __launch_bounds__(64 * kGWaves) k_gsplit(GSArgs a) {
   if (t_end > n_valid) t_end = n_valid;
   if (part >= a.n_parts) t_end = t_begin;
 
-  const float* trow = s_q + a.dp * 8;
-  const float* tsum = s_q + (kGMaxD + kGMaxM) * 8;
-  const int g32 = a.dp >> 5;
-  const int ns = (a.m + 31) >> 5;
-  const int nq = a.g - qg * 8 < 8 ? a.g - qg * 8 : 8;
+  const int nu = a.dp / 16, ns = (a.m + 31) / 32, ndb = a.dp / 16;
+  // this lane's key slice: coordinates g4 dp/4 .. + dp/4 - 1 start at bit
+  // sb of the row; nkw dwords from dword kd0 hold it, shifted down by ksh
+  const int sb = g4 * (a.dp / 4) * BK;
+  const int kd0 = sb >> 5, ksh = sb & 31;
+  const int nkw = (ksh + (a.dp / 4) * BK + 31) >> 5;
   const char* kbase = a.kidx + seq * a.k_stride * a.k_pitch;
   const char* sbase = ns ? a.ksign + seq * a.k_stride * a.ks_pitch : nullptr;
   const int64_t vblk0 = seq * (a.v_stride >> 5);
-  float* s_w = reinterpret_cast<float*>(s_work + wave * (kGW + kGSlot));     // [64][8]
-  char* s_v = s_work + wave * (kGW + kGSlot) + kGW;                          // one tile32 block
+  char* s_v = s_work + wave * kGSlot;
+  const uint32_t* s_v32 = reinterpret_cast<const uint32_t*>(s_v);
+  float* stage = &s_sc[wave][0];
   const uint32_t vmask = (1u << a.bv) - 1u;
-  // value coordinates of this lane: i = lane + 64 r, bit offset of index i of
-  // token 0 in a block (coordinates past the block's 16 g16 are clamped and
-  // their sums discarded)
-  const int nr = (a.dp + 63) >> 6;
-  int cib[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    int i = lane + 64 * r;
-    if (i >= 16 * a.g16) i = 0;
-    cib[r] = (((i & 15) * a.g16 + (i >> 4)) * 8) * a.bv;
-  }
+  // value fields of coordinate 16 db + c16: token slots e = 0..7 (tokens
+  // 4 g4 + e % 4 + 16 (e / 4)) are 8 consecutive fields from bit
+  // vp0 + 8 bv db of the block
+  const int vp0 = (16 * g4 + c16) * a.g16 * 8 * a.bv;
 
   auto phys = [&](int64_t pos) -> int64_t {
     if (!paged) return pos;
@@ -242,162 +278,151 @@ __global__ void __launch_bounds__(64 * kGWaves) k_gsplit(GSArgs a) {
     return (pg << a.psh) | (pos & ((1LL << a.psh) - 1));
   };
 
-  float M[8], l[8], o[8][4];
+  float M = -INFINITY, l = 0.f;
+  f32x4 acc_o[kGNu];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    M[c] = -INFINITY;
-    l[c] = 0.f;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) o[c][r] = 0.f;
-  }
+  for (int db = 0; db < kGNu; ++db) acc_o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int64_t t0 = t_begin; t0 < t_end; t0 += 64) {
-    const int64_t pos = t0 + lane;
-    const bool valid = pos < t_end;
-    const int64_t pp = phys(valid ? pos : t0);
-    // ---- logits (lane = token)
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += 32) {
+    const int lim = t_end - t0 < 32 ? (int)(t_end - t0) : 32;
+    // the tile's 32 positions lie in one page (pages hold >= 32 positions)
+    const int64_t pt0 = phys(t0);
+    // ---- raw loads: key slices and sign words of tokens c16 and 16 + c16
+    uint32_t kw[2][KW + 1], sw[2][kGNs];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      const int tk = 16 * blk + c16 < lim ? 16 * blk + c16 : lim - 1;
+      const uint32_t* kr = reinterpret_cast<const uint32_t*>(kbase + (pt0 + tk) * a.k_pitch) + kd0;
+#pragma unroll
+      for (int i = 0; i <= KW; ++i) kw[blk][i] = i < nkw ? kr[i] : 0u;
+      const uint32_t* sr = ns ? reinterpret_cast<const uint32_t*>(sbase + (pt0 + tk) * a.ks_pitch) : nullptr;
+#pragma unroll
+      for (int c = 0; c < kGNs; ++c) sw[blk][c] = c < ns ? sr[c] : 0u;
+    }
     {
-      const uint32_t* kr = reinterpret_cast<const uint32_t*>(kbase + pp * a.k_pitch);
-      uint32_t kw[BK];
-#pragma unroll
-      for (int j = 0; j < BK; ++j) kw[j] = kr[j];
-      for (int gi = 0; gi < g32; ++gi) {
-        uint32_t kn[BK];
-        const int gn = gi + 1 < g32 ? gi + 1 : gi;
-#pragma unroll
-        for (int j = 0; j < BK; ++j) kn[j] = kr[gn * BK + j];
-        const float* qv = s_q + gi * 256;
-        // four coordinates per batch: all their LDS reads are issued before
-        // the FMAs that consume them
-#pragma unroll
-        for (int u0 = 0; u0 < 32; u0 += 4) {
-          float cv[4];
-          f32x4 q0[4], q1[4];
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            cv[k] = s_kc[kfield<BK>(kw, (u0 + k) * BK)];
-            q0[k] = *reinterpret_cast<const f32x4*>(qv + (u0 + k) * 8);
-            q1[k] = *reinterpret_cast<const f32x4*>(qv + (u0 + k) * 8 + 4);
-          }
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-#pragma unroll
-            for (int c = 0; c < 4; ++c) acc[c] = fmaf(cv[k], q0[k][c], acc[c]);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) acc[4 + c] = fmaf(cv[k], q1[k][c], acc[4 + c]);
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < BK; ++j) kw[j] = kn[j];
-      }
+      const int tk = (lane & 31) < lim ? (lane & 31) : lim - 1;
+      const int64_t r = seq * a.k_stride + pt0 + tk;
+      const float ks = a.kscale[r];
+      const float kr = ns ? a.krnorm[r] : 0.f;
+      const float vs = a.vscale[seq * a.v_stride + pt0 + tk];
+      stage[lane] = lane < 32 ? ks : kr;
+      if (lane < 32) stage[64 + lane] = vs;
     }
-    float accs[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    float rn = 0.f;
-    if (ns) {
-      const uint32_t* sr = reinterpret_cast<const uint32_t*>(sbase + pp * a.ks_pitch);
-      rn = a.krnorm[seq * a.k_stride + pp];
-      for (int gs = 0; gs < ns; ++gs) {
-        const uint32_t sw = sr[gs];
-        const float* tv = trow + gs * 256;
+    {
+      // the tile32 block of the tile into the wave's slot
+      const u32x4* src = reinterpret_cast<const u32x4*>(a.vidx + (vblk0 + (pt0 >> 5)) * (int64_t)a.blk_bytes);
+      u32x4* dv = reinterpret_cast<u32x4*>(s_v);
+      for (int e = lane; e < (a.blk_bytes >> 4); e += 64) dv[e] = src[e];
+    }
+    // key slices shifted to bit 0
 #pragma unroll
-        for (int j0 = 0; j0 < 32; j0 += 4) {
-          f32x4 t0[4], t1[4];
+    for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            t0[k] = *reinterpret_cast<const f32x4*>(tv + (j0 + k) * 8);
-            t1[k] = *reinterpret_cast<const f32x4*>(tv + (j0 + k) * 8 + 4);
-          }
+      for (int i = 0; i < KW; ++i) kw[blk][i] = __builtin_amdgcn_alignbit(kw[blk][i + 1], kw[blk][i], ksh);
+
+    // ---- S^T = K^ Q~^T (16 tokens x 16 columns per block)
+    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    f32x4 accq[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    // (fully unrolled with guards, so every register array index is a constant)
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const float f = (float)((sw >> (j0 + k)) & 1u);
+    for (int u = 0; u < kGNu; ++u) {
+      if (u < nu) {
+        const u32x4 qb = *reinterpret_cast<const u32x4*>(&s_op[(u * 64 + lane) * 4]);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) accs[c] = fmaf(f, t0[k][c], accs[c]);
+        for (int blk = 0; blk < 2; ++blk) {
+          u32x4 ka;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) accs[4 + c] = fmaf(f, t1[k][c], accs[4 + c]);
-          }
+          for (int e = 0; e < 4; ++e) ka[e] = s_kt[kfield<KW + 1>(kw[blk], (4 * u + e) * BK, BK)];
+          acc[blk] = mfma(ka, qb, acc[blk]);
         }
       }
     }
-    const float ks = a.kscale[seq * a.k_stride + pp];
-    const float vs = a.vscale[seq * a.v_stride + pp];
-    float s[8];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      float v = ks * acc[c];
-      if (ns) v = fmaf(rn, fmaf(2.f, accs[c], -tsum[c]), v);
-      s[c] = valid ? v : -INFINITY;
-    }
-    if (a.logits && valid) {
-      float* dst = a.logits + ((int64_t)b * a.Hq + (int64_t)h * a.g + qg * 8) * a.n_ctx + pos;
-      for (int c = 0; c < nq; ++c) dst[(int64_t)c * a.n_ctx] = s[c] * kLn2;
-    }
-    // ---- online softmax (base 2); the tile holds at least one valid token
-    float w[8];
+    for (int c = 0; c < kGNs; ++c) {
+      if (c < ns) {
+        const u32x4 tb = *reinterpret_cast<const u32x4*>(&s_op[kGQop + (c * 64 + lane) * 4]);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const float tm = wave_max(s[c]);
-      if (tm > M[c]) {
-        const float al = __builtin_amdgcn_exp2f(M[c] - tm);   // 0 while M = -inf
-        M[c] = tm;
-        l[c] *= al;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) o[c][r] *= al;
+        for (int blk = 0; blk < 2; ++blk)
+          accq[blk] = mfma(s_sgn[(sw[blk][c] >> (8 * g4)) & 0xFFu], tb, accq[blk]);
       }
-      const float p = valid ? __builtin_amdgcn_exp2f(s[c] - M[c]) : 0.f;
-      l[c] += p;
-      w[c] = valid ? p * vs : 0.f;
     }
-    *reinterpret_cast<f32x4*>(s_w + lane * 8) = f32x4{w[0], w[1], w[2], w[3]};
-    *reinterpret_cast<f32x4*>(s_w + lane * 8 + 4) = f32x4{w[4], w[5], w[6], w[7]};
-    // ---- weights x values (lane = coordinate), one 32-token block at a time
-    for (int bi = 0; bi < 2; ++bi) {
-      const int64_t tb = t0 + 32 * bi;
-      if (tb >= t_end) break;
-      const int64_t blk = vblk0 + (phys(tb) >> 5);
-      const f32x4* src = reinterpret_cast<const f32x4*>(a.vidx + blk * a.blk_bytes);
-      f32x4* sv = reinterpret_cast<f32x4*>(s_v);
-      for (int e = lane; e < (a.blk_bytes >> 4); e += 64) sv[e] = src[e];
-      const uint32_t* s32 = reinterpret_cast<const uint32_t*>(s_v);
-      const int ntb = t_end - tb < 32 ? (int)(t_end - tb) : 32;
-      // two tokens per batch (weights of a token past ntb are 0)
-      for (int t = 0; t < ntb; t += 2) {
-        f32x4 w0[2], w1[2];
-        float cv[2][4];
+    // logits (base 2): the scales per column, then hi + lo columns
+    float lg[2][4];
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          const int tk = t + k;
-          w0[k] = *reinterpret_cast<const f32x4*>(s_w + (32 * bi + tk) * 8);
-          w1[k] = *reinterpret_cast<const f32x4*>(s_w + (32 * bi + tk) * 8 + 4);
-          const int tt = (16 * ((tk & 15) >> 2) * a.g16 * 8 + (tk & 3) + 4 * (tk >> 4)) * a.bv;
+    for (int blk = 0; blk < 2; ++blk) {
+      const f32x4 ks = *reinterpret_cast<const f32x4*>(stage + 16 * blk + 4 * g4);
+      const f32x4 kr = *reinterpret_cast<const f32x4*>(stage + 32 + 16 * blk + 4 * g4);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            cv[k][r] = 0.f;
-            if (r >= nr) break;
-            const int p = cib[r] + tt;
-            const uint32_t lo = s32[p >> 5], hi = s32[(p >> 5) + 1];
-            cv[k][r] = s_vc[__builtin_amdgcn_alignbit(hi, lo, p & 31) & vmask];
-          }
+      for (int r = 0; r < 4; ++r) {
+        float u = ks[r] * acc[blk][r];
+        if (ns) u = fmaf(kr[r], accq[blk][r], u);
+        u += dpp_ror8(u);
+        lg[blk][r] = 16 * blk + 4 * g4 + r < lim ? u : -INFINITY;
+      }
+    }
+    if (a.logits && c16 < 8 && qg * 8 + c16 < a.g) {
+      float* dst = a.logits + ((int64_t)b * a.Hq + (int64_t)h * a.g + qg * 8 + c16) * a.n_ctx + t0;
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int tt = 16 * blk + 4 * g4 + r;
+          if (tt < lim) dst[tt] = lg[blk][r] * kLn2;
         }
+    }
+    // ---- online softmax (base 2); a column's maximum over the tile's tokens
+    float tm = fmaxf(fmaxf(fmaxf(lg[0][0], lg[0][1]), fmaxf(lg[0][2], lg[0][3])),
+                     fmaxf(fmaxf(lg[1][0], lg[1][1]), fmaxf(lg[1][2], lg[1][3])));
+    tm = fmaxf(tm, __shfl_xor(tm, 16));
+    tm = fmaxf(tm, __shfl_xor(tm, 32));
+    if (tm > M) {                       // the tile holds a valid token, so tm > -inf
+      const float al = __builtin_amdgcn_exp2f(M - tm);    // 0 while M = -inf
+      l *= al;
 #pragma unroll
-        for (int k = 0; k < 2; ++k)
+      for (int db = 0; db < kGNu; ++db) acc_o[db] *= al;
+      M = tm;
+    }
+    const f32x4 vs0 = *reinterpret_cast<const f32x4*>(stage + 64 + 4 * g4);
+    const f32x4 vs1 = *reinterpret_cast<const f32x4*>(stage + 80 + 4 * g4);
+    // weights of the lane's token slots e (tokens 4 g4 + e % 4 + 16 (e / 4)):
+    // hi part in columns < 8, the remainder in the others, each twice
+    u32x4 pop[2];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            if (r >= nr) break;
+    for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-            for (int c = 0; c < 4; ++c) o[c][r] = fmaf(w0[k][c], cv[k][r], o[c][r]);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) o[4 + c][r] = fmaf(w1[k][c], cv[k][r], o[4 + c][r]);
-          }
+      for (int r = 0; r < 4; ++r) {
+        const float p = __builtin_amdgcn_exp2f(lg[blk][r] - M);   // 0 for -inf
+        l += p;
+        const float w = 16 * blk + 4 * g4 + r < lim ? p * (blk == 0 ? vs0[r] : vs1[r]) : 0.f;
+        const uint32_t hi = bf16_rne(w);
+        const uint32_t x = c16 < 8 ? hi : bf16_rne(w - __uint_as_float(hi << 16));
+        pop[blk][r] = x | (x << 16);
       }
+    // ---- O^T += V^ P^T, coordinates 16 db + c16
+#pragma unroll
+    for (int db = 0; db < kGNu; ++db) {
+      if (db >= ndb) continue;
+      const int p0 = vp0 + 8 * a.bv * db, p1 = p0 + 4 * a.bv;
+      const uint32_t w0 = __builtin_amdgcn_alignbit(s_v32[(p0 >> 5) + 1], s_v32[p0 >> 5], p0 & 31);
+      const uint32_t w1 = __builtin_amdgcn_alignbit(s_v32[(p1 >> 5) + 1], s_v32[p1 >> 5], p1 & 31);
+      u32x4 va0, va1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        va0[e] = s_vt[__builtin_amdgcn_ubfe(w0, e * a.bv, a.bv)];
+        va1[e] = s_vt[__builtin_amdgcn_ubfe(w1, e * a.bv, a.bv)];
+      }
+      acc_o[db] = mfma(va0, pop[0], acc_o[db]);
+      acc_o[db] = mfma(va1, pop[1], acc_o[db]);
     }
   }
+  (void)vmask;
 
   // positions of this wave's range that no tile covered (beyond len_b)
   if (a.logits && part < a.n_parts) {
     int64_t to = t_begin + a.chunk;
     if (to > a.n_ctx) to = a.n_ctx;
     const int64_t from = t_end > t_begin ? t_end : t_begin;
+    const int nq = a.g - qg * 8 < 8 ? a.g - qg * 8 : 8;
     for (int c = 0; c < nq; ++c) {
       float* dst = a.logits + ((int64_t)b * a.Hq + (int64_t)h * a.g + qg * 8 + c) * a.n_ctx;
       for (int64_t t = from + lane; t < to; t += 64) dst[t] = -INFINITY;
@@ -405,27 +430,23 @@ __global__ void __launch_bounds__(64 * kGWaves) k_gsplit(GSArgs a) {
   }
 
   // ---- wave partials -> LDS, then one record per workgroup (fixed order)
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    float v = l[c];
-#pragma unroll
-    for (int k = 1; k < 64; k <<= 1) v += __shfl_xor(v, k);
-    l[c] = v;
-  }
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
   __syncthreads();
   float (*s_o)[8][kGMaxD] = reinterpret_cast<float (*)[8][kGMaxD]>(s_work);
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int i = lane + 64 * r;
-    if (i < a.dp) {
+  for (int db = 0; db < kGNu; ++db) {
+    if (db >= ndb) continue;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) s_o[wave][c][i] = i < a.d ? o[c][r] : 0.f;
+    for (int r = 0; r < 4; ++r) {
+      const float o = acc_o[db][r] + dpp_ror8(acc_o[db][r]);
+      const int i = 16 * db + 4 * g4 + r;
+      if (c16 < 8) s_o[wave][c16][i] = i < a.d ? o : 0.f;
     }
   }
   if (lane < 8) {
-#pragma unroll
-    for (int c = 0; c < 8; ++c)
-      if (lane == c) { s_M[wave][c] = M[c]; s_l[wave][c] = l[c]; }
+    s_M[wave][lane] = M;
+    s_l[wave][lane] = l;
   }
   __syncthreads();
   const int64_t rec0 = ((int64_t)row * a.n_wg + blockIdx.x) * 8;
@@ -521,14 +542,14 @@ bool decode_generic_supported(const tq_codebook* kcb, const tq_codebook* vcb) {
          kcb->p.bits <= 8 && vcb->p.bits >= 1 && vcb->p.bits <= 8;
 }
 
-int64_t decode_generic_row_bytes(int d) { return grow_floats(pad32(d)) * 4; }
+int64_t decode_generic_row_bytes(int d) { return grow_dwords(pad32(d)) * 4; }
 
 hipError_t launch_decode_generic(const tq_codebook* kcb, const tq_codebook* vcb, const void* q, tq_dtype qdt,
                                  const DecodePlan& plan, const tq_codes& k, const tq_codes& v,
                                  const int32_t* seq_lens, float sm_scale, float* out, float* logits, void* ws,
                                  hipStream_t stream, const PageMap& pm) {
   char* w = static_cast<char*>(ws);
-  float* gq = reinterpret_cast<float*>(w + plan.off_qop);
+  uint32_t* qop = reinterpret_cast<uint32_t*>(w + plan.off_qop);
   float* part_o = reinterpret_cast<float*>(w + plan.off_part_o);
   float* part_ml = reinterpret_cast<float*>(w + plan.off_part_ml);
   if (plan.rows == 0) return hipSuccess;
@@ -542,14 +563,14 @@ hipError_t launch_decode_generic(const tq_codebook* kcb, const tq_codebook* vcb,
   pa.qscale = sm_scale * kLog2e;
   pa.rotT = kcb->dev.rotT;
   pa.sprotT = kcb->dev.sprotT;
-  pa.gq = gq;
+  pa.qop = qop;
   hipLaunchKernelGGL(k_gprologue, dim3((unsigned)plan.rows), dim3(256), 0, stream, pa);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
   if (plan.n_parts > 0) {
     GSArgs sa{};
-    sa.gq = gq;
+    sa.qop = qop;
     sa.kidx = static_cast<const char*>(k.idx);
     sa.ksign = static_cast<const char*>(k.sign);
     sa.kscale = k.scale;
