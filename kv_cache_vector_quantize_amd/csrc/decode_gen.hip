@@ -202,22 +202,38 @@ __device__ inline uint32_t kfield(const uint32_t (&wd)[NW], int off, int w) {
   return v & ((1u << w) - 1u);
 }
 
-template <int BK>
+// BIG: d > 128 (up to 16 query MFMAs and coordinate blocks); otherwise d <= 128
+// (up to 8), which leaves the registers to load each tile one tile ahead.
+template <int BK, bool BIG>
 __global__ void __launch_bounds__(64 * kGWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) k_gsplit(GSArgs a) {
-  constexpr int KW = 2 * BK;                  // key dwords of a lane's coordinate slice (dp/4 <= 64 fields)
+  constexpr int NU = BIG ? kGNu : kGNu / 2;   // query MFMAs per block / coordinate blocks, at most
+  constexpr int KW = NU * BK / 8;             // key dwords of a lane's coordinate slice (dp/4 fields)
   __shared__ __align__(16) uint32_t s_kt[kGTab];     // bf16 hi | lo << 16 of key centroid e
   __shared__ __align__(16) uint32_t s_vt[kGTab];     // the same for value centroids
+  // codes of <= 4 bits: entry a | b << bits holds the table entries of a and b
+  // (two coordinates of a key, two token slots of a value)
+  __shared__ __align__(16) uint2 s_kp[BK <= 4 ? 256 : 1];
+  __shared__ __align__(16) uint2 s_vp[256];
   __shared__ __align__(16) u32x4 s_sgn[256];         // byte -> eight bf16 +-1
   __shared__ __align__(16) uint32_t s_op[kGQop + kGTop];   // query operands, sketch operands at kGQop
   __shared__ __align__(16) char s_work[kGLds];
   __shared__ __align__(16) float s_sc[kGWaves][96];  // per wave: kscale[32], rnorm[32], vscale[32]
   __shared__ float s_M[kGWaves][8], s_l[kGWaves][8];
   const int tid = threadIdx.x;
+  auto hilo = [](const float* cent, int n, int e) {   // bf16 hi | lo << 16 of centroid e (0 past n)
+    const float c = e < n ? cent[e] : 0.f;
+    const uint32_t hi = bf16_rne(c);
+    return hi | (bf16_rne(c - __uint_as_float(hi << 16)) << 16);
+  };
   for (int i = tid; i < kGTab; i += 64 * kGWaves) {
-    const float ck = i < a.lk ? a.kcent[i] : 0.f, cv = i < a.lv ? a.vcent[i] : 0.f;
-    const uint32_t hk = bf16_rne(ck), hv = bf16_rne(cv);
-    s_kt[i] = hk | (bf16_rne(ck - __uint_as_float(hk << 16)) << 16);
-    s_vt[i] = hv | (bf16_rne(cv - __uint_as_float(hv << 16)) << 16);
+    s_kt[i] = hilo(a.kcent, a.lk, i);
+    s_vt[i] = hilo(a.vcent, a.lv, i);
+    if constexpr (BK <= 4) {
+      if (i < (1 << (2 * BK)))
+        s_kp[i] = make_uint2(hilo(a.kcent, a.lk, i & ((1 << BK) - 1)), hilo(a.kcent, a.lk, i >> BK));
+    }
+    if (a.bv <= 4 && i < (1 << (2 * a.bv)))
+      s_vp[i] = make_uint2(hilo(a.vcent, a.lv, i & ((1 << a.bv) - 1)), hilo(a.vcent, a.lv, i >> a.bv));
     uint32_t w[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p)
@@ -279,60 +295,97 @@ __global__ void __launch_bounds__(64 * kGWaves) __attribute__((amdgpu_waves_per_
   };
 
   float M = -INFINITY, l = 0.f;
-  f32x4 acc_o[kGNu];
+  f32x4 acc_o[NU];
 #pragma unroll
-  for (int db = 0; db < kGNu; ++db) acc_o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int db = 0; db < NU; ++db) acc_o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int64_t t0 = t_begin; t0 < t_end; t0 += 32) {
+  // Raw data of one tile: key slices and sign words of tokens c16 and
+  // 16 + c16, the token scalars of lane % 32, the lane's share of the tile32
+  // block.  For d <= 128 the next tile's loads go in flight as soon as the
+  // current one's are consumed (past the last tile they repeat it, so the
+  // count of loads in flight is the same on every pass); for d > 128 a tile
+  // is loaded when it is reached.
+  constexpr int VB = NU / 2;                  // 16-byte words of a tile32 block per lane
+  struct Raw {
+    uint32_t kw[2][KW + 1];
+    uint32_t sw[2][kGNs];
+    float ks, kr, vs;
+    u32x4 vb[VB];
+  };
+  const int nvb = a.blk_bytes >> 4;
+  auto load = [&](Raw& R, const int64_t t0) {
     const int lim = t_end - t0 < 32 ? (int)(t_end - t0) : 32;
-    // the tile's 32 positions lie in one page (pages hold >= 32 positions)
-    const int64_t pt0 = phys(t0);
-    // ---- raw loads: key slices and sign words of tokens c16 and 16 + c16
-    uint32_t kw[2][KW + 1], sw[2][kGNs];
+    const int64_t pt0 = phys(t0);       // the tile's 32 positions lie in one page
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       const int tk = 16 * blk + c16 < lim ? 16 * blk + c16 : lim - 1;
       const uint32_t* kr = reinterpret_cast<const uint32_t*>(kbase + (pt0 + tk) * a.k_pitch) + kd0;
 #pragma unroll
-      for (int i = 0; i <= KW; ++i) kw[blk][i] = i < nkw ? kr[i] : 0u;
+      for (int i = 0; i <= KW; ++i) R.kw[blk][i] = i < nkw ? kr[i] : 0u;
       const uint32_t* sr = ns ? reinterpret_cast<const uint32_t*>(sbase + (pt0 + tk) * a.ks_pitch) : nullptr;
 #pragma unroll
-      for (int c = 0; c < kGNs; ++c) sw[blk][c] = c < ns ? sr[c] : 0u;
+      for (int c = 0; c < kGNs; ++c) R.sw[blk][c] = c < ns ? sr[c] : 0u;
     }
+    const int tk = (lane & 31) < lim ? (lane & 31) : lim - 1;
+    const int64_t r = seq * a.k_stride + pt0 + tk;
+    R.ks = a.kscale[r];
+    R.kr = ns ? a.krnorm[r] : 0.f;
+    R.vs = a.vscale[seq * a.v_stride + pt0 + tk];
+    const u32x4* src = reinterpret_cast<const u32x4*>(a.vidx + (vblk0 + (pt0 >> 5)) * (int64_t)a.blk_bytes);
+#pragma unroll
+    for (int j = 0; j < VB; ++j) R.vb[j] = lane + 64 * j < nvb ? src[lane + 64 * j] : u32x4{0u, 0u, 0u, 0u};
+  };
+
+  const int64_t ntile = t_end > t_begin ? (t_end - t_begin + 31) / 32 : 0;
+  const int64_t t_last = t_begin + 32 * (ntile - 1);
+  Raw R;
+  if constexpr (!BIG) {
+    if (ntile > 0) load(R, t_begin);
+  }
+  for (int64_t it = 0; it < ntile; ++it) {
+    const int64_t t0 = t_begin + 32 * it;
+    const int lim = t_end - t0 < 32 ? (int)(t_end - t0) : 32;
+    if constexpr (BIG) load(R, t0);
+    // ---- consume the tile: scalars and the value block into the wave's
+    // LDS slots, key slices shifted to bit 0, sign words
+    stage[lane] = lane < 32 ? R.ks : R.kr;
+    if (lane < 32) stage[64 + lane] = R.vs;
     {
-      const int tk = (lane & 31) < lim ? (lane & 31) : lim - 1;
-      const int64_t r = seq * a.k_stride + pt0 + tk;
-      const float ks = a.kscale[r];
-      const float kr = ns ? a.krnorm[r] : 0.f;
-      const float vs = a.vscale[seq * a.v_stride + pt0 + tk];
-      stage[lane] = lane < 32 ? ks : kr;
-      if (lane < 32) stage[64 + lane] = vs;
-    }
-    {
-      // the tile32 block of the tile into the wave's slot
-      const u32x4* src = reinterpret_cast<const u32x4*>(a.vidx + (vblk0 + (pt0 >> 5)) * (int64_t)a.blk_bytes);
       u32x4* dv = reinterpret_cast<u32x4*>(s_v);
-      for (int e = lane; e < (a.blk_bytes >> 4); e += 64) dv[e] = src[e];
+#pragma unroll
+      for (int j = 0; j < VB; ++j)
+        if (lane + 64 * j < nvb) dv[lane + 64 * j] = R.vb[j];
     }
-    // key slices shifted to bit 0
+    uint32_t kw[2][KW + 1], sw[2][kGNs];
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
+    for (int blk = 0; blk < 2; ++blk) {
 #pragma unroll
-      for (int i = 0; i < KW; ++i) kw[blk][i] = __builtin_amdgcn_alignbit(kw[blk][i + 1], kw[blk][i], ksh);
+      for (int i = 0; i < KW; ++i) kw[blk][i] = __builtin_amdgcn_alignbit(R.kw[blk][i + 1], R.kw[blk][i], ksh);
+      kw[blk][KW] = 0u;
+#pragma unroll
+      for (int c = 0; c < kGNs; ++c) sw[blk][c] = R.sw[blk][c];
+    }
+    if constexpr (!BIG) load(R, t0 + 32 < t_last ? t0 + 32 : t_last);
 
     // ---- S^T = K^ Q~^T (16 tokens x 16 columns per block)
     f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
     f32x4 accq[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
     // (fully unrolled with guards, so every register array index is a constant)
 #pragma unroll
-    for (int u = 0; u < kGNu; ++u) {
+    for (int u = 0; u < NU; ++u) {
       if (u < nu) {
         const u32x4 qb = *reinterpret_cast<const u32x4*>(&s_op[(u * 64 + lane) * 4]);
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
           u32x4 ka;
+          if constexpr (BK <= 4) {
+            const uint2 e0 = s_kp[kfield<KW + 1>(kw[blk], 4 * u * BK, 2 * BK)];
+            const uint2 e1 = s_kp[kfield<KW + 1>(kw[blk], (4 * u + 2) * BK, 2 * BK)];
+            ka = u32x4{e0.x, e0.y, e1.x, e1.y};
+          } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) ka[e] = s_kt[kfield<KW + 1>(kw[blk], (4 * u + e) * BK, BK)];
+            for (int e = 0; e < 4; ++e) ka[e] = s_kt[kfield<KW + 1>(kw[blk], (4 * u + e) * BK, BK)];
+          }
           acc[blk] = mfma(ka, qb, acc[blk]);
         }
       }
@@ -379,7 +432,7 @@ __global__ void __launch_bounds__(64 * kGWaves) __attribute__((amdgpu_waves_per_
       const float al = __builtin_amdgcn_exp2f(M - tm);    // 0 while M = -inf
       l *= al;
 #pragma unroll
-      for (int db = 0; db < kGNu; ++db) acc_o[db] *= al;
+      for (int db = 0; db < NU; ++db) acc_o[db] *= al;
       M = tm;
     }
     const f32x4 vs0 = *reinterpret_cast<const f32x4*>(stage + 64 + 4 * g4);
@@ -400,16 +453,26 @@ __global__ void __launch_bounds__(64 * kGWaves) __attribute__((amdgpu_waves_per_
       }
     // ---- O^T += V^ P^T, coordinates 16 db + c16
 #pragma unroll
-    for (int db = 0; db < kGNu; ++db) {
+    for (int db = 0; db < NU; ++db) {
       if (db >= ndb) continue;
-      const int p0 = vp0 + 8 * a.bv * db, p1 = p0 + 4 * a.bv;
+      const int p0 = vp0 + 8 * a.bv * db;
       const uint32_t w0 = __builtin_amdgcn_alignbit(s_v32[(p0 >> 5) + 1], s_v32[p0 >> 5], p0 & 31);
-      const uint32_t w1 = __builtin_amdgcn_alignbit(s_v32[(p1 >> 5) + 1], s_v32[p1 >> 5], p1 & 31);
       u32x4 va0, va1;
+      if (a.bv <= 4) {
+        // all 8 fields in one window, read as pairs
+        const int b2 = 2 * a.bv;
+        const uint2 e0 = s_vp[__builtin_amdgcn_ubfe(w0, 0, b2)], e1 = s_vp[__builtin_amdgcn_ubfe(w0, b2, b2)];
+        const uint2 e2 = s_vp[__builtin_amdgcn_ubfe(w0, 2 * b2, b2)], e3 = s_vp[__builtin_amdgcn_ubfe(w0, 3 * b2, b2)];
+        va0 = u32x4{e0.x, e0.y, e1.x, e1.y};
+        va1 = u32x4{e2.x, e2.y, e3.x, e3.y};
+      } else {
+        const int p1 = p0 + 4 * a.bv;
+        const uint32_t w1 = __builtin_amdgcn_alignbit(s_v32[(p1 >> 5) + 1], s_v32[p1 >> 5], p1 & 31);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        va0[e] = s_vt[__builtin_amdgcn_ubfe(w0, e * a.bv, a.bv)];
-        va1[e] = s_vt[__builtin_amdgcn_ubfe(w1, e * a.bv, a.bv)];
+        for (int e = 0; e < 4; ++e) {
+          va0[e] = s_vt[__builtin_amdgcn_ubfe(w0, e * a.bv, a.bv)];
+          va1[e] = s_vt[__builtin_amdgcn_ubfe(w1, e * a.bv, a.bv)];
+        }
       }
       acc_o[db] = mfma(va0, pop[0], acc_o[db]);
       acc_o[db] = mfma(va1, pop[1], acc_o[db]);
@@ -435,7 +498,7 @@ __global__ void __launch_bounds__(64 * kGWaves) __attribute__((amdgpu_waves_per_
   __syncthreads();
   float (*s_o)[8][kGMaxD] = reinterpret_cast<float (*)[8][kGMaxD]>(s_work);
 #pragma unroll
-  for (int db = 0; db < kGNu; ++db) {
+  for (int db = 0; db < NU; ++db) {
     if (db >= ndb) continue;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -530,7 +593,8 @@ __global__ void __launch_bounds__(256) k_gcombine(GCArgs a) {
 
 template <int BK>
 void launch_gsplit(const GSArgs& a, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL(k_gsplit<BK>, grid, dim3(64 * kGWaves), 0, st, a);
+  if (a.dp > 128) hipLaunchKernelGGL((k_gsplit<BK, true>), grid, dim3(64 * kGWaves), 0, st, a);
+  else hipLaunchKernelGGL((k_gsplit<BK, false>), grid, dim3(64 * kGWaves), 0, st, a);
 }
 
 }  // namespace
