@@ -455,15 +455,18 @@ __global__ void __launch_bounds__(256, NP == 2 ? 3 : 1) k_q128(Q128Args a) {
 template <int DT>
 __global__ void __launch_bounds__(512, 1) k_q128sk(Q128Args a) {
   constexpr bool XLO = DT != TQ_BF16, XLO2 = DT == TQ_F32;
-  __shared__ __align__(16) uint16_t xh[TILE][XS];
-  __shared__ __align__(16) uint16_t xl[XLO ? TILE : 1][XS];
-  __shared__ __align__(16) uint16_t xl2[XLO2 ? TILE : 1][XS];
+  // one barrier per pass: the staged tile and its scales alternate between
+  // two buffers, the per-vector norms and flags (also read by the sketch
+  // waves one pass later) between three
+  __shared__ __align__(16) uint16_t xh[2][TILE][XS];
+  __shared__ __align__(16) uint16_t xl[XLO ? 2 : 1][XLO ? TILE : 1][XS];
+  __shared__ __align__(16) uint16_t xl2[XLO2 ? 2 : 1][XLO2 ? TILE : 1][XS];
   __shared__ int2 s_tab[kQ128Cells];
   __shared__ float s_cent[256];
-  __shared__ float s_ig[TILE];
+  __shared__ float s_ig[2][TILE];
   __shared__ float s_c2[4][TILE];
-  __shared__ float s_n[2][TILE];
-  __shared__ int s_valid[2][TILE];
+  __shared__ float s_n[3][TILE];
+  __shared__ int s_valid[3][TILE];
   __shared__ __align__(16) uint16_t rh[2][TILE][XS];
   __shared__ __align__(16) uint16_t rl[2][TILE][XS];
   __shared__ float s_r2[2][4][TILE];
@@ -517,12 +520,13 @@ __global__ void __launch_bounds__(512, 1) k_q128sk(Q128Args a) {
   };
 
   const int G1 = (int)gridDim.x, G2 = 2 * G1;
-  // one pass: the rotation waves take `tile` (if < n_tiles) into buffer q,
-  // the sketch waves take tile - G1 (if this is not the first pass) from
-  // buffer q ^ 1
-  auto step = [&](Share<DT>& cur, const int tile, const int q) __attribute__((always_inline)) {
+  // pass `it`: the rotation waves take `tile` (if < n_tiles) into buffers
+  // q = it % 2 and n3 = it % 3, the sketch waves take tile - G1 (if this is
+  // not the first pass) from buffers q ^ 1 and (it + 2) % 3
+  auto step = [&](Share<DT>& cur, const int tile, const int q, const int it) __attribute__((always_inline)) {
     const bool have = tile < a.n_tiles;
     const bool prev = tile - G1 >= (int)blockIdx.x;
+    const int n3 = it % 3, p3 = (it + 2) % 3;
     // (a) stage this thread's share; |x| in fp32, reduced over the row's 8 threads
     if (rot && have) {
       int seq;
@@ -539,7 +543,7 @@ __global__ void __launch_bounds__(512, 1) k_q128sk(Q128Args a) {
             const bf16x2 v = __builtin_bit_cast(bf16x2, w4[k]);
             s2 = __builtin_amdgcn_fdot2_f32_bf16(v, v, s2, false);
           }
-          *reinterpret_cast<uint4*>(&xh[r8][c0 + 8 * c]) = cur.w[c];
+          *reinterpret_cast<uint4*>(&xh[q][r8][c0 + 8 * c]) = cur.w[c];
         }
       } else {
         float xv[16];
@@ -573,13 +577,13 @@ __global__ void __launch_bounds__(512, 1) k_q128sk(Q128Args a) {
           if constexpr (XLO2)
             mw[k] = bf16_bits(e0 - bf16_float(l0)) | (bf16_bits(e1 - bf16_float(l1)) << 16);
         }
-        *reinterpret_cast<uint4*>(&xh[r8][c0]) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-        *reinterpret_cast<uint4*>(&xh[r8][c0 + 8]) = make_uint4(hw[4], hw[5], hw[6], hw[7]);
-        *reinterpret_cast<uint4*>(&xl[r8][c0]) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-        *reinterpret_cast<uint4*>(&xl[r8][c0 + 8]) = make_uint4(lw[4], lw[5], lw[6], lw[7]);
+        *reinterpret_cast<uint4*>(&xh[q][r8][c0]) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        *reinterpret_cast<uint4*>(&xh[q][r8][c0 + 8]) = make_uint4(hw[4], hw[5], hw[6], hw[7]);
+        *reinterpret_cast<uint4*>(&xl[q][r8][c0]) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+        *reinterpret_cast<uint4*>(&xl[q][r8][c0 + 8]) = make_uint4(lw[4], lw[5], lw[6], lw[7]);
         if constexpr (XLO2) {
-          *reinterpret_cast<uint4*>(&xl2[r8][c0]) = make_uint4(mw[0], mw[1], mw[2], mw[3]);
-          *reinterpret_cast<uint4*>(&xl2[r8][c0 + 8]) = make_uint4(mw[4], mw[5], mw[6], mw[7]);
+          *reinterpret_cast<uint4*>(&xl2[q][r8][c0]) = make_uint4(mw[0], mw[1], mw[2], mw[3]);
+          *reinterpret_cast<uint4*>(&xl2[q][r8][c0 + 8]) = make_uint4(mw[4], mw[5], mw[6], mw[7]);
         }
       }
       s2 += __shfl_xor(s2, 1);
@@ -588,9 +592,9 @@ __global__ void __launch_bounds__(512, 1) k_q128sk(Q128Args a) {
       if ((tid & 7) == 0) {
         const int64_t p = abs0 + r8;
         const float n = sqrtf(s2);
-        s_n[q][r8] = n;
-        s_ig[r8] = n > 0.f ? G / n : 0.f;
-        s_valid[q][r8] = (p >= a.tok_off && p < a.tok_off + a.n_tok) ? 1 : 0;
+        s_n[n3][r8] = n;
+        s_ig[q][r8] = n > 0.f ? G / n : 0.f;
+        s_valid[n3][r8] = (p >= a.tok_off && p < a.tok_off + a.n_tok) ? 1 : 0;
       }
     }
     __syncthreads();
@@ -606,11 +610,11 @@ __global__ void __launch_bounds__(512, 1) k_q128sk(Q128Args a) {
       f32x16 acs = {};
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        const bf16x8 xo = *reinterpret_cast<const bf16x8*>(&xh[c32][16 * s + 8 * hl]);
+        const bf16x8 xo = *reinterpret_cast<const bf16x8*>(&xh[q][c32][16 * s + 8 * hl]);
         if constexpr (XLO) {
-          const bf16x8 xq = *reinterpret_cast<const bf16x8*>(&xl[c32][16 * s + 8 * hl]);
+          const bf16x8 xq = *reinterpret_cast<const bf16x8*>(&xl[q][c32][16 * s + 8 * hl]);
           if constexpr (XLO2) {
-            const bf16x8 xr = *reinterpret_cast<const bf16x8*>(&xl2[c32][16 * s + 8 * hl]);
+            const bf16x8 xr = *reinterpret_cast<const bf16x8*>(&xl2[q][c32][16 * s + 8 * hl]);
             acs = mfma32(op[s], xr, acs);
           }
           acs = mfma32(op[8 + s], xq, acs);
@@ -625,7 +629,7 @@ __global__ void __launch_bounds__(512, 1) k_q128sk(Q128Args a) {
       // (c) indices: element v is coordinate 32 wq + 8(v/4) + 4hl + v%4 of vector c32
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const float key = fmaf(acc[v], s_ig[c32], G);
+        const float key = fmaf(acc[v], s_ig[q][c32], G);
         const int c = min((int)key, cmax);
         const int2 e = s_tab[c];
         iv[v] = e.x + (key >= __int_as_float(e.y) ? 1 : 0);
@@ -663,12 +667,12 @@ __global__ void __launch_bounds__(512, 1) k_q128sk(Q128Args a) {
       bits |= (uint32_t)__shfl_xor((int)bits, 32);
       const int rows = a.m - 32 * wq;          // sketch rows of this word
       if (rows < 32) bits &= rows > 0 ? (1u << rows) - 1u : 0u;
-      const bool qvalid = s_valid[pq][c32] != 0;
+      const bool qvalid = s_valid[p3][c32] != 0;
       const int64_t pos0 = row0(tile - G1);
       if (hl == 0 && qvalid && rows > 0) a.sign[(((pos0 + c32) * a.sign_pitch) >> 2) + wq] = bits;
       if (wq == 0 && hl == 0 && qvalid)
         a.rnorm[pos0 + c32] =
-            s_n[pq][c32] * sqrtf(((s_r2[pq][0][c32] + s_r2[pq][1][c32]) + s_r2[pq][2][c32]) + s_r2[pq][3][c32]);
+            s_n[p3][c32] * sqrtf(((s_r2[pq][0][c32] + s_r2[pq][1][c32]) + s_r2[pq][2][c32]) + s_r2[pq][3][c32]);
     }
     if (need_c) __syncthreads();
 
@@ -687,7 +691,7 @@ __global__ void __launch_bounds__(512, 1) k_q128sk(Q128Args a) {
       }
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) go[qq] = (uint32_t)__shfl_xor((int)gv[qq], 32);
-      const bool valid = s_valid[q][c32] != 0;
+      const bool valid = s_valid[n3][c32] != 0;
       if (hl == 0 && valid) {
         uint32_t* dst = reinterpret_cast<uint32_t*>(a.idx + (pos0 + c32) * a.idx_pitch) + wq * b;
         if (b == 4 && row16) {
@@ -711,7 +715,7 @@ __global__ void __launch_bounds__(512, 1) k_q128sk(Q128Args a) {
       }
       // (e) scale |x| (or |x| / |y^|) and (g) the residual
       // r = y - (scale / |x|) c[idx] of this lane's 16 coordinates
-      const float qn = s_n[q][c32];
+      const float qn = s_n[n3][c32];
       float ratio = 1.f;                       // scale / |x|
       if (need_c) {
         const float nh = sqrtf(((s_c2[0][c32] + s_c2[1][c32]) + s_c2[2][c32]) + s_c2[3][c32]);
@@ -741,7 +745,8 @@ __global__ void __launch_bounds__(512, 1) k_q128sk(Q128Args a) {
       r2 += __shfl_xor(r2, 32);
       if (hl == 0) s_r2[q][wq][c32] = r2;
     }
-    __syncthreads();
+    // no barrier here: what the next pass writes before its barrier (the
+    // other staging buffers, the next norm slot) is not read by this pass
   };
 
   Share<DT> s0, s1;
@@ -751,11 +756,11 @@ __global__ void __launch_bounds__(512, 1) k_q128sk(Q128Args a) {
     if (tile + G1 < a.n_tiles) fetch(s1, tile + G1);
   }
   __syncthreads();
-  for (;;) {
-    step(s0, tile, 0);
+  for (int it = 0;; it += 2) {
+    step(s0, tile, 0, it);
     if (tile >= a.n_tiles) break;
     tile += G1;
-    step(s1, tile, 1);
+    step(s1, tile, 1, it + 1);
     if (tile >= a.n_tiles) break;
     tile += G1;
   }
