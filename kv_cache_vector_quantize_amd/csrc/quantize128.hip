@@ -141,15 +141,22 @@ template <int DT, bool T32, int NP>
 // two-part variants keep three workgroups per CU
 __global__ void __launch_bounds__(256, NP == 2 ? 3 : 1) k_q128(Q128Args a) {
   constexpr bool XLO = DT != TQ_BF16, XLO2 = DT == TQ_F32;
-  __shared__ __align__(16) uint16_t xh[TILE][XS];
-  __shared__ __align__(16) uint16_t xl[XLO ? TILE : 1][XS];
-  __shared__ __align__(16) uint16_t xl2[XLO2 ? TILE : 1][XS];
-  __shared__ __align__(16) uint32_t tb[T32 ? 2 : 1][T32 ? 1024 : 1];   // tile32 block values, field masks
+  // NB = 2 (bf16 input): the staged tile, its per-vector data and (tile32)
+  // the assembled block alternate between two buffers, so a tile ends
+  // without a barrier (the next tile's staging writes the other buffers);
+  // fp16 and fp32 input stage two or three parts of x and keep one buffer
+  // and the barrier, which holds their LDS to what three workgroups per CU
+  // can share
+  constexpr int NB = DT == TQ_BF16 ? 2 : 1;
+  __shared__ __align__(16) uint16_t xh[NB][TILE][XS];
+  __shared__ __align__(16) uint16_t xl[XLO ? NB : 1][XLO ? TILE : 1][XS];
+  __shared__ __align__(16) uint16_t xl2[XLO2 ? NB : 1][XLO2 ? TILE : 1][XS];
+  __shared__ __align__(16) uint32_t tb[T32 ? NB : 1][T32 ? 2 : 1][T32 ? 1024 : 1];   // tile32 block values, field masks
   __shared__ int2 s_tab[kQ128Cells];
   __shared__ float s_cent[256];
-  __shared__ float s_n[TILE], s_ig[TILE];
+  __shared__ float s_n[NB][TILE], s_ig[NB][TILE];
   __shared__ float s_c2[4][TILE];
-  __shared__ int s_valid[TILE];
+  __shared__ int s_valid[NB][TILE];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int c32 = lane & 31, hl = lane >> 5;
@@ -188,7 +195,7 @@ __global__ void __launch_bounds__(256, NP == 2 ? 3 : 1) k_q128(Q128Args a) {
   // two tiles in flight per workgroup: the share of tile + 2 G is fetched
   // into the registers of tile as soon as that tile sits in LDS
   const int G2 = 2 * (int)gridDim.x;
-  auto step = [&](Share<DT>& cur, const int tile) __attribute__((always_inline)) {
+  auto step = [&](Share<DT>& cur, const int tile, const int q) __attribute__((always_inline)) {
     int seq;
     int64_t blk;
     where(tile, seq, blk);
@@ -211,7 +218,7 @@ __global__ void __launch_bounds__(256, NP == 2 ? 3 : 1) k_q128(Q128Args a) {
             const bf16x2 v = __builtin_bit_cast(bf16x2, w4[k]);
             s2 = __builtin_amdgcn_fdot2_f32_bf16(v, v, s2, false);
           }
-          *reinterpret_cast<uint4*>(&xh[r8][c0 + 8 * c]) = cur.w[c];
+          *reinterpret_cast<uint4*>(&xh[q][r8][c0 + 8 * c]) = cur.w[c];
         }
       } else {
         float xv[16];
@@ -245,13 +252,13 @@ __global__ void __launch_bounds__(256, NP == 2 ? 3 : 1) k_q128(Q128Args a) {
           if constexpr (XLO2)
             mw[k] = bf16_bits(e0 - bf16_float(l0)) | (bf16_bits(e1 - bf16_float(l1)) << 16);
         }
-        *reinterpret_cast<uint4*>(&xh[r8][c0]) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-        *reinterpret_cast<uint4*>(&xh[r8][c0 + 8]) = make_uint4(hw[4], hw[5], hw[6], hw[7]);
-        *reinterpret_cast<uint4*>(&xl[r8][c0]) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-        *reinterpret_cast<uint4*>(&xl[r8][c0 + 8]) = make_uint4(lw[4], lw[5], lw[6], lw[7]);
+        *reinterpret_cast<uint4*>(&xh[q][r8][c0]) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        *reinterpret_cast<uint4*>(&xh[q][r8][c0 + 8]) = make_uint4(hw[4], hw[5], hw[6], hw[7]);
+        *reinterpret_cast<uint4*>(&xl[q][r8][c0]) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+        *reinterpret_cast<uint4*>(&xl[q][r8][c0 + 8]) = make_uint4(lw[4], lw[5], lw[6], lw[7]);
         if constexpr (XLO2) {
-          *reinterpret_cast<uint4*>(&xl2[r8][c0]) = make_uint4(mw[0], mw[1], mw[2], mw[3]);
-          *reinterpret_cast<uint4*>(&xl2[r8][c0 + 8]) = make_uint4(mw[4], mw[5], mw[6], mw[7]);
+          *reinterpret_cast<uint4*>(&xl2[q][r8][c0]) = make_uint4(mw[0], mw[1], mw[2], mw[3]);
+          *reinterpret_cast<uint4*>(&xl2[q][r8][c0 + 8]) = make_uint4(mw[4], mw[5], mw[6], mw[7]);
         }
       }
       s2 += __shfl_xor(s2, 1);
@@ -260,9 +267,9 @@ __global__ void __launch_bounds__(256, NP == 2 ? 3 : 1) k_q128(Q128Args a) {
       if ((tid & 7) == 0) {
         const int64_t p = abs0 + r8;
         const float n = sqrtf(s2);
-        s_n[r8] = n;
-        s_ig[r8] = n > 0.f ? G / n : 0.f;
-        s_valid[r8] = (p >= a.tok_off && p < a.tok_off + a.n_tok) ? 1 : 0;
+        s_n[q][r8] = n;
+        s_ig[q][r8] = n > 0.f ? G / n : 0.f;
+        s_valid[q][r8] = (p >= a.tok_off && p < a.tok_off + a.n_tok) ? 1 : 0;
       }
     }
     __syncthreads();
@@ -274,11 +281,11 @@ __global__ void __launch_bounds__(256, NP == 2 ? 3 : 1) k_q128(Q128Args a) {
     f32x16 acc = {};
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const bf16x8 xo = *reinterpret_cast<const bf16x8*>(&xh[c32][16 * s + 8 * hl]);
+      const bf16x8 xo = *reinterpret_cast<const bf16x8*>(&xh[q][c32][16 * s + 8 * hl]);
       if constexpr (XLO) {
-        const bf16x8 xq = *reinterpret_cast<const bf16x8*>(&xl[c32][16 * s + 8 * hl]);
+        const bf16x8 xq = *reinterpret_cast<const bf16x8*>(&xl[q][c32][16 * s + 8 * hl]);
         if constexpr (XLO2) {
-          const bf16x8 xr = *reinterpret_cast<const bf16x8*>(&xl2[c32][16 * s + 8 * hl]);
+          const bf16x8 xr = *reinterpret_cast<const bf16x8*>(&xl2[q][c32][16 * s + 8 * hl]);
           acc = prod(acc, xr, ph[s]);
         }
         acc = prod(acc, xq, pl[s]);
@@ -296,7 +303,7 @@ __global__ void __launch_bounds__(256, NP == 2 ? 3 : 1) k_q128(Q128Args a) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int vec = T32 ? 8 * (v >> 2) + 4 * hl + (v & 3) : c32;
-      const float key = fmaf(acc[v], s_ig[vec], G);
+      const float key = fmaf(acc[v], s_ig[q][vec], G);
       const int c = min((int)key, cmax);
       const int2 e = s_tab[c];
       iv[v] = e.x + (key >= __int_as_float(e.y) ? 1 : 0);
@@ -340,7 +347,7 @@ __global__ void __launch_bounds__(256, NP == 2 ? 3 : 1) k_q128(Q128Args a) {
       }
 #pragma unroll
       for (int q = 0; q < 4; ++q) go[q] = (uint32_t)__shfl_xor((int)gv[q], 32);
-      if (hl == 0 && s_valid[c32]) {
+      if (hl == 0 && s_valid[q][c32]) {
         uint32_t* dst = reinterpret_cast<uint32_t*>(a.idx + (pos0 + c32) * a.idx_pitch) + wave * b;
         if (b == 4 && row16) {
           *reinterpret_cast<uint4*>(dst) = make_uint4(gv[0] | (go[0] << 16), gv[1] | (go[1] << 16),
@@ -377,11 +384,11 @@ __global__ void __launch_bounds__(256, NP == 2 ? 3 : 1) k_q128(Q128Args a) {
         for (int e = 0; e < 8; ++e) {
           const int v = 4 * (qq + 2 * (e >> 2)) + (e & 3);
           val |= (uint64_t)iv[v] << (e * b);
-          if (!full && s_valid[8 * (v >> 2) + 4 * hl + (v & 3)]) msk |= fm << (e * b);
+          if (!full && s_valid[q][8 * (v >> 2) + 4 * hl + (v & 3)]) msk |= fm << (e * b);
         }
         const int grp = (16 * Gq + C) * 8 + j;
-        uint8_t* vb = reinterpret_cast<uint8_t*>(tb[0]) + grp * b;
-        uint8_t* mb = reinterpret_cast<uint8_t*>(tb[1]) + grp * b;
+        uint8_t* vb = reinterpret_cast<uint8_t*>(tb[q][0]) + grp * b;
+        uint8_t* mb = reinterpret_cast<uint8_t*>(tb[q][1]) + grp * b;
         if (b == 4) {
           *reinterpret_cast<uint32_t*>(vb) = (uint32_t)val;
           if (!full) *reinterpret_cast<uint32_t*>(mb) = (uint32_t)msk;
@@ -402,8 +409,8 @@ __global__ void __launch_bounds__(256, NP == 2 ? 3 : 1) k_q128(Q128Args a) {
 
     // (e) scale: |x|, or |x| / |y^| with norm correction
     if (need_c) __syncthreads();
-    if (wave == 0 && hl == 0 && s_valid[c32]) {
-      const float n = s_n[c32];
+    if (wave == 0 && hl == 0 && s_valid[q][c32]) {
+      const float n = s_n[q][c32];
       float sc = n;
       if (need_c) {
         const float nh = sqrtf(((s_c2[0][c32] + s_c2[1][c32]) + s_c2[2][c32]) + s_c2[3][c32]);
@@ -411,8 +418,9 @@ __global__ void __launch_bounds__(256, NP == 2 ? 3 : 1) k_q128(Q128Args a) {
       }
       a.scale[pos0 + c32] = sc;
     }
-    // the next tile's staging overwrites what this tile's waves still read
-    __syncthreads();
+    // with one buffer the next tile's staging overwrites what this tile's
+    // waves still read; tile32 blocks are assembled by all waves
+    if (NB == 1 || T32) __syncthreads();
 
     if constexpr (T32) {
       // (f) the assembled tile32 block: 512*b bytes = 128*b words
@@ -420,13 +428,13 @@ __global__ void __launch_bounds__(256, NP == 2 ? 3 : 1) k_q128(Q128Args a) {
       uint32_t* dst = reinterpret_cast<uint32_t*>(a.idx) + (oseq * (a.seq_stride / TILE) + oblk) * (int64_t)words;
       for (int w = tid; w < words; w += 256) {
         if (full) {
-          dst[w] = tb[0][w];
+          dst[w] = tb[q][0][w];
         } else {
-          const uint32_t nm = tb[1][w];
-          if (nm != 0u) dst[w] = (dst[w] & ~nm) | (tb[0][w] & nm);
+          const uint32_t nm = tb[q][1][w];
+          if (nm != 0u) dst[w] = (dst[w] & ~nm) | (tb[q][0][w] & nm);
         }
       }
-      __syncthreads();
+      if (NB == 1) __syncthreads();
     }
   };
 
@@ -436,9 +444,9 @@ __global__ void __launch_bounds__(256, NP == 2 ? 3 : 1) k_q128(Q128Args a) {
   if (tile + (int)gridDim.x < a.n_tiles) fetch(s1, tile + (int)gridDim.x);
   __syncthreads();
   for (; tile < a.n_tiles; tile += G2) {
-    step(s0, tile);
+    step(s0, tile, 0);
     if (tile + (int)gridDim.x >= a.n_tiles) break;
-    step(s1, tile + (int)gridDim.x);
+    step(s1, tile + (int)gridDim.x, NB - 1);
   }
 }
 
