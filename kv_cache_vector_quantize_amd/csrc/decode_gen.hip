@@ -301,10 +301,11 @@ __global__ void __launch_bounds__(64 * kGWaves) __attribute__((amdgpu_waves_per_
 
   // Raw data of one tile: key slices and sign words of tokens c16 and
   // 16 + c16, the token scalars of lane % 32, the lane's share of the tile32
-  // block.  For d <= 128 the next tile's loads go in flight as soon as the
-  // current one's are consumed (past the last tile they repeat it, so the
-  // count of loads in flight is the same on every pass); for d > 128 a tile
-  // is loaded when it is reached.
+  // block.  The next tile's loads go in flight while the current one is
+  // computed (past the last tile they repeat it, so the count of loads in
+  // flight is the same on every pass): for d <= 128 as soon as the current
+  // one's are consumed, for d > 128 (16 output accumulators) after the key
+  // and sketch products, when the current key words are dead.
   constexpr int VB = NU / 2;                  // 16-byte words of a tile32 block per lane
   struct Raw {
     uint32_t kw[2][KW + 1];
@@ -339,13 +340,11 @@ __global__ void __launch_bounds__(64 * kGWaves) __attribute__((amdgpu_waves_per_
   const int64_t ntile = t_end > t_begin ? (t_end - t_begin + 31) / 32 : 0;
   const int64_t t_last = t_begin + 32 * (ntile - 1);
   Raw R;
-  if constexpr (!BIG) {
-    if (ntile > 0) load(R, t_begin);
-  }
+  if (ntile > 0) load(R, t_begin);
   for (int64_t it = 0; it < ntile; ++it) {
     const int64_t t0 = t_begin + 32 * it;
+    const int64_t t_next = t0 + 32 < t_last ? t0 + 32 : t_last;
     const int lim = t_end - t0 < 32 ? (int)(t_end - t0) : 32;
-    if constexpr (BIG) load(R, t0);
     // ---- consume the tile: scalars and the value block into the wave's
     // LDS slots, key slices shifted to bit 0, sign words
     stage[lane] = lane < 32 ? R.ks : R.kr;
@@ -365,7 +364,7 @@ __global__ void __launch_bounds__(64 * kGWaves) __attribute__((amdgpu_waves_per_
 #pragma unroll
       for (int c = 0; c < kGNs; ++c) sw[blk][c] = R.sw[blk][c];
     }
-    if constexpr (!BIG) load(R, t0 + 32 < t_last ? t0 + 32 : t_last);
+    if constexpr (!BIG) load(R, t_next);
 
     // ---- S^T = K^ Q~^T (16 tokens x 16 columns per block)
     f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
@@ -399,6 +398,7 @@ __global__ void __launch_bounds__(64 * kGWaves) __attribute__((amdgpu_waves_per_
           accq[blk] = mfma(s_sgn[(sw[blk][c] >> (8 * g4)) & 0xFFu], tb, accq[blk]);
       }
     }
+    if constexpr (BIG) load(R, t_next);
     // logits (base 2): the scales per column, then hi + lo columns
     float lg[2][4];
 #pragma unroll
