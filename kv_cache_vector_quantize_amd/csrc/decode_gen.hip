@@ -314,23 +314,27 @@ __global__ void __launch_bounds__(64 * kGWaves) __attribute__((amdgpu_waves_per_
     u32x4 vb[VB];
   };
   const int nvb = a.blk_bytes >> 4;
+  const int kp32 = (int)a.k_pitch, sp32 = (int)a.ks_pitch;     // <= 256 and 32 bytes
   auto load = [&](Raw& R, const int64_t t0) {
     const int lim = t_end - t0 < 32 ? (int)(t_end - t0) : 32;
     const int64_t pt0 = phys(t0);       // the tile's 32 positions lie in one page
+    // the tile's first row (uniform), then 32-bit lane offsets
+    const char* kt = kbase + pt0 * a.k_pitch + 4 * kd0;
+    const char* st = ns ? sbase + pt0 * a.ks_pitch : nullptr;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       const int tk = 16 * blk + c16 < lim ? 16 * blk + c16 : lim - 1;
-      const uint32_t* kr = reinterpret_cast<const uint32_t*>(kbase + (pt0 + tk) * a.k_pitch) + kd0;
+      const uint32_t* kr = reinterpret_cast<const uint32_t*>(kt + (uint32_t)(tk * kp32));
 #pragma unroll
       for (int i = 0; i <= KW; ++i) R.kw[blk][i] = i < nkw ? kr[i] : 0u;
-      const uint32_t* sr = ns ? reinterpret_cast<const uint32_t*>(sbase + (pt0 + tk) * a.ks_pitch) : nullptr;
+      const uint32_t* sr = ns ? reinterpret_cast<const uint32_t*>(st + (uint32_t)(tk * sp32)) : nullptr;
 #pragma unroll
       for (int c = 0; c < kGNs; ++c) R.sw[blk][c] = c < ns ? sr[c] : 0u;
     }
     const int tk = (lane & 31) < lim ? (lane & 31) : lim - 1;
-    const int64_t r = seq * a.k_stride + pt0 + tk;
-    R.ks = a.kscale[r];
-    R.kr = ns ? a.krnorm[r] : 0.f;
+    const int64_t r = seq * a.k_stride + pt0;
+    R.ks = a.kscale[r + tk];
+    R.kr = ns ? a.krnorm[r + tk] : 0.f;
     R.vs = a.vscale[seq * a.v_stride + pt0 + tk];
     const u32x4* src = reinterpret_cast<const u32x4*>(a.vidx + (vblk0 + (pt0 >> 5)) * (int64_t)a.blk_bytes);
 #pragma unroll
@@ -409,9 +413,15 @@ __global__ void __launch_bounds__(64 * kGWaves) __attribute__((amdgpu_waves_per_
       for (int r = 0; r < 4; ++r) {
         float u = ks[r] * acc[blk][r];
         if (ns) u = fmaf(kr[r], accq[blk][r], u);
-        u += dpp_ror8(u);
-        lg[blk][r] = 16 * blk + 4 * g4 + r < lim ? u : -INFINITY;
+        lg[blk][r] = u + dpp_ror8(u);
       }
+    }
+    if (lim < 32) {                     // the tile's tokens past the end of the range
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (16 * blk + 4 * g4 + r >= lim) lg[blk][r] = -INFINITY;
     }
     if (a.logits && c16 < 8 && qg * 8 + c16 < a.g) {
       float* dst = a.logits + ((int64_t)b * a.Hq + (int64_t)h * a.g + qg * 8 + c16) * a.n_ctx + t0;
@@ -437,8 +447,11 @@ __global__ void __launch_bounds__(64 * kGWaves) __attribute__((amdgpu_waves_per_
     }
     const f32x4 vs0 = *reinterpret_cast<const f32x4*>(stage + 64 + 4 * g4);
     const f32x4 vs1 = *reinterpret_cast<const f32x4*>(stage + 80 + 4 * g4);
-    // weights of the lane's token slots e (tokens 4 g4 + e % 4 + 16 (e / 4)):
-    // hi part in columns < 8, the remainder in the others, each twice
+    // weights of the lane's token slots e (tokens 4 g4 + e % 4 + 16 (e / 4)),
+    // each twice: the bf16-truncated weight in columns < 8, the truncated
+    // remainder in the others (about 2^-16 of the weight left out).  Tokens
+    // past the range have p = 0 and the finite scale of a token in it.
+    const float sel_lo = c16 >= 8 ? 1.f : 0.f;
     u32x4 pop[2];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
@@ -446,10 +459,9 @@ __global__ void __launch_bounds__(64 * kGWaves) __attribute__((amdgpu_waves_per_
       for (int r = 0; r < 4; ++r) {
         const float p = __builtin_amdgcn_exp2f(lg[blk][r] - M);   // 0 for -inf
         l += p;
-        const float w = 16 * blk + 4 * g4 + r < lim ? p * (blk == 0 ? vs0[r] : vs1[r]) : 0.f;
-        const uint32_t hi = bf16_rne(w);
-        const uint32_t x = c16 < 8 ? hi : bf16_rne(w - __uint_as_float(hi << 16));
-        pop[blk][r] = x | (x << 16);
+        const float w = p * (blk == 0 ? vs0[r] : vs1[r]);
+        const float x = fmaf(-sel_lo, __uint_as_float(__float_as_uint(w) & 0xFFFF0000u), w);
+        pop[blk][r] = __builtin_amdgcn_perm(__float_as_uint(x), __float_as_uint(x), 0x03020302u);
       }
     // ---- O^T += V^ P^T, coordinates 16 db + c16
 #pragma unroll
