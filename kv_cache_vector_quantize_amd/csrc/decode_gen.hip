@@ -279,7 +279,6 @@ __global__ void __launch_bounds__(64 * kGWaves) __attribute__((amdgpu_waves_per_
   char* s_v = s_work + wave * kGSlot;
   const uint32_t* s_v32 = reinterpret_cast<const uint32_t*>(s_v);
   float* stage = &s_sc[wave][0];
-  const uint32_t vmask = (1u << a.bv) - 1u;
   // value fields of coordinate 16 db + c16: token slots e = 0..7 (tokens
   // 4 g4 + e % 4 + 16 (e / 4)) are 8 consecutive fields from bit
   // vp0 + 8 bv db of the block
@@ -490,7 +489,6 @@ __global__ void __launch_bounds__(64 * kGWaves) __attribute__((amdgpu_waves_per_
       acc_o[db] = mfma(va1, pop[1], acc_o[db]);
     }
   }
-  (void)vmask;
 
   // positions of this wave's range that no tile covered (beyond len_b)
   if (a.logits && part < a.n_parts) {
