@@ -154,7 +154,8 @@ __global__ void __launch_bounds__(256, NP == 2 ? 3 : 1) k_q128(Q128Args a) {
   __shared__ __align__(16) uint32_t tb[T32 ? NB : 1][T32 ? 2 : 1][T32 ? 1024 : 1];   // tile32 block values, field masks
   __shared__ int2 s_tab[kQ128Cells];
   __shared__ float s_cent[256];
-  __shared__ float s_n[NB][TILE], s_ig[NB][TILE];
+  __shared__ __align__(16) float s_n[NB][TILE];
+  __shared__ __align__(16) float s_ig[NB][TILE];
   __shared__ float s_c2[4][TILE];
   __shared__ int s_valid[NB][TILE];
 
@@ -380,11 +381,22 @@ __global__ void __launch_bounds__(256, NP == 2 ? 3 : 1) k_q128(Q128Args a) {
       for (int qq = 0; qq < 2; ++qq) {
         const int Gq = hl + 2 * qq;
         uint64_t val = 0, msk = 0;
+        if (b <= 4) {
+          // the 8 fields fit one word: 32-bit shifts
+          uint32_t v32 = 0u;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int v = 4 * (qq + 2 * (e >> 2)) + (e & 3);
-          val |= (uint64_t)iv[v] << (e * b);
-          if (!full && s_valid[q][8 * (v >> 2) + 4 * hl + (v & 3)]) msk |= fm << (e * b);
+          for (int e = 0; e < 8; ++e) v32 |= (uint32_t)iv[4 * (qq + 2 * (e >> 2)) + (e & 3)] << (e * b);
+          val = v32;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) val |= (uint64_t)iv[4 * (qq + 2 * (e >> 2)) + (e & 3)] << (e * b);
+        }
+        if (!full) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int v = 4 * (qq + 2 * (e >> 2)) + (e & 3);
+            if (s_valid[q][8 * (v >> 2) + 4 * hl + (v & 3)]) msk |= fm << (e * b);
+          }
         }
         const int grp = (16 * Gq + C) * 8 + j;
         uint8_t* vb = reinterpret_cast<uint8_t*>(tb[q][0]) + grp * b;
