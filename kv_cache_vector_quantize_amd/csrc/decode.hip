@@ -6,26 +6,31 @@
 // correction of the inner product.
 //
 // Three launches:
-//  1. prologue, one workgroup per row = (batch, KV head, group of <= 8 query
-//     heads): q~ = Pi_K q scaled by sm_scale*log2(e), t = sqrt(pi/2)/m S_K q~,
-//     split into bf16 hi + lo and written in the lane order of the B operand
-//     of v_mfma_f32_16x16x32_bf16 (columns 0-7 = hi of the 8 queries, 8-15 =
+//  1. prologue, grid (4, rows), a row = (batch, KV head, group of <= 8 query
+//     heads), each workgroup two query slots of the row: q~ = Pi_K q scaled
+//     by sm_scale*log2(e), t = sqrt(pi/2)/m S_K q~, split into bf16 hi + lo
+//     and written in the lane order of the B operand of
+//     v_mfma_f32_16x16x32_bf16 (columns 0-7 = hi of the 8 queries, 8-15 =
 //     lo of the same queries).
-//  2. split: a workgroup of 4 waves covers 4 consecutive token chunks of one
-//     row; each wave streams 32-token tiles and computes on MFMA
+//  2. split: a workgroup of 8 waves covers 8 consecutive token chunks of one
+//     row; each wave streams 32-token tiles (the next tile's loads in
+//     flight) and computes on MFMA
 //       S^T = K^ Q~^T   (16 tokens x 16 query columns per block),
 //       the QJL term T^ (2 sigma) - sum(t)  (-sum(t) is the accumulator's
-//       initial value; sign bits become bf16 {0, 2.0} with two ALU ops),
+//       initial value; each sign bit stays at a bf16 exponent bit, one AND
+//       per two signs),
 //       O^T += V^ P^T   (in the value codebook's rotated domain),
 //     with an online softmax in base 2 whose reference maximum is only moved
 //     when a tile exceeds it by more than 2^8.  Code operands come from bf16
-//     hi/lo tables in LDS indexed by a pair of packed indices; hi and lo sit
-//     next to each other in the contraction dimension (operand dwords
-//     hi,lo,hi,lo against a duplicated other operand), so a 64-bit table read
-//     lands directly in the MFMA operand registers.  The 4 waves' partial
-//     (max, sum, o~) are merged in LDS and written once per workgroup.
-//  3. combine, one workgroup per row: log-sum-exp merge of the workgroups'
+//     hi/lo tables in LDS (pair tables, quad tables for 2- and 3-bit keys)
+//     indexed by packed indices; hi and lo sit next to each other in the
+//     contraction dimension (operand dwords hi,lo,hi,lo against a duplicated
+//     other operand), so a table read lands directly in the MFMA operand
+//     registers.  The 8 waves' partial (max, sum, o~) are merged in LDS and
+//     written once per workgroup.
+//  3. combine, grid (4, rows): log-sum-exp merge of the workgroups'
 //     partials in a fixed order, then out = Pi_V^T o~ / l.
+// Other head dimensions, code widths and sketch sizes go to decode_gen.hip.
 #include <algorithm>
 #include <type_traits>
 

@@ -20,14 +20,14 @@
 // bits against the 1e-4 the zone rule allows (8-bit codebooks have 16x the
 // boundaries and need the third part).
 //
-// Keys with a sketch (row layout) take three parts of Pi, so y and the
-// residual r = y - (scale/|x|) c[idx] carry fp32-level error and |r| its
-// relative accuracy.  Each wave writes its 32 coordinates of r to LDS as bf16
-// hi + lo; after the tile's barrier wave w forms sketch rows 32w .. 32w + 31
-// of u = S r with hi.hi + hi.lo + lo.hi products of S (registers) and r
-// (about 2^-17 of |S_j| |r|, far inside the 1e-5 zone of the sign rule),
-// packs their signs into word w of each sign row and, in wave 0, writes
-// rnorm = |x| |r|.
+// Keys with a sketch (row layout, k_q128sk) take three parts of Pi, so y and
+// the residual r = y - (scale/|x|) c[idx] carry fp32-level error and |r| its
+// relative accuracy.  Eight waves: the four rotation waves write their 32
+// coordinates of r to LDS as bf16 hi + lo; one pass later sketch wave w
+// forms sketch rows 32w .. 32w + 31 of u = S r with hi.hi + hi.lo + lo.hi
+// products of S (registers) and r (about 2^-17 of |S_j| |r|, far inside the
+// 1e-5 zone of the sign rule), packs their signs into word w of each sign
+// row and, in sketch wave 0, writes rnorm = |x| |r|.
 // Row layout codes take z^T (rows = coordinates: a lane holds 16 coordinates
 // of one vector); tile32 codes take z (rows = vectors: a lane holds one
 // coordinate of 16 vectors, which is how a tile32 record is ordered).
@@ -40,9 +40,9 @@
 // per coordinate; fp32 rounding of the key only matters when a boundary lies
 // within ~3e-7 of y.
 //
-// Pipeline.  The next tile's input is loaded into registers while the current
-// tile is rotated, indexed and packed; the grid holds as many workgroups as
-// stay resident, each looping over tiles.
+// Pipeline.  The inputs of the next two tiles are in flight in registers
+// while the current tile is rotated, indexed and packed; the grid holds as
+// many workgroups as stay resident, each looping over tiles.
 #include "tq_internal.hpp"
 
 namespace tq {

@@ -10,31 +10,36 @@
 // (no softmax scale), and the result is the k largest s_j per query, ties to
 // the lower index.
 //
-// k_ip_prologue  one workgroup per query: q~ = Pi q, t = sqrt(pi/2)/m S q~,
-//                written as bf16 hi/lo MFMA B operands for blocks of 8 queries.
-// k_ip_score2    (k <= 16) grid (database chunk, group of 128 queries); eight
-//                waves (two per SIMD) hold two 8-query blocks each as MFMA B
-//                operands in registers.  Each 16-row database tile is unpacked once per
-//                workgroup into A operands in LDS (centroid operand from the
-//                pair table, sign operand from sign bytes) and feeds all 16
-//                blocks through v_mfma_f32_16x16x32_bf16 (hi/lo query
-//                columns).  Tiles go in pairs between barriers: while the
-//                MFMAs of a tile run, the tile two ahead is unpacked, and
-//                raw code rows are fetched four to five tiles ahead.
-//                Each query keeps one unsorted top-k list in LDS with its
-//                worst entry (score, slot): the four lanes that hold the
-//                query's rows insert in row order, a better candidate
-//                overwrites the worst slot and one 128-bit read pass finds
-//                the new worst; every lane filters against a cached copy of
-//                the worst score.  The workgroup then sorts each list into k
-//                candidates per (query, chunk).  For large databases a first
-//                pass over every 64th tile gives each query the k-th best
-//                score of that sample, a lower bound of its final k-th score
-//                that the full pass starts from, so few candidates reach the
-//                lists.
-// k_ip_score     (k > 16) the same product with one 8-query block per
-//                workgroup and each wave unpacking its own tiles.
-// k_ip_merge     one wave per query selects the final k from the candidates.
+// The result is the exact top-k of s_j evaluated in float64 from the codes.
+// One call launches, in order:
+// k_ip_prologue  four queries per workgroup: q~ = Pi q and t = sqrt(pi/2)/m
+//                S q~ in float64, the norms the error bound needs, and the
+//                MFMA B operands: fp16, each query scaled by a power of two
+//                (k <= 16), or bf16 hi/lo (k > 16).
+// k_ip_bounds    one pass over the codes: per-workgroup maxima of |scale|,
+//                |rnorm| and |c[idx]|_2, reduced by k_ip_refine.
+// k_ip_score16   (topk_common.hpp; k <= 16) 256 (or 128) queries per
+//                workgroup, 8 waves x 2 (or 1) blocks of 16 queries as fp16
+//                B operands in registers; each 16-row database tile is
+//                unpacked once into LDS A operands (fp16 hi/lo centroids from
+//                a pair table, +-1 signs from a byte table) and feeds every
+//                block through v_mfma_f32_16x16x32_f16.  Candidates above
+//                the query's floor are appended to LDS buffers with an LDS
+//                atomic; a refresh keeps the best kc when a buffer fills.
+//                For large databases a sample pass over every 64th tile
+//                first writes the score of every sampled row, and
+//                k_ip_floor takes each query's kc-th best of them by a radix
+//                select: the full pass starts from that floor.
+// k_ip_score     (16 < k <= 32) the bf16 hi/lo product, one 8-query block
+//                per workgroup, each wave unpacking its own tiles.
+// k_ip_merge     the kc best candidates of each query over the chunks.
+// k_ip_refine    rescores the candidates in float64 from the codes, ranks
+//                them (ties to the lower index) and keeps the top k when the
+//                kc-th approximate score plus the bound on the approximate
+//                score's error is below the k-th exact score; other queries
+//                go to a list.
+// k_ip_fallback, k_ip_fbmerge  the exact float64 scan of the listed queries
+//                over 64 database chunks, and the merge of its lists.
 #include "topk_common.hpp"
 
 namespace tq {
