@@ -263,14 +263,31 @@ struct IBArgs {
 constexpr int kBoundRows = 256;
 constexpr int kBoundBlocks = 1024;    // most workgroups of k_ip_bounds
 
-template <int B>
+template <int B, bool WIDE>
 __global__ void __launch_bounds__(256) k_ip_bounds(IBArgs a) {
+  // widths that divide a byte read |c|^2 sums byte by byte: bt[v] is the sum
+  // of c^2 over the codes of byte value v
+  constexpr bool kBytes = B == 1 || B == 2 || B == 4 || B == 8;
   __shared__ float c2[1 << B];
-  __shared__ __align__(16) uint32_t rows[kBoundRows * (kIpMaxRowBytes / 4) + 8];
+  __shared__ float bt[kBytes ? 256 : 1];
+  // a minimal row holds B ceil(d/32) <= 8 B words (d <= 256): the buffer is
+  // sized for that, so narrow codes leave room for more resident workgroups;
+  // WIDE takes rows padded up to the largest pitch
+  constexpr int kRowWords = WIDE ? kIpMaxRowBytes / 4 : 8 * B;
+  __shared__ __align__(16) uint32_t rows[kBoundRows * kRowWords + 8];
   const int tid = threadIdx.x;
   if (tid < (1 << B)) {
     const double c = a.cent64[tid];
     c2[tid] = (float)(c * c);
+  }
+  if constexpr (kBytes) {
+    float sb = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8 / B; ++k) {
+      const double c = a.cent64[(tid >> (k * B)) & ((1 << B) - 1)];
+      sb += (float)(c * c);
+    }
+    bt[tid] = sb;
   }
   constexpr uint32_t mask = (1u << B) - 1u;
   const int groups = (a.d + 31) / 32;
@@ -282,7 +299,7 @@ __global__ void __launch_bounds__(256) k_ip_bounds(IBArgs a) {
     __syncthreads();                     // the previous rows are consumed (and c2 is ready)
     if ((reinterpret_cast<uintptr_t>(src) & 15u) == 0) {
       // 16-byte loads, all of a thread's share in flight before the stores
-      constexpr int kPer = kBoundRows * (kIpMaxRowBytes / 4) / 4 / 256;
+      constexpr int kPer = kBoundRows * kRowWords / 4 / 256;
       const int nw4 = nw >> 2;
       const uint4* s4 = reinterpret_cast<const uint4*>(src);
       uint4* r4 = reinterpret_cast<uint4*>(rows);
@@ -304,7 +321,19 @@ __global__ void __launch_bounds__(256) k_ip_bounds(IBArgs a) {
       if (a.rnorm) mr = fmaxf(mr, fabsf(a.rnorm[base + tid]));
       const uint32_t* ir = rows + tid * a.rw;
       float s0 = 0.f, s1 = 0.f;
-      for (int gi = 0; gi < groups; ++gi) {
+      int gi = 0;
+      if constexpr (kBytes) {
+        // whole groups of 32 codes (4B bytes) by byte
+        for (; gi < a.d / 32; ++gi) {
+#pragma unroll
+          for (int j = 0; j < B; ++j) {
+            const uint32_t w = ir[B * gi + j];
+            s0 += bt[w & 0xFFu] + bt[(w >> 8) & 0xFFu];
+            s1 += bt[(w >> 16) & 0xFFu] + bt[w >> 24];
+          }
+        }
+      }
+      for (; gi < groups; ++gi) {
         // codes 32 gi .. 32 gi + 31 occupy words B gi .. B gi + B - 1 (past
         // the row's words only for codes past d, which count 0)
         uint32_t w[B];
@@ -336,6 +365,12 @@ __global__ void __launch_bounds__(256) k_ip_bounds(IBArgs a) {
     const float v = fmaxf(fmaxf(part[tid][0], part[tid][1]), fmaxf(part[tid][2], part[tid][3]));
     a.bpart[blockIdx.x * 3 + tid] = (tid == 2) ? sqrtf(v) : v;
   }
+}
+
+template <int B>
+void launch_bounds(const IBArgs& a, bool wide, dim3 g, dim3 b, hipStream_t st) {
+  if (wide) hipLaunchKernelGGL((k_ip_bounds<B, true>), g, b, 0, st, a);
+  else hipLaunchKernelGGL((k_ip_bounds<B, false>), g, b, 0, st, a);
 }
 
 // Order-preserving keys of floats (larger float, larger key) and back.
@@ -1037,15 +1072,17 @@ hipError_t launch_topk(const tq_codebook* cb, const float* queries, const TopkPl
     if (nb < 1) nb = 1;
     nbp = (int)nb;
     const dim3 g((unsigned)nb), b(256);
+    // rows padded past 8 B words take the buffer for the largest pitch
+    const bool wide = rw > 8 * cb->p.bits;
     switch (cb->p.bits) {
-      case 1: hipLaunchKernelGGL(k_ip_bounds<1>, g, b, 0, stream, ba); break;
-      case 2: hipLaunchKernelGGL(k_ip_bounds<2>, g, b, 0, stream, ba); break;
-      case 3: hipLaunchKernelGGL(k_ip_bounds<3>, g, b, 0, stream, ba); break;
-      case 4: hipLaunchKernelGGL(k_ip_bounds<4>, g, b, 0, stream, ba); break;
-      case 5: hipLaunchKernelGGL(k_ip_bounds<5>, g, b, 0, stream, ba); break;
-      case 6: hipLaunchKernelGGL(k_ip_bounds<6>, g, b, 0, stream, ba); break;
-      case 7: hipLaunchKernelGGL(k_ip_bounds<7>, g, b, 0, stream, ba); break;
-      default: hipLaunchKernelGGL(k_ip_bounds<8>, g, b, 0, stream, ba); break;
+      case 1: launch_bounds<1>(ba, wide, g, b, stream); break;
+      case 2: launch_bounds<2>(ba, wide, g, b, stream); break;
+      case 3: launch_bounds<3>(ba, wide, g, b, stream); break;
+      case 4: launch_bounds<4>(ba, wide, g, b, stream); break;
+      case 5: launch_bounds<5>(ba, wide, g, b, stream); break;
+      case 6: launch_bounds<6>(ba, wide, g, b, stream); break;
+      case 7: launch_bounds<7>(ba, wide, g, b, stream); break;
+      default: launch_bounds<8>(ba, wide, g, b, stream); break;
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
