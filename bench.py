@@ -18,7 +18,9 @@ Printed: ONE JSON line with the contract fields plus
   (B=32, 32 query / 4 KV heads);
 * vector_search: tq_ip_topk queries/s, MFMA rate and recall on 1e6 coded
   vectors of d=200 with 1000 queries;
-* copy_GBps: the box's device-to-device copy rate (1 GiB);
+* copy_GBps: the box's device-to-device copy rate (1 GiB); read_GBps and
+  write_GBps: the rates of a kernel that only reads and of one that only
+  writes 1 GiB (the ceilings of read- and store-dominated kernels);
 * cpu_baseline: the float64 CPU oracle timed on a bounded sample.
 """
 from __future__ import annotations
@@ -178,7 +180,8 @@ def quantize_leg(torch, tq, synth, dev, iters, warm):
                 rotation_TFLOP_per_s=round(flops / (ms * 1e-3) / 1e12, 2),
                 mfma_TFLOP_per_s=round(mfma_flops / (ms * 1e-3) / 1e12, 2),
                 mfma_frac_bf16_peak=round(mfma_flops / (ms * 1e-3) / 2.5e15, 4),
-                bytes_per_call=int(in_bytes + out_bytes), dequantize=deq)
+                bytes_per_call=int(in_bytes + out_bytes), read_bytes_per_call=int(in_bytes),
+                write_bytes_per_call=int(out_bytes), dequantize=deq)
 
 
 def sketch_build_leg(torch, tq, W, iters, warm):
@@ -223,7 +226,9 @@ def dequantize_leg(torch, tq, kcb, vcb, kc, vc, n_seq, n_tok, iters, warm):
     tq.tq_profile_enable(False)
     kern_ms, kern_spread = kernel_spread(tq, tq.TQ_KERNEL_DEQUANTIZE)
     n_vec = 2 * n_seq * n_tok
-    nbytes = n_vec * ((d * kcb.bits // 8 + 4) + d * 2)
+    rbytes = n_vec * (d * kcb.bits // 8 + 4)
+    wbytes = n_vec * d * 2
+    nbytes = rbytes + wbytes
     # Pi^T hi.hi + hi.lo + lo.hi on 32x32x16 bf16 MFMAs: three issued products
     # per useful one
     mfma_flops = 3 * 2.0 * d * d * n_vec
@@ -235,7 +240,7 @@ def dequantize_leg(torch, tq, kcb, vcb, kc, vc, n_seq, n_tok, iters, warm):
                 kernel_ms_spread=kern_spread,
                 kernel_GB_per_s=round(nbytes / 2 / (kern_ms * 1e-3) / 1e9, 1),
                 mfma_TFLOP_per_s=round(mfma_flops / (ms * 1e-3) / 1e12, 2),
-                bytes_per_call=int(nbytes))
+                bytes_per_call=int(nbytes), read_bytes_per_call=int(rbytes), write_bytes_per_call=int(wbytes))
 
 
 def dequant_attend_leg(torch, tq, W, iters, warm, copy_gbps):
@@ -846,6 +851,21 @@ def main():
     res["read_GBps"] = round((1 << 30) / (rmed * 1e-3) / 1e9, 1)
     res["read_ms_spread"] = spread(rper)
     res["roofline"]["frac_of_read_ceiling"] = round(res["roofline"]["achieved"] / res["read_GBps"], 4)
+    # streaming-write ceiling: a kernel that only writes 1 GiB (median of 20)
+    for _ in range(3):
+        tq.tq_stream_write(src, 0)
+    _, wper = timed_iters(torch, lambda: tq.tq_stream_write(src, 0), 20)
+    wmed = float(np.median(wper))
+    res["write_GBps"] = round((1 << 30) / (wmed * 1e-3) / 1e9, 1)
+    res["write_ms_spread"] = spread(wper)
+    # the quantize and dequantize calls against the time their reads and
+    # writes take at the streaming ceilings
+    if "quantize" in res:
+        for leg in (res["quantize"], res["quantize"]["dequantize"]):
+            floor_ms = (leg["read_bytes_per_call"] / (res["read_GBps"] * 1e9)
+                        + leg["write_bytes_per_call"] / (res["write_GBps"] * 1e9)) * 1e3
+            leg["stream_floor_ms"] = round(floor_ms, 4)
+            leg["frac_of_stream_ceiling"] = round(floor_ms / leg["ms_per_call"], 4)
     del src, sink
     if not args.no_ab:
         print("[bench] dequantize-then-attend leg", file=sys.stderr, flush=True)

@@ -407,6 +407,13 @@ tq_status tq_profile_durations(int32_t kernel, double* ms, int64_t capacity, int
  * against.  Errors: TQ_ERR_INVALID, TQ_ERR_HIP. */
 tq_status tq_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream);
 
+/* Measurement helper (not part of the method): enqueues a kernel that only
+ * writes: every 32-bit word of the first `bytes` bytes of buf (device,
+ * 16-byte aligned, bytes a multiple of 16) becomes `value`, with 16-byte
+ * stores.  Its rate is the device's streaming-write ceiling, the bound of the
+ * store-dominated kernels (dequantize).  Errors: TQ_ERR_INVALID, TQ_ERR_HIP. */
+tq_status tq_stream_write(void* buf, int64_t bytes, uint32_t value, void* stream);
+
 /* Message of the last failing call on this thread ("" if none).  With the
  * environment variable TQ_LOG set (to anything but "0") when the library is
  * first used, every hot-path call (codebook builds, quantize, decode, top-k,

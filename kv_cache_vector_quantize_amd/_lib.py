@@ -27,7 +27,7 @@ EXPORTS = (
     "tq_code_row_bytes", "tq_quantize_kv", "tq_attn_decode_workspace", "tq_attn_decode",
     "tq_ip_topk_workspace", "tq_ip_topk", "tq_dequantize", "tq_quantize_kv_paged",
     "tq_attn_decode_paged_workspace", "tq_attn_decode_paged", "tq_profile_enable", "tq_profile_read",
-    "tq_codebook_solver_limits", "tq_profile_durations", "tq_stream_read", "tq_attn_decode_noalloc",
+    "tq_codebook_solver_limits", "tq_profile_durations", "tq_stream_read", "tq_stream_write", "tq_attn_decode_noalloc",
     "tq_polar_codebook_build", "tq_polar_codebook_values", "tq_ip_topk_exact_scan", "tq_ip_topk_scan_count",
     "tq_last_error",
 )
@@ -100,6 +100,7 @@ def lib() -> ctypes.CDLL:
     L.tq_profile_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
     L.tq_profile_durations.argtypes = [i32, dp, i64, ctypes.POINTER(i64)]
     L.tq_stream_read.argtypes = [vp, i64, vp, vp]
+    L.tq_stream_write.argtypes = [vp, i64, ctypes.c_uint32, vp]
     for name in EXPORTS:
         if name != "tq_last_error":
             getattr(L, name).restype = ctypes.c_int
@@ -484,6 +485,14 @@ def tq_profile_durations(kernel: int):
     ms = np.zeros(max(1, n.value))
     _check(lib().tq_profile_durations(int(kernel), _dptr(ms), n.value, ctypes.byref(n)))
     return ms[:n.value]
+
+
+def tq_stream_write(buf, value=0, stream=None):
+    """Enqueue a write-only pass over the device tensor ``buf`` (its byte size
+    a multiple of 16): every 32-bit word becomes ``value``."""
+    nbytes = buf.numel() * buf.element_size()
+    _check(lib().tq_stream_write(ctypes.c_void_p(buf.data_ptr()), nbytes, ctypes.c_uint32(value & 0xFFFFFFFF),
+                                 _stream_handle(stream)))
 
 
 def tq_stream_read(buf, sink, stream=None):

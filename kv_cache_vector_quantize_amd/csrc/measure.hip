@@ -1,6 +1,7 @@
-// Measurement helper: a plain streaming read of a device buffer, giving the
-// rate at which this device's HBM can be read by a kernel that only loads
-// (the ceiling against which the memory-bound kernels' rates are read).
+// Measurement helpers: a plain streaming read and a plain streaming write of a
+// device buffer, giving the rates at which this device's HBM can be read by a
+// kernel that only loads and written by one that only stores (the ceilings
+// against which the memory-bound kernels' rates are read).
 #include "tq_internal.hpp"
 
 namespace tq {
@@ -31,15 +32,34 @@ __global__ void __launch_bounds__(kReadThreads) k_stream_read(const u32x4* __res
   if (x == 0x9E3779B9u) sink[0] = x;
 }
 
+// Grid-stride 16-byte stores of one value.
+__global__ void __launch_bounds__(kReadThreads) k_stream_write(u32x4* __restrict__ buf, int64_t n16, uint32_t value) {
+  const int64_t stride = (int64_t)gridDim.x * kReadThreads;
+  const u32x4 v = {value, value, value, value};
+  for (int64_t i = (int64_t)blockIdx.x * kReadThreads + threadIdx.x; i < n16; i += stride)
+    __builtin_nontemporal_store(v, buf + i);
+}
+
+int64_t stream_grid(int64_t n16) {
+  const int64_t grid = (n16 + kReadThreads - 1) / kReadThreads;
+  return grid > 256 * 16 ? 256 * 16 : grid;    // 16 workgroups per CU, grid-stride beyond
+}
+
 }  // namespace
 
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t stream) {
   const int64_t n16 = bytes / 16;
   if (n16 <= 0) return hipSuccess;
-  int64_t grid = (n16 + kReadThreads - 1) / kReadThreads;
-  if (grid > 256 * 16) grid = 256 * 16;    // 16 workgroups per CU, grid-stride beyond
-  hipLaunchKernelGGL(k_stream_read, dim3((unsigned)grid), dim3(kReadThreads), 0, stream,
+  hipLaunchKernelGGL(k_stream_read, dim3((unsigned)stream_grid(n16)), dim3(kReadThreads), 0, stream,
                      static_cast<const u32x4*>(buf), n16, sink);
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_write(void* buf, int64_t bytes, uint32_t value, hipStream_t stream) {
+  const int64_t n16 = bytes / 16;
+  if (n16 <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_stream_write, dim3((unsigned)stream_grid(n16)), dim3(kReadThreads), 0, stream,
+                     static_cast<u32x4*>(buf), n16, value);
   return hipGetLastError();
 }
 

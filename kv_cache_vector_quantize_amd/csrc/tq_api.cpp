@@ -1138,6 +1138,16 @@ tq_status tq_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* s
   return TQ_OK;
 }
 
+tq_status tq_stream_write(void* buf, int64_t bytes, uint32_t value, void* stream) {
+  if (bytes < 0 || bytes % 16) return fail(TQ_ERR_INVALID, "bytes must be a non-negative multiple of 16");
+  if (bytes == 0) return TQ_OK;
+  if (!buf) return fail(TQ_ERR_INVALID, "buf must be non-NULL");
+  if (!aligned(buf, 16)) return fail(TQ_ERR_INVALID, "buf must be 16-byte aligned");
+  hipError_t e = launch_stream_write(buf, bytes, value, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "stream write launch");
+  return TQ_OK;
+}
+
 tq_status tq_profile_read(int32_t kernel, double* total_ms, int64_t* launches) {
   if (kernel < 0 || kernel > 3) return fail(TQ_ERR_INVALID, "unknown kernel id");
   double tot = 0.0;

@@ -278,5 +278,6 @@ hipError_t launch_polar_dequantize(const tq_codebook* cb, const DequantJob& job,
 // Streaming read of bytes (a multiple of 16) of buf; writes sink[0] only
 // in the rare case that the XOR of the data equals a fixed value.
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t stream);
+hipError_t launch_stream_write(void* buf, int64_t bytes, uint32_t value, hipStream_t stream);
 
 }  // namespace tq

@@ -558,3 +558,20 @@ def test_decode_deterministic(dev):
     lg2, out2, _ = _run_decode(dev, kcb, vcb, q, kc, vc, N)
     assert torch.equal(idx1, kc.idx)
     assert np.array_equal(lg1, lg2) and np.array_equal(out1, out2)
+
+
+def test_stream_measurement_kernels(dev):
+    """The streaming read and write kernels the ceilings are measured with:
+    the write sets every word (and nothing past the range), the read leaves
+    the sink alone unless the XOR of the buffer equals its fixed value."""
+    _say("stream read / write helpers")
+    buf = torch.zeros(4096 + 64, dtype=torch.int32, device=dev)
+    tq.tq_stream_write(buf[:4096], 0x12345678)
+    torch.cuda.synchronize()
+    assert bool((buf[:4096] == 0x12345678).all()) and bool((buf[4096:] == 0).all())
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    tq.tq_stream_read(buf[:4096], sink)
+    torch.cuda.synchronize()
+    assert bool((sink == 0).all())
+    with pytest.raises(tq.TQError):
+        tq.tq_stream_write(buf[:3], 0)
