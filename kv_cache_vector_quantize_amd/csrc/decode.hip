@@ -7,8 +7,9 @@
 //
 // Three launches:
 //  1. prologue, grid (4, rows), a row = (batch, KV head, group of <= 8 query
-//     heads), each workgroup two query slots of the row: q~ = Pi_K q scaled
-//     by sm_scale*log2(e), t = sqrt(pi/2)/m S_K q~, split into bf16 hi + lo
+//     heads), each workgroup 32 coordinates (and sketch rows) of all the
+//     row's query slots: q~ = Pi_K q scaled by sm_scale*log2(e),
+//     t = sqrt(pi/2)/m S_K q~, split into bf16 hi + lo
 //     and written in the lane order of the B operand of
 //     v_mfma_f32_16x16x32_bf16 (columns 0-7 = hi of the 8 queries, 8-15 =
 //     lo of the same queries).
@@ -46,7 +47,7 @@ typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 constexpr int D = 128;                 // head dimension of this kernel family
 constexpr int QOP_Q = 8 * 64 * 4;      // Q operand dwords: 8 MFMAs x 64 lanes x 4
 constexpr int QOP_T = 4 * 64 * 4;      // T operand dwords
-constexpr int QOP_DWORDS = QOP_Q + QOP_T + 16;
+constexpr int QOP_DWORDS = QOP_Q + QOP_T + 64;   // + QJL offsets [4 parts][16 columns]
 constexpr int kSignShift = 64;    // the sketch-query operand carries 2^-kSignShift
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
@@ -113,45 +114,57 @@ __device__ inline void stage_store(float (*dst)[D], const Stage& st, int cols, i
   }
 }
 
-// Grid (4, rows): workgroup (part, row) serves query slots 2 part and
-// 2 part + 1 of the row.  The rotation and the folded sketch S Pi are staged
-// in LDS by one batch of coalesced 16-byte loads; thread (i, c) forms
-// coordinate i of q~ = Pi q' and of t = sqrt(pi/2)/m (S Pi) q' for slot c in
-// one pass (q' = sm_scale log2(e) q), then writes the operand dwords of its
-// two columns (hi and lo) of the slots.
+// Grid (4, rows): workgroup (part, row) forms coordinates 32 part .. 32 part
+// + 31 of q~ = Pi q' and rows 32 part .. 32 part + 31 of t = sqrt(pi/2)/m
+// (S Pi) q' for all 8 query slots of the row (q' = sm_scale log2(e) q):
+// exactly the operand dwords of lane group g4 = part.  Only the part's 32
+// columns of the two matrices are staged (32 KB, one batch of coalesced
+// 16-byte loads); thread (i, c) forms coordinate i of slot c, then the
+// workgroup writes its lane group's operand dwords and its share of the
+// QJL accumulator offsets.
 __global__ void __launch_bounds__(256) k_prologue(PArgs a) {
-  __shared__ __align__(16) float mat[D][D];
-  __shared__ __align__(16) float mat2[D][D];
-  __shared__ __align__(16) float qs[2][D];
-  __shared__ float qt[2][D];
-  __shared__ float tt[2][D];
+  __shared__ __align__(16) float mat[D][32];
+  __shared__ __align__(16) float mat2[D][32];
+  __shared__ __align__(16) float qs[8][D];
+  __shared__ float qt[8][32];
+  __shared__ float tt[8][32];
   const int part = blockIdx.x, row = blockIdx.y;
   const int qg = row % a.qgroups;
   const int bh = row / a.qgroups;          // b * Hkv + h
   const int b = bh / a.Hkv, h = bh % a.Hkv;
   const int tid = threadIdx.x;
-  const int i = tid & (D - 1), c = tid >> 7;
-  const int slot = 2 * part + c;           // query slot within the row's group of 8
-  const bool live = qg * 8 + slot < a.g;
-  // all matrix loads first (one round trip; without a sketch the second batch
-  // re-reads the rotation and is not stored), then the query element
-  const bool sk = a.m > 0;
-  Stage st, st2;
-  stage_load(st, a.rotKT, D, tid);
-  stage_load(st2, sk ? a.sprotKT : a.rotKT, sk ? a.mp : D, tid);
-  {
-    const int j = qg * 8 + (live ? slot : 0);
-    const int64_t off = ((int64_t)b * a.Hq + h * a.g + j) * D + i;
+  const bool sk = a.m > 0 && 32 * part < a.mp;
+  // all matrix loads first (one round trip), then the query elements:
+  // 16-byte chunk c = tid + 256 j is row c / 8, columns 32 part + 4 (c % 8)
+  f32x4 r1[4], r2[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int c = tid + 256 * j;
+    const int k = c >> 3, i4 = 32 * part + 4 * (c & 7);
+    r1[j] = *reinterpret_cast<const f32x4*>(a.rotKT + (int64_t)k * D + i4);
+    r2[j] = sk ? *reinterpret_cast<const f32x4*>(a.sprotKT + (int64_t)k * a.mp + i4) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = tid + 256 * j;
+    const int slot = e >> 7, i = e & (D - 1);
+    const bool live = qg * 8 + slot < a.g;
+    const int64_t off = ((int64_t)b * a.Hq + h * a.g + qg * 8 + (live ? slot : 0)) * D + i;
     float v;
     if (a.qdt == TQ_F32) v = static_cast<const float*>(a.q)[off];
     else if (a.qdt == TQ_BF16) v = __uint_as_float((uint32_t) static_cast<const uint16_t*>(a.q)[off] << 16);
     else v = (float)static_cast<const _Float16*>(a.q)[off];
-    qs[c][i] = live ? v * a.qscale : 0.f;
+    qs[slot][i] = live ? v * a.qscale : 0.f;
   }
-  stage_store(mat, st, D, tid);
-  if (sk) stage_store(mat2, st2, a.mp, tid);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int c = tid + 256 * j;
+    *reinterpret_cast<f32x4*>(&mat[c >> 3][4 * (c & 7)]) = r1[j];
+    *reinterpret_cast<f32x4*>(&mat2[c >> 3][4 * (c & 7)]) = r2[j];
+  }
   __syncthreads();
   {
+    const int i = tid & 31, c = tid >> 5;
     float s1 = 0.f, s2 = 0.f;
 #pragma unroll 4
     for (int k = 0; k < D; k += 4) {
@@ -171,58 +184,53 @@ __global__ void __launch_bounds__(256) k_prologue(PArgs a) {
   // Q operand [u][lane][p]: MFMA u, lane group g4 covers dims 32*g4 + 4u .. +3;
   // dwords p = 0,1 -> dims (4u, 4u+1) (hi then lo slot of the key operand),
   // p = 2,3 -> dims (4u+2, 4u+3).  Columns 0-7 hold hi, 8-15 lo.  This
-  // workgroup writes the columns of its slots: f -> (u, g4, lo, c, p).
+  // workgroup writes lane group g4 = part: f -> (u, col, p).
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
     const int f = tid + 256 * r;
-    const int p = f & 3, cl = (f >> 2) & 1, lo = (f >> 3) & 1, g4 = (f >> 4) & 3, u = f >> 6;
-    const int col = 8 * lo + 2 * part + cl;
-    const int lane = 16 * g4 + col;
-    const int dim = 32 * g4 + 4 * u + 2 * (p >> 1);
+    const int p = f & 3, col = (f >> 2) & 15, u = f >> 6;
+    const int cl = col & 7, lo = col >> 3;
+    const int dim = 4 * u + 2 * (p >> 1);
     uint32_t hv[2];
     for (int h2 = 0; h2 < 2; ++h2) {
       const float v = qt[cl][dim + h2];
       const uint32_t hi = bf16_rne_bits(v);
       hv[h2] = lo ? bf16_rne_bits(v - __uint_as_float(hi << 16)) : hi;
     }
-    dst[(u * 64 + lane) * 4 + p] = hv[0] | (hv[1] << 16);
+    dst[(u * 64 + 16 * part + col) * 4 + p] = hv[0] | (hv[1] << 16);
   }
   // T operand [cc][lane][p]: dword p of MFMA cc faces sign dword K = 4cc + p
   // of lane group g4, whose low / high halves hold sign bits jl / jh at bf16
   // bit P; the entry is t of sketch row 32*g4 + j times 2^(128 - 2^(P-7)) and
   // 2^-kSignShift (exact power-of-two scalings).
   if (a.m > 0) {
-    const int f = tid;
-    const int p = f & 3, cl = (f >> 2) & 1, lo = (f >> 3) & 1, g4 = (f >> 4) & 3, cc = f >> 6;
-    const int col = 8 * lo + 2 * part + cl;
-    const int lane = 16 * g4 + col;
+    const int p = tid & 3, col = (tid >> 2) & 15, cc = tid >> 6;
+    const int cl = col & 7, lo = col >> 3;
     const int K = 4 * cc + p;
     const int P = (K < 8) ? 14 - K : 22 - K;
     const int ex = 128 - (1 << (P - 7)) - kSignShift;
     uint32_t hv[2];
     for (int h2 = 0; h2 < 2; ++h2) {
       const int j = h2 ? 30 - K : (K == 15 ? 31 : 14 - K);
-      const float v = ldexpf(tt[cl][32 * g4 + j], ex);
+      const float v = ldexpf(tt[cl][j], ex);
       const uint32_t hi = bf16_rne_bits(v);
       hv[h2] = lo ? bf16_rne_bits(v - __uint_as_float(hi << 16)) : hi;
     }
-    dst[QOP_Q + (cc * 64 + lane) * 4 + p] = hv[0] | (hv[1] << 16);
+    dst[QOP_Q + (cc * 64 + 16 * part + col) * 4 + p] = hv[0] | (hv[1] << 16);
   }
-  // QJL accumulator offsets: -sum_j (hi + lo) of t for the hi columns, in the
-  // scale of the sign products (2^-kSignShift); the lo columns start at 0
+  // QJL accumulator offsets, this part's share: -sum over its 32 sketch rows
+  // of (hi + lo) of t, in the scale of the sign products (2^-kSignShift), for
+  // the hi columns; the lo columns start at 0
   if (tid < 16) {
-    const int cl = tid >> 3, pp = tid & 7;
     float s = 0.f;
-    for (int j = pp; j < D; j += 8) {
-      const float v = tt[cl][j];
-      const float fh = __uint_as_float(bf16_rne_bits(v) << 16);
-      s += fh + __uint_as_float(bf16_rne_bits(v - fh) << 16);
+    if (tid < 8) {
+      for (int j = 0; j < 32; ++j) {
+        const float v = tt[tid][j];
+        const float fh = __uint_as_float(bf16_rne_bits(v) << 16);
+        s += fh + __uint_as_float(bf16_rne_bits(v - fh) << 16);
+      }
     }
-    s += __shfl_xor(s, 1);
-    s += __shfl_xor(s, 2);
-    s += __shfl_xor(s, 4);
-    float* cinit = reinterpret_cast<float*>(dst) + QOP_Q + QOP_T;
-    if (pp == 0) { cinit[2 * part + cl] = -ldexpf(s, -kSignShift); cinit[2 * part + cl + 8] = 0.f; }
+    reinterpret_cast<float*>(dst)[QOP_Q + QOP_T + 16 * part + tid] = tid < 8 ? -ldexpf(s, -kSignShift) : 0.f;
   }
 }
 
@@ -533,7 +541,12 @@ __global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_e
 #pragma unroll
     for (int c = 0; c < 4; ++c) ta[c] = __builtin_bit_cast(bf16x8, qop[QOP_Q / 4 + c * 64 + lane]);
   }
-  const float cinit = QJL ? reinterpret_cast<const float*>(a.qop + (int64_t)row * QOP_DWORDS)[QOP_Q + QOP_T + c16] : 0.f;
+  float cinit = 0.f;
+  if constexpr (QJL) {
+    // the prologue's four parts of the offset, summed in a fixed order
+    const float* ci = reinterpret_cast<const float*>(a.qop + (int64_t)row * QOP_DWORDS) + QOP_Q + QOP_T + c16;
+    cinit = ((ci[0] + ci[16]) + ci[32]) + ci[48];
+  }
   const float sel_lo = (c16 >= 8) ? 1.f : 0.f;
   static_assert(kSignShift == 64, "the staged residual norms carry 2^kSignShift");
 
