@@ -101,6 +101,38 @@ __device__ inline uint2 split_pair(float y0, float y1) {
   return make_uint2(h, __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){r0, r1}, bf16x2)));
 }
 
+// The b bytes (b <= 8) of one tile32 group, little-endian; the block base is
+// 4-byte aligned, so 4-, 2- and 1-byte groups are naturally aligned and
+// 8-byte ones are two words.
+__device__ inline uint64_t group_load(const uint8_t* p, int b) {
+  if (b == 4) return *reinterpret_cast<const uint32_t*>(p);
+  if (b == 2) return *reinterpret_cast<const uint16_t*>(p);
+  if (b == 1) return *p;
+  if (b == 8) {
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(p);
+    return (uint64_t)w[0] | ((uint64_t)w[1] << 32);
+  }
+  uint64_t v = 0;
+  for (int k = 0; k < b; ++k) v |= (uint64_t)p[k] << (8 * k);
+  return v;
+}
+
+__device__ inline void group_store(uint8_t* p, int b, uint64_t v) {
+  if (b == 4) {
+    *reinterpret_cast<uint32_t*>(p) = (uint32_t)v;
+  } else if (b == 2) {
+    *reinterpret_cast<uint16_t*>(p) = (uint16_t)v;
+  } else if (b == 1) {
+    *p = (uint8_t)v;
+  } else if (b == 8) {
+    uint32_t* w = reinterpret_cast<uint32_t*>(p);
+    w[0] = (uint32_t)v;
+    w[1] = (uint32_t)(v >> 32);
+  } else {
+    for (int k = 0; k < b; ++k) p[k] = (uint8_t)(v >> (8 * k));
+  }
+}
+
 // A thread's share of a tile: row tid/8, 16 consecutive input elements from
 // coordinate 16*(tid%8), as raw 16-byte words (zero for rows outside the
 // written range).
@@ -141,9 +173,9 @@ template <int DT, bool T32, int NP>
 // two-part variants keep three workgroups per CU
 __global__ void __launch_bounds__(256, NP == 2 ? 3 : 1) k_q128(Q128Args a) {
   constexpr bool XLO = DT != TQ_BF16, XLO2 = DT == TQ_F32;
-  // NB = 2 (bf16 input): the staged tile, its per-vector data and (tile32)
-  // the assembled block alternate between two buffers, so a tile ends
-  // without a barrier (the next tile's staging writes the other buffers);
+  // NB = 2 (bf16 input): the staged tile and its per-vector data alternate
+  // between two buffers, so a tile ends without a barrier (the next tile's
+  // staging writes the other buffers);
   // fp16 and fp32 input stage two or three parts of x and keep one buffer
   // and the barrier, which holds their LDS to what three workgroups per CU
   // can share
@@ -151,7 +183,6 @@ __global__ void __launch_bounds__(256, NP == 2 ? 3 : 1) k_q128(Q128Args a) {
   __shared__ __align__(16) uint16_t xh[NB][TILE][XS];
   __shared__ __align__(16) uint16_t xl[XLO ? NB : 1][XLO ? TILE : 1][XS];
   __shared__ __align__(16) uint16_t xl2[XLO2 ? NB : 1][XLO2 ? TILE : 1][XS];
-  __shared__ __align__(16) uint32_t tb[T32 ? NB : 1][T32 ? 2 : 1][T32 ? 1024 : 1];   // tile32 block values, field masks
   __shared__ int2 s_tab[kQ128Cells];
   __shared__ float s_cent[256];
   __shared__ __align__(16) float s_n[NB][TILE];
@@ -373,9 +404,11 @@ __global__ void __launch_bounds__(256, NP == 2 ? 3 : 1) k_q128(Q128Args a) {
       // tile32 record r' = 16G + C holds coordinate 16j + C for tokens
       // 4G + e%4 + 16(e/4), e = 0..7, as 8 consecutive b-bit fields (b bytes)
       // of group r'*8 + j; this lane holds the groups G = hl and G = 2 + hl of
-      // coordinate 32w + c32.  The block is assembled in LDS (values and, for
-      // partial tiles, field masks), then written out with whole words.
+      // coordinate 32w + c32.  Every group has one owner, which stores its b
+      // bytes straight into the block (merging with the stored fields of
+      // positions outside the written range in a partial tile).
       const int C = c32 & 15, j = 2 * wave + (c32 >> 4);
+      uint8_t* blk = a.idx + (oseq * (a.seq_stride / TILE) + oblk) * (int64_t)(512 * b);
       const uint64_t fm = (uint64_t)((1u << b) - 1u);
 #pragma unroll
       for (int qq = 0; qq < 2; ++qq) {
@@ -398,24 +431,9 @@ __global__ void __launch_bounds__(256, NP == 2 ? 3 : 1) k_q128(Q128Args a) {
             if (s_valid[q][8 * (v >> 2) + 4 * hl + (v & 3)]) msk |= fm << (e * b);
           }
         }
-        const int grp = (16 * Gq + C) * 8 + j;
-        uint8_t* vb = reinterpret_cast<uint8_t*>(tb[q][0]) + grp * b;
-        uint8_t* mb = reinterpret_cast<uint8_t*>(tb[q][1]) + grp * b;
-        if (b == 4) {
-          *reinterpret_cast<uint32_t*>(vb) = (uint32_t)val;
-          if (!full) *reinterpret_cast<uint32_t*>(mb) = (uint32_t)msk;
-        } else if (b == 8) {
-          *reinterpret_cast<uint2*>(vb) = make_uint2((uint32_t)val, (uint32_t)(val >> 32));
-          if (!full) *reinterpret_cast<uint2*>(mb) = make_uint2((uint32_t)msk, (uint32_t)(msk >> 32));
-        } else if (b == 2) {
-          *reinterpret_cast<uint16_t*>(vb) = (uint16_t)val;
-          if (!full) *reinterpret_cast<uint16_t*>(mb) = (uint16_t)msk;
-        } else {
-          for (int k = 0; k < b; ++k) {
-            vb[k] = (uint8_t)(val >> (8 * k));
-            if (!full) mb[k] = (uint8_t)(msk >> (8 * k));
-          }
-        }
+        uint8_t* gp = blk + ((16 * Gq + C) * 8 + j) * b;
+        if (full) group_store(gp, b, val);
+        else if (msk != 0) group_store(gp, b, (group_load(gp, b) & ~msk) | (val & msk));
       }
     }
 
@@ -431,23 +449,8 @@ __global__ void __launch_bounds__(256, NP == 2 ? 3 : 1) k_q128(Q128Args a) {
       a.scale[pos0 + c32] = sc;
     }
     // with one buffer the next tile's staging overwrites what this tile's
-    // waves still read; tile32 blocks are assembled by all waves
-    if (NB == 1 || T32) __syncthreads();
-
-    if constexpr (T32) {
-      // (f) the assembled tile32 block: 512*b bytes = 128*b words
-      const int words = 128 * b;
-      uint32_t* dst = reinterpret_cast<uint32_t*>(a.idx) + (oseq * (a.seq_stride / TILE) + oblk) * (int64_t)words;
-      for (int w = tid; w < words; w += 256) {
-        if (full) {
-          dst[w] = tb[q][0][w];
-        } else {
-          const uint32_t nm = tb[q][1][w];
-          if (nm != 0u) dst[w] = (dst[w] & ~nm) | (tb[q][0][w] & nm);
-        }
-      }
-      if (NB == 1) __syncthreads();
-    }
+    // waves still read
+    if (NB == 1) __syncthreads();
   };
 
   Share<DT> s0, s1;
