@@ -494,7 +494,7 @@ def bit_sweep_leg(torch, tq, synth, dev, iters, warm):
 
 
 def head_dims_leg(torch, tq, synth, dev, iters, warm):
-    """Decode at head dimensions other than 128 (the fp32 kernels): the 32K
+    """Decode at head dimensions other than 128 (the kernels of decode_gen.hip): the 32K
     GQA layer (B=32, 32 query / 4 KV heads, context 32768, bf16 K/V N(0,1)
     with outlier channels 3/77 x20) with 3-bit keys + QJL m=d and 4-bit
     values, for d = 64, 96 and 256, and at d = 128 with 5-bit keys (a width
@@ -533,7 +533,7 @@ def head_dims_leg(torch, tq, synth, dev, iters, warm):
                         split_kernel_ms_spread=split_spread, bytes_per_token_head=bpt,
                         split_GBps=round(gbs, 1), frac_hbm=round(gbs / HBM_PEAK_GBS, 4)))
         del kc, vc, kcb, vcb, ws
-    return dict(workload="decode at other head dimensions (fp32 kernels): B=32, Hq=32, Hkv=4, context 32768, "
+    return dict(workload="decode at other head dimensions (any-shape MFMA kernels): B=32, Hq=32, Hkv=4, context 32768, "
                          "bf16 K/V N(0,1) with channels 3/77 (those below d) x20, bf16 queries",
                 variants=res)
 

@@ -1055,7 +1055,7 @@ DecodePlan plan_decode(int64_t B, int64_t Hq, int64_t Hkv, int64_t n_ctx, int d,
   p.n_wg = (p.n_parts + kWaves - 1) / kWaves;
   size_t off = 0;
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
-  // query operands: the MFMA kernels' (d = 128) or the fp32 kernels' per row,
+  // query operands: the d = 128 kernels' or the any-shape kernels' per row,
   // whichever is larger, so one size serves every codebook of this d
   const size_t qrow = std::max<size_t>((size_t)QOP_DWORDS * 4, (size_t)decode_generic_row_bytes(d));
   p.off_qop = off; off = al(off + (size_t)p.rows * qrow);

@@ -1,7 +1,8 @@
 """GPU parity of decode attention at the shapes the d = 128 MFMA kernels do not
 take: head dimensions 3..256 other than 128, and at d = 128 the code widths
 (1, 5, 6, 7 bits) and sketch sizes (m > 128) those kernels lack.  These run on
-the fp32 kernels of decode_gen.hip.
+the any-shape kernels of decode_gen.hip (bf16 hi/lo MFMA operands, like the
+d = 128 kernels).
 
 The oracle quantizes the seeded inputs and packs its own codes; the GPU decodes
 those codes and both sides are held to the decode bars (logits within 1e-4 of

@@ -81,7 +81,7 @@ def _table(B, n_lp, n_pages, seed):
 
 @pytest.mark.parametrize("pt,N,lens,d,kb,km,vb", [
     (64, 300, None, 128, 3, 128, 4), (32, 200, [200, 77], 128, 3, 128, 4), (128, 513, [1, 513], 128, 3, 128, 4),
-    # head dimensions of the fp32 kernels
+    # head dimensions of the any-shape kernels (decode_gen.hip)
     (32, 200, [200, 77], 96, 4, 64, 3), (64, 300, None, 200, 2, 200, 4)])
 def test_paged_decode_matches_oracle(dev, pt, N, lens, d, kb, km, vb):
     _say("paged decode", pt, N, lens, d, kb, km, vb)
