@@ -134,8 +134,10 @@ __device__ inline void group_store(uint8_t* p, int b, uint64_t v) {
 }
 
 // A thread's share of a tile: row tid/8, 16 consecutive input elements from
-// coordinate 16*(tid%8), as raw 16-byte words (zero for rows outside the
-// written range).
+// coordinate 16*(tid%8), as raw 16-byte words.  Every fetch issues the same
+// loads (rows outside the written range read a row inside it and are zeroed
+// when staged), so the count of loads in flight is the same on every path
+// into a tile and a tile's wait does not drain the next tile's loads.
 template <int DT>
 struct Share {
   static constexpr int NW = DT == TQ_F32 ? 4 : 2;
@@ -143,13 +145,8 @@ struct Share {
 };
 
 template <int DT>
-__device__ inline void share_load(Share<DT>& sh, const void* x, int64_t e0, bool valid, bool vec_ok) {
+__device__ inline void share_load(Share<DT>& sh, const void* x, int64_t e0, bool vec_ok) {
   constexpr int EB = DT == TQ_F32 ? 4 : 2;
-  if (!valid) {
-#pragma unroll
-    for (int c = 0; c < Share<DT>::NW; ++c) sh.w[c] = make_uint4(0u, 0u, 0u, 0u);
-    return;
-  }
   const char* p = static_cast<const char*>(x) + e0 * EB;
   if (vec_ok) {
 #pragma unroll
@@ -168,6 +165,20 @@ __device__ inline void share_load(Share<DT>& sh, const void* x, int64_t e0, bool
     for (int c = 0; c < Share<DT>::NW; ++c) sh.w[c] = make_uint4(t[4 * c], t[4 * c + 1], t[4 * c + 2], t[4 * c + 3]);
   }
 }
+
+// The staged words of a share: zero for a row outside the written range.
+template <int DT>
+__device__ inline void share_mask(Share<DT>& sh, bool valid) {
+  const uint32_t m = valid ? 0xFFFFFFFFu : 0u;   // an AND in place, no branch
+#pragma unroll
+  for (int c = 0; c < Share<DT>::NW; ++c) {
+    sh.w[c].x &= m; sh.w[c].y &= m; sh.w[c].z &= m; sh.w[c].w &= m;
+  }
+}
+
+// All vector-memory loads issued so far have landed (vmcnt(0), other counters
+// left alone): the loop that follows then never waits on the operand loads.
+__device__ inline void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 template <int DT, bool T32, int NP>
 // two-part variants keep three workgroups per CU
@@ -218,10 +229,10 @@ __global__ void __launch_bounds__(256, NP == 2 ? 3 : 1) k_q128(Q128Args a) {
   auto fetch = [&](Share<DT>& sh, int tile) {
     int seq;
     int64_t blk;
-    where(tile, seq, blk);
-    const int64_t p = blk * TILE + r8;
-    const bool valid = p >= a.tok_off && p < a.tok_off + a.n_tok;
-    share_load<DT>(sh, a.x, ((int64_t)seq * a.n_tok + (p - a.tok_off)) * 128 + c0, valid, vec_ok);
+    where(tile < a.n_tiles ? tile : a.n_tiles - 1, seq, blk);
+    int64_t p = blk * TILE + r8;
+    p = p < a.tok_off ? a.tok_off : (p >= a.tok_off + a.n_tok ? a.tok_off + a.n_tok - 1 : p);
+    share_load<DT>(sh, a.x, ((int64_t)seq * a.n_tok + (p - a.tok_off)) * 128 + c0, vec_ok);
   };
 
   // two tiles in flight per workgroup: the share of tile + 2 G is fetched
@@ -240,6 +251,7 @@ __global__ void __launch_bounds__(256, NP == 2 ? 3 : 1) k_q128(Q128Args a) {
     // (a) stage this thread's share; |x| in fp32 from the input values,
     // reduced over the row's 8 threads
     {
+      share_mask<DT>(cur, abs0 + r8 >= a.tok_off && abs0 + r8 < a.tok_off + a.n_tok);
       float s2 = 0.f;
       if constexpr (DT == TQ_BF16) {
 #pragma unroll
@@ -306,7 +318,7 @@ __global__ void __launch_bounds__(256, NP == 2 ? 3 : 1) k_q128(Q128Args a) {
     }
     __syncthreads();
     // the share of the tile after next goes in flight while this one is computed
-    if (tile + G2 < a.n_tiles) fetch(cur, tile + G2);
+    fetch(cur, tile + G2);
 
     // (b) rotation: row layout -> D[coordinate][vector], tile32 -> D[vector][coordinate]
     auto prod = [&](f32x16 c, bf16x8 xo, bf16x8 po) { return T32 ? mfma32(xo, po, c) : mfma32(po, xo, c); };
@@ -455,8 +467,9 @@ __global__ void __launch_bounds__(256, NP == 2 ? 3 : 1) k_q128(Q128Args a) {
 
   Share<DT> s0, s1;
   int tile = blockIdx.x;
-  if (tile < a.n_tiles) fetch(s0, tile);
-  if (tile + (int)gridDim.x < a.n_tiles) fetch(s1, tile + (int)gridDim.x);
+  wait_loads();
+  fetch(s0, tile);
+  fetch(s1, tile + (int)gridDim.x);
   __syncthreads();
   for (; tile < a.n_tiles; tile += G2) {
     step(s0, tile, 0);
@@ -536,10 +549,10 @@ __global__ void __launch_bounds__(512, 1) k_q128sk(Q128Args a) {
   auto fetch = [&](Share<DT>& sh, int tile) {
     int seq;
     int64_t blk;
-    where(tile, seq, blk);
-    const int64_t p = blk * TILE + r8;
-    const bool valid = p >= a.tok_off && p < a.tok_off + a.n_tok;
-    share_load<DT>(sh, a.x, ((int64_t)seq * a.n_tok + (p - a.tok_off)) * 128 + c0, valid, vec_ok);
+    where(tile < a.n_tiles ? tile : a.n_tiles - 1, seq, blk);
+    int64_t p = blk * TILE + r8;
+    p = p < a.tok_off ? a.tok_off : (p >= a.tok_off + a.n_tok ? a.tok_off + a.n_tok - 1 : p);
+    share_load<DT>(sh, a.x, ((int64_t)seq * a.n_tok + (p - a.tok_off)) * 128 + c0, vec_ok);
   };
 
   const int G1 = (int)gridDim.x, G2 = 2 * G1;
@@ -556,6 +569,7 @@ __global__ void __launch_bounds__(512, 1) k_q128sk(Q128Args a) {
       int64_t blk;
       where(tile, seq, blk);
       const int64_t abs0 = blk * TILE;
+      share_mask<DT>(cur, abs0 + r8 >= a.tok_off && abs0 + r8 < a.tok_off + a.n_tok);
       float s2 = 0.f;
       if constexpr (DT == TQ_BF16) {
 #pragma unroll
@@ -622,11 +636,15 @@ __global__ void __launch_bounds__(512, 1) k_q128sk(Q128Args a) {
     }
     __syncthreads();
 
+    // the share of the tile after next goes in flight while this one is
+    // computed, on every pass and in all waves, so that every path into a
+    // staging waits alike and no share register is copied while its load is
+    // in flight (the sketch waves' loads repeat the rotation waves'
+    // addresses and hit the cache)
+    fetch(cur, tile + G2);
     int iv[16];
     f32x16 acc = {};
     if (rot && have) {
-      // the share of the tile after next goes in flight while this one is computed
-      if (tile + G2 < a.n_tiles) fetch(cur, tile + G2);
       // (b) rotation: D[coordinate][vector], coordinates 32 wq .. 32 wq + 31;
       // the hi.hi products and the smaller ones go to two accumulators so
       // the two chains interleave
@@ -774,10 +792,9 @@ __global__ void __launch_bounds__(512, 1) k_q128sk(Q128Args a) {
 
   Share<DT> s0, s1;
   int tile = blockIdx.x;
-  if (rot) {
-    if (tile < a.n_tiles) fetch(s0, tile);
-    if (tile + G1 < a.n_tiles) fetch(s1, tile + G1);
-  }
+  wait_loads();
+  fetch(s0, tile);
+  fetch(s1, tile + G1);
   __syncthreads();
   for (int it = 0;; it += 2) {
     step(s0, tile, 0, it);

@@ -157,7 +157,11 @@ __device__ inline void page_block(const PageMap& pm, int64_t seq, int64_t blk, i
   oseq = seq - b * pm.hkv;
   int64_t lp = blk >> pm.ppb_shift;
   lp = lp < pm.max_pages ? lp : pm.max_pages - 1;
-  int64_t pg = pm.table[b * pm.max_pages + lp];
+  // the block's page is the same for the whole workgroup: read it through
+  // the scalar cache (constant address space), so that it takes no part in
+  // the vector-memory waits of the tile loads in flight
+  typedef const __attribute__((address_space(4))) int32_t* ctab_t;
+  int64_t pg = ((ctab_t)(uintptr_t)pm.table)[b * pm.max_pages + lp];
   pg = pg < 0 ? 0 : (pg >= pm.n_pages ? pm.n_pages - 1 : pg);
   oblk = (pg << pm.ppb_shift) + (blk & ((1LL << pm.ppb_shift) - 1));
 }
