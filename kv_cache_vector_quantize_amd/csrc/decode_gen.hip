@@ -15,7 +15,9 @@
 //     parts in columns 0-7, lo parts in 8-15, each value twice, facing the hi
 //     and lo of a centroid); the sketch operand of MFMA c holds sketch rows
 //     32c + 8 g4 .. + 7 (hi / lo columns).
-//  2. k_gsplit<BK>, 8 waves per workgroup, each wave a chunk of the row in
+//  2. k_gsplit<BK, BIG, WV>, 8 waves per workgroup (BIG: d > 128, up to 16
+//     query MFMAs and output blocks; WV: value codes over 4 bits, whose
+//     tile32 share per lane is twice as large), each wave a chunk of the row in
 //     32-token tiles of two 16-token blocks.  Key logits: a lane holds the
 //     key bits of its token's coordinates g4 dp/4 .. (g4 + 1) dp/4 - 1 in
 //     registers (BK is a template parameter, so the fields of MFMA u sit at
@@ -204,7 +206,7 @@ __device__ inline uint32_t kfield(const uint32_t (&wd)[NW], int off, int w) {
 
 // BIG: d > 128 (up to 16 query MFMAs and coordinate blocks); otherwise d <= 128
 // (up to 8), which leaves the registers to load each tile one tile ahead.
-template <int BK, bool BIG>
+template <int BK, bool BIG, bool WV>
 __global__ void __launch_bounds__(64 * kGWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) k_gsplit(GSArgs a) {
   constexpr int NU = BIG ? kGNu : kGNu / 2;   // query MFMAs per block / coordinate blocks, at most
   constexpr int KW = NU * BK / 8;             // key dwords of a lane's coordinate slice (dp/4 fields)
@@ -302,10 +304,14 @@ __global__ void __launch_bounds__(64 * kGWaves) __attribute__((amdgpu_waves_per_
   // 16 + c16, the token scalars of lane % 32, the lane's share of the tile32
   // block.  The next tile's loads go in flight while the current one is
   // computed (past the last tile they repeat it, so the count of loads in
-  // flight is the same on every pass): for d <= 128 as soon as the current
-  // one's are consumed, for d > 128 (16 output accumulators) after the key
-  // and sketch products, when the current key words are dead.
-  constexpr int VB = NU / 2;                  // 16-byte words of a tile32 block per lane
+  // flight is the same on every pass): as soon as the current one's are
+  // consumed, except with 16 output accumulators and key codes over 4 bits or
+  // value codes over 4 bits (registers): then after the key and sketch
+  // products, when the current key words are dead.
+  // 16-byte words of a tile32 block per lane: g16 bv / 16 (WV: value codes
+  // of more than 4 bits)
+  constexpr int VB = WV ? NU / 2 : NU / 4;
+  constexpr bool kEarly = !BIG || (!WV && BK <= 4);
   struct Raw {
     uint32_t kw[2][KW + 1];
     uint32_t sw[2][kGNs];
@@ -367,7 +373,7 @@ __global__ void __launch_bounds__(64 * kGWaves) __attribute__((amdgpu_waves_per_
 #pragma unroll
       for (int c = 0; c < kGNs; ++c) sw[blk][c] = R.sw[blk][c];
     }
-    if constexpr (!BIG) load(R, t_next);
+    if constexpr (kEarly) load(R, t_next);
 
     // ---- S^T = K^ Q~^T (16 tokens x 16 columns per block)
     f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
@@ -401,7 +407,7 @@ __global__ void __launch_bounds__(64 * kGWaves) __attribute__((amdgpu_waves_per_
           accq[blk] = mfma(s_sgn[(sw[blk][c] >> (8 * g4)) & 0xFFu], tb, accq[blk]);
       }
     }
-    if constexpr (BIG) load(R, t_next);
+    if constexpr (!kEarly) load(R, t_next);
     // logits (base 2): the scales per column, then hi + lo columns
     float lg[2][4];
 #pragma unroll
@@ -469,7 +475,7 @@ __global__ void __launch_bounds__(64 * kGWaves) __attribute__((amdgpu_waves_per_
       const int p0 = vp0 + 8 * a.bv * db;
       const uint32_t w0 = __builtin_amdgcn_alignbit(s_v32[(p0 >> 5) + 1], s_v32[p0 >> 5], p0 & 31);
       u32x4 va0, va1;
-      if (a.bv <= 4) {
+      if constexpr (!WV) {
         // all 8 fields in one window, read as pairs
         const int b2 = 2 * a.bv;
         const uint2 e0 = s_vp[__builtin_amdgcn_ubfe(w0, 0, b2)], e1 = s_vp[__builtin_amdgcn_ubfe(w0, b2, b2)];
@@ -603,8 +609,14 @@ __global__ void __launch_bounds__(256) k_gcombine(GCArgs a) {
 
 template <int BK>
 void launch_gsplit(const GSArgs& a, dim3 grid, hipStream_t st) {
-  if (a.dp > 128) hipLaunchKernelGGL((k_gsplit<BK, true>), grid, dim3(64 * kGWaves), 0, st, a);
-  else hipLaunchKernelGGL((k_gsplit<BK, false>), grid, dim3(64 * kGWaves), 0, st, a);
+  const bool wv = a.bv > 4;
+  if (a.dp > 128) {
+    if (wv) hipLaunchKernelGGL((k_gsplit<BK, true, true>), grid, dim3(64 * kGWaves), 0, st, a);
+    else hipLaunchKernelGGL((k_gsplit<BK, true, false>), grid, dim3(64 * kGWaves), 0, st, a);
+  } else {
+    if (wv) hipLaunchKernelGGL((k_gsplit<BK, false, true>), grid, dim3(64 * kGWaves), 0, st, a);
+    else hipLaunchKernelGGL((k_gsplit<BK, false, false>), grid, dim3(64 * kGWaves), 0, st, a);
+  }
 }
 
 }  // namespace
