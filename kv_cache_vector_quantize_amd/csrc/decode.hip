@@ -693,6 +693,7 @@ __global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_e
         ek[u][1] = lookup<BK, L::KC>(s_kt, field<BK>(T.kw[0], (4 * u + 2) * BK, 2 * BK), laneoff);
       }
     }
+    __builtin_amdgcn_s_setprio(1);
     // ---- QJL sign products (VALU work while the lookups land)
     f32x4 accq[2];
 #pragma unroll
@@ -736,6 +737,7 @@ __global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_e
       else acc[1] = mfma(as_bf16x8(ek[u][0].x, ek[u][0].y, ek[u][1].x, ek[u][1].y), qa[u], acc[1]);
       if (u & 1) vlook(T, u >> 1, ev[u >> 1]);
     }
+    __builtin_amdgcn_s_setprio(0);
     // lg = logit - Meff (base 2): the scales are applied per column before the
     // hi and lo columns are summed (both columns of a row share the token), and
     // each column carries -Meff/2
@@ -830,6 +832,7 @@ __global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_e
     const bf16x8 pop0 = as_bf16x8(pb[0], pb[0], pb[1], pb[1]);
     const bf16x8 pop1 = as_bf16x8(pb[2], pb[2], pb[3], pb[3]);
 
+    __builtin_amdgcn_s_setprio(1);
     // ---- O^T += V^ P^T (coordinates 16*db + c16); operand dwords
     // (hi, lo, hi, lo) of token slot pairs against duplicated weights; the
     // lookups of block db + 4 replace those of block db
@@ -840,6 +843,7 @@ __global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_e
       acc_o[db] = mfma(as_bf16x8(e[2].x, e[2].y, e[3].x, e[3].y), pop1, acc_o[db]);
       if (db < 4) vlook(T, db + 4, ev[db & 3]);
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // two-stage pipeline over full tiles: the next tile's loads are in flight
