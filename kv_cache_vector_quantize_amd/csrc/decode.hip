@@ -23,7 +23,7 @@
 //       O^T += V^ P^T   (in the value codebook's rotated domain),
 //     with an online softmax in base 2 whose reference maximum is only moved
 //     when a tile exceeds it by more than 2^8.  Code operands come from bf16
-//     hi/lo tables in LDS (pair tables, quad tables for 2- and 3-bit keys)
+//     hi/lo tables in LDS (pair tables, a quad table for 2-bit keys)
 //     indexed by packed indices; hi and lo sit next to each other in the
 //     contraction dimension (operand dwords hi,lo,hi,lo against a duplicated
 //     other operand), so a table read lands directly in the MFMA operand
@@ -282,17 +282,13 @@ __device__ inline uint32_t window(const uint32_t (&wd)[NW], int off) {
   return wd[i] >> s;
 }
 
-// Byte address in the quad key table of the operand of coordinates 4u ..
-// 4u + 3 of a lane's key bits (BK = 2: with the lane's copy offset, one
-// byte permute; BK = 3: the 12-bit index moved to bit 4 and masked).
+// Byte address in the 2-bit quad key table of the operand of coordinates
+// 4u .. 4u + 3 of a lane's key bits, with the lane's copy offset: one byte
+// permute.
 template <int BK>
 __device__ inline uint32_t quad_addr(const uint32_t (&kw)[BK], int u, uint32_t laneoff16) {
-  if constexpr (BK == 2) {
-    return __builtin_amdgcn_perm(kw[u >> 2], laneoff16, 0x0C0C0000u | ((4u + (u & 3)) << 8));
-  } else {
-    const uint32_t w = u == 0 ? (kw[0] << 4) : window<BK>(kw, 12 * u - 4);
-    return w & 0xFFF0u;
-  }
+  static_assert(BK == 2, "quad tables serve 2-bit keys");
+  return __builtin_amdgcn_perm(kw[u >> 2], laneoff16, 0x0C0C0000u | ((4u + (u & 3)) << 8));
 }
 
 template <int B>
@@ -316,16 +312,18 @@ constexpr int plain_bytes(int b) { return (b <= 4) ? table_entries_rt(b) * 8 : t
 constexpr int kPolarTrigEntries = 16 + 6 * 4;
 constexpr int kPolarKeyDwords = 5;      // code dwords a lane reads per token
 
-// Keys of 2 or 3 bits use a quad table: one 16-byte entry per four
-// coordinates (a 4 b-bit index, contiguous in the packed row) holds the
-// operand dwords {hi, lo} of both coordinate pairs, so one ds_read_b128
-// lands a whole MFMA operand.  The 2-bit table (4 KB) is held as 16
-// interleaved copies (entry e of copy c at byte e * 256 + c * 16: the 16
-// lanes of a read pass hit distinct banks); the 3-bit one (64 KB) once.
+// Keys of 2 bits use a quad table: one 16-byte entry per four coordinates
+// (an 8-bit index, one byte of the packed row) holds the operand dwords
+// {hi, lo} of both coordinate pairs, so one ds_read_b128 lands a whole MFMA
+// operand.  The table (4 KB) is held as 16 interleaved copies (entry e of
+// copy c at byte e * 256 + c * 16: the 16 lanes of a read pass hit distinct
+// banks).  Keys of 3 bits read a pair table whose index is a byte of the key
+// bits (see kw3_addr): a 3-bit quad table (64 KB) fits in LDS only once, and
+// its random 16-byte reads then collide in the banks.
 template <int BK>
 struct QuadKeys {
-  static constexpr bool on = BK == 2 || BK == 3;
-  static constexpr int copies = BK == 2 ? 16 : 1;
+  static constexpr bool on = BK == 2;
+  static constexpr int copies = 16;
   static constexpr int bytes = on ? (16 << (4 * BK)) * copies : 0;
 };
 
@@ -334,9 +332,11 @@ struct SplitLds {
   static constexpr bool VC = BV <= 4 && table_entries_rt(BV) * 8 * kCopies <= kCopyBudget;
   static constexpr int VBYTES = VC ? table_entries_rt(BV) * 8 * kCopies : plain_bytes(BV);
   static constexpr bool KQ = QuadKeys<BK>::on;
-  static constexpr bool KC = !KQ && BK >= 1 && BK <= 4 && VBYTES + table_entries_rt(BK) * 8 * kCopies <= kCopyBudget;
+  static constexpr bool KW = BK == 3;   // pair table indexed by key-bit windows (256 entries, 32 copies)
+  static constexpr bool KC = !KQ && !KW && BK >= 1 && BK <= 4 && VBYTES + table_entries_rt(BK) * 8 * kCopies <= kCopyBudget;
   static constexpr int KBYTES = BK == 0 ? kPolarTrigEntries * 8
                                         : KQ ? QuadKeys<BK>::bytes
+                                        : KW ? 256 * 8 * kCopies
                                              : (KC ? table_entries_rt(BK) * 8 * kCopies : plain_bytes(BK));
   static constexpr int OBYTES = kWaves * 8 * D * 4;    // merge buffer, aliases the tables
   static constexpr int RAW = (KBYTES + VBYTES > OBYTES) ? KBYTES + VBYTES : OBYTES;
@@ -457,6 +457,30 @@ __device__ inline void polar_operands(const uint32_t (&kw)[kPolarKeyDwords], con
   }
 }
 
+// 3-bit keys: the 16 six-bit pair fields of a lane's 96 key bits (pair j at
+// bit 6j) sit at byte 0 or byte 3 of eight 32-bit windows: window
+// (j & 3) + 4 (j >> 3) starts at the bit of pair j & 11, and pair j + 4 lies
+// 24 bits above pair j.  Seven funnel shifts form them.
+__device__ inline void kw3_windows(const uint32_t (&kw)[3], uint32_t (&w)[8]) {
+  w[0] = kw[0];
+  w[1] = __builtin_amdgcn_alignbit(kw[1], kw[0], 6);
+  w[2] = __builtin_amdgcn_alignbit(kw[1], kw[0], 12);
+  w[3] = __builtin_amdgcn_alignbit(kw[1], kw[0], 18);
+  w[4] = __builtin_amdgcn_alignbit(kw[2], kw[1], 16);
+  w[5] = __builtin_amdgcn_alignbit(kw[2], kw[1], 22);
+  w[6] = __builtin_amdgcn_alignbit(kw[2], kw[1], 28);
+  w[7] = kw[2] >> 2;
+}
+// Byte address of pair j in the 256-entry pair table, whose index is the
+// window byte (the pair's six bits and two bits of the next field; entry e
+// holds pair e & 63), with the lane's copy offset: one byte permute.  The
+// table is held as 32 interleaved copies like the value table (64 KB).
+__device__ inline uint32_t kw3_addr(const uint32_t (&w)[8], int j, uint32_t laneoff) {
+  const int wi = (j & 3) + 4 * (j >> 3);
+  const uint32_t t = ((j >> 2) & 1) ? 3u : 0u;
+  return __builtin_amdgcn_perm(w[wi], laneoff, 0x0C0C0000u | ((4u + t) << 8));
+}
+
 // Global loads of one 32-token tile for one lane.
 template <int BK, int BV>
 struct Tile {
@@ -490,6 +514,10 @@ __global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_e
       const uint4* kt = reinterpret_cast<const uint4*>(a.ktab);
       uint4* dk = reinterpret_cast<uint4*>(s_raw);
       for (int i = tid; i < L::KBYTES / 16; i += NT) dk[i] = kt[i / QuadKeys<BK>::copies];
+    } else if constexpr (L::KW) {
+      const uint2* kt = reinterpret_cast<const uint2*>(a.ktab);
+      uint2* dk = reinterpret_cast<uint2*>(s_raw);
+      for (int i = tid; i < L::KBYTES / 8; i += NT) dk[i] = kt[(i >> 5) & 63];
     } else {
       const uint2* kt = reinterpret_cast<const uint2*>(a.ktab);
       uint2* dk = reinterpret_cast<uint2*>(s_raw);
@@ -686,6 +714,14 @@ __global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_e
         eq[u] = *reinterpret_cast<const uint4*>(s_kt + quad_addr<BK>(T.kw[0], u, laneoff16));
     } else if constexpr (BK == 0) {
       polar_operands(T.kw[0], pl, reinterpret_cast<const f32x2*>(s_kt), ek);
+    } else if constexpr (L::KW) {
+      uint32_t w8[8];
+      kw3_windows(T.kw[0], w8);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        ek[u][0] = *reinterpret_cast<const uint2*>(s_kt + kw3_addr(w8, 2 * u, laneoff));
+        ek[u][1] = *reinterpret_cast<const uint2*>(s_kt + kw3_addr(w8, 2 * u + 1, laneoff));
+      }
     } else {
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -721,6 +757,15 @@ __global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_e
       for (int u = 0; u < 8; ++u)
         acc[0] = mfma(as_bf16x8(ek[u][0].x, ek[u][0].y, ek[u][1].x, ek[u][1].y), qa[u], acc[0]);
       polar_operands(T.kw[1], pl, reinterpret_cast<const f32x2*>(s_kt), ek);
+    } else if constexpr (L::KW) {
+      uint32_t w8[8];
+      kw3_windows(T.kw[1], w8);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        acc[0] = mfma(as_bf16x8(ek[u][0].x, ek[u][0].y, ek[u][1].x, ek[u][1].y), qa[u], acc[0]);
+        ek[u][0] = *reinterpret_cast<const uint2*>(s_kt + kw3_addr(w8, 2 * u, laneoff));
+        ek[u][1] = *reinterpret_cast<const uint2*>(s_kt + kw3_addr(w8, 2 * u + 1, laneoff));
+      }
     } else {
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -1109,7 +1154,7 @@ hipError_t launch_decode(const tq_codebook* kcb, const tq_codebook* vcb, const v
     sa.vscale = v.scale;
     sa.v_stride = v.seq_stride;
     sa.ktab = kcb->pq.polar ? reinterpret_cast<const uint32_t*>(kcb->dev.ptrig)
-                            : (kcb->p.bits <= 3 && kcb->p.bits >= 2 ? kcb->dev.quad_tab : kcb->dev.pair_tab);
+                            : (kcb->p.bits == 2 ? kcb->dev.quad_tab : kcb->dev.pair_tab);
     sa.vtab = vcb->dev.pair_tab;
     sa.ktab_dwords = kcb->dev.pair_tab_dwords;
     sa.vtab_dwords = vcb->dev.pair_tab_dwords;

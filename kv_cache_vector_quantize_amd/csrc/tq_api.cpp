@@ -412,7 +412,7 @@ tq_status tq_codebook_build(const tq_params* params, tq_codebook** out) {
         return hip_fail(e, "codebook upload");
       }
     }
-    if (cb->p.bits <= 3) {
+    if (cb->p.bits == 2) {
       const int b = cb->p.bits;
       const size_t n4 = (size_t)1 << (4 * b);
       std::vector<uint32_t> quad(4 * n4);

@@ -58,7 +58,7 @@ struct DeviceCodebook {
   //  bits  > 4: entry a holds one dword {hi(c[a]) | lo(c[a]) << 16}
   uint32_t* pair_tab = nullptr;
   int pair_tab_dwords = 0;
-  //  quad_tab (bits <= 3): entry e = a | b << bits | c << 2 bits | d << 3 bits
+  //  quad_tab (bits == 2): entry e = a | b << bits | c << 2 bits | d << 3 bits
   //  holds four dwords {hi(c[a]) | hi(c[b]) << 16, lo(c[a]) | lo(c[b]) << 16,
   //  hi(c[c]) | hi(c[d]) << 16, lo(c[c]) | lo(c[d]) << 16}: one 16-byte read
   //  gives the decode key operand of four coordinates
