@@ -375,6 +375,7 @@ __global__ void __launch_bounds__(64 * kGWaves) __attribute__((amdgpu_waves_per_
     }
     if constexpr (kEarly) load(R, t_next);
 
+    __builtin_amdgcn_s_setprio(1);
     // ---- S^T = K^ Q~^T (16 tokens x 16 columns per block)
     f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
     f32x4 accq[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
@@ -438,6 +439,7 @@ __global__ void __launch_bounds__(64 * kGWaves) __attribute__((amdgpu_waves_per_
           if (tt < lim) dst[tt] = lg[blk][r] * kLn2;
         }
     }
+    __builtin_amdgcn_s_setprio(0);
     // ---- online softmax (base 2); a column's maximum over the tile's tokens
     float tm = fmaxf(fmaxf(fmaxf(lg[0][0], lg[0][1]), fmaxf(lg[0][2], lg[0][3])),
                      fmaxf(fmaxf(lg[1][0], lg[1][1]), fmaxf(lg[1][2], lg[1][3])));
@@ -468,6 +470,7 @@ __global__ void __launch_bounds__(64 * kGWaves) __attribute__((amdgpu_waves_per_
         const float x = fmaf(-sel_lo, __uint_as_float(__float_as_uint(w) & 0xFFFF0000u), w);
         pop[blk][r] = __builtin_amdgcn_perm(__float_as_uint(x), __float_as_uint(x), 0x03020302u);
       }
+    __builtin_amdgcn_s_setprio(1);
     // ---- O^T += V^ P^T, coordinates 16 db + c16
 #pragma unroll
     for (int db = 0; db < NU; ++db) {
@@ -494,6 +497,7 @@ __global__ void __launch_bounds__(64 * kGWaves) __attribute__((amdgpu_waves_per_
       acc_o[db] = mfma(va0, pop[0], acc_o[db]);
       acc_o[db] = mfma(va1, pop[1], acc_o[db]);
     }
+    __builtin_amdgcn_s_setprio(0);
   }
 
   // positions of this wave's range that no tile covered (beyond len_b)

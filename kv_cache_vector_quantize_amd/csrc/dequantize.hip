@@ -394,6 +394,7 @@ __global__ void __launch_bounds__(256) k_dq128(DQArgs a) {
     lds_barrier();     // stage buf complete; stage buf ^ 1 and block buf ^ 1 free / ready
     build(rb, buf ^ 1, buf ^ 1);
 
+    __builtin_amdgcn_s_setprio(1);
     f32x16 acc = {}, accq = {};
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
@@ -412,6 +413,7 @@ __global__ void __launch_bounds__(256) k_dq128(DQArgs a) {
         accq = mfma32(ql[s], Bq, accq);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     int seq;
     int64_t blk;
     locate(k0, seq, blk);
