@@ -38,7 +38,10 @@
 // inside it, so idx = count + (y >= boundary).  Both sides of the compare are
 // taken in cell coordinates, key = z (G / |x|) + G against (t + 1) G, one FMA
 // per coordinate; fp32 rounding of the key only matters when a boundary lies
-// within ~3e-7 of y.
+// within ~3e-7 of y.  The staged table is padded to kQ128Cells entries with
+// the last cell, so the truncated key needs no clamp: for finite input |y|
+// exceeds 1 by far less than one cell.  |x| comes from the hardware square
+// root (within 1 ulp) and G / |x| from the hardware reciprocal.
 //
 // Pipeline.  The inputs of the next two tiles are in flight in registers
 // while the current tile is rotated, indexed and packed; the grid holds as
@@ -176,6 +179,23 @@ __device__ inline void share_mask(Share<DT>& sh, bool valid) {
   }
 }
 
+// Sum over each group of 8 consecutive lanes, in every lane of the group: DPP
+// exchanges within quads (lane ^ 1, lane ^ 2), then between the two quads of
+// each half row (mirror within 8 lanes); no LDS round trip.
+__device__ inline float sum8(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+  return v;
+}
+
+// |x| from |x|^2: the hardware square root (within 1 ulp) for normal inputs,
+// the correctly rounded library one below 2^-100
+__device__ inline float norm_from_sq(float s2) {
+  if (__builtin_expect(s2 < 0x1p-100f, 0)) return sqrtf(s2);
+  return __builtin_amdgcn_sqrtf(s2);
+}
+
 // All vector-memory loads issued so far have landed (vmcnt(0), other counters
 // left alone): the loop that follows then never waits on the operand loads.
 __device__ inline void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
@@ -207,7 +227,7 @@ __global__ void __launch_bounds__(256, NP == 2 ? 3 : 1) k_q128(Q128Args a) {
   const bool need_c = a.nc != 0;
   const float G = a.G;
   const int cmax = a.ncell - 1;
-  for (int i = tid; i < a.ncell; i += 256) s_tab[i] = a.qtab[i];
+  for (int i = tid; i < kQ128Cells; i += 256) s_tab[i] = a.qtab[i < cmax ? i : cmax];
   for (int i = tid; i < L; i += 256) s_cent[i] = a.cent[i];
 
   bf16x8 ph[8], pl[8], pm[NP == 3 ? 8 : 1];
@@ -305,14 +325,12 @@ __global__ void __launch_bounds__(256, NP == 2 ? 3 : 1) k_q128(Q128Args a) {
           *reinterpret_cast<uint4*>(&xl2[q][r8][c0 + 8]) = make_uint4(mw[4], mw[5], mw[6], mw[7]);
         }
       }
-      s2 += __shfl_xor(s2, 1);
-      s2 += __shfl_xor(s2, 2);
-      s2 += __shfl_xor(s2, 4);
+      s2 = sum8(s2);
       if ((tid & 7) == 0) {
         const int64_t p = abs0 + r8;
-        const float n = sqrtf(s2);
+        const float n = norm_from_sq(s2);
         s_n[q][r8] = n;
-        s_ig[q][r8] = n > 0.f ? G / n : 0.f;
+        s_ig[q][r8] = n > 0.f ? G * __builtin_amdgcn_rcpf(n) : 0.f;
         s_valid[q][r8] = (p >= a.tok_off && p < a.tok_off + a.n_tok) ? 1 : 0;
       }
     }
@@ -348,7 +366,7 @@ __global__ void __launch_bounds__(256, NP == 2 ? 3 : 1) k_q128(Q128Args a) {
     for (int v = 0; v < 16; ++v) {
       const int vec = T32 ? 8 * (v >> 2) + 4 * hl + (v & 3) : c32;
       const float key = fmaf(acc[v], s_ig[q][vec], G);
-      const int c = min((int)key, cmax);
+      const int c = (int)key;
       const int2 e = s_tab[c];
       iv[v] = e.x + (key >= __int_as_float(e.y) ? 1 : 0);
     }
@@ -390,7 +408,7 @@ __global__ void __launch_bounds__(256, NP == 2 ? 3 : 1) k_q128(Q128Args a) {
         gv[q] = g;
       }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) go[q] = (uint32_t)__shfl_xor((int)gv[q], 32);
+      for (int q = 0; q < 4; ++q) go[q] = __builtin_amdgcn_permlane32_swap(gv[q], gv[q], false, false)[1];
       if (hl == 0 && s_valid[q][c32]) {
         uint32_t* dst = reinterpret_cast<uint32_t*>(a.idx + (pos0 + c32) * a.idx_pitch) + wave * b;
         if (b == 4 && row16) {
@@ -516,7 +534,7 @@ __global__ void __launch_bounds__(512, 1) k_q128sk(Q128Args a) {
   const bool need_c = a.nc != 0;
   const float G = a.G;
   const int cmax = a.ncell - 1;
-  for (int i = tid; i < a.ncell; i += 512) s_tab[i] = a.qtab[i];
+  for (int i = tid; i < kQ128Cells; i += 512) s_tab[i] = a.qtab[i < cmax ? i : cmax];
   for (int i = tid; i < L; i += 512) s_cent[i] = a.cent[i];
 
   // rotation waves: op[8 p + s] = part p (hi, lo, lo2) of Pi at k-step s;
@@ -623,14 +641,12 @@ __global__ void __launch_bounds__(512, 1) k_q128sk(Q128Args a) {
           *reinterpret_cast<uint4*>(&xl2[q][r8][c0 + 8]) = make_uint4(mw[4], mw[5], mw[6], mw[7]);
         }
       }
-      s2 += __shfl_xor(s2, 1);
-      s2 += __shfl_xor(s2, 2);
-      s2 += __shfl_xor(s2, 4);
+      s2 = sum8(s2);
       if ((tid & 7) == 0) {
         const int64_t p = abs0 + r8;
-        const float n = sqrtf(s2);
+        const float n = norm_from_sq(s2);
         s_n[n3][r8] = n;
-        s_ig[q][r8] = n > 0.f ? G / n : 0.f;
+        s_ig[q][r8] = n > 0.f ? G * __builtin_amdgcn_rcpf(n) : 0.f;
         s_valid[n3][r8] = (p >= a.tok_off && p < a.tok_off + a.n_tok) ? 1 : 0;
       }
     }
@@ -671,7 +687,7 @@ __global__ void __launch_bounds__(512, 1) k_q128sk(Q128Args a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const float key = fmaf(acc[v], s_ig[q][c32], G);
-        const int c = min((int)key, cmax);
+        const int c = (int)key;
         const int2 e = s_tab[c];
         iv[v] = e.x + (key >= __int_as_float(e.y) ? 1 : 0);
       }
