@@ -271,7 +271,8 @@ __global__ void __launch_bounds__(256, NP == 2 ? 3 : 1) k_q128(Q128Args a) {
     // (a) stage this thread's share; |x| in fp32 from the input values,
     // reduced over the row's 8 threads
     {
-      share_mask<DT>(cur, abs0 + r8 >= a.tok_off && abs0 + r8 < a.tok_off + a.n_tok);
+      // a tile inside the written range stages every row as loaded
+      if (!full) share_mask<DT>(cur, abs0 + r8 >= a.tok_off && abs0 + r8 < a.tok_off + a.n_tok);
       float s2 = 0.f;
       if constexpr (DT == TQ_BF16) {
 #pragma unroll
@@ -587,7 +588,8 @@ __global__ void __launch_bounds__(512, 1) k_q128sk(Q128Args a) {
       int64_t blk;
       where(tile, seq, blk);
       const int64_t abs0 = blk * TILE;
-      share_mask<DT>(cur, abs0 + r8 >= a.tok_off && abs0 + r8 < a.tok_off + a.n_tok);
+      if (!(abs0 >= a.tok_off && abs0 + TILE <= a.tok_off + a.n_tok))
+        share_mask<DT>(cur, abs0 + r8 >= a.tok_off && abs0 + r8 < a.tok_off + a.n_tok);
       float s2 = 0.f;
       if constexpr (DT == TQ_BF16) {
 #pragma unroll
