@@ -441,6 +441,16 @@ __global__ void __launch_bounds__(256, NP == 2 ? 3 : 1) k_q128(Q128Args a) {
       const int C = c32 & 15, j = 2 * wave + (c32 >> 4);
       uint8_t* blk = a.idx + (oseq * (a.seq_stride / TILE) + oblk) * (int64_t)(512 * b);
       const uint64_t fm = (uint64_t)((1u << b) - 1u);
+      if (b == 4 && full) {
+        // 4-bit codes, whole tile: each group is one aligned word
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq) {
+          uint32_t v32 = 0u;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v32 |= (uint32_t)iv[4 * (qq + 2 * (e >> 2)) + (e & 3)] << (4 * e);
+          reinterpret_cast<uint32_t*>(blk)[(16 * (hl + 2 * qq) + C) * 8 + j] = v32;
+        }
+      } else
 #pragma unroll
       for (int qq = 0; qq < 2; ++qq) {
         const int Gq = hl + 2 * qq;
