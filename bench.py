@@ -5,7 +5,9 @@ A step is one serving-style pass over the 128K-context decode layer
 (B=8, 64 query heads, 8 KV heads, d=128, context 131072; keys 3-bit + 1-bit
 QJL m=128, values 4-bit): quantize the step's new key/value vector of every
 sequence into the compressed cache (position ctx-1), then decode attention
-for all 512 query heads straight from the packed codes.  Inputs and the
+for all 512 query heads straight from the packed codes, in one
+tq_attn_decode_append call (append + query prologue in one launch, then the
+split and combine launches).  Inputs and the
 compressed cache are resident in HBM before the timed region.
 
 Printed: ONE JSON line with the contract fields plus
@@ -132,8 +134,10 @@ def decode_workload(torch, tq, synth, dev):
     tau = 1.0 / math.sqrt(d)
 
     def step():
-        tq.tq_quantize_kv(kcb, vcb, k_new, v_new, kc, vc, tok_offset=N - 1)
-        tq.tq_attn_decode(kcb, vcb, q, kc, vc, N, tau, out=out, workspace=ws)
+        # one call: the new token of every sequence is quantized into the
+        # caches at position N - 1 (the query prologue rides in that launch),
+        # then the 8 query heads of each KV head attend over all N positions
+        tq.tq_attn_decode_append(kcb, vcb, k_new, v_new, N - 1, q, kc, vc, N, tau, out=out, workspace=ws)
 
     per_token_head = (3 * d // 8) + 4 * ((128 + 31) // 32) + 4 + 4 + (4 * d // 8) + 4   # 140 B
     cfg = dict(workload="decode-128k GQA layer", B=B, Hq=Hq, Hkv=Hkv, d=d, context=N,

@@ -243,6 +243,26 @@ tq_status tq_attn_decode(const tq_codebook* kcb, const tq_codebook* vcb, const v
                          float sm_scale, float* out, float* logits, void* workspace,
                          size_t ws_bytes, void* stream);
 
+/* One decode step: append the step's new keys and values to the caches,
+ * then attend ([WIT] 如何实现 item 1: quantize at each cache update, rotate
+ * the query once, attention from the indices).  Same results as
+ * tq_quantize_kv(kcb, vcb, k_new, v_new, kv_dtype, B*Hkv, n_new, tok_offset,
+ * k, v, stream) followed by tq_attn_decode(...) with the remaining
+ * arguments; the query prologue of the d = 128 kernels then runs in the
+ * append launch instead of a launch of its own.
+ *  k_new, v_new  device [B*Hkv][n_new][d] (sequence s = b*Hkv + h), dtype
+ *                kv_dtype, both required; written to positions
+ *                [tok_offset, tok_offset + n_new) with tok_offset + n_new <= n_ctx
+ *  other arguments as tq_attn_decode (workspace: tq_attn_decode_workspace)
+ * Every argument of both parts is checked before anything is launched.
+ * Errors: those of tq_quantize_kv and tq_attn_decode. */
+tq_status tq_attn_decode_append(const tq_codebook* kcb, const tq_codebook* vcb, const void* k_new,
+                                const void* v_new, int32_t kv_dtype, int64_t n_new, int64_t tok_offset,
+                                const void* q, int32_t qdt, int64_t B, int64_t Hq, int64_t Hkv,
+                                const tq_codes* k, const tq_codes* v, const int32_t* seq_lens, int64_t n_ctx,
+                                float sm_scale, float* out, float* logits, void* workspace, size_t ws_bytes,
+                                void* stream);
+
 /* tq_attn_decode for callers that cannot allocate device memory: code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
  * Same computation, arguments, results and errors as tq_attn_decode, but

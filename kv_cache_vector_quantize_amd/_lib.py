@@ -28,6 +28,7 @@ EXPORTS = (
     "tq_ip_topk_workspace", "tq_ip_topk", "tq_dequantize", "tq_quantize_kv_paged",
     "tq_attn_decode_paged_workspace", "tq_attn_decode_paged", "tq_profile_enable", "tq_profile_read",
     "tq_codebook_solver_limits", "tq_profile_durations", "tq_stream_read", "tq_stream_write", "tq_attn_decode_noalloc",
+    "tq_attn_decode_append",
     "tq_polar_codebook_build", "tq_polar_codebook_values", "tq_ip_topk_exact_scan", "tq_ip_topk_scan_count",
     "tq_last_error",
 )
@@ -84,6 +85,9 @@ def lib() -> ctypes.CDLL:
     L.tq_attn_decode.argtypes = [vp, vp, vp, i32, i64, i64, i64, ctypes.POINTER(tq_codes),
                                  ctypes.POINTER(tq_codes), vp, i64, ctypes.c_float, vp, vp, vp,
                                  ctypes.c_size_t, vp]
+    L.tq_attn_decode_append.argtypes = [vp, vp, vp, vp, i32, i64, i64, vp, i32, i64, i64, i64,
+                                         ctypes.POINTER(tq_codes), ctypes.POINTER(tq_codes), vp, i64,
+                                         ctypes.c_float, vp, vp, vp, ctypes.c_size_t, vp]
     L.tq_attn_decode_noalloc.argtypes = [vp, vp, vp, i32, i64, i64, i64, ctypes.POINTER(tq_codes),
                                          ctypes.POINTER(tq_codes), vp, i64, ctypes.c_float, vp, vp, vp]
     L.tq_ip_topk_workspace.argtypes = [i64, i64, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
@@ -358,6 +362,34 @@ def tq_attn_decode(kcb, vcb, q, k_codes: Codes, v_codes: Codes, n_ctx: int, sm_s
         ctypes.byref(vd), seq_lens.data_ptr() if seq_lens is not None else None, int(n_ctx),
         float(sm_scale), out.data_ptr(), logits.data_ptr() if logits is not None else None,
         workspace.data_ptr(), workspace.numel(), _stream_handle(stream)))
+    return out
+
+
+def tq_attn_decode_append(kcb, vcb, k_new, v_new, tok_offset: int, q, k_codes: Codes, v_codes: Codes,
+                          n_ctx: int, sm_scale: float, seq_lens=None, out=None, logits=None, workspace=None,
+                          stream=None):
+    """One decode step: k_new, v_new ([B*Hkv, n_new, d] torch tensors, same
+    dtype) go to positions [tok_offset, tok_offset + n_new) of their
+    sequences, then q ([B, Hq, d]) attends.  Returns out (fp32 [B, Hq, d])."""
+    import torch
+    B, Hq, d = q.shape
+    Hkv = k_codes.n_seq // B
+    for t in (k_new, v_new):
+        if not t.is_contiguous():
+            raise ValueError("inputs must be contiguous")
+    n_new = k_new.shape[1]
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        ws = tq_attn_decode_workspace(B, Hq, Hkv, n_ctx, d)
+        workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=q.device)
+    kd, vd = k_codes.descriptor(), v_codes.descriptor()
+    _check(lib().tq_attn_decode_append(
+        kcb.handle, vcb.handle, k_new.data_ptr(), v_new.data_ptr(), _dtype_code(k_new), int(n_new),
+        int(tok_offset), q.data_ptr(), _dtype_code(q), B, Hq, Hkv, ctypes.byref(kd), ctypes.byref(vd),
+        seq_lens.data_ptr() if seq_lens is not None else None, int(n_ctx), float(sm_scale), out.data_ptr(),
+        logits.data_ptr() if logits is not None else None, workspace.data_ptr(), workspace.numel(),
+        _stream_handle(stream)))
     return out
 
 

@@ -12,6 +12,7 @@
 // block of Z = X Pi^T; with QJL, waves dp/32.. keep a 32-row slice of S and
 // compute U = R S^T the same way, and each 64-lane ballot of U >= 0 is two
 // finished 32-bit sign words.
+#include "decode_prologue.hpp"
 #include "tq_internal.hpp"
 
 namespace tq {
@@ -343,6 +344,10 @@ struct SmallJob {
 
 struct SmallArgs {
   SmallJob job[2];
+  int64_t nvec;      // vectors per job (n_seq * n_tok)
+  int njobs;         // job rows of the grid; a further row runs the decode prologue
+  PArgs pro;         // decode query prologue of pro_rows rows (4 workgroups each)
+  int64_t pro_rows;
 };
 
 __device__ inline float wave_sum(float v) {
@@ -362,6 +367,15 @@ __global__ void __launch_bounds__(4 * NI) k_quantize_small(SmallArgs sa) {
   // memory round trip in total.
   constexpr int NT = 4 * NI, KQ = NI / 4, NW = NI / 64;
   constexpr bool PRE = NI == 128;
+  if ((int)blockIdx.y >= sa.njobs) {
+    // the fused decode step: workgroup (4 row + part) of this grid row forms
+    // the query operands of decode row `row` (its first 256 threads work,
+    // the others only meet its barriers)
+    if ((int64_t)(blockIdx.x >> 2) >= sa.pro_rows) return;
+    prologue::run(sa.pro, (int)(blockIdx.x & 3), (int)(blockIdx.x >> 2), threadIdx.x < 256);
+    return;
+  }
+  if ((int64_t)blockIdx.x >= sa.nvec) return;   // the grid is as wide as the prologue's
   const SmallJob& a = sa.job[blockIdx.y];
   __shared__ float xs[NI];
   __shared__ float part[4][NI];
@@ -542,11 +556,19 @@ static SmallJob make_small_job(const tq_codebook* cb, const QuantJob& job) {
 }
 
 hipError_t launch_quantize_small(const tq_codebook* const* cbs, const QuantJob* jobs, int njobs,
-                                 hipStream_t stream) {
+                                 hipStream_t stream, const PArgs* pro, int64_t pro_rows) {
   SmallArgs sa{};
   for (int t = 0; t < njobs; ++t) sa.job[t] = make_small_job(cbs[t], jobs[t]);
   const int64_t nvec = jobs[0].n_seq * jobs[0].n_tok;
-  const dim3 grid((unsigned)nvec, (unsigned)njobs);
+  sa.nvec = nvec;
+  sa.njobs = njobs;
+  if (pro) {
+    sa.pro = *pro;
+    sa.pro_rows = pro_rows;
+  }
+  const int64_t gx = pro && 4 * pro_rows > nvec ? 4 * pro_rows : nvec;
+  if (gx > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)gx, (unsigned)(njobs + (pro ? 1 : 0)));
   ProfileScope prof(TQ_KERNEL_QUANTIZE, stream);
   bool wide = false;
   for (int t = 0; t < njobs; ++t) wide = wide || cbs[t]->dp > 128 || cbs[t]->mp > 128;

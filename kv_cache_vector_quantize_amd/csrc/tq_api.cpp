@@ -716,7 +716,8 @@ namespace {
 tq_status quantize_impl(const tq_codebook* kcb, const tq_codebook* vcb, const void* k, const void* v,
                         tq_dtype dt, int64_t n_seq, int64_t n_tok, int64_t tok_offset,
                         const tq_codes* k_out, const tq_codes* v_out, void* stream, int64_t need_len,
-                        const PageMap& pm) {
+                        const PageMap& pm, const PArgs* pro = nullptr, int64_t pro_rows = 0,
+                        bool* pro_done = nullptr) {
   const void* xs[2] = {k, v};
   const tq_codebook* cbs[2] = {kcb, vcb};
   const tq_codes* outs[2] = {k_out, v_out};
@@ -751,8 +752,9 @@ tq_status quantize_impl(const tq_codebook* kcb, const tq_codebook* vcb, const vo
       sc[nj] = cbs[t];
       sj[nj++] = QuantJob{xs[t], dt, n_seq, n_tok, tok_offset, *outs[t], pm};
     }
-    hipError_t e = launch_quantize_small(sc, sj, nj, static_cast<hipStream_t>(stream));
+    hipError_t e = launch_quantize_small(sc, sj, nj, static_cast<hipStream_t>(stream), pro, pro_rows);
     if (e != hipSuccess) return hip_fail(e, "quantize launch");
+    if (pro_done) *pro_done = pro != nullptr;
     return TQ_OK;
   }
   for (int t = 0; t < 2; ++t) {
@@ -860,7 +862,8 @@ namespace {
 tq_status decode_impl(const tq_codebook* kcb, const tq_codebook* vcb, const void* q, int32_t qdt_in, int64_t B,
                       int64_t Hq, int64_t Hkv, const tq_codes* k, const tq_codes* v, const int32_t* seq_lens,
                       int64_t n_ctx, float sm_scale, float* out, float* logits, void* workspace,
-                      size_t ws_bytes, void* stream, int64_t need_len, int page_tokens, const PageMap& pm) {
+                      size_t ws_bytes, void* stream, int64_t need_len, int page_tokens, const PageMap& pm,
+                      bool launch = true, bool prologue_done = false, DecodePlan* plan_out = nullptr) {
   if (!kcb || !vcb) return fail(TQ_ERR_INVALID, "codebook is NULL");
   if (!dtype_ok(qdt_in)) return fail(TQ_ERR_INVALID, "bad dtype");
   const tq_dtype qdt = static_cast<tq_dtype>(qdt_in);
@@ -900,8 +903,10 @@ tq_status decode_impl(const tq_codebook* kcb, const tq_codebook* vcb, const void
     return fail(TQ_ERR_INVALID, "workspace missing or smaller than the workspace query");
   if (!aligned(workspace, 256)) return fail(TQ_ERR_INVALID, "workspace must be 256-byte aligned");
   if (!aligned(out, 16)) return fail(TQ_ERR_INVALID, "out must be 16-byte aligned");
+  if (plan_out) *plan_out = plan;
+  if (!launch) return TQ_OK;
   hipError_t e = launch_decode(kcb, vcb, q, qdt, plan, *k, *v, seq_lens, sm_scale, out,
-                               logits, workspace, static_cast<hipStream_t>(stream), pm);
+                               logits, workspace, static_cast<hipStream_t>(stream), pm, prologue_done);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return TQ_OK;
 }
@@ -924,6 +929,44 @@ tq_status tq_attn_decode(const tq_codebook* kcb, const tq_codebook* vcb, const v
                        workspace, ws_bytes, stream, n_ctx, 0, PageMap{});
   } catch (...) {
     return fail(TQ_ERR_ALLOC, "tq_attn_decode: unexpected exception");
+  }
+}
+
+tq_status tq_attn_decode_append(const tq_codebook* kcb, const tq_codebook* vcb, const void* k_new,
+                                const void* v_new, int32_t kv_dtype, int64_t n_new, int64_t tok_offset,
+                                const void* q, int32_t qdt, int64_t B, int64_t Hq, int64_t Hkv,
+                                const tq_codes* k, const tq_codes* v, const int32_t* seq_lens, int64_t n_ctx,
+                                float sm_scale, float* out, float* logits, void* workspace, size_t ws_bytes,
+                                void* stream) {
+  log_call("tq_attn_decode_append kv_dtype=%d n_new=%lld tok_offset=%lld qdt=%d B=%lld Hq=%lld Hkv=%lld "
+           "n_ctx=%lld sm_scale=%g seq_lens=%p out=%p logits=%p workspace=%p ws_bytes=%zu stream=%p",
+           kv_dtype, (long long)n_new, (long long)tok_offset, qdt, (long long)B, (long long)Hq, (long long)Hkv,
+           (long long)n_ctx, (double)sm_scale, (const void*)seq_lens, (void*)out, (void*)logits, workspace,
+           ws_bytes, stream);
+  try {
+    if (!k_new || !v_new) return fail(TQ_ERR_INVALID, "k_new and v_new must be non-NULL");
+    if (!dtype_ok(kv_dtype)) return fail(TQ_ERR_INVALID, "bad dtype");
+    if (n_new < 1 || tok_offset < 0 || tok_offset + n_new > n_ctx)
+      return fail(TQ_ERR_INVALID, "need n_new >= 1 and 0 <= tok_offset, tok_offset + n_new <= n_ctx");
+    // every check of both calls before anything is launched
+    DecodePlan plan{};
+    tq_status s = decode_impl(kcb, vcb, q, qdt, B, Hq, Hkv, k, v, seq_lens, n_ctx, sm_scale, out, logits,
+                              workspace, ws_bytes, stream, n_ctx, 0, PageMap{}, false, false, &plan);
+    if (s != TQ_OK) return s;
+    if (B * Hq == 0)
+      return quantize_impl(kcb, vcb, k_new, v_new, static_cast<tq_dtype>(kv_dtype), B * Hkv, n_new, tok_offset, k, v,
+                           stream, tok_offset + n_new, PageMap{});
+    PArgs pro{};
+    const bool fuse = n_new <= kSmallMaxTok && !kcb->pq.polar && !vcb->pq.polar &&
+                      make_decode_prologue(kcb, vcb, q, static_cast<tq_dtype>(qdt), plan, sm_scale, workspace, &pro);
+    bool pro_done = false;
+    s = quantize_impl(kcb, vcb, k_new, v_new, static_cast<tq_dtype>(kv_dtype), B * Hkv, n_new, tok_offset, k, v,
+                      stream, tok_offset + n_new, PageMap{}, fuse ? &pro : nullptr, plan.rows, &pro_done);
+    if (s != TQ_OK) return s;
+    return decode_impl(kcb, vcb, q, qdt, B, Hq, Hkv, k, v, seq_lens, n_ctx, sm_scale, out, logits, workspace,
+                       ws_bytes, stream, n_ctx, 0, PageMap{}, true, pro_done, nullptr);
+  } catch (...) {
+    return fail(TQ_ERR_ALLOC, "tq_attn_decode_append: unexpected exception");
   }
 }
 

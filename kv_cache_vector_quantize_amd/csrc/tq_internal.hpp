@@ -184,8 +184,23 @@ hipError_t launch_quantize128(const tq_codebook* cb, const QuantJob& job, hipStr
 
 // Few vectors per sequence (appends): one workgroup per vector; K and V jobs in
 // one launch.  njobs in 1..2, jobs share n_seq, n_tok and dtype.
+// Query prologue of the d = 128 decode kernels (decode_prologue.hpp): one
+// workgroup per (part, row) of a plan, part 0..3 covering 32 coordinates.
+struct PArgs {
+  const void* q;
+  int qdt;
+  int Hq, Hkv, g, qgroups;
+  int m, mp;
+  float qscale;           // sm_scale * log2(e)
+  const float* rotKT;     // [128][128], rotKT[k][i] = Pi_K[i][k]
+  const float* sprotKT;   // [128][mp], sprotKT[k][j] = sqrt(pi/2)/m (S_K Pi_K)[j][k] (or null)
+  uint32_t* qop;          // [rows][query-operand dwords]
+};
+
+// pro != nullptr: the launch also runs the decode query prologue of pro_rows
+// rows (4 workgroups per row) beside the appends, saving its own launch.
 hipError_t launch_quantize_small(const tq_codebook* const* cbs, const QuantJob* jobs, int njobs,
-                                 hipStream_t stream);
+                                 hipStream_t stream, const PArgs* pro = nullptr, int64_t pro_rows = 0);
 constexpr int64_t kSmallMaxTok = 8;   // appends of up to this many tokens per sequence
 
 // Dequantize positions [tok_offset, tok_offset + n_tok) of n_seq sequences
@@ -220,7 +235,11 @@ hipError_t launch_decode(const tq_codebook* kcb, const tq_codebook* vcb, const v
                          tq_dtype qdt, const DecodePlan& plan, const tq_codes& k,
                          const tq_codes& v, const int32_t* seq_lens, float sm_scale,
                          float* out, float* logits, void* ws, hipStream_t stream,
-                         const PageMap& pm = PageMap{});
+                         const PageMap& pm = PageMap{}, bool prologue_done = false);
+// The query-prologue arguments of a d = 128 plan (false when the any-shape
+// kernels serve the codebooks, whose prologue is their own).
+bool make_decode_prologue(const tq_codebook* kcb, const tq_codebook* vcb, const void* q, tq_dtype qdt,
+                          const DecodePlan& plan, float sm_scale, void* ws, PArgs* out);
 
 // d = 128 MFMA kernels (decode.hip)
 bool decode_supported(const tq_codebook* kcb, const tq_codebook* vcb);
